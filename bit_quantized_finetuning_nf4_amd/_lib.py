@@ -1,0 +1,108 @@
+"""ctypes view of libqlora.so (include/qlora.h).
+
+The library is loaded on first use from this package directory.  There is no
+fallback: a missing library is an error.
+"""
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqlora.so")
+
+QLORA_OK = 0
+QLORA_OP_FWD, QLORA_OP_BWD, QLORA_OP_GEMV = 0, 1, 2
+
+STATUS_NAMES = {
+    0: "QLORA_OK", 1: "QLORA_E_NULL", 2: "QLORA_E_ALIGN", 3: "QLORA_E_SHAPE",
+    4: "QLORA_E_UNSUPPORTED", 5: "QLORA_E_WORKSPACE", 6: "QLORA_E_HIP",
+}
+
+# every function include/qlora.h declares
+EXPORTS = [
+    "qlora_status_str", "qlora_last_hip_error", "qlora_version", "qlora_nf4_levels",
+    "qlora_sizes", "qlora_workspace_bytes", "qlora_quantize", "qlora_dequant",
+    "qlora_linear_fwd", "qlora_linear_bwd", "qlora_gemv",
+]
+
+
+class Nf4WeightDesc(ctypes.Structure):
+    _fields_ = [
+        ("rows", ctypes.c_int64),
+        ("cols", ctypes.c_int64),
+        ("blocksize", ctypes.c_int32),
+        ("group_blocks", ctypes.c_int32),
+        ("codes", ctypes.c_void_p),
+        ("absmax_q", ctypes.c_void_p),
+        ("group_scale", ctypes.c_void_p),
+    ]
+
+
+class GemvJobDesc(ctypes.Structure):
+    _fields_ = [
+        ("W", ctypes.POINTER(Nf4WeightDesc)),
+        ("x", ctypes.c_void_p),
+        ("A", ctypes.c_void_p),
+        ("B", ctypes.c_void_p),
+        ("r", ctypes.c_int32),
+        ("alpha", ctypes.c_float),
+        ("y", ctypes.c_void_p),
+    ]
+
+
+class QloraError(RuntimeError):
+    def __init__(self, status, what):
+        self.status = status
+        msg = STATUS_NAMES.get(status, str(status))
+        try:
+            msg = lib().qlora_status_str(status).decode()
+            if status == 6:
+                msg += f" (hipError {lib().qlora_last_hip_error()})"
+        except Exception:  # pragma: no cover
+            pass
+        super().__init__(f"{what}: {msg}")
+
+
+_lib = None
+
+
+def lib():
+    """Load libqlora.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is missing: build it with `python -m bit_quantized_finetuning_nf4_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+    W = ctypes.POINTER(Nf4WeightDesc)
+    L.qlora_status_str.restype = ctypes.c_char_p
+    L.qlora_status_str.argtypes = [ctypes.c_int]
+    L.qlora_last_hip_error.restype = ctypes.c_int
+    L.qlora_last_hip_error.argtypes = []
+    L.qlora_version.restype = ctypes.c_char_p
+    L.qlora_version.argtypes = []
+    L.qlora_nf4_levels.restype = None
+    L.qlora_nf4_levels.argtypes = [ctypes.POINTER(ctypes.c_float)]
+    L.qlora_sizes.restype = ctypes.c_int
+    L.qlora_sizes.argtypes = [i64, i64, i32, i32, ctypes.POINTER(sz), ctypes.POINTER(sz), ctypes.POINTER(sz)]
+    L.qlora_workspace_bytes.restype = sz
+    L.qlora_workspace_bytes.argtypes = [ctypes.c_int, i64, i64, i64, i32, i32]
+    L.qlora_quantize.restype = ctypes.c_int
+    L.qlora_quantize.argtypes = [vp, W, vp]
+    L.qlora_dequant.restype = ctypes.c_int
+    L.qlora_dequant.argtypes = [W, vp, vp]
+    L.qlora_linear_fwd.restype = ctypes.c_int
+    L.qlora_linear_fwd.argtypes = [W, vp, i64, vp, vp, i32, f32, vp, vp, vp, sz, vp]
+    L.qlora_linear_bwd.restype = ctypes.c_int
+    L.qlora_linear_bwd.argtypes = [W, vp, vp, i64, vp, vp, i32, f32, vp, vp, vp, vp, vp, sz, vp]
+    L.qlora_gemv.restype = ctypes.c_int
+    L.qlora_gemv.argtypes = [ctypes.POINTER(GemvJobDesc), i32, vp, sz, vp]
+    _lib = L
+    return L
+
+
+def check(status, what):
+    if status != QLORA_OK:
+        raise QloraError(status, what)

@@ -1,0 +1,311 @@
+// capi.hip -- the extern "C" boundary of libqlora (declared in include/qlora.h).
+//
+// Every entry point validates all of its arguments before it enqueues
+// anything, never allocates and never synchronizes.  Scratch memory comes
+// from the caller's workspace, carved as follows (each piece 256-byte
+// aligned):
+//   FWD  (r > 0): U bf16 [M x r] | split partials of X A^T (fp32)
+//   BWD  (r > 0): G bf16 [M x r] | U bf16 [M x r] | split partials (fp32,
+//                 the largest of X A^T, dY B, G^T X, dY^T U)
+//   GEMV        : per job, 128 fp32 for u = A x
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstring>
+
+#include "../../include/qlora.h"
+#include "kernels.h"
+
+using namespace qlora;
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+constexpr size_t kAlign = 256;
+constexpr int kMaxRank = 128;
+constexpr int kMaxJobs = 4096;
+constexpr int64_t kMaxGemvCols = 65536;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+qlora_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return QLORA_OK;
+  g_last_hip_error = (int)e;
+  return QLORA_E_HIP;
+}
+
+qlora_status check_weight(const qlora_nf4_weight* q) {
+  if (!q) return QLORA_E_NULL;
+  if (q->rows <= 0 || q->cols <= 0) return QLORA_E_SHAPE;
+  if (q->blocksize != 64 || q->group_blocks != 256) return QLORA_E_UNSUPPORTED;
+  if (!q->codes || !q->absmax_q || !q->group_scale) return QLORA_E_NULL;
+  if (!aligned16(q->codes) || (reinterpret_cast<uintptr_t>(q->group_scale) & 3u)) return QLORA_E_ALIGN;
+  return QLORA_OK;
+}
+
+// GEMM paths: K % 64 == 0 (blocks never straddle rows), N % 8 == 0 (16-byte
+// rows of dY / Y), 32-bit tile indices.
+qlora_status check_gemm_weight(const qlora_nf4_weight* q) {
+  qlora_status st = check_weight(q);
+  if (st != QLORA_OK) return st;
+  if (q->cols % 64 != 0 || q->rows % 8 != 0) return QLORA_E_UNSUPPORTED;
+  return QLORA_OK;
+}
+
+qlora_status check_rank(int32_t r, const void* A, const void* B) {
+  if (r < 0 || r > kMaxRank || r % 8 != 0) return QLORA_E_UNSUPPORTED;
+  if (r > 0) {
+    if (!A || !B) return QLORA_E_NULL;
+    if (!aligned16(A) || !aligned16(B)) return QLORA_E_ALIGN;
+  }
+  return QLORA_OK;
+}
+
+Nf4View view(const qlora_nf4_weight* q) {
+  return Nf4View{q->codes, q->absmax_q, q->group_scale, q->rows, q->cols};
+}
+
+struct FwdLayout {
+  size_t u, part, total;
+};
+FwdLayout fwd_layout(int64_t M, int64_t N, int64_t K, int32_t r) {
+  FwdLayout L{0, 0, 0};
+  if (r == 0) return L;
+  L.u = 0;
+  L.part = align_up((size_t)M * r * 2);
+  L.total = L.part + align_up(skinny_partial_bytes(M, r, K, kXAt));
+  (void)N;
+  return L;
+}
+
+struct BwdLayout {
+  size_t g, u, part, total;
+};
+BwdLayout bwd_layout(int64_t M, int64_t N, int64_t K, int32_t r) {
+  BwdLayout L{0, 0, 0, 0};
+  if (r == 0) return L;
+  const size_t mr = align_up((size_t)M * r * 2);
+  L.g = 0;
+  L.u = mr;
+  L.part = 2 * mr;
+  size_t p = skinny_partial_bytes(M, r, K, kXAt);
+  p = std::max(p, skinny_partial_bytes(M, r, N, kDyB));
+  p = std::max(p, skinny_partial_bytes(r, K, M, kGtX));
+  p = std::max(p, skinny_partial_bytes(N, r, M, kDytU));
+  L.total = L.part + align_up(p);
+  return L;
+}
+
+char* ws_at(void* ws, size_t off) { return static_cast<char*>(ws) + off; }
+
+}  // namespace
+
+extern "C" {
+
+const char* qlora_status_str(qlora_status s) {
+  switch (s) {
+    case QLORA_OK: return "QLORA_OK";
+    case QLORA_E_NULL: return "QLORA_E_NULL: a required pointer is NULL";
+    case QLORA_E_ALIGN: return "QLORA_E_ALIGN: a pointer is not 16-byte aligned";
+    case QLORA_E_SHAPE: return "QLORA_E_SHAPE: a size is not positive or sizes disagree";
+    case QLORA_E_UNSUPPORTED: return "QLORA_E_UNSUPPORTED: unsupported blocksize, group, shape or rank";
+    case QLORA_E_WORKSPACE: return "QLORA_E_WORKSPACE: workspace smaller than qlora_workspace_bytes()";
+    case QLORA_E_HIP: return "QLORA_E_HIP: HIP launch error (see qlora_last_hip_error)";
+  }
+  return "QLORA_E_UNKNOWN";
+}
+
+int qlora_last_hip_error(void) { return g_last_hip_error; }
+
+const char* qlora_version(void) { return "0.1.0"; }
+
+void qlora_nf4_levels(float out[16]) {
+  // Same bit patterns as the device table (device.h); see the construction
+  // there.
+  static const uint32_t bits[16] = {
+      0xBF800000u, 0xBF3239B1u, 0xBF066B2Eu, 0xBECA329Eu, 0xBE91A24Bu, 0xBE3D353Du,
+      0xBDBA7869u, 0x00000000u, 0x3DA2FB01u, 0x3E24CADFu, 0x3E7C04DAu, 0x3EAD0336u,
+      0x3EE1A4B5u, 0x3F1007A9u, 0x3F3913B0u, 0x3F800000u};
+  if (!out) return;
+  std::memcpy(out, bits, sizeof(bits));
+}
+
+qlora_status qlora_sizes(int64_t rows, int64_t cols, int32_t blocksize, int32_t group_blocks,
+                         size_t* codes_bytes, size_t* absmax_q_bytes, size_t* scale_bytes) {
+  if (rows <= 0 || cols <= 0) return QLORA_E_SHAPE;
+  if (blocksize != 64 || group_blocks != 256) return QLORA_E_UNSUPPORTED;
+  if (rows > (int64_t)1 << 40 || cols > (int64_t)1 << 40 || rows > INT64_MAX / cols) return QLORA_E_SHAPE;
+  const int64_t n = rows * cols;
+  const int64_t nb = (n + 63) / 64;
+  const int64_t ng = (nb + 255) / 256;
+  if (codes_bytes) *codes_bytes = (size_t)((n + 1) / 2);
+  if (absmax_q_bytes) *absmax_q_bytes = (size_t)nb;
+  if (scale_bytes) *scale_bytes = (size_t)ng * sizeof(float);
+  return QLORA_OK;
+}
+
+size_t qlora_workspace_bytes(qlora_op op, int64_t M, int64_t N, int64_t K, int32_t r, int32_t njobs) {
+  switch (op) {
+    case QLORA_OP_FWD:
+      if (M <= 0 || N <= 0 || K <= 0 || r < 0 || r > kMaxRank) return 0;
+      return fwd_layout(M, N, K, r).total;
+    case QLORA_OP_BWD:
+      if (M <= 0 || N <= 0 || K <= 0 || r < 0 || r > kMaxRank) return 0;
+      return bwd_layout(M, N, K, r).total;
+    case QLORA_OP_GEMV:
+      if (njobs <= 0 || njobs > kMaxJobs) return 0;
+      return (size_t)njobs * kMaxRank * sizeof(float);
+  }
+  return 0;
+}
+
+qlora_status qlora_quantize(const uint16_t* W, const qlora_nf4_weight* q, void* stream) {
+  qlora_status st = check_weight(q);
+  if (st != QLORA_OK) return st;
+  if (!W) return QLORA_E_NULL;
+  if (!aligned16(W)) return QLORA_E_ALIGN;
+  if (q->rows > INT64_MAX / q->cols) return QLORA_E_SHAPE;
+  const int64_t n = q->rows * q->cols;
+  if ((n + 16383) / 16384 > 0x7FFFFFFF) return QLORA_E_SHAPE;
+  return hip_status(launch_quantize(W, n, q->codes, q->absmax_q, q->group_scale, (hipStream_t)stream));
+}
+
+qlora_status qlora_dequant(const qlora_nf4_weight* q, uint16_t* W_out, void* stream) {
+  qlora_status st = check_weight(q);
+  if (st != QLORA_OK) return st;
+  if (!W_out) return QLORA_E_NULL;
+  if (!aligned16(W_out)) return QLORA_E_ALIGN;
+  if (q->rows > INT64_MAX / q->cols) return QLORA_E_SHAPE;
+  const int64_t n = q->rows * q->cols;
+  if ((n + 63) / 64 / 256 > 0x7FFFFFFF) return QLORA_E_SHAPE;
+  return hip_status(launch_dequant(q->codes, q->absmax_q, q->group_scale, n, W_out, (hipStream_t)stream));
+}
+
+qlora_status qlora_linear_fwd(const qlora_nf4_weight* W, const uint16_t* X, int64_t M, const uint16_t* A,
+                              const uint16_t* B, int32_t r, float alpha, uint16_t* Y, uint16_t* U_save,
+                              void* ws, size_t ws_bytes, void* stream) {
+  qlora_status st = check_gemm_weight(W);
+  if (st != QLORA_OK) return st;
+  if (M <= 0 || M > 0x7FFFFFFF) return QLORA_E_SHAPE;
+  if (!X || !Y) return QLORA_E_NULL;
+  if (!aligned16(X) || !aligned16(Y) || (U_save && !aligned16(U_save))) return QLORA_E_ALIGN;
+  if ((st = check_rank(r, A, B)) != QLORA_OK) return st;
+  const FwdLayout L = fwd_layout(M, W->rows, W->cols, r);
+  if (ws_bytes < L.total) return QLORA_E_WORKSPACE;
+  if (L.total > 0 && !ws) return QLORA_E_NULL;
+  if (L.total > 0 && !aligned16(ws)) return QLORA_E_ALIGN;
+  hipStream_t s = (hipStream_t)stream;
+  const Nf4View v = view(W);
+  const bf16_t* U = nullptr;
+  float sc = 0.0f;
+  if (r > 0) {
+    sc = (float)((double)alpha / (double)r);  // s = RN32(alpha / r)
+    bf16_t* Ud = U_save ? U_save : reinterpret_cast<bf16_t*>(ws_at(ws, L.u));
+    float* part = reinterpret_cast<float*>(ws_at(ws, L.part));
+    st = hip_status(launch_xat(X, A, M, W->cols, r, part, Ud, nullptr, 1.0f, s));
+    if (st != QLORA_OK) return st;
+    U = Ud;
+  }
+  return hip_status(launch_fwd(v, X, M, U, B, r, sc, Y, s));
+}
+
+qlora_status qlora_linear_bwd(const qlora_nf4_weight* W, const uint16_t* X, const uint16_t* dY, int64_t M,
+                              const uint16_t* A, const uint16_t* B, int32_t r, float alpha,
+                              const uint16_t* U_saved, uint16_t* dX, float* dA, float* dB, void* ws,
+                              size_t ws_bytes, void* stream) {
+  qlora_status st = check_gemm_weight(W);
+  if (st != QLORA_OK) return st;
+  if (M <= 0 || M > 0x7FFFFFFF) return QLORA_E_SHAPE;
+  if (!dY) return QLORA_E_NULL;
+  if (!aligned16(dY) || (dX && !aligned16(dX)) || (U_saved && !aligned16(U_saved))) return QLORA_E_ALIGN;
+  if ((st = check_rank(r, A, B)) != QLORA_OK) return st;
+  if (r > 0) {
+    if (!dA || !dB || !X) return QLORA_E_NULL;
+    if (!aligned16(dA) || !aligned16(dB) || !aligned16(X)) return QLORA_E_ALIGN;
+  } else {
+    if (dA || dB) return QLORA_E_SHAPE;  // no adapter, no adapter gradients
+  }
+  const BwdLayout L = bwd_layout(M, W->rows, W->cols, r);
+  if (ws_bytes < L.total) return QLORA_E_WORKSPACE;
+  if (L.total > 0 && !ws) return QLORA_E_NULL;
+  if (L.total > 0 && !aligned16(ws)) return QLORA_E_ALIGN;
+  hipStream_t s = (hipStream_t)stream;
+  const Nf4View v = view(W);
+  const int64_t N = W->rows, K = W->cols;
+  if (r == 0) {
+    if (!dX) return QLORA_OK;
+    return hip_status(launch_dx(v, dY, M, nullptr, nullptr, 0, 0.0f, dX, s));
+  }
+  const float sc = (float)((double)alpha / (double)r);
+  bf16_t* G = reinterpret_cast<bf16_t*>(ws_at(ws, L.g));
+  float* part = reinterpret_cast<float*>(ws_at(ws, L.part));
+  const bf16_t* U = U_saved;
+  if (!U) {
+    bf16_t* Ud = reinterpret_cast<bf16_t*>(ws_at(ws, L.u));
+    st = hip_status(launch_xat(X, A, M, K, r, part, Ud, nullptr, 1.0f, s));
+    if (st != QLORA_OK) return st;
+    U = Ud;
+  }
+  st = hip_status(launch_dyb(dY, B, M, N, r, part, G, 1.0f, s));
+  if (st != QLORA_OK) return st;
+  if (dX) {
+    st = hip_status(launch_dx(v, dY, M, G, A, r, sc, dX, s));
+    if (st != QLORA_OK) return st;
+  }
+  st = hip_status(launch_gtx(G, X, M, K, r, part, dA, sc, s));
+  if (st != QLORA_OK) return st;
+  return hip_status(launch_dytu(dY, U, M, N, r, part, dB, sc, s));
+}
+
+qlora_status qlora_gemv(const qlora_gemv_job* jobs, int32_t njobs, void* ws, size_t ws_bytes, void* stream) {
+  if (!jobs) return QLORA_E_NULL;
+  if (njobs <= 0) return QLORA_E_SHAPE;
+  if (njobs > kMaxJobs) return QLORA_E_UNSUPPORTED;
+  const size_t need = (size_t)njobs * kMaxRank * sizeof(float);
+  bool any_rank = false;
+  for (int i = 0; i < njobs; ++i) {
+    const qlora_gemv_job& J = jobs[i];
+    qlora_status st = check_weight(J.W);
+    if (st != QLORA_OK) return st;
+    if (J.W->cols % 64 != 0 || J.W->cols > kMaxGemvCols || J.W->rows > 0x7FFFFFFF) return QLORA_E_UNSUPPORTED;
+    if (!J.x || !J.y) return QLORA_E_NULL;
+    if (!aligned16(J.x) || !aligned16(J.y)) return QLORA_E_ALIGN;
+    if ((st = check_rank(J.r, J.A, J.B)) != QLORA_OK) return st;
+    any_rank = any_rank || J.r > 0;
+  }
+  if (any_rank) {
+    if (ws_bytes < need) return QLORA_E_WORKSPACE;
+    if (!ws) return QLORA_E_NULL;
+    if (!aligned16(ws)) return QLORA_E_ALIGN;
+  }
+  // Convert in chunks to keep the host copy small.
+  constexpr int kChunk = 240;
+  GemvJob buf[kChunk];
+  for (int base = 0; base < njobs; base += kChunk) {
+    const int cnt = std::min(kChunk, njobs - base);
+    for (int i = 0; i < cnt; ++i) {
+      const qlora_gemv_job& J = jobs[base + i];
+      GemvJob& D = buf[i];
+      D.codes = J.W->codes;
+      D.absmax_q = J.W->absmax_q;
+      D.group_scale = J.W->group_scale;
+      D.x = J.x;
+      D.A = J.r > 0 ? J.A : nullptr;
+      D.B = J.r > 0 ? J.B : nullptr;
+      D.y = J.y;
+      D.u = J.r > 0 ? reinterpret_cast<float*>(ws_at(ws, (size_t)(base + i) * kMaxRank * sizeof(float))) : nullptr;
+      D.N = (int32_t)J.W->rows;
+      D.K = (int32_t)J.W->cols;
+      D.r = J.r;
+      D.s = J.r > 0 ? (float)((double)J.alpha / (double)J.r) : 0.0f;
+    }
+    qlora_status st = hip_status(launch_gemv(buf, cnt, (hipStream_t)stream));
+    if (st != QLORA_OK) return st;
+  }
+  return QLORA_OK;
+}
+
+}  // extern "C"

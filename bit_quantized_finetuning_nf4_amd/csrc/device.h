@@ -1,0 +1,165 @@
+// device.h -- gfx950 device helpers shared by the libqlora kernels:
+// vector types, the NF4 / Q8 codebooks, the byte-permute NF4 decoder,
+// LDS tile addressing and the bf16 MFMA wrapper.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qlora {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+typedef uint16_t bf16_t;  // bf16 bit pattern in global memory
+
+constexpr int kBlock = 64;         // weights per absmax block
+constexpr int kGroupBlocks = 256;  // blocks per second-level group
+
+// NF4 levels as fp32 bit patterns, ascending.  Construction (deepfa.ir blog,
+// "1. 4-bit NormalFloat (NF4)": normal quantiles, equal mass per bucket,
+// normalised to [-1, 1], exact zero): with delta = 929/960, 8 positive
+// levels Phi^-1(delta + (1/2 - delta) j/8), j = 0..7, 7 negative levels
+// -Phi^-1(delta + (1/2 - delta) j/7), j = 0..6, and 0, all divided by
+// Phi^-1(delta) and rounded to fp32.
+__constant__ constexpr uint32_t kNf4LevelBits[16] = {
+    0xBF800000u, 0xBF3239B1u, 0xBF066B2Eu, 0xBECA329Eu, 0xBE91A24Bu, 0xBE3D353Du,
+    0xBDBA7869u, 0x00000000u, 0x3DA2FB01u, 0x3E24CADFu, 0x3E7C04DAu, 0x3EAD0336u,
+    0x3EE1A4B5u, 0x3F1007A9u, 0x3F3913B0u, 0x3F800000u};
+
+// Encoder thresholds: T_k is the exact midpoint of levels k and k+1 rounded
+// toward -inf to fp32.  For any fp32 x, #{k : x > T_k} is the index of the
+// nearest level with ties going to the lower index.
+__constant__ constexpr uint32_t kNf4ThreshBits[15] = {
+    0xBF591CD9u, 0xBF1C5270u, 0xBEEB847Du, 0xBEADEA75u, 0xBE703CEAu,
+    0xBE0D38B9u, 0xBD3A7869u, 0x3D22FB01u, 0x3DF6485Fu, 0x3E5067DCu,
+    0x3E9582D1u, 0x3EC753F5u, 0x3F006D01u, 0x3F248DACu, 0x3F5C89D8u};
+
+__device__ __forceinline__ float u2f(uint32_t u) { return __builtin_bit_cast(float, u); }
+__device__ __forceinline__ uint32_t f2u(float f) { return __builtin_bit_cast(uint32_t, f); }
+
+// Second-level code value Q8[q] = RN32(q / 255): the fp64 quotient is
+// correctly rounded and 53 >= 2*24 + 2 bits, so rounding it again to fp32
+// gives the correctly rounded fp32 quotient.
+__device__ __forceinline__ float q8_value(uint32_t q) {
+  return (float)((double)q / 255.0);
+}
+
+// bf16 bit pattern -> fp32 (exact)
+__device__ __forceinline__ float bf2f(uint32_t b) { return u2f(b << 16); }
+
+// Two fp32 -> packed bf16 pair {lo, hi}, round to nearest even
+// (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  __bf16 a = (__bf16)lo;
+  __bf16 b = (__bf16)hi;
+  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+__device__ __forceinline__ uint32_t perm(uint32_t s0, uint32_t s1, uint32_t sel) {
+  return __builtin_amdgcn_perm(s0, s1, sel);
+}
+
+// ---------------------------------------------------------------------------
+// Byte-permute NF4 decoder.
+//
+// A per-block table of the 16 dequantized bf16 values v[c] = RNE_bf16(RN32(
+// L[c] * t)) is kept as two byte planes of four dwords each: lo[j] holds the
+// low bytes of v[4j..4j+3], hi[j] the high bytes.  v_perm_b32 selects bytes
+// from a 64-bit pair with selectors 0..7 and returns 0xFF for selectors >= 13,
+// so a 16-entry byte lookup is two perms ANDed: entries 0..7 use selector
+// sa = c + (c & 8) (c for c < 8, >= 16 otherwise) and entries 8..15 use
+// sb = sa ^ 0x10 (c - 8 for c >= 8, >= 16 otherwise).
+// ---------------------------------------------------------------------------
+struct Nf4Table {
+  uint32_t lo[4];
+  uint32_t hi[4];
+};
+
+__device__ __forceinline__ Nf4Table make_table(float t) {
+  uint32_t p[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    p[i] = pack_bf16x2(u2f(kNf4LevelBits[2 * i]) * t, u2f(kNf4LevelBits[2 * i + 1]) * t);
+  Nf4Table T;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    T.lo[j] = perm(p[2 * j + 1], p[2 * j], 0x06040200u);
+    T.hi[j] = perm(p[2 * j + 1], p[2 * j], 0x07050301u);
+  }
+  return T;
+}
+
+// Four lookups: idx holds four codes (0..15), one per byte.
+__device__ __forceinline__ void lookup4(uint32_t idx, const Nf4Table& T, uint32_t& lo, uint32_t& hi) {
+  const uint32_t sa = idx + (idx & 0x08080808u);
+  const uint32_t sb = sa ^ 0x10101010u;
+  lo = perm(T.lo[1], T.lo[0], sa) & perm(T.lo[3], T.lo[2], sb);
+  hi = perm(T.hi[1], T.hi[0], sa) & perm(T.hi[3], T.hi[2], sb);
+}
+
+// Eight codes (one packed dword, element i in nibble i) -> eight bf16 in
+// natural order: out[d] = {v[c_2d], v[c_2d+1]}.
+__device__ __forceinline__ void dequant8(uint32_t c, const Nf4Table& T, uint32_t out[4]) {
+  const uint32_t e = c & 0x0F0F0F0Fu;           // elements 0,2,4,6
+  const uint32_t o = (c >> 4) & 0x0F0F0F0Fu;    // elements 1,3,5,7
+  uint32_t le, he, lo, ho;
+  lookup4(e, T, le, he);
+  lookup4(o, T, lo, ho);
+  const uint32_t l01 = perm(lo, le, 0x05010400u);   // lo bytes of elements 0..3
+  const uint32_t h01 = perm(ho, he, 0x05010400u);
+  const uint32_t l23 = perm(lo, le, 0x07030602u);   // lo bytes of elements 4..7
+  const uint32_t h23 = perm(ho, he, 0x07030602u);
+  out[0] = perm(h01, l01, 0x05010400u);
+  out[1] = perm(h01, l01, 0x07030602u);
+  out[2] = perm(h23, l23, 0x05010400u);
+  out[3] = perm(h23, l23, 0x07030602u);
+}
+
+// Four consecutive codes (nibbles 0..3 of the low half, or 4..7 of the high
+// half of c) spread into one byte each.
+__device__ __forceinline__ uint32_t spread4(uint32_t c, bool high_half) {
+  const uint32_t t = perm(0u, c, high_half ? 0x0C030C02u : 0x0C010C00u);
+  return ((t << 4) | t) & 0x0F0F0F0Fu;
+}
+
+// Two rows of eight codes each (same columns) -> eight dwords, one per
+// column k: out[k] = {v0[c0_k], v1[c1_k]}  (row pair packed along k-major).
+__device__ __forceinline__ void dequant8x2_pairs(uint32_t c0, uint32_t c1, const Nf4Table& T0,
+                                                 const Nf4Table& T1, uint32_t out[8]) {
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    uint32_t l0, h0, l1, h1;
+    lookup4(spread4(c0, half), T0, l0, h0);
+    lookup4(spread4(c1, half), T1, l1, h1);
+    const uint32_t P = perm(l1, l0, 0x05010400u);
+    const uint32_t Q = perm(h1, h0, 0x05010400u);
+    const uint32_t P2 = perm(l1, l0, 0x07030602u);
+    const uint32_t Q2 = perm(h1, h0, 0x07030602u);
+    out[4 * half + 0] = perm(Q, P, 0x05010400u);
+    out[4 * half + 1] = perm(Q, P, 0x07030602u);
+    out[4 * half + 2] = perm(Q2, P2, 0x05010400u);
+    out[4 * half + 3] = perm(Q2, P2, 0x07030602u);
+  }
+}
+
+// Block scale t = RN32(Q8[q] * s2).
+__device__ __forceinline__ float block_scale(uint32_t q, float s2) { return q8_value(q) * s2; }
+
+// ---------------------------------------------------------------------------
+// LDS tiles: rows of 64 bf16 (128 B = 8 chunks of 16 B); chunk c of row r is
+// stored at chunk position c ^ swz(r), swz(r) = (r ^ r>>3 ^ r>>6) & 7.
+// Eight consecutive rows reading one logical chunk (MFMA operand reads) and
+// rows 8 or 32 apart writing one column (transposing producers) both land
+// on eight different 16-byte bank groups.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int lds_swz(int row) { return (row ^ (row >> 3) ^ (row >> 6)) & 7; }
+__device__ __forceinline__ int lds_chunk_off(int row, int chunk) {  // in bf16 elements
+  return row * 64 + ((chunk ^ lds_swz(row)) << 3);
+}
+
+__device__ __forceinline__ f32x16_t mfma32x32x16(const bf16x8_t& a, const bf16x8_t& b, const f32x16_t& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+}  // namespace qlora

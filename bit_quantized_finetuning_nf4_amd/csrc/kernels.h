@@ -1,0 +1,62 @@
+// kernels.h -- launch helpers implemented by the .hip files (internal).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qlora {
+
+typedef uint16_t bf16_t;
+
+struct Nf4View {
+  const uint8_t* codes;
+  const uint8_t* absmax_q;
+  const float* group_scale;
+  int64_t N;  // rows
+  int64_t K;  // cols, K % 64 == 0 on the GEMM/GEMV paths
+};
+
+hipError_t launch_quantize(const bf16_t* W, int64_t numel, uint8_t* codes, uint8_t* absmax_q,
+                           float* group_scale, hipStream_t s);
+hipError_t launch_dequant(const uint8_t* codes, const uint8_t* absmax_q, const float* group_scale,
+                          int64_t numel, bf16_t* out, hipStream_t s);
+
+// Y = X deq(W)^T + s * U * B^T  (U already holds X A^T in bf16; r may be 0)
+hipError_t launch_fwd(const Nf4View& W, const bf16_t* X, int64_t M, const bf16_t* U, const bf16_t* B,
+                      int r, float s, bf16_t* Y, hipStream_t st);
+
+// dX = dY deq(W) + s * G * A  (G = dY B in bf16; r may be 0)
+hipError_t launch_dx(const Nf4View& W, const bf16_t* dY, int64_t M, const bf16_t* G, const bf16_t* A,
+                     int r, float s, bf16_t* dX, hipStream_t st);
+
+// Skinny products with a deterministic split-contraction reduction.
+// out_bf16 / out_f32 (either may be null) receive scale * result.
+size_t skinny_partial_bytes(int64_t rows, int64_t cols, int64_t contraction, int kind);
+enum SkinnyKind { kXAt = 0, kDyB = 1, kGtX = 2, kDytU = 3 };
+hipError_t launch_xat(const bf16_t* X, const bf16_t* A, int64_t M, int64_t K, int r, float* part,
+                      bf16_t* out, bf16_t* out2, float scale, hipStream_t st);
+hipError_t launch_dyb(const bf16_t* dY, const bf16_t* B, int64_t M, int64_t N, int r, float* part,
+                      bf16_t* out, float scale, hipStream_t st);
+hipError_t launch_gtx(const bf16_t* G, const bf16_t* X, int64_t M, int64_t K, int r, float* part,
+                      float* dA, float scale, hipStream_t st);
+hipError_t launch_dytu(const bf16_t* dY, const bf16_t* U, int64_t M, int64_t N, int r, float* part,
+                       float* dB, float scale, hipStream_t st);
+
+// Batch-1 decode.
+struct GemvJob {
+  const uint8_t* codes;
+  const uint8_t* absmax_q;
+  const float* group_scale;
+  const bf16_t* x;
+  const bf16_t* A;
+  const bf16_t* B;
+  bf16_t* y;
+  float* u;  // r fp32 scratch (A x)
+  int32_t N;
+  int32_t K;
+  int32_t r;
+  float s;
+};
+hipError_t launch_gemv(const GemvJob* jobs, int njobs, hipStream_t st);
+
+}  // namespace qlora

@@ -1,0 +1,193 @@
+"""Python binding of libqlora: argument marshalling only.
+
+PyTorch provides device memory and the current HIP stream; every step of the
+computation runs in the library's HIP kernels.  All tensors must be on the
+GPU; there is no CPU path.
+"""
+
+import ctypes
+from dataclasses import dataclass
+from typing import Optional, Sequence
+
+import torch
+
+from . import _lib
+from ._lib import GemvJobDesc, Nf4WeightDesc, check, lib
+
+BLOCKSIZE = 64
+GROUP_BLOCKS = 256
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _need(t, dtype, name, shape=None):
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor (no CPU path)")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t
+
+
+def sizes(rows, cols):
+    """(codes bytes, absmax_q bytes, group_scale bytes) of a rows x cols weight."""
+    c, a, s = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    check(lib().qlora_sizes(rows, cols, BLOCKSIZE, GROUP_BLOCKS, ctypes.byref(c), ctypes.byref(a),
+                            ctypes.byref(s)), "qlora_sizes")
+    return c.value, a.value, s.value
+
+
+def nf4_levels():
+    buf = (ctypes.c_float * 16)()
+    lib().qlora_nf4_levels(buf)
+    return torch.tensor(list(buf), dtype=torch.float32)
+
+
+def workspace_bytes(op, M=0, N=0, K=0, r=0, njobs=0):
+    return int(lib().qlora_workspace_bytes(op, M, N, K, r, njobs))
+
+
+def workspace(nbytes, device):
+    """A workspace tensor (uint8) of at least nbytes, or None when 0."""
+    if nbytes == 0:
+        return None
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+@dataclass
+class QuantizedWeight:
+    """An NF4 + double-quantized weight [rows x cols] held in torch tensors."""
+    rows: int
+    cols: int
+    codes: torch.Tensor        # uint8 [ceil(rows*cols/2)]
+    absmax_q: torch.Tensor     # uint8 [nb]
+    group_scale: torch.Tensor  # float32 [ng]
+
+    def desc(self) -> Nf4WeightDesc:
+        return Nf4WeightDesc(self.rows, self.cols, BLOCKSIZE, GROUP_BLOCKS, self.codes.data_ptr(),
+                             self.absmax_q.data_ptr(), self.group_scale.data_ptr())
+
+    @staticmethod
+    def empty(rows, cols, device):
+        c, a, s = sizes(rows, cols)
+        return QuantizedWeight(rows, cols,
+                               torch.empty(c, dtype=torch.uint8, device=device),
+                               torch.empty(a, dtype=torch.uint8, device=device),
+                               torch.empty(s // 4, dtype=torch.float32, device=device))
+
+    def nbytes(self):
+        return self.codes.numel() + self.absmax_q.numel() + 4 * self.group_scale.numel()
+
+
+def quantize(W: torch.Tensor, out: Optional[QuantizedWeight] = None) -> QuantizedWeight:
+    """bf16 W [rows x cols] -> NF4 codes + 8-bit absmax codes + fp32 group scales."""
+    _need(W, torch.bfloat16, "W")
+    rows, cols = (W.shape[0], W.shape[1]) if W.dim() == 2 else (1, W.numel())
+    q = out if out is not None else QuantizedWeight.empty(rows, cols, W.device)
+    d = q.desc()
+    check(lib().qlora_quantize(_ptr(W), ctypes.byref(d), _stream()), "qlora_quantize")
+    return q
+
+
+def dequant(q: QuantizedWeight, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """NF4 weight -> bf16 [rows x cols]."""
+    if out is None:
+        out = torch.empty(q.rows, q.cols, dtype=torch.bfloat16, device=q.codes.device)
+    _need(out, torch.bfloat16, "out")
+    d = q.desc()
+    check(lib().qlora_dequant(ctypes.byref(d), _ptr(out), _stream()), "qlora_dequant")
+    return out
+
+
+def linear_fwd(q: QuantizedWeight, X: torch.Tensor, A=None, B=None, alpha: float = 0.0,
+               save_u: bool = False, out=None, u_out=None, ws=None):
+    """Y = X deq(W)^T + (alpha/r) (X A^T) B^T.  Returns Y, or (Y, U) with save_u."""
+    _need(X, torch.bfloat16, "X")
+    M = X.shape[0]
+    r = 0 if A is None else A.shape[0]
+    if r:
+        _need(A, torch.bfloat16, "A", (r, q.cols))
+        _need(B, torch.bfloat16, "B", (q.rows, r))
+    Y = out if out is not None else torch.empty(M, q.rows, dtype=torch.bfloat16, device=X.device)
+    U = None
+    if save_u and r:
+        U = u_out if u_out is not None else torch.empty(M, r, dtype=torch.bfloat16, device=X.device)
+    nbytes = workspace_bytes(_lib.QLORA_OP_FWD, M, q.rows, q.cols, r)
+    if ws is None:
+        ws = workspace(nbytes, X.device)
+    d = q.desc()
+    check(lib().qlora_linear_fwd(ctypes.byref(d), _ptr(X), M, _ptr(A), _ptr(B), r, float(alpha), _ptr(Y),
+                                 _ptr(U), _ptr(ws), 0 if ws is None else ws.numel(), _stream()),
+          "qlora_linear_fwd")
+    return (Y, U) if save_u else Y
+
+
+def linear_bwd(q: QuantizedWeight, X: torch.Tensor, dY: torch.Tensor, A=None, B=None, alpha: float = 0.0,
+               U: Optional[torch.Tensor] = None, need_dx: bool = True, dX=None, dA=None, dB=None, ws=None):
+    """Returns (dX, dA, dB): dX bf16 [M x K] (or None), dA [r x K] and dB [N x r] fp32 (or None)."""
+    _need(dY, torch.bfloat16, "dY")
+    M = dY.shape[0]
+    r = 0 if A is None else A.shape[0]
+    if r:
+        _need(X, torch.bfloat16, "X", (M, q.cols))
+        _need(A, torch.bfloat16, "A", (r, q.cols))
+        _need(B, torch.bfloat16, "B", (q.rows, r))
+        dA = dA if dA is not None else torch.empty(r, q.cols, dtype=torch.float32, device=dY.device)
+        dB = dB if dB is not None else torch.empty(q.rows, r, dtype=torch.float32, device=dY.device)
+    else:
+        dA = dB = None
+    if need_dx:
+        dX = dX if dX is not None else torch.empty(M, q.cols, dtype=torch.bfloat16, device=dY.device)
+    else:
+        dX = None
+    nbytes = workspace_bytes(_lib.QLORA_OP_BWD, M, q.rows, q.cols, r)
+    if ws is None:
+        ws = workspace(nbytes, dY.device)
+    d = q.desc()
+    check(lib().qlora_linear_bwd(ctypes.byref(d), _ptr(X), _ptr(dY), M, _ptr(A), _ptr(B), r, float(alpha),
+                                 _ptr(U), _ptr(dX), _ptr(dA), _ptr(dB), _ptr(ws),
+                                 0 if ws is None else ws.numel(), _stream()),
+          "qlora_linear_bwd")
+    return dX, dA, dB
+
+
+@dataclass
+class GemvJob:
+    q: QuantizedWeight
+    x: torch.Tensor
+    A: Optional[torch.Tensor] = None
+    B: Optional[torch.Tensor] = None
+    alpha: float = 0.0
+    y: Optional[torch.Tensor] = None
+
+
+def gemv(jobs: Sequence[GemvJob], ws=None):
+    """Batch-1 decode for independent linears; returns the list of y tensors."""
+    n = len(jobs)
+    descs = (Nf4WeightDesc * n)()
+    arr = (GemvJobDesc * n)()
+    outs = []
+    for i, j in enumerate(jobs):
+        _need(j.x, torch.bfloat16, "x", (j.q.cols,))
+        r = 0 if j.A is None else j.A.shape[0]
+        y = j.y if j.y is not None else torch.empty(j.q.rows, dtype=torch.bfloat16, device=j.x.device)
+        outs.append(y)
+        descs[i] = j.q.desc()
+        arr[i] = GemvJobDesc(ctypes.pointer(descs[i]), j.x.data_ptr(), None if r == 0 else j.A.data_ptr(),
+                             None if r == 0 else j.B.data_ptr(), r, float(j.alpha), y.data_ptr())
+    nbytes = workspace_bytes(_lib.QLORA_OP_GEMV, njobs=n)
+    if ws is None:
+        ws = workspace(nbytes, jobs[0].x.device)
+    check(lib().qlora_gemv(arr, n, _ptr(ws), 0 if ws is None else ws.numel(), _stream()), "qlora_gemv")
+    return outs

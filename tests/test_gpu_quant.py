@@ -1,0 +1,104 @@
+"""GPU parity of qlora_quantize / qlora_dequant against the oracle.
+
+Bit-exact: NF4 codes (packed bytes), 8-bit absmax codes, fp32 group scales
+and the dequantized bf16 weights, on seeded inputs spanning many groups, a
+ragged block and group, odd element counts, zero blocks and zero groups,
+outlier-heavy blocks, tiny and denormal magnitudes.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from bit_quantized_finetuning_nf4_amd import ops, synth
+from tests.helpers import bits_to_torch, torch_to_bits
+
+pytestmark = pytest.mark.gpu
+
+
+def _gpu_quantize(bits, shape):
+    W = bits_to_torch(bits.reshape(shape))
+    q = ops.quantize(W)
+    deq = ops.dequant(q)
+    torch.cuda.synchronize()
+    return (q.codes.cpu().numpy(), q.absmax_q.cpu().numpy(), q.group_scale.cpu().numpy(),
+            torch_to_bits(deq).ravel())
+
+
+def _check(bits, shape, label):
+    print(f"[quant parity] {label} shape={shape}", flush=True)
+    codes, aq, s2, deq = _gpu_quantize(bits, shape)
+    rc, raq, rs2 = oracle.quantize(bits)
+    rdeq = oracle.dequant(rc, raq, rs2, bits.size)
+    assert np.array_equal(codes, rc), f"{label}: NF4 codes differ at {np.flatnonzero(codes != rc)[:8]}"
+    assert np.array_equal(aq, raq), f"{label}: absmax codes differ at {np.flatnonzero(aq != raq)[:8]}"
+    assert np.array_equal(s2.view(np.uint32), rs2.view(np.uint32)), f"{label}: group scales differ"
+    assert np.array_equal(deq, rdeq), f"{label}: dequantized bf16 differ at {np.flatnonzero(deq != rdeq)[:8]}"
+
+
+def test_nf4_levels_bitwise():
+    assert np.array_equal(ops.nf4_levels().numpy().view(np.uint32), oracle.nf4_levels().view(np.uint32))
+
+
+def test_quantize_small_config():
+    d = synth.small_numpy(0)
+    _check(d["W"].ravel(), (1024, 1024), "1024x1024 N(0,0.02)")
+
+
+@pytest.mark.parametrize("rows,cols", [(1, 1), (1, 63), (1, 65), (3, 7), (257, 64), (129, 130),
+                                       (5, 64 * 257 + 37 - (64 * 257 + 37) % 5)])
+def test_quantize_ragged(rows, cols):
+    rng = np.random.default_rng(rows * 1000 + cols)
+    bits = synth.to_bf16_bits(rng.standard_normal(rows * cols) * 0.02)
+    _check(bits, (rows, cols), "ragged")
+
+
+def test_quantize_special_values():
+    rng = np.random.default_rng(7)
+    n = 64 * 256 * 3 + 64 * 5
+    w = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    w[: 64 * 256] = 0.0                                   # an all-zero group
+    w[64 * 256: 64 * 256 + 64] = 0.0                      # an all-zero block in a live group
+    blk = slice(64 * 300, 64 * 301)
+    w[blk] = np.where(rng.random(64) < 0.5, 1.0, -1.0) * 0.03   # only +-a in a block
+    w[64 * 302] = 0.5                                     # huge outlier: its block has a tiny x for the rest
+    w[64 * 400: 64 * 401] = rng.standard_normal(64) * 1e-38    # fp32-denormal-range magnitudes
+    w[64 * 401: 64 * 402] = rng.standard_normal(64) * 3e-40
+    w[64 * 402: 64 * 403] = -0.0
+    outl = rng.random(n) < 0.001
+    w[outl] *= 8
+    _check(synth.to_bf16_bits(w), (n // 64, 64), "special values")
+
+
+def test_quantize_outlier_config_shape():
+    # the 65B-shaped layer's distribution (0.1 % outliers x 8) on a smaller tensor
+    W = synth.normal_bf16((2048, 4096), 0.02, 11, "cuda", outliers=0.001)
+    bits = torch_to_bits(W).ravel()
+    _check(bits, (2048, 4096), "outliers")
+
+
+def test_quantize_deterministic_and_bounded():
+    # guard bands around every output stay untouched; two runs are identical
+    rows, cols = 300, 1000
+    n = rows * cols
+    W = synth.normal_bf16((rows, cols), 0.02, 3, "cuda")
+    c_b, a_b, s_b = ops.sizes(rows, cols)
+    pad = 256
+    codes = torch.full((c_b + 2 * pad,), 0xA5, dtype=torch.uint8, device="cuda")
+    aq = torch.full((a_b + 2 * pad,), 0x5A, dtype=torch.uint8, device="cuda")
+    gs = torch.full((s_b // 4 + 2 * pad,), -7.0, dtype=torch.float32, device="cuda")
+    q = ops.QuantizedWeight(rows, cols, codes[pad:pad + c_b], aq[pad:pad + a_b], gs[pad:pad + s_b // 4])
+    ops.quantize(W, out=q)
+    first = (q.codes.clone(), q.absmax_q.clone(), q.group_scale.clone())
+    ops.quantize(W, out=q)
+    buf = torch.full((n + 256,), 0x7BCD, dtype=torch.int16, device="cuda")
+    deq = buf[128:128 + n].view(torch.bfloat16).view(rows, cols)
+    ops.dequant(q, out=deq)
+    torch.cuda.synchronize()
+    assert torch.equal(first[0], q.codes) and torch.equal(first[1], q.absmax_q)
+    assert torch.equal(first[2].view(torch.int32), q.group_scale.view(torch.int32))
+    for b, fill in ((codes, 0xA5), (aq, 0x5A)):
+        assert torch.all(b[:pad] == fill) and torch.all(b[-pad:] == fill)
+    assert torch.all(gs[:pad] == -7.0) and torch.all(gs[-pad:] == -7.0)
+    assert torch.all(buf[:128] == 0x7BCD) and torch.all(buf[128 + n:] == 0x7BCD)
