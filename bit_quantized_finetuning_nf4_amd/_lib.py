@@ -11,7 +11,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libqlora.so")
 
 QLORA_OK = 0
-QLORA_OP_FWD, QLORA_OP_BWD, QLORA_OP_GEMV = 0, 1, 2
+QLORA_OP_FWD, QLORA_OP_BWD, QLORA_OP_GEMV, QLORA_OP_LORA = 0, 1, 2, 3
 
 STATUS_NAMES = {
     0: "QLORA_OK", 1: "QLORA_E_NULL", 2: "QLORA_E_ALIGN", 3: "QLORA_E_SHAPE",
@@ -23,6 +23,7 @@ EXPORTS = [
     "qlora_status_str", "qlora_last_hip_error", "qlora_version", "qlora_nf4_levels",
     "qlora_sizes", "qlora_workspace_bytes", "qlora_quantize", "qlora_dequant",
     "qlora_linear_fwd", "qlora_linear_bwd", "qlora_gemv",
+    "qlora_lora_down", "qlora_lora_dy_b", "qlora_lora_grads", "qlora_nf4_fwd", "qlora_nf4_dx",
 ]
 
 
@@ -99,6 +100,16 @@ def lib():
     L.qlora_linear_bwd.argtypes = [W, vp, vp, i64, vp, vp, i32, f32, vp, vp, vp, vp, vp, sz, vp]
     L.qlora_gemv.restype = ctypes.c_int
     L.qlora_gemv.argtypes = [ctypes.POINTER(GemvJobDesc), i32, vp, sz, vp]
+    L.qlora_lora_down.restype = ctypes.c_int
+    L.qlora_lora_down.argtypes = [vp, vp, i64, i64, i32, vp, vp, sz, vp]
+    L.qlora_lora_dy_b.restype = ctypes.c_int
+    L.qlora_lora_dy_b.argtypes = [vp, vp, i64, i64, i32, vp, vp, sz, vp]
+    L.qlora_lora_grads.restype = ctypes.c_int
+    L.qlora_lora_grads.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, f32, vp, vp, vp, sz, vp]
+    L.qlora_nf4_fwd.restype = ctypes.c_int
+    L.qlora_nf4_fwd.argtypes = [W, vp, i64, vp, vp, i32, f32, vp, vp]
+    L.qlora_nf4_dx.restype = ctypes.c_int
+    L.qlora_nf4_dx.argtypes = [W, vp, i64, vp, vp, i32, f32, vp, vp]
     _lib = L
     return L
 

@@ -81,6 +81,8 @@ FwdLayout fwd_layout(int64_t M, int64_t N, int64_t K, int32_t r) {
   return L;
 }
 
+size_t lora_part_bytes(int64_t M, int64_t N, int64_t K, int32_t r);
+
 struct BwdLayout {
   size_t g, u, part, total;
 };
@@ -91,15 +93,31 @@ BwdLayout bwd_layout(int64_t M, int64_t N, int64_t K, int32_t r) {
   L.g = 0;
   L.u = mr;
   L.part = 2 * mr;
-  size_t p = skinny_partial_bytes(M, r, K, kXAt);
-  p = std::max(p, skinny_partial_bytes(M, r, N, kDyB));
-  p = std::max(p, skinny_partial_bytes(r, K, M, kGtX));
-  p = std::max(p, skinny_partial_bytes(N, r, M, kDytU));
-  L.total = L.part + align_up(p);
+  L.total = L.part + lora_part_bytes(M, N, K, r);
   return L;
 }
 
 char* ws_at(void* ws, size_t off) { return static_cast<char*>(ws) + off; }
+
+size_t lora_part_bytes(int64_t M, int64_t N, int64_t K, int32_t r) {
+  if (r == 0) return 0;
+  size_t p = skinny_partial_bytes(M, r, K, kXAt);
+  p = std::max(p, skinny_partial_bytes(M, r, N, kDyB));
+  p = std::max(p, skinny_partial_bytes(r, K, M, kGtX));
+  p = std::max(p, skinny_partial_bytes(N, r, M, kDytU));
+  return align_up(p);
+}
+
+qlora_status check_ws(void* ws, size_t ws_bytes, size_t need) {
+  if (ws_bytes < need) return QLORA_E_WORKSPACE;
+  if (need > 0 && !ws) return QLORA_E_NULL;
+  if (need > 0 && !aligned16(ws)) return QLORA_E_ALIGN;
+  return QLORA_OK;
+}
+
+qlora_status check_adapter_rank(int32_t r) {
+  return (r <= 0 || r > kMaxRank || r % 8 != 0) ? QLORA_E_UNSUPPORTED : QLORA_OK;
+}
 
 }  // namespace
 
@@ -158,6 +176,9 @@ size_t qlora_workspace_bytes(qlora_op op, int64_t M, int64_t N, int64_t K, int32
     case QLORA_OP_GEMV:
       if (njobs <= 0 || njobs > kMaxJobs) return 0;
       return (size_t)njobs * kMaxRank * sizeof(float);
+    case QLORA_OP_LORA:
+      if (M <= 0 || N <= 0 || K <= 0 || r < 0 || r > kMaxRank) return 0;
+      return lora_part_bytes(M, N, K, r);
   }
   return 0;
 }
@@ -258,6 +279,72 @@ qlora_status qlora_linear_bwd(const qlora_nf4_weight* W, const uint16_t* X, cons
   st = hip_status(launch_gtx(G, X, M, K, r, part, dA, sc, s));
   if (st != QLORA_OK) return st;
   return hip_status(launch_dytu(dY, U, M, N, r, part, dB, sc, s));
+}
+
+qlora_status qlora_lora_down(const uint16_t* X, const uint16_t* A, int64_t M, int64_t K, int32_t r, uint16_t* U,
+                             void* ws, size_t ws_bytes, void* stream) {
+  qlora_status st = check_adapter_rank(r);
+  if (st != QLORA_OK) return st;
+  if (M <= 0 || M > 0x7FFFFFFF || K <= 0 || K % 8 != 0) return QLORA_E_SHAPE;
+  if (!X || !A || !U) return QLORA_E_NULL;
+  if (!aligned16(X) || !aligned16(A) || !aligned16(U)) return QLORA_E_ALIGN;
+  if ((st = check_ws(ws, ws_bytes, align_up(skinny_partial_bytes(M, r, K, kXAt)))) != QLORA_OK) return st;
+  return hip_status(launch_xat(X, A, M, K, r, static_cast<float*>(ws), U, nullptr, 1.0f, (hipStream_t)stream));
+}
+
+qlora_status qlora_lora_dy_b(const uint16_t* dY, const uint16_t* B, int64_t M, int64_t N, int32_t r, uint16_t* G,
+                             void* ws, size_t ws_bytes, void* stream) {
+  qlora_status st = check_adapter_rank(r);
+  if (st != QLORA_OK) return st;
+  if (M <= 0 || M > 0x7FFFFFFF || N <= 0 || N % 8 != 0) return QLORA_E_SHAPE;
+  if (!dY || !B || !G) return QLORA_E_NULL;
+  if (!aligned16(dY) || !aligned16(B) || !aligned16(G)) return QLORA_E_ALIGN;
+  if ((st = check_ws(ws, ws_bytes, align_up(skinny_partial_bytes(M, r, N, kDyB)))) != QLORA_OK) return st;
+  return hip_status(launch_dyb(dY, B, M, N, r, static_cast<float*>(ws), G, 1.0f, (hipStream_t)stream));
+}
+
+qlora_status qlora_lora_grads(const uint16_t* X, const uint16_t* dY, const uint16_t* U, const uint16_t* G,
+                              int64_t M, int64_t N, int64_t K, int32_t r, float alpha, float* dA, float* dB,
+                              void* ws, size_t ws_bytes, void* stream) {
+  qlora_status st = check_adapter_rank(r);
+  if (st != QLORA_OK) return st;
+  if (M <= 0 || M > 0x7FFFFFFF || N <= 0 || N % 8 != 0 || K <= 0 || K % 8 != 0) return QLORA_E_SHAPE;
+  if (!X || !dY || !U || !G || !dA || !dB) return QLORA_E_NULL;
+  if (!aligned16(X) || !aligned16(dY) || !aligned16(U) || !aligned16(G) || !aligned16(dA) || !aligned16(dB))
+    return QLORA_E_ALIGN;
+  const size_t need = align_up(std::max(skinny_partial_bytes(r, K, M, kGtX), skinny_partial_bytes(N, r, M, kDytU)));
+  if ((st = check_ws(ws, ws_bytes, need)) != QLORA_OK) return st;
+  const float sc = (float)((double)alpha / (double)r);
+  hipStream_t s = (hipStream_t)stream;
+  st = hip_status(launch_gtx(G, X, M, K, r, static_cast<float*>(ws), dA, sc, s));
+  if (st != QLORA_OK) return st;
+  return hip_status(launch_dytu(dY, U, M, N, r, static_cast<float*>(ws), dB, sc, s));
+}
+
+qlora_status qlora_nf4_fwd(const qlora_nf4_weight* W, const uint16_t* X, int64_t M, const uint16_t* U,
+                           const uint16_t* B, int32_t r, float alpha, uint16_t* Y, void* stream) {
+  qlora_status st = check_gemm_weight(W);
+  if (st != QLORA_OK) return st;
+  if (M <= 0 || M > 0x7FFFFFFF) return QLORA_E_SHAPE;
+  if (!X || !Y) return QLORA_E_NULL;
+  if (!aligned16(X) || !aligned16(Y)) return QLORA_E_ALIGN;
+  if ((st = check_rank(r, U, B)) != QLORA_OK) return st;
+  const float sc = r > 0 ? (float)((double)alpha / (double)r) : 0.0f;
+  return hip_status(launch_fwd(view(W), X, M, r > 0 ? U : nullptr, r > 0 ? B : nullptr, r, sc, Y,
+                               (hipStream_t)stream));
+}
+
+qlora_status qlora_nf4_dx(const qlora_nf4_weight* W, const uint16_t* dY, int64_t M, const uint16_t* G,
+                          const uint16_t* A, int32_t r, float alpha, uint16_t* dX, void* stream) {
+  qlora_status st = check_gemm_weight(W);
+  if (st != QLORA_OK) return st;
+  if (M <= 0 || M > 0x7FFFFFFF) return QLORA_E_SHAPE;
+  if (!dY || !dX) return QLORA_E_NULL;
+  if (!aligned16(dY) || !aligned16(dX)) return QLORA_E_ALIGN;
+  if ((st = check_rank(r, G, A)) != QLORA_OK) return st;
+  const float sc = r > 0 ? (float)((double)alpha / (double)r) : 0.0f;
+  return hip_status(launch_dx(view(W), dY, M, r > 0 ? G : nullptr, r > 0 ? A : nullptr, r, sc, dX,
+                              (hipStream_t)stream));
 }
 
 qlora_status qlora_gemv(const qlora_gemv_job* jobs, int32_t njobs, void* ws, size_t ws_bytes, void* stream) {

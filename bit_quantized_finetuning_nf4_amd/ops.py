@@ -172,6 +172,37 @@ class GemvJob:
     y: Optional[torch.Tensor] = None
 
 
+class GemvPlan:
+    """Job descriptors built once; calling the plan enqueues one qlora_gemv."""
+
+    def __init__(self, jobs: Sequence[GemvJob], ws=None):
+        n = len(jobs)
+        self._descs = (Nf4WeightDesc * n)()
+        self._arr = (GemvJobDesc * n)()
+        self.outputs = []
+        self._keep = list(jobs)
+        for i, j in enumerate(jobs):
+            _need(j.x, torch.bfloat16, "x", (j.q.cols,))
+            r = 0 if j.A is None else j.A.shape[0]
+            if r:
+                _need(j.A, torch.bfloat16, "A", (r, j.q.cols))
+                _need(j.B, torch.bfloat16, "B", (j.q.rows, r))
+            y = j.y if j.y is not None else torch.empty(j.q.rows, dtype=torch.bfloat16, device=j.x.device)
+            self.outputs.append(y)
+            self._descs[i] = j.q.desc()
+            self._arr[i] = GemvJobDesc(ctypes.pointer(self._descs[i]), j.x.data_ptr(),
+                                       None if r == 0 else j.A.data_ptr(), None if r == 0 else j.B.data_ptr(),
+                                       r, float(j.alpha), y.data_ptr())
+        self.n = n
+        nbytes = workspace_bytes(_lib.QLORA_OP_GEMV, njobs=n)
+        self.ws = ws if ws is not None else workspace(nbytes, jobs[0].x.device)
+
+    def __call__(self):
+        check(lib().qlora_gemv(self._arr, self.n, _ptr(self.ws), 0 if self.ws is None else self.ws.numel(),
+                               _stream()), "qlora_gemv")
+        return self.outputs
+
+
 def gemv(jobs: Sequence[GemvJob], ws=None):
     """Batch-1 decode for independent linears; returns the list of y tensors."""
     n = len(jobs)
@@ -191,3 +222,74 @@ def gemv(jobs: Sequence[GemvJob], ws=None):
         ws = workspace(nbytes, jobs[0].x.device)
     check(lib().qlora_gemv(arr, n, _ptr(ws), 0 if ws is None else ws.numel(), _stream()), "qlora_gemv")
     return outs
+
+
+# ---- building blocks (the two fused GEMMs and the LoRA side products) ----
+
+def lora_down(X, A, U=None, ws=None):
+    """U [M x r] = X A^T (bf16)."""
+    _need(X, torch.bfloat16, "X")
+    M, K = X.shape
+    r = A.shape[0]
+    _need(A, torch.bfloat16, "A", (r, K))
+    U = U if U is not None else torch.empty(M, r, dtype=torch.bfloat16, device=X.device)
+    if ws is None:
+        ws = workspace(workspace_bytes(_lib.QLORA_OP_LORA, M, 8, K, r), X.device)
+    check(lib().qlora_lora_down(_ptr(X), _ptr(A), M, K, r, _ptr(U), _ptr(ws), 0 if ws is None else ws.numel(),
+                                _stream()), "qlora_lora_down")
+    return U
+
+
+def lora_dy_b(dY, B, G=None, ws=None):
+    """G [M x r] = dY B (bf16)."""
+    _need(dY, torch.bfloat16, "dY")
+    M, N = dY.shape
+    r = B.shape[1]
+    _need(B, torch.bfloat16, "B", (N, r))
+    G = G if G is not None else torch.empty(M, r, dtype=torch.bfloat16, device=dY.device)
+    if ws is None:
+        ws = workspace(workspace_bytes(_lib.QLORA_OP_LORA, M, N, 8, r), dY.device)
+    check(lib().qlora_lora_dy_b(_ptr(dY), _ptr(B), M, N, r, _ptr(G), _ptr(ws), 0 if ws is None else ws.numel(),
+                                _stream()), "qlora_lora_dy_b")
+    return G
+
+
+def lora_grads(X, dY, U, G, alpha, dA=None, dB=None, ws=None):
+    """dA [r x K] = s G^T X, dB [N x r] = s dY^T U (fp32)."""
+    M, K = X.shape
+    N = dY.shape[1]
+    r = U.shape[1]
+    for t, n, shp in ((X, "X", (M, K)), (dY, "dY", (M, N)), (U, "U", (M, r)), (G, "G", (M, r))):
+        _need(t, torch.bfloat16, n, shp)
+    dA = dA if dA is not None else torch.empty(r, K, dtype=torch.float32, device=X.device)
+    dB = dB if dB is not None else torch.empty(N, r, dtype=torch.float32, device=X.device)
+    if ws is None:
+        ws = workspace(workspace_bytes(_lib.QLORA_OP_LORA, M, N, K, r), X.device)
+    check(lib().qlora_lora_grads(_ptr(X), _ptr(dY), _ptr(U), _ptr(G), M, N, K, r, float(alpha), _ptr(dA),
+                                 _ptr(dB), _ptr(ws), 0 if ws is None else ws.numel(), _stream()),
+          "qlora_lora_grads")
+    return dA, dB
+
+
+def nf4_fwd(q: QuantizedWeight, X, U=None, B=None, alpha: float = 0.0, out=None):
+    """The fused forward GEMM: Y = X deq(W)^T + s U B^T."""
+    _need(X, torch.bfloat16, "X")
+    M = X.shape[0]
+    r = 0 if U is None else U.shape[1]
+    Y = out if out is not None else torch.empty(M, q.rows, dtype=torch.bfloat16, device=X.device)
+    d = q.desc()
+    check(lib().qlora_nf4_fwd(ctypes.byref(d), _ptr(X), M, _ptr(U), _ptr(B), r, float(alpha), _ptr(Y),
+                              _stream()), "qlora_nf4_fwd")
+    return Y
+
+
+def nf4_dx(q: QuantizedWeight, dY, G=None, A=None, alpha: float = 0.0, out=None):
+    """The fused backward GEMM: dX = dY deq(W) + s G A."""
+    _need(dY, torch.bfloat16, "dY")
+    M = dY.shape[0]
+    r = 0 if G is None else G.shape[1]
+    dX = out if out is not None else torch.empty(M, q.cols, dtype=torch.bfloat16, device=dY.device)
+    d = q.desc()
+    check(lib().qlora_nf4_dx(ctypes.byref(d), _ptr(dY), M, _ptr(G), _ptr(A), r, float(alpha), _ptr(dX),
+                             _stream()), "qlora_nf4_dx")
+    return dX

@@ -65,7 +65,12 @@ typedef enum {
   QLORA_E_HIP = 6          /* a HIP launch/copy error; see qlora_last_hip_error */
 } qlora_status;
 
-typedef enum { QLORA_OP_FWD = 0, QLORA_OP_BWD = 1, QLORA_OP_GEMV = 2 } qlora_op;
+typedef enum {
+  QLORA_OP_FWD = 0,   /* qlora_linear_fwd                                   */
+  QLORA_OP_BWD = 1,   /* qlora_linear_bwd                                   */
+  QLORA_OP_GEMV = 2,  /* qlora_gemv                                         */
+  QLORA_OP_LORA = 3   /* qlora_lora_down, qlora_lora_dy_b, qlora_lora_grads */
+} qlora_op;
 
 /* A quantized weight: host struct holding device pointers.
  * codes: ceil(rows*cols/2) bytes; absmax_q: nb bytes; group_scale: ng fp32,
@@ -114,7 +119,9 @@ qlora_status qlora_sizes(int64_t rows, int64_t cols, int32_t blocksize, int32_t 
 
 /* Bytes of scratch the given call needs (0 when none).  FWD/BWD: M tokens,
  * N = rows, K = cols, LoRA rank r; GEMV: njobs jobs, with N and K the
- * largest rows/cols among them.  Returns 0 for invalid sizes. */
+ * largest rows/cols among them; LORA: the split-contraction partial sums of
+ * the LoRA side products of one M x N x K, rank-r layer.  Returns 0 for
+ * invalid sizes. */
 size_t qlora_workspace_bytes(qlora_op op, int64_t M, int64_t N, int64_t K, int32_t r, int32_t njobs);
 
 /* Quantize bf16 W [rows x cols] into q (codes, absmax_q, group_scale are
@@ -148,6 +155,43 @@ qlora_status qlora_linear_bwd(const qlora_nf4_weight* W, const uint16_t* X, cons
                               int64_t M, const uint16_t* A, const uint16_t* B, int32_t r,
                               float alpha, const uint16_t* U_saved, uint16_t* dX,
                               float* dA, float* dB, void* ws, size_t ws_bytes, void* stream);
+
+/* ---- Building blocks of the forward and backward passes ----------------
+ * qlora_linear_fwd = qlora_lora_down + qlora_nf4_fwd;
+ * qlora_linear_bwd = [qlora_lora_down] + qlora_lora_dy_b + qlora_nf4_dx
+ *                    + qlora_lora_grads.
+ * They let a caller keep U and G, reuse them, or time the two fused NF4
+ * GEMMs on their own.  Same conventions as above; ws is sized by
+ * qlora_workspace_bytes(QLORA_OP_LORA, M, N, K, r, 0). */
+
+/* U [M x r] = X A^T (bf16).  deepfa.ir "LoRA: Prerequisite": the adapter's
+ * down-projection.  r in (0, 128], r % 8 == 0, K % 8 == 0. */
+qlora_status qlora_lora_down(const uint16_t* X, const uint16_t* A, int64_t M, int64_t K, int32_t r,
+                             uint16_t* U, void* ws, size_t ws_bytes, void* stream);
+
+/* G [M x r] = dY B (bf16): the gradient reaching the adapter's
+ * down-projection output.  N % 8 == 0. */
+qlora_status qlora_lora_dy_b(const uint16_t* dY, const uint16_t* B, int64_t M, int64_t N, int32_t r,
+                             uint16_t* G, void* ws, size_t ws_bytes, void* stream);
+
+/* dA [r x K] = s G^T X and dB [N x r] = s dY^T U (fp32, overwritten),
+ * s = RN32(alpha / r).  Glossary "Definition": weight gradients only for
+ * the LoRA matrices. */
+qlora_status qlora_lora_grads(const uint16_t* X, const uint16_t* dY, const uint16_t* U, const uint16_t* G,
+                              int64_t M, int64_t N, int64_t K, int32_t r, float alpha, float* dA, float* dB,
+                              void* ws, size_t ws_bytes, void* stream);
+
+/* The fused forward GEMM: Y = X deq(W)^T + s U B^T, with U = X A^T given
+ * (r == 0: U = B = NULL).  No workspace.  deepfa.ir "QLoRA's Working
+ * Process": dequantization to BF16 on the fly inside the product. */
+qlora_status qlora_nf4_fwd(const qlora_nf4_weight* W, const uint16_t* X, int64_t M, const uint16_t* U,
+                           const uint16_t* B, int32_t r, float alpha, uint16_t* Y, void* stream);
+
+/* The fused backward GEMM: dX = dY deq(W) + s G A, with G = dY B given
+ * (r == 0: G = A = NULL).  No workspace.  insights4ai page: gradients flow
+ * through the frozen 4-bit weights. */
+qlora_status qlora_nf4_dx(const qlora_nf4_weight* W, const uint16_t* dY, int64_t M, const uint16_t* G,
+                          const uint16_t* A, int32_t r, float alpha, uint16_t* dX, void* stream);
 
 /* Batch-1 decode for njobs independent products (host job array, read
  * before return).  Each job needs cols % 64 == 0.  njobs <= 4096.
