@@ -38,22 +38,25 @@ __constant__ constexpr uint32_t kNf4ThreshBits[15] = {
 __device__ __forceinline__ float u2f(uint32_t u) { return __builtin_bit_cast(float, u); }
 __device__ __forceinline__ uint32_t f2u(float f) { return __builtin_bit_cast(uint32_t, f); }
 
-// Second-level code value Q8[q] = RN32(q / 255): the fp64 quotient is
-// correctly rounded and 53 >= 2*24 + 2 bits, so rounding it again to fp32
-// gives the correctly rounded fp32 quotient.
+// Second-level code value Q8[q] = RN32(q / 255).  The fp64 product
+// q * RN64(1/255) is within 2^-52 relative of q / 255, while q / 255 (an
+// 8-bit by 8-bit quotient) is never closer than 2^-33 relative to an fp32
+// rounding boundary, so rounding the product to fp32 gives RN32(q / 255)
+// for every q in 0..255.
 __device__ __forceinline__ float q8_value(uint32_t q) {
-  return (float)((double)q / 255.0);
+  return (float)((double)q * (1.0 / 255.0));
 }
 
 // bf16 bit pattern -> fp32 (exact)
 __device__ __forceinline__ float bf2f(uint32_t b) { return u2f(b << 16); }
 
 // Two fp32 -> packed bf16 pair {lo, hi}, round to nearest even
-// (v_cvt_pk_bf16_f32 on gfx950).
+// (one v_cvt_pk_bf16_f32 on gfx950).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  __bf16 a = (__bf16)lo;
-  __bf16 b = (__bf16)hi;
-  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
 __device__ __forceinline__ uint32_t perm(uint32_t s0, uint32_t s1, uint32_t sel) {
@@ -157,6 +160,10 @@ __device__ __forceinline__ int lds_swz(int row) { return (row ^ (row >> 3) ^ (ro
 __device__ __forceinline__ int lds_chunk_off(int row, int chunk) {  // in bf16 elements
   return row * 64 + ((chunk ^ lds_swz(row)) << 3);
 }
+
+// Scheduling hints: interleave instruction classes inside one basic block.
+enum : int { kSchedValu = 0x002, kSchedMfma = 0x008, kSchedDsRead = 0x100, kSchedDsWrite = 0x200 };
+#define QLORA_SCHED(mask, n) __builtin_amdgcn_sched_group_barrier((mask), (n), 0)
 
 __device__ __forceinline__ f32x16_t mfma32x32x16(const bf16x8_t& a, const bf16x8_t& b, const f32x16_t& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);

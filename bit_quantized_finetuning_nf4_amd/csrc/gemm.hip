@@ -1,8 +1,7 @@
 // gemm.hip -- LDS-tiled bf16 MFMA products of the QLoRA linear layer.
 //
-//   forward   Y  = X deq(W)^T + s (X A^T) B^T       (fused NF4 dequant + LoRA)
-//   backward  dX = dY deq(W) + s (dY B) A            (fused NF4 dequant + LoRA)
-//             dA = s (dY B)^T X,  dB = s dY^T (X A^T)
+//   U = X A^T,  G = dY B,  dA = s (dY B)^T X,  dB = s dY^T (X A^T)
+// (the fused NF4 GEMMs live in gemm_nf4.hip)
 //
 // deepfa.ir blog, "LoRA: Prerequisite" and "QLoRA's Working Process" (the
 // 4-bit weights are dequantized to BF16 on the fly in the forward and
@@ -138,95 +137,6 @@ struct TransTile {
   }
 };
 
-// NF4 weight rows as the tile rows (forward): thread t owns W row n0 + t and
-// dequantizes its whole 64-element block of the step into one LDS row.
-struct Nf4RowTile {
-  const uint8_t* codes;
-  const uint8_t* absmax_q;
-  const float* group_scale;
-  int64_t N, K, n0;
-  uint4 c0, c1;
-  uint32_t q;
-  float s2;
-
-  __device__ __forceinline__ void load(int step) {
-    const int64_t n = n0 + threadIdx.x;
-    if (n < N) {
-      const int64_t b = n * (K >> 6) + step;
-      const uint4* p = reinterpret_cast<const uint4*>(codes + b * 32);
-      c0 = p[0];
-      c1 = p[1];
-      q = absmax_q[b];
-      s2 = group_scale[b >> 8];
-    } else {
-      c0 = c1 = make_uint4(0x77777777u, 0x77777777u, 0x77777777u, 0x77777777u);
-      q = 0;
-      s2 = 0.0f;
-    }
-  }
-  __device__ __forceinline__ void store(bf16_t* lds) const {
-    const int r = threadIdx.x;
-    const Nf4Table T = make_table(block_scale(q, s2));
-    const uint32_t cw[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
-#pragma unroll
-    for (int ch = 0; ch < 8; ++ch) {
-      uint32_t o[4];
-      dequant8(cw[ch], T, o);
-      *reinterpret_cast<uint4*>(lds + lds_chunk_off(r, ch)) = make_uint4(o[0], o[1], o[2], o[3]);
-    }
-  }
-};
-
-// NF4 weight columns as the tile rows (backward dX, contraction over N):
-// tile rows k in [k0, k0 + 256), step covers W rows [64 step, 64 step + 64).
-// Thread (p, kq) dequantizes W rows 2p, 2p+1 x 32 columns and writes 32
-// dwords {deq(W[2p][k]), deq(W[2p+1][k])} into LDS rows k.
-struct Nf4TransTile {
-  const uint8_t* codes;
-  const uint8_t* absmax_q;
-  const float* group_scale;
-  int64_t N, K, k0;
-  uint4 c[2];
-  uint32_t q[2];
-  float s2[2];
-
-  __device__ __forceinline__ void load(int step) {
-    const int lane = threadIdx.x & 63;
-    const int p = 8 * (threadIdx.x >> 6) + (lane & 7), kq = lane >> 3;
-    const int64_t k = k0 + 32 * kq;
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      const int64_t n = (int64_t)step * 64 + 2 * p + r;
-      if (n < N && k < K) {
-        const int64_t b = n * (K >> 6) + (k >> 6);
-        c[r] = *reinterpret_cast<const uint4*>(codes + ((n * K + k) >> 1));
-        q[r] = absmax_q[b];
-        s2[r] = group_scale[b >> 8];
-      } else {
-        c[r] = make_uint4(0x77777777u, 0x77777777u, 0x77777777u, 0x77777777u);
-        q[r] = 0;
-        s2[r] = 0.0f;
-      }
-    }
-  }
-  __device__ __forceinline__ void store(bf16_t* lds) const {
-    const int lane = threadIdx.x & 63;
-    const int p = 8 * (threadIdx.x >> 6) + (lane & 7), kq = lane >> 3;
-    const Nf4Table T0 = make_table(block_scale(q[0], s2[0]));
-    const Nf4Table T1 = make_table(block_scale(q[1], s2[1]));
-    const uint32_t w0[4] = {c[0].x, c[0].y, c[0].z, c[0].w};
-    const uint32_t w1[4] = {c[1].x, c[1].y, c[1].z, c[1].w};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      uint32_t o[8];
-      dequant8x2_pairs(w0[j], w1[j], T0, T1, o);
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        *reinterpret_cast<uint32_t*>(lds + lds_chunk_off(32 * kq + 8 * j + e, p >> 2) + 2 * (p & 3)) = o[e];
-    }
-  }
-};
-
 // ---------------------------------------------------------------------------
 // MFMA core: wave tile of FI x FJ 32x32 sub-tiles; As rows = output columns
 // (starting at ia), Bs rows = output rows (starting at jb).
@@ -310,136 +220,6 @@ __device__ __forceinline__ void map_tile(int tiles_c, int tiles_r, int& tc, int&
   if ((nwg & 7) == 0) id = (id & 7) * (nwg >> 3) + (id >> 3);
   tc = id % tiles_c;
   tr = id / tiles_c;
-}
-
-// ---------------------------------------------------------------------------
-// Fused forward: 256 (tokens) x 256 (outputs) tile, 2x2 waves of 128x128.
-// ---------------------------------------------------------------------------
-constexpr int kBigTile = 256;
-constexpr size_t kBigLds = 4u * kBigTile * 64 * sizeof(bf16_t);  // 2 buffers x (A + B) = 128 KiB
-
-__global__ __launch_bounds__(kThreads, 1) void fwd_kernel(Nf4View W, const bf16_t* __restrict__ X, int64_t M,
-                                                          const bf16_t* __restrict__ U,
-                                                          const bf16_t* __restrict__ Bl, int r, float s,
-                                                          bf16_t* __restrict__ Y, int tiles_n, int tiles_m) {
-  extern __shared__ __align__(16) bf16_t smem[];
-  bf16_t* As0 = smem;
-  bf16_t* As1 = smem + kBigTile * 64;
-  bf16_t* Bs0 = smem + 2 * kBigTile * 64;
-  bf16_t* Bs1 = smem + 3 * kBigTile * 64;
-  int tn, tm;
-  map_tile(tiles_n, tiles_m, tn, tm);
-  const int64_t n0 = (int64_t)tn * kBigTile, m0 = (int64_t)tm * kBigTile;
-  const int w = threadIdx.x >> 6, wr = w >> 1, wc = w & 1;
-
-  f32x16_t acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
-
-  Nf4RowTile wl{W.codes, W.absmax_q, W.group_scale, W.N, W.K, n0};
-  RowTile<kBigTile> xl(TileDesc{X, W.K, M, W.K}, m0);
-  const int nsteps = (int)(W.K >> 6);
-  wl.load(0);
-  xl.load(0);
-  wl.store(As0);
-  xl.store(Bs0);
-  __syncthreads();
-  for (int st = 0; st < nsteps; ++st) {
-    const bool odd = st & 1;
-    if (st + 1 < nsteps) {
-      wl.load(st + 1);
-      xl.load(st + 1);
-    }
-    mma_step<4, 4>(acc, odd ? As1 : As0, odd ? Bs1 : Bs0, wc * 128, wr * 128);
-    if (st + 1 < nsteps) {
-      wl.store(odd ? As0 : As1);
-      xl.store(odd ? Bs0 : Bs1);
-    }
-    __syncthreads();
-  }
-  if (r > 0) {
-    // LoRA up-projection as extra contraction steps over the rank:
-    // acc += (s U) B^T with U = X A^T
-    RowTile<kBigTile> bl(TileDesc{Bl, r, W.N, r}, n0);
-    RowTile<kBigTile> ul(TileDesc{U, r, M, r}, m0);
-    for (int st = 0; st * 64 < r; ++st) {
-      bl.load(st);
-      ul.load(st);
-      bl.store(As0);
-      ul.store_scaled(Bs0, s);
-      __syncthreads();
-      mma_step<4, 4>(acc, As0, Bs0, wc * 128, wr * 128);
-      __syncthreads();
-    }
-  }
-  epilogue<4, 4>(acc, n0 + wc * 128, m0 + wr * 128, StoreBf16{Y, W.N, M, W.N});
-}
-
-// ---------------------------------------------------------------------------
-// Fused backward dX: 256 (tokens) x 256 (inputs k) tile, contraction over N.
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kThreads, 1) void dx_kernel(Nf4View W, const bf16_t* __restrict__ dY, int64_t M,
-                                                         const bf16_t* __restrict__ G,
-                                                         const bf16_t* __restrict__ Al, int r, float s,
-                                                         bf16_t* __restrict__ dX, int tiles_k, int tiles_m) {
-  extern __shared__ __align__(16) bf16_t smem[];
-  bf16_t* As0 = smem;
-  bf16_t* As1 = smem + kBigTile * 64;
-  bf16_t* Bs0 = smem + 2 * kBigTile * 64;
-  bf16_t* Bs1 = smem + 3 * kBigTile * 64;
-  int tk, tm;
-  map_tile(tiles_k, tiles_m, tk, tm);
-  const int64_t k0 = (int64_t)tk * kBigTile, m0 = (int64_t)tm * kBigTile;
-  const int w = threadIdx.x >> 6, wr = w >> 1, wc = w & 1;
-
-  f32x16_t acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
-
-  Nf4TransTile wl{W.codes, W.absmax_q, W.group_scale, W.N, W.K, k0};
-  RowTile<kBigTile> yl(TileDesc{dY, W.N, M, W.N}, m0);
-  const int nsteps = (int)((W.N + 63) >> 6);
-  wl.load(0);
-  yl.load(0);
-  wl.store(As0);
-  yl.store(Bs0);
-  __syncthreads();
-  for (int st = 0; st < nsteps; ++st) {
-    const bool odd = st & 1;
-    if (st + 1 < nsteps) {
-      wl.load(st + 1);
-      yl.load(st + 1);
-    }
-    mma_step<4, 4>(acc, odd ? As1 : As0, odd ? Bs1 : Bs0, wc * 128, wr * 128);
-    if (st + 1 < nsteps) {
-      wl.store(odd ? As0 : As1);
-      yl.store(odd ? Bs0 : Bs1);
-    }
-    __syncthreads();
-  }
-  if (r > 0) {
-    // acc += (s G) A with G = dY B; A [r x K] is contraction-major here
-    TransTile<kBigTile> al(TileDesc{Al, W.K, r, W.K}, k0);
-    RowTile<kBigTile> gl(TileDesc{G, r, M, r}, m0);
-    for (int st = 0; st * 64 < r; ++st) {
-      al.load(st);
-      gl.load(st);
-      al.store(As0);
-      gl.store_scaled(Bs0, s);
-      __syncthreads();
-      mma_step<4, 4>(acc, As0, Bs0, wc * 128, wr * 128);
-      __syncthreads();
-    }
-  }
-  epilogue<4, 4>(acc, k0 + wc * 128, m0 + wr * 128, StoreBf16{dX, W.K, M, W.K});
 }
 
 // ---------------------------------------------------------------------------
@@ -537,28 +317,6 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(const float* __restric
 // ---------------------------------------------------------------------------
 static hipError_t set_lds(const void* fn, size_t bytes) {
   return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
-}
-
-hipError_t launch_fwd(const Nf4View& W, const bf16_t* X, int64_t M, const bf16_t* U, const bf16_t* B, int r,
-                      float s, bf16_t* Y, hipStream_t st) {
-  const int tiles_n = (int)((W.N + kBigTile - 1) / kBigTile);
-  const int tiles_m = (int)((M + kBigTile - 1) / kBigTile);
-  hipError_t e = set_lds(reinterpret_cast<const void*>(&fwd_kernel), kBigLds);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(fwd_kernel, dim3(tiles_n * tiles_m), dim3(kThreads), kBigLds, st, W, X, M, U, B, r, s, Y,
-                     tiles_n, tiles_m);
-  return hipGetLastError();
-}
-
-hipError_t launch_dx(const Nf4View& W, const bf16_t* dY, int64_t M, const bf16_t* G, const bf16_t* A, int r,
-                     float s, bf16_t* dX, hipStream_t st) {
-  const int tiles_k = (int)((W.K + kBigTile - 1) / kBigTile);
-  const int tiles_m = (int)((M + kBigTile - 1) / kBigTile);
-  hipError_t e = set_lds(reinterpret_cast<const void*>(&dx_kernel), kBigLds);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(dx_kernel, dim3(tiles_k * tiles_m), dim3(kThreads), kBigLds, st, W, dY, M, G, A, r, s, dX,
-                     tiles_k, tiles_m);
-  return hipGetLastError();
 }
 
 // Split of the contraction: enough workgroups to cover the chip, at least
