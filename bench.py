@@ -55,7 +55,7 @@ def gemv_bytes(N, K, r):
 
 def source_digest():
     h = hashlib.sha256()
-    for f in ("device.h", "gemm.hip"):
+    for f in ("device.h", "gemm_nf4.hip"):
         h.update(open(os.path.join(ROOT, "bit_quantized_finetuning_nf4_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
 

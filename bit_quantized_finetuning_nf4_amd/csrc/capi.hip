@@ -47,11 +47,21 @@ qlora_status check_weight(const qlora_nf4_weight* q) {
 }
 
 // GEMM paths: K % 64 == 0 (blocks never straddle rows), N % 8 == 0 (16-byte
-// rows of dY / Y), 32-bit tile indices.
+// rows of dY / Y), codes addressed with 32-bit byte offsets (N K / 2 below
+// 2^32).
 qlora_status check_gemm_weight(const qlora_nf4_weight* q) {
   qlora_status st = check_weight(q);
   if (st != QLORA_OK) return st;
   if (q->cols % 64 != 0 || q->rows % 8 != 0) return QLORA_E_UNSUPPORTED;
+  if (q->rows > (int64_t)0xFFFFFFFF / (q->cols / 2)) return QLORA_E_UNSUPPORTED;
+  return QLORA_OK;
+}
+
+// The fused GEMMs address the token-side matrices (X [M x K], dY [M x N])
+// with 32-bit byte offsets: M K and M N below 2^31 elements.
+qlora_status check_tokens(int64_t M, const qlora_nf4_weight* q) {
+  if (M <= 0 || M > 0x7FFFFFFF) return QLORA_E_SHAPE;
+  if (M > (int64_t)0x7FFFFFFF / q->cols || M > (int64_t)0x7FFFFFFF / q->rows) return QLORA_E_UNSUPPORTED;
   return QLORA_OK;
 }
 
@@ -210,7 +220,7 @@ qlora_status qlora_linear_fwd(const qlora_nf4_weight* W, const uint16_t* X, int6
                               void* ws, size_t ws_bytes, void* stream) {
   qlora_status st = check_gemm_weight(W);
   if (st != QLORA_OK) return st;
-  if (M <= 0 || M > 0x7FFFFFFF) return QLORA_E_SHAPE;
+  if ((st = check_tokens(M, W)) != QLORA_OK) return st;
   if (!X || !Y) return QLORA_E_NULL;
   if (!aligned16(X) || !aligned16(Y) || (U_save && !aligned16(U_save))) return QLORA_E_ALIGN;
   if ((st = check_rank(r, A, B)) != QLORA_OK) return st;
@@ -239,7 +249,7 @@ qlora_status qlora_linear_bwd(const qlora_nf4_weight* W, const uint16_t* X, cons
                               size_t ws_bytes, void* stream) {
   qlora_status st = check_gemm_weight(W);
   if (st != QLORA_OK) return st;
-  if (M <= 0 || M > 0x7FFFFFFF) return QLORA_E_SHAPE;
+  if ((st = check_tokens(M, W)) != QLORA_OK) return st;
   if (!dY) return QLORA_E_NULL;
   if (!aligned16(dY) || (dX && !aligned16(dX)) || (U_saved && !aligned16(U_saved))) return QLORA_E_ALIGN;
   if ((st = check_rank(r, A, B)) != QLORA_OK) return st;
@@ -325,7 +335,7 @@ qlora_status qlora_nf4_fwd(const qlora_nf4_weight* W, const uint16_t* X, int64_t
                            const uint16_t* B, int32_t r, float alpha, uint16_t* Y, void* stream) {
   qlora_status st = check_gemm_weight(W);
   if (st != QLORA_OK) return st;
-  if (M <= 0 || M > 0x7FFFFFFF) return QLORA_E_SHAPE;
+  if ((st = check_tokens(M, W)) != QLORA_OK) return st;
   if (!X || !Y) return QLORA_E_NULL;
   if (!aligned16(X) || !aligned16(Y)) return QLORA_E_ALIGN;
   if ((st = check_rank(r, U, B)) != QLORA_OK) return st;
@@ -338,7 +348,7 @@ qlora_status qlora_nf4_dx(const qlora_nf4_weight* W, const uint16_t* dY, int64_t
                           const uint16_t* A, int32_t r, float alpha, uint16_t* dX, void* stream) {
   qlora_status st = check_gemm_weight(W);
   if (st != QLORA_OK) return st;
-  if (M <= 0 || M > 0x7FFFFFFF) return QLORA_E_SHAPE;
+  if ((st = check_tokens(M, W)) != QLORA_OK) return st;
   if (!dY || !dX) return QLORA_E_NULL;
   if (!aligned16(dY) || !aligned16(dX)) return QLORA_E_ALIGN;
   if ((st = check_rank(r, G, A)) != QLORA_OK) return st;

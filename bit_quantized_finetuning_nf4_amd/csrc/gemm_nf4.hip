@@ -9,27 +9,24 @@
 //
 // Both kernels: 256 threads (4 waves), 256 x 256 output tile, each wave a
 // 128 x 128 sub-tile held in 256 accumulator registers, bf16 MFMA 32x32x16
-// with fp32 accumulation, contraction in steps of 64 with two LDS buffers.
-// While the MFMAs of step s run, the producers fill the other buffer for
-// step s+1: the NF4 codes of step s+1 (loaded two steps ahead) are
-// dequantized into LDS between the MFMA groups, and the token-side tile of
-// step s+1 is loaded into registers at the start of step s and written to
-// LDS at its end.  The MFMA "A" operand is the output-column side and "B"
-// the output-row (token) side; both hold their contraction elements in
-// natural order (the MFMA pairs slot e of every A row with slot e of every
-// B column).
+// with fp32 accumulation.  The contraction runs in stages of 32 through a
+// ring of four LDS stage buffers (weight half + token half), one barrier per
+// stage, placed between its two MFMA halves:
 //
-// LDS layouts.  On gfx950 8-byte LDS reads stream at about twice the rate
-// of 16-byte reads, and sixteen lanes are served together, so:
-//   R  row-fragment tiles: rows of 64 bf16 padded to 136 bytes.  A fragment
-//      (16 bytes of one row) is read as two adjacent 8-byte halves; sixteen
-//      consecutive rows reading the same half sit 17 units of 8 bytes apart
-//      and so hit sixteen different bank groups.
-//   T  transposed tiles (backward weight side): rows = contraction index,
-//      256 bf16 padded to 544 bytes; read with ds_read_b64_tr_b16, which
-//      hands each lane of a 16-lane group one column of a 4-row block.  The
-//      four rows of a block sit 68 units apart (4 bank groups), so the 16
-//      addresses hit 16 different bank groups.
+//   substep s:  issue the loads of stage s+3 (token tile) and of the codes
+//               ahead; dequantize stage s+2 into its ring slot; MFMAs on
+//               stage s (first half) | barrier | MFMAs on stage s (second
+//               half) while the first fragments of stage s+1 are read.
+//
+// The dequantization (NF4 code -> block-scaled bf16 by a byte-permute table,
+// see device.h) is interleaved with the MFMAs of the same wave; a weight
+// element is dequantized once per 256-token tile.
+//
+// Token-side tiles are stored as rows of 32 bf16 (64 bytes), 16-byte chunk c
+// of row r at position c ^ ((r >> 2) & 3): sixteen consecutive rows reading
+// one logical chunk (the MFMA fragment pattern) cover all 64 LDS banks, and
+// so do the producers' 16-byte writes.  The MFMA "A" operand is the output
+// column side (weight rows / columns), "B" the token side.
 #include "device.h"
 #include "kernels.h"
 
@@ -38,27 +35,55 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kTile = 256;
-constexpr int kRS = 136;                         // R-layout row stride (bytes)
-constexpr int kTS = 544;                         // T-layout row stride (bytes)
-constexpr int kRTileBytes = kTile * kRS;         // 34816
-constexpr int kTTileBytes = 64 * kTS;            // 34816
-static_assert(kRTileBytes == kTTileBytes, "tiles share one buffer size");
-constexpr int kBuf = kRTileBytes;
-constexpr size_t kLds = 4u * kBuf;               // 2 buffers x 2 operands = 136 KiB
+constexpr int kStages = 4;                       // ring depth
+constexpr int kOp = kTile * 64;                  // 16 KiB: 256 rows x 32 bf16
+constexpr int kStage = 2 * kOp;                  // weight half at 0, token half at kOp
 
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef short v4s __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4s lds_v4s;
 
-__device__ __forceinline__ uint2 lds_read8(const char* p) { return *reinterpret_cast<const uint2*>(p); }
-__device__ __forceinline__ void lds_write8(char* p, uint32_t a, uint32_t b) {
-  *reinterpret_cast<uint2*>(p) = make_uint2(a, b);
+// Raw buffer resource over `bytes` bytes: loads past the end return zero.
+__device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)bytes, 0x00020000);
 }
-__device__ __forceinline__ uint2 lds_read_tr(const char* p) {
-  const v4s v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(p));
-  return __builtin_bit_cast(uint2, v);
+// 16 bytes per lane from global memory straight into LDS (lane-linear at `lds`).
+__device__ __forceinline__ void dma16(rsrc_t r, char* lds, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
 }
-__device__ __forceinline__ bf16x8_t frag(uint2 lo, uint2 hi) {
-  return __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
+__device__ __forceinline__ uint4 buf_load16(rsrc_t r, uint32_t voff, uint32_t soff) {
+  const u32x4_t v = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// s_waitcnt with vmcnt = vm and lgkmcnt = lgkm (expcnt not waited).
+constexpr int wait_imm(int vm, int lgkm) { return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | (lgkm << 8); }
+#define QLORA_WAIT(vm, lgkm) __builtin_amdgcn_s_waitcnt(wait_imm((vm), (lgkm)))
+
+// LDS accesses use native vector types: the compiler can then tell them
+// apart from the DMA destinations instead of waiting for every DMA in flight.
+__device__ __forceinline__ bf16x8_t rd16(const char* p) { return *reinterpret_cast<const bf16x8_t*>(p); }
+__device__ __forceinline__ uint4 rdu16(const char* p) {
+  const u32x4_t v = *reinterpret_cast<const u32x4_t*>(p);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void wr16(char* p, const uint4& v) {
+  const u32x4_t x = {v.x, v.y, v.z, v.w};
+  *reinterpret_cast<u32x4_t*>(p) = x;
+}
+
+// Position of 16-byte chunk c of row r in a 64-byte-row tile.
+__device__ __forceinline__ int spos(int r, int c) { return r * 64 + 16 * (c ^ ((r >> 2) & 3)); }
+
+// Fragment read offsets in a 64-byte-row tile for the two k16 halves of a
+// stage: lane (lr, h) reads chunk 2 kk + h of row lr.
+struct FragOffs {
+  int o0, o1;
+};
+__device__ __forceinline__ FragOffs frag_offs(int lane) {
+  const int lr = lane & 31, h = lane >> 5;
+  return FragOffs{spos(lr, h), spos(lr, 2 + h)};
 }
 
 __device__ __forceinline__ void zero_acc(f32x16_t (&acc)[4][4]) {
@@ -78,19 +103,22 @@ __device__ __forceinline__ void mfma_block(f32x16_t (&acc)[FI][FJ], const bf16x8
     for (int j = 0; j < FJ; ++j) acc[i][j] = mfma32x32x16(a[i], b[j], acc[i][j]);
 }
 
-// Interleave one contraction sub-step: 16 MFMAs, the fragment reads of the
-// next sub-step early, the producer's VALU work spread between the MFMAs
-// and its LDS writes at the end.
-__device__ __forceinline__ void schedule_substep() {
+// One MFMA half-stage: 16 MFMAs, the fragment reads of the next half early
+// (READS DS reads per slot), six VALU producer instructions after each MFMA
+// and the producer's LDS writes late.
+template <int READS>
+__device__ __forceinline__ void schedule_half() {
 #pragma unroll
   for (int x = 0; x < 16; ++x) {
     QLORA_SCHED(kSchedMfma, 1);
-    if (x < 8) QLORA_SCHED(kSchedDsRead, 1);
-    QLORA_SCHED(kSchedValu, 5);
-    if (x >= 12) QLORA_SCHED(kSchedDsWrite, 1);
+    if (x < 8) QLORA_SCHED(kSchedDsRead, READS);
+    QLORA_SCHED(kSchedValu, 6);
+    if (x == 11 || x == 15) QLORA_SCHED(kSchedDsWrite, 1);
   }
 }
 
+// Tile order: consecutive workgroups share the token tile (the column-side
+// tiles vary fastest); the eight XCDs receive contiguous ranges.
 __device__ __forceinline__ void map_tile(int tiles_c, int tiles_r, int& tc, int& tr) {
   const int nwg = tiles_c * tiles_r;
   int id = blockIdx.x;
@@ -99,203 +127,163 @@ __device__ __forceinline__ void map_tile(int tiles_c, int tiles_r, int& tc, int&
   tr = id / tiles_c;
 }
 
-// ---------------------------------------------------------------------------
-// NF4 codes of one (row, 64-block): 32 bytes of codes + absmax code + scale.
-// ---------------------------------------------------------------------------
-struct BlockCodes {
-  uint4 c0, c1;
-  uint32_t q;
-  float s2;
-};
-
-// Block index of (row n, 64-block blk) is n K/64 + blk: `boff` = n K/64 per
-// lane (32-bit), blk uniform.
-__device__ __forceinline__ void load_block(BlockCodes& bc, const Nf4View& W, uint32_t boff, int64_t blk, bool valid) {
-  if (valid) {
-    const uint4* p = reinterpret_cast<const uint4*>(W.codes + blk * 32 + (uint64_t)boff * 32u);
-    bc.c0 = p[0];
-    bc.c1 = p[1];
-    bc.q = (W.absmax_q + blk)[boff];
-    bc.s2 = W.group_scale[(boff + (uint32_t)blk) >> 8];
-  } else {
-    bc.c0 = bc.c1 = make_uint4(0x77777777u, 0x77777777u, 0x77777777u, 0x77777777u);
-    bc.q = 0;
-    bc.s2 = 0.0f;
-  }
-}
-
-__device__ __forceinline__ uint32_t code_word(const BlockCodes& bc, int ch) {
-  switch (ch) {
-    case 0: return bc.c0.x; case 1: return bc.c0.y; case 2: return bc.c0.z; case 3: return bc.c0.w;
-    case 4: return bc.c1.x; case 5: return bc.c1.y; case 6: return bc.c1.z; default: return bc.c1.w;
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Token-side tile (layout R) staged through registers: 256 rows x 128 bytes
-// per step, 8 x 16 bytes per thread; 8 consecutive lanes read one row.
-// Rows past the end re-read the last row (finite data, never stored);
-// columns past `cols` (rank and contraction tails) are zero.
-// ---------------------------------------------------------------------------
-struct RTileRegs {
-  uint4 v[8];
-};
-
-// Per-lane byte offsets of the 8 rows a thread loads (rows past the end are
-// clamped to the last row); `ld` in elements.
-struct RTileOffs {
-  uint32_t o[8];
-};
-
-__device__ __forceinline__ void r_offsets(RTileOffs& O, int64_t ld, int64_t rows, int64_t row0) {
-#pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    const int idx = threadIdx.x + kThreads * q;
-    int64_t gr = row0 + (idx >> 3);
-    gr = gr < rows ? gr : rows - 1;
-    O.o[q] = (uint32_t)(2 * (gr * ld + 8 * (idx & 7)));
-  }
-}
-
-// Load step `step` of a row-major tile: uniform base (src + 64 step) plus the
-// lane's 32-bit byte offset.  `col_clamp` (bytes, multiple of 16) keeps a
-// ragged last step inside each row; the excess columns meet zero weights.
-__device__ __forceinline__ void r_load(RTileRegs& R, const bf16_t* src, const RTileOffs& O, int step,
-                                       uint32_t col_bytes_left) {
-  const char* base = reinterpret_cast<const char*>(src + (int64_t)step * 64);
-  const uint32_t cmax = col_bytes_left - 16;
-#pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    const uint32_t c16 = 16u * ((threadIdx.x + kThreads * q) & 7);
-    const uint32_t off = O.o[q] - c16 + (c16 < cmax ? c16 : cmax);
-    R.v[q] = *reinterpret_cast<const uint4*>(base + off);
-  }
-}
-
-__device__ __forceinline__ void r_load_masked(RTileRegs& R, const bf16_t* src, int64_t ld, int64_t rows,
-                                              int64_t cols, int64_t row0, int step) {
-#pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    const int idx = threadIdx.x + kThreads * q;
-    const int64_t gr = row0 + (idx >> 3), gc = (int64_t)step * 64 + 8 * (idx & 7);
-    R.v[q] = make_uint4(0u, 0u, 0u, 0u);
-    if (gr < rows && gc < cols) R.v[q] = *reinterpret_cast<const uint4*>(src + gr * ld + gc);
-  }
-}
-
-__device__ __forceinline__ void r_store(char* lds, const RTileRegs& R) {
-#pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    const int idx = threadIdx.x + kThreads * q;
-    char* p = lds + (idx >> 3) * kRS + 16 * (idx & 7);
-    lds_write8(p, R.v[q].x, R.v[q].y);
-    lds_write8(p + 8, R.v[q].z, R.v[q].w);
-  }
-}
-
-__device__ __forceinline__ void r_scale(RTileRegs& R, float s) {
-#pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    uint4& v = R.v[q];
-    v.x = pack_bf16x2(bf2f(v.x & 0xFFFFu) * s, bf2f(v.x >> 16) * s);
-    v.y = pack_bf16x2(bf2f(v.y & 0xFFFFu) * s, bf2f(v.y >> 16) * s);
-    v.z = pack_bf16x2(bf2f(v.z & 0xFFFFu) * s, bf2f(v.z >> 16) * s);
-    v.w = pack_bf16x2(bf2f(v.w & 0xFFFFu) * s, bf2f(v.w >> 16) * s);
-  }
-}
-
-// Fragment (layout R) for sub-step kk: lane (lr, h) reads the 16 bytes of
-// chunk 2kk + h of its fragment row; `base` already holds the lane's row
-// and h offset.
-__device__ __forceinline__ bf16x8_t r_frag(const char* base, int kk) {
-  const char* p = base + 32 * kk;
-  return frag(lds_read8(p), lds_read8(p + 8));
-}
-
-// Per-lane byte offset of a lane's fragment row within a tile.
-__device__ __forceinline__ int r_lane_off(int lane) { return (lane & 31) * kRS + 16 * (lane >> 5); }
-
-__device__ __forceinline__ void store_acc_bf16(const f32x16_t (&acc)[4][4], bf16_t* out, int64_t ld, int64_t rows,
-                                               int64_t cols, int64_t col0, int64_t row0) {
-  const int lane = threadIdx.x & 63, lr = lane & 31, h = lane >> 5;
+// Output: lane (lr, h) of wave (wr, wc) holds token row0 + 128 wr + 32 j + lr
+// and columns col0 + 128 wc + 32 i + 8 q + 4 h + 0..3.
+__device__ __forceinline__ void store_tile(const f32x16_t (&acc)[4][4], bf16_t* out, int64_t ld, int64_t rows,
+                                           int64_t cols, int64_t row0, int64_t col0) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wr = w >> 1, wc = w & 1, lr = lane & 31, h = lane >> 5;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int64_t row = row0 + 32 * j + lr;
+      const int64_t row = row0 + wr * 128 + 32 * j + lr;
       if (row >= rows) continue;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int64_t col = col0 + 32 * i + 8 * q + 4 * h;
-        if (col < cols) {  // cols % 8 == 0, so the 4 columns are all in range
+        const int64_t col = col0 + wc * 128 + 32 * i + 8 * q + 4 * h;
+        if (col < cols)  // cols % 8 == 0: the four columns are all in range
           *reinterpret_cast<uint2*>(out + row * ld + col) =
-              make_uint2(pack_bf16x2(acc[i][j][4 * q + 0], acc[i][j][4 * q + 1]),
+              make_uint2(pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
                          pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]));
-        }
       }
     }
 }
 
-// ---------------------------------------------------------------------------
-// Forward kernel
-// ---------------------------------------------------------------------------
-// Weight-side producer: thread t owns W row t of the tile and dequantizes
-// chunks [ch0, ch0 + n) of its 64-element block into LDS row t (layout R).
-__device__ __forceinline__ void fwd_dequant_chunks(char* As, const BlockCodes& bc, const Nf4Table& T, int ch0,
-                                                   int n) {
-  char* row = As + threadIdx.x * kRS;
+// 16 bytes of a bf16 row scaled by s (fp32 product rounded to bf16).
+__device__ __forceinline__ uint4 scale16(uint4 v, float s) {
+  v.x = pack_bf16x2(bf2f(v.x & 0xFFFFu) * s, bf2f(v.x >> 16) * s);
+  v.y = pack_bf16x2(bf2f(v.y & 0xFFFFu) * s, bf2f(v.y >> 16) * s);
+  v.z = pack_bf16x2(bf2f(v.z & 0xFFFFu) * s, bf2f(v.z >> 16) * s);
+  v.w = pack_bf16x2(bf2f(v.w & 0xFFFFu) * s, bf2f(v.w >> 16) * s);
+  return v;
+}
+
+// Token half of the LoRA tail: (s T)[row0 + row, j0 + 8 c ..] into a
+// 64-byte-row tile (T is rows x rank, zero past the rank and the last row).
+__device__ __forceinline__ void tail_tokens(char* dst, const bf16_t* T, int64_t rows, int r, int64_t row0, int j0,
+                                            float s) {
 #pragma unroll
-  for (int k = 0; k < n; ++k) {
-    const int ch = ch0 + k;
-    uint32_t o[4];
-    dequant8(code_word(bc, ch), T, o);
-    lds_write8(row + 16 * ch, o[0], o[1]);
-    lds_write8(row + 16 * ch + 8, o[2], o[3]);
+  for (int e = 0; e < 4; ++e) {
+    const int idx = threadIdx.x + kThreads * e;
+    const int row = idx >> 2, c = idx & 3, col = j0 + 8 * c;
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (col < r && row0 + row < rows) v = scale16(*reinterpret_cast<const uint4*>(T + (row0 + row) * r + col), s);
+    wr16(dst + spos(row, c), v);
   }
 }
 
-struct FwdCtx {
-  Nf4View W;
-  const bf16_t* X;
-  RTileOffs xo;
-  uint32_t wboff;  // owned W row * K / 64
-  bool wvalid;
-  int nsteps;
+// ===========================================================================
+// Forward: Y = X deq(W)^T + s U B^T.  Weight half = W rows n0.. (dequantized
+// by thread t = row t), token half = X rows m0.. (DMA).  The NF4 codes of
+// four stages (64 bytes per row) are also brought in by DMA, into a double
+// buffer after the ring: one coalesced 64-byte piece per row instead of a
+// 16-byte scattered load per row and stage.
+// ===========================================================================
+constexpr int kCodes = kTile * 64;               // codes of 4 stages
+constexpr int kCodeBase = kStages * kStage;      // 128 KiB
+constexpr size_t kLdsFwd = (size_t)kCodeBase + 2 * kCodes;   // 160 KiB
+
+// DMA pattern for a 256-row x 64-byte tile: wave w, instruction q covers
+// rows 64 q + 16 w .. +15 (1 KiB, lane-linear); lane j -> row + (j >> 2),
+// position j & 3, which holds chunk (j & 3) ^ ((j >> 4) & 3).
+__device__ __forceinline__ int dma_row(int q, int w, int j) { return 64 * q + 16 * w + (j >> 2); }
+__device__ __forceinline__ int dma_chunk(int j) { return (j & 3) ^ ((j >> 4) & 3); }
+
+struct Fwd {
+  rsrc_t xr, cr;          // X, NF4 codes
+  uint32_t xo[4], co[4];  // per-lane byte offsets of the four DMA instructions
+  const uint8_t* aq;      // absmax codes of the owned row
+  const float* gs;        // group scales
+  uint32_t ablk0;         // block index of (owned row, block 0)
+  int nsub, nblk, w;
 };
 
-// One contraction step: MFMAs on (Ac, Bc) while producing step st+1 into
-// (An, Bn) from `cur` (the codes of step st+1); the codes of step st+2 are
-// loaded into `nxt`.
-__device__ __forceinline__ void fwd_step(f32x16_t (&acc)[4][4], bf16x8_t (&fa)[2][4], bf16x8_t (&fb)[2][4],
-                                         const FwdCtx& c, int st, const char* Ac, const char* Bc, char* An,
-                                         char* Bn, const BlockCodes& cur, BlockCodes& nxt, RTileRegs& xr,
-                                         int aoff, int boff) {
-  const bool more = st + 1 < c.nsteps;
-  if (more) r_load(xr, c.X, c.xo, st + 1, 128u);
-  if (st + 2 < c.nsteps) load_block(nxt, c.W, c.wboff, st + 2, c.wvalid);
-  // Branch-free producer (on the last step it fills a buffer nobody reads)
-  // so that the scheduler can interleave it with the MFMAs.
-  const Nf4Table T = make_table(block_scale(cur.q, cur.s2));
+struct Scale {
+  uint32_t q;
+  float s2;
+};
+
+__device__ __forceinline__ void fwd_dma_x(char* smem, const Fwd& f, int stage, int buf) {
+  const uint32_t soff = (uint32_t)min(stage, f.nsub - 1) * 64u;
+  char* dst = smem + buf * kStage + kOp;
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) {
-    if (kk < 3) {
+  for (int q = 0; q < 4; ++q) dma16(f.xr, dst + (64 * q + 16 * f.w) * 64, f.xo[q], soff);
+}
+template <int BUF>   // BUF == chunk & 1
+__device__ __forceinline__ void fwd_dma_codes(char* smem, const Fwd& f, int chunk) {
+  const int nch = (f.nsub + 3) >> 2;
+  const uint32_t soff = (uint32_t)min(chunk, nch - 1) * 64u;
+  char* dst = smem + kCodeBase + BUF * kCodes;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        fa[(kk + 1) & 1][i] = r_frag(Ac + aoff + 32 * kRS * i, kk + 1);
-        fb[(kk + 1) & 1][i] = r_frag(Bc + boff + 32 * kRS * i, kk + 1);
-      }
-    }
-    mfma_block<4, 4>(acc, fa[kk & 1], fb[kk & 1]);
-    fwd_dequant_chunks(An, cur, T, 2 * kk, 2);
-    schedule_substep();
+  for (int q = 0; q < 4; ++q) dma16(f.cr, dst + (64 * q + 16 * f.w) * 64, f.co[q], soff);
+}
+__device__ __forceinline__ Scale fwd_scale(const Fwd& f, int blk) {
+  const int b = min(blk, f.nblk - 1);
+  return Scale{f.aq[b], f.gs[(f.ablk0 + (uint32_t)b) >> 8]};
+}
+
+// Dequantize chunks c0, c0+1 (8 elements each) of the owned row's codes of a
+// stage into ring buffer `buf`.
+__device__ __forceinline__ void fwd_produce(char* smem, const uint4& cw, const Nf4Table& T, int buf, int c0) {
+  char* row = smem + buf * kStage;
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int c = c0 + k;
+    const uint32_t word = c == 0 ? cw.x : c == 1 ? cw.y : c == 2 ? cw.z : cw.w;
+    uint32_t o[4];
+    dequant8(word, T, o);
+    wr16(row + spos(threadIdx.x, c), make_uint4(o[0], o[1], o[2], o[3]));
   }
-  if (more) r_store(Bn, xr);
-  __syncthreads();
+}
+
+struct Frags {
+  bf16x8_t a0[4], b0[4], a1[4], b1[4];
+};
+
+// Substep s, U8 = s mod 8 (ring slot U8 & 3, code buffer of the produced
+// stage ((U8 + 2) >> 2) & 1): MFMAs on stage s, token DMA of stage s+3,
+// code DMA of chunk s/4 + 2 (U8 & 3 == 2), dequantization of stage s+2,
+// scales of block s/2 + 2 (U8 even; the table of block (s+2)/2 is built
+// from the scales loaded two substeps earlier).
+template <int U8>
+__device__ __forceinline__ void fwd_substep(char* smem, const Fwd& f, int s, f32x16_t (&acc)[4][4], Frags& F,
+                                            Nf4Table& T, Scale& sA, Scale& sB, int an, int bm, FragOffs fo) {
+  constexpr int U = U8 & 3;
+  constexpr int PS = U8 + 2;
+  const char* cur = smem + U * kStage;
+  const char* nxt = smem + ((U + 1) & 3) * kStage;
+  __builtin_amdgcn_sched_barrier(0);
+  fwd_dma_x(smem, f, s + 3, (U + 3) & 3);
+  if (U == 2) fwd_dma_codes<(U8 >> 2)>(smem, f, (s >> 2) + 2);
+  if (U == 0) sA = fwd_scale(f, (s >> 1) + 2);
+  if (U == 2) sB = fwd_scale(f, (s >> 1) + 2);
+  __builtin_amdgcn_sched_barrier(0);
+  const uint4 cw = rdu16(smem + kCodeBase + ((PS >> 2) & 1) * kCodes + spos(threadIdx.x, PS & 3));
+  if (U == 0) T = make_table(block_scale(sB.q, sB.s2));
+  if (U == 2) T = make_table(block_scale(sA.q, sA.s2));
+  // first half: k16 0 of stage s; read k16 1
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    fa[0][i] = r_frag(An + aoff + 32 * kRS * i, 0);
-    fb[0][i] = r_frag(Bn + boff + 32 * kRS * i, 0);
+    F.a1[i] = rd16(cur + an + i * 2048 + fo.o1);
+    F.b1[i] = rd16(cur + kOp + bm + i * 2048 + fo.o1);
   }
+  mfma_block<4, 4>(acc, F.a0, F.b0);
+  fwd_produce(smem, cw, T, (U + 2) & 3, 0);
+  schedule_half<1>();
+  // The token tile of stage s+1 (issued two substeps ago) has landed once
+  // at most the loads of the last two substeps are in flight: 4 token DMAs
+  // per substep, 4 code DMAs at U == 2, 2 scale loads at even U.
+  QLORA_WAIT(U == 0 ? 10 : U == 1 ? 10 : 14, 0);
+  __builtin_amdgcn_s_barrier();
+  // second half: k16 1 of stage s; read k16 0 of stage s+1
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    F.a0[i] = rd16(nxt + an + i * 2048 + fo.o0);
+    F.b0[i] = rd16(nxt + kOp + bm + i * 2048 + fo.o0);
+  }
+  mfma_block<4, 4>(acc, F.a1, F.b1);
+  fwd_produce(smem, cw, T, (U + 2) & 3, 2);
+  schedule_half<1>();
 }
 
 __global__ __launch_bounds__(kThreads, 1) void nf4_fwd_kernel(Nf4View W, const bf16_t* __restrict__ X, int64_t M,
@@ -303,161 +291,229 @@ __global__ __launch_bounds__(kThreads, 1) void nf4_fwd_kernel(Nf4View W, const b
                                                               const bf16_t* __restrict__ Bl, int r, float s,
                                                               bf16_t* __restrict__ Y, int tiles_n, int tiles_m) {
   extern __shared__ __align__(16) char smem[];
-  char* const A0 = smem;
-  char* const A1 = smem + kBuf;
-  char* const B0 = smem + 2 * kBuf;
-  char* const B1 = smem + 3 * kBuf;
   int tn, tm;
   map_tile(tiles_n, tiles_m, tn, tm);
   const int64_t n0 = (int64_t)tn * kTile, m0 = (int64_t)tm * kTile;
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6, wr = w >> 1, wc = w & 1;
-  FwdCtx c;
-  c.W = W;
-  c.X = X;
-  r_offsets(c.xo, W.K, M, m0);
-  c.wboff = (uint32_t)((n0 + t) * (W.K >> 6));
-  c.wvalid = n0 + t < W.N;
-  c.nsteps = (int)(W.K >> 6);
-  const int aoff = wc * 128 * kRS + r_lane_off(lane);
-  const int boff = wr * 128 * kRS + r_lane_off(lane);
+  const int t = threadIdx.x, lane = t & 63, wr = (t >> 6) >> 1, wc = (t >> 6) & 1;
+  const int64_t N = W.N, K = W.K;
+
+  Fwd f;
+  f.w = __builtin_amdgcn_readfirstlane(t >> 6);
+  __builtin_assume(f.w >= 0 && f.w < 4);
+  f.xr = make_rsrc(X, (uint32_t)(M * K * 2));
+  f.cr = make_rsrc(W.codes, (uint32_t)(N * K / 2));
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    // rows past the end re-read the last row: finite data, never stored
+    const int row = dma_row(q, t >> 6, lane);
+    const int64_t xm = min(m0 + row, M - 1), wn = min(n0 + row, N - 1);
+    f.xo[q] = (uint32_t)(xm * K * 2 + dma_chunk(lane) * 16);
+    f.co[q] = (uint32_t)(wn * (K / 2) + dma_chunk(lane) * 16);
+  }
+  const int64_t own = min(n0 + t, N - 1);
+  f.ablk0 = (uint32_t)(own * (K >> 6));
+  f.aq = W.absmax_q + f.ablk0;
+  f.gs = W.group_scale;
+  f.nsub = (int)(K >> 5);
+  f.nblk = (int)(K >> 6);
+  const FragOffs fo = frag_offs(lane);
+  const int an = wc * 128 * 64, bm = wr * 128 * 64;
 
   f32x16_t acc[4][4];
   zero_acc(acc);
 
-  // prologue: step 0 into buffer 0, codes of step 1 in flight
-  BlockCodes bcA, bcB;
-  RTileRegs xr;
-  r_load(xr, X, c.xo, 0, 128u);
-  load_block(bcA, W, c.wboff, 0, c.wvalid);
-  bcB = bcA;
-  if (c.nsteps > 1) load_block(bcB, W, c.wboff, 1, c.wvalid);
-  {
-    const Nf4Table T = make_table(block_scale(bcA.q, bcA.s2));
-    fwd_dequant_chunks(A0, bcA, T, 0, 8);
+  // prologue: code chunks 0 and 1, scales of blocks 0 and 1, token stages
+  // 0..2; then stages 0 and 1 are dequantized
+  fwd_dma_codes<0>(smem, f, 0);
+  fwd_dma_codes<1>(smem, f, 1);
+  Scale sA = fwd_scale(f, 0), sB = fwd_scale(f, 1);
+  fwd_dma_x(smem, f, 0, 0);
+  fwd_dma_x(smem, f, 1, 1);
+  fwd_dma_x(smem, f, 2, 2);
+  QLORA_WAIT(0, 0);
+  __builtin_amdgcn_s_barrier();
+  Nf4Table T = make_table(block_scale(sA.q, sA.s2));
+#pragma unroll
+  for (int st = 0; st < 2; ++st) {
+    const uint4 cw = rdu16(smem + kCodeBase + spos(t, st));
+    fwd_produce(smem, cw, T, st, 0);
+    fwd_produce(smem, cw, T, st, 2);
   }
-  r_store(B0, xr);
-  __syncthreads();
-
-  bf16x8_t fa[2][4], fb[2][4];
+  QLORA_WAIT(0, 0);
+  __builtin_amdgcn_s_barrier();
+  Frags F;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    fa[0][i] = r_frag(A0 + aoff + 32 * kRS * i, 0);
-    fb[0][i] = r_frag(B0 + boff + 32 * kRS * i, 0);
+    F.a0[i] = rd16(smem + an + i * 2048 + fo.o0);
+    F.b0[i] = rd16(smem + kOp + bm + i * 2048 + fo.o0);
   }
-  // two steps per iteration: buffers and code registers alternate
-  // statically; an odd last step is peeled
+  // K % 64 == 0, so the stage count is even
   int st = 0;
-  for (; st + 1 < c.nsteps; st += 2) {
-    fwd_step(acc, fa, fb, c, st, A0, B0, A1, B1, bcB, bcA, xr, aoff, boff);
-    fwd_step(acc, fa, fb, c, st + 1, A1, B1, A0, B0, bcA, bcB, xr, aoff, boff);
+#define QLORA_FWD_SUB(u) fwd_substep<u>(smem, f, st + u, acc, F, T, sA, sB, an, bm, fo)
+  for (; st + 8 <= f.nsub; st += 8) {
+    QLORA_FWD_SUB(0); QLORA_FWD_SUB(1); QLORA_FWD_SUB(2); QLORA_FWD_SUB(3);
+    QLORA_FWD_SUB(4); QLORA_FWD_SUB(5); QLORA_FWD_SUB(6); QLORA_FWD_SUB(7);
   }
-  if (st < c.nsteps) fwd_step(acc, fa, fb, c, st, A0, B0, A1, B1, bcB, bcA, xr, aoff, boff);
+  const int rem = f.nsub - st;
+  if (rem >= 2) { QLORA_FWD_SUB(0); QLORA_FWD_SUB(1); }
+  if (rem >= 4) { QLORA_FWD_SUB(2); QLORA_FWD_SUB(3); }
+  if (rem >= 6) { QLORA_FWD_SUB(4); QLORA_FWD_SUB(5); }
+#undef QLORA_FWD_SUB
+  // drain the DMAs still in flight (clamped re-loads) before reusing the ring
+  QLORA_WAIT(0, 0);
+  __builtin_amdgcn_s_barrier();
 
   if (r > 0) {
-    // LoRA up-projection: extra contraction steps over the rank,
-    // acc += (s U) B^T, through the same LDS layout.
-    for (st = 0; st * 64 < r; ++st) {
-      r_load_masked(xr, Bl, r, W.N, r, n0, st);
-      r_store(A0, xr);
-      r_load_masked(xr, U, r, M, r, m0, st);
-      r_scale(xr, s);
-      r_store(B0, xr);
-      __syncthreads();
+    // LoRA up-projection: acc += (s U) B^T over the rank, 32 at a time
+    for (int j0 = 0; j0 < r; j0 += 32) {
+      char* wb = smem;
+      char* xb = smem + kOp;
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
+      for (int e = 0; e < 4; ++e) {
+        const int idx = t + kThreads * e;
+        const int row = idx >> 2, c = idx & 3, col = j0 + 8 * c;
+        uint4 v = make_uint4(0u, 0u, 0u, 0u);
+        if (col < r && n0 + row < N) v = *reinterpret_cast<const uint4*>(Bl + (n0 + row) * r + col);
+        wr16(wb + spos(row, c), v);
+      }
+      tail_tokens(xb, U, M, r, m0, j0, s);
+      QLORA_WAIT(0, 0);
+      __builtin_amdgcn_s_barrier();
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const int o = kk ? fo.o1 : fo.o0;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          fa[0][i] = r_frag(A0 + aoff + 32 * kRS * i, kk);
-          fb[0][i] = r_frag(B0 + boff + 32 * kRS * i, kk);
+          F.a0[i] = rd16(wb + an + i * 2048 + o);
+          F.b0[i] = rd16(xb + bm + i * 2048 + o);
         }
-        mfma_block<4, 4>(acc, fa[0], fb[0]);
+        mfma_block<4, 4>(acc, F.a0, F.b0);
       }
-      __syncthreads();
+      QLORA_WAIT(0, 0);
+      __builtin_amdgcn_s_barrier();
     }
   }
-  store_acc_bf16(acc, Y, W.N, M, W.N, n0 + wc * 128, m0 + wr * 128);
+  store_tile(acc, Y, N, M, N, m0, n0);
 }
 
-// ---------------------------------------------------------------------------
-// Backward dX kernel
-// ---------------------------------------------------------------------------
-// Weight-side tile (layout T): 64 contraction rows x 256 columns.  Thread t
-// owns row t >> 2 and 64-column block t & 3.
-__device__ __forceinline__ char* t_chunk(char* lds, int row, int blk, int ch) {
-  return lds + row * kTS + 128 * blk + 16 * ch;
+// ===========================================================================
+// Backward: dX = dY deq(W) + s G A.  Output tile 256 (m) x 256 (k); the
+// contraction runs over n.  Weight half of a stage = 32 rows n x 256
+// columns k, rows of 512 bytes with 32-byte block b of row n at position
+// b ^ (n & 3), read transposed (ds_read_b64_tr_b16) as the A operand: the
+// four rows that one 16-lane group of a transposed read touches land on
+// four different 32-byte bank groups.  Thread t dequantizes row t >> 3,
+// columns 32 (t & 7) .. +31 (its codes are 16 coalesced bytes), chunk p in
+// order p ^ ((t >> 2) & 1), which keeps the 16-byte writes conflict-free.
+// The dY tile goes through registers: the transposed reads cannot be told
+// apart from DMA destinations by the compiler, which would then wait for
+// every DMA in flight before each of them.
+// ===========================================================================
+constexpr int kWRow = 512;
+constexpr size_t kLdsDx = (size_t)kStages * kStage;   // 128 KiB
+__device__ __forceinline__ int tpos(int n, int b) { return n * kWRow + 32 * (b ^ (n & 3)); }
+
+__device__ __forceinline__ uint2 rd_tr(const char* p) {
+  const v4s v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(p));
+  return __builtin_bit_cast(uint2, v);
+}
+// A fragment: columns of 8 contraction rows (two transposed reads 4 rows apart).
+__device__ __forceinline__ bf16x8_t tfrag(const char* p) {
+  const uint2 lo = rd_tr(p), hi = rd_tr(p + 4 * kWRow);
+  return __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
 }
 
-// Per-lane byte offset of the first transpose read of fragment i at kk = 0:
-// as a source lane of its 16-lane group (g, s) it addresses row
-// 8h + (s >> 2), columns ia + 32 i + 16 half16 + 4 (s & 3) .. +3.  kk adds
-// 16 rows, the second read 4 rows.
-__device__ __forceinline__ int t_frag_off(int lane, int ia, int i) {
-  const int g = lane >> 4, s = lane & 15, h = g >> 1, half16 = g & 1;
-  return (8 * h + (s >> 2)) * kTS + 2 * (ia + 32 * i + 16 * half16 + 4 * (s & 3));
-}
-
-__device__ __forceinline__ bf16x8_t t_frag(const char* p, int kk) {
-  const char* q = p + kk * 16 * kTS;
-  return frag(lds_read_tr(q), lds_read_tr(q + 4 * kTS));
-}
-
-struct DxCtx {
-  Nf4View W;
-  const bf16_t* dY;
-  RTileOffs yo;
-  uint32_t ybytes;  // 2 N: bytes per dY row
-  uint32_t wboff;   // block index of (row orow, column kcol)
-  int64_t kcol;
-  int orow, oblk;
-  bool kvalid;
-  int nsteps;
+struct Dx {
+  rsrc_t yr, cr, ar, gr;      // dY, codes, absmax codes, group scales
+  uint32_t yo[4];             // dY lane offsets of the four 16-byte pieces (stage 0)
+  int ypos[4];                // their LDS offsets within a token half
+  uint32_t co, ao;            // codes / absmax lane offsets at stage 0
+  uint32_t cstride, astride;  // per-stage strides (32 rows)
+  uint32_t ablk, kb;          // block index at stage 0, K / 64
+  int nsub;
+};
+struct Codes {
+  uint4 c;
+  uint32_t q;
+  float s2;
+};
+struct YRegs {
+  uint4 v[4];
 };
 
-// Codes of contraction step `step`: W row 64 step + orow, 64-column block
-// kcol / 64; its block index is wboff + 64 step K/64 (the uniform part).
-__device__ __forceinline__ void dx_wload(BlockCodes& bc, const DxCtx& c, int step) {
-  const int64_t n = (int64_t)step * 64 + c.orow;
-  load_block(bc, c.W, c.wboff, (int64_t)step * 64 * (c.W.K >> 6), c.kvalid && n < c.W.N);
+// Codes, absmax code and group scale of a stage for this thread.  Rows past
+// N read as zero through the buffer range check: absmax code 0 gives block
+// scale 0, so those rows dequantize to zero and meet the padded dY columns.
+__device__ __forceinline__ void dx_load_codes(Codes& c, const Dx& d, int stage) {
+  const uint32_t st = (uint32_t)min(stage, d.nsub - 1);
+  c.c = buf_load16(d.cr, d.co, st * d.cstride);
+  c.q = __builtin_amdgcn_raw_buffer_load_b8(d.ar, d.ao, st * d.astride, 0);
+  const uint32_t g = (d.ablk + st * 32u * d.kb) >> 8;
+  c.s2 = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(d.gr, g * 4u, 0, 0));
 }
-
-__device__ __forceinline__ void dx_dequant(char* As, const DxCtx& c, const BlockCodes& bc, const Nf4Table& T, int ch0,
-                                           int cnt) {
+__device__ __forceinline__ void dx_load_y(YRegs& y, const Dx& d, int stage) {
+  const uint32_t soff = (uint32_t)min(stage, d.nsub - 1) * 64u;
 #pragma unroll
-  for (int k = 0; k < cnt; ++k) {
+  for (int q = 0; q < 4; ++q) y.v[q] = buf_load16(d.yr, d.yo[q], soff);
+}
+__device__ __forceinline__ void dx_store_y(char* smem, const Dx& d, const YRegs& y, int buf) {
+  char* dst = smem + buf * kStage + kOp;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) wr16(dst + d.ypos[q], y.v[q]);
+}
+// Dequantize chunks 2 half, 2 half + 1 of this thread's 32 columns into
+// ring buffer `buf`.
+__device__ __forceinline__ void dx_produce(char* smem, const Codes& c, const Nf4Table& T, int buf, int half) {
+  const int t = threadIdx.x, n = t >> 3, j = t & 7, flip = (t >> 2) & 1;
+  char* base = smem + buf * kStage;
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int p = (2 * half + k) ^ flip;
+    const uint32_t word = p == 0 ? c.c.x : p == 1 ? c.c.y : p == 2 ? c.c.z : c.c.w;
     uint32_t o[4];
-    dequant8(code_word(bc, ch0 + k), T, o);
-    *reinterpret_cast<uint4*>(t_chunk(As, c.orow, c.oblk, ch0 + k)) = make_uint4(o[0], o[1], o[2], o[3]);
+    dequant8(word, T, o);
+    const int ch = 4 * j + p;   // 16-byte chunk of the row (8 columns)
+    wr16(base + tpos(n, ch >> 1) + 16 * (ch & 1), make_uint4(o[0], o[1], o[2], o[3]));
   }
 }
 
-__device__ __forceinline__ void dx_step(f32x16_t (&acc)[4][4], bf16x8_t (&fa)[2][4], bf16x8_t (&fb)[2][4],
-                                        const DxCtx& c, int st, const char* Ac, const char* Bc, char* An, char* Bn,
-                                        const BlockCodes& cur, BlockCodes& nxt, RTileRegs& yr, const int (&aoff)[4],
-                                        int boff) {
-  const bool more = st + 1 < c.nsteps;
-  if (more) r_load(yr, c.dY, c.yo, st + 1, c.ybytes - 128u * (st + 1));
-  if (st + 2 < c.nsteps) dx_wload(nxt, c, st + 2);
-  const Nf4Table T = make_table(block_scale(cur.q, cur.s2));
-#pragma unroll
-  for (int kk = 0; kk < 4; ++kk) {
-    if (kk < 3) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        fa[(kk + 1) & 1][i] = t_frag(Ac + aoff[i], kk + 1);
-        fb[(kk + 1) & 1][i] = r_frag(Bc + boff + 32 * kRS * i, kk + 1);
-      }
-    }
-    mfma_block<4, 4>(acc, fa[kk & 1], fb[kk & 1]);
-    dx_dequant(An, c, cur, T, 2 * kk, 2);
-    schedule_substep();
-  }
-  if (more) r_store(Bn, yr);
-  __syncthreads();
+// Substep s, U8 = s mod 8: loads of codes for stage s+4 (register set U8 & 3)
+// and dY of stage s+3; dY of stage s+2 (loaded one substep ago) is stored
+// after the barrier; dequantization of stage s+2.
+template <int U8>
+__device__ __forceinline__ void dx_substep(char* smem, const Dx& d, int s, f32x16_t (&acc)[4][4], Frags& F,
+                                           Codes (&cs)[4], YRegs (&ys)[2], const int (&ao)[4], int bm,
+                                           FragOffs fo) {
+  constexpr int U = U8 & 3;
+  const char* cur = smem + U * kStage;
+  const char* nxt = smem + ((U + 1) & 3) * kStage;
+  __builtin_amdgcn_sched_barrier(0);
+  dx_load_codes(cs[U], d, s + 4);   // set U is free: stage s was dequantized two substeps ago
+  dx_load_y(ys[U8 & 1], d, s + 3);
+  __builtin_amdgcn_sched_barrier(0);
+  const Codes& pc = cs[(U + 2) & 3];
+  const Nf4Table T = make_table(block_scale(pc.q, pc.s2));
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    fa[0][i] = t_frag(An + aoff[i], 0);
-    fb[0][i] = r_frag(Bn + boff + 32 * kRS * i, 0);
+    F.a1[i] = tfrag(cur + ao[i] + 16 * kWRow);
+    F.b1[i] = rd16(cur + kOp + bm + i * 2048 + fo.o1);
   }
+  mfma_block<4, 4>(acc, F.a0, F.b0);
+  dx_produce(smem, pc, T, (U + 2) & 3, 0);
+  schedule_half<2>();
+  QLORA_WAIT(63, 0);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  dx_store_y(smem, d, ys[(U8 + 1) & 1], (U + 2) & 3);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    F.a0[i] = tfrag(nxt + ao[i]);
+    F.b0[i] = rd16(nxt + kOp + bm + i * 2048 + fo.o0);
+  }
+  mfma_block<4, 4>(acc, F.a1, F.b1);
+  dx_produce(smem, pc, T, (U + 2) & 3, 1);
+  schedule_half<2>();
 }
 
 __global__ __launch_bounds__(kThreads, 1) void nf4_dx_kernel(Nf4View W, const bf16_t* __restrict__ dY, int64_t M,
@@ -465,92 +521,126 @@ __global__ __launch_bounds__(kThreads, 1) void nf4_dx_kernel(Nf4View W, const bf
                                                              const bf16_t* __restrict__ Al, int r, float s,
                                                              bf16_t* __restrict__ dX, int tiles_k, int tiles_m) {
   extern __shared__ __align__(16) char smem[];
-  char* const A0 = smem;
-  char* const A1 = smem + kBuf;
-  char* const B0 = smem + 2 * kBuf;
-  char* const B1 = smem + 3 * kBuf;
   int tk, tm;
   map_tile(tiles_k, tiles_m, tk, tm);
   const int64_t k0 = (int64_t)tk * kTile, m0 = (int64_t)tm * kTile;
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6, wr = w >> 1, wc = w & 1;
-  DxCtx c;
-  c.W = W;
-  c.dY = dY;
-  r_offsets(c.yo, W.N, M, m0);
-  c.ybytes = (uint32_t)(2 * W.N);
-  c.orow = t >> 2;
-  c.oblk = t & 3;
-  c.kcol = k0 + 64 * (t & 3);
-  c.kvalid = c.kcol < W.K;
-  c.wboff = (uint32_t)(c.orow * (W.K >> 6) + (c.kvalid ? (c.kcol >> 6) : 0));
-  c.nsteps = (int)((W.N + 63) >> 6);
+  const int t = threadIdx.x, lane = t & 63, wr = (t >> 6) >> 1, wc = (t >> 6) & 1;
+  const int64_t N = W.N, K = W.K;
 
-  int aoff[4];
+  Dx d;
+  d.yr = make_rsrc(dY, (uint32_t)(M * N * 2));
+  d.cr = make_rsrc(W.codes, (uint32_t)(N * K / 2));
+  d.ar = make_rsrc(W.absmax_q, (uint32_t)(N * (K >> 6)));
+  d.gr = make_rsrc(W.group_scale, (uint32_t)(((N * (K >> 6) + 255) >> 8) * 4));
 #pragma unroll
-  for (int i = 0; i < 4; ++i) aoff[i] = t_frag_off(lane, wc * 128, i);
-  const int boff = wr * 128 * kRS + r_lane_off(lane);
+  for (int q = 0; q < 4; ++q) {
+    const int idx = t + kThreads * q, row = idx >> 2, c = idx & 3;
+    const int64_t ym = min(m0 + row, M - 1);
+    d.yo[q] = (uint32_t)(ym * N * 2 + c * 16);
+    d.ypos[q] = spos(row, c);
+  }
+  {
+    const int64_t kc = min(k0 + 32 * (t & 7), K - 32);   // columns past K: any in-range block
+    const int64_t n = t >> 3;
+    d.kb = (uint32_t)(K >> 6);
+    d.co = (uint32_t)(n * (K / 2) + kc / 2);
+    d.ao = (uint32_t)(n * (K >> 6) + (kc >> 6));
+    d.ablk = d.ao;
+    d.cstride = (uint32_t)(32 * (K / 2));
+    d.astride = (uint32_t)(32 * (K >> 6));
+  }
+  d.nsub = (int)((N + 31) >> 5);
+  // A fragment i: as a source lane of its 16-lane group (g, sl) a lane reads
+  // row 8 (g >> 1) + (sl >> 2) and columns 128 wc + 32 i + 16 (g & 1) + 4 (sl & 3)
+  int ao[4];
+  {
+    const int g = lane >> 4, sl = lane & 15, n0 = 8 * (g >> 1) + (sl >> 2);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ao[i] = tpos(n0, wc * 8 + 2 * i + (g & 1)) + 8 * (sl & 3);
+  }
+  const FragOffs fo = frag_offs(lane);
+  const int bm = wr * 128 * 64;
 
   f32x16_t acc[4][4];
   zero_acc(acc);
 
-  BlockCodes bcA, bcB;
-  RTileRegs yr;
-  r_load(yr, dY, c.yo, 0, c.ybytes);
-  dx_wload(bcA, c, 0);
-  bcB = bcA;
-  if (c.nsteps > 1) dx_wload(bcB, c, 1);
-  {
-    const Nf4Table T = make_table(block_scale(bcA.q, bcA.s2));
-    dx_dequant(A0, c, bcA, T, 0, 8);
+  Codes cs[4];
+  YRegs ys[2];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) dx_load_codes(cs[p], d, p);
+  dx_load_y(ys[0], d, 0);
+  dx_store_y(smem, d, ys[0], 0);
+  dx_load_y(ys[0], d, 1);
+  dx_store_y(smem, d, ys[0], 1);
+  dx_load_y(ys[1], d, 2);   // stored by substep 0
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const Nf4Table T = make_table(block_scale(cs[p].q, cs[p].s2));
+    dx_produce(smem, cs[p], T, p, 0);
+    dx_produce(smem, cs[p], T, p, 1);
   }
-  r_store(B0, yr);
-  __syncthreads();
-
-  bf16x8_t fa[2][4], fb[2][4];
+  QLORA_WAIT(0, 0);
+  __builtin_amdgcn_s_barrier();
+  Frags F;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    fa[0][i] = t_frag(A0 + aoff[i], 0);
-    fb[0][i] = r_frag(B0 + boff + 32 * kRS * i, 0);
+    F.a0[i] = tfrag(smem + ao[i]);
+    F.b0[i] = rd16(smem + kOp + bm + i * 2048 + fo.o0);
   }
   int st = 0;
-  for (; st + 1 < c.nsteps; st += 2) {
-    dx_step(acc, fa, fb, c, st, A0, B0, A1, B1, bcB, bcA, yr, aoff, boff);
-    dx_step(acc, fa, fb, c, st + 1, A1, B1, A0, B0, bcA, bcB, yr, aoff, boff);
+#define QLORA_DX_SUB(u) dx_substep<u>(smem, d, st + u, acc, F, cs, ys, ao, bm, fo)
+  for (; st + 8 <= d.nsub; st += 8) {
+    QLORA_DX_SUB(0); QLORA_DX_SUB(1); QLORA_DX_SUB(2); QLORA_DX_SUB(3);
+    QLORA_DX_SUB(4); QLORA_DX_SUB(5); QLORA_DX_SUB(6); QLORA_DX_SUB(7);
   }
-  if (st < c.nsteps) dx_step(acc, fa, fb, c, st, A0, B0, A1, B1, bcB, bcA, yr, aoff, boff);
+  const int rem = d.nsub - st;
+  if (rem >= 1) QLORA_DX_SUB(0);
+  if (rem >= 2) QLORA_DX_SUB(1);
+  if (rem >= 3) QLORA_DX_SUB(2);
+  if (rem >= 4) QLORA_DX_SUB(3);
+  if (rem >= 5) QLORA_DX_SUB(4);
+  if (rem >= 6) QLORA_DX_SUB(5);
+  if (rem >= 7) QLORA_DX_SUB(6);
+#undef QLORA_DX_SUB
+  QLORA_WAIT(0, 0);
+  __builtin_amdgcn_s_barrier();
 
   if (r > 0) {
-    // acc += (s G) A over the rank: A [r x K] rows are contraction rows of
-    // the weight-side layout, copied without dequantization.
-    for (st = 0; st * 64 < r; ++st) {
+    // acc += (s G) A over the rank, 32 at a time: rows j of A are
+    // contraction rows of the weight half, copied without dequantization
+    for (int j0 = 0; j0 < r; j0 += 32) {
+      char* wb = smem;
+      char* yb = smem + kOp;
       {
-        const int64_t j = (int64_t)st * 64 + c.orow;
-        const bool ok = j < r && c.kvalid;
-        const bf16_t* src = Al + j * W.K + c.kcol;
+        const int n = t >> 3, jj = t & 7, flip = (t >> 2) & 1;
+        const int64_t row = j0 + n;
 #pragma unroll
-        for (int ch = 0; ch < 8; ++ch) {
+        for (int k = 0; k < 4; ++k) {
+          const int p = k ^ flip, ch = 4 * jj + p;
+          const int64_t col = k0 + 8 * ch;
           uint4 v = make_uint4(0u, 0u, 0u, 0u);
-          if (ok) v = *reinterpret_cast<const uint4*>(src + 8 * ch);
-          *reinterpret_cast<uint4*>(t_chunk(A0, c.orow, c.oblk, ch)) = v;
+          if (row < r && col < K) v = *reinterpret_cast<const uint4*>(Al + row * K + col);
+          wr16(wb + tpos(n, ch >> 1) + 16 * (ch & 1), v);
         }
       }
-      r_load_masked(yr, G, r, M, r, m0, st);
-      r_scale(yr, s);
-      r_store(B0, yr);
-      __syncthreads();
+      tail_tokens(yb, G, M, r, m0, j0, s);
+      QLORA_WAIT(0, 0);
+      __builtin_amdgcn_s_barrier();
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
+      for (int kk = 0; kk < 2; ++kk) {
+        const int o = kk ? fo.o1 : fo.o0;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          fa[0][i] = t_frag(A0 + aoff[i], kk);
-          fb[0][i] = r_frag(B0 + boff + 32 * kRS * i, kk);
+          F.a0[i] = tfrag(wb + ao[i] + kk * 16 * kWRow);
+          F.b0[i] = rd16(yb + bm + i * 2048 + o);
         }
-        mfma_block<4, 4>(acc, fa[0], fb[0]);
+        mfma_block<4, 4>(acc, F.a0, F.b0);
       }
-      __syncthreads();
+      QLORA_WAIT(0, 0);
+      __builtin_amdgcn_s_barrier();
     }
   }
-  store_acc_bf16(acc, dX, W.K, M, W.K, k0 + wc * 128, m0 + wr * 128);
+  store_tile(acc, dX, K, M, K, m0, k0);
 }
 
 }  // namespace
@@ -560,9 +650,9 @@ hipError_t launch_fwd(const Nf4View& W, const bf16_t* X, int64_t M, const bf16_t
   const int tiles_n = (int)((W.N + kTile - 1) / kTile);
   const int tiles_m = (int)((M + kTile - 1) / kTile);
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&nf4_fwd_kernel),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds);
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsFwd);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(nf4_fwd_kernel, dim3(tiles_n * tiles_m), dim3(kThreads), kLds, st, W, X, M, U, B, r, s, Y,
+  hipLaunchKernelGGL(nf4_fwd_kernel, dim3(tiles_n * tiles_m), dim3(kThreads), kLdsFwd, st, W, X, M, U, B, r, s, Y,
                      tiles_n, tiles_m);
   return hipGetLastError();
 }
@@ -572,9 +662,9 @@ hipError_t launch_dx(const Nf4View& W, const bf16_t* dY, int64_t M, const bf16_t
   const int tiles_k = (int)((W.K + kTile - 1) / kTile);
   const int tiles_m = (int)((M + kTile - 1) / kTile);
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&nf4_dx_kernel),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds);
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsDx);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(nf4_dx_kernel, dim3(tiles_k * tiles_m), dim3(kThreads), kLds, st, W, dY, M, G, A, r, s, dX,
+  hipLaunchKernelGGL(nf4_dx_kernel, dim3(tiles_k * tiles_m), dim3(kThreads), kLdsDx, st, W, dY, M, G, A, r, s, dX,
                      tiles_k, tiles_m);
   return hipGetLastError();
 }

@@ -59,8 +59,10 @@ typedef enum {
   QLORA_E_ALIGN = 2,       /* a pointer is not 16-byte aligned               */
   QLORA_E_SHAPE = 3,       /* a size is not positive, or sizes disagree      */
   QLORA_E_UNSUPPORTED = 4, /* blocksize != 64, group != 256, cols % 64 != 0
-                              on the GEMM/GEMV paths, r outside [0,128] or
-                              r % 8 != 0, too many jobs                     */
+                              on the GEMM/GEMV paths, rows % 8 != 0 or
+                              rows*cols/2 >= 2^32 on the GEMM paths, M*rows
+                              or M*cols >= 2^31 on the fused GEMMs, r
+                              outside [0,128] or r % 8 != 0, too many jobs */
   QLORA_E_WORKSPACE = 5,   /* ws_bytes smaller than qlora_workspace_bytes()  */
   QLORA_E_HIP = 6          /* a HIP launch/copy error; see qlora_last_hip_error */
 } qlora_status;
