@@ -73,6 +73,47 @@ def traffic_for(kernel):
     return e.get("hbm_bytes_per_launch")
 
 
+TRAFFIC_KERNELS = {"nf4_fwd_kernel": "fwd_kernel", "nf4_dx_kernel": "dx_kernel",
+                   "quantize_kernel": "quantize_kernel", "nf4_gemv_kernel": "gemv_kernel"}
+
+
+def summarize_pmc(fetch_csv, write_csv, copy_mib):
+    """Average FETCH_SIZE / WRITE_SIZE (KiB per dispatch) per kernel from two
+    rocprofv3 counter runs, each scaled by what the same counter reads for the
+    elementwise copy probe of known size (copy_mib MiB read and written)."""
+    import csv
+    import re
+
+    def per_kernel(path, counter):
+        acc = {}
+        for row in csv.DictReader(open(path)):
+            if row["Counter_Name"] != counter:
+                continue
+            name = row["Kernel_Name"]
+            m = re.search(r"(\w+_kernel)\b", name)
+            key = m.group(1) if m else name
+            if "neg_kernel" in name or ("elementwise" in name and "neg" in name):
+                key = "copy_probe"
+            acc.setdefault(key, {}).setdefault(row["Dispatch_Id"], 0.0)
+            acc[key][row["Dispatch_Id"]] += float(row["Counter_Value"])
+        return {k: sum(v.values()) / len(v) * 1024.0 for k, v in acc.items()}   # bytes per dispatch
+
+    fetch = per_kernel(fetch_csv, "FETCH_SIZE")
+    write = per_kernel(write_csv, "WRITE_SIZE")
+    probe = copy_mib * 1024 * 1024
+    f_scale = probe / fetch["copy_probe"]
+    w_scale = probe / write["copy_probe"]
+    out = {"_note": "HBM bytes per launch = FETCH_SIZE x fetch_scale + WRITE_SIZE x write_scale, averaged over "
+                    "the dispatches of one bench run; scales from an elementwise copy of copy_probe_bytes",
+           "copy_probe_bytes": probe, "fetch_scale": f_scale, "write_scale": w_scale}
+    for k, name in TRAFFIC_KERNELS.items():
+        if k in fetch and k in write:
+            out[name] = {"source_digest": source_digest(), "fetch_bytes_per_launch": fetch[k] * f_scale,
+                         "write_bytes_per_launch": write[k] * w_scale,
+                         "hbm_bytes_per_launch": fetch[k] * f_scale + write[k] * w_scale}
+    return out
+
+
 def cpu_baseline(lin, M, r, alpha, dev_tensors, min_seconds=10.0, max_reps=20):
     """fp64 oracle fwd+bwd on one linear of the workload (host cores)."""
     import numpy as np
@@ -114,7 +155,16 @@ def main():
     ap.add_argument("--decode-layers", type=int, default=80)
     ap.add_argument("--decode-passes", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="after the timed steps, run one elementwise copy (negation) of this many MiB: "
+                         "a kernel of known traffic for scaling the FETCH_SIZE / WRITE_SIZE counters")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="do not run: turn two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, "
+                         "WRITE_SIZE) of a --copy-probe-mib run into profiles/traffic.json on stdout")
     args = ap.parse_args()
+    if args.summarize_pmc:
+        print(json.dumps(summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.copy_probe_mib), indent=1))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
               "(sharding is described in DESIGN.md); use --gpus 1", file=sys.stderr)
@@ -201,6 +251,15 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
+
+    if args.copy_probe_mib > 0:
+        n = args.copy_probe_mib * 1024 * 1024 // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
 
     ph = {"quantize": 0.0, "forward": 0.0, "backward": 0.0, "decode_gemv": 0.0}
     fwd_ms, dx_ms = 0.0, 0.0

@@ -27,7 +27,7 @@ from .nf4 import nf4_levels, nf4_levels_fp64, q8_levels, NF4_OFFSET
 from .bf16 import f32_to_bf16_bits, bf16_bits_to_f32, bf16_bits_to_f64
 from .quant import (nf4_encode, q8_encode, quantize, dequant, storage_sizes,
                     BLOCKSIZE, GROUP_BLOCKS)
-from .linear import linear_fwd, linear_bwd, gemv, lora_scale
+from .linear import linear_fwd, linear_bwd, adapter_grads, gemv, lora_scale
 
 __all__ = [
     "nf4_levels", "nf4_levels_fp64", "q8_levels", "NF4_OFFSET",

@@ -45,6 +45,17 @@ def linear_fwd(Wd, X, A=None, B=None, alpha=0.0):
     return Y
 
 
+def adapter_grads(X, dY, A, B, alpha):
+    """(dA [r x K], dB [N x r]): the adapters' gradients, which do not involve
+    the frozen weight."""
+    X, dY, A, B = _f64(X), _f64(dY), _f64(A), _f64(B)
+    s = lora_scale(alpha, A.shape[0])
+    G = dY @ B                       # [M x r]
+    dA = s * (G.T @ X)
+    dB = s * (dY.T @ (X @ A.T))
+    return dA, dB
+
+
 def linear_bwd(Wd, X, dY, A=None, B=None, alpha=0.0):
     """Return (dX [M x K], dA [r x K] or None, dB [N x r] or None)."""
     Wd, X, dY, A, B = _f64(Wd), _f64(X), _f64(dY), _f64(A), _f64(B)
@@ -52,10 +63,8 @@ def linear_bwd(Wd, X, dY, A=None, B=None, alpha=0.0):
     if A is None or A.shape[0] == 0:
         return dX, None, None
     s = lora_scale(alpha, A.shape[0])
-    G = dY @ B                       # [M x r]
-    dX = dX + s * (G @ A)
-    dA = s * (G.T @ X)
-    dB = s * (dY.T @ (X @ A.T))
+    dX = dX + s * ((dY @ B) @ A)
+    dA, dB = adapter_grads(X, dY, A, B, alpha)
     return dX, dA, dB
 
 

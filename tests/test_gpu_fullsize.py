@@ -1,0 +1,90 @@
+"""GPU parity at the full layer shapes, in the launch configuration bench.py
+times (same seeds, sizes and calls).
+
+The oracle quantizes each whole weight (about 30 s for 1.8e8 weights) and
+computes, in fp64: the quantized storage of every group (bit-exact), Y and dX
+on sampled token rows (every column; rows are independent), and dA, dB in
+full.  The decode GEMV of one 65B-shaped layer set is checked on sampled
+output rows.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from bit_quantized_finetuning_nf4_amd import ops, synth
+from tests.helpers import assert_close, oracle_quantize_rows, torch_to_bits, torch_to_f64
+
+pytestmark = pytest.mark.gpu
+
+# (layer set, linear index): the 65B gate (the largest N) and down (the
+# largest K) projections, a 13B and a 7B projection
+CASES = [("llama65b", 4), ("llama65b", 6), ("llama13b", 4), ("llama7b", 6)]
+SET_INDEX = {"llama7b": 1, "llama13b": 2, "llama65b": 3}
+
+
+def _rows(M, n, seed):
+    rng = np.random.default_rng(seed)
+    inner = rng.choice(np.arange(1, M - 1), size=n - 2, replace=False)
+    return np.sort(np.concatenate([[0, M - 1], inner]))
+
+
+@pytest.mark.parametrize("set_name,li", CASES)
+def test_linear_full_shape(set_name, li):
+    cfg = synth.LAYER_SETS[set_name]
+    name, N, K = cfg["linears"][li]
+    M, r, alpha = cfg["M"], cfg["r"], cfg["alpha"]
+    label = f"{set_name} {name} {N}x{K} M={M} r={r}"
+    print(f"[full-size parity] {label}", flush=True)
+    t = synth.linear_inputs(N, K, M, r, synth.layer_set_seed(SET_INDEX[set_name], li), "cuda",
+                            outliers=cfg["outliers"])
+    q = ops.quantize(t["W"])
+    Y, U = ops.linear_fwd(q, t["X"], t["A"], t["B"], alpha, save_u=True)
+    dX, dA, dB = ops.linear_bwd(q, t["X"], t["dY"], t["A"], t["B"], alpha, U=U)
+    torch.cuda.synchronize()
+
+    # quantized storage: every byte against the oracle's quantization
+    w_bits = torch_to_bits(t["W"]).ravel()
+    codes, aq, s2 = oracle.quantize(w_bits)
+    assert np.array_equal(q.codes.cpu().numpy(), codes), f"{label}: NF4 codes differ"
+    assert np.array_equal(q.absmax_q.cpu().numpy(), aq), f"{label}: absmax codes differ"
+    assert np.array_equal(q.group_scale.cpu().numpy().view(np.uint32), s2.view(np.uint32)), \
+        f"{label}: group scales differ"
+    Wd = oracle.bf16_bits_to_f64(oracle.dequant(codes, aq, s2, w_bits.size)).reshape(N, K)
+
+    f64 = lambda k: torch_to_f64(t[k])
+    X, A, B, dY = f64("X"), f64("A"), f64("B"), f64("dY")
+    rows = _rows(M, 48, N + K)
+    Yr = oracle.linear_fwd(Wd, X[rows], A, B, alpha)
+    dXr, _, _ = oracle.linear_bwd(Wd, X[rows], dY[rows], A, B, alpha)
+    dAr, dBr = oracle.adapter_grads(X, dY, A, B, alpha)
+    assert_close(torch_to_f64(Y)[rows], Yr, f"{label} Y (48 rows)")
+    assert_close(torch_to_f64(dX)[rows], dXr, f"{label} dX (48 rows)")
+    assert_close(torch_to_f64(dA), dAr, f"{label} dA")
+    assert_close(torch_to_f64(dB), dBr, f"{label} dB")
+
+
+def test_decode_gemv_65b_layer_set():
+    cfg = synth.LAYER_SETS["llama65b"]
+    r, alpha = cfg["r"], cfg["alpha"]
+    x_attn = synth.normal_bf16((8192,), 1.0, 10_000_000, "cuda")
+    x_down = synth.normal_bf16((22016,), 1.0, 10_000_001, "cuda")
+    jobs, data = [], []
+    for i, (name, N, K) in enumerate(cfg["linears"]):
+        seed = synth.layer_set_seed(4, i, layer=1)
+        W = synth.normal_bf16((N, K), 0.02, seed * 16, "cuda", outliers=cfg["outliers"])
+        A = synth.normal_bf16((r, K), 0.01, seed * 16 + 1, "cuda")
+        B = synth.normal_bf16((N, r), 0.01, seed * 16 + 2, "cuda")
+        x = x_down if name == "down" else x_attn
+        q = ops.quantize(W)
+        jobs.append(ops.GemvJob(q, x, A, B, alpha))
+        data.append((name, N, K, torch_to_bits(W).ravel(), x, A, B))
+    ys = ops.gemv(jobs)
+    torch.cuda.synchronize()
+    for (name, N, K, w_bits, x, A, B), y in zip(data, ys):
+        rows = _rows(N, 64, N + K + 7)
+        deq = oracle_quantize_rows(w_bits, K, rows)
+        Wd = np.stack([deq[n] for n in rows])
+        yr = oracle.gemv(Wd, torch_to_f64(x), torch_to_f64(A), torch_to_f64(B)[rows], alpha)
+        assert_close(torch_to_f64(y)[rows], yr, f"decode {name} {N}x{K} (64 rows)")
