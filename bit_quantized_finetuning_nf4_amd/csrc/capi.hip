@@ -368,6 +368,9 @@ qlora_status qlora_gemv(const qlora_gemv_job* jobs, int32_t njobs, void* ws, siz
     qlora_status st = check_weight(J.W);
     if (st != QLORA_OK) return st;
     if (J.W->cols % 64 != 0 || J.W->cols > kMaxGemvCols || J.W->rows > 0x7FFFFFFF) return QLORA_E_UNSUPPORTED;
+    // codes addressed with 32-bit byte offsets, including a prefetch of up to
+    // four blocks past the last row
+    if (J.W->rows > ((int64_t)0xFFFFFFFF - 256) / (J.W->cols / 2)) return QLORA_E_UNSUPPORTED;
     if (!J.x || !J.y) return QLORA_E_NULL;
     if (!aligned16(J.x) || !aligned16(J.y)) return QLORA_E_ALIGN;
     if ((st = check_rank(J.r, J.A, J.B)) != QLORA_OK) return st;

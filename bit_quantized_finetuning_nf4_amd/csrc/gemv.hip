@@ -11,11 +11,11 @@
 //     the block's fp32 partial dot product afterwards;
 //   * the multiply-adds run on the matrix cores: v_mfma_f32_32x32x16_bf16
 //     with the decoded weights as the B operand (lane j <-> weight row j)
-//     and x as A-operand row bi for block bi of the iteration, so one
-//     accumulator tile collects four blocks' partial dots in rows 0..3;
+//     and x broadcast to every row of the A operand, a fresh accumulator per
+//     block;
 //   * a workgroup of 4 waves owns 128 weight rows; each lane pair (j, j+32)
 //     streams the two 16-byte halves of each block of row j, so a wave reads
-//     whole 128-byte lines.
+//     whole 128-byte lines over four blocks.
 // x is staged once per workgroup in LDS, with each group of 8 elements in
 // the order (0,2,4,6,1,3,5,7) that the decoder produces.
 #include "device.h"
@@ -25,7 +25,7 @@ namespace qlora {
 
 constexpr int kGemvThreads = 256;
 constexpr int kGemvRows = 128;       // weight rows per workgroup
-constexpr int kDownRows = 16;        // LoRA-A rows per workgroup in phase 1
+constexpr int kDownRows = 4;         // LoRA-A rows per workgroup in phase 1 (one per wave)
 constexpr int kMaxBatch = 24;        // jobs per launch (kernel-argument batch)
 
 struct GemvBatch {
@@ -33,6 +33,20 @@ struct GemvBatch {
   int wg_begin[kMaxBatch + 1];
   int njobs;
 };
+
+namespace {
+
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// Raw buffer resource over `bytes` bytes: loads past the end return zero.
+__device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 buf_load16(rsrc_t r, uint32_t voff) {
+  const u32x4_t v = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
 
 __device__ __forceinline__ int find_job(const GemvBatch& b) {
   int j = 0;
@@ -45,54 +59,71 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-// Phase 1: u = A x for every job with r > 0 (fp32, into the job's scratch).
+__device__ __forceinline__ float dot8(uint4 a, uint4 x) {
+  const uint32_t aw[4] = {a.x, a.y, a.z, a.w}, xw[4] = {x.x, x.y, x.z, x.w};
+  float s = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    s += bf2f(aw[e] & 0xFFFFu) * bf2f(xw[e] & 0xFFFFu);
+    s += bf2f(aw[e] >> 16) * bf2f(xw[e] >> 16);
+  }
+  return s;
+}
+
+// Decode 8 codes into bf16 pairs in the order {0,2},{4,6},{1,3},{5,7}.
+__device__ __forceinline__ bf16x8_t dequant8_eo(uint32_t c, const Nf4Table& T) {
+  uint32_t le, he, lo, ho;
+  lookup4(c & 0x0F0F0F0Fu, T, le, he);
+  lookup4((c >> 4) & 0x0F0F0F0Fu, T, lo, ho);
+  return __builtin_bit_cast(bf16x8_t, make_uint4(perm(he, le, 0x05010400u), perm(he, le, 0x07030602u),
+                                                 perm(ho, lo, 0x05010400u), perm(ho, lo, 0x07030602u)));
+}
+
+}  // namespace
+
+// Phase 1: u = A x for every job with r > 0 (fp32, into the job's scratch);
+// one wave per adapter row, four 16-byte loads of A and x in flight per lane.
 __global__ __launch_bounds__(kGemvThreads) void lora_down_kernel(GemvBatch b) {
   const int j = find_job(b);
   const GemvJob& J = b.jobs[j];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int row0 = (blockIdx.x - b.wg_begin[j]) * kDownRows + 4 * w;
-  float acc[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int k = lane * 8; k < J.K; k += 512) {
-    const uint4 xv = *reinterpret_cast<const uint4*>(J.x + k);
-    const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+  const int row = (blockIdx.x - b.wg_begin[j]) * kDownRows + w;
+  if (row >= J.r) return;   // uniform per wave; the kernel has no barrier
+  const bf16_t* a = J.A + (int64_t)row * J.K;
+  float acc = 0.0f;
+  for (int k0 = lane * 8; k0 < J.K; k0 += 4 * 512) {
+    uint4 av[4], xv[4];
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const int row = row0 + rr;
-      if (row < J.r) {
-        const uint4 av = *reinterpret_cast<const uint4*>(J.A + (int64_t)row * J.K + k);
-        const uint32_t aw[4] = {av.x, av.y, av.z, av.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          acc[rr] += bf2f(aw[e] & 0xFFFFu) * bf2f(xw[e] & 0xFFFFu);
-          acc[rr] += bf2f(aw[e] >> 16) * bf2f(xw[e] >> 16);
-        }
+    for (int u = 0; u < 4; ++u) {
+      const int k = k0 + 512 * u;
+      av[u] = xv[u] = make_uint4(0u, 0u, 0u, 0u);
+      if (k < J.K) {
+        av[u] = *reinterpret_cast<const uint4*>(a + k);
+        xv[u] = *reinterpret_cast<const uint4*>(J.x + k);
       }
     }
-  }
 #pragma unroll
-  for (int rr = 0; rr < 4; ++rr) {
-    const float v = wave_sum(acc[rr]);
-    if (lane == 0 && row0 + rr < J.r) J.u[row0 + rr] = v;
+    for (int u = 0; u < 4; ++u) acc += dot8(av[u], xv[u]);
   }
-}
-
-// Decode 8 codes into bf16 pairs in the order {0,2},{4,6},{1,3},{5,7}.
-__device__ __forceinline__ void dequant8_eo(uint32_t c, const Nf4Table& T, uint32_t out[4]) {
-  uint32_t le, he, lo, ho;
-  lookup4(c & 0x0F0F0F0Fu, T, le, he);
-  lookup4((c >> 4) & 0x0F0F0F0Fu, T, lo, ho);
-  out[0] = perm(he, le, 0x05010400u);
-  out[1] = perm(he, le, 0x07030602u);
-  out[2] = perm(ho, lo, 0x05010400u);
-  out[3] = perm(ho, lo, 0x07030602u);
+  acc = wave_sum(acc);
+  if (lane == 0) J.u[row] = acc;
 }
 
 // Phase 2: the NF4 GEMV with the LoRA up-projection in the epilogue.
+//
+// Wave w of a workgroup owns weight rows 32 w .. 32 w + 31 of the group's
+// 128; lanes j and j + 32 stream the two 16-byte halves of each block of row
+// j.  Per block, four MFMAs take x (broadcast to every row of the A operand)
+// against the decoded unscaled levels of the 32 rows (B operand), starting
+// from a zero accumulator, so every row of the result holds the 32 rows'
+// partial dot products for the block; the block scale multiplies them in
+// fp32.  The codes of the next four blocks are in flight while the current
+// four are decoded.
 __global__ __launch_bounds__(kGemvThreads) void nf4_gemv_kernel(GemvBatch b) {
   extern __shared__ __align__(16) uint32_t xs[];  // K/2 dwords
   const int j = find_job(b);
   const GemvJob& J = b.jobs[j];
-  const int K = J.K, N = J.N;
+  const int K = J.K, N = J.N, nblk = K >> 6;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int jr = lane & 31, h = lane >> 5;
 
@@ -107,57 +138,60 @@ __global__ __launch_bounds__(kGemvThreads) void nf4_gemv_kernel(GemvBatch b) {
 
   const Nf4Table T = make_table(1.0f);  // bf16 of the unscaled levels
   const int64_t n = (int64_t)(blockIdx.x - b.wg_begin[j]) * kGemvRows + 32 * w + jr;
-  const bool valid = n < N;
-  const int nblk = K >> 6;
-  const uint8_t* crow = J.codes + (n * K >> 1) + 16 * h;
-  const int64_t brow = n * nblk;
-  const bool quad_aligned = (nblk & 3) == 0;
+  // Rows past N address the first byte past the arrays: the range check
+  // returns zero codes and absmax code 0, i.e. block scale 0.
+  const int64_t nc = n < N ? n : N;
+  const int64_t nb = (int64_t)N * nblk;
+  const rsrc_t cr = make_rsrc(J.codes, (uint32_t)(nb * 32));
+  const rsrc_t ar = make_rsrc(J.absmax_q, (uint32_t)nb);
+  const uint32_t crow = (uint32_t)(nc * nblk * 32) + 16u * h;
+  const uint32_t brow = (uint32_t)(nc * nblk);
+  const bool quad = (nblk & 3) == 0;
   float acc = 0.0f;
 
+  uint4 cw[4];
+#pragma unroll
+  for (int bi = 0; bi < 4; ++bi) cw[bi] = buf_load16(cr, crow + 32u * bi);
   for (int b0 = 0; b0 < nblk; b0 += 4) {
-    uint4 cw[4];
+    // scales of blocks b0 .. b0+3 (zero past the last block)
+    float t[4];
+    if (quad) {
+      const uint32_t q4 = __builtin_amdgcn_raw_buffer_load_b32(ar, brow + b0, 0, 0);
+      const float s2 = J.group_scale[(brow + b0 < nb ? brow + b0 : nb - 1) >> 8];
 #pragma unroll
-    for (int bi = 0; bi < 4; ++bi) {
-      if (valid && b0 + bi < nblk) {
-        cw[bi] = *reinterpret_cast<const uint4*>(crow + 32 * (b0 + bi));
-      } else {
-        cw[bi].x = cw[bi].y = cw[bi].z = cw[bi].w = 0x77777777u;  // code 7 = level 0
+      for (int bi = 0; bi < 4; ++bi) t[bi] = block_scale((q4 >> (8 * bi)) & 0xFFu, s2);
+    } else {
+#pragma unroll
+      for (int bi = 0; bi < 4; ++bi) {
+        const uint32_t blk = brow + b0 + bi;
+        const uint32_t q = __builtin_amdgcn_raw_buffer_load_b8(ar, blk, 0, 0);
+        const float s2 = J.group_scale[(blk < nb ? blk : nb - 1) >> 8];
+        t[bi] = b0 + bi < nblk ? block_scale(q, s2) : 0.0f;
       }
     }
-    float t[4] = {0.f, 0.f, 0.f, 0.f};
-    if (valid) {
-      if (quad_aligned) {
-        const uint32_t q4 = *reinterpret_cast<const uint32_t*>(J.absmax_q + brow + b0);
-        const float s2 = J.group_scale[(brow + b0) >> 8];
+    // codes of the next four blocks (past the row end they are never used)
+    uint4 cn[4];
 #pragma unroll
-        for (int bi = 0; bi < 4; ++bi) t[bi] = block_scale((q4 >> (8 * bi)) & 0xFFu, s2);
-      } else {
-#pragma unroll
-        for (int bi = 0; bi < 4; ++bi)
-          if (b0 + bi < nblk)
-            t[bi] = block_scale(J.absmax_q[brow + b0 + bi], J.group_scale[(brow + b0 + bi) >> 8]);
-      }
-    }
-    f32x16_t C;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) C[e] = 0.0f;
+    for (int bi = 0; bi < 4; ++bi) cn[bi] = buf_load16(cr, crow + 32u * (b0 + 4 + bi));
 #pragma unroll
     for (int bi = 0; bi < 4; ++bi) {
+      if (b0 + bi >= nblk) break;   // uniform: a ragged last quad of blocks
+      const uint32_t* xb = xs + 32 * (b0 + bi) + 16 * h;
       const uint32_t words[4] = {cw[bi].x, cw[bi].y, cw[bi].z, cw[bi].w};
+      f32x16_t D = {};
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
-        uint32_t o[4];
-        dequant8_eo(words[kk], T, o);
-        const bf16x8_t bop = __builtin_bit_cast(bf16x8_t, make_uint4(o[0], o[1], o[2], o[3]));
-        uint4 av = make_uint4(0u, 0u, 0u, 0u);
-        if (jr == bi && b0 + bi < nblk) av = *reinterpret_cast<const uint4*>(xs + 32 * (b0 + bi) + 16 * h + 4 * kk);
-        C = mfma32x32x16(__builtin_bit_cast(bf16x8_t, av), bop, C);
+        const bf16x8_t xa = *reinterpret_cast<const bf16x8_t*>(xb + 4 * kk);
+        D = mfma32x32x16(xa, dequant8_eo(words[kk], T), D);
       }
+      acc += t[bi] * D[0];
     }
-    acc += t[0] * C[0] + t[1] * C[1] + t[2] * C[2] + t[3] * C[3];
+#pragma unroll
+    for (int bi = 0; bi < 4; ++bi) cw[bi] = cn[bi];
   }
 
   // LoRA up-projection: lanes j and j+32 take alternate groups of 8 ranks
+  const bool valid = n < N;
   float lora = 0.0f;
   if (J.r > 0 && valid) {
     const bf16_t* brp = J.B + n * J.r;
