@@ -7,11 +7,12 @@
 //   FWD  (r > 0): U bf16 [M x r] | split partials of X A^T (fp32)
 //   BWD  (r > 0): G bf16 [M x r] | U bf16 [M x r] | split partials (fp32,
 //                 the largest of X A^T, dY B, G^T X, dY^T U)
-//   GEMV        : per job, 128 fp32 for u = A x
+//   GEMV        : per job, 128 fp32 for u = A x | the device job table
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
 #include <cstring>
+#include <vector>
 
 #include "../../include/qlora.h"
 #include "kernels.h"
@@ -25,7 +26,7 @@ thread_local int g_last_hip_error = 0;
 constexpr size_t kAlign = 256;
 constexpr int kMaxRank = 128;
 constexpr int kMaxJobs = 4096;
-constexpr int64_t kMaxGemvCols = 65536;
+constexpr int64_t kMaxGemvCols = 32768;  // x is staged whole in LDS beside the 64 KiB table
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -184,8 +185,8 @@ size_t qlora_workspace_bytes(qlora_op op, int64_t M, int64_t N, int64_t K, int32
       if (M <= 0 || N <= 0 || K <= 0 || r < 0 || r > kMaxRank) return 0;
       return bwd_layout(M, N, K, r).total;
     case QLORA_OP_GEMV:
-      if (njobs <= 0 || njobs > kMaxJobs) return 0;
-      return (size_t)njobs * kMaxRank * sizeof(float);
+      if (njobs <= 0 || njobs > kMaxJobs || N <= 0) return 0;
+      return align_up((size_t)njobs * kMaxRank * sizeof(float)) + gemv_table_bound(njobs, N);
     case QLORA_OP_LORA:
       if (M <= 0 || N <= 0 || K <= 0 || r < 0 || r > kMaxRank) return 0;
       return lora_part_bytes(M, N, K, r);
@@ -361,51 +362,40 @@ qlora_status qlora_gemv(const qlora_gemv_job* jobs, int32_t njobs, void* ws, siz
   if (!jobs) return QLORA_E_NULL;
   if (njobs <= 0) return QLORA_E_SHAPE;
   if (njobs > kMaxJobs) return QLORA_E_UNSUPPORTED;
-  const size_t need = (size_t)njobs * kMaxRank * sizeof(float);
-  bool any_rank = false;
   for (int i = 0; i < njobs; ++i) {
     const qlora_gemv_job& J = jobs[i];
     qlora_status st = check_weight(J.W);
     if (st != QLORA_OK) return st;
     if (J.W->cols % 64 != 0 || J.W->cols > kMaxGemvCols || J.W->rows > 0x7FFFFFFF) return QLORA_E_UNSUPPORTED;
-    // codes addressed with 32-bit byte offsets, including a prefetch of up to
-    // four blocks past the last row
-    if (J.W->rows > ((int64_t)0xFFFFFFFF - 256) / (J.W->cols / 2)) return QLORA_E_UNSUPPORTED;
+    // codes addressed with 32-bit byte offsets, including the prefetch of
+    // one row's worth of blocks past the last row
+    if (J.W->rows + 1 > ((int64_t)0xFFFFFFFF - 256) / (J.W->cols / 2)) return QLORA_E_UNSUPPORTED;
     if (!J.x || !J.y) return QLORA_E_NULL;
     if (!aligned16(J.x) || !aligned16(J.y)) return QLORA_E_ALIGN;
     if ((st = check_rank(J.r, J.A, J.B)) != QLORA_OK) return st;
-    any_rank = any_rank || J.r > 0;
   }
-  if (any_rank) {
-    if (ws_bytes < need) return QLORA_E_WORKSPACE;
-    if (!ws) return QLORA_E_NULL;
-    if (!aligned16(ws)) return QLORA_E_ALIGN;
+  if (!ws) return QLORA_E_NULL;
+  if (!aligned16(ws)) return QLORA_E_ALIGN;
+  std::vector<GemvJob> buf((size_t)njobs);
+  for (int i = 0; i < njobs; ++i) {
+    const qlora_gemv_job& J = jobs[i];
+    GemvJob& D = buf[(size_t)i];
+    D.codes = J.W->codes;
+    D.absmax_q = J.W->absmax_q;
+    D.group_scale = J.W->group_scale;
+    D.x = J.x;
+    D.A = J.r > 0 ? J.A : nullptr;
+    D.B = J.r > 0 ? J.B : nullptr;
+    D.y = J.y;
+    D.u = J.r > 0 ? reinterpret_cast<float*>(ws_at(ws, (size_t)i * kMaxRank * sizeof(float))) : nullptr;
+    D.N = (int32_t)J.W->rows;
+    D.K = (int32_t)J.W->cols;
+    D.r = J.r;
+    D.s = J.r > 0 ? (float)((double)J.alpha / (double)J.r) : 0.0f;
   }
-  // Convert in chunks to keep the host copy small.
-  constexpr int kChunk = 240;
-  GemvJob buf[kChunk];
-  for (int base = 0; base < njobs; base += kChunk) {
-    const int cnt = std::min(kChunk, njobs - base);
-    for (int i = 0; i < cnt; ++i) {
-      const qlora_gemv_job& J = jobs[base + i];
-      GemvJob& D = buf[i];
-      D.codes = J.W->codes;
-      D.absmax_q = J.W->absmax_q;
-      D.group_scale = J.W->group_scale;
-      D.x = J.x;
-      D.A = J.r > 0 ? J.A : nullptr;
-      D.B = J.r > 0 ? J.B : nullptr;
-      D.y = J.y;
-      D.u = J.r > 0 ? reinterpret_cast<float*>(ws_at(ws, (size_t)(base + i) * kMaxRank * sizeof(float))) : nullptr;
-      D.N = (int32_t)J.W->rows;
-      D.K = (int32_t)J.W->cols;
-      D.r = J.r;
-      D.s = J.r > 0 ? (float)((double)J.alpha / (double)J.r) : 0.0f;
-    }
-    qlora_status st = hip_status(launch_gemv(buf, cnt, (hipStream_t)stream));
-    if (st != QLORA_OK) return st;
-  }
-  return QLORA_OK;
+  const size_t u_bytes = align_up((size_t)njobs * kMaxRank * sizeof(float));
+  if (ws_bytes < u_bytes || ws_bytes - u_bytes < gemv_table_bytes(buf.data(), njobs)) return QLORA_E_WORKSPACE;
+  return hip_status(launch_gemv(buf.data(), njobs, ws_at(ws, u_bytes), (hipStream_t)stream));
 }
 
 }  // extern "C"

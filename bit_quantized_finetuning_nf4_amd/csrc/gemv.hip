@@ -4,37 +4,50 @@
 // an 8-16x speed-up is expected; glossary "QLoRA", Definition: the frozen
 // weights are 4-bit NF4 with double-quantized constants.
 //
-// The product streams 0.516 bytes per weight from HBM, so the kernel is
-// built around the per-weight ALU cost of decoding:
-//   * codes are decoded by byte permutes against the constant table of the
-//     16 unscaled levels in bf16; the block scale t = Q8[q] s2 multiplies
-//     the block's fp32 partial dot product afterwards;
-//   * the multiply-adds run on the matrix cores: v_mfma_f32_32x32x16_bf16
-//     with the decoded weights as the B operand (lane j <-> weight row j)
-//     and x broadcast to every row of the A operand, a fresh accumulator per
-//     block;
-//   * a workgroup of 4 waves owns 128 weight rows; each lane pair (j, j+32)
-//     streams the two 16-byte halves of each block of row j, so a wave reads
-//     whole 128-byte lines over four blocks.
-// x is staged once per workgroup in LDS, with each group of 8 elements in
-// the order (0,2,4,6,1,3,5,7) that the decoder produces.
+// The product streams 0.516 bytes per weight from HBM.  A wave64 VALU
+// instruction costs four cycles on a 16-lane SIMD, so at 8 TB/s a decode
+// that spends more than about three lane-instructions per weight becomes the
+// bound.  This kernel spends one v_perm and one LDS read per two weights:
+//
+//   * LDS lookup table.  Entry e (a code byte: two weights) is the bf16 pair
+//     {L[e & 15], L[e >> 4]} of unscaled levels.  The 256 entries are stored
+//     once per lane column: entry e of column c sits at byte e*256 + c*4, so
+//     lane c always reads bank c and a wave's 64 lookups never conflict
+//     (64 KiB).  One v_perm builds the address from a code byte and the lane
+//     column; one ds_read_b32 returns two ready bf16 weights.
+//   * MFMA v_mfma_f32_16x16x32_bf16.  Lane l = (n, q), n = l % 16, q = l / 16,
+//     supplies B operand column n (weight row n of its 16-row group) for one
+//     NF4 block, the block 4s + q of step s; eight MFMAs cover the block's
+//     64 weights.  The A operand is "diagonal": rows 4q .. 4q+3 of A hold x
+//     over block 4s + q and zero elsewhere.  Row m of the 16 x 16 result is
+//     then the partial dot product of weight row n with block 4s + m/4 alone,
+//     so every lane finds its own block's partial in its accumulator and
+//     applies that block's scale t = Q8[q_b] s2 in fp32.
+//   * x is staged in LDS (zero-padded to whole four-block steps) behind the
+//     table, with a 128-byte zero run for the off-diagonal A lanes.
+//
+// The job table lives in device memory (written by one copy per call), so
+// one launch covers every job and the partial last wave of workgroups is
+// paid once per call instead of once per small batch.
+#include <cstring>
+#include <vector>
+
 #include "device.h"
 #include "kernels.h"
 
 namespace qlora {
 
-constexpr int kGemvThreads = 256;
-constexpr int kGemvRows = 128;       // weight rows per workgroup
-constexpr int kDownRows = 4;         // LoRA-A rows per workgroup in phase 1 (one per wave)
-constexpr int kMaxBatch = 24;        // jobs per launch (kernel-argument batch)
-
-struct GemvBatch {
-  GemvJob jobs[kMaxBatch];
-  int wg_begin[kMaxBatch + 1];
-  int njobs;
-};
-
 namespace {
+
+constexpr int kGvWaves = 16;                               // waves per workgroup
+constexpr int kGvThreads = 64 * kGvWaves;
+constexpr int kGvGroups = 2;                               // 16-row groups per wave
+constexpr int kGvRows = kGvWaves * 16 * kGvGroups;         // weight rows per workgroup
+constexpr int kLutBytes = 256 * 64 * 4;                    // 256 entries x 64 lane columns
+constexpr int kZeroBytes = 128;
+constexpr int kDownThreads = 256;
+constexpr int kDownRows = 4;                               // adapter rows per workgroup (one per wave)
+static_assert(kGvThreads == 1024, "the table fill below assumes 16 waves");
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
@@ -48,17 +61,6 @@ __device__ __forceinline__ uint4 buf_load16(rsrc_t r, uint32_t voff) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
-__device__ __forceinline__ int find_job(const GemvBatch& b) {
-  int j = 0;
-  while (j + 1 < b.njobs && (int)blockIdx.x >= b.wg_begin[j + 1]) ++j;
-  return j;
-}
-
-__device__ __forceinline__ float wave_sum(float v) {
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-  return v;
-}
-
 __device__ __forceinline__ float dot8(uint4 a, uint4 x) {
   const uint32_t aw[4] = {a.x, a.y, a.z, a.w}, xw[4] = {x.x, x.y, x.z, x.w};
   float s = 0.0f;
@@ -70,24 +72,49 @@ __device__ __forceinline__ float dot8(uint4 a, uint4 x) {
   return s;
 }
 
-// Decode 8 codes into bf16 pairs in the order {0,2},{4,6},{1,3},{5,7}.
-__device__ __forceinline__ bf16x8_t dequant8_eo(uint32_t c, const Nf4Table& T) {
-  uint32_t le, he, lo, ho;
-  lookup4(c & 0x0F0F0F0Fu, T, le, he);
-  lookup4((c >> 4) & 0x0F0F0F0Fu, T, lo, ho);
-  return __builtin_bit_cast(bf16x8_t, make_uint4(perm(he, le, 0x05010400u), perm(he, le, 0x07030602u),
-                                                 perm(ho, lo, 0x05010400u), perm(ho, lo, 0x07030602u)));
+__device__ __forceinline__ float wave_sum(float v) {
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// bf16 (round to nearest even) of the unscaled NF4 level c.
+__device__ __forceinline__ uint32_t level_bf16(int c) {
+  return pack_bf16x2(u2f(kNf4LevelBits[c]), 0.0f) & 0xFFFFu;
+}
+
+__device__ __forceinline__ f32x4_t mfma16x16x32(const bf16x8_t& a, const bf16x8_t& b, const f32x4_t& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// The kernel has no static LDS, so its dynamic LDS starts at address 0 and
+// plain 32-bit LDS addresses index it (no base add per access).
+typedef __attribute__((address_space(3))) uint32_t lds_u32;
+typedef __attribute__((address_space(3))) u32x4_t lds_u128;
+__device__ __forceinline__ uint32_t lds_ld32(uint32_t addr) { return *(const lds_u32*)(size_t)addr; }
+__device__ __forceinline__ u32x4_t lds_ld128(uint32_t addr) { return *(const lds_u128*)(size_t)addr; }
+__device__ __forceinline__ void lds_st32(uint32_t addr, uint32_t v) { *(lds_u32*)(size_t)addr = v; }
+__device__ __forceinline__ void lds_st128(uint32_t addr, uint4 v) {
+  *(lds_u128*)(size_t)addr = u32x4_t{v.x, v.y, v.z, v.w};
+}
+
+// Eight weights (one code dword, element i in nibble i) -> bf16 x 8.  Table
+// address of code byte i: byte << 8 | lane column << 2, built by one v_perm.
+__device__ __forceinline__ bf16x8_t decode8(uint32_t c, uint32_t col) {
+  const uint4 v = make_uint4(lds_ld32(perm(c, col, 0x0C0C0400u)), lds_ld32(perm(c, col, 0x0C0C0500u)),
+                             lds_ld32(perm(c, col, 0x0C0C0600u)), lds_ld32(perm(c, col, 0x0C0C0700u)));
+  return __builtin_bit_cast(bf16x8_t, v);
 }
 
 }  // namespace
 
 // Phase 1: u = A x for every job with r > 0 (fp32, into the job's scratch);
 // one wave per adapter row, four 16-byte loads of A and x in flight per lane.
-__global__ __launch_bounds__(kGemvThreads) void lora_down_kernel(GemvBatch b) {
-  const int j = find_job(b);
-  const GemvJob& J = b.jobs[j];
+__global__ __launch_bounds__(kDownThreads) void lora_down_kernel(const GemvJob* __restrict__ jobs,
+                                                                 const int2* __restrict__ map) {
+  const int2 m = map[blockIdx.x];
+  const GemvJob& J = jobs[m.x];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int row = (blockIdx.x - b.wg_begin[j]) * kDownRows + w;
+  const int row = m.y * kDownRows + w;
   if (row >= J.r) return;   // uniform per wave; the kernel has no barrier
   const bf16_t* a = J.A + (int64_t)row * J.K;
   float acc = 0.0f;
@@ -110,144 +137,200 @@ __global__ __launch_bounds__(kGemvThreads) void lora_down_kernel(GemvBatch b) {
 }
 
 // Phase 2: the NF4 GEMV with the LoRA up-projection in the epilogue.
-//
-// Wave w of a workgroup owns weight rows 32 w .. 32 w + 31 of the group's
-// 128; lanes j and j + 32 stream the two 16-byte halves of each block of row
-// j.  Per block, four MFMAs take x (broadcast to every row of the A operand)
-// against the decoded unscaled levels of the 32 rows (B operand), starting
-// from a zero accumulator, so every row of the result holds the 32 rows'
-// partial dot products for the block; the block scale multiplies them in
-// fp32.  The codes of the next four blocks are in flight while the current
-// four are decoded.
-__global__ __launch_bounds__(kGemvThreads) void nf4_gemv_kernel(GemvBatch b) {
-  extern __shared__ __align__(16) uint32_t xs[];  // K/2 dwords
-  const int j = find_job(b);
-  const GemvJob& J = b.jobs[j];
+// Workgroup = (job, tile of kGvRows rows); wave w owns rows
+// tile*kGvRows + 32w .. +31 as two 16-row groups.
+__global__ __launch_bounds__(kGvThreads) void nf4_gemv_kernel(const GemvJob* __restrict__ jobs,
+                                                              const int2* __restrict__ map) {
+  extern __shared__ __align__(16) uint8_t lds_dyn[];  // addressed from 0 (see lds_ld32)
+  const int2 m = map[blockIdx.x];
+  const GemvJob& J = jobs[m.x];
   const int K = J.K, N = J.N, nblk = K >> 6;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int jr = lane & 31, h = lane >> 5;
+  const int nsteps = (nblk + 3) >> 2;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int nl = lane & 15, q = lane >> 4;
+  const uint32_t xoff = kLutBytes, zoff = kLutBytes + (uint32_t)nsteps * 512u;
 
-  // stage x, each group of 8 reordered to (0,2,4,6,1,3,5,7)
-  for (int i = threadIdx.x; i < K / 8; i += kGemvThreads) {
-    const uint4 v = *reinterpret_cast<const uint4*>(J.x + 8 * i);
-    *reinterpret_cast<uint4*>(xs + 4 * i) =
-        make_uint4(perm(v.y, v.x, 0x05040100u), perm(v.w, v.z, 0x05040100u), perm(v.y, v.x, 0x07060302u),
-                   perm(v.w, v.z, 0x07060302u));
+  const uint32_t nb = (uint32_t)N * (uint32_t)nblk;
+  const rsrc_t cr = make_rsrc(J.codes, nb * 32u);
+  const rsrc_t ar = make_rsrc(J.absmax_q, nb);
+  const rsrc_t sr = make_rsrc(J.group_scale, ((nb + 255u) >> 8) * 4u);
+
+  // Per group: the lane's row (rows past N read the first byte past the
+  // arrays: zero codes, absmax code 0 and so block scale 0) and the offset
+  // of its first block, 4s + q at s = 0.
+  int row[kGvGroups];
+  uint32_t bidx[kGvGroups];
+#pragma unroll
+  for (int g = 0; g < kGvGroups; ++g) {
+    row[g] = m.y * kGvRows + w * (16 * kGvGroups) + 16 * g + nl;
+    bidx[g] = (uint32_t)(row[g] < N ? row[g] : N) * (uint32_t)nblk + (uint32_t)q;
   }
+
+  // codes of step 0, in flight during the prologue
+  uint4 c0[kGvGroups], c1[kGvGroups];
+#pragma unroll
+  for (int g = 0; g < kGvGroups; ++g) {
+    c0[g] = buf_load16(cr, bidx[g] * 32u);
+    c1[g] = buf_load16(cr, bidx[g] * 32u + 16u);
+  }
+
+  // table: thread (w, lane) writes entries e = w + 16 i, column lane
+  {
+    const uint32_t lo = level_bf16(w);
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      lds_st32((uint32_t)(w + 16 * i) * 256u + 4u * lane, lo | (level_bf16(i) << 16));
+  }
+  // x, zero-padded to nsteps * 256 elements, then the zero run
+  for (int i = tid; i < nsteps * 32; i += kGvThreads) {
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (8 * i < K) v = *reinterpret_cast<const uint4*>(J.x + 8 * i);
+    lds_st128(xoff + 16u * i, v);
+  }
+  if (tid < kZeroBytes / 16) lds_st128(zoff + 16u * tid, make_uint4(0u, 0u, 0u, 0u));
   __syncthreads();
 
-  const Nf4Table T = make_table(1.0f);  // bf16 of the unscaled levels
-  const int64_t n = (int64_t)(blockIdx.x - b.wg_begin[j]) * kGemvRows + 32 * w + jr;
-  // Rows past N address the first byte past the arrays: the range check
-  // returns zero codes and absmax code 0, i.e. block scale 0.
-  const int64_t nc = n < N ? n : N;
-  const int64_t nb = (int64_t)N * nblk;
-  const rsrc_t cr = make_rsrc(J.codes, (uint32_t)(nb * 32));
-  const rsrc_t ar = make_rsrc(J.absmax_q, (uint32_t)nb);
-  const uint32_t crow = (uint32_t)(nc * nblk * 32) + 16u * h;
-  const uint32_t brow = (uint32_t)(nc * nblk);
-  const bool quad = (nblk & 3) == 0;
-  float acc = 0.0f;
+  const uint32_t col = 4u * lane;
+  const bool diag = (nl >> 2) == q;
+  uint32_t xa = diag ? xoff + 128u * q : zoff;
+  const uint32_t xinc = diag ? 512u : 0u;
 
-  uint4 cw[4];
+  float acc[kGvGroups];
 #pragma unroll
-  for (int bi = 0; bi < 4; ++bi) cw[bi] = buf_load16(cr, crow + 32u * bi);
-  for (int b0 = 0; b0 < nblk; b0 += 4) {
-    // scales of blocks b0 .. b0+3 (zero past the last block)
-    float t[4];
-    if (quad) {
-      const uint32_t q4 = __builtin_amdgcn_raw_buffer_load_b32(ar, brow + b0, 0, 0);
-      const float s2 = J.group_scale[(brow + b0 < nb ? brow + b0 : nb - 1) >> 8];
+  for (int g = 0; g < kGvGroups; ++g) acc[g] = 0.0f;
+
+  for (int s = 0; s < nsteps; ++s) {
+    const bool live = 4 * s + q < nblk;   // false only in a ragged last step
+    float t[kGvGroups];
+    uint4 n0[kGvGroups], n1[kGvGroups];
 #pragma unroll
-      for (int bi = 0; bi < 4; ++bi) t[bi] = block_scale((q4 >> (8 * bi)) & 0xFFu, s2);
-    } else {
+    for (int g = 0; g < kGvGroups; ++g) {
+      const uint32_t b = bidx[g] + 4u * s;
+      const uint32_t aq = __builtin_amdgcn_raw_buffer_load_b8(ar, b, 0, 0);
+      const float s2 = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(sr, (b >> 8) * 4u, 0, 0));
+      t[g] = live ? block_scale(aq, s2) : 0.0f;
+      n0[g] = buf_load16(cr, (b + 4u) * 32u);
+      n1[g] = buf_load16(cr, (b + 4u) * 32u + 16u);
+    }
+    f32x4_t D[kGvGroups];
 #pragma unroll
-      for (int bi = 0; bi < 4; ++bi) {
-        const uint32_t blk = brow + b0 + bi;
-        const uint32_t q = __builtin_amdgcn_raw_buffer_load_b8(ar, blk, 0, 0);
-        const float s2 = J.group_scale[(blk < nb ? blk : nb - 1) >> 8];
-        t[bi] = b0 + bi < nblk ? block_scale(q, s2) : 0.0f;
+    for (int g = 0; g < kGvGroups; ++g) D[g] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const bf16x8_t a = __builtin_bit_cast(bf16x8_t, lds_ld128(xa + 16u * j));
+#pragma unroll
+      for (int g = 0; g < kGvGroups; ++g) {
+        const uint32_t cw = j < 4 ? (j == 0 ? c0[g].x : j == 1 ? c0[g].y : j == 2 ? c0[g].z : c0[g].w)
+                                  : (j == 4 ? c1[g].x : j == 5 ? c1[g].y : j == 6 ? c1[g].z : c1[g].w);
+        D[g] = mfma16x16x32(a, decode8(cw, col), D[g]);
       }
     }
-    // codes of the next four blocks (past the row end they are never used)
-    uint4 cn[4];
 #pragma unroll
-    for (int bi = 0; bi < 4; ++bi) cn[bi] = buf_load16(cr, crow + 32u * (b0 + 4 + bi));
-#pragma unroll
-    for (int bi = 0; bi < 4; ++bi) {
-      if (b0 + bi >= nblk) break;   // uniform: a ragged last quad of blocks
-      const uint32_t* xb = xs + 32 * (b0 + bi) + 16 * h;
-      const uint32_t words[4] = {cw[bi].x, cw[bi].y, cw[bi].z, cw[bi].w};
-      f32x16_t D = {};
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const bf16x8_t xa = *reinterpret_cast<const bf16x8_t*>(xb + 4 * kk);
-        D = mfma32x32x16(xa, dequant8_eo(words[kk], T), D);
-      }
-      acc += t[bi] * D[0];
+    for (int g = 0; g < kGvGroups; ++g) {
+      acc[g] += t[g] * D[g][0];
+      c0[g] = n0[g];
+      c1[g] = n1[g];
     }
-#pragma unroll
-    for (int bi = 0; bi < 4; ++bi) cw[bi] = cn[bi];
+    xa += xinc;
   }
 
-  // LoRA up-projection: lanes j and j+32 take alternate groups of 8 ranks
-  const bool valid = n < N;
-  float lora = 0.0f;
-  if (J.r > 0 && valid) {
-    const bf16_t* brp = J.B + n * J.r;
-    for (int i = 8 * h; i < J.r; i += 16) {
-      const uint4 v = *reinterpret_cast<const uint4*>(brp + i);
-      const uint32_t vw[4] = {v.x, v.y, v.z, v.w};
+  // LoRA up-projection: the four lanes of a row take alternate 8-rank chunks
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        lora += bf2f(vw[e] & 0xFFFFu) * J.u[i + 2 * e];
-        lora += bf2f(vw[e] >> 16) * J.u[i + 2 * e + 1];
+  for (int g = 0; g < kGvGroups; ++g) {
+    const bool valid = row[g] < N;
+    float lora = 0.0f;
+    if (J.r > 0 && valid) {
+      const bf16_t* brp = J.B + (int64_t)row[g] * J.r;
+      for (int i = 8 * q; i < J.r; i += 32) {
+        const uint4 v = *reinterpret_cast<const uint4*>(brp + i);
+        const float4 u0 = *reinterpret_cast<const float4*>(J.u + i);
+        const float4 u1 = *reinterpret_cast<const float4*>(J.u + i + 4);
+        lora += bf2f(v.x & 0xFFFFu) * u0.x + bf2f(v.x >> 16) * u0.y + bf2f(v.y & 0xFFFFu) * u0.z +
+                bf2f(v.y >> 16) * u0.w + bf2f(v.z & 0xFFFFu) * u1.x + bf2f(v.z >> 16) * u1.y +
+                bf2f(v.w & 0xFFFFu) * u1.z + bf2f(v.w >> 16) * u1.w;
       }
     }
-  }
-  lora += __shfl_xor(lora, 32);
-  if (h == 0 && valid) {
-    const float y = acc + J.s * lora;
-    J.y[n] = (bf16_t)(pack_bf16x2(y, 0.0f) & 0xFFFFu);
+    float part = acc[g];
+    part += __shfl_xor(part, 16);
+    part += __shfl_xor(part, 32);
+    lora += __shfl_xor(lora, 16);
+    lora += __shfl_xor(lora, 32);
+    if (q == 0 && valid) {
+      const float y = part + J.s * lora;
+      J.y[row[g]] = (bf16_t)(pack_bf16x2(y, 0.0f) & 0xFFFFu);
+    }
   }
 }
 
-hipError_t launch_gemv(const GemvJob* jobs, int njobs, hipStream_t st) {
-  for (int base = 0; base < njobs; base += kMaxBatch) {
-    const int cnt = njobs - base < kMaxBatch ? njobs - base : kMaxBatch;
-    GemvBatch down{}, main{};
-    int wd = 0, wm = 0, maxK = 0, nd = 0;
-    for (int i = 0; i < cnt; ++i) {
-      const GemvJob& J = jobs[base + i];
-      main.jobs[i] = J;
-      main.wg_begin[i] = wm;
-      wm += (J.N + kGemvRows - 1) / kGemvRows;
-      if (J.K > maxK) maxK = J.K;
-      if (J.r > 0) {
-        down.jobs[nd] = J;
-        down.wg_begin[nd] = wd;
-        wd += (J.r + kDownRows - 1) / kDownRows;
-        ++nd;
-      }
-    }
-    main.wg_begin[cnt] = wm;
-    main.njobs = cnt;
-    down.wg_begin[nd] = wd;
-    down.njobs = nd;
-    if (nd > 0) {
-      hipLaunchKernelGGL(lora_down_kernel, dim3(wd), dim3(kGemvThreads), 0, st, down);
-      hipError_t e = hipGetLastError();
-      if (e != hipSuccess) return e;
-    }
-    const size_t lds = (size_t)maxK * sizeof(bf16_t);
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&nf4_gemv_kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(nf4_gemv_kernel, dim3(wm), dim3(kGemvThreads), lds, st, main);
+namespace {
+
+struct TablePlan {
+  size_t jobs_off, main_off, down_off, total;
+  int n_main, n_down;
+};
+
+TablePlan plan_table(const GemvJob* jobs, int njobs) {
+  TablePlan p{};
+  for (int i = 0; i < njobs; ++i) {
+    p.n_main += (jobs[i].N + kGvRows - 1) / kGvRows;
+    if (jobs[i].r > 0) p.n_down += (jobs[i].r + kDownRows - 1) / kDownRows;
+  }
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  p.jobs_off = 0;
+  p.main_off = up((size_t)njobs * sizeof(GemvJob));
+  p.down_off = p.main_off + up((size_t)p.n_main * sizeof(int2));
+  p.total = p.down_off + up((size_t)p.n_down * sizeof(int2));
+  return p;
+}
+
+}  // namespace
+
+size_t gemv_table_bound(int njobs, int64_t max_rows) {
+  if (njobs <= 0 || max_rows <= 0) return 0;
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  const size_t tiles = (size_t)njobs * (size_t)((max_rows + kGvRows - 1) / kGvRows);
+  const size_t downs = (size_t)njobs * (128 / kDownRows);
+  return up((size_t)njobs * sizeof(GemvJob)) + up(tiles * sizeof(int2)) + up(downs * sizeof(int2));
+}
+
+size_t gemv_table_bytes(const GemvJob* jobs, int njobs) { return plan_table(jobs, njobs).total; }
+
+size_t gemv_lds_bytes(int64_t K) {
+  const int64_t nsteps = (K / 64 + 3) / 4;
+  return (size_t)kLutBytes + (size_t)nsteps * 512 + kZeroBytes;
+}
+
+hipError_t launch_gemv(const GemvJob* jobs, int njobs, void* table, hipStream_t st) {
+  const TablePlan p = plan_table(jobs, njobs);
+  std::vector<uint8_t> host(p.total, 0);
+  std::memcpy(host.data() + p.jobs_off, jobs, (size_t)njobs * sizeof(GemvJob));
+  int2* mm = reinterpret_cast<int2*>(host.data() + p.main_off);
+  int2* dm = reinterpret_cast<int2*>(host.data() + p.down_off);
+  int maxK = 0;
+  for (int i = 0, im = 0, id = 0; i < njobs; ++i) {
+    const GemvJob& J = jobs[i];
+    for (int t = 0; t < (J.N + kGvRows - 1) / kGvRows; ++t) mm[im++] = make_int2(i, t);
+    if (J.r > 0)
+      for (int t = 0; t < (J.r + kDownRows - 1) / kDownRows; ++t) dm[id++] = make_int2(i, t);
+    if (J.K > maxK) maxK = J.K;
+  }
+  uint8_t* dev = static_cast<uint8_t*>(table);
+  hipError_t e = hipMemcpyAsync(dev, host.data(), p.total, hipMemcpyHostToDevice, st);
+  if (e != hipSuccess) return e;
+  const GemvJob* djobs = reinterpret_cast<const GemvJob*>(dev + p.jobs_off);
+  if (p.n_down > 0) {
+    hipLaunchKernelGGL(lora_down_kernel, dim3(p.n_down), dim3(kDownThreads), 0, st, djobs,
+                       reinterpret_cast<const int2*>(dev + p.down_off));
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  return hipSuccess;
+  const size_t lds = gemv_lds_bytes(maxK);
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&nf4_gemv_kernel),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(nf4_gemv_kernel, dim3(p.n_main), dim3(kGvThreads), lds, st, djobs,
+                     reinterpret_cast<const int2*>(dev + p.main_off));
+  return hipGetLastError();
 }
 
 }  // namespace qlora

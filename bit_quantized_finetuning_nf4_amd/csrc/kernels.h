@@ -57,6 +57,12 @@ struct GemvJob {
   int32_t r;
   float s;
 };
-hipError_t launch_gemv(const GemvJob* jobs, int njobs, hipStream_t st);
+// The job table (jobs and workgroup maps) is written into `table` (device
+// memory of at least gemv_table_bytes(jobs, njobs)) by one host-to-device
+// copy on `st`; then u = A x and the NF4 GEMV run as one launch each.
+size_t gemv_table_bytes(const GemvJob* jobs, int njobs);
+size_t gemv_table_bound(int njobs, int64_t max_rows);  // upper bound for any njobs jobs of <= max_rows rows
+size_t gemv_lds_bytes(int64_t K);
+hipError_t launch_gemv(const GemvJob* jobs, int njobs, void* table, hipStream_t st);
 
 }  // namespace qlora

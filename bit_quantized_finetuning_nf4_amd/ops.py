@@ -194,7 +194,8 @@ class GemvPlan:
                                        None if r == 0 else j.A.data_ptr(), None if r == 0 else j.B.data_ptr(),
                                        r, float(j.alpha), y.data_ptr())
         self.n = n
-        nbytes = workspace_bytes(_lib.QLORA_OP_GEMV, njobs=n)
+        nbytes = workspace_bytes(_lib.QLORA_OP_GEMV, N=max(j.q.rows for j in jobs),
+                                 K=max(j.q.cols for j in jobs), njobs=n)
         self.ws = ws if ws is not None else workspace(nbytes, jobs[0].x.device)
 
     def __call__(self):
@@ -217,7 +218,8 @@ def gemv(jobs: Sequence[GemvJob], ws=None):
         descs[i] = j.q.desc()
         arr[i] = GemvJobDesc(ctypes.pointer(descs[i]), j.x.data_ptr(), None if r == 0 else j.A.data_ptr(),
                              None if r == 0 else j.B.data_ptr(), r, float(j.alpha), y.data_ptr())
-    nbytes = workspace_bytes(_lib.QLORA_OP_GEMV, njobs=n)
+    nbytes = workspace_bytes(_lib.QLORA_OP_GEMV, N=max(j.q.rows for j in jobs), K=max(j.q.cols for j in jobs),
+                             njobs=n)
     if ws is None:
         ws = workspace(nbytes, jobs[0].x.device)
     check(lib().qlora_gemv(arr, n, _ptr(ws), 0 if ws is None else ws.numel(), _stream()), "qlora_gemv")

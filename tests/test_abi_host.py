@@ -79,7 +79,10 @@ def test_workspace_query(L):
     fwd = L.qlora_workspace_bytes(0, 4096, 8192, 8192, 64, 0)
     bwd = L.qlora_workspace_bytes(1, 4096, 8192, 8192, 64, 0)
     assert fwd >= 4096 * 64 * 2 and bwd >= 2 * 4096 * 64 * 2
-    assert L.qlora_workspace_bytes(2, 0, 0, 0, 0, 560) == 560 * 128 * 4
+    # GEMV: u = A x per job plus the device job table; N is the largest row count
+    gv = L.qlora_workspace_bytes(2, 0, 22016, 8192, 64, 560)
+    assert gv >= 560 * 128 * 4 + 560 * 72
+    assert L.qlora_workspace_bytes(2, 0, 0, 0, 0, 560) == 0       # N required
     assert L.qlora_workspace_bytes(0, 0, 8, 8, 16, 0) == 0       # invalid -> 0
 
 
@@ -124,5 +127,11 @@ def test_validation_happens_before_any_launch(L):
     jobs = (_lib.GemvJobDesc * 1)(job)
     assert L.qlora_gemv(jobs, 0, None, 0, None) == 3
     assert L.qlora_gemv(jobs, 5000, None, 0, None) == 4
+    assert L.qlora_gemv(jobs, 1, None, 0, None) == 1             # the job table needs a workspace
+    assert L.qlora_gemv(jobs, 1, fake, 16, None) == 5             # too small for it
+    wide = _desc(rows=64, cols=32768 + 64, codes=4096, aq=8192, s2=12288)
+    jobs[0].W = ctypes.pointer(wide)
+    assert L.qlora_gemv(jobs, 1, fake, 1 << 20, None) == 4        # x is staged whole in LDS
+    jobs[0].W = ctypes.pointer(d)
     jobs[0].r = 16
     assert L.qlora_gemv(jobs, 1, None, 0, None) == 1
