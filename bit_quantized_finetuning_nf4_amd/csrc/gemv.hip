@@ -42,6 +42,7 @@ namespace {
 constexpr int kGvWaves = 16;                               // waves per workgroup
 constexpr int kGvThreads = 64 * kGvWaves;
 constexpr int kGvGroups = 2;                               // 16-row groups per wave
+constexpr int kGvDepth = 3;                                // steps of loads in flight per wave
 constexpr int kGvRows = kGvWaves * 16 * kGvGroups;         // weight rows per workgroup
 constexpr int kLutBytes = 256 * 64 * 4;                    // 256 entries x 64 lane columns
 constexpr int kZeroBytes = 128;
@@ -105,6 +106,26 @@ __device__ __forceinline__ bf16x8_t decode8(uint32_t c, uint32_t col) {
   return __builtin_bit_cast(bf16x8_t, v);
 }
 
+// One step's loads for the lane's kGvGroups rows: the 32 code bytes of block
+// 4s + q, its absmax code and its group's scale.
+struct Stage {
+  uint4 c0[kGvGroups], c1[kGvGroups];
+  uint32_t aq[kGvGroups];
+  float s2[kGvGroups];
+};
+
+__device__ __forceinline__ void load_stage(Stage& st, rsrc_t cr, rsrc_t ar, rsrc_t sr,
+                                           const uint32_t (&bidx)[kGvGroups], int s) {
+#pragma unroll
+  for (int g = 0; g < kGvGroups; ++g) {
+    const uint32_t b = bidx[g] + 4u * (uint32_t)s;
+    st.c0[g] = buf_load16(cr, b * 32u);
+    st.c1[g] = buf_load16(cr, b * 32u + 16u);
+    st.aq[g] = __builtin_amdgcn_raw_buffer_load_b8(ar, b, 0, 0);
+    st.s2[g] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(sr, (b >> 8) * 4u, 0, 0));
+  }
+}
+
 }  // namespace
 
 // Phase 1: u = A x for every job with r > 0 (fp32, into the job's scratch);
@@ -166,26 +187,30 @@ __global__ __launch_bounds__(kGvThreads) void nf4_gemv_kernel(const GemvJob* __r
     bidx[g] = (uint32_t)(row[g] < N ? row[g] : N) * (uint32_t)nblk + (uint32_t)q;
   }
 
-  // codes of step 0, in flight during the prologue
-  uint4 c0[kGvGroups], c1[kGvGroups];
+  // x (zero-padded to nsteps * 256 elements) is fetched first, then the
+  // first kGvDepth steps' loads, so that waiting for x before the barrier
+  // does not wait for the codes.
+  constexpr int kXChunks = 4;   // 16-byte chunks per thread: K <= 32768
+  const rsrc_t xr = make_rsrc(J.x, (uint32_t)K * 2u);   // the zero padding comes from the range check
+  uint4 xv[kXChunks];
 #pragma unroll
-  for (int g = 0; g < kGvGroups; ++g) {
-    c0[g] = buf_load16(cr, bidx[g] * 32u);
-    c1[g] = buf_load16(cr, bidx[g] * 32u + 16u);
-  }
+  for (int c = 0; c < kXChunks; ++c) xv[c] = buf_load16(xr, 16u * (uint32_t)(tid + c * kGvThreads));
+  Stage st[kGvDepth];
+#pragma unroll
+  for (int i = 0; i < kGvDepth; ++i) load_stage(st[i], cr, ar, sr, bidx, i < nsteps ? i : nsteps - 1);
 
   // table: thread (w, lane) writes entries e = w + 16 i, column lane
   {
-    const uint32_t lo = level_bf16(w);
+    const uint32_t lo = level_bf16(__builtin_amdgcn_readfirstlane(w));   // w is wave-uniform: a scalar load
 #pragma unroll
     for (int i = 0; i < 16; ++i)
       lds_st32((uint32_t)(w + 16 * i) * 256u + 4u * lane, lo | (level_bf16(i) << 16));
   }
-  // x, zero-padded to nsteps * 256 elements, then the zero run
-  for (int i = tid; i < nsteps * 32; i += kGvThreads) {
-    uint4 v = make_uint4(0u, 0u, 0u, 0u);
-    if (8 * i < K) v = *reinterpret_cast<const uint4*>(J.x + 8 * i);
-    lds_st128(xoff + 16u * i, v);
+  // chunks past the staged x are zero (range check) and land in the zero run
+#pragma unroll
+  for (int c = 0; c < kXChunks; ++c) {
+    const int i = tid + c * kGvThreads;
+    lds_st128(i < nsteps * 32 ? xoff + 16u * i : zoff + 16u * (i & 7), xv[c]);
   }
   if (tid < kZeroBytes / 16) lds_st128(zoff + 16u * tid, make_uint4(0u, 0u, 0u, 0u));
   __syncthreads();
@@ -199,40 +224,46 @@ __global__ __launch_bounds__(kGvThreads) void nf4_gemv_kernel(const GemvJob* __r
 #pragma unroll
   for (int g = 0; g < kGvGroups; ++g) acc[g] = 0.0f;
 
-  for (int s = 0; s < nsteps; ++s) {
+  // Step s consumes the stage loaded kGvDepth steps earlier and refills it
+  // with step s + kGvDepth (clamped to the last step: a re-read of lines
+  // already in cache, never used).  The main loop runs whole rounds of
+  // kGvDepth steps with no branch inside, so the load counters are tracked
+  // exactly across the round; the last partial round follows.
+  auto step = [&](Stage& cur, int s, bool refill) {
     const bool live = 4 * s + q < nblk;   // false only in a ragged last step
     float t[kGvGroups];
-    uint4 n0[kGvGroups], n1[kGvGroups];
-#pragma unroll
-    for (int g = 0; g < kGvGroups; ++g) {
-      const uint32_t b = bidx[g] + 4u * s;
-      const uint32_t aq = __builtin_amdgcn_raw_buffer_load_b8(ar, b, 0, 0);
-      const float s2 = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(sr, (b >> 8) * 4u, 0, 0));
-      t[g] = live ? block_scale(aq, s2) : 0.0f;
-      n0[g] = buf_load16(cr, (b + 4u) * 32u);
-      n1[g] = buf_load16(cr, (b + 4u) * 32u + 16u);
-    }
     f32x4_t D[kGvGroups];
 #pragma unroll
-    for (int g = 0; g < kGvGroups; ++g) D[g] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int g = 0; g < kGvGroups; ++g) {
+      t[g] = live ? block_scale(cur.aq[g] & 0xFFu, cur.s2[g]) : 0.0f;
+      D[g] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const bf16x8_t a = __builtin_bit_cast(bf16x8_t, lds_ld128(xa + 16u * j));
 #pragma unroll
       for (int g = 0; g < kGvGroups; ++g) {
-        const uint32_t cw = j < 4 ? (j == 0 ? c0[g].x : j == 1 ? c0[g].y : j == 2 ? c0[g].z : c0[g].w)
-                                  : (j == 4 ? c1[g].x : j == 5 ? c1[g].y : j == 6 ? c1[g].z : c1[g].w);
+        const uint32_t cw = j < 4 ? (j == 0 ? cur.c0[g].x : j == 1 ? cur.c0[g].y : j == 2 ? cur.c0[g].z : cur.c0[g].w)
+                                  : (j == 4 ? cur.c1[g].x : j == 5 ? cur.c1[g].y : j == 6 ? cur.c1[g].z : cur.c1[g].w);
         D[g] = mfma16x16x32(a, decode8(cw, col), D[g]);
       }
     }
 #pragma unroll
-    for (int g = 0; g < kGvGroups; ++g) {
-      acc[g] += t[g] * D[g][0];
-      c0[g] = n0[g];
-      c1[g] = n1[g];
-    }
+    for (int g = 0; g < kGvGroups; ++g) acc[g] += t[g] * D[g][0];
     xa += xinc;
+    if (refill) {
+      const int sn = s + kGvDepth;
+      load_stage(cur, cr, ar, sr, bidx, sn < nsteps ? sn : nsteps - 1);
+    }
+  };
+  int s0 = 0;
+  for (; s0 + kGvDepth <= nsteps; s0 += kGvDepth) {
+#pragma unroll
+    for (int i = 0; i < kGvDepth; ++i) step(st[i], s0 + i, true);
   }
+#pragma unroll
+  for (int i = 0; i < kGvDepth - 1; ++i)
+    if (s0 + i < nsteps) step(st[i], s0 + i, false);
 
   // LoRA up-projection: the four lanes of a row take alternate 8-rank chunks
 #pragma unroll
