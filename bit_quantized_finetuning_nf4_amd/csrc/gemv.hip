@@ -16,13 +16,17 @@
 //     (64 KiB).  One v_perm builds the address from a code byte and the lane
 //     column; one ds_read_b32 returns two ready bf16 weights.
 //   * MFMA v_mfma_f32_16x16x32_bf16.  Lane l = (n, q), n = l % 16, q = l / 16,
-//     supplies B operand column n (weight row n of its 16-row group) for one
-//     NF4 block, the block 4s + q of step s; eight MFMAs cover the block's
-//     64 weights.  The A operand is "diagonal": rows 4q .. 4q+3 of A hold x
-//     over block 4s + q and zero elsewhere.  Row m of the 16 x 16 result is
-//     then the partial dot product of weight row n with block 4s + m/4 alone,
-//     so every lane finds its own block's partial in its accumulator and
-//     applies that block's scale t = Q8[q_b] s2 in fp32.
+//     supplies B operand column n (weight row n of its 16-row group).  A
+//     step covers four NF4 blocks (128 code bytes) of each of the 16 rows;
+//     lane q loads bytes 16q .. 16q+15 and 64+16q .. 64+16q+15 of its row, so
+//     the four lanes of a row read two contiguous 64-byte runs, and each of
+//     its two 16-byte pieces is half of one block.  Each piece feeds a chain
+//     of four MFMAs whose A operand is "diagonal": rows 4q .. 4q+3 of A hold
+//     the x values under lane-group q's piece and zero elsewhere.  Row m of
+//     the 16 x 16 result is then the partial dot product of weight row n
+//     with lane-group m/4's piece alone, so every lane finds its own piece's
+//     partial in its accumulator and applies that block's scale
+//     t = Q8[q_b] s2 in fp32.
 //   * x is staged in LDS (zero-padded to whole four-block steps) behind the
 //     table, with a 128-byte zero run for the off-diagonal A lanes.
 //
@@ -41,11 +45,10 @@ namespace {
 
 constexpr int kGvWaves = 16;                               // waves per workgroup
 constexpr int kGvThreads = 64 * kGvWaves;
-constexpr int kGvGroups = 2;                               // 16-row groups per wave
-constexpr int kGvDepth = 3;                                // steps of loads in flight per wave
-constexpr int kGvRows = kGvWaves * 16 * kGvGroups;         // weight rows per workgroup
+constexpr int kGvRows = kGvWaves * 16;                     // weight rows per workgroup, 16 per wave
+constexpr int kGvDepth = 4;                                // steps of codes in flight per wave (a round)
 constexpr int kLutBytes = 256 * 64 * 4;                    // 256 entries x 64 lane columns
-constexpr int kZeroBytes = 128;
+constexpr int kZeroBytes = 512;                           // zero run read by the off-diagonal A lanes
 constexpr int kDownThreads = 256;
 constexpr int kDownRows = 4;                               // adapter rows per workgroup (one per wave)
 static_assert(kGvThreads == 1024, "the table fill below assumes 16 waves");
@@ -106,24 +109,22 @@ __device__ __forceinline__ bf16x8_t decode8(uint32_t c, uint32_t col) {
   return __builtin_bit_cast(bf16x8_t, v);
 }
 
-// One step's loads for the lane's kGvGroups rows: the 32 code bytes of block
-// 4s + q, its absmax code and its group's scale.
-struct Stage {
-  uint4 c0[kGvGroups], c1[kGvGroups];
-  uint32_t aq[kGvGroups];
-  float s2[kGvGroups];
-};
+// Absmax codes of 16 blocks from `block` (a multiple of 8), as two separate
+// 8-byte loads: with K % 512 == 0 a row's absmax codes are a whole number of
+// 8-byte units, so neither load straddles the end of the array (the second
+// one takes its +8 through the scalar offset, which keeps the compiler from
+// fusing the pair into one 16-byte access).
+__device__ __forceinline__ void load_absmax16(rsrc_t ar, uint32_t block, uint2 (&out)[2]) {
+  out[0] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(ar, block, 0, 0));
+  out[1] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(ar, block, 8, 0));
+}
 
-__device__ __forceinline__ void load_stage(Stage& st, rsrc_t cr, rsrc_t ar, rsrc_t sr,
-                                           const uint32_t (&bidx)[kGvGroups], int s) {
-#pragma unroll
-  for (int g = 0; g < kGvGroups; ++g) {
-    const uint32_t b = bidx[g] + 4u * (uint32_t)s;
-    st.c0[g] = buf_load16(cr, b * 32u);
-    st.c1[g] = buf_load16(cr, b * 32u + 16u);
-    st.aq[g] = __builtin_amdgcn_raw_buffer_load_b8(ar, b, 0, 0);
-    st.s2[g] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(sr, (b >> 8) * 4u, 0, 0));
-  }
+// The lane's two 16-byte code pieces in one step: `off` and `off` + 64.
+struct Codes {
+  uint4 lo, hi;
+};
+__device__ __forceinline__ Codes load_codes(rsrc_t cr, uint32_t off) {
+  return Codes{buf_load16(cr, off), buf_load16(cr, off + 64u)};
 }
 
 }  // namespace
@@ -159,7 +160,15 @@ __global__ __launch_bounds__(kDownThreads) void lora_down_kernel(const GemvJob* 
 
 // Phase 2: the NF4 GEMV with the LoRA up-projection in the epilogue.
 // Workgroup = (job, tile of kGvRows rows); wave w owns rows
-// tile*kGvRows + 32w .. +31 as two 16-row groups.
+// tile*kGvRows + 16w .. +15, lane (n, q) row n of them.  Loads run a round
+// (kGvDepth steps) ahead:
+//   * codes: two 16-byte loads per lane per step;
+//   * absmax codes: with kQuad (K % 512 == 0, absmax_q 8-byte aligned), one
+//     8-byte load per row per two steps, lane q taking byte q of each 4-byte
+//     step; otherwise one byte load per step;
+//   * group scales: a row of at most 32768 columns touches at most three
+//     256-block groups, so the three scales are loaded once per tile.
+template <bool kQuad>
 __global__ __launch_bounds__(kGvThreads) void nf4_gemv_kernel(const GemvJob* __restrict__ jobs,
                                                               const int2* __restrict__ map) {
   extern __shared__ __align__(16) uint8_t lds_dyn[];  // addressed from 0 (see lds_ld32)
@@ -175,29 +184,40 @@ __global__ __launch_bounds__(kGvThreads) void nf4_gemv_kernel(const GemvJob* __r
   const rsrc_t cr = make_rsrc(J.codes, nb * 32u);
   const rsrc_t ar = make_rsrc(J.absmax_q, nb);
   const rsrc_t sr = make_rsrc(J.group_scale, ((nb + 255u) >> 8) * 4u);
+  const rsrc_t xr = make_rsrc(J.x, (uint32_t)K * 2u);   // zero padding comes from the range check
 
-  // Per group: the lane's row (rows past N read the first byte past the
-  // arrays: zero codes, absmax code 0 and so block scale 0) and the offset
-  // of its first block, 4s + q at s = 0.
-  int row[kGvGroups];
-  uint32_t bidx[kGvGroups];
-#pragma unroll
-  for (int g = 0; g < kGvGroups; ++g) {
-    row[g] = m.y * kGvRows + w * (16 * kGvGroups) + 16 * g + nl;
-    bidx[g] = (uint32_t)(row[g] < N ? row[g] : N) * (uint32_t)nblk + (uint32_t)q;
-  }
+  // The lane's row; rows past N read the first byte past the arrays (zero
+  // codes, absmax code 0, so block scale 0).  Its two pieces in step s are
+  // half (q & 1) of blocks 4s + hb and 4s + 2 + hb, hb = q >> 1.
+  const int row = m.y * kGvRows + 16 * w + nl;
+  const uint32_t rbase = (uint32_t)(row < N ? row : N) * (uint32_t)nblk;   // first block of the row
+  const uint32_t hb = (uint32_t)q >> 1;
+  const uint32_t cbase = rbase * 32u + 16u * (uint32_t)q;                   // code byte of the first piece at s = 0
 
-  // x (zero-padded to nsteps * 256 elements) is fetched first, then the
-  // first kGvDepth steps' loads, so that waiting for x before the barrier
-  // does not wait for the codes.
+  // x first (waited for before the barrier), then the row's group scales,
+  // absmax codes and the first round of codes.
   constexpr int kXChunks = 4;   // 16-byte chunks per thread: K <= 32768
-  const rsrc_t xr = make_rsrc(J.x, (uint32_t)K * 2u);   // the zero padding comes from the range check
   uint4 xv[kXChunks];
 #pragma unroll
   for (int c = 0; c < kXChunks; ++c) xv[c] = buf_load16(xr, 16u * (uint32_t)(tid + c * kGvThreads));
-  Stage st[kGvDepth];
+  const uint32_t g0 = rbase >> 8;
+  const float s2a = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(sr, g0 * 4u, 0, 0));
+  const float s2b = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(sr, g0 * 4u + 4u, 0, 0));
+  const float s2c = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(sr, g0 * 4u + 8u, 0, 0));
+  uint2 aqr[2];                  // kQuad: absmax codes of the round's 16 blocks (steps 4k .. 4k+3)
+  uint32_t aqs[kGvDepth][2];     // !kQuad: the two pieces' absmax codes per step
+  if constexpr (kQuad) load_absmax16(ar, rbase, aqr);
+  Codes cs[kGvDepth];
+  auto load_step = [&](int i, int si) __attribute__((always_inline)) {
+    cs[i] = load_codes(cr, cbase + 128u * (uint32_t)si);
+    if constexpr (!kQuad) {
+      const uint32_t b = rbase + 4u * (uint32_t)si + hb;
+      aqs[i][0] = __builtin_amdgcn_raw_buffer_load_b8(ar, b, 0, 0);
+      aqs[i][1] = __builtin_amdgcn_raw_buffer_load_b8(ar, b + 2u, 0, 0);
+    }
+  };
 #pragma unroll
-  for (int i = 0; i < kGvDepth; ++i) load_stage(st[i], cr, ar, sr, bidx, i < nsteps ? i : nsteps - 1);
+  for (int i = 0; i < kGvDepth; ++i) load_step(i, i < nsteps ? i : nsteps - 1);
 
   // table: thread (w, lane) writes entries e = w + 16 i, column lane
   {
@@ -217,111 +237,152 @@ __global__ __launch_bounds__(kGvThreads) void nf4_gemv_kernel(const GemvJob* __r
 
   const uint32_t col = 4u * lane;
   const bool diag = (nl >> 2) == q;
-  uint32_t xa = diag ? xoff + 128u * q : zoff;
+  // diagonal lanes: x under the first piece at 64q (bytes) into the step,
+  // the second 256 bytes further; off-diagonal lanes read the zero run
+  uint32_t xa = diag ? xoff + 64u * q : zoff;
   const uint32_t xinc = diag ? 512u : 0u;
+  float acc = 0.0f;
 
-  float acc[kGvGroups];
-#pragma unroll
-  for (int g = 0; g < kGvGroups; ++g) acc[g] = 0.0f;
-
-  // Step s consumes the stage loaded kGvDepth steps earlier and refills it
-  // with step s + kGvDepth (clamped to the last step: a re-read of lines
-  // already in cache, never used).  The main loop runs whole rounds of
-  // kGvDepth steps with no branch inside, so the load counters are tracked
-  // exactly across the round; the last partial round follows.
-  auto step = [&](Stage& cur, int s, bool refill) {
-    const bool live = 4 * s + q < nblk;   // false only in a ragged last step
-    float t[kGvGroups];
-    f32x4_t D[kGvGroups];
-#pragma unroll
-    for (int g = 0; g < kGvGroups; ++g) {
-      t[g] = live ? block_scale(cur.aq[g] & 0xFFu, cur.s2[g]) : 0.0f;
-      D[g] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const bf16x8_t a = __builtin_bit_cast(bf16x8_t, lds_ld128(xa + 16u * j));
-#pragma unroll
-      for (int g = 0; g < kGvGroups; ++g) {
-        const uint32_t cw = j < 4 ? (j == 0 ? cur.c0[g].x : j == 1 ? cur.c0[g].y : j == 2 ? cur.c0[g].z : cur.c0[g].w)
-                                  : (j == 4 ? cur.c1[g].x : j == 5 ? cur.c1[g].y : j == 6 ? cur.c1[g].z : cur.c1[g].w);
-        D[g] = mfma16x16x32(a, decode8(cw, col), D[g]);
-      }
-    }
-#pragma unroll
-    for (int g = 0; g < kGvGroups; ++g) acc[g] += t[g] * D[g][0];
-    xa += xinc;
-    if (refill) {
-      const int sn = s + kGvDepth;
-      load_stage(cur, cr, ar, sr, bidx, sn < nsteps ? sn : nsteps - 1);
-    }
+  // Block scale of block `b` (its absmax code `aq`), zero past the row end.
+  // (The group scales are passed by value: choosing among variables
+  // captured by reference would make the compiler pick among their
+  // addresses and keep them in scratch memory.)
+  auto scale = [&](uint32_t aq, uint32_t bi, float s2a_, float s2b_, float s2c_) __attribute__((always_inline)) {
+    const uint32_t gi = ((rbase + bi) >> 8) - g0;
+    const float s2 = gi == 0 ? s2a_ : gi == 1 ? s2b_ : s2c_;
+    return bi < (uint32_t)nblk ? block_scale(aq, s2) : 0.0f;   // ragged last step
   };
+  // One step: two chains of four MFMAs over the lane's two pieces.
+  auto step = [&](const Codes& c, uint32_t aq0, uint32_t aq1, int s, float s2a_, float s2b_, float s2c_)
+                  __attribute__((always_inline)) {
+    const uint32_t bi = 4u * (uint32_t)s + hb;   // block index within the row
+    const float t0 = scale(aq0, bi, s2a_, s2b_, s2c_);
+    const float t1 = scale(aq1, bi + 2u, s2a_, s2b_, s2c_);
+    f32x4_t D0 = {0.0f, 0.0f, 0.0f, 0.0f}, D1 = {0.0f, 0.0f, 0.0f, 0.0f};
+    const uint32_t lw[4] = {c.lo.x, c.lo.y, c.lo.z, c.lo.w}, hw[4] = {c.hi.x, c.hi.y, c.hi.z, c.hi.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bf16x8_t a0 = __builtin_bit_cast(bf16x8_t, lds_ld128(xa + 16u * j));
+      const bf16x8_t a1 = __builtin_bit_cast(bf16x8_t, lds_ld128(xa + 256u + 16u * j));
+      D0 = mfma16x16x32(a0, decode8(lw[j], col), D0);
+      D1 = mfma16x16x32(a1, decode8(hw[j], col), D1);
+    }
+    acc += t0 * D0[0];
+    acc += t1 * D1[0];
+    xa += xinc;
+  };
+  auto aq_of = [&](int i, uint32_t byte) __attribute__((always_inline)) -> uint32_t {   // kQuad
+    const uint32_t d = (i & 1) ? aqr[i >> 1].y : aqr[i >> 1].x;
+    return __builtin_amdgcn_ubfe(d, 8u * byte, 8u);
+  };
+  auto run_step = [&](int i, int s) __attribute__((always_inline)) {
+    if constexpr (kQuad) step(cs[i], aq_of(i, hb), aq_of(i, hb + 2u), s, s2a, s2b, s2c);
+    else step(cs[i], aqs[i][0], aqs[i][1], s, s2a, s2b, s2c);
+  };
+
+  // Rounds of kGvDepth steps with no branch inside, so the load counters
+  // are tracked exactly; each step refills its slot with the step one round
+  // later (clamped to the last step: a re-read of lines already in cache).
   int s0 = 0;
   for (; s0 + kGvDepth <= nsteps; s0 += kGvDepth) {
+    uint2 aqn[2];
+    if constexpr (kQuad) {
+      load_absmax16(ar, rbase + 4u * (uint32_t)(s0 + kGvDepth), aqn);   // the next round
+      __builtin_amdgcn_sched_barrier(0);
+    }
 #pragma unroll
-    for (int i = 0; i < kGvDepth; ++i) step(st[i], s0 + i, true);
+    for (int i = 0; i < kGvDepth; ++i) {
+      const int s = s0 + i;
+      run_step(i, s);
+      load_step(i, s + kGvDepth < nsteps ? s + kGvDepth : nsteps - 1);
+      __builtin_amdgcn_sched_barrier(0);   // issue the refill here, a round ahead of its use
+    }
+    if constexpr (kQuad) {
+      aqr[0] = aqn[0];
+      aqr[1] = aqn[1];
+    }
   }
 #pragma unroll
   for (int i = 0; i < kGvDepth - 1; ++i)
-    if (s0 + i < nsteps) step(st[i], s0 + i, false);
+    if (s0 + i < nsteps) run_step(i, s0 + i);   // uniform
 
   // LoRA up-projection: the four lanes of a row take alternate 8-rank chunks
-#pragma unroll
-  for (int g = 0; g < kGvGroups; ++g) {
-    const bool valid = row[g] < N;
-    float lora = 0.0f;
-    if (J.r > 0 && valid) {
-      const bf16_t* brp = J.B + (int64_t)row[g] * J.r;
-      for (int i = 8 * q; i < J.r; i += 32) {
-        const uint4 v = *reinterpret_cast<const uint4*>(brp + i);
-        const float4 u0 = *reinterpret_cast<const float4*>(J.u + i);
-        const float4 u1 = *reinterpret_cast<const float4*>(J.u + i + 4);
-        lora += bf2f(v.x & 0xFFFFu) * u0.x + bf2f(v.x >> 16) * u0.y + bf2f(v.y & 0xFFFFu) * u0.z +
-                bf2f(v.y >> 16) * u0.w + bf2f(v.z & 0xFFFFu) * u1.x + bf2f(v.z >> 16) * u1.y +
-                bf2f(v.w & 0xFFFFu) * u1.z + bf2f(v.w >> 16) * u1.w;
-      }
+  const bool valid = row < N;
+  float lora = 0.0f;
+  if (J.r > 0 && valid) {
+    const bf16_t* brp = J.B + (int64_t)row * J.r;
+    for (int i = 8 * q; i < J.r; i += 32) {
+      const uint4 v = *reinterpret_cast<const uint4*>(brp + i);
+      const float4 u0 = *reinterpret_cast<const float4*>(J.u + i);
+      const float4 u1 = *reinterpret_cast<const float4*>(J.u + i + 4);
+      lora += bf2f(v.x & 0xFFFFu) * u0.x + bf2f(v.x >> 16) * u0.y + bf2f(v.y & 0xFFFFu) * u0.z +
+              bf2f(v.y >> 16) * u0.w + bf2f(v.z & 0xFFFFu) * u1.x + bf2f(v.z >> 16) * u1.y +
+              bf2f(v.w & 0xFFFFu) * u1.z + bf2f(v.w >> 16) * u1.w;
     }
-    float part = acc[g];
-    part += __shfl_xor(part, 16);
-    part += __shfl_xor(part, 32);
-    lora += __shfl_xor(lora, 16);
-    lora += __shfl_xor(lora, 32);
-    if (q == 0 && valid) {
-      const float y = part + J.s * lora;
-      J.y[row[g]] = (bf16_t)(pack_bf16x2(y, 0.0f) & 0xFFFFu);
-    }
+  }
+  float part = acc;
+  part += __shfl_xor(part, 16);
+  part += __shfl_xor(part, 32);
+  lora += __shfl_xor(lora, 16);
+  lora += __shfl_xor(lora, 32);
+  if (q == 0 && valid) {
+    const float y = part + J.s * lora;
+    J.y[row] = (bf16_t)(pack_bf16x2(y, 0.0f) & 0xFFFFu);
   }
 }
 
 namespace {
 
+// Tiles of jobs whose absmax rows can be read 8 bytes at a time.
+bool quad_job(const GemvJob& J) {
+  return (J.K % 512) == 0 && (reinterpret_cast<uintptr_t>(J.absmax_q) & 7u) == 0;
+}
+
 struct TablePlan {
-  size_t jobs_off, main_off, down_off, total;
-  int n_main, n_down;
+  size_t jobs_off, quad_off, other_off, down_off, total;
+  int n_quad, n_other, n_down;
 };
+
+size_t up256(size_t x) { return (x + 255) / 256 * 256; }
 
 TablePlan plan_table(const GemvJob* jobs, int njobs) {
   TablePlan p{};
   for (int i = 0; i < njobs; ++i) {
-    p.n_main += (jobs[i].N + kGvRows - 1) / kGvRows;
+    (quad_job(jobs[i]) ? p.n_quad : p.n_other) += (jobs[i].N + kGvRows - 1) / kGvRows;
     if (jobs[i].r > 0) p.n_down += (jobs[i].r + kDownRows - 1) / kDownRows;
   }
-  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
   p.jobs_off = 0;
-  p.main_off = up((size_t)njobs * sizeof(GemvJob));
-  p.down_off = p.main_off + up((size_t)p.n_main * sizeof(int2));
-  p.total = p.down_off + up((size_t)p.n_down * sizeof(int2));
+  p.quad_off = up256((size_t)njobs * sizeof(GemvJob));
+  p.other_off = p.quad_off + up256((size_t)p.n_quad * sizeof(int2));
+  p.down_off = p.other_off + up256((size_t)p.n_other * sizeof(int2));
+  p.total = p.down_off + up256((size_t)p.n_down * sizeof(int2));
   return p;
+}
+
+template <bool kQuad>
+hipError_t launch_main(const GemvJob* djobs, const int2* map, int n, size_t lds, hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  // The kernel addresses its LDS from 0, which holds only while the
+  // compiler has given it no static LDS.
+  hipFuncAttributes fa{};
+  hipError_t e = hipFuncGetAttributes(&fa, reinterpret_cast<const void*>(&nf4_gemv_kernel<kQuad>));
+  if (e != hipSuccess) return e;
+  if (fa.sharedSizeBytes != 0) return hipErrorInvalidKernelFile;
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&nf4_gemv_kernel<kQuad>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(nf4_gemv_kernel<kQuad>, dim3(n), dim3(kGvThreads), lds, st, djobs, map);
+  return hipGetLastError();
 }
 
 }  // namespace
 
 size_t gemv_table_bound(int njobs, int64_t max_rows) {
   if (njobs <= 0 || max_rows <= 0) return 0;
-  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
   const size_t tiles = (size_t)njobs * (size_t)((max_rows + kGvRows - 1) / kGvRows);
   const size_t downs = (size_t)njobs * (128 / kDownRows);
-  return up((size_t)njobs * sizeof(GemvJob)) + up(tiles * sizeof(int2)) + up(downs * sizeof(int2));
+  // two tile maps (each padded to 256 bytes) share the tiles
+  return up256((size_t)njobs * sizeof(GemvJob)) + up256(tiles * sizeof(int2)) + 256 + up256(downs * sizeof(int2));
 }
 
 size_t gemv_table_bytes(const GemvJob* jobs, int njobs) { return plan_table(jobs, njobs).total; }
@@ -335,12 +396,14 @@ hipError_t launch_gemv(const GemvJob* jobs, int njobs, void* table, hipStream_t 
   const TablePlan p = plan_table(jobs, njobs);
   std::vector<uint8_t> host(p.total, 0);
   std::memcpy(host.data() + p.jobs_off, jobs, (size_t)njobs * sizeof(GemvJob));
-  int2* mm = reinterpret_cast<int2*>(host.data() + p.main_off);
+  int2* qm = reinterpret_cast<int2*>(host.data() + p.quad_off);
+  int2* om = reinterpret_cast<int2*>(host.data() + p.other_off);
   int2* dm = reinterpret_cast<int2*>(host.data() + p.down_off);
   int maxK = 0;
-  for (int i = 0, im = 0, id = 0; i < njobs; ++i) {
+  for (int i = 0, iq = 0, io = 0, id = 0; i < njobs; ++i) {
     const GemvJob& J = jobs[i];
-    for (int t = 0; t < (J.N + kGvRows - 1) / kGvRows; ++t) mm[im++] = make_int2(i, t);
+    const bool quad = quad_job(J);
+    for (int t = 0; t < (J.N + kGvRows - 1) / kGvRows; ++t) (quad ? qm[iq++] : om[io++]) = make_int2(i, t);
     if (J.r > 0)
       for (int t = 0; t < (J.r + kDownRows - 1) / kDownRows; ++t) dm[id++] = make_int2(i, t);
     if (J.K > maxK) maxK = J.K;
@@ -356,12 +419,9 @@ hipError_t launch_gemv(const GemvJob* jobs, int njobs, void* table, hipStream_t 
     if (e != hipSuccess) return e;
   }
   const size_t lds = gemv_lds_bytes(maxK);
-  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&nf4_gemv_kernel),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  e = launch_main<true>(djobs, reinterpret_cast<const int2*>(dev + p.quad_off), p.n_quad, lds, st);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(nf4_gemv_kernel, dim3(p.n_main), dim3(kGvThreads), lds, st, djobs,
-                     reinterpret_cast<const int2*>(dev + p.main_off));
-  return hipGetLastError();
+  return launch_main<false>(djobs, reinterpret_cast<const int2*>(dev + p.other_off), p.n_other, lds, st);
 }
 
 }  // namespace qlora

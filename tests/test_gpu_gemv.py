@@ -49,8 +49,10 @@ def test_small_config_one_token():
     _run([dict(W=d["W"], x=d["X"][0], A=d["A"], B=d["B"], alpha=d["alpha"])], "1024^2 r8")
 
 
+# (37, 22016): a row's absmax codes end mid-way through a 16-block load unit
+# (344 blocks), and the last row's last two steps read up to the array end.
 @pytest.mark.parametrize("N,K,r", [(1024, 1024, 64), (1000, 576, 16), (130, 64, 8), (257, 8192, 128),
-                                   (64, 320, 0)])
+                                   (64, 320, 0), (37, 22016, 64), (300, 1536, 8)])
 def test_single_job_shapes(N, K, r):
     _run([_job(N, K, r, seed=N + K + r)], f"N{N} K{K} r{r}")
 
