@@ -15,20 +15,22 @@
 //     lane c always reads bank c and a wave's 64 lookups never conflict
 //     (64 KiB).  One v_perm builds the address from a code byte and the lane
 //     column; one ds_read_b32 returns two ready bf16 weights.
-//   * MFMA v_mfma_f32_16x16x32_bf16.  Lane l = (n, q), n = l % 16, q = l / 16,
-//     supplies B operand column n (weight row n of its 16-row group).  A
-//     step covers four NF4 blocks (128 code bytes) of each of the 16 rows;
-//     lane q loads bytes 16q .. 16q+15 and 64+16q .. 64+16q+15 of its row, so
-//     the four lanes of a row read two contiguous 64-byte runs, and each of
-//     its two 16-byte pieces is half of one block.  Each piece feeds a chain
-//     of four MFMAs whose A operand is "diagonal": rows 4q .. 4q+3 of A hold
-//     the x values under lane-group q's piece and zero elsewhere.  Row m of
-//     the 16 x 16 result is then the partial dot product of weight row n
-//     with lane-group m/4's piece alone, so every lane finds its own piece's
-//     partial in its accumulator and applies that block's scale
-//     t = Q8[q_b] s2 in fp32.
-//   * x is staged in LDS (zero-padded to whole four-block steps) behind the
-//     table, with a 128-byte zero run for the off-diagonal A lanes.
+//   * Loads.  A step covers 256 code bytes (eight NF4 blocks) of each row.
+//     One 16-byte load per lane brings four whole rows' steps: lanes
+//     4r+p + 16g (r, p, g in 0..3) read chunk 4p+g of row r, so every load
+//     touches eight 128-byte lines of four rows.  (Loads spread over sixteen
+//     rows stall in the vector L1's address translation.)
+//   * MFMA v_mfma_f32_16x16x32_bf16.  B column c = 4r + p is (row r,
+//     position p); its four k-groups g are chunks 4p+g, so one MFMA covers
+//     dword j of the sixteen chunks of four rows.  A row m carries x for
+//     position m >> 2, restricted to the k-groups of one block: rows with
+//     m & 1 = h keep k-groups 2h, 2h+1 (block 2p+h of the step) and are zero
+//     elsewhere.  Result row 4p + h of column c is then the partial dot
+//     product of row r with block 2p+h alone; lane c + 16p holds it and
+//     applies the block's scale t = Q8[q_b] s2 in fp32.  x is shared by the
+//     four rows, so one A operand serves four row sets.
+//   * x is staged in LDS (zero-padded to whole steps) behind the table, with
+//     a zero run for the A lanes outside their block.
 //
 // The job table lives in device memory (written by one copy per call), so
 // one launch covers every job and the partial last wave of workgroups is
@@ -45,8 +47,10 @@ namespace {
 
 constexpr int kGvWaves = 16;                               // waves per workgroup
 constexpr int kGvThreads = 64 * kGvWaves;
-constexpr int kGvRows = kGvWaves * 16;                     // weight rows per workgroup, 16 per wave
-constexpr int kGvDepth = 4;                                // steps of codes in flight per wave (a round)
+constexpr int kGvSets = 2;                                 // sets of four rows per wave
+constexpr int kGvRows = kGvWaves * 4 * kGvSets;            // weight rows per workgroup
+constexpr int kGvDepth = 2;                                // steps of loads in flight per wave (a round)
+constexpr int kStepBlocks = 8;                             // NF4 blocks per row per step (256 code bytes)
 constexpr int kLutBytes = 256 * 64 * 4;                    // 256 entries x 64 lane columns
 constexpr int kZeroBytes = 512;                           // zero run read by the off-diagonal A lanes
 constexpr int kDownThreads = 256;
@@ -95,6 +99,7 @@ __device__ __forceinline__ f32x4_t mfma16x16x32(const bf16x8_t& a, const bf16x8_
 typedef __attribute__((address_space(3))) uint32_t lds_u32;
 typedef __attribute__((address_space(3))) u32x4_t lds_u128;
 __device__ __forceinline__ uint32_t lds_ld32(uint32_t addr) { return *(const lds_u32*)(size_t)addr; }
+__device__ __forceinline__ float lds_ldf(uint32_t addr) { return __builtin_bit_cast(float, lds_ld32(addr)); }
 __device__ __forceinline__ u32x4_t lds_ld128(uint32_t addr) { return *(const lds_u128*)(size_t)addr; }
 __device__ __forceinline__ void lds_st32(uint32_t addr, uint32_t v) { *(lds_u32*)(size_t)addr = v; }
 __device__ __forceinline__ void lds_st128(uint32_t addr, uint4 v) {
@@ -107,24 +112,6 @@ __device__ __forceinline__ bf16x8_t decode8(uint32_t c, uint32_t col) {
   const uint4 v = make_uint4(lds_ld32(perm(c, col, 0x0C0C0400u)), lds_ld32(perm(c, col, 0x0C0C0500u)),
                              lds_ld32(perm(c, col, 0x0C0C0600u)), lds_ld32(perm(c, col, 0x0C0C0700u)));
   return __builtin_bit_cast(bf16x8_t, v);
-}
-
-// Absmax codes of 16 blocks from `block` (a multiple of 8), as two separate
-// 8-byte loads: with K % 512 == 0 a row's absmax codes are a whole number of
-// 8-byte units, so neither load straddles the end of the array (the second
-// one takes its +8 through the scalar offset, which keeps the compiler from
-// fusing the pair into one 16-byte access).
-__device__ __forceinline__ void load_absmax16(rsrc_t ar, uint32_t block, uint2 (&out)[2]) {
-  out[0] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(ar, block, 0, 0));
-  out[1] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(ar, block, 8, 0));
-}
-
-// The lane's two 16-byte code pieces in one step: `off` and `off` + 64.
-struct Codes {
-  uint4 lo, hi;
-};
-__device__ __forceinline__ Codes load_codes(rsrc_t cr, uint32_t off) {
-  return Codes{buf_load16(cr, off), buf_load16(cr, off + 64u)};
 }
 
 }  // namespace
@@ -160,25 +147,24 @@ __global__ __launch_bounds__(kDownThreads) void lora_down_kernel(const GemvJob* 
 
 // Phase 2: the NF4 GEMV with the LoRA up-projection in the epilogue.
 // Workgroup = (job, tile of kGvRows rows); wave w owns rows
-// tile*kGvRows + 16w .. +15, lane (n, q) row n of them.  Loads run a round
-// (kGvDepth steps) ahead:
-//   * codes: two 16-byte loads per lane per step;
-//   * absmax codes: with kQuad (K % 512 == 0, absmax_q 8-byte aligned), one
-//     8-byte load per row per two steps, lane q taking byte q of each 4-byte
-//     step; otherwise one byte load per step;
-//   * group scales: a row of at most 32768 columns touches at most three
-//     256-block groups, so the three scales are loaded once per tile.
-template <bool kQuad>
+// tile*kGvRows + 4 kGvSets w onwards as kGvSets sets of four.  Lane l = c + 16g,
+// c = 4r + p: row r of each set, position p, k-group g.  With kPair (even
+// block count per row, 2-byte aligned absmax_q) a lane reads its two blocks'
+// absmax codes with one 2-byte load, otherwise with two byte loads.  Loads
+// run a round (kGvDepth steps) ahead; a row of at most 32768 columns touches
+// at most three 256-block groups, so their scales are loaded once per tile.
+template <bool kPair>
 __global__ __launch_bounds__(kGvThreads) void nf4_gemv_kernel(const GemvJob* __restrict__ jobs,
                                                               const int2* __restrict__ map) {
   extern __shared__ __align__(16) uint8_t lds_dyn[];  // addressed from 0 (see lds_ld32)
   const int2 m = map[blockIdx.x];
   const GemvJob& J = jobs[m.x];
   const int K = J.K, N = J.N, nblk = K >> 6;
-  const int nsteps = (nblk + 3) >> 2;
+  const int nsteps = (nblk + kStepBlocks - 1) / kStepBlocks;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int nl = lane & 15, q = lane >> 4;
-  const uint32_t xoff = kLutBytes, zoff = kLutBytes + (uint32_t)nsteps * 512u;
+  const int c = lane & 15, g = lane >> 4, r = c >> 2, p = c & 3;
+  // LDS: code-byte table | x (nsteps * 1024 bytes) | zero run | Q8 table
+  const uint32_t xoff = kLutBytes, zoff = kLutBytes + (uint32_t)nsteps * 1024u, q8off = zoff + kZeroBytes;
 
   const uint32_t nb = (uint32_t)N * (uint32_t)nblk;
   const rsrc_t cr = make_rsrc(J.codes, nb * 32u);
@@ -186,34 +172,42 @@ __global__ __launch_bounds__(kGvThreads) void nf4_gemv_kernel(const GemvJob* __r
   const rsrc_t sr = make_rsrc(J.group_scale, ((nb + 255u) >> 8) * 4u);
   const rsrc_t xr = make_rsrc(J.x, (uint32_t)K * 2u);   // zero padding comes from the range check
 
-  // The lane's row; rows past N read the first byte past the arrays (zero
-  // codes, absmax code 0, so block scale 0).  Its two pieces in step s are
-  // half (q & 1) of blocks 4s + hb and 4s + 2 + hb, hb = q >> 1.
-  const int row = m.y * kGvRows + 16 * w + nl;
-  const uint32_t rbase = (uint32_t)(row < N ? row : N) * (uint32_t)nblk;   // first block of the row
-  const uint32_t hb = (uint32_t)q >> 1;
-  const uint32_t cbase = rbase * 32u + 16u * (uint32_t)q;                   // code byte of the first piece at s = 0
+  // Row of each set; rows past N read the first byte past the arrays (zero
+  // codes, absmax code 0, so block scale 0).
+  uint32_t rb[kGvSets];   // first block of the row
+#pragma unroll
+  for (int k = 0; k < kGvSets; ++k) {
+    const int row = m.y * kGvRows + 4 * kGvSets * w + 4 * k + r;
+    rb[k] = (uint32_t)(row < N ? row : N) * (uint32_t)nblk;
+  }
+  const uint32_t chunk = 16u * (uint32_t)(4 * p + g);   // code byte of the lane's chunk within a step
+  const uint32_t pblk = 2u * (uint32_t)p;                // first of the lane's two blocks within a step
 
-  // x first (waited for before the barrier), then the row's group scales,
-  // absmax codes and the first round of codes.
+  // x first (waited for before the barrier), then the group scales and the
+  // first round of codes and absmax codes.
   constexpr int kXChunks = 4;   // 16-byte chunks per thread: K <= 32768
   uint4 xv[kXChunks];
 #pragma unroll
-  for (int c = 0; c < kXChunks; ++c) xv[c] = buf_load16(xr, 16u * (uint32_t)(tid + c * kGvThreads));
-  const uint32_t g0 = rbase >> 8;
-  const float s2a = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(sr, g0 * 4u, 0, 0));
-  const float s2b = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(sr, g0 * 4u + 4u, 0, 0));
-  const float s2c = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(sr, g0 * 4u + 8u, 0, 0));
-  uint2 aqr[2];                  // kQuad: absmax codes of the round's 16 blocks (steps 4k .. 4k+3)
-  uint32_t aqs[kGvDepth][2];     // !kQuad: the two pieces' absmax codes per step
-  if constexpr (kQuad) load_absmax16(ar, rbase, aqr);
-  Codes cs[kGvDepth];
+  for (int i = 0; i < kXChunks; ++i) xv[i] = buf_load16(xr, 16u * (uint32_t)(tid + i * kGvThreads));
+  float s2v[kGvSets][3];
+#pragma unroll
+  for (int k = 0; k < kGvSets; ++k)
+#pragma unroll
+    for (int i = 0; i < 3; ++i)
+      s2v[k][i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(sr, ((rb[k] >> 8) + i) * 4u, 0, 0));
+  uint4 cs[kGvDepth][kGvSets];
+  uint32_t aq[kGvDepth][kGvSets];   // the lane's two absmax codes, byte 0 and byte 1
   auto load_step = [&](int i, int si) __attribute__((always_inline)) {
-    cs[i] = load_codes(cr, cbase + 128u * (uint32_t)si);
-    if constexpr (!kQuad) {
-      const uint32_t b = rbase + 4u * (uint32_t)si + hb;
-      aqs[i][0] = __builtin_amdgcn_raw_buffer_load_b8(ar, b, 0, 0);
-      aqs[i][1] = __builtin_amdgcn_raw_buffer_load_b8(ar, b + 2u, 0, 0);
+#pragma unroll
+    for (int k = 0; k < kGvSets; ++k) {
+      const uint32_t b = rb[k] + kStepBlocks * (uint32_t)si + pblk;
+      cs[i][k] = buf_load16(cr, rb[k] * 32u + 256u * (uint32_t)si + chunk);
+      if constexpr (kPair) {
+        aq[i][k] = __builtin_amdgcn_raw_buffer_load_b16(ar, b, 0, 0);
+      } else {
+        aq[i][k] = __builtin_amdgcn_raw_buffer_load_b8(ar, b, 0, 0) |
+                   ((uint32_t)__builtin_amdgcn_raw_buffer_load_b8(ar, b + 1u, 0, 0) << 8);
+      }
     }
   };
 #pragma unroll
@@ -228,56 +222,65 @@ __global__ __launch_bounds__(kGvThreads) void nf4_gemv_kernel(const GemvJob* __r
   }
   // chunks past the staged x are zero (range check) and land in the zero run
 #pragma unroll
-  for (int c = 0; c < kXChunks; ++c) {
-    const int i = tid + c * kGvThreads;
-    lds_st128(i < nsteps * 32 ? xoff + 16u * i : zoff + 16u * (i & 7), xv[c]);
+  for (int i = 0; i < kXChunks; ++i) {
+    const int ci = tid + i * kGvThreads;
+    lds_st128(ci < nsteps * 64 ? xoff + 16u * ci : zoff + 16u * (ci & 7), xv[i]);
   }
   if (tid < kZeroBytes / 16) lds_st128(zoff + 16u * tid, make_uint4(0u, 0u, 0u, 0u));
+  if (tid < 256) lds_st32(q8off + 4u * tid, __builtin_bit_cast(uint32_t, q8_value((uint32_t)tid)));
   __syncthreads();
 
   const uint32_t col = 4u * lane;
-  const bool diag = (nl >> 2) == q;
-  // diagonal lanes: x under the first piece at 64q (bytes) into the step,
-  // the second 256 bytes further; off-diagonal lanes read the zero run
-  uint32_t xa = diag ? xoff + 64u * q : zoff;
-  const uint32_t xinc = diag ? 512u : 0u;
-  float acc = 0.0f;
+  // A lane (row m = c, k-group g) carries x for position m >> 2 when g lies
+  // in block half m & 1, else reads the zero run.
+  const bool xon = (g >> 1) == (c & 1);
+  uint32_t xa = xon ? xoff + 256u * (uint32_t)(c >> 2) + 64u * (uint32_t)g : zoff;
+  const uint32_t xinc = xon ? 1024u : 0u;
+  const bool holds = g == p;   // this lane's accumulator is (row r, blocks 2p, 2p+1)
+  float acc[kGvSets];
+#pragma unroll
+  for (int k = 0; k < kGvSets; ++k) acc[k] = 0.0f;
 
-  // Block scale of block `b` (its absmax code `aq`), zero past the row end.
-  // (The group scales are passed by value: choosing among variables
-  // captured by reference would make the compiler pick among their
-  // addresses and keep them in scratch memory.)
-  auto scale = [&](uint32_t aq, uint32_t bi, float s2a_, float s2b_, float s2c_) __attribute__((always_inline)) {
-    const uint32_t gi = ((rbase + bi) >> 8) - g0;
-    const float s2 = gi == 0 ? s2a_ : gi == 1 ? s2b_ : s2c_;
-    return bi < (uint32_t)nblk ? block_scale(aq, s2) : 0.0f;   // ragged last step
+  // Block scales.  The lane's two blocks of a step lie in one 256-block
+  // group when the row has an even number of blocks (kPair); otherwise each
+  // block finds its own group.  Q8[q] comes from a table in LDS.  Blocks
+  // past the row end (a ragged last step) meet zero-padded x, so their
+  // partial is zero and their scale (finite) needs no masking.  The group
+  // scales come in by value: choosing among variables captured by reference
+  // would make the compiler pick among their addresses and keep them in
+  // scratch memory.
+  uint32_t gb1[kGvSets], gb2[kGvSets];   // first block (within the row) of the row's second and third group
+#pragma unroll
+  for (int k = 0; k < kGvSets; ++k) {
+    gb1[k] = 256u - (rb[k] & 255u);
+    gb2[k] = gb1[k] + 256u;
+  }
+  auto group_scale = [&](int k, uint32_t bi, float sa, float sb, float sc) __attribute__((always_inline)) {
+    return bi >= gb2[k] ? sc : bi >= gb1[k] ? sb : sa;
   };
-  // One step: two chains of four MFMAs over the lane's two pieces.
-  auto step = [&](const Codes& c, uint32_t aq0, uint32_t aq1, int s, float s2a_, float s2b_, float s2c_)
-                  __attribute__((always_inline)) {
-    const uint32_t bi = 4u * (uint32_t)s + hb;   // block index within the row
-    const float t0 = scale(aq0, bi, s2a_, s2b_, s2c_);
-    const float t1 = scale(aq1, bi + 2u, s2a_, s2b_, s2c_);
-    f32x4_t D0 = {0.0f, 0.0f, 0.0f, 0.0f}, D1 = {0.0f, 0.0f, 0.0f, 0.0f};
-    const uint32_t lw[4] = {c.lo.x, c.lo.y, c.lo.z, c.lo.w}, hw[4] = {c.hi.x, c.hi.y, c.hi.z, c.hi.w};
+  auto step = [&](int i, int s) __attribute__((always_inline)) {
+    f32x4_t D[kGvSets];
+#pragma unroll
+    for (int k = 0; k < kGvSets; ++k) D[k] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const bf16x8_t a0 = __builtin_bit_cast(bf16x8_t, lds_ld128(xa + 16u * j));
-      const bf16x8_t a1 = __builtin_bit_cast(bf16x8_t, lds_ld128(xa + 256u + 16u * j));
-      D0 = mfma16x16x32(a0, decode8(lw[j], col), D0);
-      D1 = mfma16x16x32(a1, decode8(hw[j], col), D1);
+      const bf16x8_t a = __builtin_bit_cast(bf16x8_t, lds_ld128(xa + 16u * j));
+#pragma unroll
+      for (int k = 0; k < kGvSets; ++k) {
+        const uint32_t cw = j == 0 ? cs[i][k].x : j == 1 ? cs[i][k].y : j == 2 ? cs[i][k].z : cs[i][k].w;
+        D[k] = mfma16x16x32(a, decode8(cw, col), D[k]);
+      }
     }
-    acc += t0 * D0[0];
-    acc += t1 * D1[0];
+    const uint32_t bi = kStepBlocks * (uint32_t)s + pblk;
+#pragma unroll
+    for (int k = 0; k < kGvSets; ++k) {
+      const float q0 = lds_ldf(q8off + 4u * (aq[i][k] & 0xFFu));
+      const float q1 = lds_ldf(q8off + 4u * ((aq[i][k] >> 8) & 0xFFu));
+      const float s20 = group_scale(k, bi, s2v[k][0], s2v[k][1], s2v[k][2]);
+      const float s21 = kPair ? s20 : group_scale(k, bi + 1u, s2v[k][0], s2v[k][1], s2v[k][2]);
+      acc[k] += (q0 * s20) * D[k][0] + (q1 * s21) * D[k][1];
+    }
     xa += xinc;
-  };
-  auto aq_of = [&](int i, uint32_t byte) __attribute__((always_inline)) -> uint32_t {   // kQuad
-    const uint32_t d = (i & 1) ? aqr[i >> 1].y : aqr[i >> 1].x;
-    return __builtin_amdgcn_ubfe(d, 8u * byte, 8u);
-  };
-  auto run_step = [&](int i, int s) __attribute__((always_inline)) {
-    if constexpr (kQuad) step(cs[i], aq_of(i, hb), aq_of(i, hb + 2u), s, s2a, s2b, s2c);
-    else step(cs[i], aqs[i][0], aqs[i][1], s, s2a, s2b, s2c);
   };
 
   // Rounds of kGvDepth steps with no branch inside, so the load counters
@@ -285,62 +288,58 @@ __global__ __launch_bounds__(kGvThreads) void nf4_gemv_kernel(const GemvJob* __r
   // later (clamped to the last step: a re-read of lines already in cache).
   int s0 = 0;
   for (; s0 + kGvDepth <= nsteps; s0 += kGvDepth) {
-    uint2 aqn[2];
-    if constexpr (kQuad) {
-      load_absmax16(ar, rbase + 4u * (uint32_t)(s0 + kGvDepth), aqn);   // the next round
-      __builtin_amdgcn_sched_barrier(0);
-    }
 #pragma unroll
     for (int i = 0; i < kGvDepth; ++i) {
       const int s = s0 + i;
-      run_step(i, s);
+      step(i, s);
       load_step(i, s + kGvDepth < nsteps ? s + kGvDepth : nsteps - 1);
       __builtin_amdgcn_sched_barrier(0);   // issue the refill here, a round ahead of its use
-    }
-    if constexpr (kQuad) {
-      aqr[0] = aqn[0];
-      aqr[1] = aqn[1];
     }
   }
 #pragma unroll
   for (int i = 0; i < kGvDepth - 1; ++i)
-    if (s0 + i < nsteps) run_step(i, s0 + i);   // uniform
+    if (s0 + i < nsteps) step(i, s0 + i);   // uniform
 
-  // LoRA up-projection: the four lanes of a row take alternate 8-rank chunks
-  const bool valid = row < N;
-  float lora = 0.0f;
-  if (J.r > 0 && valid) {
-    const bf16_t* brp = J.B + (int64_t)row * J.r;
-    for (int i = 8 * q; i < J.r; i += 32) {
-      const uint4 v = *reinterpret_cast<const uint4*>(brp + i);
-      const float4 u0 = *reinterpret_cast<const float4*>(J.u + i);
-      const float4 u1 = *reinterpret_cast<const float4*>(J.u + i + 4);
-      lora += bf2f(v.x & 0xFFFFu) * u0.x + bf2f(v.x >> 16) * u0.y + bf2f(v.y & 0xFFFFu) * u0.z +
-              bf2f(v.y >> 16) * u0.w + bf2f(v.z & 0xFFFFu) * u1.x + bf2f(v.z >> 16) * u1.y +
-              bf2f(v.w & 0xFFFFu) * u1.z + bf2f(v.w >> 16) * u1.w;
+  // Per set: the row total is the sum over the four lanes holding it
+  // (c = 4r + p, g = p); the LoRA up-projection is split over the sixteen
+  // lanes of the row by 8-rank chunks 4g + p.  One reduction over g (lanes
+  // 16 and 32 apart) and p (1 and 2 apart) adds both.
+#pragma unroll
+  for (int k = 0; k < kGvSets; ++k) {
+    const int row = m.y * kGvRows + 4 * kGvSets * w + 4 * k + r;
+    const bool valid = row < N;
+    float lora = 0.0f;
+    if (J.r > 0 && valid) {
+      const bf16_t* brp = J.B + (int64_t)row * J.r;
+      for (int i = 8 * (4 * g + p); i < J.r; i += 128) {
+        const uint4 v = *reinterpret_cast<const uint4*>(brp + i);
+        const float4 u0 = *reinterpret_cast<const float4*>(J.u + i);
+        const float4 u1 = *reinterpret_cast<const float4*>(J.u + i + 4);
+        lora += bf2f(v.x & 0xFFFFu) * u0.x + bf2f(v.x >> 16) * u0.y + bf2f(v.y & 0xFFFFu) * u0.z +
+                bf2f(v.y >> 16) * u0.w + bf2f(v.z & 0xFFFFu) * u1.x + bf2f(v.z >> 16) * u1.y +
+                bf2f(v.w & 0xFFFFu) * u1.z + bf2f(v.w >> 16) * u1.w;
+      }
     }
-  }
-  float part = acc;
-  part += __shfl_xor(part, 16);
-  part += __shfl_xor(part, 32);
-  lora += __shfl_xor(lora, 16);
-  lora += __shfl_xor(lora, 32);
-  if (q == 0 && valid) {
-    const float y = part + J.s * lora;
-    J.y[row] = (bf16_t)(pack_bf16x2(y, 0.0f) & 0xFFFFu);
+    float part = (holds ? acc[k] : 0.0f) + J.s * lora;
+    part += __shfl_xor(part, 16);
+    part += __shfl_xor(part, 32);
+    part += __shfl_xor(part, 1);
+    part += __shfl_xor(part, 2);
+    if (lane == 4 * r && valid) J.y[row] = (bf16_t)(pack_bf16x2(part, 0.0f) & 0xFFFFu);
   }
 }
 
 namespace {
 
-// Tiles of jobs whose absmax rows can be read 8 bytes at a time.
-bool quad_job(const GemvJob& J) {
-  return (J.K % 512) == 0 && (reinterpret_cast<uintptr_t>(J.absmax_q) & 7u) == 0;
+// Tiles of jobs whose absmax codes can be read two at a time (an even
+// number of blocks per row and a 2-byte aligned array).
+bool pair_job(const GemvJob& J) {
+  return (J.K % 128) == 0 && (reinterpret_cast<uintptr_t>(J.absmax_q) & 1u) == 0;
 }
 
 struct TablePlan {
-  size_t jobs_off, quad_off, other_off, down_off, total;
-  int n_quad, n_other, n_down;
+  size_t jobs_off, pair_off, other_off, down_off, total;
+  int n_pair, n_other, n_down;
 };
 
 size_t up256(size_t x) { return (x + 255) / 256 * 256; }
@@ -348,30 +347,30 @@ size_t up256(size_t x) { return (x + 255) / 256 * 256; }
 TablePlan plan_table(const GemvJob* jobs, int njobs) {
   TablePlan p{};
   for (int i = 0; i < njobs; ++i) {
-    (quad_job(jobs[i]) ? p.n_quad : p.n_other) += (jobs[i].N + kGvRows - 1) / kGvRows;
+    (pair_job(jobs[i]) ? p.n_pair : p.n_other) += (jobs[i].N + kGvRows - 1) / kGvRows;
     if (jobs[i].r > 0) p.n_down += (jobs[i].r + kDownRows - 1) / kDownRows;
   }
   p.jobs_off = 0;
-  p.quad_off = up256((size_t)njobs * sizeof(GemvJob));
-  p.other_off = p.quad_off + up256((size_t)p.n_quad * sizeof(int2));
+  p.pair_off = up256((size_t)njobs * sizeof(GemvJob));
+  p.other_off = p.pair_off + up256((size_t)p.n_pair * sizeof(int2));
   p.down_off = p.other_off + up256((size_t)p.n_other * sizeof(int2));
   p.total = p.down_off + up256((size_t)p.n_down * sizeof(int2));
   return p;
 }
 
-template <bool kQuad>
+template <bool kPair>
 hipError_t launch_main(const GemvJob* djobs, const int2* map, int n, size_t lds, hipStream_t st) {
   if (n == 0) return hipSuccess;
   // The kernel addresses its LDS from 0, which holds only while the
   // compiler has given it no static LDS.
   hipFuncAttributes fa{};
-  hipError_t e = hipFuncGetAttributes(&fa, reinterpret_cast<const void*>(&nf4_gemv_kernel<kQuad>));
+  hipError_t e = hipFuncGetAttributes(&fa, reinterpret_cast<const void*>(&nf4_gemv_kernel<kPair>));
   if (e != hipSuccess) return e;
   if (fa.sharedSizeBytes != 0) return hipErrorInvalidKernelFile;
-  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&nf4_gemv_kernel<kQuad>),
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&nf4_gemv_kernel<kPair>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(nf4_gemv_kernel<kQuad>, dim3(n), dim3(kGvThreads), lds, st, djobs, map);
+  hipLaunchKernelGGL(nf4_gemv_kernel<kPair>, dim3(n), dim3(kGvThreads), lds, st, djobs, map);
   return hipGetLastError();
 }
 
@@ -388,22 +387,22 @@ size_t gemv_table_bound(int njobs, int64_t max_rows) {
 size_t gemv_table_bytes(const GemvJob* jobs, int njobs) { return plan_table(jobs, njobs).total; }
 
 size_t gemv_lds_bytes(int64_t K) {
-  const int64_t nsteps = (K / 64 + 3) / 4;
-  return (size_t)kLutBytes + (size_t)nsteps * 512 + kZeroBytes;
+  const int64_t nsteps = (K / 64 + kStepBlocks - 1) / kStepBlocks;
+  return (size_t)kLutBytes + (size_t)nsteps * 1024 + kZeroBytes + 256 * sizeof(float);
 }
 
 hipError_t launch_gemv(const GemvJob* jobs, int njobs, void* table, hipStream_t st) {
   const TablePlan p = plan_table(jobs, njobs);
   std::vector<uint8_t> host(p.total, 0);
   std::memcpy(host.data() + p.jobs_off, jobs, (size_t)njobs * sizeof(GemvJob));
-  int2* qm = reinterpret_cast<int2*>(host.data() + p.quad_off);
+  int2* pm = reinterpret_cast<int2*>(host.data() + p.pair_off);
   int2* om = reinterpret_cast<int2*>(host.data() + p.other_off);
   int2* dm = reinterpret_cast<int2*>(host.data() + p.down_off);
   int maxK = 0;
-  for (int i = 0, iq = 0, io = 0, id = 0; i < njobs; ++i) {
+  for (int i = 0, ip = 0, io = 0, id = 0; i < njobs; ++i) {
     const GemvJob& J = jobs[i];
-    const bool quad = quad_job(J);
-    for (int t = 0; t < (J.N + kGvRows - 1) / kGvRows; ++t) (quad ? qm[iq++] : om[io++]) = make_int2(i, t);
+    const bool pair = pair_job(J);
+    for (int t = 0; t < (J.N + kGvRows - 1) / kGvRows; ++t) (pair ? pm[ip++] : om[io++]) = make_int2(i, t);
     if (J.r > 0)
       for (int t = 0; t < (J.r + kDownRows - 1) / kDownRows; ++t) dm[id++] = make_int2(i, t);
     if (J.K > maxK) maxK = J.K;
@@ -419,7 +418,7 @@ hipError_t launch_gemv(const GemvJob* jobs, int njobs, void* table, hipStream_t 
     if (e != hipSuccess) return e;
   }
   const size_t lds = gemv_lds_bytes(maxK);
-  e = launch_main<true>(djobs, reinterpret_cast<const int2*>(dev + p.quad_off), p.n_quad, lds, st);
+  e = launch_main<true>(djobs, reinterpret_cast<const int2*>(dev + p.pair_off), p.n_pair, lds, st);
   if (e != hipSuccess) return e;
   return launch_main<false>(djobs, reinterpret_cast<const int2*>(dev + p.other_off), p.n_other, lds, st);
 }
