@@ -373,6 +373,8 @@ qlora_status qlora_gemv(const qlora_gemv_job* jobs, int32_t njobs, void* ws, siz
     if (!J.x || !J.y) return QLORA_E_NULL;
     if (!aligned16(J.x) || !aligned16(J.y)) return QLORA_E_ALIGN;
     if ((st = check_rank(J.r, J.A, J.B)) != QLORA_OK) return st;
+    // B [rows x r] addressed with 32-bit byte offsets
+    if (J.r > 0 && J.W->rows > (int64_t)0xFFFFFFFF / (2 * (int64_t)J.r)) return QLORA_E_UNSUPPORTED;
   }
   if (!ws) return QLORA_E_NULL;
   if (!aligned16(ws)) return QLORA_E_ALIGN;
@@ -394,8 +396,9 @@ qlora_status qlora_gemv(const qlora_gemv_job* jobs, int32_t njobs, void* ws, siz
     D.s = J.r > 0 ? (float)((double)J.alpha / (double)J.r) : 0.0f;
   }
   const size_t u_bytes = align_up((size_t)njobs * kMaxRank * sizeof(float));
-  if (ws_bytes < u_bytes || ws_bytes - u_bytes < gemv_table_bytes(buf.data(), njobs)) return QLORA_E_WORKSPACE;
-  return hip_status(launch_gemv(buf.data(), njobs, ws_at(ws, u_bytes), (hipStream_t)stream));
+  const size_t table_bytes = gemv_table_bound(njobs, 1);
+  if (ws_bytes < u_bytes || ws_bytes - u_bytes < table_bytes) return QLORA_E_WORKSPACE;
+  return hip_status(launch_gemv(buf.data(), njobs, ws_at(ws, u_bytes), table_bytes, (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -28,13 +28,17 @@
 //     elsewhere.  Result row 4p + h of column c is then the partial dot
 //     product of row r with block 2p+h alone; lane c + 16p holds it and
 //     applies the block's scale t = Q8[q_b] s2 in fp32.  x is shared by the
-//     four rows, so one A operand serves four row sets.
-//   * x is staged in LDS (zero-padded to whole steps) behind the table, with
-//     a zero run for the A lanes outside their block.
+//     row sets of a wave, so one A operand serves all of them.
+//   * Persistent workgroups.  One 16-wave workgroup per CU (the 64 KiB table
+//     and x fill its LDS) walks a contiguous, cost-balanced range of row
+//     tiles.  The tables are built once; x is restaged only when the job's
+//     x changes; the code loads run one step ahead straight across tile
+//     boundaries, and each tile's LoRA rows and the next tile's group scales
+//     are fetched when the tile starts, so no tile boundary waits on memory.
 //
 // The job table lives in device memory (written by one copy per call), so
-// one launch covers every job and the partial last wave of workgroups is
-// paid once per call instead of once per small batch.
+// one launch covers every job.
+#include <algorithm>
 #include <cstring>
 #include <vector>
 
@@ -49,10 +53,12 @@ constexpr int kGvWaves = 16;                               // waves per workgrou
 constexpr int kGvThreads = 64 * kGvWaves;
 constexpr int kGvSets = 2;                                 // sets of four rows per wave
 constexpr int kGvRows = kGvWaves * 4 * kGvSets;            // weight rows per workgroup
-constexpr int kGvDepth = 2;                                // steps of loads in flight per wave (a round)
 constexpr int kStepBlocks = 8;                             // NF4 blocks per row per step (256 code bytes)
 constexpr int kLutBytes = 256 * 64 * 4;                    // 256 entries x 64 lane columns
-constexpr int kZeroBytes = 512;                           // zero run read by the off-diagonal A lanes
+constexpr int kZeroBytes = 512;                            // zero run read by the off-diagonal A lanes
+constexpr int kQ8Bytes = 256 * 4;                          // Q8[q] = RN32(q / 255) as fp32
+constexpr int kQ8Off = kLutBytes, kZeroOff = kQ8Off + kQ8Bytes, kXOff = kZeroOff + kZeroBytes;   // LDS layout
+constexpr int kMaxGvGroups = 1024;                         // persistent workgroups per launch, at most
 constexpr int kDownThreads = 256;
 constexpr int kDownRows = 4;                               // adapter rows per workgroup (one per wave)
 static_assert(kGvThreads == 1024, "the table fill below assumes 16 waves");
@@ -145,232 +151,306 @@ __global__ __launch_bounds__(kDownThreads) void lora_down_kernel(const GemvJob* 
   if (lane == 0) J.u[row] = acc;
 }
 
-// Phase 2: the NF4 GEMV with the LoRA up-projection in the epilogue.
-// Workgroup = (job, tile of kGvRows rows); wave w owns rows
-// tile*kGvRows + 4 kGvSets w onwards as kGvSets sets of four.  Lane l = c + 16g,
-// c = 4r + p: row r of each set, position p, k-group g.  With kPair (even
-// block count per row, 2-byte aligned absmax_q) a lane reads its two blocks'
-// absmax codes with one 2-byte load, otherwise with two byte loads.  Loads
-// run a round (kGvDepth steps) ahead; a row of at most 32768 columns touches
-// at most three 256-block groups, so their scales are loaded once per tile.
+// Phase 2: the NF4 GEMV and the LoRA up-projection, persistent.
+//
+// Workgroup b owns segments segs[range[b] .. range[b+1]); a segment is
+// (job, first tile, tile count) of consecutive tiles of one job.  Within a
+// tile of kGvRows rows, wave w owns rows 4 kGvSets w + 4k + r (set k, row r
+// of the set).  Lane l = c + 16g, c = 4r + p: row r, position p, k-group g.
+// With kPair (even block count per row, 2-byte aligned absmax_q) a lane
+// reads its two blocks' absmax codes with one 2-byte load, otherwise with two
+// byte loads.  A row of at most 32768 columns touches at most three
+// 256-block groups, so three group scales per row cover a tile.
 template <bool kPair>
 __global__ __launch_bounds__(kGvThreads) void nf4_gemv_kernel(const GemvJob* __restrict__ jobs,
-                                                              const int2* __restrict__ map) {
+                                                              const int4* __restrict__ segs,
+                                                              const int* __restrict__ range, int max_steps) {
   extern __shared__ __align__(16) uint8_t lds_dyn[];  // addressed from 0 (see lds_ld32)
-  const int2 m = map[blockIdx.x];
-  const GemvJob& J = jobs[m.x];
-  const int K = J.K, N = J.N, nblk = K >> 6;
-  const int nsteps = (nblk + kStepBlocks - 1) / kStepBlocks;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int c = lane & 15, g = lane >> 4, r = c >> 2, p = c & 3;
-  // LDS: code-byte table | x (nsteps * 1024 bytes) | zero run | Q8 table
-  const uint32_t xoff = kLutBytes, zoff = kLutBytes + (uint32_t)nsteps * 1024u, q8off = zoff + kZeroBytes;
+  const uint32_t col = 4u * lane;
 
-  const uint32_t nb = (uint32_t)N * (uint32_t)nblk;
-  const rsrc_t cr = make_rsrc(J.codes, nb * 32u);
-  const rsrc_t ar = make_rsrc(J.absmax_q, nb);
-  const rsrc_t sr = make_rsrc(J.group_scale, ((nb + 255u) >> 8) * 4u);
-  const rsrc_t xr = make_rsrc(J.x, (uint32_t)K * 2u);   // zero padding comes from the range check
-
-  // Row of each set; rows past N read the first byte past the arrays (zero
-  // codes, absmax code 0, so block scale 0).
-  uint32_t rb[kGvSets];   // first block of the row
-#pragma unroll
-  for (int k = 0; k < kGvSets; ++k) {
-    const int row = m.y * kGvRows + 4 * kGvSets * w + 4 * k + r;
-    rb[k] = (uint32_t)(row < N ? row : N) * (uint32_t)nblk;
-  }
-  const uint32_t chunk = 16u * (uint32_t)(4 * p + g);   // code byte of the lane's chunk within a step
-  const uint32_t pblk = 2u * (uint32_t)p;                // first of the lane's two blocks within a step
-
-  // x first (waited for before the barrier), then the group scales and the
-  // first round of codes and absmax codes.
-  constexpr int kXChunks = 4;   // 16-byte chunks per thread: K <= 32768
-  uint4 xv[kXChunks];
-#pragma unroll
-  for (int i = 0; i < kXChunks; ++i) xv[i] = buf_load16(xr, 16u * (uint32_t)(tid + i * kGvThreads));
-  float s2v[kGvSets][3];
-#pragma unroll
-  for (int k = 0; k < kGvSets; ++k)
-#pragma unroll
-    for (int i = 0; i < 3; ++i)
-      s2v[k][i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(sr, ((rb[k] >> 8) + i) * 4u, 0, 0));
-  uint4 cs[kGvDepth][kGvSets];
-  uint32_t aq[kGvDepth][kGvSets];   // the lane's two absmax codes, byte 0 and byte 1
-  auto load_step = [&](int i, int si) __attribute__((always_inline)) {
-#pragma unroll
-    for (int k = 0; k < kGvSets; ++k) {
-      const uint32_t b = rb[k] + kStepBlocks * (uint32_t)si + pblk;
-      cs[i][k] = buf_load16(cr, rb[k] * 32u + 256u * (uint32_t)si + chunk);
-      if constexpr (kPair) {
-        aq[i][k] = __builtin_amdgcn_raw_buffer_load_b16(ar, b, 0, 0);
-      } else {
-        aq[i][k] = __builtin_amdgcn_raw_buffer_load_b8(ar, b, 0, 0) |
-                   ((uint32_t)__builtin_amdgcn_raw_buffer_load_b8(ar, b + 1u, 0, 0) << 8);
-      }
-    }
-  };
-#pragma unroll
-  for (int i = 0; i < kGvDepth; ++i) load_step(i, i < nsteps ? i : nsteps - 1);
-
-  // table: thread (w, lane) writes entries e = w + 16 i, column lane
+  // tables, once: thread (w, lane) writes code-byte entries e = w + 16 i of
+  // column lane; the first 256 threads write Q8; the first 32 the zero run
   {
     const uint32_t lo = level_bf16(__builtin_amdgcn_readfirstlane(w));   // w is wave-uniform: a scalar load
 #pragma unroll
     for (int i = 0; i < 16; ++i)
       lds_st32((uint32_t)(w + 16 * i) * 256u + 4u * lane, lo | (level_bf16(i) << 16));
+    if (tid < 256) lds_st32(kQ8Off + 4u * tid, __builtin_bit_cast(uint32_t, q8_value((uint32_t)tid)));
+    if (tid < kZeroBytes / 16) lds_st128(kZeroOff + 16u * tid, make_uint4(0u, 0u, 0u, 0u));
   }
-  // chunks past the staged x are zero (range check) and land in the zero run
-#pragma unroll
-  for (int i = 0; i < kXChunks; ++i) {
-    const int ci = tid + i * kGvThreads;
-    lds_st128(ci < nsteps * 64 ? xoff + 16u * ci : zoff + 16u * (ci & 7), xv[i]);
-  }
-  if (tid < kZeroBytes / 16) lds_st128(zoff + 16u * tid, make_uint4(0u, 0u, 0u, 0u));
-  if (tid < 256) lds_st32(q8off + 4u * tid, __builtin_bit_cast(uint32_t, q8_value((uint32_t)tid)));
-  __syncthreads();
 
-  const uint32_t col = 4u * lane;
   // A lane (row m = c, k-group g) carries x for position m >> 2 when g lies
   // in block half m & 1, else reads the zero run.
   const bool xon = (g >> 1) == (c & 1);
-  uint32_t xa = xon ? xoff + 256u * (uint32_t)(c >> 2) + 64u * (uint32_t)g : zoff;
+  const uint32_t xa0 = xon ? kXOff + 256u * (uint32_t)(c >> 2) + 64u * (uint32_t)g : kZeroOff;
   const uint32_t xinc = xon ? 1024u : 0u;
-  const bool holds = g == p;   // this lane's accumulator is (row r, blocks 2p, 2p+1)
-  float acc[kGvSets];
-#pragma unroll
-  for (int k = 0; k < kGvSets; ++k) acc[k] = 0.0f;
+  const bool holds = g == p;                       // the lane's accumulators are (row r, blocks 2p, 2p+1)
+  const uint32_t chunk = 16u * (uint32_t)(4 * p + g);   // code byte of the lane's chunk within a step
+  const uint32_t pblk = 2u * (uint32_t)p;               // first of the lane's two blocks within a step
+  const uint32_t rchunk = (uint32_t)(4 * g + p);        // the lane's 8-rank chunk of the LoRA term
 
-  // Block scales.  The lane's two blocks of a step lie in one 256-block
-  // group when the row has an even number of blocks (kPair); otherwise each
-  // block finds its own group.  Q8[q] comes from a table in LDS.  Blocks
-  // past the row end (a ragged last step) meet zero-padded x, so their
-  // partial is zero and their scale (finite) needs no masking.  The group
-  // scales come in by value: choosing among variables captured by reference
-  // would make the compiler pick among their addresses and keep them in
-  // scratch memory.
-  uint32_t gb1[kGvSets], gb2[kGvSets];   // first block (within the row) of the row's second and third group
+  const void* staged = nullptr;
+  for (int si = range[blockIdx.x]; si < range[blockIdx.x + 1]; ++si) {
+    const int4 sg = segs[si];
+    const GemvJob& J = jobs[sg.x];
+    const int K = J.K, N = J.N, nblk = K >> 6, R = J.r;
+    const int nsteps = (nblk + kStepBlocks - 1) / kStepBlocks;
+    const uint32_t nb = (uint32_t)N * (uint32_t)nblk;
+    const rsrc_t cr = make_rsrc(J.codes, nb * 32u);
+    const rsrc_t ar = make_rsrc(J.absmax_q, nb);
+    const rsrc_t sr = make_rsrc(J.group_scale, ((nb + 255u) >> 8) * 4u);
+    const rsrc_t br = make_rsrc(J.B, (uint32_t)N * (uint32_t)R * 2u);
+    const rsrc_t ur = make_rsrc(J.u, (uint32_t)R * 4u);
+
+    if (J.x != staged) {   // uniform: restage x (zero-padded to whole steps)
+      const rsrc_t xr = make_rsrc(J.x, (uint32_t)K * 2u);
+      constexpr int kXChunks = 4;   // 16-byte chunks per thread: K <= 32768
+      uint4 xv[kXChunks];
 #pragma unroll
-  for (int k = 0; k < kGvSets; ++k) {
-    gb1[k] = 256u - (rb[k] & 255u);
-    gb2[k] = gb1[k] + 256u;
-  }
-  auto group_scale = [&](int k, uint32_t bi, float sa, float sb, float sc) __attribute__((always_inline)) {
-    return bi >= gb2[k] ? sc : bi >= gb1[k] ? sb : sa;
-  };
-  auto step = [&](int i, int s) __attribute__((always_inline)) {
-    f32x4_t D[kGvSets];
+      for (int i = 0; i < kXChunks; ++i) xv[i] = buf_load16(xr, 16u * (uint32_t)(tid + i * kGvThreads));
+      __syncthreads();   // every wave is done with the previous x
 #pragma unroll
-    for (int k = 0; k < kGvSets; ++k) D[k] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+      for (int i = 0; i < kXChunks; ++i) {
+        const int ci = tid + i * kGvThreads;
+        if (ci < max_steps * 64) lds_st128(kXOff + 16u * ci, xv[i]);
+      }
+      __syncthreads();
+      staged = J.x;
+    }
+
+    // The lane's u chunk (zero past r: range check).
+    const uint4 u0b = buf_load16(ur, 32u * rchunk), u1b = buf_load16(ur, 32u * rchunk + 16u);
+    const float uv[8] = {u2f(u0b.x), u2f(u0b.y), u2f(u0b.z), u2f(u0b.w),
+                         u2f(u1b.x), u2f(u1b.y), u2f(u1b.z), u2f(u1b.w)};
+
+    // Row of set k in tile t; rows past N read the first byte past the
+    // arrays (zero codes, absmax code 0, so block scale 0).
+    const int t_first = sg.y, t_last = sg.y + sg.z - 1;
+    auto row_of = [&](int t, int k) __attribute__((always_inline)) {
+      return t * kGvRows + 4 * kGvSets * w + 4 * k + r;
+    };
+    auto rbase_of = [&](int t, int k) __attribute__((always_inline)) -> uint32_t {
+      const int row = row_of(t, k);
+      return (uint32_t)(row < N ? row : N) * (uint32_t)nblk;
+    };
+    uint32_t rbc[kGvSets], rbn[kGvSets];   // first block of the row: this tile, next tile
+    float s2c[kGvSets][3], s2n[kGvSets][3];
+    auto load_s2 = [&](float (&dst)[kGvSets][3], const uint32_t (&rb)[kGvSets]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const bf16x8_t a = __builtin_bit_cast(bf16x8_t, lds_ld128(xa + 16u * j));
+      for (int k = 0; k < kGvSets; ++k)
+#pragma unroll
+        for (int i = 0; i < 3; ++i)
+          dst[k][i] = u2f(__builtin_amdgcn_raw_buffer_load_b32(sr, ((rb[k] >> 8) + i) * 4u, 0, 0));
+    };
+    // one step's loads: the chunk of codes and the two absmax codes per set
+    uint4 cs[kGvSets];
+    uint32_t aq[kGvSets];
+    auto load_step = [&](uint4 (&c_)[kGvSets], uint32_t (&a_)[kGvSets], const uint32_t (&rb)[kGvSets], int s)
+                         __attribute__((always_inline)) {
 #pragma unroll
       for (int k = 0; k < kGvSets; ++k) {
-        const uint32_t cw = j == 0 ? cs[i][k].x : j == 1 ? cs[i][k].y : j == 2 ? cs[i][k].z : cs[i][k].w;
-        D[k] = mfma16x16x32(a, decode8(cw, col), D[k]);
+        c_[k] = buf_load16(cr, rb[k] * 32u + 256u * (uint32_t)s + chunk);
+        const uint32_t b = rb[k] + kStepBlocks * (uint32_t)s + pblk;
+        if constexpr (kPair) {
+          a_[k] = __builtin_amdgcn_raw_buffer_load_b16(ar, b, 0, 0);
+        } else {
+          a_[k] = __builtin_amdgcn_raw_buffer_load_b8(ar, b, 0, 0) |
+                  ((uint32_t)__builtin_amdgcn_raw_buffer_load_b8(ar, b + 1u, 0, 0) << 8);
+        }
       }
-    }
-    const uint32_t bi = kStepBlocks * (uint32_t)s + pblk;
+    };
 #pragma unroll
     for (int k = 0; k < kGvSets; ++k) {
-      const float q0 = lds_ldf(q8off + 4u * (aq[i][k] & 0xFFu));
-      const float q1 = lds_ldf(q8off + 4u * ((aq[i][k] >> 8) & 0xFFu));
-      const float s20 = group_scale(k, bi, s2v[k][0], s2v[k][1], s2v[k][2]);
-      const float s21 = kPair ? s20 : group_scale(k, bi + 1u, s2v[k][0], s2v[k][1], s2v[k][2]);
-      acc[k] += (q0 * s20) * D[k][0] + (q1 * s21) * D[k][1];
+      rbc[k] = rbase_of(t_first, k);
+      rbn[k] = rbase_of(t_first + 1 <= t_last ? t_first + 1 : t_last, k);
     }
-    xa += xinc;
-  };
+    load_s2(s2c, rbc);
+    load_step(cs, aq, rbc, 0);
 
-  // Rounds of kGvDepth steps with no branch inside, so the load counters
-  // are tracked exactly; each step refills its slot with the step one round
-  // later (clamped to the last step: a re-read of lines already in cache).
-  int s0 = 0;
-  for (; s0 + kGvDepth <= nsteps; s0 += kGvDepth) {
+    for (int t = t_first; t <= t_last; ++t) {
+      // tile start: this tile's LoRA rows and the next tile's group scales
+      uint4 bq[kGvSets];
 #pragma unroll
-    for (int i = 0; i < kGvDepth; ++i) {
-      const int s = s0 + i;
-      step(i, s);
-      load_step(i, s + kGvDepth < nsteps ? s + kGvDepth : nsteps - 1);
-      __builtin_amdgcn_sched_barrier(0);   // issue the refill here, a round ahead of its use
-    }
-  }
+      for (int k = 0; k < kGvSets; ++k) {
+        const int row = row_of(t, k);
+        bq[k] = buf_load16(br, (uint32_t)(row < N ? row : N) * (uint32_t)R * 2u + 16u * rchunk);
+      }
+      load_s2(s2n, rbn);
+      uint32_t gb1[kGvSets], gb2[kGvSets];   // first block (within the row) of its second and third group
 #pragma unroll
-  for (int i = 0; i < kGvDepth - 1; ++i)
-    if (s0 + i < nsteps) step(i, s0 + i);   // uniform
+      for (int k = 0; k < kGvSets; ++k) {
+        gb1[k] = 256u - (rbc[k] & 255u);
+        gb2[k] = gb1[k] + 256u;
+      }
+      float acc[kGvSets];
+#pragma unroll
+      for (int k = 0; k < kGvSets; ++k) acc[k] = 0.0f;
+      uint32_t xa = xa0;
 
-  // Per set: the row total is the sum over the four lanes holding it
-  // (c = 4r + p, g = p); the LoRA up-projection is split over the sixteen
-  // lanes of the row by 8-rank chunks 4g + p.  One reduction over g (lanes
-  // 16 and 32 apart) and p (1 and 2 apart) adds both.
+      for (int s = 0; s < nsteps; ++s) {
+        // the next step's loads first: this tile's step s+1, or the next
+        // tile's step 0 (on the last tile, a re-read of its own last step)
+        const bool more = s + 1 < nsteps;
+        uint32_t rbl[kGvSets];
 #pragma unroll
-  for (int k = 0; k < kGvSets; ++k) {
-    const int row = m.y * kGvRows + 4 * kGvSets * w + 4 * k + r;
-    const bool valid = row < N;
-    float lora = 0.0f;
-    if (J.r > 0 && valid) {
-      const bf16_t* brp = J.B + (int64_t)row * J.r;
-      for (int i = 8 * (4 * g + p); i < J.r; i += 128) {
-        const uint4 v = *reinterpret_cast<const uint4*>(brp + i);
-        const float4 u0 = *reinterpret_cast<const float4*>(J.u + i);
-        const float4 u1 = *reinterpret_cast<const float4*>(J.u + i + 4);
-        lora += bf2f(v.x & 0xFFFFu) * u0.x + bf2f(v.x >> 16) * u0.y + bf2f(v.y & 0xFFFFu) * u0.z +
-                bf2f(v.y >> 16) * u0.w + bf2f(v.z & 0xFFFFu) * u1.x + bf2f(v.z >> 16) * u1.y +
-                bf2f(v.w & 0xFFFFu) * u1.z + bf2f(v.w >> 16) * u1.w;
+        for (int k = 0; k < kGvSets; ++k) rbl[k] = more || t == t_last ? rbc[k] : rbn[k];
+        const int sl = more ? s + 1 : (t == t_last ? s : 0);
+        uint4 csn[kGvSets];
+        uint32_t aqn[kGvSets];
+        load_step(csn, aqn, rbl, sl);
+        __builtin_amdgcn_sched_barrier(0);   // keep the loads ahead of this step's work
+
+        // this step: two chains of four MFMAs per set, then the block scales
+        f32x4_t D[kGvSets];
+#pragma unroll
+        for (int k = 0; k < kGvSets; ++k) D[k] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const bf16x8_t a = __builtin_bit_cast(bf16x8_t, lds_ld128(xa + 16u * j));
+#pragma unroll
+          for (int k = 0; k < kGvSets; ++k) {
+            const uint32_t cw = j == 0 ? cs[k].x : j == 1 ? cs[k].y : j == 2 ? cs[k].z : cs[k].w;
+            D[k] = mfma16x16x32(a, decode8(cw, col), D[k]);
+          }
+        }
+        // Blocks past the row end (a ragged last step) meet zero-padded x:
+        // their partial is zero and their (finite) scale needs no mask.
+        const uint32_t bi = kStepBlocks * (uint32_t)s + pblk;
+#pragma unroll
+        for (int k = 0; k < kGvSets; ++k) {
+          const float q0 = lds_ldf(kQ8Off + 4u * (aq[k] & 0xFFu));
+          const float q1 = lds_ldf(kQ8Off + 4u * ((aq[k] >> 8) & 0xFFu));
+          const float s20 = bi >= gb2[k] ? s2c[k][2] : bi >= gb1[k] ? s2c[k][1] : s2c[k][0];
+          const float s21 = kPair ? s20 : (bi + 1u >= gb2[k] ? s2c[k][2] : bi + 1u >= gb1[k] ? s2c[k][1] : s2c[k][0]);
+          acc[k] += (q0 * s20) * D[k][0] + (q1 * s21) * D[k][1];
+        }
+        xa += xinc;
+#pragma unroll
+        for (int k = 0; k < kGvSets; ++k) {
+          cs[k] = csn[k];
+          aq[k] = aqn[k];
+        }
+      }
+
+      // Tile end.  Per set: the row total is the sum over the four lanes
+      // holding it (c = 4r + p, g = p); the LoRA up-projection is split
+      // over the sixteen lanes of the row by 8-rank chunk 4g + p.  One
+      // reduction over g (lanes 16 and 32 apart) and p (1 and 2 apart)
+      // adds both.
+#pragma unroll
+      for (int k = 0; k < kGvSets; ++k) {
+        const int row = row_of(t, k);
+        const uint32_t bw[4] = {bq[k].x, bq[k].y, bq[k].z, bq[k].w};
+        float lora = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) lora += bf2f(bw[e] & 0xFFFFu) * uv[2 * e] + bf2f(bw[e] >> 16) * uv[2 * e + 1];
+        float part = (holds ? acc[k] : 0.0f) + J.s * lora;
+        part += __shfl_xor(part, 16);
+        part += __shfl_xor(part, 32);
+        part += __shfl_xor(part, 1);
+        part += __shfl_xor(part, 2);
+        if (lane == 4 * r && row < N) J.y[row] = (bf16_t)(pack_bf16x2(part, 0.0f) & 0xFFFFu);
+      }
+#pragma unroll
+      for (int k = 0; k < kGvSets; ++k) {
+        rbc[k] = rbn[k];
+        rbn[k] = rbase_of(t + 2 <= t_last ? t + 2 : t_last, k);
+#pragma unroll
+        for (int i = 0; i < 3; ++i) s2c[k][i] = s2n[k][i];
       }
     }
-    float part = (holds ? acc[k] : 0.0f) + J.s * lora;
-    part += __shfl_xor(part, 16);
-    part += __shfl_xor(part, 32);
-    part += __shfl_xor(part, 1);
-    part += __shfl_xor(part, 2);
-    if (lane == 4 * r && valid) J.y[row] = (bf16_t)(pack_bf16x2(part, 0.0f) & 0xFFFFu);
   }
 }
 
 namespace {
 
-// Tiles of jobs whose absmax codes can be read two at a time (an even
-// number of blocks per row and a 2-byte aligned array).
+// Jobs whose absmax codes can be read two at a time (an even number of
+// blocks per row and a 2-byte aligned array).
 bool pair_job(const GemvJob& J) {
   return (J.K % 128) == 0 && (reinterpret_cast<uintptr_t>(J.absmax_q) & 1u) == 0;
 }
 
-struct TablePlan {
-  size_t jobs_off, pair_off, other_off, down_off, total;
-  int n_pair, n_other, n_down;
-};
-
 size_t up256(size_t x) { return (x + 255) / 256 * 256; }
 
-TablePlan plan_table(const GemvJob* jobs, int njobs) {
-  TablePlan p{};
+// One launch's work: its tiles cut into `groups` contiguous ranges of about
+// equal cost (rows x columns), each range a list of per-job segments.
+struct LaunchPlan {
+  std::vector<int4> segs;
+  std::vector<int> range;   // groups + 1 offsets into segs; empty when the launch has no tiles
+  int max_steps = 0;
+  int groups() const { return range.empty() ? 0 : (int)range.size() - 1; }
+};
+
+LaunchPlan plan_launch(const GemvJob* jobs, int njobs, bool pair, int max_groups) {
+  LaunchPlan lp;
+  struct Tile { int job, t; double cost; };
+  std::vector<Tile> tiles;
+  double total = 0.0;
   for (int i = 0; i < njobs; ++i) {
-    (pair_job(jobs[i]) ? p.n_pair : p.n_other) += (jobs[i].N + kGvRows - 1) / kGvRows;
-    if (jobs[i].r > 0) p.n_down += (jobs[i].r + kDownRows - 1) / kDownRows;
+    if (pair_job(jobs[i]) != pair) continue;
+    const int nt = (jobs[i].N + kGvRows - 1) / kGvRows;
+    for (int t = 0; t < nt; ++t) {
+      const int rows = std::min(kGvRows, jobs[i].N - t * kGvRows);
+      const double cost = (double)rows * (double)jobs[i].K;
+      tiles.push_back({i, t, cost});
+      total += cost;
+    }
+    const int steps = (jobs[i].K / 64 + kStepBlocks - 1) / kStepBlocks;
+    if (steps > lp.max_steps) lp.max_steps = steps;
   }
-  p.jobs_off = 0;
-  p.pair_off = up256((size_t)njobs * sizeof(GemvJob));
-  p.other_off = p.pair_off + up256((size_t)p.n_pair * sizeof(int2));
-  p.down_off = p.other_off + up256((size_t)p.n_other * sizeof(int2));
-  p.total = p.down_off + up256((size_t)p.n_down * sizeof(int2));
-  return p;
+  if (tiles.empty()) return lp;
+  const int groups = std::min<int>(max_groups, (int)tiles.size());
+  lp.range.push_back(0);
+  double acc = 0.0;
+  size_t ti = 0;
+  for (int b = 0; b < groups; ++b) {
+    const double target = total * (double)(b + 1) / (double)groups;
+    const size_t first = ti;
+    // take tiles while the cumulative cost stays at or below the target,
+    // at least one per group, and leave one tile for each later group
+    while (ti < tiles.size() && (ti == first || acc + tiles[ti].cost <= target * (1.0 + 1e-12)) &&
+           tiles.size() - ti > (size_t)(groups - 1 - b)) {
+      acc += tiles[ti].cost;
+      ++ti;
+    }
+    if (b == groups - 1)
+      while (ti < tiles.size()) acc += tiles[ti++].cost;
+    for (size_t k = first; k < ti;) {
+      size_t e = k + 1;
+      while (e < ti && tiles[e].job == tiles[k].job) ++e;
+      lp.segs.push_back(make_int4(tiles[k].job, tiles[k].t, (int)(e - k), 0));
+      k = e;
+    }
+    lp.range.push_back((int)lp.segs.size());
+  }
+  return lp;
+}
+
+int device_cus() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 256;
+  return cus > 0 ? std::min(cus, kMaxGvGroups) : 256;
 }
 
 template <bool kPair>
-hipError_t launch_main(const GemvJob* djobs, const int2* map, int n, size_t lds, hipStream_t st) {
-  if (n == 0) return hipSuccess;
+hipError_t launch_main(const GemvJob* djobs, const int4* segs, const int* range, int groups, int max_steps,
+                       hipStream_t st) {
+  if (groups <= 0) return hipSuccess;
   // The kernel addresses its LDS from 0, which holds only while the
   // compiler has given it no static LDS.
   hipFuncAttributes fa{};
   hipError_t e = hipFuncGetAttributes(&fa, reinterpret_cast<const void*>(&nf4_gemv_kernel<kPair>));
   if (e != hipSuccess) return e;
   if (fa.sharedSizeBytes != 0) return hipErrorInvalidKernelFile;
+  const size_t lds = (size_t)kXOff + (size_t)max_steps * 1024;
   e = hipFuncSetAttribute(reinterpret_cast<const void*>(&nf4_gemv_kernel<kPair>),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(nf4_gemv_kernel<kPair>, dim3(n), dim3(kGvThreads), lds, st, djobs, map);
+  hipLaunchKernelGGL(nf4_gemv_kernel<kPair>, dim3(groups), dim3(kGvThreads), lds, st, djobs, segs, range,
+                     max_steps);
   return hipGetLastError();
 }
 
@@ -378,49 +458,59 @@ hipError_t launch_main(const GemvJob* djobs, const int2* map, int n, size_t lds,
 
 size_t gemv_table_bound(int njobs, int64_t max_rows) {
   if (njobs <= 0 || max_rows <= 0) return 0;
-  const size_t tiles = (size_t)njobs * (size_t)((max_rows + kGvRows - 1) / kGvRows);
+  // jobs | per launch kind: segments (at most one per job plus one per
+  // group boundary) and group offsets | lora_down map
+  const size_t segs = (size_t)njobs + kMaxGvGroups;
   const size_t downs = (size_t)njobs * (128 / kDownRows);
-  // two tile maps (each padded to 256 bytes) share the tiles
-  return up256((size_t)njobs * sizeof(GemvJob)) + up256(tiles * sizeof(int2)) + 256 + up256(downs * sizeof(int2));
+  return up256((size_t)njobs * sizeof(GemvJob)) + 2 * (up256(segs * sizeof(int4)) + up256((kMaxGvGroups + 1) * sizeof(int))) +
+         up256(downs * sizeof(int2));
 }
-
-size_t gemv_table_bytes(const GemvJob* jobs, int njobs) { return plan_table(jobs, njobs).total; }
 
 size_t gemv_lds_bytes(int64_t K) {
   const int64_t nsteps = (K / 64 + kStepBlocks - 1) / kStepBlocks;
-  return (size_t)kLutBytes + (size_t)nsteps * 1024 + kZeroBytes + 256 * sizeof(float);
+  return (size_t)kXOff + (size_t)nsteps * 1024;
 }
 
-hipError_t launch_gemv(const GemvJob* jobs, int njobs, void* table, hipStream_t st) {
-  const TablePlan p = plan_table(jobs, njobs);
-  std::vector<uint8_t> host(p.total, 0);
-  std::memcpy(host.data() + p.jobs_off, jobs, (size_t)njobs * sizeof(GemvJob));
-  int2* pm = reinterpret_cast<int2*>(host.data() + p.pair_off);
-  int2* om = reinterpret_cast<int2*>(host.data() + p.other_off);
-  int2* dm = reinterpret_cast<int2*>(host.data() + p.down_off);
-  int maxK = 0;
-  for (int i = 0, ip = 0, io = 0, id = 0; i < njobs; ++i) {
-    const GemvJob& J = jobs[i];
-    const bool pair = pair_job(J);
-    for (int t = 0; t < (J.N + kGvRows - 1) / kGvRows; ++t) (pair ? pm[ip++] : om[io++]) = make_int2(i, t);
-    if (J.r > 0)
-      for (int t = 0; t < (J.r + kDownRows - 1) / kDownRows; ++t) dm[id++] = make_int2(i, t);
-    if (J.K > maxK) maxK = J.K;
+hipError_t launch_gemv(const GemvJob* jobs, int njobs, void* table, size_t table_bytes, hipStream_t st) {
+  const int groups = device_cus();
+  const LaunchPlan lp[2] = {plan_launch(jobs, njobs, true, groups), plan_launch(jobs, njobs, false, groups)};
+  std::vector<int2> down;
+  for (int i = 0; i < njobs; ++i)
+    for (int t = 0; jobs[i].r > 0 && t < (jobs[i].r + kDownRows - 1) / kDownRows; ++t) down.push_back(make_int2(i, t));
+  // layout
+  size_t off = up256((size_t)njobs * sizeof(GemvJob));
+  size_t seg_off[2], rng_off[2];
+  for (int k = 0; k < 2; ++k) {
+    seg_off[k] = off;
+    off += up256(lp[k].segs.size() * sizeof(int4));
+    rng_off[k] = off;
+    off += up256(lp[k].range.size() * sizeof(int));
   }
+  const size_t down_off = off;
+  off += up256(down.size() * sizeof(int2));
+  if (off > table_bytes) return hipErrorInvalidValue;   // the caller's check makes this unreachable
+  std::vector<uint8_t> host(off, 0);
+  std::memcpy(host.data(), jobs, (size_t)njobs * sizeof(GemvJob));
+  for (int k = 0; k < 2; ++k) {
+    if (!lp[k].segs.empty()) std::memcpy(host.data() + seg_off[k], lp[k].segs.data(), lp[k].segs.size() * sizeof(int4));
+    if (!lp[k].range.empty()) std::memcpy(host.data() + rng_off[k], lp[k].range.data(), lp[k].range.size() * sizeof(int));
+  }
+  if (!down.empty()) std::memcpy(host.data() + down_off, down.data(), down.size() * sizeof(int2));
   uint8_t* dev = static_cast<uint8_t*>(table);
-  hipError_t e = hipMemcpyAsync(dev, host.data(), p.total, hipMemcpyHostToDevice, st);
+  hipError_t e = hipMemcpyAsync(dev, host.data(), off, hipMemcpyHostToDevice, st);
   if (e != hipSuccess) return e;
-  const GemvJob* djobs = reinterpret_cast<const GemvJob*>(dev + p.jobs_off);
-  if (p.n_down > 0) {
-    hipLaunchKernelGGL(lora_down_kernel, dim3(p.n_down), dim3(kDownThreads), 0, st, djobs,
-                       reinterpret_cast<const int2*>(dev + p.down_off));
+  const GemvJob* djobs = reinterpret_cast<const GemvJob*>(dev);
+  if (!down.empty()) {
+    hipLaunchKernelGGL(lora_down_kernel, dim3((unsigned)down.size()), dim3(kDownThreads), 0, st, djobs,
+                       reinterpret_cast<const int2*>(dev + down_off));
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const size_t lds = gemv_lds_bytes(maxK);
-  e = launch_main<true>(djobs, reinterpret_cast<const int2*>(dev + p.pair_off), p.n_pair, lds, st);
+  e = launch_main<true>(djobs, reinterpret_cast<const int4*>(dev + seg_off[0]), reinterpret_cast<const int*>(dev + rng_off[0]),
+                        lp[0].groups(), lp[0].max_steps, st);
   if (e != hipSuccess) return e;
-  return launch_main<false>(djobs, reinterpret_cast<const int2*>(dev + p.other_off), p.n_other, lds, st);
+  return launch_main<false>(djobs, reinterpret_cast<const int4*>(dev + seg_off[1]),
+                            reinterpret_cast<const int*>(dev + rng_off[1]), lp[1].groups(), lp[1].max_steps, st);
 }
 
 }  // namespace qlora

@@ -57,12 +57,13 @@ struct GemvJob {
   int32_t r;
   float s;
 };
-// The job table (jobs and workgroup maps) is written into `table` (device
-// memory of at least gemv_table_bytes(jobs, njobs)) by one host-to-device
-// copy on `st`; then u = A x and the NF4 GEMV run as one launch each.
-size_t gemv_table_bytes(const GemvJob* jobs, int njobs);
-size_t gemv_table_bound(int njobs, int64_t max_rows);  // upper bound for any njobs jobs of <= max_rows rows
+// The job table (jobs, per-workgroup tile segments and the u = A x map) is
+// written into `table` (device memory of at least gemv_table_bound(njobs,
+// max rows) bytes) by one host-to-device copy on `st`; then u = A x and the
+// NF4 GEMV run as one launch each (two when some jobs need the byte-wise
+// absmax path).
+size_t gemv_table_bound(int njobs, int64_t max_rows);
 size_t gemv_lds_bytes(int64_t K);
-hipError_t launch_gemv(const GemvJob* jobs, int njobs, void* table, hipStream_t st);
+hipError_t launch_gemv(const GemvJob* jobs, int njobs, void* table, size_t table_bytes, hipStream_t st);
 
 }  // namespace qlora
