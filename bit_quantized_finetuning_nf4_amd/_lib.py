@@ -22,7 +22,7 @@ STATUS_NAMES = {
 EXPORTS = [
     "qlora_status_str", "qlora_last_hip_error", "qlora_version", "qlora_nf4_levels",
     "qlora_sizes", "qlora_workspace_bytes", "qlora_quantize", "qlora_dequant",
-    "qlora_linear_fwd", "qlora_linear_bwd", "qlora_gemv",
+    "qlora_linear_fwd", "qlora_linear_bwd", "qlora_gemv", "qlora_gemv_prepare", "qlora_gemv_run",
     "qlora_lora_down", "qlora_lora_dy_b", "qlora_lora_grads", "qlora_nf4_fwd", "qlora_nf4_dx",
 ]
 
@@ -49,6 +49,11 @@ class GemvJobDesc(ctypes.Structure):
         ("alpha", ctypes.c_float),
         ("y", ctypes.c_void_p),
     ]
+
+
+class GemvPlanDesc(ctypes.Structure):
+    """qlora_gemv_plan: filled by qlora_gemv_prepare, read by qlora_gemv_run."""
+    _fields_ = [("priv", ctypes.c_uint64 * 16)]
 
 
 class QloraError(RuntimeError):
@@ -100,6 +105,10 @@ def lib():
     L.qlora_linear_bwd.argtypes = [W, vp, vp, i64, vp, vp, i32, f32, vp, vp, vp, vp, vp, sz, vp]
     L.qlora_gemv.restype = ctypes.c_int
     L.qlora_gemv.argtypes = [ctypes.POINTER(GemvJobDesc), i32, vp, sz, vp]
+    L.qlora_gemv_prepare.restype = ctypes.c_int
+    L.qlora_gemv_prepare.argtypes = [ctypes.POINTER(GemvJobDesc), i32, vp, sz, ctypes.POINTER(GemvPlanDesc), vp]
+    L.qlora_gemv_run.restype = ctypes.c_int
+    L.qlora_gemv_run.argtypes = [ctypes.POINTER(GemvPlanDesc), vp]
     L.qlora_lora_down.restype = ctypes.c_int
     L.qlora_lora_down.argtypes = [vp, vp, i64, i64, i32, vp, vp, sz, vp]
     L.qlora_lora_dy_b.restype = ctypes.c_int

@@ -26,7 +26,8 @@ thread_local int g_last_hip_error = 0;
 constexpr size_t kAlign = 256;
 constexpr int kMaxRank = 128;
 constexpr int kMaxJobs = 4096;
-constexpr int64_t kMaxGemvCols = 32768;  // x is staged whole in LDS beside the 64 KiB table
+constexpr int64_t kMaxGemvCols = 32768;
+constexpr uint64_t kPlanMagic = 0x51474D56504C414EULL;   // marks a plan filled by qlora_gemv_prepare  // x is staged whole in LDS beside the 64 KiB table
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -358,8 +359,9 @@ qlora_status qlora_nf4_dx(const qlora_nf4_weight* W, const uint16_t* dY, int64_t
                               (hipStream_t)stream));
 }
 
-qlora_status qlora_gemv(const qlora_gemv_job* jobs, int32_t njobs, void* ws, size_t ws_bytes, void* stream) {
-  if (!jobs) return QLORA_E_NULL;
+qlora_status qlora_gemv_prepare(const qlora_gemv_job* jobs, int32_t njobs, void* ws, size_t ws_bytes,
+                                qlora_gemv_plan* plan, void* stream) {
+  if (!jobs || !plan) return QLORA_E_NULL;
   if (njobs <= 0) return QLORA_E_SHAPE;
   if (njobs > kMaxJobs) return QLORA_E_UNSUPPORTED;
   for (int i = 0; i < njobs; ++i) {
@@ -398,7 +400,28 @@ qlora_status qlora_gemv(const qlora_gemv_job* jobs, int32_t njobs, void* ws, siz
   const size_t u_bytes = align_up((size_t)njobs * kMaxRank * sizeof(float));
   const size_t table_bytes = gemv_table_bound(njobs, 1);
   if (ws_bytes < u_bytes || ws_bytes - u_bytes < table_bytes) return QLORA_E_WORKSPACE;
-  return hip_status(launch_gemv(buf.data(), njobs, ws_at(ws, u_bytes), table_bytes, (hipStream_t)stream));
+  GemvLaunch L{};
+  qlora_status st = hip_status(gemv_prepare(buf.data(), njobs, ws_at(ws, u_bytes), table_bytes, &L, (hipStream_t)stream));
+  if (st != QLORA_OK) return st;
+  static_assert(sizeof(GemvLaunch) + sizeof(uint64_t) <= sizeof(qlora_gemv_plan), "plan storage");
+  std::memset(plan, 0, sizeof(*plan));
+  plan->priv[0] = kPlanMagic;
+  std::memcpy(&plan->priv[1], &L, sizeof(L));
+  return QLORA_OK;
+}
+
+qlora_status qlora_gemv_run(const qlora_gemv_plan* plan, void* stream) {
+  if (!plan) return QLORA_E_NULL;
+  if (plan->priv[0] != kPlanMagic) return QLORA_E_SHAPE;
+  GemvLaunch L;
+  std::memcpy(&L, &plan->priv[1], sizeof(L));
+  return hip_status(gemv_run(L, (hipStream_t)stream));
+}
+
+qlora_status qlora_gemv(const qlora_gemv_job* jobs, int32_t njobs, void* ws, size_t ws_bytes, void* stream) {
+  qlora_gemv_plan plan;
+  const qlora_status st = qlora_gemv_prepare(jobs, njobs, ws, ws_bytes, &plan, stream);
+  return st != QLORA_OK ? st : qlora_gemv_run(&plan, stream);
 }
 
 }  // extern "C"

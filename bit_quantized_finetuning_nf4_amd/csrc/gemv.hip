@@ -59,8 +59,8 @@ constexpr int kZeroBytes = 512;                            // zero run read by t
 constexpr int kQ8Bytes = 256 * 4;                          // Q8[q] = RN32(q / 255) as fp32
 constexpr int kQ8Off = kLutBytes, kZeroOff = kQ8Off + kQ8Bytes, kXOff = kZeroOff + kZeroBytes;   // LDS layout
 constexpr int kMaxGvGroups = 1024;                         // persistent workgroups per launch, at most
-constexpr int kDownThreads = 256;
-constexpr int kDownRows = 4;                               // adapter rows per workgroup (one per wave)
+constexpr int kDownThreads = 256;                          // u = A x: one workgroup per adapter row
+constexpr int kDownUnroll = 4;                             // 16-byte loads of A per thread in flight
 static_assert(kGvThreads == 1024, "the table fill below assumes 16 waves");
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
@@ -122,33 +122,39 @@ __device__ __forceinline__ bf16x8_t decode8(uint32_t c, uint32_t col) {
 
 }  // namespace
 
-// Phase 1: u = A x for every job with r > 0 (fp32, into the job's scratch);
-// one wave per adapter row, four 16-byte loads of A and x in flight per lane.
+// Phase 1: u = A x for every job with r > 0 (fp32, into the job's scratch).
+// One workgroup per adapter row: each thread keeps up to kDownUnroll
+// 16-byte loads of A (and of x, an L2 hit) in flight, then the workgroup
+// sums its partials.
 __global__ __launch_bounds__(kDownThreads) void lora_down_kernel(const GemvJob* __restrict__ jobs,
                                                                  const int2* __restrict__ map) {
+  __shared__ float part[kDownThreads / 64];
   const int2 m = map[blockIdx.x];
   const GemvJob& J = jobs[m.x];
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int row = m.y * kDownRows + w;
-  if (row >= J.r) return;   // uniform per wave; the kernel has no barrier
-  const bf16_t* a = J.A + (int64_t)row * J.K;
+  const int K = J.K, row = m.y;
+  const rsrc_t arr = make_rsrc(J.A + (int64_t)row * K, (uint32_t)K * 2u);   // zero past the row
+  const rsrc_t xr = make_rsrc(J.x, (uint32_t)K * 2u);
   float acc = 0.0f;
-  for (int k0 = lane * 8; k0 < J.K; k0 += 4 * 512) {
-    uint4 av[4], xv[4];
+  for (int c0 = 0; c0 < K / 8; c0 += kDownThreads * kDownUnroll) {
+    uint4 av[kDownUnroll], xv[kDownUnroll];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int k = k0 + 512 * u;
-      av[u] = xv[u] = make_uint4(0u, 0u, 0u, 0u);
-      if (k < J.K) {
-        av[u] = *reinterpret_cast<const uint4*>(a + k);
-        xv[u] = *reinterpret_cast<const uint4*>(J.x + k);
-      }
+    for (int u = 0; u < kDownUnroll; ++u) {
+      const uint32_t off = 16u * (uint32_t)(c0 + (int)threadIdx.x + u * kDownThreads);
+      av[u] = buf_load16(arr, off);
+      xv[u] = buf_load16(xr, off);
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) acc += dot8(av[u], xv[u]);
+    for (int u = 0; u < kDownUnroll; ++u) acc += dot8(av[u], xv[u]);
   }
   acc = wave_sum(acc);
-  if (lane == 0) J.u[row] = acc;
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float t = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kDownThreads / 64; ++i) t += part[i];
+    J.u[row] = t;
+  }
 }
 
 // Phase 2: the NF4 GEMV and the LoRA up-projection, persistent.
@@ -461,7 +467,7 @@ size_t gemv_table_bound(int njobs, int64_t max_rows) {
   // jobs | per launch kind: segments (at most one per job plus one per
   // group boundary) and group offsets | lora_down map
   const size_t segs = (size_t)njobs + kMaxGvGroups;
-  const size_t downs = (size_t)njobs * (128 / kDownRows);
+  const size_t downs = (size_t)njobs * 128;
   return up256((size_t)njobs * sizeof(GemvJob)) + 2 * (up256(segs * sizeof(int4)) + up256((kMaxGvGroups + 1) * sizeof(int))) +
          up256(downs * sizeof(int2));
 }
@@ -471,46 +477,57 @@ size_t gemv_lds_bytes(int64_t K) {
   return (size_t)kXOff + (size_t)nsteps * 1024;
 }
 
-hipError_t launch_gemv(const GemvJob* jobs, int njobs, void* table, size_t table_bytes, hipStream_t st) {
+hipError_t gemv_prepare(const GemvJob* jobs, int njobs, void* table, size_t table_bytes, GemvLaunch* out,
+                        hipStream_t st) {
   const int groups = device_cus();
   const LaunchPlan lp[2] = {plan_launch(jobs, njobs, true, groups), plan_launch(jobs, njobs, false, groups)};
   std::vector<int2> down;
   for (int i = 0; i < njobs; ++i)
-    for (int t = 0; jobs[i].r > 0 && t < (jobs[i].r + kDownRows - 1) / kDownRows; ++t) down.push_back(make_int2(i, t));
-  // layout
+    for (int t = 0; t < jobs[i].r; ++t) down.push_back(make_int2(i, t));
+  // layout: jobs | per launch kind: segments, group offsets | u = A x map
+  GemvLaunch L{};
   size_t off = up256((size_t)njobs * sizeof(GemvJob));
-  size_t seg_off[2], rng_off[2];
   for (int k = 0; k < 2; ++k) {
-    seg_off[k] = off;
+    L.seg_off[k] = off;
     off += up256(lp[k].segs.size() * sizeof(int4));
-    rng_off[k] = off;
+    L.rng_off[k] = off;
     off += up256(lp[k].range.size() * sizeof(int));
+    L.groups[k] = lp[k].groups();
+    L.max_steps[k] = lp[k].max_steps;
   }
-  const size_t down_off = off;
+  L.down_off = off;
+  L.n_down = (int)down.size();
   off += up256(down.size() * sizeof(int2));
   if (off > table_bytes) return hipErrorInvalidValue;   // the caller's check makes this unreachable
   std::vector<uint8_t> host(off, 0);
   std::memcpy(host.data(), jobs, (size_t)njobs * sizeof(GemvJob));
   for (int k = 0; k < 2; ++k) {
-    if (!lp[k].segs.empty()) std::memcpy(host.data() + seg_off[k], lp[k].segs.data(), lp[k].segs.size() * sizeof(int4));
-    if (!lp[k].range.empty()) std::memcpy(host.data() + rng_off[k], lp[k].range.data(), lp[k].range.size() * sizeof(int));
+    if (!lp[k].segs.empty()) std::memcpy(host.data() + L.seg_off[k], lp[k].segs.data(), lp[k].segs.size() * sizeof(int4));
+    if (!lp[k].range.empty()) std::memcpy(host.data() + L.rng_off[k], lp[k].range.data(), lp[k].range.size() * sizeof(int));
   }
-  if (!down.empty()) std::memcpy(host.data() + down_off, down.data(), down.size() * sizeof(int2));
-  uint8_t* dev = static_cast<uint8_t*>(table);
-  hipError_t e = hipMemcpyAsync(dev, host.data(), off, hipMemcpyHostToDevice, st);
+  if (!down.empty()) std::memcpy(host.data() + L.down_off, down.data(), down.size() * sizeof(int2));
+  L.table = table;
+  hipError_t e = hipMemcpyAsync(table, host.data(), off, hipMemcpyHostToDevice, st);
   if (e != hipSuccess) return e;
+  *out = L;
+  return hipSuccess;
+}
+
+hipError_t gemv_run(const GemvLaunch& L, hipStream_t st) {
+  const uint8_t* dev = static_cast<const uint8_t*>(L.table);
   const GemvJob* djobs = reinterpret_cast<const GemvJob*>(dev);
-  if (!down.empty()) {
-    hipLaunchKernelGGL(lora_down_kernel, dim3((unsigned)down.size()), dim3(kDownThreads), 0, st, djobs,
-                       reinterpret_cast<const int2*>(dev + down_off));
-    e = hipGetLastError();
+  if (L.n_down > 0) {
+    hipLaunchKernelGGL(lora_down_kernel, dim3((unsigned)L.n_down), dim3(kDownThreads), 0, st, djobs,
+                       reinterpret_cast<const int2*>(dev + L.down_off));
+    const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  e = launch_main<true>(djobs, reinterpret_cast<const int4*>(dev + seg_off[0]), reinterpret_cast<const int*>(dev + rng_off[0]),
-                        lp[0].groups(), lp[0].max_steps, st);
+  const hipError_t e = launch_main<true>(djobs, reinterpret_cast<const int4*>(dev + L.seg_off[0]),
+                                         reinterpret_cast<const int*>(dev + L.rng_off[0]), L.groups[0],
+                                         L.max_steps[0], st);
   if (e != hipSuccess) return e;
-  return launch_main<false>(djobs, reinterpret_cast<const int4*>(dev + seg_off[1]),
-                            reinterpret_cast<const int*>(dev + rng_off[1]), lp[1].groups(), lp[1].max_steps, st);
+  return launch_main<false>(djobs, reinterpret_cast<const int4*>(dev + L.seg_off[1]),
+                            reinterpret_cast<const int*>(dev + L.rng_off[1]), L.groups[1], L.max_steps[1], st);
 }
 
 }  // namespace qlora

@@ -57,13 +57,22 @@ struct GemvJob {
   int32_t r;
   float s;
 };
-// The job table (jobs, per-workgroup tile segments and the u = A x map) is
-// written into `table` (device memory of at least gemv_table_bound(njobs,
-// max rows) bytes) by one host-to-device copy on `st`; then u = A x and the
-// NF4 GEMV run as one launch each (two when some jobs need the byte-wise
-// absmax path).
+// gemv_prepare writes the job table (jobs, per-workgroup tile segments and
+// the u = A x map) into `table` (device memory of at least
+// gemv_table_bound(njobs, max rows) bytes) by one host-to-device copy on
+// `st`; gemv_run then launches u = A x and the NF4 GEMV (two launches of it
+// when some jobs need the byte-wise absmax path).
 size_t gemv_table_bound(int njobs, int64_t max_rows);
 size_t gemv_lds_bytes(int64_t K);
-hipError_t launch_gemv(const GemvJob* jobs, int njobs, void* table, size_t table_bytes, hipStream_t st);
+// What gemv_run needs besides the table in device memory.
+struct GemvLaunch {
+  void* table;
+  uint64_t seg_off[2], rng_off[2], down_off;
+  int32_t groups[2], max_steps[2];
+  int32_t n_down;
+};
+hipError_t gemv_prepare(const GemvJob* jobs, int njobs, void* table, size_t table_bytes, GemvLaunch* out,
+                        hipStream_t st);
+hipError_t gemv_run(const GemvLaunch& L, hipStream_t st);
 
 }  // namespace qlora

@@ -12,7 +12,7 @@ from typing import Optional, Sequence
 import torch
 
 from . import _lib
-from ._lib import GemvJobDesc, Nf4WeightDesc, check, lib
+from ._lib import GemvJobDesc, GemvPlanDesc, Nf4WeightDesc, check, lib
 
 BLOCKSIZE = 64
 GROUP_BLOCKS = 256
@@ -173,7 +173,9 @@ class GemvJob:
 
 
 class GemvPlan:
-    """Job descriptors built once; calling the plan enqueues one qlora_gemv."""
+    """A prepared decode call: the job table is written into the workspace once
+    (qlora_gemv_prepare, on the current stream); calling the plan enqueues
+    qlora_gemv_run.  The tensors the jobs name must stay alive and in place."""
 
     def __init__(self, jobs: Sequence[GemvJob], ws=None):
         n = len(jobs)
@@ -197,10 +199,12 @@ class GemvPlan:
         nbytes = workspace_bytes(_lib.QLORA_OP_GEMV, N=max(j.q.rows for j in jobs),
                                  K=max(j.q.cols for j in jobs), njobs=n)
         self.ws = ws if ws is not None else workspace(nbytes, jobs[0].x.device)
+        self._plan = GemvPlanDesc()
+        check(lib().qlora_gemv_prepare(self._arr, n, _ptr(self.ws), 0 if self.ws is None else self.ws.numel(),
+                                       ctypes.byref(self._plan), _stream()), "qlora_gemv_prepare")
 
     def __call__(self):
-        check(lib().qlora_gemv(self._arr, self.n, _ptr(self.ws), 0 if self.ws is None else self.ws.numel(),
-                               _stream()), "qlora_gemv")
+        check(lib().qlora_gemv_run(ctypes.byref(self._plan), _stream()), "qlora_gemv_run")
         return self.outputs
 
 

@@ -196,10 +196,35 @@ qlora_status qlora_nf4_dx(const qlora_nf4_weight* W, const uint16_t* dY, int64_t
                           const uint16_t* A, int32_t r, float alpha, uint16_t* dX, void* stream);
 
 /* Batch-1 decode for njobs independent products (host job array, read
- * before return).  Each job needs cols % 64 == 0.  njobs <= 4096.
+ * before return): y = deq(W) x + s B (A x), s = RN32(alpha / r), y bf16
+ * (overwritten).  Each job needs cols % 64 == 0 and cols <= 32768 (x is
+ * staged whole in on-chip memory), and rows * r * 2 < 2^32.  njobs <= 4096.
+ * ws is sized by qlora_workspace_bytes(QLORA_OP_GEMV, 0, max rows, max
+ * cols, 0, njobs); it holds u = A x and the job table, which the call writes
+ * with an asynchronous host-to-device copy on `stream`.  Equivalent to
+ * qlora_gemv_prepare followed by qlora_gemv_run.
  * whatthefuture.ai article: 4-bit inference speed. */
 qlora_status qlora_gemv(const qlora_gemv_job* jobs, int32_t njobs, void* ws, size_t ws_bytes,
                         void* stream);
+
+/* A prepared decode call, for callers that repeat the same jobs (a decode
+ * loop over fixed layers and buffers).  The fields belong to the library. */
+typedef struct {
+  uint64_t priv[16];
+} qlora_gemv_plan;
+
+/* Validate the jobs and write their table into ws (as qlora_gemv does);
+ * fill *plan.  The copy is ordered on `stream`.  Same errors as
+ * qlora_gemv; nothing is enqueued on error. */
+qlora_status qlora_gemv_prepare(const qlora_gemv_job* jobs, int32_t njobs, void* ws, size_t ws_bytes,
+                                qlora_gemv_plan* plan, void* stream);
+
+/* Launch a prepared decode call on `stream`.  The workspace and every
+ * buffer the jobs name must still hold what they held at prepare time (the
+ * inputs may have new values); a stream other than the prepare stream must
+ * be ordered after it by the caller.  QLORA_E_SHAPE for a plan that
+ * qlora_gemv_prepare did not fill. */
+qlora_status qlora_gemv_run(const qlora_gemv_plan* plan, void* stream);
 
 #ifdef __cplusplus
 }

@@ -133,5 +133,11 @@ def test_validation_happens_before_any_launch(L):
     jobs[0].W = ctypes.pointer(wide)
     assert L.qlora_gemv(jobs, 1, fake, 1 << 20, None) == 4        # x is staged whole in LDS
     jobs[0].W = ctypes.pointer(d)
+    # prepared calls: a plan is required, and an unfilled plan is refused
+    plan = _lib.GemvPlanDesc()
+    assert L.qlora_gemv_prepare(jobs, 1, fake, 1 << 20, None, None) == 1
+    assert L.qlora_gemv_prepare(jobs, 1, fake, 16, ctypes.byref(plan), None) == 5
+    assert L.qlora_gemv_run(None, None) == 1
+    assert L.qlora_gemv_run(ctypes.byref(plan), None) == 3
     jobs[0].r = 16
     assert L.qlora_gemv(jobs, 1, None, 0, None) == 1

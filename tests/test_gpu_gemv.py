@@ -72,3 +72,24 @@ def test_gemv_matches_forward_at_one_token():
     ref = _oracle_y(d)
     assert_close(torch_to_f64(y), ref, "gemv")
     assert_close(torch_to_f64(Y)[0], ref, "fwd M=1")
+
+
+def test_prepared_plan_reruns_with_new_inputs():
+    """qlora_gemv_prepare once, qlora_gemv_run three times: the inputs change
+    in place between runs and every run matches the oracle."""
+    shapes = [(512, 1024, 64), (1536, 1024, 64), (300, 22016, 16), (64, 576, 8)]
+    ds = [_job(N, K, r, seed=500 + i) for i, (N, K, r) in enumerate(shapes)]
+    qs = [ops.quantize(bits_to_torch(d["W"])) for d in ds]
+    xs = [bits_to_torch(d["x"]) for d in ds]
+    plan = ops.GemvPlan([ops.GemvJob(q, x, bits_to_torch(d["A"]), bits_to_torch(d["B"]), d["alpha"])
+                         for q, x, d in zip(qs, xs, ds)])
+    for run in range(3):
+        print(f"[gemv parity] prepared plan, run {run}", flush=True)
+        for i, d in enumerate(ds):
+            rng = np.random.default_rng(1000 * run + i)
+            d["x"] = synth.to_bf16_bits(rng.standard_normal(d["x"].shape))
+            xs[i].copy_(bits_to_torch(d["x"]))
+        ys = plan()
+        torch.cuda.synchronize()
+        for i, (d, y) in enumerate(zip(ds, ys)):
+            assert_close(torch_to_f64(y), _oracle_y(d), f"run {run} job {i}")
