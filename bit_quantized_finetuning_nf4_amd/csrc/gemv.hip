@@ -53,6 +53,10 @@ constexpr int kGvWaves = 16;                               // waves per workgrou
 constexpr int kGvThreads = 64 * kGvWaves;
 constexpr int kGvSets = 2;                                 // sets of four rows per wave
 constexpr int kGvRows = kGvWaves * 4 * kGvSets;            // weight rows per workgroup
+#ifndef QLORA_GEMV_AHEAD
+#define QLORA_GEMV_AHEAD 1
+#endif
+constexpr int kGvAhead = QLORA_GEMV_AHEAD;                 // steps of code loads in flight per wave (1 or 2)
 constexpr int kStepBlocks = 8;                             // NF4 blocks per row per step (256 code bytes)
 constexpr int kLutBytes = 256 * 64 * 4;                    // 256 entries x 64 lane columns
 constexpr int kZeroBytes = 512;                            // zero run read by the off-diagonal A lanes
@@ -273,7 +277,26 @@ __global__ __launch_bounds__(kGvThreads) void nf4_gemv_kernel(const GemvJob* __r
       rbn[k] = rbase_of(t_first + 1 <= t_last ? t_first + 1 : t_last, k);
     }
     load_s2(s2c, rbc);
-    load_step(cs, aq, rbc, 0);
+    // Loads run kGvAhead steps ahead of use, straight across tile
+    // boundaries: (tl, sl) is the next step to load; past the segment's
+    // last step it stays on that step (a re-read of cached lines).
+    int tl = t_first, sl = 0;
+    auto load_next = [&](uint4 (&c_)[kGvSets], uint32_t (&a_)[kGvSets]) __attribute__((always_inline)) {
+      uint32_t rb[kGvSets];
+#pragma unroll
+      for (int k = 0; k < kGvSets; ++k) rb[k] = rbase_of(tl, k);
+      load_step(c_, a_, rb, sl);
+      if (tl < t_last || sl + 1 < nsteps) {   // uniform scalar bookkeeping
+        if (++sl == nsteps) {
+          sl = 0;
+          ++tl;
+        }
+      }
+    };
+    load_next(cs, aq);
+    uint4 cs1[kGvSets];
+    uint32_t aq1[kGvSets];
+    if constexpr (kGvAhead == 2) load_next(cs1, aq1);
 
     for (int t = t_first; t <= t_last; ++t) {
       // tile start: this tile's LoRA rows and the next tile's group scales
@@ -296,16 +319,10 @@ __global__ __launch_bounds__(kGvThreads) void nf4_gemv_kernel(const GemvJob* __r
       uint32_t xa = xa0;
 
       for (int s = 0; s < nsteps; ++s) {
-        // the next step's loads first: this tile's step s+1, or the next
-        // tile's step 0 (on the last tile, a re-read of its own last step)
-        const bool more = s + 1 < nsteps;
-        uint32_t rbl[kGvSets];
-#pragma unroll
-        for (int k = 0; k < kGvSets; ++k) rbl[k] = more || t == t_last ? rbc[k] : rbn[k];
-        const int sl = more ? s + 1 : (t == t_last ? s : 0);
+        // the loads kGvAhead steps ahead first
         uint4 csn[kGvSets];
         uint32_t aqn[kGvSets];
-        load_step(csn, aqn, rbl, sl);
+        load_next(csn, aqn);
         __builtin_amdgcn_sched_barrier(0);   // keep the loads ahead of this step's work
 
         // this step: two chains of four MFMAs per set, then the block scales
@@ -335,8 +352,15 @@ __global__ __launch_bounds__(kGvThreads) void nf4_gemv_kernel(const GemvJob* __r
         xa += xinc;
 #pragma unroll
         for (int k = 0; k < kGvSets; ++k) {
-          cs[k] = csn[k];
-          aq[k] = aqn[k];
+          if constexpr (kGvAhead == 2) {
+            cs[k] = cs1[k];
+            aq[k] = aq1[k];
+            cs1[k] = csn[k];
+            aq1[k] = aqn[k];
+          } else {
+            cs[k] = csn[k];
+            aq[k] = aqn[k];
+          }
         }
       }
 
