@@ -397,6 +397,310 @@ __global__ __launch_bounds__(kThreads, 1) void nf4_fwd_kernel(Nf4View W, const b
 }
 
 // ===========================================================================
+// Forward with the weight operand in registers.  Wave w owns weight rows
+// n0 + 64 w .. +63 (two 32-row A fragments) against all 256 tokens of the
+// tile (eight 32-token B fragments): still 16 accumulator tiles per wave,
+// but every weight element a wave multiplies is one it dequantized itself,
+// straight into its MFMA A registers.  Only the token tile (DMA, a ring of
+// kRSlots stages) and the NF4 codes (DMA, four stages per chunk) pass
+// through LDS; no dequantized weight is written to LDS or waited for.
+//
+// k order inside a 32-wide stage: lane half h of an MFMA takes k 16h + 8kk
+// .. +7 in k16 step kk, so a lane's weight codes for a stage are the 8
+// contiguous bytes 8h .. 8h+7 of its row's 16, and its token fragment of
+// step kk is 16-byte chunk 2h + kk of the token row.
+//
+// Substep s (U8 = s mod 8, token ring slot s & 7): DMA of token stage
+// s + kRAhead; at s & 3 == 3 the DMA of code chunk s/4 + 2; at odd s the
+// scales of block (s+1)/2 + 2; then the MFMAs of stage s (k16 0 | barrier |
+// k16 1) with the dequantization of stage s+1 (row 0 in the first half, row
+// 1 in the second) between them.
+// ===========================================================================
+#ifndef QLORA_FWDR_AHEAD
+#define QLORA_FWDR_AHEAD 6
+#endif
+constexpr int kRSlots = 8;                                            // token ring depth (stage s in slot s & 7)
+constexpr int kRAhead = QLORA_FWDR_AHEAD;                             // token stages DMA'd ahead of use
+static_assert(kRAhead >= 3 && kRAhead <= kRSlots - 1, "the slot being refilled must be read out");
+constexpr int kRCodeBase = kRSlots * kOp;                             // 128 KiB
+constexpr size_t kLdsFwdR = (size_t)kRCodeBase + 2 * kCodes;          // 160 KiB
+
+// Loads issued by substep u (mod 8) of the register-A forward: 4 token DMAs,
+// 4 code DMAs at u & 3 == 3, 4 scale loads at odd u.
+constexpr int fwdr_loads(int u) { return 4 + ((u & 3) == 3 ? 4 : 0) + ((u & 1) ? 4 : 0); }
+// vmcnt for substep u: the token stage it reads next (issued kRAhead - 1
+// substeps earlier) has landed once the loads of the kRAhead - 2 later
+// substeps and of this one are all that may be in flight.  The code and
+// scale loads of the issuing substep itself are not counted (their order
+// against its token DMAs is the compiler's): a wait for more than needed,
+// never less.
+constexpr int fwdr_vmcnt(int u) {
+  int n = 0;
+  for (int k = 0; k <= kRAhead - 2; ++k) n += fwdr_loads((u - k + 64) & 7);
+  return n;
+}
+
+struct FwdR {
+  rsrc_t xr, cr;          // X, NF4 codes
+  uint32_t xo[4], co[4];  // per-lane byte offsets of the four DMA instructions
+  const uint8_t* aq[2];   // absmax codes of the lane's two rows (block 0)
+  const float* gs;        // group scales
+  uint32_t ablk0[2];      // block index of (row, block 0)
+  int nsub, nblk, w;
+  int crow[2];            // code-tile byte offset of the lane's 8-byte piece in row i (chunk position 0)
+  int cswz[2];            // the rows' chunk swizzle, (row >> 2) & 3
+};
+
+__device__ __forceinline__ void fwdr_dma_x(char* smem, const FwdR& f, int stage, int slot) {
+  const uint32_t soff = (uint32_t)min(stage, f.nsub - 1) * 64u;
+  char* dst = smem + slot * kOp;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) dma16(f.xr, dst + (64 * q + 16 * f.w) * 64, f.xo[q], soff);
+}
+template <int BUF>   // BUF == chunk & 1
+__device__ __forceinline__ void fwdr_dma_codes(char* smem, const FwdR& f, int chunk) {
+  const int nch = (f.nsub + 3) >> 2;
+  const uint32_t soff = (uint32_t)min(chunk, nch - 1) * 64u;
+  char* dst = smem + kRCodeBase + BUF * kCodes;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) dma16(f.cr, dst + (64 * q + 16 * f.w) * 64, f.co[q], soff);
+}
+__device__ __forceinline__ Scale fwdr_scale(const FwdR& f, int i, int blk) {
+  const int b = min(blk, f.nblk - 1);
+  return Scale{f.aq[i][b], f.gs[(f.ablk0[i] + (uint32_t)b) >> 8]};
+}
+// The lane's 8 code bytes (16 weights) of row i in stage st: chunk st & 3 of
+// the row in code buffer (st >> 2) & 1 (chunk c of row r at position
+// c ^ ((r >> 2) & 3)).
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint2 fwdr_codes(const char* smem, const FwdR& f, int i, int st) {
+  const char* p = smem + kRCodeBase + ((st >> 2) & 1) * kCodes + f.crow[i] + 16 * ((st & 3) ^ f.cswz[i]);
+  const u32x2_t v = *reinterpret_cast<const u32x2_t*>(p);   // a native vector type (see rd16)
+  return make_uint2(v.x, v.y);
+}
+
+struct FragsR {
+  bf16x8_t b0[8], b1[8];   // token fragments of k16 steps 0 and 1
+  bf16x8_t a[2][2];        // weight fragments of the current stage [row][kk]
+  bf16x8_t an[2][2];       // ... of the next stage
+};
+
+template <int FI, int FJ>
+__device__ __forceinline__ void mfma_rows(f32x16_t (&acc)[FI][FJ], const bf16x8_t (&a)[FI], const bf16x8_t (&b)[FJ]) {
+#pragma unroll
+  for (int i = 0; i < FI; ++i)
+#pragma unroll
+    for (int j = 0; j < FJ; ++j) acc[i][j] = mfma32x32x16(a[i], b[j], acc[i][j]);
+}
+
+// Eight weights (a code dword) -> bf16 x 8 fragment.
+__device__ __forceinline__ bf16x8_t deq_frag(uint32_t c, const Nf4Table& T) {
+  uint32_t o[4];
+  dequant8(c, T, o);
+  return __builtin_bit_cast(bf16x8_t, make_uint4(o[0], o[1], o[2], o[3]));
+}
+
+// One MFMA half of the register-A forward: 16 MFMAs, eight token-fragment
+// reads early, about three VALU instructions per MFMA.
+__device__ __forceinline__ void schedule_half_r() {
+#pragma unroll
+  for (int x = 0; x < 16; ++x) {
+    QLORA_SCHED(kSchedMfma, 1);
+    if (x < 8) QLORA_SCHED(kSchedDsRead, 1);
+    QLORA_SCHED(kSchedValu, 4);
+  }
+}
+
+template <int U8>
+__device__ __forceinline__ void fwdr_substep(char* smem, const FwdR& f, int s, f32x16_t (&acc)[2][8], FragsR& F,
+                                             Nf4Table (&T)[2], Scale (&sc)[4][2], int fo0, int fo1) {
+  constexpr int U = U8 & 3;
+  const char* cur = smem + U8 * kOp;
+  const char* nxt = smem + ((U8 + 1) & 7) * kOp;
+  __builtin_amdgcn_sched_barrier(0);
+  fwdr_dma_x(smem, f, s + kRAhead, (U8 + kRAhead) & 7);
+  if constexpr (U == 3) fwdr_dma_codes<(U8 >> 2) & 1>(smem, f, (s >> 2) + 2);
+  if constexpr (U8 & 1) {
+    constexpr int SL = (((U8 + 1) >> 1) + 2) & 3;
+    sc[SL][0] = fwdr_scale(f, 0, ((s + 1) >> 1) + 2);
+    sc[SL][1] = fwdr_scale(f, 1, ((s + 1) >> 1) + 2);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  // codes of stage s+1 (both rows read before this substep's barrier: the
+  // code buffer is overwritten by DMA after the next one)
+  const uint2 c0 = fwdr_codes(smem, f, 0, s + 1), c1 = fwdr_codes(smem, f, 1, s + 1);
+  if constexpr (U8 & 1) {   // stage s+1 starts block (s+1)/2
+    constexpr int SL = ((U8 + 1) >> 1) & 3;
+    T[0] = make_table(block_scale(sc[SL][0].q, sc[SL][0].s2));
+    T[1] = make_table(block_scale(sc[SL][1].q, sc[SL][1].s2));
+  }
+  // first half: k16 0 of stage s; read k16 1 of stage s; dequantize row 0 of stage s+1
+#pragma unroll
+  for (int j = 0; j < 8; ++j) F.b1[j] = rd16(cur + j * 2048 + fo1);
+  {
+    const bf16x8_t a0[2] = {F.a[0][0], F.a[1][0]};
+    mfma_rows<2, 8>(acc, a0, F.b0);
+  }
+  F.an[0][0] = deq_frag(c0.x, T[0]);
+  F.an[0][1] = deq_frag(c0.y, T[0]);
+  schedule_half_r();
+  QLORA_WAIT(fwdr_vmcnt(U8), 0);
+  __builtin_amdgcn_s_barrier();
+  // second half: k16 1 of stage s; read k16 0 of stage s+1; dequantize row 1 of stage s+1
+#pragma unroll
+  for (int j = 0; j < 8; ++j) F.b0[j] = rd16(nxt + j * 2048 + fo0);
+  {
+    const bf16x8_t a1[2] = {F.a[0][1], F.a[1][1]};
+    mfma_rows<2, 8>(acc, a1, F.b1);
+  }
+  F.an[1][0] = deq_frag(c1.x, T[1]);
+  F.an[1][1] = deq_frag(c1.y, T[1]);
+  schedule_half_r();
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) F.a[i][kk] = F.an[i][kk];
+}
+
+__global__ __launch_bounds__(kThreads, 1) void nf4_fwd_r_kernel(Nf4View W, const bf16_t* __restrict__ X, int64_t M,
+                                                                const bf16_t* __restrict__ U,
+                                                                const bf16_t* __restrict__ Bl, int r, float s,
+                                                                bf16_t* __restrict__ Y, int tiles_n, int tiles_m) {
+  extern __shared__ __align__(16) char smem[];
+  int tn, tm;
+  map_tile(tiles_n, tiles_m, tn, tm);
+  const int64_t n0 = (int64_t)tn * kTile, m0 = (int64_t)tm * kTile;
+  const int t = threadIdx.x, lane = t & 63, lr = lane & 31, h = lane >> 5;
+  const int64_t N = W.N, K = W.K;
+
+  FwdR f;
+  f.w = __builtin_amdgcn_readfirstlane(t >> 6);
+  __builtin_assume(f.w >= 0 && f.w < 4);
+  f.xr = make_rsrc(X, (uint32_t)(M * K * 2));
+  f.cr = make_rsrc(W.codes, (uint32_t)(N * K / 2));
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    // rows past the end re-read the last row: finite data, never stored
+    const int row = dma_row(q, t >> 6, lane);
+    const int64_t xm = min(m0 + row, M - 1), wn = min(n0 + row, N - 1);
+    f.xo[q] = (uint32_t)(xm * K * 2 + dma_chunk(lane) * 16);
+    f.co[q] = (uint32_t)(wn * (K / 2) + dma_chunk(lane) * 16);
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int rt = 64 * f.w + 32 * i + lr;   // row within the tile
+    const int64_t own = min(n0 + rt, N - 1);
+    f.ablk0[i] = (uint32_t)(own * (K >> 6));
+    f.aq[i] = W.absmax_q + f.ablk0[i];
+    f.crow[i] = rt * 64 + 8 * h;
+    f.cswz[i] = (rt >> 2) & 3;
+  }
+  f.gs = W.group_scale;
+  f.nsub = (int)(K >> 5);
+  f.nblk = (int)(K >> 6);
+  // token fragment offsets: lane (lr, h) reads chunk 2h + kk of token row lr (+ 32 j)
+  const int fo0 = spos(lr, 2 * h), fo1 = spos(lr, 2 * h + 1);
+
+  f32x16_t acc[2][8];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+  // prologue: code chunks 0 and 1, scales of blocks 0..2, token stages
+  // 0 .. kRAhead - 1
+  fwdr_dma_codes<0>(smem, f, 0);
+  fwdr_dma_codes<1>(smem, f, 1);
+  Scale sc[4][2];
+#pragma unroll
+  for (int b = 0; b < 3; ++b)
+#pragma unroll
+    for (int i = 0; i < 2; ++i) sc[b][i] = fwdr_scale(f, i, b);
+#pragma unroll
+  for (int st = 0; st < kRAhead; ++st) fwdr_dma_x(smem, f, st, st);
+  QLORA_WAIT(0, 0);
+  __builtin_amdgcn_s_barrier();
+  Nf4Table T[2];
+  FragsR F;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    T[i] = make_table(block_scale(sc[0][i].q, sc[0][i].s2));
+    const uint2 c = fwdr_codes(smem, f, i, 0);
+    F.a[i][0] = deq_frag(c.x, T[i]);
+    F.a[i][1] = deq_frag(c.y, T[i]);
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) F.b0[j] = rd16(smem + j * 2048 + fo0);
+  // K % 64 == 0, so the stage count is even
+  int st = 0;
+#define QLORA_FWDR_SUB(u) fwdr_substep<u>(smem, f, st + u, acc, F, T, sc, fo0, fo1)
+  for (; st + 8 <= f.nsub; st += 8) {
+    QLORA_FWDR_SUB(0); QLORA_FWDR_SUB(1); QLORA_FWDR_SUB(2); QLORA_FWDR_SUB(3);
+    QLORA_FWDR_SUB(4); QLORA_FWDR_SUB(5); QLORA_FWDR_SUB(6); QLORA_FWDR_SUB(7);
+  }
+  const int rem = f.nsub - st;
+  if (rem >= 2) { QLORA_FWDR_SUB(0); QLORA_FWDR_SUB(1); }
+  if (rem >= 4) { QLORA_FWDR_SUB(2); QLORA_FWDR_SUB(3); }
+  if (rem >= 6) { QLORA_FWDR_SUB(4); QLORA_FWDR_SUB(5); }
+#undef QLORA_FWDR_SUB
+  // drain the DMAs still in flight (clamped re-loads) before reusing the ring
+  QLORA_WAIT(0, 0);
+  __builtin_amdgcn_s_barrier();
+
+  if (r > 0) {
+    // LoRA up-projection: acc += B (s U)^T over the rank, 32 at a time; the
+    // weight operand comes straight from B (rows of the lane, ranks 16h + 8kk)
+    for (int j0 = 0; j0 < r; j0 += 32) {
+      char* xb = smem;
+      tail_tokens(xb, U, M, r, m0, j0, s);
+      bf16x8_t a[2][2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int64_t n = n0 + 64 * f.w + 32 * i + lr;
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          const int col = j0 + 16 * h + 8 * kk;
+          uint4 v = make_uint4(0u, 0u, 0u, 0u);
+          if (col < r && n < N) v = *reinterpret_cast<const uint4*>(Bl + n * r + col);
+          a[i][kk] = __builtin_bit_cast(bf16x8_t, v);
+        }
+      }
+      QLORA_WAIT(0, 0);
+      __builtin_amdgcn_s_barrier();
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        bf16x8_t b[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) b[j] = rd16(xb + j * 2048 + (kk ? fo1 : fo0));
+        const bf16x8_t ak[2] = {a[0][kk], a[1][kk]};
+        mfma_rows<2, 8>(acc, ak, b);
+      }
+      QLORA_WAIT(0, 0);
+      __builtin_amdgcn_s_barrier();
+    }
+  }
+  // Output: lane (lr, h) of wave w holds token m0 + 32 j + lr and weight
+  // columns n0 + 64 w + 32 i + 8 q + 4 h + 0..3.
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int64_t row = m0 + 32 * j + lr;
+      if (row >= M) continue;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t col = n0 + 64 * f.w + 32 * i + 8 * q + 4 * h;
+        if (col < N)  // N % 8 == 0: the four columns are all in range
+          *reinterpret_cast<uint2*>(Y + row * N + col) =
+              make_uint2(pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
+                         pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]));
+      }
+    }
+}
+
+// ===========================================================================
 // Backward: dX = dY deq(W) + s G A.  Output tile 256 (m) x 256 (k); the
 // contraction runs over n.  Weight half of a stage = 32 rows n x 256
 // columns k, rows of 512 bytes with 32-byte block b of row n at position
@@ -649,11 +953,17 @@ hipError_t launch_fwd(const Nf4View& W, const bf16_t* X, int64_t M, const bf16_t
                       float s, bf16_t* Y, hipStream_t st) {
   const int tiles_n = (int)((W.N + kTile - 1) / kTile);
   const int tiles_m = (int)((M + kTile - 1) / kTile);
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&nf4_fwd_kernel),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsFwd);
+#ifdef QLORA_FWD_LDS_WEIGHTS
+  auto* fn = &nf4_fwd_kernel;
+  const size_t lds = kLdsFwd;
+#else
+  auto* fn = &nf4_fwd_r_kernel;
+  const size_t lds = kLdsFwdR;
+#endif
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(nf4_fwd_kernel, dim3(tiles_n * tiles_m), dim3(kThreads), kLdsFwd, st, W, X, M, U, B, r, s, Y,
-                     tiles_n, tiles_m);
+  hipLaunchKernelGGL(fn, dim3(tiles_n * tiles_m), dim3(kThreads), lds, st, W, X, M, U, B, r, s, Y, tiles_n, tiles_m);
   return hipGetLastError();
 }
 
