@@ -402,53 +402,64 @@ __global__ __launch_bounds__(kThreads, 1) void nf4_fwd_kernel(Nf4View W, const b
 // tile (eight 32-token B fragments): still 16 accumulator tiles per wave,
 // but every weight element a wave multiplies is one it dequantized itself,
 // straight into its MFMA A registers.  Only the token tile (DMA, a ring of
-// kRSlots stages) and the NF4 codes (DMA, four stages per chunk) pass
-// through LDS; no dequantized weight is written to LDS or waited for.
+// kRSlots stages shared by the four waves) and the wave's own NF4 codes
+// (DMA, two stages per chunk, four chunk buffers) pass through LDS; no
+// dequantized weight is written to LDS.
 //
 // k order inside a 32-wide stage: lane half h of an MFMA takes k 16h + 8kk
 // .. +7 in k16 step kk, so a lane's weight codes for a stage are the 8
 // contiguous bytes 8h .. 8h+7 of its row's 16, and its token fragment of
 // step kk is 16-byte chunk 2h + kk of the token row.
 //
-// Substep s (U8 = s mod 8, token ring slot s & 7): DMA of token stage
-// s + kRAhead; at s & 3 == 3 the DMA of code chunk s/4 + 2; at odd s the
-// scales of block (s+1)/2 + 2; then the MFMAs of stage s (k16 0 | barrier |
-// k16 1) with the dequantization of stage s+1 (row 0 in the first half, row
-// 1 in the second) between them.
+// Substep s (U8 = s mod 8; token stage s sits in ring slot s & 7), one
+// barrier each:
+//   wait until token stage s+1 and the code chunk of stage s+2 have landed;
+//   barrier (the token stage is then visible from every wave, and every
+//   wave has finished reading the slot about to be refilled);
+//   DMA token stage s + kRAhead; odd s: DMA code chunk (s+7)/2; even s:
+//   load the scales of block s/2 + 3;
+//   read the codes of stage s+2 (used by the next substep); odd s: build
+//   the tables of block (s+1)/2 (stage s+1 starts it);
+//   first half:  MFMAs of k16 step 0 of stage s; read step 1 of stage s;
+//                dequantize step 1 of stage s+1;
+//   second half: MFMAs of step 1 of stage s; read step 0 of stage s+1;
+//                dequantize step 0 of stage s+1 into the registers step 0
+//                of stage s has just freed.
 // ===========================================================================
 #ifndef QLORA_FWDR_AHEAD
 #define QLORA_FWDR_AHEAD 6
 #endif
 constexpr int kRSlots = 8;                                            // token ring depth (stage s in slot s & 7)
 constexpr int kRAhead = QLORA_FWDR_AHEAD;                             // token stages DMA'd ahead of use
-static_assert(kRAhead >= 3 && kRAhead <= kRSlots - 1, "the slot being refilled must be read out");
+// The refilled slot (stage s + kRAhead - 8) was last read in substep s-1 at
+// the latest; the code chunk DMA'd at substep 2c-7 is read at substep 2c-2.
+static_assert(kRAhead >= 2 && kRAhead <= 6, "ring / code-chunk schedule");
+constexpr int kRChunk = kTile * 32;                                   // 8 KiB: codes of two stages
 constexpr int kRCodeBase = kRSlots * kOp;                             // 128 KiB
-constexpr size_t kLdsFwdR = (size_t)kRCodeBase + 2 * kCodes;          // 160 KiB
+constexpr size_t kLdsFwdR = (size_t)kRCodeBase + 4 * kRChunk;         // 160 KiB
 
-// Loads issued by substep u (mod 8) of the register-A forward: 4 token DMAs,
-// 4 code DMAs at u & 3 == 3, 4 scale loads at odd u.
-constexpr int fwdr_loads(int u) { return 4 + ((u & 3) == 3 ? 4 : 0) + ((u & 1) ? 4 : 0); }
-// vmcnt for substep u: the token stage it reads next (issued kRAhead - 1
-// substeps earlier) has landed once the loads of the kRAhead - 2 later
-// substeps and of this one are all that may be in flight.  The code and
-// scale loads of the issuing substep itself are not counted (their order
-// against its token DMAs is the compiler's): a wait for more than needed,
-// never less.
+// Loads issued by substep v of the register-A forward: 4 token DMAs, then
+// 2 code DMAs at odd v or 4 scale loads at even v.
+constexpr int fwdr_loads(int v) { return 4 + ((v & 1) ? 2 : 4); }
+// vmcnt at the start of substep u: token stage u+1 (issued at substep
+// u + 1 - kRAhead) has landed once only the loads of substeps
+// u + 2 - kRAhead .. u - 1 may be in flight.
 constexpr int fwdr_vmcnt(int u) {
   int n = 0;
-  for (int k = 0; k <= kRAhead - 2; ++k) n += fwdr_loads((u - k + 64) & 7);
+  for (int v = u + 2 - kRAhead; v <= u - 1; ++v) n += fwdr_loads(v & 7);
   return n;
 }
+static_assert(fwdr_vmcnt(0) < 64 && fwdr_vmcnt(1) < 64, "vmcnt field");
 
 struct FwdR {
   rsrc_t xr, cr;          // X, NF4 codes
-  uint32_t xo[4], co[4];  // per-lane byte offsets of the four DMA instructions
+  uint32_t xo[4];         // per-lane byte offsets of the four token DMA instructions
+  uint32_t co[2];         // ... of the two code DMA instructions (row 64 w + lane, stage half p)
   const uint8_t* aq[2];   // absmax codes of the lane's two rows (block 0)
   const float* gs;        // group scales
   uint32_t ablk0[2];      // block index of (row, block 0)
   int nsub, nblk, w;
-  int crow[2];            // code-tile byte offset of the lane's 8-byte piece in row i (chunk position 0)
-  int cswz[2];            // the rows' chunk swizzle, (row >> 2) & 3
+  int crow[2];            // code-chunk byte offset of the lane's 8-byte piece in row i
 };
 
 __device__ __forceinline__ void fwdr_dma_x(char* smem, const FwdR& f, int stage, int slot) {
@@ -457,32 +468,31 @@ __device__ __forceinline__ void fwdr_dma_x(char* smem, const FwdR& f, int stage,
 #pragma unroll
   for (int q = 0; q < 4; ++q) dma16(f.xr, dst + (64 * q + 16 * f.w) * 64, f.xo[q], soff);
 }
-template <int BUF>   // BUF == chunk & 1
+// Code chunk c (stages 2c, 2c+1) of the wave's 64 rows into buffer BUF:
+// stage half p of row r at BUF * kRChunk + p * 4096 + 16 r.
+template <int BUF>
 __device__ __forceinline__ void fwdr_dma_codes(char* smem, const FwdR& f, int chunk) {
-  const int nch = (f.nsub + 3) >> 2;
-  const uint32_t soff = (uint32_t)min(chunk, nch - 1) * 64u;
-  char* dst = smem + kRCodeBase + BUF * kCodes;
+  const uint32_t soff = (uint32_t)min(chunk, (f.nsub >> 1) - 1) * 32u;
+  char* dst = smem + kRCodeBase + BUF * kRChunk + 64 * f.w * 16;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) dma16(f.cr, dst + (64 * q + 16 * f.w) * 64, f.co[q], soff);
+  for (int p = 0; p < 2; ++p) dma16(f.cr, dst + p * 4096, f.co[p], soff);
 }
 __device__ __forceinline__ Scale fwdr_scale(const FwdR& f, int i, int blk) {
   const int b = min(blk, f.nblk - 1);
   return Scale{f.aq[i][b], f.gs[(f.ablk0[i] + (uint32_t)b) >> 8]};
 }
-// The lane's 8 code bytes (16 weights) of row i in stage st: chunk st & 3 of
-// the row in code buffer (st >> 2) & 1 (chunk c of row r at position
-// c ^ ((r >> 2) & 3)).
+// The lane's 8 code bytes (16 weights) of row i in stage st.
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint2 fwdr_codes(const char* smem, const FwdR& f, int i, int st) {
-  const char* p = smem + kRCodeBase + ((st >> 2) & 1) * kCodes + f.crow[i] + 16 * ((st & 3) ^ f.cswz[i]);
+  const char* p = smem + kRCodeBase + ((st >> 1) & 3) * kRChunk + (st & 1) * 4096 + f.crow[i];
   const u32x2_t v = *reinterpret_cast<const u32x2_t*>(p);   // a native vector type (see rd16)
   return make_uint2(v.x, v.y);
 }
 
 struct FragsR {
   bf16x8_t b0[8], b1[8];   // token fragments of k16 steps 0 and 1
-  bf16x8_t a[2][2];        // weight fragments of the current stage [row][kk]
-  bf16x8_t an[2][2];       // ... of the next stage
+  bf16x8_t a0[2], a1[2];   // weight fragments of the current stage, steps 0 and 1 [row]
+  uint2 c[2];              // codes of the next stage [row]
 };
 
 template <int FI, int FJ>
@@ -500,66 +510,152 @@ __device__ __forceinline__ bf16x8_t deq_frag(uint32_t c, const Nf4Table& T) {
   return __builtin_bit_cast(bf16x8_t, make_uint4(o[0], o[1], o[2], o[3]));
 }
 
-// One MFMA half of the register-A forward: 16 MFMAs, eight token-fragment
-// reads early, about three VALU instructions per MFMA.
-__device__ __forceinline__ void schedule_half_r() {
-#pragma unroll
-  for (int x = 0; x < 16; ++x) {
-    QLORA_SCHED(kSchedMfma, 1);
-    if (x < 8) QLORA_SCHED(kSchedDsRead, 1);
-    QLORA_SCHED(kSchedValu, 4);
+// The dequantization work of a substep is cut into chunks of five or six
+// VALU instructions, one chunk after each MFMA, and every MFMA slot is fenced
+// so that the compiler keeps the interleave (left to itself it bunches a
+// whole decode between two MFMAs and leaves the matrix unit idle).
+//
+// Decode of one code dword (eight weights) in five chunks; the steps are
+// those of dequant8.
+struct DqState {
+  uint32_t sa, sb, o, le, he, lo, ho, l01, h01;
+};
+template <int K>
+__device__ __forceinline__ void dq_chunk(DqState& d, uint32_t c, const Nf4Table& T, bf16x8_t& out) {
+  if constexpr (K == 0) {
+    const uint32_t e = c & 0x0F0F0F0Fu;
+    d.o = (c >> 4) & 0x0F0F0F0Fu;
+    d.sa = e + (e & 0x08080808u);
+    d.sb = d.sa ^ 0x10101010u;
+  } else if constexpr (K == 1) {
+    d.le = perm(T.lo[1], T.lo[0], d.sa) & perm(T.lo[3], T.lo[2], d.sb);
+    d.he = perm(T.hi[1], T.hi[0], d.sa) & perm(T.hi[3], T.hi[2], d.sb);
+  } else if constexpr (K == 2) {
+    d.sa = d.o + (d.o & 0x08080808u);
+    d.sb = d.sa ^ 0x10101010u;
+    d.lo = perm(T.lo[1], T.lo[0], d.sa) & perm(T.lo[3], T.lo[2], d.sb);
+  } else if constexpr (K == 3) {
+    d.ho = perm(T.hi[1], T.hi[0], d.sa) & perm(T.hi[3], T.hi[2], d.sb);
+    d.l01 = perm(d.lo, d.le, 0x05010400u);
+    d.h01 = perm(d.ho, d.he, 0x05010400u);
+  } else {
+    const uint32_t l23 = perm(d.lo, d.le, 0x07030602u);
+    const uint32_t h23 = perm(d.ho, d.he, 0x07030602u);
+    out = __builtin_bit_cast(bf16x8_t, make_uint4(perm(d.h01, d.l01, 0x05010400u), perm(d.h01, d.l01, 0x07030602u),
+                                                  perm(h23, l23, 0x05010400u), perm(h23, l23, 0x07030602u)));
   }
+}
+// Table of one block in six chunks; the steps are those of make_table.
+struct TbState {
+  float t;
+  uint32_t p[8];
+};
+template <int K>
+__device__ __forceinline__ void tb_chunk(TbState& b, const Scale& sc, Nf4Table& T) {
+  auto pair = [&](int i) {
+    b.p[i] = pack_bf16x2(u2f(kNf4LevelBits[2 * i]) * b.t, u2f(kNf4LevelBits[2 * i + 1]) * b.t);
+  };
+  if constexpr (K == 0) {
+    b.t = block_scale(sc.q, sc.s2);
+    pair(0);
+  } else if constexpr (K < 4) {
+    pair(2 * K - 1);
+    pair(2 * K);
+  } else if constexpr (K == 4) {
+    pair(7);
+    T.lo[0] = perm(b.p[1], b.p[0], 0x06040200u);
+    T.hi[0] = perm(b.p[1], b.p[0], 0x07050301u);
+    T.lo[1] = perm(b.p[3], b.p[2], 0x06040200u);
+  } else {
+    T.hi[1] = perm(b.p[3], b.p[2], 0x07050301u);
+#pragma unroll
+    for (int j = 2; j < 4; ++j) {
+      T.lo[j] = perm(b.p[2 * j + 1], b.p[2 * j], 0x06040200u);
+      T.hi[j] = perm(b.p[2 * j + 1], b.p[2 * j], 0x07050301u);
+    }
+  }
+}
+
+// MFMA slot X (0..31) of a register-A forward substep: slot X < 16 is
+// fragment pair (row X & 1, token fragment X >> 1) of k16 step 0, slot
+// X >= 16 the same for step 1.  Besides its MFMA a slot carries:
+//   global loads  token DMA (stage s + kRAhead) in slots 1, 3, 5, 7; odd s:
+//                 code DMA (chunk (s+7)/2) in slots 9, 11; even s: the
+//                 absmax code and group scale of block s/2 + 3 in slots 9, 11
+//                 (row 0) and 13, 15 (row 1)
+//   LDS reads     slots 0..7: step 1 of stage s, fragment X; slots 16..23:
+//                 step 0 of stage s+1, fragment X - 16 (its register was last
+//                 read by slot 2(X-16)+1)
+//   VALU chunks   odd s:  tables of block (s+1)/2 in slots 0..11, step 1 of
+//                         stage s+1 in 12..21, step 0 of stage s+1 in 22..31
+//                 even s: step 1 of stage s+1 in 0..9, step 0 in 16..25
+//                 (step 0 is written over the step 0 registers of stage s,
+//                 last read by slot 15)
+template <int U8, int X>
+__device__ __forceinline__ void fwdr_slot(char* smem, const FwdR& f, int s, f32x16_t (&acc)[2][8], FragsR& F,
+                                          Nf4Table (&T)[2], Scale (&sc)[4][2], bf16x8_t (&n1)[2], DqState& dq,
+                                          TbState& tb, int fo0, int fo1) {
+  constexpr bool kOdd = (U8 & 1) != 0;
+  constexpr int i = X & 1, j = (X & 15) >> 1;
+  if constexpr (X < 16)
+    acc[i][j] = mfma32x32x16(F.a0[i], F.b0[j], acc[i][j]);
+  else
+    acc[i][j] = mfma32x32x16(F.a1[i], F.b1[j], acc[i][j]);
+  // global loads
+  if constexpr (X < 8 && (X & 1)) {
+    const uint32_t soff = (uint32_t)min(s + kRAhead, f.nsub - 1) * 64u;
+    dma16(f.xr, smem + ((U8 + kRAhead) & 7) * kOp + (64 * (X >> 1) + 16 * f.w) * 64, f.xo[X >> 1], soff);
+  } else if constexpr (kOdd && (X == 9 || X == 11)) {
+    constexpr int c8 = (U8 + 7) >> 1;   // chunk (s+7)/2 is c8 mod 4
+    const uint32_t soff = (uint32_t)min((s + 7) >> 1, (f.nsub >> 1) - 1) * 32u;
+    dma16(f.cr, smem + kRCodeBase + (c8 & 3) * kRChunk + 64 * f.w * 16 + ((X - 9) >> 1) * 4096, f.co[(X - 9) >> 1],
+          soff);
+  } else if constexpr (!kOdd && X >= 9 && X <= 15 && (X & 1)) {
+    constexpr int SL = ((U8 >> 1) + 3) & 3, row = (X - 9) >> 2;
+    const int b = min((s >> 1) + 3, f.nblk - 1);
+    if constexpr (((X - 9) >> 1) & 1)
+      sc[SL][row].s2 = f.gs[(f.ablk0[row] + (uint32_t)b) >> 8];
+    else
+      sc[SL][row].q = f.aq[row][b];
+  }
+  // LDS reads
+  if constexpr (X < 8) F.b1[X] = rd16(smem + U8 * kOp + X * 2048 + fo1);
+  if constexpr (X >= 16 && X < 24) F.b0[X - 16] = rd16(smem + ((U8 + 1) & 7) * kOp + (X - 16) * 2048 + fo0);
+  // VALU chunks
+  if constexpr (kOdd) {
+    constexpr int SL = ((U8 + 1) >> 1) & 3;
+    if constexpr (X < 12) tb_chunk<X % 6>(tb, sc[SL][X / 6], T[X / 6]);
+    else if constexpr (X < 22) dq_chunk<(X - 12) % 5>(dq, F.c[(X - 12) / 5].y, T[(X - 12) / 5], n1[(X - 12) / 5]);
+    else dq_chunk<(X - 22) % 5>(dq, F.c[(X - 22) / 5].x, T[(X - 22) / 5], F.a0[(X - 22) / 5]);
+  } else {
+    if constexpr (X < 10) dq_chunk<X % 5>(dq, F.c[X / 5].y, T[X / 5], n1[X / 5]);
+    else if constexpr (X >= 16 && X < 26) dq_chunk<(X - 16) % 5>(dq, F.c[(X - 16) / 5].x, T[(X - 16) / 5], F.a0[(X - 16) / 5]);
+  }
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 template <int U8>
 __device__ __forceinline__ void fwdr_substep(char* smem, const FwdR& f, int s, f32x16_t (&acc)[2][8], FragsR& F,
                                              Nf4Table (&T)[2], Scale (&sc)[4][2], int fo0, int fo1) {
-  constexpr int U = U8 & 3;
-  const char* cur = smem + U8 * kOp;
-  const char* nxt = smem + ((U8 + 1) & 7) * kOp;
   __builtin_amdgcn_sched_barrier(0);
-  fwdr_dma_x(smem, f, s + kRAhead, (U8 + kRAhead) & 7);
-  if constexpr (U == 3) fwdr_dma_codes<(U8 >> 2) & 1>(smem, f, (s >> 2) + 2);
-  if constexpr (U8 & 1) {
-    constexpr int SL = (((U8 + 1) >> 1) + 2) & 3;
-    sc[SL][0] = fwdr_scale(f, 0, ((s + 1) >> 1) + 2);
-    sc[SL][1] = fwdr_scale(f, 1, ((s + 1) >> 1) + 2);
-  }
-  __builtin_amdgcn_sched_barrier(0);
-  // codes of stage s+1 (both rows read before this substep's barrier: the
-  // code buffer is overwritten by DMA after the next one)
-  const uint2 c0 = fwdr_codes(smem, f, 0, s + 1), c1 = fwdr_codes(smem, f, 1, s + 1);
-  if constexpr (U8 & 1) {   // stage s+1 starts block (s+1)/2
-    constexpr int SL = ((U8 + 1) >> 1) & 3;
-    T[0] = make_table(block_scale(sc[SL][0].q, sc[SL][0].s2));
-    T[1] = make_table(block_scale(sc[SL][1].q, sc[SL][1].s2));
-  }
-  // first half: k16 0 of stage s; read k16 1 of stage s; dequantize row 0 of stage s+1
-#pragma unroll
-  for (int j = 0; j < 8; ++j) F.b1[j] = rd16(cur + j * 2048 + fo1);
-  {
-    const bf16x8_t a0[2] = {F.a[0][0], F.a[1][0]};
-    mfma_rows<2, 8>(acc, a0, F.b0);
-  }
-  F.an[0][0] = deq_frag(c0.x, T[0]);
-  F.an[0][1] = deq_frag(c0.y, T[0]);
-  schedule_half_r();
-  QLORA_WAIT(fwdr_vmcnt(U8), 0);
+  QLORA_WAIT(fwdr_vmcnt(U8), 15);
   __builtin_amdgcn_s_barrier();
-  // second half: k16 1 of stage s; read k16 0 of stage s+1; dequantize row 1 of stage s+1
-#pragma unroll
-  for (int j = 0; j < 8; ++j) F.b0[j] = rd16(nxt + j * 2048 + fo0);
-  {
-    const bf16x8_t a1[2] = {F.a[0][1], F.a[1][1]};
-    mfma_rows<2, 8>(acc, a1, F.b1);
-  }
-  F.an[1][0] = deq_frag(c1.x, T[1]);
-  F.an[1][1] = deq_frag(c1.y, T[1]);
-  schedule_half_r();
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) F.a[i][kk] = F.an[i][kk];
+  __builtin_amdgcn_sched_barrier(0);
+  // codes of stage s+2, for the next substep
+  const uint2 cn0 = fwdr_codes(smem, f, 0, s + 2), cn1 = fwdr_codes(smem, f, 1, s + 2);
+  bf16x8_t n1[2];
+  DqState dq;
+  TbState tb;
+#define QLORA_FWDR_SLOT(x) fwdr_slot<U8, x>(smem, f, s, acc, F, T, sc, n1, dq, tb, fo0, fo1)
+#define QLORA_FWDR_SLOT4(x) QLORA_FWDR_SLOT(x); QLORA_FWDR_SLOT(x + 1); QLORA_FWDR_SLOT(x + 2); QLORA_FWDR_SLOT(x + 3)
+  QLORA_FWDR_SLOT4(0); QLORA_FWDR_SLOT4(4); QLORA_FWDR_SLOT4(8); QLORA_FWDR_SLOT4(12);
+  QLORA_FWDR_SLOT4(16); QLORA_FWDR_SLOT4(20); QLORA_FWDR_SLOT4(24); QLORA_FWDR_SLOT4(28);
+#undef QLORA_FWDR_SLOT4
+#undef QLORA_FWDR_SLOT
+  F.a1[0] = n1[0];
+  F.a1[1] = n1[1];
+  F.c[0] = cn0;
+  F.c[1] = cn1;
 }
 
 __global__ __launch_bounds__(kThreads, 1) void nf4_fwd_r_kernel(Nf4View W, const bf16_t* __restrict__ X, int64_t M,
@@ -581,10 +677,13 @@ __global__ __launch_bounds__(kThreads, 1) void nf4_fwd_r_kernel(Nf4View W, const
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     // rows past the end re-read the last row: finite data, never stored
-    const int row = dma_row(q, t >> 6, lane);
-    const int64_t xm = min(m0 + row, M - 1), wn = min(n0 + row, N - 1);
+    const int64_t xm = min(m0 + dma_row(q, t >> 6, lane), M - 1);
     f.xo[q] = (uint32_t)(xm * K * 2 + dma_chunk(lane) * 16);
-    f.co[q] = (uint32_t)(wn * (K / 2) + dma_chunk(lane) * 16);
+  }
+  {
+    const int64_t wn = min(n0 + 64 * f.w + lane, N - 1);
+#pragma unroll
+    for (int p = 0; p < 2; ++p) f.co[p] = (uint32_t)(wn * (K / 2) + 16 * p);
   }
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
@@ -592,8 +691,7 @@ __global__ __launch_bounds__(kThreads, 1) void nf4_fwd_r_kernel(Nf4View W, const
     const int64_t own = min(n0 + rt, N - 1);
     f.ablk0[i] = (uint32_t)(own * (K >> 6));
     f.aq[i] = W.absmax_q + f.ablk0[i];
-    f.crow[i] = rt * 64 + 8 * h;
-    f.cswz[i] = (rt >> 2) & 3;
+    f.crow[i] = rt * 16 + 8 * h;
   }
   f.gs = W.group_scale;
   f.nsub = (int)(K >> 5);
@@ -609,10 +707,12 @@ __global__ __launch_bounds__(kThreads, 1) void nf4_fwd_r_kernel(Nf4View W, const
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-  // prologue: code chunks 0 and 1, scales of blocks 0..2, token stages
+  // prologue: code chunks 0..3, scales of blocks 0..2, token stages
   // 0 .. kRAhead - 1
   fwdr_dma_codes<0>(smem, f, 0);
   fwdr_dma_codes<1>(smem, f, 1);
+  fwdr_dma_codes<2>(smem, f, 2);
+  fwdr_dma_codes<3>(smem, f, 3);
   Scale sc[4][2];
 #pragma unroll
   for (int b = 0; b < 3; ++b)
@@ -628,8 +728,9 @@ __global__ __launch_bounds__(kThreads, 1) void nf4_fwd_r_kernel(Nf4View W, const
   for (int i = 0; i < 2; ++i) {
     T[i] = make_table(block_scale(sc[0][i].q, sc[0][i].s2));
     const uint2 c = fwdr_codes(smem, f, i, 0);
-    F.a[i][0] = deq_frag(c.x, T[i]);
-    F.a[i][1] = deq_frag(c.y, T[i]);
+    F.a0[i] = deq_frag(c.x, T[i]);
+    F.a1[i] = deq_frag(c.y, T[i]);
+    F.c[i] = fwdr_codes(smem, f, i, 1);
   }
 #pragma unroll
   for (int j = 0; j < 8; ++j) F.b0[j] = rd16(smem + j * 2048 + fo0);
@@ -648,7 +749,6 @@ __global__ __launch_bounds__(kThreads, 1) void nf4_fwd_r_kernel(Nf4View W, const
   // drain the DMAs still in flight (clamped re-loads) before reusing the ring
   QLORA_WAIT(0, 0);
   __builtin_amdgcn_s_barrier();
-
   if (r > 0) {
     // LoRA up-projection: acc += B (s U)^T over the rank, 32 at a time; the
     // weight operand comes straight from B (rows of the lane, ranks 16h + 8kk)
