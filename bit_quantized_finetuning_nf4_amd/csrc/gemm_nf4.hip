@@ -549,11 +549,16 @@ __device__ __forceinline__ void dq_chunk(DqState& d, uint32_t c, const Nf4Table&
 struct TbState {
   float t;
   uint32_t p[8];
+  Nf4Table T;   // the table of the lane's own row, before the lane-half swap
 };
+// The products by the levels 0 (code 7) and 1 (code 15) are 0 and t
+// exactly (t is finite and not negative), so they are not multiplied out.
 template <int K>
 __device__ __forceinline__ void tb_chunk(TbState& b, const Scale& sc, Nf4Table& T) {
   auto pair = [&](int i) {
-    b.p[i] = pack_bf16x2(u2f(kNf4LevelBits[2 * i]) * b.t, u2f(kNf4LevelBits[2 * i + 1]) * b.t);
+    const float lo = u2f(kNf4LevelBits[2 * i]) * b.t;
+    const float hi = (2 * i + 1 == 7) ? 0.0f : (2 * i + 1 == 15) ? b.t : u2f(kNf4LevelBits[2 * i + 1]) * b.t;
+    b.p[i] = pack_bf16x2(lo, hi);
   };
   if constexpr (K == 0) {
     b.t = block_scale(sc.q, sc.s2);
@@ -586,8 +591,10 @@ __device__ __forceinline__ void tb_chunk(TbState& b, const Scale& sc, Nf4Table& 
 //   LDS reads     slots 0..7: step 1 of stage s, fragment X; slots 16..23:
 //                 step 0 of stage s+1, fragment X - 16 (its register was last
 //                 read by slot 2(X-16)+1)
-//   VALU chunks   odd s:  tables of block (s+1)/2 in slots 0..11, step 1 of
-//                         stage s+1 in 12..21, step 0 of stage s+1 in 22..31
+//   VALU chunks   odd s:  in slots 0..5 lane half h builds the table of block
+//                         (s+1)/2 for row h, and slot 6 swaps lane halves
+//                         so that every lane holds both rows' tables; step 1
+//                         of stage s+1 in 7..16, step 0 in 17..26
 //                 even s: step 1 of stage s+1 in 0..9, step 0 in 16..25
 //                 (step 0 is written over the step 0 registers of stage s,
 //                 last read by slot 15)
@@ -597,6 +604,8 @@ __device__ __forceinline__ void fwdr_slot(char* smem, const FwdR& f, int s, f32x
                                           TbState& tb, int fo0, int fo1) {
   constexpr bool kOdd = (U8 & 1) != 0;
   constexpr int i = X & 1, j = (X & 15) >> 1;
+  // the step-1 fragments (read in slots 0..7) and the codes: one wait for all
+  if constexpr (X == 16) QLORA_WAIT(63, 0);
   if constexpr (X < 16)
     acc[i][j] = mfma32x32x16(F.a0[i], F.b0[j], acc[i][j]);
   else
@@ -624,9 +633,28 @@ __device__ __forceinline__ void fwdr_slot(char* smem, const FwdR& f, int s, f32x
   // VALU chunks
   if constexpr (kOdd) {
     constexpr int SL = ((U8 + 1) >> 1) & 3;
-    if constexpr (X < 12) tb_chunk<X % 6>(tb, sc[SL][X / 6], T[X / 6]);
-    else if constexpr (X < 22) dq_chunk<(X - 12) % 5>(dq, F.c[(X - 12) / 5].y, T[(X - 12) / 5], n1[(X - 12) / 5]);
-    else dq_chunk<(X - 22) % 5>(dq, F.c[(X - 22) / 5].x, T[(X - 22) / 5], F.a0[(X - 22) / 5]);
+    if constexpr (X < 6) {
+      const bool hi = (threadIdx.x & 32) != 0;
+      const Scale mine{hi ? sc[SL][1].q : sc[SL][0].q, hi ? sc[SL][1].s2 : sc[SL][0].s2};
+      tb_chunk<X>(tb, mine, tb.T);
+    } else if constexpr (X == 6) {
+      // lanes 0..31 hold row 0's table and lanes 32..63 row 1's: swapping the
+      // upper half of one copy with the lower half of another gives each row's
+      // table in every lane
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const u32x2_t lo = __builtin_amdgcn_permlane32_swap(tb.T.lo[q], tb.T.lo[q], false, false);
+        const u32x2_t hi = __builtin_amdgcn_permlane32_swap(tb.T.hi[q], tb.T.hi[q], false, false);
+        T[0].lo[q] = lo[0];
+        T[1].lo[q] = lo[1];
+        T[0].hi[q] = hi[0];
+        T[1].hi[q] = hi[1];
+      }
+    } else if constexpr (X >= 7 && X < 17) {
+      dq_chunk<(X - 7) % 5>(dq, F.c[(X - 7) / 5].y, T[(X - 7) / 5], n1[(X - 7) / 5]);
+    } else if constexpr (X >= 17 && X < 27) {
+      dq_chunk<(X - 17) % 5>(dq, F.c[(X - 17) / 5].x, T[(X - 17) / 5], F.a0[(X - 17) / 5]);
+    }
   } else {
     if constexpr (X < 10) dq_chunk<X % 5>(dq, F.c[X / 5].y, T[X / 5], n1[X / 5]);
     else if constexpr (X >= 16 && X < 26) dq_chunk<(X - 16) % 5>(dq, F.c[(X - 16) / 5].x, T[(X - 16) / 5], F.a0[(X - 16) / 5]);
@@ -638,7 +666,9 @@ template <int U8>
 __device__ __forceinline__ void fwdr_substep(char* smem, const FwdR& f, int s, f32x16_t (&acc)[2][8], FragsR& F,
                                              Nf4Table (&T)[2], Scale (&sc)[4][2], int fo0, int fo1) {
   __builtin_amdgcn_sched_barrier(0);
-  QLORA_WAIT(fwdr_vmcnt(U8), 15);
+  // the LDS reads of the last substep (step 0 of stage s, issued 16 slots
+  // ago) are waited for here too
+  QLORA_WAIT(fwdr_vmcnt(U8), 0);
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
   // codes of stage s+2, for the next substep
