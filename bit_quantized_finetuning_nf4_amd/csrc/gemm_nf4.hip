@@ -911,43 +911,118 @@ __device__ __forceinline__ void dx_produce(char* smem, const Codes& c, const Nf4
   }
 }
 
-// Substep s, U8 = s mod 8: loads of codes for stage s+4 (register set U8 & 3)
-// and dY of stage s+3; dY of stage s+2 (loaded one substep ago) is stored
-// after the barrier; dequantization of stage s+2.
+// Substep s, U8 = s mod 8, one barrier at its start: the barrier makes stage
+// s+1 (dequantized and stored during substep s-1) visible, and every wave has
+// finished reading stage s-2, whose ring buffer (s+2) & 3 this substep fills.
+// 32 MFMA slots, fenced one from another; slot x = 16 kk + 4 i + j is
+// fragment (i, j) of k16 step kk.  Besides its MFMA a slot carries:
+//   LDS reads     slots 0..11: step 1 of stage s (A fragment i in slots 2i,
+//                 2i + 1, B fragment j in slot 8 + j); slots 16..27: step 0
+//                 of stage s+1 in the same pattern, into the registers
+//                 step 0 of stage s has finished with
+//   global loads  slots 1, 3, 5, 7: dY of stage s+3; slots 9, 11, 13:
+//                 codes, absmax code and group scale of stage s+4
+//   LDS writes    slots 2, 6, 10, 14: dY of stage s+2 (loaded last
+//                 substep); slots 11, 16, 21, 26: the four dequantized
+//                 16-byte chunks of stage s+2
+//   VALU chunks   slots 0..5: table of the thread's row and block; slots
+//                 6..25: the four decodes, five chunks each
+template <int I>
+__device__ __forceinline__ uint32_t u4_word(const uint4& v) {
+  return I == 0 ? v.x : I == 1 ? v.y : I == 2 ? v.z : v.w;
+}
+
+template <int U8, int X>
+__device__ __forceinline__ void dx_slot(char* smem, const Dx& d, int s, f32x16_t (&acc)[4][4], Frags& F,
+                                        Codes (&cs)[4], YRegs (&ys)[2], const int (&ao)[4], int bm, FragOffs fo,
+                                        TbState& tb, Nf4Table& T, DqState& dq, bf16x8_t& dqo) {
+  constexpr int U = U8 & 3;
+  constexpr int kk = X >> 4, i = (X >> 2) & 3, j = X & 3, y = X & 15;
+  const char* cur = smem + U * kStage;
+  const char* nxt = smem + ((U + 1) & 3) * kStage;
+  if constexpr (kk == 0)
+    acc[i][j] = mfma32x32x16(F.a0[i], F.b0[j], acc[i][j]);
+  else
+    acc[i][j] = mfma32x32x16(F.a1[i], F.b1[j], acc[i][j]);
+  // LDS reads: A fragment r = y / 2 is two transposed reads 4 rows apart
+  if constexpr (y < 8) {
+    constexpr int r = y >> 1, part = y & 1;
+    const char* p = (kk == 0 ? cur + 16 * kWRow : nxt) + ao[r] + part * 4 * kWRow;
+    const uint2 v = rd_tr(p);
+    bf16x8_t& a = kk == 0 ? F.a1[r] : F.a0[r];
+    uint4 w = __builtin_bit_cast(uint4, a);
+    if constexpr (part == 0) {
+      w.x = v.x;
+      w.y = v.y;
+    } else {
+      w.z = v.x;
+      w.w = v.y;
+    }
+    a = __builtin_bit_cast(bf16x8_t, w);
+  } else if constexpr (y < 12) {
+    if constexpr (kk == 0)
+      F.b1[y - 8] = rd16(cur + kOp + bm + (y - 8) * 2048 + fo.o1);
+    else
+      F.b0[y - 8] = rd16(nxt + kOp + bm + (y - 8) * 2048 + fo.o0);
+  }
+  // global loads
+  if constexpr (kk == 0 && y < 8 && (y & 1)) {
+    const uint32_t soff = (uint32_t)min(s + 3, d.nsub - 1) * 64u;
+    ys[U8 & 1].v[y >> 1] = buf_load16(d.yr, d.yo[y >> 1], soff);
+  }
+  if constexpr (kk == 0 && (y == 9 || y == 11 || y == 13)) {
+    const uint32_t st = (uint32_t)min(s + 4, d.nsub - 1);
+    if constexpr (y == 9) cs[U].c = buf_load16(d.cr, d.co, st * d.cstride);
+    if constexpr (y == 11) cs[U].q = __builtin_amdgcn_raw_buffer_load_b8(d.ar, d.ao, st * d.astride, 0);
+    if constexpr (y == 13) {
+      const uint32_t g = (d.ablk + st * 32u * d.kb) >> 8;
+      cs[U].s2 = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(d.gr, g * 4u, 0, 0));
+    }
+  }
+  // LDS writes
+  if constexpr (kk == 0 && (y & 3) == 2) wr16(smem + ((U + 2) & 3) * kStage + kOp + d.ypos[y >> 2],
+                                                ys[(U8 + 1) & 1].v[y >> 2]);
+  constexpr int kProduced = (X == 11) ? 0 : (X == 16) ? 1 : (X == 21) ? 2 : (X == 26) ? 3 : -1;
+  if constexpr (kProduced >= 0) {
+    const int t = threadIdx.x, n = t >> 3, jj = t & 7, flip = (t >> 2) & 1;
+    const int p = kProduced ^ flip, ch = 4 * jj + p;   // 16-byte chunk of the row (8 columns)
+    wr16(smem + ((U + 2) & 3) * kStage + tpos(n, ch >> 1) + 16 * (ch & 1), __builtin_bit_cast(uint4, dqo));
+  }
+  // VALU chunks: stage s+2 from code set (U + 2) & 3
+  {
+    const Codes& pc = cs[(U + 2) & 3];
+    if constexpr (X < 6) {
+      tb_chunk<X>(tb, Scale{pc.q, pc.s2}, T);
+    } else if constexpr (X < 26) {
+      constexpr int dd = (X - 6) / 5, kc = (X - 6) % 5;
+      // chunk dd ^ flip: a select between two fixed words (a runtime index
+      // into the code registers would send them to scratch)
+      const bool flip = (threadIdx.x & 4) != 0;
+      const uint32_t word = flip ? u4_word<dd ^ 1>(pc.c) : u4_word<dd>(pc.c);
+      dq_chunk<kc>(dq, word, T, dqo);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 template <int U8>
 __device__ __forceinline__ void dx_substep(char* smem, const Dx& d, int s, f32x16_t (&acc)[4][4], Frags& F,
                                            Codes (&cs)[4], YRegs (&ys)[2], const int (&ao)[4], int bm,
                                            FragOffs fo) {
-  constexpr int U = U8 & 3;
-  const char* cur = smem + U * kStage;
-  const char* nxt = smem + ((U + 1) & 3) * kStage;
   __builtin_amdgcn_sched_barrier(0);
-  dx_load_codes(cs[U], d, s + 4);   // set U is free: stage s was dequantized two substeps ago
-  dx_load_y(ys[U8 & 1], d, s + 3);
-  __builtin_amdgcn_sched_barrier(0);
-  const Codes& pc = cs[(U + 2) & 3];
-  const Nf4Table T = make_table(block_scale(pc.q, pc.s2));
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    F.a1[i] = tfrag(cur + ao[i] + 16 * kWRow);
-    F.b1[i] = rd16(cur + kOp + bm + i * 2048 + fo.o1);
-  }
-  mfma_block<4, 4>(acc, F.a0, F.b0);
-  dx_produce(smem, pc, T, (U + 2) & 3, 0);
-  schedule_half<2>();
   QLORA_WAIT(63, 0);
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
-  dx_store_y(smem, d, ys[(U8 + 1) & 1], (U + 2) & 3);
-  __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    F.a0[i] = tfrag(nxt + ao[i]);
-    F.b0[i] = rd16(nxt + kOp + bm + i * 2048 + fo.o0);
-  }
-  mfma_block<4, 4>(acc, F.a1, F.b1);
-  dx_produce(smem, pc, T, (U + 2) & 3, 1);
-  schedule_half<2>();
+  TbState tb;
+  Nf4Table T;
+  DqState dq;
+  bf16x8_t dqo;
+#define QLORA_DX_SLOT(x) dx_slot<U8, x>(smem, d, s, acc, F, cs, ys, ao, bm, fo, tb, T, dq, dqo)
+#define QLORA_DX_SLOT4(x) QLORA_DX_SLOT(x); QLORA_DX_SLOT(x + 1); QLORA_DX_SLOT(x + 2); QLORA_DX_SLOT(x + 3)
+  QLORA_DX_SLOT4(0); QLORA_DX_SLOT4(4); QLORA_DX_SLOT4(8); QLORA_DX_SLOT4(12);
+  QLORA_DX_SLOT4(16); QLORA_DX_SLOT4(20); QLORA_DX_SLOT4(24); QLORA_DX_SLOT4(28);
+#undef QLORA_DX_SLOT4
+#undef QLORA_DX_SLOT
 }
 
 __global__ __launch_bounds__(kThreads, 1) void nf4_dx_kernel(Nf4View W, const bf16_t* __restrict__ dY, int64_t M,
