@@ -54,9 +54,13 @@ def gemv_bytes(N, K, r):
 
 
 def source_digest():
+    """Digest of every kernel source: traffic figures taken on other sources are not reported."""
     h = hashlib.sha256()
-    for f in ("device.h", "gemm_nf4.hip"):
-        h.update(open(os.path.join(ROOT, "bit_quantized_finetuning_nf4_amd", "csrc", f), "rb").read())
+    d = os.path.join(ROOT, "bit_quantized_finetuning_nf4_amd", "csrc")
+    for f in sorted(os.listdir(d)):
+        if f.endswith((".hip", ".h")):
+            h.update(f.encode())
+            h.update(open(os.path.join(d, f), "rb").read())
     return h.hexdigest()[:16]
 
 
@@ -73,7 +77,7 @@ def traffic_for(kernel):
     return e.get("hbm_bytes_per_launch")
 
 
-TRAFFIC_KERNELS = {"nf4_fwd_kernel": "fwd_kernel", "nf4_dx_kernel": "dx_kernel",
+TRAFFIC_KERNELS = {"nf4_fwd_r_kernel": "fwd_kernel", "nf4_fwd_kernel": "fwd_kernel", "nf4_dx_kernel": "dx_kernel",
                    "quantize_kernel": "quantize_kernel", "nf4_gemv_kernel": "gemv_kernel"}
 
 
