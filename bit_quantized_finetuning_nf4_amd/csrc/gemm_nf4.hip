@@ -831,6 +831,272 @@ __global__ __launch_bounds__(kThreads, 1) void nf4_fwd_r_kernel(Nf4View W, const
 }
 
 // ===========================================================================
+// Forward with eight waves (two per SIMD).  The tile is still 256 weight
+// rows x 256 tokens, but wave w owns only weight rows n0 + 32 w .. +31 (one
+// A fragment) against all 256 tokens: 8 accumulator tiles (128 registers),
+// so two waves share each SIMD.  A wave issues one instruction per cycle
+// slot at best, and one wave alone cannot keep the matrix unit busy while
+// it also issues the decode, the LDS reads and the loads; with two waves the
+// SIMD issues one wave's VALU or LDS work beside the other's MFMA.  The
+// decode per MFMA is unchanged (each weight still feeds 256 tokens); the
+// token fragments are read from LDS twice as often (1 KiB per MFMA).
+//
+// Substep s (stage s, ring slot s & 7), one barrier each, 16 MFMA slots
+// x = 8 kk + j (fragment j, k16 step kk), fenced from one another:
+//   after the MFMA of slot x, the LDS read of the fragment slot x + 8 needs
+//   (step 1 of stage s, or step 0 of stage s+1) into the register slot x
+//   has just used; slot 0 also reads the lane's codes of stage s+2;
+//   slots 1, 3: token DMA of stage s + kR8Ahead; odd s, slot 5: the wave's
+//   code DMA of chunk (s+7)/2; even s, slots 5, 7: absmax code and group
+//   scale of block s/2 + 3;
+//   VALU chunks: odd s builds the table of block (s+1)/2 (slots 0..5);
+//   step 1 of stage s+1 is decoded next, step 0 after slot 7 (into the
+//   registers of step 0 of stage s).
+// ===========================================================================
+#ifndef QLORA_FWD8_AHEAD
+#define QLORA_FWD8_AHEAD 6
+#endif
+constexpr int kThreads8 = 512;
+constexpr int kR8Ahead = QLORA_FWD8_AHEAD;
+static_assert(kR8Ahead >= 2 && kR8Ahead <= 6, "ring / code-chunk schedule");
+// Loads of substep v, token DMAs first: 2 token DMAs, then 1 code DMA (odd
+// v) or 2 scale loads (even v).
+constexpr int fwd8_tail(int v) { return (v & 1) ? 1 : 2; }
+constexpr int fwd8_loads(int v) { return 2 + fwd8_tail(v); }
+// vmcnt at the start of substep u: every load of substep u + 1 - kR8Ahead
+// has landed once only the loads of the later substeps may be in flight.
+// That covers token stage u+1 and the code chunk c DMA'd at substep 2c - 7,
+// which substep 2c - 2 reads first.
+constexpr int fwd8_vmcnt(int u) {
+  int n = 0;
+  for (int v = u + 2 - kR8Ahead; v <= u - 1; ++v) n += fwd8_loads(v);
+  return n;
+}
+static_assert(fwd8_vmcnt(0) < 64 && fwd8_vmcnt(1) < 64, "vmcnt field");
+
+struct Fwd8 {
+  rsrc_t xr, cr;
+  uint32_t xo[2];         // lane offsets of the wave's two token DMA instructions
+  uint32_t co;            // lane offset of the wave's code DMA (row 32 w + (lane & 31), stage half lane >> 5)
+  const uint8_t* aq;      // absmax codes of the lane's row (block 0)
+  const float* gs;
+  uint32_t ablk0;
+  int nsub, nblk, w;
+  int crow;               // byte offset of the lane's 8 code bytes in a chunk buffer (stage half 0)
+};
+
+__device__ __forceinline__ void fwd8_dma_x(char* smem, const Fwd8& f, int q, int stage, int slot) {
+  const uint32_t soff = (uint32_t)min(stage, f.nsub - 1) * 64u;
+  dma16(f.xr, smem + slot * kOp + (2 * f.w + q) * 1024, f.xo[q], soff);
+}
+template <int BUF>
+__device__ __forceinline__ void fwd8_dma_codes(char* smem, const Fwd8& f, int chunk) {
+  const uint32_t soff = (uint32_t)min(chunk, (f.nsub >> 1) - 1) * 32u;
+  dma16(f.cr, smem + kRCodeBase + BUF * kRChunk + f.w * 1024, f.co, soff);
+}
+__device__ __forceinline__ uint2 fwd8_codes(const char* smem, const Fwd8& f, int st) {
+  const u32x2_t v = *reinterpret_cast<const u32x2_t*>(smem + kRCodeBase + ((st >> 1) & 3) * kRChunk + (st & 1) * 512 +
+                                                      f.crow);
+  return make_uint2(v.x, v.y);
+}
+
+template <int U8, int X>
+__device__ __forceinline__ void fwd8_slot(char* smem, const Fwd8& f, int s, f32x16_t (&acc)[8], bf16x8_t (&b)[8],
+                                          bf16x8_t& a0, bf16x8_t& a1, bf16x8_t& n1, uint2& c, uint2& cn,
+                                          Nf4Table& T, Scale (&sc)[4], DqState& dq, TbState& tb, int fo0, int fo1) {
+  constexpr bool kOdd = (U8 & 1) != 0;
+  constexpr int kk = X >> 3, j = X & 7;
+  acc[j] = mfma32x32x16(kk ? a1 : a0, b[j], acc[j]);
+  if constexpr (kk == 0)
+    b[j] = rd16(smem + U8 * kOp + j * 2048 + fo1);
+  else
+    b[j] = rd16(smem + ((U8 + 1) & 7) * kOp + j * 2048 + fo0);
+  if constexpr (X == 0) cn = fwd8_codes(smem, f, s + 2);
+  // global loads
+  if constexpr (X == 1 || X == 3) fwd8_dma_x(smem, f, X >> 1, s + kR8Ahead, (U8 + kR8Ahead) & 7);
+  if constexpr (kOdd && X == 5) fwd8_dma_codes<((U8 + 7) >> 1) & 3>(smem, f, (s + 7) >> 1);
+  if constexpr (!kOdd && (X == 5 || X == 7)) {
+    constexpr int SL = ((U8 >> 1) + 3) & 3;
+    const int bk = min((s >> 1) + 3, f.nblk - 1);
+    if constexpr (X == 5)
+      sc[SL].q = f.aq[bk];
+    else
+      sc[SL].s2 = f.gs[(f.ablk0 + (uint32_t)bk) >> 8];
+  }
+  // VALU chunks
+  if constexpr (kOdd) {
+    constexpr int SL = ((U8 + 1) >> 1) & 3;
+    if constexpr (X < 6) tb_chunk<X>(tb, sc[SL], T);
+    else if constexpr (X < 11) dq_chunk<X - 6>(dq, c.y, T, n1);
+    else dq_chunk<X - 11>(dq, c.x, T, a0);
+  } else {
+    if constexpr (X < 5) dq_chunk<X>(dq, c.y, T, n1);
+    else if constexpr (X >= 8 && X < 13) dq_chunk<X - 8>(dq, c.x, T, a0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int U8>
+__device__ __forceinline__ void fwd8_substep(char* smem, const Fwd8& f, int s, f32x16_t (&acc)[8], bf16x8_t (&b)[8],
+                                             bf16x8_t& a0, bf16x8_t& a1, uint2& c, Nf4Table& T, Scale (&sc)[4],
+                                             int fo0, int fo1) {
+  __builtin_amdgcn_sched_barrier(0);
+  QLORA_WAIT(fwd8_vmcnt(U8), 15);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  bf16x8_t n1;
+  uint2 cn;
+  DqState dq;
+  TbState tb;
+#define QLORA_FWD8_SLOT(x) fwd8_slot<U8, x>(smem, f, s, acc, b, a0, a1, n1, c, cn, T, sc, dq, tb, fo0, fo1)
+#define QLORA_FWD8_SLOT4(x) QLORA_FWD8_SLOT(x); QLORA_FWD8_SLOT(x + 1); QLORA_FWD8_SLOT(x + 2); QLORA_FWD8_SLOT(x + 3)
+  QLORA_FWD8_SLOT4(0); QLORA_FWD8_SLOT4(4); QLORA_FWD8_SLOT4(8); QLORA_FWD8_SLOT4(12);
+#undef QLORA_FWD8_SLOT4
+#undef QLORA_FWD8_SLOT
+  a1 = n1;
+  c = cn;
+}
+
+// Token half of the LoRA tail with 512 threads: (s U)[m0 + row, j0 + 8 c ..].
+__device__ __forceinline__ void tail_tokens8(char* dst, const bf16_t* Ut, int64_t rows, int r, int64_t row0, int j0,
+                                             float s) {
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const int idx = threadIdx.x + kThreads8 * e;
+    const int row = idx >> 2, cc = idx & 3, col = j0 + 8 * cc;
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (col < r && row0 + row < rows) v = scale16(*reinterpret_cast<const uint4*>(Ut + (row0 + row) * r + col), s);
+    wr16(dst + spos(row, cc), v);
+  }
+}
+
+__global__ __launch_bounds__(kThreads8, 1) void nf4_fwd_r8_kernel(Nf4View W, const bf16_t* __restrict__ X, int64_t M,
+                                                                  const bf16_t* __restrict__ U,
+                                                                  const bf16_t* __restrict__ Bl, int r, float s,
+                                                                  bf16_t* __restrict__ Y, int tiles_n, int tiles_m) {
+  extern __shared__ __align__(16) char smem[];
+  int tn, tm;
+  map_tile(tiles_n, tiles_m, tn, tm);
+  const int64_t n0 = (int64_t)tn * kTile, m0 = (int64_t)tm * kTile;
+  const int t = threadIdx.x, lane = t & 63, lr = lane & 31, h = lane >> 5;
+  const int64_t N = W.N, K = W.K;
+
+  Fwd8 f;
+  f.w = __builtin_amdgcn_readfirstlane(t >> 6);
+  __builtin_assume(f.w >= 0 && f.w < 8);
+  f.nsub = (int)(K >> 5);
+  f.nblk = (int)(K >> 6);
+  f.xr = make_rsrc(X, (uint32_t)(M * K * 2));
+  f.cr = make_rsrc(W.codes, (uint32_t)(N * K / 2));
+  // token DMA: instruction q of wave w fills tile rows 16 (2w + q) .. +15,
+  // four lanes per row (lane j: row j >> 2, position j & 3 holding chunk
+  // dma_chunk(j))
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int row = 16 * (2 * f.w + q) + (lane >> 2);
+    const int64_t xm = min(m0 + row, M - 1);   // rows past the end re-read the last row: never stored
+    f.xo[q] = (uint32_t)(xm * K * 2 + dma_chunk(lane) * 16);
+  }
+  const int64_t own = min(n0 + 32 * f.w + lr, N - 1);
+  // code DMA: lane l brings stage half l >> 5 of row 32 w + (l & 31)
+  f.co = (uint32_t)(own * (K / 2) + 16 * h);
+  f.crow = f.w * 1024 + lr * 16 + 8 * h;
+  f.ablk0 = (uint32_t)(own * (K >> 6));
+  f.aq = W.absmax_q + f.ablk0;
+  f.gs = W.group_scale;
+  const int fo0 = spos(lr, 2 * h), fo1 = spos(lr, 2 * h + 1);
+
+  f32x16_t acc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[j][e] = 0.0f;
+
+  // prologue: code chunks 0..3, scales of blocks 0..2, token stages 0 .. kR8Ahead - 1
+  fwd8_dma_codes<0>(smem, f, 0);
+  fwd8_dma_codes<1>(smem, f, 1);
+  fwd8_dma_codes<2>(smem, f, 2);
+  fwd8_dma_codes<3>(smem, f, 3);
+  Scale sc[4];
+#pragma unroll
+  for (int bk = 0; bk < 3; ++bk) {
+    const int b2 = min(bk, f.nblk - 1);
+    sc[bk] = Scale{f.aq[b2], f.gs[(f.ablk0 + (uint32_t)b2) >> 8]};
+  }
+#pragma unroll
+  for (int st = 0; st < kR8Ahead; ++st)
+#pragma unroll
+    for (int q = 0; q < 2; ++q) fwd8_dma_x(smem, f, q, st, st);
+  QLORA_WAIT(0, 0);
+  __builtin_amdgcn_s_barrier();
+  Nf4Table T = make_table(block_scale(sc[0].q, sc[0].s2));
+  bf16x8_t a0, a1;
+  {
+    const uint2 c0 = fwd8_codes(smem, f, 0);
+    a0 = deq_frag(c0.x, T);
+    a1 = deq_frag(c0.y, T);
+  }
+  uint2 c = fwd8_codes(smem, f, 1);
+  bf16x8_t b[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) b[j] = rd16(smem + j * 2048 + fo0);
+  // K % 64 == 0, so the stage count is even
+  int st = 0;
+#define QLORA_FWD8_SUB(u) fwd8_substep<u>(smem, f, st + u, acc, b, a0, a1, c, T, sc, fo0, fo1)
+  for (; st + 8 <= f.nsub; st += 8) {
+    QLORA_FWD8_SUB(0); QLORA_FWD8_SUB(1); QLORA_FWD8_SUB(2); QLORA_FWD8_SUB(3);
+    QLORA_FWD8_SUB(4); QLORA_FWD8_SUB(5); QLORA_FWD8_SUB(6); QLORA_FWD8_SUB(7);
+  }
+  const int rem = f.nsub - st;
+  if (rem >= 2) { QLORA_FWD8_SUB(0); QLORA_FWD8_SUB(1); }
+  if (rem >= 4) { QLORA_FWD8_SUB(2); QLORA_FWD8_SUB(3); }
+  if (rem >= 6) { QLORA_FWD8_SUB(4); QLORA_FWD8_SUB(5); }
+#undef QLORA_FWD8_SUB
+  // drain the DMAs and reads still in flight (clamped re-loads) before reusing the ring
+  QLORA_WAIT(0, 0);
+  __builtin_amdgcn_s_barrier();
+
+  if (r > 0) {
+    // LoRA up-projection: acc += B (s U)^T over the rank, 32 at a time; the
+    // weight operand comes straight from B (row of the lane, ranks 16h + 8kk)
+    for (int j0 = 0; j0 < r; j0 += 32) {
+      tail_tokens8(smem, U, M, r, m0, j0, s);
+      bf16x8_t a[2];
+      const int64_t n = n0 + 32 * f.w + lr;
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const int col = j0 + 16 * h + 8 * kk;
+        uint4 v = make_uint4(0u, 0u, 0u, 0u);
+        if (col < r && n < N) v = *reinterpret_cast<const uint4*>(Bl + n * r + col);
+        a[kk] = __builtin_bit_cast(bf16x8_t, v);
+      }
+      QLORA_WAIT(0, 0);
+      __builtin_amdgcn_s_barrier();
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[j] = mfma32x32x16(a[kk], rd16(smem + j * 2048 + (kk ? fo1 : fo0)), acc[j]);
+      QLORA_WAIT(0, 0);
+      __builtin_amdgcn_s_barrier();
+    }
+  }
+  // Output: lane (lr, h) of wave w holds token m0 + 32 j + lr and weight
+  // columns n0 + 32 w + 8 q + 4 h + 0..3.
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int64_t row = m0 + 32 * j + lr;
+    if (row >= M) continue;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int64_t col = n0 + 32 * f.w + 8 * q + 4 * h;
+      if (col < N)  // N % 8 == 0: the four columns are all in range
+        *reinterpret_cast<uint2*>(Y + row * N + col) = make_uint2(pack_bf16x2(acc[j][4 * q], acc[j][4 * q + 1]),
+                                                                  pack_bf16x2(acc[j][4 * q + 2], acc[j][4 * q + 3]));
+    }
+  }
+}
+
+// ===========================================================================
 // Backward: dX = dY deq(W) + s G A.  Output tile 256 (m) x 256 (k); the
 // contraction runs over n.  Weight half of a stage = 32 rows n x 256
 // columns k, rows of 512 bytes with 32-byte block b of row n at position
@@ -1158,17 +1424,23 @@ hipError_t launch_fwd(const Nf4View& W, const bf16_t* X, int64_t M, const bf16_t
                       float s, bf16_t* Y, hipStream_t st) {
   const int tiles_n = (int)((W.N + kTile - 1) / kTile);
   const int tiles_m = (int)((M + kTile - 1) / kTile);
-#ifdef QLORA_FWD_LDS_WEIGHTS
+#if defined(QLORA_FWD_LDS_WEIGHTS)
   auto* fn = &nf4_fwd_kernel;
   const size_t lds = kLdsFwd;
-#else
+  const int threads = kThreads;
+#elif defined(QLORA_FWD_FOUR_WAVES)
   auto* fn = &nf4_fwd_r_kernel;
   const size_t lds = kLdsFwdR;
+  const int threads = kThreads;
+#else
+  auto* fn = &nf4_fwd_r8_kernel;
+  const size_t lds = kLdsFwdR;
+  const int threads = kThreads8;
 #endif
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
                                      (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(fn, dim3(tiles_n * tiles_m), dim3(kThreads), lds, st, W, X, M, U, B, r, s, Y, tiles_n, tiles_m);
+  hipLaunchKernelGGL(fn, dim3(tiles_n * tiles_m), dim3(threads), lds, st, W, X, M, U, B, r, s, Y, tiles_n, tiles_m);
   return hipGetLastError();
 }
 
