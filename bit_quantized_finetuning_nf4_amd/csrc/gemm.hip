@@ -333,7 +333,7 @@ static SkinnyShape skinny_shape(int64_t rows, int64_t cols, int64_t contraction,
   sh.tiles_c = (int)((cols + BC - 1) / BC);
   sh.total_steps = (int)((contraction + 63) / 64);
   const int tiles = sh.tiles_r * sh.tiles_c;
-  int want = (1024 + tiles - 1) / tiles;
+  int want = (512 + tiles - 1) / tiles;   // about two workgroups per CU: fewer partial sums to write and re-read
   const int max_splits = sh.total_steps / 4 > 0 ? sh.total_steps / 4 : 1;
   if (want > max_splits) want = max_splits;
   if (want < 1) want = 1;

@@ -831,7 +831,10 @@ __global__ __launch_bounds__(kThreads, 1) void nf4_fwd_r_kernel(Nf4View W, const
 }
 
 // ===========================================================================
-// Forward with eight waves (two per SIMD).  The tile is still 256 weight
+// Forward with eight waves (two per SIMD), built with QLORA_FWD_EIGHT_WAVES.
+// It takes 9 % fewer cycles per stage than the four-wave kernel but draws
+// more power (twice the LDS reads), and under sustained load its clock
+// settles about 10 % lower, so it is not the default.  The tile is still 256 weight
 // rows x 256 tokens, but wave w owns only weight rows n0 + 32 w .. +31 (one
 // A fragment) against all 256 tokens: 8 accumulator tiles (128 registers),
 // so two waves share each SIMD.  A wave issues one instruction per cycle
@@ -1428,14 +1431,14 @@ hipError_t launch_fwd(const Nf4View& W, const bf16_t* X, int64_t M, const bf16_t
   auto* fn = &nf4_fwd_kernel;
   const size_t lds = kLdsFwd;
   const int threads = kThreads;
-#elif defined(QLORA_FWD_FOUR_WAVES)
-  auto* fn = &nf4_fwd_r_kernel;
-  const size_t lds = kLdsFwdR;
-  const int threads = kThreads;
-#else
+#elif defined(QLORA_FWD_EIGHT_WAVES)
   auto* fn = &nf4_fwd_r8_kernel;
   const size_t lds = kLdsFwdR;
   const int threads = kThreads8;
+#else
+  auto* fn = &nf4_fwd_r_kernel;
+  const size_t lds = kLdsFwdR;
+  const int threads = kThreads;
 #endif
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
                                      (int)lds);
