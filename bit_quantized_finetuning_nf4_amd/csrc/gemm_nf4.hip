@@ -120,7 +120,8 @@ __device__ __forceinline__ void schedule_half() {
 // Tile order: consecutive workgroups share the token tile (the column-side
 // tiles vary fastest); the eight XCDs receive contiguous ranges.
 __device__ __forceinline__ void map_tile(int tiles_c, int tiles_r, int& tc, int& tr) {
-  const int nwg = tiles_c * tiles_r;
+  (void)tiles_r;
+  const int nwg = (int)gridDim.x;   // the launch may cover only the first tiles of the grid
   int id = blockIdx.x;
   if ((nwg & 7) == 0) id = (id & 7) * (nwg >> 3) + (id >> 3);
   tc = id % tiles_c;
@@ -859,27 +860,28 @@ __global__ __launch_bounds__(kThreads, 1) void nf4_fwd_r_kernel(Nf4View W, const
 #ifndef QLORA_FWD8_AHEAD
 #define QLORA_FWD8_AHEAD 6
 #endif
-constexpr int kThreads8 = 512;
 constexpr int kR8Ahead = QLORA_FWD8_AHEAD;
 static_assert(kR8Ahead >= 2 && kR8Ahead <= 6, "ring / code-chunk schedule");
-// Loads of substep v, token DMAs first: 2 token DMAs, then 1 code DMA (odd
-// v) or 2 scale loads (even v).
+// Loads of substep v, token DMAs first: 16 / WAVES token DMAs per wave, then
+// 1 code DMA (odd v) or 2 scale loads (even v).
 constexpr int fwd8_tail(int v) { return (v & 1) ? 1 : 2; }
-constexpr int fwd8_loads(int v) { return 2 + fwd8_tail(v); }
+template <int WAVES>
+constexpr int fwd8_loads(int v) { return 16 / WAVES + fwd8_tail(v); }
 // vmcnt at the start of substep u: every load of substep u + 1 - kR8Ahead
 // has landed once only the loads of the later substeps may be in flight.
 // That covers token stage u+1 and the code chunk c DMA'd at substep 2c - 7,
 // which substep 2c - 2 reads first.
+template <int WAVES>
 constexpr int fwd8_vmcnt(int u) {
   int n = 0;
-  for (int v = u + 2 - kR8Ahead; v <= u - 1; ++v) n += fwd8_loads(v);
+  for (int v = u + 2 - kR8Ahead; v <= u - 1; ++v) n += fwd8_loads<WAVES>(v);
   return n;
 }
-static_assert(fwd8_vmcnt(0) < 64 && fwd8_vmcnt(1) < 64, "vmcnt field");
+static_assert(fwd8_vmcnt<4>(0) < 64 && fwd8_vmcnt<4>(1) < 64, "vmcnt field");
 
 struct Fwd8 {
   rsrc_t xr, cr;
-  uint32_t xo[2];         // lane offsets of the wave's two token DMA instructions
+  uint32_t xo[4];         // lane offsets of the wave's token DMA instructions (16 / WAVES of them)
   uint32_t co;            // lane offset of the wave's code DMA (row 32 w + (lane & 31), stage half lane >> 5)
   const uint8_t* aq;      // absmax codes of the lane's row (block 0)
   const float* gs;
@@ -888,9 +890,11 @@ struct Fwd8 {
   int crow;               // byte offset of the lane's 8 code bytes in a chunk buffer (stage half 0)
 };
 
+// Token DMA instruction q of wave w fills tile rows 16 ((16 / WAVES) w + q) .. +15.
+template <int WAVES>
 __device__ __forceinline__ void fwd8_dma_x(char* smem, const Fwd8& f, int q, int stage, int slot) {
   const uint32_t soff = (uint32_t)min(stage, f.nsub - 1) * 64u;
-  dma16(f.xr, smem + slot * kOp + (2 * f.w + q) * 1024, f.xo[q], soff);
+  dma16(f.xr, smem + slot * kOp + ((16 / WAVES) * f.w + q) * 1024, f.xo[q], soff);
 }
 template <int BUF>
 __device__ __forceinline__ void fwd8_dma_codes(char* smem, const Fwd8& f, int chunk) {
@@ -903,7 +907,7 @@ __device__ __forceinline__ uint2 fwd8_codes(const char* smem, const Fwd8& f, int
   return make_uint2(v.x, v.y);
 }
 
-template <int U8, int X>
+template <int WAVES, int U8, int X>
 __device__ __forceinline__ void fwd8_slot(char* smem, const Fwd8& f, int s, f32x16_t (&acc)[8], bf16x8_t (&b)[8],
                                           bf16x8_t& a0, bf16x8_t& a1, bf16x8_t& n1, uint2& c, uint2& cn,
                                           Nf4Table& T, Scale (&sc)[4], DqState& dq, TbState& tb, int fo0, int fo1) {
@@ -916,7 +920,7 @@ __device__ __forceinline__ void fwd8_slot(char* smem, const Fwd8& f, int s, f32x
     b[j] = rd16(smem + ((U8 + 1) & 7) * kOp + j * 2048 + fo0);
   if constexpr (X == 0) cn = fwd8_codes(smem, f, s + 2);
   // global loads
-  if constexpr (X == 1 || X == 3) fwd8_dma_x(smem, f, X >> 1, s + kR8Ahead, (U8 + kR8Ahead) & 7);
+  if constexpr (X >= 1 && X <= 16 / WAVES) fwd8_dma_x<WAVES>(smem, f, X - 1, s + kR8Ahead, (U8 + kR8Ahead) & 7);
   if constexpr (kOdd && X == 5) fwd8_dma_codes<((U8 + 7) >> 1) & 3>(smem, f, (s + 7) >> 1);
   if constexpr (!kOdd && (X == 5 || X == 7)) {
     constexpr int SL = ((U8 >> 1) + 3) & 3;
@@ -939,19 +943,19 @@ __device__ __forceinline__ void fwd8_slot(char* smem, const Fwd8& f, int s, f32x
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int U8>
+template <int WAVES, int U8>
 __device__ __forceinline__ void fwd8_substep(char* smem, const Fwd8& f, int s, f32x16_t (&acc)[8], bf16x8_t (&b)[8],
                                              bf16x8_t& a0, bf16x8_t& a1, uint2& c, Nf4Table& T, Scale (&sc)[4],
                                              int fo0, int fo1) {
   __builtin_amdgcn_sched_barrier(0);
-  QLORA_WAIT(fwd8_vmcnt(U8), 15);
+  QLORA_WAIT(fwd8_vmcnt<WAVES>(U8), 15);
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
   bf16x8_t n1;
   uint2 cn;
   DqState dq;
   TbState tb;
-#define QLORA_FWD8_SLOT(x) fwd8_slot<U8, x>(smem, f, s, acc, b, a0, a1, n1, c, cn, T, sc, dq, tb, fo0, fo1)
+#define QLORA_FWD8_SLOT(x) fwd8_slot<WAVES, U8, x>(smem, f, s, acc, b, a0, a1, n1, c, cn, T, sc, dq, tb, fo0, fo1)
 #define QLORA_FWD8_SLOT4(x) QLORA_FWD8_SLOT(x); QLORA_FWD8_SLOT(x + 1); QLORA_FWD8_SLOT(x + 2); QLORA_FWD8_SLOT(x + 3)
   QLORA_FWD8_SLOT4(0); QLORA_FWD8_SLOT4(4); QLORA_FWD8_SLOT4(8); QLORA_FWD8_SLOT4(12);
 #undef QLORA_FWD8_SLOT4
@@ -960,12 +964,13 @@ __device__ __forceinline__ void fwd8_substep(char* smem, const Fwd8& f, int s, f
   c = cn;
 }
 
-// Token half of the LoRA tail with 512 threads: (s U)[m0 + row, j0 + 8 c ..].
+// Token half of the LoRA tail with THREADS threads: (s U)[m0 + row, j0 + 8 c ..].
+template <int THREADS>
 __device__ __forceinline__ void tail_tokens8(char* dst, const bf16_t* Ut, int64_t rows, int r, int64_t row0, int j0,
                                              float s) {
 #pragma unroll
-  for (int e = 0; e < 2; ++e) {
-    const int idx = threadIdx.x + kThreads8 * e;
+  for (int e = 0; e < 1024 / THREADS; ++e) {
+    const int idx = threadIdx.x + THREADS * e;
     const int row = idx >> 2, cc = idx & 3, col = j0 + 8 * cc;
     uint4 v = make_uint4(0u, 0u, 0u, 0u);
     if (col < r && row0 + row < rows) v = scale16(*reinterpret_cast<const uint4*>(Ut + (row0 + row) * r + col), s);
@@ -973,30 +978,46 @@ __device__ __forceinline__ void tail_tokens8(char* dst, const bf16_t* Ut, int64_
   }
 }
 
-__global__ __launch_bounds__(kThreads8, 1) void nf4_fwd_r8_kernel(Nf4View W, const bf16_t* __restrict__ X, int64_t M,
-                                                                  const bf16_t* __restrict__ U,
-                                                                  const bf16_t* __restrict__ Bl, int r, float s,
-                                                                  bf16_t* __restrict__ Y, int tiles_n, int tiles_m) {
+// WAVES waves own 32 WAVES weight rows of a 256-token tile.  TAIL_BASE < 0:
+// the tiles are those of a grid of 32 WAVES-row tiles (map_tile).  Otherwise
+// (WAVES == 4) workgroup b takes half b & 1 (128 rows) of 256-row tile
+// tail_base + b / 2 in the row-major order of a tiles_n x tiles_m grid of
+// 256 x 256 tiles: the split last round of a launch whose tile count is not
+// a multiple of the CU count.
+template <int WAVES>
+__global__ __launch_bounds__(64 * WAVES, 1) void nf4_fwd_n32_kernel(Nf4View W, const bf16_t* __restrict__ X,
+                                                                    int64_t M, const bf16_t* __restrict__ U,
+                                                                    const bf16_t* __restrict__ Bl, int r, float s,
+                                                                    bf16_t* __restrict__ Y, int tiles_n, int tiles_m,
+                                                                    int tail_base) {
   extern __shared__ __align__(16) char smem[];
-  int tn, tm;
-  map_tile(tiles_n, tiles_m, tn, tm);
-  const int64_t n0 = (int64_t)tn * kTile, m0 = (int64_t)tm * kTile;
+  int64_t n0, m0;
+  if (tail_base < 0) {
+    int tn, tm;
+    map_tile(tiles_n, tiles_m, tn, tm);
+    n0 = (int64_t)tn * 32 * WAVES;
+    m0 = (int64_t)tm * kTile;
+  } else {
+    const int p = tail_base + (int)(blockIdx.x >> 1);
+    n0 = (int64_t)(p % tiles_n) * kTile + 128 * (blockIdx.x & 1);
+    m0 = (int64_t)(p / tiles_n) * kTile;
+  }
   const int t = threadIdx.x, lane = t & 63, lr = lane & 31, h = lane >> 5;
   const int64_t N = W.N, K = W.K;
 
   Fwd8 f;
   f.w = __builtin_amdgcn_readfirstlane(t >> 6);
-  __builtin_assume(f.w >= 0 && f.w < 8);
+  __builtin_assume(f.w >= 0 && f.w < WAVES);
   f.nsub = (int)(K >> 5);
   f.nblk = (int)(K >> 6);
   f.xr = make_rsrc(X, (uint32_t)(M * K * 2));
   f.cr = make_rsrc(W.codes, (uint32_t)(N * K / 2));
-  // token DMA: instruction q of wave w fills tile rows 16 (2w + q) .. +15,
-  // four lanes per row (lane j: row j >> 2, position j & 3 holding chunk
-  // dma_chunk(j))
+  // token DMA: instruction q of wave w fills tile rows 16 ((16 / WAVES) w +
+  // q) .. +15, four lanes per row (lane j: row j >> 2, position j & 3
+  // holding chunk dma_chunk(j))
 #pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int row = 16 * (2 * f.w + q) + (lane >> 2);
+  for (int q = 0; q < 16 / WAVES; ++q) {
+    const int row = 16 * ((16 / WAVES) * f.w + q) + (lane >> 2);
     const int64_t xm = min(m0 + row, M - 1);   // rows past the end re-read the last row: never stored
     f.xo[q] = (uint32_t)(xm * K * 2 + dma_chunk(lane) * 16);
   }
@@ -1029,7 +1050,7 @@ __global__ __launch_bounds__(kThreads8, 1) void nf4_fwd_r8_kernel(Nf4View W, con
 #pragma unroll
   for (int st = 0; st < kR8Ahead; ++st)
 #pragma unroll
-    for (int q = 0; q < 2; ++q) fwd8_dma_x(smem, f, q, st, st);
+    for (int q = 0; q < 16 / WAVES; ++q) fwd8_dma_x<WAVES>(smem, f, q, st, st);
   QLORA_WAIT(0, 0);
   __builtin_amdgcn_s_barrier();
   Nf4Table T = make_table(block_scale(sc[0].q, sc[0].s2));
@@ -1045,7 +1066,7 @@ __global__ __launch_bounds__(kThreads8, 1) void nf4_fwd_r8_kernel(Nf4View W, con
   for (int j = 0; j < 8; ++j) b[j] = rd16(smem + j * 2048 + fo0);
   // K % 64 == 0, so the stage count is even
   int st = 0;
-#define QLORA_FWD8_SUB(u) fwd8_substep<u>(smem, f, st + u, acc, b, a0, a1, c, T, sc, fo0, fo1)
+#define QLORA_FWD8_SUB(u) fwd8_substep<WAVES, u>(smem, f, st + u, acc, b, a0, a1, c, T, sc, fo0, fo1)
   for (; st + 8 <= f.nsub; st += 8) {
     QLORA_FWD8_SUB(0); QLORA_FWD8_SUB(1); QLORA_FWD8_SUB(2); QLORA_FWD8_SUB(3);
     QLORA_FWD8_SUB(4); QLORA_FWD8_SUB(5); QLORA_FWD8_SUB(6); QLORA_FWD8_SUB(7);
@@ -1063,7 +1084,7 @@ __global__ __launch_bounds__(kThreads8, 1) void nf4_fwd_r8_kernel(Nf4View W, con
     // LoRA up-projection: acc += B (s U)^T over the rank, 32 at a time; the
     // weight operand comes straight from B (row of the lane, ranks 16h + 8kk)
     for (int j0 = 0; j0 < r; j0 += 32) {
-      tail_tokens8(smem, U, M, r, m0, j0, s);
+      tail_tokens8<64 * WAVES>(smem, U, M, r, m0, j0, s);
       bf16x8_t a[2];
       const int64_t n = n0 + 32 * f.w + lr;
 #pragma unroll
@@ -1423,28 +1444,57 @@ __global__ __launch_bounds__(kThreads, 1) void nf4_dx_kernel(Nf4View W, const bf
 
 }  // namespace
 
+// CUs of the current device (the tail split below needs the round size).
+static int gemm_cus() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 256;
+  return cus > 0 ? cus : 256;
+}
+
 hipError_t launch_fwd(const Nf4View& W, const bf16_t* X, int64_t M, const bf16_t* U, const bf16_t* B, int r,
                       float s, bf16_t* Y, hipStream_t st) {
   const int tiles_n = (int)((W.N + kTile - 1) / kTile);
   const int tiles_m = (int)((M + kTile - 1) / kTile);
+  const int tiles = tiles_n * tiles_m;
+#if defined(QLORA_FWD_LDS_WEIGHTS) || defined(QLORA_FWD_EIGHT_WAVES)
 #if defined(QLORA_FWD_LDS_WEIGHTS)
   auto* fn = &nf4_fwd_kernel;
   const size_t lds = kLdsFwd;
-  const int threads = kThreads;
-#elif defined(QLORA_FWD_EIGHT_WAVES)
-  auto* fn = &nf4_fwd_r8_kernel;
-  const size_t lds = kLdsFwdR;
-  const int threads = kThreads8;
-#else
-  auto* fn = &nf4_fwd_r_kernel;
-  const size_t lds = kLdsFwdR;
-  const int threads = kThreads;
-#endif
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
                                      (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(fn, dim3(tiles_n * tiles_m), dim3(threads), lds, st, W, X, M, U, B, r, s, Y, tiles_n, tiles_m);
+  hipLaunchKernelGGL(fn, dim3(tiles), dim3(kThreads), lds, st, W, X, M, U, B, r, s, Y, tiles_n, tiles_m);
+#else
+  auto* fn = &nf4_fwd_n32_kernel<8>;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     (int)kLdsFwdR);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(fn, dim3(tiles), dim3(512), kLdsFwdR, st, W, X, M, U, B, r, s, Y, tiles_n, tiles_m, -1);
+#endif
   return hipGetLastError();
+#else
+  // When the last round of 256 x 256 tiles would leave at least half the CUs
+  // idle, its tiles run as two 128-row halves each, in a second launch of
+  // the 32-rows-per-wave kernel, so that round takes about half as long.
+  const int cus = gemm_cus();
+  const int rest = tiles % cus;
+  const int main_tiles = (tiles > cus && rest > 0 && 2 * rest <= cus) ? tiles - rest : tiles;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&nf4_fwd_r_kernel),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsFwdR);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(nf4_fwd_r_kernel, dim3(main_tiles), dim3(kThreads), kLdsFwdR, st, W, X, M, U, B, r, s, Y,
+                     tiles_n, tiles_m);
+  e = hipGetLastError();
+  if (e != hipSuccess || main_tiles == tiles) return e;
+  auto* tail = &nf4_fwd_n32_kernel<4>;
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(tail), hipFuncAttributeMaxDynamicSharedMemorySize,
+                          (int)kLdsFwdR);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(tail, dim3(2 * (tiles - main_tiles)), dim3(kThreads), kLdsFwdR, st, W, X, M, U, B, r, s, Y,
+                     tiles_n, tiles_m, main_tiles);
+  return hipGetLastError();
+#endif
 }
 
 hipError_t launch_dx(const Nf4View& W, const bf16_t* dY, int64_t M, const bf16_t* G, const bf16_t* A, int r,

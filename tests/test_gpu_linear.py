@@ -78,6 +78,7 @@ def test_small_config():
     (1, 512, 512, 64),         # one token
     (513, 264, 320, 128),      # largest rank
     (64, 8, 64, 8),            # minimum N / K / r
+    (4300, 4104, 128, 16),     # 17 x 17 tiles: on 256 CUs the 33-tile last forward round runs as 128-row halves
 ])
 def test_shapes(M, N, K, r):
     _run(_case(M, N, K, r, seed=M + N + K + r), f"M{M} N{N} K{K} r{r}")
