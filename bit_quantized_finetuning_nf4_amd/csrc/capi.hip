@@ -321,6 +321,8 @@ qlora_status qlora_lora_grads(const uint16_t* X, const uint16_t* dY, const uint1
   qlora_status st = check_adapter_rank(r);
   if (st != QLORA_OK) return st;
   if (M <= 0 || M > 0x7FFFFFFF || N <= 0 || N % 8 != 0 || K <= 0 || K % 8 != 0) return QLORA_E_SHAPE;
+  // X and dY are addressed with 32-bit byte offsets
+  if (M > (int64_t)0x7FFFFFFF / K || M > (int64_t)0x7FFFFFFF / N) return QLORA_E_UNSUPPORTED;
   if (!X || !dY || !U || !G || !dA || !dB) return QLORA_E_NULL;
   if (!aligned16(X) || !aligned16(dY) || !aligned16(U) || !aligned16(G) || !aligned16(dA) || !aligned16(dB))
     return QLORA_E_ALIGN;

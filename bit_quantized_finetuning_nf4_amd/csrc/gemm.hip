@@ -1,6 +1,7 @@
-// gemm.hip -- LDS-tiled bf16 MFMA products of the QLoRA linear layer.
+// gemm.hip -- the four LoRA products of the QLoRA linear layer:
 //
-//   U = X A^T,  G = dY B,  dA = s (dY B)^T X,  dB = s dY^T (X A^T)
+//   U = X A^T,  G = dY B            (contraction along the rows of X / dY)
+//   dA = s G^T X,  dB = s dY^T U    (contraction over the tokens)
 // (the fused NF4 GEMMs live in gemm_nf4.hip)
 //
 // deepfa.ir blog, "LoRA: Prerequisite" and "QLoRA's Working Process" (the
@@ -8,284 +9,281 @@
 // backward passes, only the adapters are trained); glossary "QLoRA",
 // Definition (weight gradients only for the LoRA matrices).
 //
-// Engine: 256 threads (4 waves of 64), v_mfma_f32_32x32x16_bf16, fp32
-// accumulation.  The MFMA "A" operand is the output-column side (W rows,
-// LoRA ranks, ...) and the "B" operand the output-row side (tokens), so each
-// lane ends with four consecutive output columns of one row.  Both operands
-// are staged in LDS as rows of 64 contraction elements (see lds_chunk_off),
-// double buffered: the global loads of step s+1 are issued before the MFMAs
-// of step s and written to LDS (dequantizing on the way) after them.
+// All four read one large bf16 matrix (X or dY, M x K or M x N) once and a
+// small one (A, B, G or U) with the rank r <= 128 on one side, so they are
+// HBM streams with little arithmetic.  Both kernels below bring the large
+// matrix into LDS by buffer->LDS DMA through a ring of six 32-row (or
+// 32-column) stages, five stages ahead, one barrier per stage, and run a few
+// bf16 MFMAs (32x32x16, fp32 accumulation) per stage.  The contraction is
+// split over workgroups (about one per CU); each split writes fp32 partial
+// sums and reduce_kernel adds them in a fixed order, so results do not
+// depend on timing.  The rank side is padded to RP = 64 or 128 with values
+// that only reach output columns >= r, which are never stored.
 #include "device.h"
 #include "kernels.h"
+#include "lds.h"
 
 namespace qlora {
 
+namespace {
+
 constexpr int kThreads = 256;
+constexpr int kRing = 6;    // stages in the LDS ring
+constexpr int kAhead = 5;   // stages DMA'd ahead of the one being multiplied
 
-// A bf16 matrix seen by a tile producer: src[i * ld + j], i < rows, j < cols.
-struct TileDesc {
-  const bf16_t* src;
-  int64_t ld, rows, cols;
-};
-
-__device__ __forceinline__ uint4 zero4() { return make_uint4(0u, 0u, 0u, 0u); }
-
-__device__ __forceinline__ uint32_t scale_pair(uint32_t w, float s) {
-  return pack_bf16x2(bf2f(w & 0xFFFFu) * s, bf2f(w >> 16) * s);
+// Transposed-read fragment of a tile whose rows (32 per stage, 2 k16 steps)
+// are the contraction and whose columns are an MFMA operand's rows: row
+// pitch PB bytes, 32-byte column block b of row n stored at b ^ (n & 3).
+// Lane (g = lane >> 4, sl = lane & 15) reads row 8 (g >> 1) + (sl >> 2),
+// columns 32 f + 16 (g & 1) + 4 (sl & 3) .. +3; a second read 4 rows down
+// completes the lane's 8 contraction elements.
+template <int PB>
+__device__ __forceinline__ int tr_off(int f) {
+  const int lane = threadIdx.x & 63, g = lane >> 4, sl = lane & 15, n0 = 8 * (g >> 1) + (sl >> 2);
+  return n0 * PB + 32 * ((2 * f + (g & 1)) ^ (n0 & 3)) + 8 * (sl & 3);
+}
+template <int PB>
+__device__ __forceinline__ bf16x8_t tr_frag(const char* p) {
+  const uint2 lo = rd_tr(p), hi = rd_tr(p + 4 * PB);
+  return __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
+}
+// DMA of a 32-row x (PB / 2)-column tile in the layout above: instruction q
+// covers rows (512 / PB) q .. ; lane l writes byte 16 (l mod (PB / 16)) of
+// its row, which holds global column 8 (2 ((p >> 1) ^ (row & 3)) + (p & 1))
+// for p = l mod (PB / 16).
+template <int PB>
+__device__ __forceinline__ void tr_dma_coords(int q, int lane, int& row, int& col) {
+  constexpr int kLanesPerRow = PB / 16;
+  row = (64 / kLanesPerRow) * q + lane / kLanesPerRow;
+  const int p = lane % kLanesPerRow;
+  col = 8 * (2 * ((p >> 1) ^ (row & 3)) + (p & 1));
 }
 
 // ---------------------------------------------------------------------------
-// Tile producers.  Each fills one LDS tile of BR rows x 64 contraction
-// elements for contraction step `step` (elements [64 step, 64 step + 64)).
+// Row contraction: out[m][j] = sum_c P[m][c] Q(c, j), 128 rows m per
+// workgroup (wave w: rows 32 w .. +31, the MFMA B operand), all RP ranks j
+// (the A operand), stages of 32 c.  P rows are DMA'd as 64-byte rows
+// (16-byte chunk c of row m at c ^ ((m >> 2) & 3)).  Q is A [r x C] (QT =
+// false: rows j, read like P) or B [C x r] (QT = true: rows c, read
+// transposed).  Output D[j][m]: a lane holds four consecutive j of one m.
 // ---------------------------------------------------------------------------
-
-// Source rows are contiguous along the contraction: src[row * ld + c].
-// cols (the contraction extent) must be a multiple of 8.
-template <int BR>
-struct RowTile {
-  static constexpr int kPer = BR * 8 / kThreads;
-  static_assert(kPer >= 1, "tile too small");
-  const bf16_t* src;
-  int64_t ld, rows, cols, row0;
-  uint4 v[kPer];
-  __device__ __forceinline__ RowTile(const TileDesc& d, int64_t origin)
-      : src(d.src), ld(d.ld), rows(d.rows), cols(d.cols), row0(origin) {}
-
-  __device__ __forceinline__ void load(int step) {
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int idx = threadIdx.x + i * kThreads;
-      const int r = idx >> 3, ch = idx & 7;
-      const int64_t gr = row0 + r, gc = (int64_t)step * 64 + ch * 8;
-      v[i] = (gr < rows && gc < cols) ? *reinterpret_cast<const uint4*>(src + gr * ld + gc) : zero4();
-    }
-  }
-  __device__ __forceinline__ void store(bf16_t* lds) const {
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int idx = threadIdx.x + i * kThreads;
-      *reinterpret_cast<uint4*>(lds + lds_chunk_off(idx >> 3, idx & 7)) = v[i];
-    }
-  }
-  // store s * v, rounded back to bf16
-  __device__ __forceinline__ void store_scaled(bf16_t* lds, float s) const {
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int idx = threadIdx.x + i * kThreads;
-      const uint4 w = make_uint4(scale_pair(v[i].x, s), scale_pair(v[i].y, s), scale_pair(v[i].z, s),
-                                 scale_pair(v[i].w, s));
-      *reinterpret_cast<uint4*>(lds + lds_chunk_off(idx >> 3, idx & 7)) = w;
-    }
-  }
+template <int RP, bool QT>
+struct RowShape {
+  static constexpr int kP = 128 * 64;                      // 8 KiB of P per stage
+  static constexpr int kQ = RP * 64;                       // Q per stage (RP rows x 64 B, or 32 rows x 2 RP B)
+  static constexpr int kStage = kP + kQ;
+  static constexpr int kQDma = kQ / 1024 / 4;              // Q DMA instructions per wave per stage
+  static constexpr int kLoads = 2 + kQDma;                 // all DMA instructions per wave per stage
 };
 
-// Source is contraction-major: src[c * ld + x]; the tile holds rows x in
-// [x0, x0 + BX), so it is a transpose.  A task is a pair of contraction rows
-// (2p, 2p+1) times 8 consecutive x; its two 16-byte loads become eight
-// dwords {src[2p][x], src[2p+1][x]}.  Tasks are laid out in 8x8 squares
-// (8 row pairs x 8 x-groups per wave) so a wave reads whole 128-byte lines.
-// xcols must be a multiple of 8.
-template <int BX>
-struct TransTile {
-  static constexpr int kTasks = 4 * BX;
-  static constexpr int kPer = (kTasks + kThreads - 1) / kThreads;
-  const bf16_t* src;
-  int64_t ld, crows, xcols, x0;
-  uint4 v0[kPer], v1[kPer];
-  // d.rows is the contraction extent, d.cols the x extent
-  __device__ __forceinline__ TransTile(const TileDesc& d, int64_t origin)
-      : src(d.src), ld(d.ld), crows(d.rows), xcols(d.cols), x0(origin) {}
-
-  __device__ __forceinline__ static void coords(int t, int& p, int& g) {
-    const int sq = t >> 6;
-    p = ((sq & 3) << 3) | (t & 7);
-    g = ((sq >> 2) << 3) | ((t >> 3) & 7);
-  }
-  __device__ __forceinline__ void load(int step) {
+template <int RP, bool QT>
+__global__ __launch_bounds__(kThreads, 1) void rskinny_kernel(const bf16_t* __restrict__ P, int64_t M, int64_t C,
+                                                              const bf16_t* __restrict__ Q, int r,
+                                                              int stages_per_split, int tiles_m,
+                                                              float* __restrict__ part) {
+  using S = RowShape<RP, QT>;
+  extern __shared__ __align__(16) char smem[];
+  const int tm = blockIdx.x % tiles_m, sp = blockIdx.x / tiles_m;
+  const int t = threadIdx.x, w = t >> 6, lane = t & 63, lr = lane & 31, h = lane >> 5;
+  const int64_t m0 = (int64_t)tm * 128;
+  const int nst = (int)((C + 31) / 32);
+  const int s0 = sp * stages_per_split, s1 = min(nst, s0 + stages_per_split);
+  // P rows of this tile only (rows past M read as zero); Q whole
+  const rsrc_t pr = make_rsrc(P + m0 * C, (uint32_t)(min((int64_t)128, M - m0) * C * 2));
+  const rsrc_t qr = make_rsrc(Q, (uint32_t)((int64_t)r * C * 2));
+  uint32_t po[2], qo[S::kQDma > 0 ? S::kQDma : 1];
+  int pl[2], ql[S::kQDma > 0 ? S::kQDma : 1];
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int t = threadIdx.x + i * kThreads;
-      v0[i] = zero4();
-      v1[i] = zero4();
-      if (kTasks % kThreads == 0 || t < kTasks) {
-        int p, g;
-        coords(t, p, g);
-        const int64_t c = (int64_t)step * 64 + 2 * p, x = x0 + 8 * g;
-        if (x < xcols) {
-          if (c < crows) v0[i] = *reinterpret_cast<const uint4*>(src + c * ld + x);
-          if (c + 1 < crows) v1[i] = *reinterpret_cast<const uint4*>(src + (c + 1) * ld + x);
+  for (int q = 0; q < 2; ++q) {   // P: instruction q of wave w fills rows 16 (2w + q) .. +15
+    const int row = 16 * (2 * w + q) + (lane >> 2), ch = (lane & 3) ^ ((lane >> 4) & 3);
+    po[q] = (uint32_t)(row * C * 2 + ch * 16);
+    pl[q] = 16 * (2 * w + q) * 64;
+  }
+#pragma unroll
+  for (int q = 0; q < S::kQDma; ++q) {
+    const int gi = S::kQDma * w + q;   // 1 KiB piece of the stage's Q tile
+    if constexpr (!QT) {               // rows j of A, 64 bytes per stage
+      const int row = 16 * gi + (lane >> 2), ch = (lane & 3) ^ ((lane >> 4) & 3);
+      qo[q] = (uint32_t)(row * C * 2 + ch * 16);
+    } else {                           // rows c of B, 2 RP bytes, transposed layout
+      int row, col;
+      tr_dma_coords<2 * RP>(gi, lane, row, col);
+      qo[q] = (uint32_t)(row * r * 2 + col * 2);
+    }
+    ql[q] = S::kP + gi * 1024;
+  }
+  auto dma = [&](int st, int slot) {
+    const int ss = min(st, s1 - 1);    // past the split: re-load its last stage (never read)
+    char* base = smem + slot * S::kStage;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) dma16(pr, base + pl[q], po[q], (uint32_t)ss * 64u);
+#pragma unroll
+    for (int q = 0; q < S::kQDma; ++q)
+      dma16(qr, base + ql[q], qo[q], QT ? (uint32_t)ss * 32u * (uint32_t)r * 2u : (uint32_t)ss * 64u);
+  };
+
+  constexpr int FJ = RP / 32;
+  f32x16_t acc[FJ];
+#pragma unroll
+  for (int f = 0; f < FJ; ++f)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[f][e] = 0.0f;
+
+  if (s0 < s1) {
+#pragma unroll
+    for (int a = 0; a < kAhead; ++a) dma(s0 + a, a);
+    int slot = 0;
+    for (int st = s0; st < s1; ++st) {
+      // stage st was issued kAhead - 1 stages before the last kAhead - 1 issues
+      QLORA_WAIT((kAhead - 1) * S::kLoads, 0);
+      __builtin_amdgcn_s_barrier();
+      dma(st + kAhead, slot == 0 ? kRing - 1 : slot - 1);   // the slot stage st - 1 used
+      const char* base = smem + slot * S::kStage;
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        // P fragment (B operand): row 32 w + lr, the 8 columns that lane half h
+        // takes in k16 step kk.  Both operands must agree on that: a 64-byte
+        // row read takes chunk 2h + kk (columns 16 h + 8 kk ..), a transposed
+        // read of 32 Q rows takes rows 16 kk + 8 h .. (chunk 2 kk + h)
+        const int ch = QT ? 2 * kk + h : 2 * h + kk;
+        bf16x8_t b = rd16(base + spos(32 * w + lr, ch));
+        if (32 * st + 8 * ch >= C) b = bf16x8_t{};   // columns past C (C % 8 == 0)
+#pragma unroll
+        for (int f = 0; f < FJ; ++f) {
+          bf16x8_t a;
+          if constexpr (!QT)
+            a = rd16(base + S::kP + spos(32 * f + lr, 2 * h + kk));
+          else
+            a = tr_frag<2 * RP>(base + S::kP + kk * 16 * 2 * RP + tr_off<2 * RP>(f));
+          acc[f] = mfma32x32x16(a, b, acc[f]);
         }
       }
+      slot = slot == kRing - 1 ? 0 : slot + 1;
     }
+    QLORA_WAIT(0, 0);
   }
-  __device__ __forceinline__ void store(bf16_t* lds) const {
+  // D[j][m]: lane (lr, h) holds m = m0 + 32 w + lr, j = 32 f + 8 q + 4 h + 0..3
+  float* out = part + (int64_t)sp * M * r;
+  const int64_t m = m0 + 32 * w + lr;
+  if (m < M) {
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int t = threadIdx.x + i * kThreads;
-      if (kTasks % kThreads == 0 || t < kTasks) {
-        int p, g;
-        coords(t, p, g);
-        const uint32_t a[4] = {v0[i].x, v0[i].y, v0[i].z, v0[i].w};
-        const uint32_t b[4] = {v1[i].x, v1[i].y, v1[i].z, v1[i].w};
+    for (int f = 0; f < FJ; ++f)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint32_t w = perm(b[e >> 1], a[e >> 1], (e & 1) ? 0x07060302u : 0x05040100u);
-          *reinterpret_cast<uint32_t*>(lds + lds_chunk_off(8 * g + e, p >> 2) + 2 * (p & 3)) = w;
+      for (int q = 0; q < 4; ++q) {
+        const int j = 32 * f + 8 * q + 4 * h;
+        if (j < r)
+          *reinterpret_cast<float4*>(out + m * r + j) =
+              make_float4(acc[f][4 * q], acc[f][4 * q + 1], acc[f][4 * q + 2], acc[f][4 * q + 3]);
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Token contraction: D = sum_m Big[m][c] Sm[m][j] for 128 columns c per
+// workgroup (wave w: columns 32 w .. +31) and all RP ranks j, stages of 32
+// tokens.  Both tiles are rows m, read transposed.  DB = false stores dA
+// [r x C] (A operand = Big, D[c][j]: four consecutive c per lane); DB = true
+// stores dB [C x r] (A operand = Sm, D[j][c]: four consecutive j per lane).
+// ---------------------------------------------------------------------------
+template <int RP>
+struct ColShape {
+  static constexpr int kBig = 32 * 256;                    // 8 KiB: 32 rows x 128 columns
+  static constexpr int kSm = 32 * 2 * RP;                  // 32 rows x RP ranks
+  static constexpr int kStage = kBig + kSm;
+  static constexpr int kSmDma = kSm / 1024 / 4;
+  static constexpr int kLoads = 2 + kSmDma;
+};
+
+template <int RP, bool DB>
+__global__ __launch_bounds__(kThreads, 1) void cskinny_kernel(const bf16_t* __restrict__ Big, int64_t M, int64_t C,
+                                                              const bf16_t* __restrict__ Sm, int r,
+                                                              int stages_per_split, int tiles_c,
+                                                              float* __restrict__ part) {
+  using S = ColShape<RP>;
+  extern __shared__ __align__(16) char smem[];
+  const int tc = blockIdx.x % tiles_c, sp = blockIdx.x / tiles_c;
+  const int t = threadIdx.x, w = t >> 6, lane = t & 63, lr = lane & 31, h = lane >> 5;
+  const int64_t c0 = (int64_t)tc * 128;
+  const int nst = (int)((M + 31) / 32);
+  const int s0 = sp * stages_per_split, s1 = min(nst, s0 + stages_per_split);
+  const rsrc_t br = make_rsrc(Big, (uint32_t)(M * C * 2));   // rows past M read as zero
+  const rsrc_t sr = make_rsrc(Sm, (uint32_t)(M * r * 2));
+  uint32_t bo[2], so[S::kSmDma];
+  int bl[2], sl[S::kSmDma];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    int row, col;
+    tr_dma_coords<256>(2 * w + q, lane, row, col);
+    bo[q] = (uint32_t)(row * C * 2 + (c0 + col) * 2);   // columns past C: never stored
+    bl[q] = (2 * w + q) * 1024;
+  }
+#pragma unroll
+  for (int q = 0; q < S::kSmDma; ++q) {
+    int row, col;
+    tr_dma_coords<2 * RP>(S::kSmDma * w + q, lane, row, col);
+    so[q] = (uint32_t)(row * r * 2 + col * 2);
+    sl[q] = S::kBig + (S::kSmDma * w + q) * 1024;
+  }
+  auto dma = [&](int st, int slot) {
+    const uint32_t ss = (uint32_t)min(st, s1 - 1);
+    char* base = smem + slot * S::kStage;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) dma16(br, base + bl[q], bo[q], ss * 32u * (uint32_t)C * 2u);
+#pragma unroll
+    for (int q = 0; q < S::kSmDma; ++q) dma16(sr, base + sl[q], so[q], ss * 32u * (uint32_t)r * 2u);
+  };
+
+  constexpr int FJ = RP / 32;
+  f32x16_t acc[FJ];
+#pragma unroll
+  for (int f = 0; f < FJ; ++f)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[f][e] = 0.0f;
+  const int bo_frag = tr_off<256>(w);
+
+  if (s0 < s1) {
+#pragma unroll
+    for (int a = 0; a < kAhead; ++a) dma(s0 + a, a);
+    int slot = 0;
+    for (int st = s0; st < s1; ++st) {
+      QLORA_WAIT((kAhead - 1) * S::kLoads, 0);
+      __builtin_amdgcn_s_barrier();
+      dma(st + kAhead, slot == 0 ? kRing - 1 : slot - 1);
+      const char* base = smem + slot * S::kStage;
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const bf16x8_t bg = tr_frag<256>(base + kk * 16 * 256 + bo_frag);
+#pragma unroll
+        for (int f = 0; f < FJ; ++f) {
+          const bf16x8_t sm = tr_frag<2 * RP>(base + S::kBig + kk * 16 * 2 * RP + tr_off<2 * RP>(f));
+          acc[f] = DB ? mfma32x32x16(sm, bg, acc[f]) : mfma32x32x16(bg, sm, acc[f]);
         }
       }
+      slot = slot == kRing - 1 ? 0 : slot + 1;
     }
+    QLORA_WAIT(0, 0);
   }
-};
-
-// ---------------------------------------------------------------------------
-// MFMA core: wave tile of FI x FJ 32x32 sub-tiles; As rows = output columns
-// (starting at ia), Bs rows = output rows (starting at jb).
-// ---------------------------------------------------------------------------
-template <int FI, int FJ>
-__device__ __forceinline__ void mma_step(f32x16_t (&acc)[FI][FJ], const bf16_t* As, const bf16_t* Bs,
-                                         int ia, int jb) {
-  const int lane = threadIdx.x & 63, lr = lane & 31, h = lane >> 5;
+  float* out = part + (int64_t)sp * C * r;
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) {
-    bf16x8_t a[FI], b[FJ];
+  for (int f = 0; f < FJ; ++f)
 #pragma unroll
-    for (int i = 0; i < FI; ++i)
-      a[i] = *reinterpret_cast<const bf16x8_t*>(As + lds_chunk_off(ia + 32 * i + lr, 2 * kk + h));
-#pragma unroll
-    for (int j = 0; j < FJ; ++j)
-      b[j] = *reinterpret_cast<const bf16x8_t*>(Bs + lds_chunk_off(jb + 32 * j + lr, 2 * kk + h));
-#pragma unroll
-    for (int i = 0; i < FI; ++i)
-#pragma unroll
-      for (int j = 0; j < FJ; ++j) acc[i][j] = mfma32x32x16(a[i], b[j], acc[i][j]);
-  }
-}
-
-struct StoreBf16 {
-  bf16_t* out;
-  int64_t ld, rows, cols;
-  __device__ __forceinline__ void operator()(int64_t row, int64_t col, float v0, float v1, float v2,
-                                             float v3) const {
-    if (row >= rows) return;
-    bf16_t* p = out + row * ld + col;
-    if (col + 3 < cols) {
-      *reinterpret_cast<uint2*>(p) = make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3));
-    } else {
-      const float v[4] = {v0, v1, v2, v3};
-      for (int e = 0; e < 4; ++e)
-        if (col + e < cols) p[e] = (bf16_t)(pack_bf16x2(v[e], 0.0f) & 0xFFFFu);
-    }
-  }
-};
-
-struct StoreF32 {
-  float* out;
-  int64_t ld, rows, cols;
-  __device__ __forceinline__ void operator()(int64_t row, int64_t col, float v0, float v1, float v2,
-                                             float v3) const {
-    if (row >= rows) return;
-    float* p = out + row * ld + col;
-    if (col + 3 < cols) {
-      *reinterpret_cast<float4*>(p) = make_float4(v0, v1, v2, v3);
-    } else {
-      const float v[4] = {v0, v1, v2, v3};
-      for (int e = 0; e < 4; ++e)
-        if (col + e < cols) p[e] = v[e];
-    }
-  }
-};
-
-// lane holds column lr of each 32x32 sub-tile and rows 8q + 4h + 0..3 of the
-// A side, i.e. four consecutive output columns of one output row.
-template <int FI, int FJ, class Store>
-__device__ __forceinline__ void epilogue(const f32x16_t (&acc)[FI][FJ], int64_t col0, int64_t row0,
-                                         const Store& st) {
-  const int lane = threadIdx.x & 63, lr = lane & 31, h = lane >> 5;
-#pragma unroll
-  for (int i = 0; i < FI; ++i)
-#pragma unroll
-    for (int j = 0; j < FJ; ++j)
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        st(row0 + 32 * j + lr, col0 + 32 * i + 8 * q + 4 * h, acc[i][j][4 * q + 0], acc[i][j][4 * q + 1],
-           acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
-}
-
-// Workgroup id -> tile: ids are first gathered per XCD (dispatch places
-// consecutive ids on consecutive XCDs), then walked column-fastest so the
-// tiles resident on one XCD share their token rows in its L2.
-__device__ __forceinline__ void map_tile(int tiles_c, int tiles_r, int& tc, int& tr) {
-  const int nwg = tiles_c * tiles_r;
-  int id = blockIdx.x;
-  if ((nwg & 7) == 0) id = (id & 7) * (nwg >> 3) + (id >> 3);
-  tc = id % tiles_c;
-  tr = id / tiles_c;
-}
-
-// ---------------------------------------------------------------------------
-// Skinny products (one side is the LoRA rank): out_part[split] = partial
-// contraction over a contiguous range of steps; a second kernel sums the
-// splits in a fixed order (deterministic) and applies the scale.
-// ---------------------------------------------------------------------------
-template <bool T, int B>
-struct Producer;
-template <int B>
-struct Producer<false, B> { using type = RowTile<B>; };
-template <int B>
-struct Producer<true, B> { using type = TransTile<B>; };
-
-template <int BR, int BC, int WR, int WC, bool ROW_T, bool COL_T>
-__global__ __launch_bounds__(kThreads) void skinny_kernel(TileDesc rd, TileDesc cd, int64_t rows, int64_t cols,
-                                                          int total_steps, int steps_per_split, int tiles_r,
-                                                          int tiles_c, float* __restrict__ part) {
-  constexpr int TJ = BR / WR, TI = BC / WC, FJ = TJ / 32, FI = TI / 32;
-  extern __shared__ __align__(16) bf16_t smem[];
-  bf16_t* const As0 = smem;
-  bf16_t* const As1 = smem + BC * 64;
-  bf16_t* const Bs0 = smem + 2 * BC * 64;
-  bf16_t* const Bs1 = smem + 2 * BC * 64 + BR * 64;
-  const int tiles = tiles_r * tiles_c;
-  const int split = blockIdx.x / tiles, rem = blockIdx.x % tiles;
-  const int tr = rem / tiles_c, tc = rem % tiles_c;
-  const int w = threadIdx.x >> 6, wr = w / WC, wc = w % WC;
-  const int64_t r0 = (int64_t)tr * BR, c0 = (int64_t)tc * BC;
-  typename Producer<ROW_T, BR>::type rl(rd, r0);
-  typename Producer<COL_T, BC>::type cl(cd, c0);
-
-  f32x16_t acc[FI][FJ];
-#pragma unroll
-  for (int i = 0; i < FI; ++i)
-#pragma unroll
-    for (int j = 0; j < FJ; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
-
-  const int s_begin = split * steps_per_split;
-  const int s_end = min(total_steps, s_begin + steps_per_split);
-  if (s_begin < s_end) {
-    rl.load(s_begin);
-    cl.load(s_begin);
-    rl.store(Bs0);
-    cl.store(As0);
-    __syncthreads();
-    for (int st = s_begin; st < s_end; ++st) {
-      const bool odd = (st - s_begin) & 1;
-      if (st + 1 < s_end) {
-        rl.load(st + 1);
-        cl.load(st + 1);
+    for (int q = 0; q < 4; ++q) {
+      if constexpr (!DB) {   // D[c][j]: c = c0 + 32 w + 8 q + 4 h + 0..3, j = 32 f + lr -> dA[j][c..]
+        const int j = 32 * f + lr;
+        const int64_t c = c0 + 32 * w + 8 * q + 4 * h;
+        if (j < r && c < C)
+          *reinterpret_cast<float4*>(out + j * C + c) =
+              make_float4(acc[f][4 * q], acc[f][4 * q + 1], acc[f][4 * q + 2], acc[f][4 * q + 3]);
+      } else {               // D[j][c]: j = 32 f + 8 q + 4 h + 0..3, c = c0 + 32 w + lr -> dB[c][j..]
+        const int j = 32 * f + 8 * q + 4 * h;
+        const int64_t c = c0 + 32 * w + lr;
+        if (j < r && c < C)
+          *reinterpret_cast<float4*>(out + c * r + j) =
+              make_float4(acc[f][4 * q], acc[f][4 * q + 1], acc[f][4 * q + 2], acc[f][4 * q + 3]);
       }
-      mma_step<FI, FJ>(acc, odd ? As1 : As0, odd ? Bs1 : Bs0, wc * TI, wr * TJ);
-      if (st + 1 < s_end) {
-        rl.store(odd ? Bs0 : Bs1);
-        cl.store(odd ? As0 : As1);
-      }
-      __syncthreads();
     }
-  }
-  epilogue<FI, FJ>(acc, c0 + wc * TI, r0 + wr * TJ, StoreF32{part + (int64_t)split * rows * cols, cols, rows, cols});
 }
 
-// out = scale * sum_s part[s]; optional bf16 outputs (two copies) or fp32.
 __global__ __launch_bounds__(kThreads) void reduce_kernel(const float* __restrict__ part, int splits, int64_t n,
                                                           float scale, float* __restrict__ out_f32,
                                                           bf16_t* __restrict__ out_bf16,
@@ -312,101 +310,96 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(const float* __restric
   }
 }
 
-// ---------------------------------------------------------------------------
-// Host-side launchers.
-// ---------------------------------------------------------------------------
-static hipError_t set_lds(const void* fn, size_t bytes) {
-  return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
-}
-
-// Split of the contraction: enough workgroups to cover the chip, at least
-// four 64-element steps per split.
-struct SkinnyShape {
-  int BR, BC, tiles_r, tiles_c, total_steps, sps, splits;
+// Splits of the contraction (stages of 32) for about `target` workgroups,
+// at least 8 stages each.  The targets (256, one per CU of the part this is
+// tuned for, and 512 for dY B) were measured; they are fixed, not the
+// device's CU count, because the workspace size a caller queries must not
+// depend on which device is current.
+struct Split {
+  int tiles, sps, splits;
 };
-
-static SkinnyShape skinny_shape(int64_t rows, int64_t cols, int64_t contraction, int BR, int BC) {
-  SkinnyShape sh;
-  sh.BR = BR;
-  sh.BC = BC;
-  sh.tiles_r = (int)((rows + BR - 1) / BR);
-  sh.tiles_c = (int)((cols + BC - 1) / BC);
-  sh.total_steps = (int)((contraction + 63) / 64);
-  const int tiles = sh.tiles_r * sh.tiles_c;
-  int want = (512 + tiles - 1) / tiles;   // about two workgroups per CU: fewer partial sums to write and re-read
-  const int max_splits = sh.total_steps / 4 > 0 ? sh.total_steps / 4 : 1;
-  if (want > max_splits) want = max_splits;
-  if (want < 1) want = 1;
-  sh.sps = (sh.total_steps + want - 1) / want;
-  sh.splits = (sh.total_steps + sh.sps - 1) / sh.sps;
-  return sh;
+Split split_for(int64_t tiles, int64_t contraction, int target) {
+  const int nst = (int)((contraction + 31) / 32);
+  int want = (int)((target + tiles - 1) / tiles);
+  want = std::max(1, std::min(want, std::max(1, nst / 8)));
+  Split s;
+  s.tiles = (int)tiles;
+  s.sps = (nst + want - 1) / want;
+  s.splits = (nst + s.sps - 1) / s.sps;
+  return s;
 }
 
-static void kind_tiles(int kind, int r, int& BR, int& BC) {
-  const bool wide = r > 64;
-  switch (kind) {
-    case kGtX: BR = wide ? 128 : 64; BC = 256; break;   // rows = rank, cols = K
-    default: BR = 128; BC = wide ? 128 : 64; break;     // rows = tokens / N, cols = rank
-  }
+Split kind_split(int64_t rows, int64_t cols, int64_t contraction, int kind) {
+  // rows x cols is the output: kXAt, kDyB [M x r]; kGtX [r x K]; kDytU [N x r]
+  const int64_t tiles = (kind == kGtX) ? (cols + 127) / 128 : (rows + 127) / 128;
+  return split_for(tiles, contraction, kind == kDyB ? 512 : 256);
 }
 
-size_t skinny_partial_bytes(int64_t rows, int64_t cols, int64_t contraction, int kind) {
-  int BR, BC;
-  const int r = (kind == kGtX) ? (int)rows : (int)cols;
-  kind_tiles(kind, r, BR, BC);
-  const SkinnyShape sh = skinny_shape(rows, cols, contraction, BR, BC);
-  return (size_t)sh.splits * (size_t)rows * (size_t)cols * sizeof(float);
-}
-
-template <int BR, int BC, int WR, int WC, bool ROW_T, bool COL_T>
-static hipError_t run_skinny(const TileDesc& rl, const TileDesc& cl, int64_t rows, int64_t cols, int64_t contraction,
-                             float* part, float scale, float* out_f32, bf16_t* out_bf16, bf16_t* out_bf16_2,
-                             hipStream_t st) {
-  const SkinnyShape sh = skinny_shape(rows, cols, contraction, BR, BC);
-  const size_t lds = 2u * (BR + BC) * 64 * sizeof(bf16_t);
-  auto* fn = &skinny_kernel<BR, BC, WR, WC, ROW_T, COL_T>;
-  hipError_t e = set_lds(reinterpret_cast<const void*>(fn), lds);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(fn, dim3(sh.tiles_r * sh.tiles_c * sh.splits), dim3(kThreads), lds, st, rl, cl, rows, cols,
-                     sh.total_steps, sh.sps, sh.tiles_r, sh.tiles_c, part);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const int64_t n = rows * cols;  // multiple of 4: cols is the rank (r % 16 == 0) or K
+hipError_t reduce(const float* part, int splits, int64_t n, float scale, float* out_f32, bf16_t* out_bf16,
+                  bf16_t* out_bf16_2, hipStream_t st) {
   hipLaunchKernelGGL(reduce_kernel, dim3((unsigned)((n / 4 + kThreads - 1) / kThreads)), dim3(kThreads), 0, st,
-                     part, sh.splits, n, scale, out_f32, out_bf16, out_bf16_2);
+                     part, splits, n, scale, out_f32, out_bf16, out_bf16_2);
   return hipGetLastError();
 }
 
-// U = X A^T  [M x r]   (rows = tokens, cols = rank, contraction K)
+template <int RP, bool QT>
+hipError_t run_rows(const bf16_t* P, int64_t M, int64_t C, const bf16_t* Q, int r, float* part, float scale,
+                    bf16_t* out, bf16_t* out2, hipStream_t st) {
+  const Split sp = split_for((M + 127) / 128, C, QT ? 512 : 256);
+  auto* fn = &rskinny_kernel<RP, QT>;
+  const size_t lds = (size_t)kRing * RowShape<RP, QT>::kStage;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(fn, dim3(sp.tiles * sp.splits), dim3(kThreads), lds, st, P, M, C, Q, r, sp.sps, sp.tiles, part);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  return reduce(part, sp.splits, M * r, scale, nullptr, out, out2, st);
+}
+
+template <int RP, bool DB>
+hipError_t run_cols(const bf16_t* Big, int64_t M, int64_t C, const bf16_t* Sm, int r, float* part, float scale,
+                    float* out, hipStream_t st) {
+  const Split sp = split_for((C + 127) / 128, M, 256);
+  auto* fn = &cskinny_kernel<RP, DB>;
+  const size_t lds = (size_t)kRing * ColShape<RP>::kStage;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(fn, dim3(sp.tiles * sp.splits), dim3(kThreads), lds, st, Big, M, C, Sm, r, sp.sps, sp.tiles,
+                     part);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  return reduce(part, sp.splits, C * r, scale, out, nullptr, nullptr, st);
+}
+
+}  // namespace
+
+size_t skinny_partial_bytes(int64_t rows, int64_t cols, int64_t contraction, int kind) {
+  const Split sp = kind_split(rows, cols, contraction, kind);
+  return (size_t)sp.splits * (size_t)rows * (size_t)cols * sizeof(float);
+}
+
 hipError_t launch_xat(const bf16_t* X, const bf16_t* A, int64_t M, int64_t K, int r, float* part, bf16_t* out,
                       bf16_t* out2, float scale, hipStream_t st) {
-  const TileDesc rl{X, K, M, K}, cl{A, K, r, K};
-  if (r <= 64) return run_skinny<128, 64, 4, 1, false, false>(rl, cl, M, r, K, part, scale, nullptr, out, out2, st);
-  return run_skinny<128, 128, 4, 1, false, false>(rl, cl, M, r, K, part, scale, nullptr, out, out2, st);
+  if (r <= 64) return run_rows<64, false>(X, M, K, A, r, part, scale, out, out2, st);
+  return run_rows<128, false>(X, M, K, A, r, part, scale, out, out2, st);
 }
 
-// G = dY B  [M x r]   (contraction N; B [N x r] is contraction-major)
 hipError_t launch_dyb(const bf16_t* dY, const bf16_t* B, int64_t M, int64_t N, int r, float* part, bf16_t* out,
                       float scale, hipStream_t st) {
-  const TileDesc rl{dY, N, M, N}, cl{B, r, N, r};
-  if (r <= 64) return run_skinny<128, 64, 4, 1, false, true>(rl, cl, M, r, N, part, scale, nullptr, out, nullptr, st);
-  return run_skinny<128, 128, 4, 1, false, true>(rl, cl, M, r, N, part, scale, nullptr, out, nullptr, st);
+  if (r <= 64) return run_rows<64, true>(dY, M, N, B, r, part, scale, out, nullptr, st);
+  return run_rows<128, true>(dY, M, N, B, r, part, scale, out, nullptr, st);
 }
 
-// dA = scale * G^T X  [r x K]   (rows = rank, cols = K, contraction M)
 hipError_t launch_gtx(const bf16_t* G, const bf16_t* X, int64_t M, int64_t K, int r, float* part, float* dA,
                       float scale, hipStream_t st) {
-  const TileDesc rl{G, r, M, r}, cl{X, K, M, K};
-  if (r <= 64) return run_skinny<64, 256, 1, 4, true, true>(rl, cl, r, K, M, part, scale, dA, nullptr, nullptr, st);
-  return run_skinny<128, 256, 2, 2, true, true>(rl, cl, r, K, M, part, scale, dA, nullptr, nullptr, st);
+  if (r <= 64) return run_cols<64, false>(X, M, K, G, r, part, scale, dA, st);
+  return run_cols<128, false>(X, M, K, G, r, part, scale, dA, st);
 }
 
-// dB = scale * dY^T U  [N x r]   (rows = N, cols = rank, contraction M)
 hipError_t launch_dytu(const bf16_t* dY, const bf16_t* U, int64_t M, int64_t N, int r, float* part, float* dB,
                        float scale, hipStream_t st) {
-  const TileDesc rl{dY, N, M, N}, cl{U, r, M, r};
-  if (r <= 64) return run_skinny<128, 64, 4, 1, true, true>(rl, cl, N, r, M, part, scale, dB, nullptr, nullptr, st);
-  return run_skinny<128, 128, 4, 1, true, true>(rl, cl, N, r, M, part, scale, dB, nullptr, nullptr, st);
+  if (r <= 64) return run_cols<64, true>(dY, M, N, U, r, part, scale, dB, st);
+  return run_cols<128, true>(dY, M, N, U, r, part, scale, dB, st);
 }
 
 }  // namespace qlora

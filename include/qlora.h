@@ -177,8 +177,9 @@ qlora_status qlora_lora_dy_b(const uint16_t* dY, const uint16_t* B, int64_t M, i
                              uint16_t* G, void* ws, size_t ws_bytes, void* stream);
 
 /* dA [r x K] = s G^T X and dB [N x r] = s dY^T U (fp32, overwritten),
- * s = RN32(alpha / r).  Glossary "Definition": weight gradients only for
- * the LoRA matrices. */
+ * s = RN32(alpha / r).  M*K and M*N must be < 2^31 (QLORA_E_UNSUPPORTED
+ * otherwise).  Glossary "Definition": weight gradients only for the LoRA
+ * matrices. */
 qlora_status qlora_lora_grads(const uint16_t* X, const uint16_t* dY, const uint16_t* U, const uint16_t* G,
                               int64_t M, int64_t N, int64_t K, int32_t r, float alpha, float* dA, float* dB,
                               void* ws, size_t ws_bytes, void* stream);
