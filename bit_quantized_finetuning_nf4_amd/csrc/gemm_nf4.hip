@@ -453,6 +453,20 @@ __device__ __forceinline__ uint2 fwdr_codes(const char* smem, const FwdR& f, int
   return make_uint2(v.x, v.y);
 }
 
+// LDS read bases of the loop: token ring half [slot / 4] at chunk 2h (0) or
+// 2h + 1 (1), and the code chunks (row 0 of the lane; row 1 is 512 B on).
+struct RdBase {
+  int tok[2][2];
+  int code;
+};
+// Codes of row i in stage ST (mod 8), read from the loop's code base.
+template <int ST>
+__device__ __forceinline__ uint2 fwdr_codes_at(const char* smem, const RdBase& rb, int i) {
+  constexpr int off = ((ST >> 1) & 3) * kRChunk + (ST & 1) * 4096;
+  const u32x2_t v = *reinterpret_cast<const u32x2_t*>(smem + rb.code + off + 512 * i);
+  return make_uint2(v.x, v.y);
+}
+
 struct FragsR {
   bf16x8_t b0[8], b1[8];   // token fragments of k16 steps 0 and 1
   bf16x8_t a0[2], a1[2];   // weight fragments of the current stage, steps 0 and 1 [row]
@@ -565,7 +579,7 @@ __device__ __forceinline__ void tb_chunk(TbState& b, const Scale& sc, Nf4Table& 
 template <int U8, int X>
 __device__ __forceinline__ void fwdr_slot(char* smem, const FwdR& f, int s, f32x16_t (&acc)[2][8], FragsR& F,
                                           Nf4Table (&T)[2], Scale (&sc)[4][2], bf16x8_t (&n1)[2], DqState& dq,
-                                          TbState& tb, int fo0, int fo1) {
+                                          TbState& tb, const RdBase& rb) {
   constexpr bool kOdd = (U8 & 1) != 0;
   constexpr int i = X & 1, j = (X & 15) >> 1;
   // the step-1 fragments (read in slots 0..7) and the codes: one wait for all
@@ -592,8 +606,11 @@ __device__ __forceinline__ void fwdr_slot(char* smem, const FwdR& f, int s, f32x
       sc[SL][row].q = f.aq[row][b];
   }
   // LDS reads
-  if constexpr (X < 8) F.b1[X] = rd16(smem + U8 * kOp + X * 2048 + fo1);
-  if constexpr (X >= 16 && X < 24) F.b0[X - 16] = rd16(smem + ((U8 + 1) & 7) * kOp + (X - 16) * 2048 + fo0);
+  if constexpr (X < 8) F.b1[X] = rd16(smem + rb.tok[U8 >> 2][1] + (U8 & 3) * kOp + X * 2048);
+  if constexpr (X >= 16 && X < 24) {
+    constexpr int SN = (U8 + 1) & 7;
+    F.b0[X - 16] = rd16(smem + rb.tok[SN >> 2][0] + (SN & 3) * kOp + (X - 16) * 2048);
+  }
   // VALU chunks
   if constexpr (kOdd) {
     constexpr int SL = ((U8 + 1) >> 1) & 3;
@@ -628,7 +645,7 @@ __device__ __forceinline__ void fwdr_slot(char* smem, const FwdR& f, int s, f32x
 
 template <int U8>
 __device__ __forceinline__ void fwdr_substep(char* smem, const FwdR& f, int s, f32x16_t (&acc)[2][8], FragsR& F,
-                                             Nf4Table (&T)[2], Scale (&sc)[4][2], int fo0, int fo1) {
+                                             Nf4Table (&T)[2], Scale (&sc)[4][2], const RdBase& rb) {
   __builtin_amdgcn_sched_barrier(0);
   // the LDS reads of the last substep (step 0 of stage s, issued 16 slots
   // ago) are waited for here too
@@ -636,11 +653,11 @@ __device__ __forceinline__ void fwdr_substep(char* smem, const FwdR& f, int s, f
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
   // codes of stage s+2, for the next substep
-  const uint2 cn0 = fwdr_codes(smem, f, 0, s + 2), cn1 = fwdr_codes(smem, f, 1, s + 2);
+  const uint2 cn0 = fwdr_codes_at<U8 + 2>(smem, rb, 0), cn1 = fwdr_codes_at<U8 + 2>(smem, rb, 1);
   bf16x8_t n1[2];
   DqState dq;
   TbState tb;
-#define QLORA_FWDR_SLOT(x) fwdr_slot<U8, x>(smem, f, s, acc, F, T, sc, n1, dq, tb, fo0, fo1)
+#define QLORA_FWDR_SLOT(x) fwdr_slot<U8, x>(smem, f, s, acc, F, T, sc, n1, dq, tb, rb)
 #define QLORA_FWDR_SLOT4(x) QLORA_FWDR_SLOT(x); QLORA_FWDR_SLOT(x + 1); QLORA_FWDR_SLOT(x + 2); QLORA_FWDR_SLOT(x + 3)
   QLORA_FWDR_SLOT4(0); QLORA_FWDR_SLOT4(4); QLORA_FWDR_SLOT4(8); QLORA_FWDR_SLOT4(12);
   QLORA_FWDR_SLOT4(16); QLORA_FWDR_SLOT4(20); QLORA_FWDR_SLOT4(24); QLORA_FWDR_SLOT4(28);
@@ -728,9 +745,21 @@ __global__ __launch_bounds__(kThreads, 1) void nf4_fwd_r_kernel(Nf4View W, const
   }
 #pragma unroll
   for (int j = 0; j < 8; ++j) F.b0[j] = rd16(smem + j * 2048 + fo0);
-  // K % 64 == 0, so the stage count is even
+  // Base addresses of the loop's LDS reads.  The ring spans 128 KiB and the
+  // codes sit above it, past the 16-bit offset field of ds_read, so the loop
+  // keeps a base per ring half and one for the codes; hiding them from the
+  // compiler stops it from folding them back into per-read address adds.
+  RdBase rb;
+  rb.tok[0][0] = fo0;
+  rb.tok[0][1] = fo1;
+  rb.tok[1][0] = fo0 + 4 * kOp;
+  rb.tok[1][1] = fo1 + 4 * kOp;
+  rb.code = kRCodeBase + f.crow[0];
+  asm volatile("" : "+v"(rb.tok[1][0]), "+v"(rb.tok[1][1]), "+v"(rb.code));
+  // K % 64 == 0, so the stage count is even; the loop's stage counter stays a
+  // multiple of 8, so ring positions follow from the substep index alone
   int st = 0;
-#define QLORA_FWDR_SUB(u) fwdr_substep<u>(smem, f, st + u, acc, F, T, sc, fo0, fo1)
+#define QLORA_FWDR_SUB(u) fwdr_substep<u>(smem, f, st + u, acc, F, T, sc, rb)
   for (; st + 8 <= f.nsub; st += 8) {
     QLORA_FWDR_SUB(0); QLORA_FWDR_SUB(1); QLORA_FWDR_SUB(2); QLORA_FWDR_SUB(3);
     QLORA_FWDR_SUB(4); QLORA_FWDR_SUB(5); QLORA_FWDR_SUB(6); QLORA_FWDR_SUB(7);
