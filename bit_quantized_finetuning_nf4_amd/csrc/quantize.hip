@@ -11,17 +11,47 @@
 
 namespace qlora {
 
-// NF4 code of an fp32 value x = RN32(w / a).
-// #{k : x > T_k} for the 15 ascending thresholds, by binary search: the
-// first step against T_7 (a constant), then three steps against thresholds
-// picked from an LDS copy of the table (T_{c+3}, T_{c+1}, T_c for the count
-// c found so far).  4 compares instead of 15.
-__device__ __forceinline__ uint32_t nf4_code(float x, const float* thr) {
-  uint32_t c = x > u2f(kNf4ThreshBits[7]) ? 8u : 0u;
-  c += x > thr[c + 3] ? 4u : 0u;
-  c += x > thr[c + 1] ? 2u : 0u;
-  c += x > thr[c] ? 1u : 0u;
-  return c;
+// NF4 codes of eight fp32 values x = RN32(w / a): c = #{k : x > T_k} over
+// the 15 ascending thresholds, by binary search with the code's bits found
+// most significant first.  The first step compares with T_7 (a constant),
+// the others with T_{8c+3}, T_{4c+1}, T_{2c} from an LDS copy of the table:
+// 4 compares instead of 15.  A compare is the sign of T - x: the difference
+// of two finite floats is rounded without changing its sign and is +0 when
+// they are equal, so its sign bit is [x > T] (no threshold is zero).  The
+// funnel shift (c : d) >> 31 appends that bit to c in one instruction.  The
+// eight searches advance step by step together, so that each step's eight
+// LDS reads are in flight at once.
+__device__ __forceinline__ uint32_t gt_bit(float t, float x) { return __builtin_bit_cast(uint32_t, t - x); }
+__device__ __forceinline__ uint32_t nf4_codes8(const float (&x)[8], const float* thr) {
+  uint32_t c[8];
+  float t[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) c[i] = gt_bit(u2f(kNf4ThreshBits[7]), x[i]) >> 31;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) t[i] = thr[8 * c[i] + 3];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) c[i] = __builtin_amdgcn_alignbit(c[i], gt_bit(t[i], x[i]), 31);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) t[i] = thr[4 * c[i] + 1];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) c[i] = __builtin_amdgcn_alignbit(c[i], gt_bit(t[i], x[i]), 31);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) t[i] = thr[2 * c[i]];
+  uint32_t packed = 0u;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) packed |= __builtin_amdgcn_alignbit(c[i], gt_bit(t[i], x[i]), 31) << (4 * i);
+  return packed;
+}
+
+// max over the eight lanes 8j .. 8j+7 of a non-negative float, on its bits
+// (ordered as the values): swap neighbours, swap pairs, then mirror the two
+// quads (DPP)
+__device__ __forceinline__ float max8_lanes(float m) {
+  uint32_t u = __builtin_bit_cast(uint32_t, m);
+  u = max(u, (uint32_t)__builtin_amdgcn_mov_dpp((int)u, 0xB1, 0xF, 0xF, true));
+  u = max(u, (uint32_t)__builtin_amdgcn_mov_dpp((int)u, 0x4E, 0xF, 0xF, true));
+  u = max(u, (uint32_t)__builtin_amdgcn_mov_dpp((int)u, 0x141, 0xF, 0xF, true));
+  return u2f(u);
 }
 
 // Nearest Q8 level to y in [0, 1], ties to the lower index.  The nearest
@@ -77,25 +107,29 @@ __global__ __launch_bounds__(256) void quantize_kernel(const bf16_t* __restrict_
 #pragma unroll
     for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(f[i]));
     // absmax of the 64-element block held by 8 consecutive lanes
-    m = fmaxf(m, __shfl_xor(m, 1));
-    m = fmaxf(m, __shfl_xor(m, 2));
-    m = fmaxf(m, __shfl_xor(m, 4));
+    m = max8_lanes(m);
     const int blk = pass * 32 + (tid >> 3);
     if ((tid & 7) == 0) amax[blk] = m;
 
     uint32_t packed = 0x77777777u;
     if (m > 0.0f) {
-      // x = RN32(w / a): the fp64 product w * RN64(1/a) is within 2^-52
-      // relative of w / a, and an fp32 rounding boundary is never closer
-      // than 2^-49 relative to such a quotient in the range where the code
-      // depends on it, so rounding the product to fp32 gives RN32(w / a).
-      const double rinv = 1.0 / (double)m;
-      packed = 0u;
+      // x = RN32(w / a) from the fp64 product w * r, r ~ 1/a.  w and a are
+      // bf16 (at most 8 significant bits) and an fp32 rounding boundary B is
+      // an odd multiple of a power of two with 25 significant bits, so
+      // w - aB is never 0 and is a multiple of a power of two at most 2^-33
+      // |w| in magnitude: w / a is at least 2^-33 relative away from every
+      // boundary.  r from the hardware reciprocal and two Newton steps is
+      // within 2^-50 relative of 1/a, the product adds 2^-53, so the product
+      // lies on the same side of every boundary as w / a and rounding it to
+      // fp32 gives RN32(w / a).
+      const double ad = (double)m;
+      double r = __builtin_amdgcn_rcp(ad);
+      r = fma(r, fma(-ad, r, 1.0), r);
+      r = fma(r, fma(-ad, r, 1.0), r);
+      float x[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float x = (float)((double)f[i] * rinv);
-        packed |= nf4_code(x, thr) << (4 * i);
-      }
+      for (int i = 0; i < 8; ++i) x[i] = (float)((double)f[i] * r);
+      packed = nf4_codes8(x, thr);
     }
     if (e0 + 8 <= numel) {
       *reinterpret_cast<uint32_t*>(codes + (e0 >> 1)) = packed;
