@@ -1432,14 +1432,6 @@ __global__ __launch_bounds__(kThreads, 1) void nf4_dx_kernel(Nf4View W, const bf
 
 }  // namespace
 
-// CUs of the current device (the tail split below needs the round size).
-static int gemm_cus() {
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-    return 256;
-  return cus > 0 ? cus : 256;
-}
-
 hipError_t launch_fwd(const Nf4View& W, const bf16_t* X, int64_t M, const bf16_t* U, const bf16_t* B, int r,
                       float s, bf16_t* Y, hipStream_t st) {
   const int tiles_n = (int)((W.N + kTile - 1) / kTile);
@@ -1465,7 +1457,7 @@ hipError_t launch_fwd(const Nf4View& W, const bf16_t* X, int64_t M, const bf16_t
   // When the last round of 256 x 256 tiles would leave at least half the CUs
   // idle, its tiles run as two 128-row halves each, in a second launch of
   // the 32-rows-per-wave kernel, so that round takes about half as long.
-  const int cus = gemm_cus();
+  const int cus = device_cu_count();   // the tail split needs the round size
   const int rest = tiles % cus;
   const int main_tiles = (tiles > cus && rest > 0 && 2 * rest <= cus) ? tiles - rest : tiles;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&nf4_fwd_r_kernel),

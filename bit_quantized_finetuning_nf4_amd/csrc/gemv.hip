@@ -458,12 +458,7 @@ LaunchPlan plan_launch(const GemvJob* jobs, int njobs, bool pair, int max_groups
   return lp;
 }
 
-int device_cus() {
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-    return 256;
-  return cus > 0 ? std::min(cus, kMaxGvGroups) : 256;
-}
+int device_cus() { return std::min(device_cu_count(), kMaxGvGroups); }
 
 template <bool kPair>
 hipError_t launch_main(const GemvJob* djobs, const int4* segs, const int* range, int groups, int max_steps,

@@ -16,6 +16,9 @@ struct Nf4View {
   int64_t K;  // cols, K % 64 == 0 on the GEMM/GEMV paths
 };
 
+// Compute units of the current device (256 if the query fails).
+int device_cu_count();
+
 hipError_t launch_quantize(const bf16_t* W, int64_t numel, uint8_t* codes, uint8_t* absmax_q,
                            float* group_scale, hipStream_t s);
 hipError_t launch_dequant(const uint8_t* codes, const uint8_t* absmax_q, const float* group_scale,

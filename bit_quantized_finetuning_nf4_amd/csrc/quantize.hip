@@ -87,16 +87,31 @@ __global__ __launch_bounds__(256) void quantize_kernel(const bf16_t* __restrict_
   const int64_t gbase = g * (int64_t)kGroupBlocks * kBlock;
   const int64_t code_bytes = (numel + 1) >> 1;
 
+  // all eight passes' loads first: 128 bytes per lane in flight
+  uint4 wv[8];
+  if (gbase + (int64_t)kGroupBlocks * kBlock <= numel) {   // a whole group (uniform branch)
+#pragma unroll
+    for (int pass = 0; pass < 8; ++pass)
+      wv[pass] = *reinterpret_cast<const uint4*>(W + gbase + (int64_t)pass * 2048 + tid * 8);
+  } else {
+#pragma unroll
+    for (int pass = 0; pass < 8; ++pass) {
+      const int64_t e0 = gbase + (int64_t)pass * 2048 + tid * 8;
+      uint32_t w[4] = {0u, 0u, 0u, 0u};
+      if (e0 + 8 <= numel) {
+        const uint4 v = *reinterpret_cast<const uint4*>(W + e0);
+        w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+      } else if (e0 < numel) {
+        for (int i = 0; i < 8; ++i)
+          if (e0 + i < numel) w[i >> 1] |= (uint32_t)W[e0 + i] << (16 * (i & 1));
+      }
+      wv[pass] = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+  }
+#pragma unroll
   for (int pass = 0; pass < 8; ++pass) {
     const int64_t e0 = gbase + (int64_t)pass * 2048 + tid * 8;
-    uint32_t w[4] = {0u, 0u, 0u, 0u};
-    if (e0 + 8 <= numel) {
-      const uint4 v = *reinterpret_cast<const uint4*>(W + e0);
-      w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
-    } else if (e0 < numel) {
-      for (int i = 0; i < 8; ++i)
-        if (e0 + i < numel) w[i >> 1] |= (uint32_t)W[e0 + i] << (16 * (i & 1));
-    }
+    const uint32_t w[4] = {wv[pass].x, wv[pass].y, wv[pass].z, wv[pass].w};
     float f[8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -116,8 +131,8 @@ __global__ __launch_bounds__(256) void quantize_kernel(const bf16_t* __restrict_
       // x = RN32(w / a) from the fp64 product w * r, r ~ 1/a.  w and a are
       // bf16 (at most 8 significant bits) and an fp32 rounding boundary B is
       // an odd multiple of a power of two with 25 significant bits, so
-      // w - aB is never 0 and is a multiple of a power of two at most 2^-33
-      // |w| in magnitude: w / a is at least 2^-33 relative away from every
+      // w - aB is a nonzero multiple of a power of two that is at least
+      // about 2^-33 |w|: w / a is at least that far, relatively, from every
       // boundary.  r from the hardware reciprocal and two Newton steps is
       // within 2^-50 relative of 1/a, the product adds 2^-53, so the product
       // lies on the same side of every boundary as w / a and rounding it to
@@ -200,6 +215,13 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict_
         out[e0 + i + j] = (bf16_t)(o[j >> 1] >> (16 * (j & 1)));
     }
   }
+}
+
+int device_cu_count() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 256;
+  return cus > 0 ? cus : 256;
 }
 
 hipError_t launch_quantize(const bf16_t* W, int64_t numel, uint8_t* codes, uint8_t* absmax_q,
