@@ -102,3 +102,50 @@ def test_quantize_deterministic_and_bounded():
         assert torch.all(b[:pad] == fill) and torch.all(b[-pad:] == fill)
     assert torch.all(gs[:pad] == -7.0) and torch.all(gs[-pad:] == -7.0)
     assert torch.all(buf[:128] == 0x7BCD) and torch.all(buf[128 + n:] == 0x7BCD)
+
+
+def _near_boundary_blocks():
+    """Blocks whose quotients w / a sit as close as bf16 allows to every
+    decision point of the encoding: the midpoint of two adjacent NF4 levels
+    (where the nearest level changes) and the fp32 rounding boundary next to
+    it (where RN32(w / a) moves from one side of that midpoint to the other).
+    One block per (absmax mantissa, side): its first element is the absmax a
+    (1 + j/128 times a power of two), the others are the three bf16 values
+    around a * target for each target."""
+    L = oracle.nf4_levels().astype(np.float64)
+    targets = []
+    for k in range(15):
+        mid = (L[k] + L[k + 1]) / 2
+        lo = np.float32(mid)
+        if float(lo) > mid:
+            lo = np.nextafter(lo, np.float32(-np.inf))
+        hi = np.nextafter(lo, np.float32(np.inf))
+        targets += [mid, (float(lo) + float(hi)) / 2]
+    rng = np.random.default_rng(20261203)
+    blocks = []
+    for j in range(128):
+        a = 1.0 + j / 128.0
+        ws = []
+        for t in targets:
+            b = int(np.array([a * t], dtype=np.float32).view(np.uint32)[0]) >> 16
+            ws += [b - 1, b, b + 1]
+        ws = np.array(ws, dtype=np.uint32)
+        for half in range(2):
+            part = ws[half * 45:(half + 1) * 45]
+            blk = np.zeros(64, dtype=np.uint32)
+            blk[0] = np.array([a], dtype=np.float32).view(np.uint32)[0] >> 16
+            blk[1:1 + part.size] = part
+            # a random power-of-two scale keeps every quotient
+            e = int(rng.integers(-20, 8))
+            f = (blk << 16).view(np.float32) * np.float32(2.0 ** e)
+            blocks.append(synth.to_bf16_bits(f))
+    bits = np.concatenate(blocks)
+    # the absmax of every block must be its first element
+    mag = np.abs(oracle.bf16_bits_to_f64(bits).reshape(-1, 64))
+    assert np.all(mag.max(axis=1) == mag[:, 0])
+    return bits
+
+
+def test_quantize_near_decision_boundaries():
+    bits = _near_boundary_blocks()
+    _check(bits, (bits.size // 64, 64), "quotients at level midpoints and fp32 rounding boundaries")
