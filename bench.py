@@ -118,6 +118,46 @@ def summarize_pmc(fetch_csv, write_csv, copy_mib):
     return out
 
 
+MFMA_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_MFMA", "SQ_INSTS_VALU",
+                 "SQ_BUSY_CU_CYCLES", "GRBM_GUI_ACTIVE", "GRBM_COUNT")
+
+
+def summarize_mfma(csv_path, simds=1024, xccs=8):
+    """Per-kernel MFMA figures from one rocprofv3 counter run of MFMA_COUNTERS:
+    MFMA busy fraction (busy SIMD-cycles over SIMDs x active cycles of one
+    XCC), bf16 MFMA flops per launch (MOPS x 512), VALU instructions per MFMA
+    instruction, and the shader clock the active cycles imply over the
+    dispatch's duration.  The counter values in the file are sums over all
+    XCCs, shader engines and SIMDs."""
+    import csv
+    import re
+
+    per = {}
+    for row in csv.DictReader(open(csv_path)):
+        m = re.search(r"(\w+_kernel)\b", row["Kernel_Name"])
+        if not m or not any(k in row["Kernel_Name"] for k in ("qlora", "nf4", "skinny")):
+            continue
+        d = per.setdefault(m.group(1), {}).setdefault(row["Dispatch_Id"], {})
+        d[row["Counter_Name"]] = d.get(row["Counter_Name"], 0.0) + float(row["Counter_Value"])
+        d["ns"] = int(row["End_Timestamp"]) - int(row["Start_Timestamp"])
+    out = {"_note": "from one rocprofv3 --pmc run of " + " ".join(MFMA_COUNTERS) + "; averages over the "
+                    "dispatches; busy = SQ_VALU_MFMA_BUSY_CYCLES / (SIMDs x GRBM_GUI_ACTIVE / XCCs); "
+                    "clock = GRBM_GUI_ACTIVE / XCCs / duration",
+           "simds": simds, "xccs": xccs}
+    for k, ds in sorted(per.items()):
+        ds = [d for d in ds.values() if all(c in d for c in MFMA_COUNTERS) and d["ns"] > 0]
+        if not ds:
+            continue
+        avg = lambda f: sum(f(d) for d in ds) / len(ds)
+        out[k] = {"dispatches": len(ds),
+                  "avg_us": avg(lambda d: d["ns"] / 1e3),
+                  "mfma_busy": avg(lambda d: d["SQ_VALU_MFMA_BUSY_CYCLES"] / (simds * d["GRBM_GUI_ACTIVE"] / xccs)),
+                  "bf16_mfma_tflop_per_launch": avg(lambda d: d["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512 / 1e12),
+                  "valu_per_mfma": avg(lambda d: d["SQ_INSTS_VALU"] / max(d["SQ_INSTS_MFMA"], 1.0)),
+                  "clock_ghz": avg(lambda d: d["GRBM_GUI_ACTIVE"] / xccs / d["ns"])}
+    return out
+
+
 def cpu_baseline(lin, M, r, alpha, dev_tensors, min_seconds=10.0, max_reps=20):
     """fp64 oracle fwd+bwd on one linear of the workload (host cores)."""
     import numpy as np
@@ -165,7 +205,13 @@ def main():
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="do not run: turn two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, "
                          "WRITE_SIZE) of a --copy-probe-mib run into profiles/traffic.json on stdout")
+    ap.add_argument("--summarize-mfma", metavar="CSV",
+                    help="do not run: per-kernel MFMA busy fraction, MFMA flops, VALU per MFMA and implied "
+                         "clock from a rocprofv3 --pmc counter_collection.csv of the MFMA_COUNTERS, on stdout")
     args = ap.parse_args()
+    if args.summarize_mfma:
+        print(json.dumps(summarize_mfma(args.summarize_mfma), indent=1))
+        return
     if args.summarize_pmc:
         print(json.dumps(summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.copy_probe_mib), indent=1))
         return
