@@ -93,19 +93,20 @@ __device__ __forceinline__ void map_tile(int tiles_c, int tiles_r, int& tc, int&
 }
 
 // Output: lane (lr, h) of wave (wr, wc) holds token row0 + 128 wr + 32 j + lr
-// and columns col0 + 128 wc + 32 i + 8 q + 4 h + 0..3.
-__device__ __forceinline__ void store_tile(const f32x16_t (&acc)[4][4], bf16_t* out, int64_t ld, int64_t rows,
+// and columns col0 + 32 FI wc + 32 i + 8 q + 4 h + 0..3.
+template <int FI>
+__device__ __forceinline__ void store_tile(const f32x16_t (&acc)[FI][4], bf16_t* out, int64_t ld, int64_t rows,
                                            int64_t cols, int64_t row0, int64_t col0) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wr = w >> 1, wc = w & 1, lr = lane & 31, h = lane >> 5;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < FI; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int64_t row = row0 + wr * 128 + 32 * j + lr;
       if (row >= rows) continue;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int64_t col = col0 + wc * 128 + 32 * i + 8 * q + 4 * h;
+        const int64_t col = col0 + wc * 32 * FI + 32 * i + 8 * q + 4 * h;
         if (col < cols)  // cols % 8 == 0: the four columns are all in range
           *reinterpret_cast<uint2*>(out + row * ld + col) =
               make_uint2(pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
@@ -1430,6 +1431,292 @@ __global__ __launch_bounds__(kThreads, 1) void nf4_dx_kernel(Nf4View W, const bf
   store_tile(acc, dX, K, M, K, m0, k0);
 }
 
+// ===========================================================================
+// dX half tile: 256 tokens x 128 columns, for the last round of a launch
+// whose full tiles would leave at least half of the CUs idle.  The ring,
+// the substep and its single barrier are those of nf4_dx_kernel with half
+// the weight columns: the weight half of a stage is 32 rows x 128 columns in
+// rows of 256 bytes (32-byte block b of row n at b ^ (n & 3)), each thread
+// dequantizes 16 weights (row t >> 3, columns 16 (t & 7) .. +15: 8 code
+// bytes and one block), and wave (wr, wc) owns tokens 128 wr .. +127 against
+// columns 64 wc .. +63, 16 MFMAs per stage.  Block b of the launch takes
+// half b & 1 of tile tile_base + b / 2.
+// ===========================================================================
+constexpr int kWRowH = 256;
+__device__ __forceinline__ int tposh(int n, int b) { return n * kWRowH + 32 * (b ^ (n & 3)); }
+__device__ __forceinline__ bf16x8_t tfragh(const char* p) {
+  const uint2 lo = rd_tr(p), hi = rd_tr(p + 4 * kWRowH);
+  return __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
+}
+
+struct CodesH {
+  uint2 c;
+  uint32_t q;
+  float s2;
+};
+struct FragsH {
+  bf16x8_t a0[2], b0[4], a1[2], b1[4];
+};
+
+__device__ __forceinline__ void dxh_load_codes(CodesH& c, const Dx& d, int stage) {
+  const uint32_t st = (uint32_t)min(stage, d.nsub - 1);
+  const u32x2_t v = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(d.cr, d.co, st * d.cstride, 0));
+  c.c = make_uint2(v.x, v.y);
+  c.q = __builtin_amdgcn_raw_buffer_load_b8(d.ar, d.ao, st * d.astride, 0);
+  const uint32_t g = (d.ablk + st * 32u * d.kb) >> 8;
+  c.s2 = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(d.gr, g * 4u, 0, 0));
+}
+// 16-byte chunk p (0, 1) of this thread's 16 columns, dequantized with T,
+// into ring buffer `buf`; chunk p of thread (n, jj) is chunk 2 jj + p of row n
+__device__ __forceinline__ void dxh_store_chunk(char* smem, int buf, int p, const bf16x8_t& v) {
+  const int t = threadIdx.x, n = t >> 3, ch = 2 * (t & 7) + p;
+  wr16(smem + buf * kStage + tposh(n, ch >> 1) + 16 * (ch & 1), __builtin_bit_cast(uint4, v));
+}
+
+// Slot x (0..15) of substep s: the MFMA of fragment pair (i, j) = ((x >> 2)
+// & 1, x & 3) of k16 step x >> 3.  Besides it:
+//   LDS reads     slots 0..7: step 1 of stage s (A fragment i in slots 2i,
+//                 2i + 1, B fragment j in slot 4 + j); slots 8..15: step 0
+//                 of stage s+1 in the same pattern, into the registers
+//                 step 0 of stage s has finished with
+//   global loads  slots 1, 3, 5, 7: dY of stage s+3; slots 9, 11, 13:
+//                 codes, absmax code and group scale of stage s+4
+//   LDS writes    slots 2, 6, 10, 14: dY of stage s+2 (loaded last
+//                 substep); slot 11: the first dequantized chunk of stage
+//                 s+2 (the second follows the last slot)
+//   VALU chunks   slots 0..5: table of the thread's row and block; slots
+//                 6..15: the two decodes, five chunks each
+template <int U8, int X>
+__device__ __forceinline__ void dxh_slot(char* smem, const Dx& d, int s, f32x16_t (&acc)[2][4], FragsH& F,
+                                         CodesH (&cs)[4], YRegs (&ys)[2], const int (&ao)[2], int bm, FragOffs fo,
+                                         TbState& tb, Nf4Table& T, DqState& dq, bf16x8_t& dqo) {
+  constexpr int U = U8 & 3;
+  constexpr int kk = X >> 3, i = (X >> 2) & 1, j = X & 3, y = X & 7;
+  const char* cur = smem + U * kStage;
+  const char* nxt = smem + ((U + 1) & 3) * kStage;
+  if constexpr (kk == 0)
+    acc[i][j] = mfma32x32x16(F.a0[i], F.b0[j], acc[i][j]);
+  else
+    acc[i][j] = mfma32x32x16(F.a1[i], F.b1[j], acc[i][j]);
+  // LDS reads: A fragment r = y / 2 is two transposed reads 4 rows apart
+  if constexpr (y < 4) {
+    constexpr int r = y >> 1, part = y & 1;
+    const char* p = (kk == 0 ? cur + 16 * kWRowH : nxt) + ao[r] + part * 4 * kWRowH;
+    const uint2 v = rd_tr(p);
+    bf16x8_t& a = kk == 0 ? F.a1[r] : F.a0[r];
+    uint4 w = __builtin_bit_cast(uint4, a);
+    if constexpr (part == 0) {
+      w.x = v.x;
+      w.y = v.y;
+    } else {
+      w.z = v.x;
+      w.w = v.y;
+    }
+    a = __builtin_bit_cast(bf16x8_t, w);
+  } else {
+    if constexpr (kk == 0)
+      F.b1[y - 4] = rd16(cur + kOp + bm + (y - 4) * 2048 + fo.o1);
+    else
+      F.b0[y - 4] = rd16(nxt + kOp + bm + (y - 4) * 2048 + fo.o0);
+  }
+  // global loads
+  if constexpr (kk == 0 && (y & 1)) {
+    const uint32_t soff = (uint32_t)min(s + 3, d.nsub - 1) * 64u;
+    ys[U8 & 1].v[y >> 1] = buf_load16(d.yr, d.yo[y >> 1], soff);
+  }
+  if constexpr (X == 9 || X == 11 || X == 13) {
+    const uint32_t st = (uint32_t)min(s + 4, d.nsub - 1);
+    if constexpr (X == 9) {
+      const u32x2_t v =
+          __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(d.cr, d.co, st * d.cstride, 0));
+      cs[U].c = make_uint2(v.x, v.y);
+    }
+    if constexpr (X == 11) cs[U].q = __builtin_amdgcn_raw_buffer_load_b8(d.ar, d.ao, st * d.astride, 0);
+    if constexpr (X == 13) {
+      const uint32_t g = (d.ablk + st * 32u * d.kb) >> 8;
+      cs[U].s2 = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(d.gr, g * 4u, 0, 0));
+    }
+  }
+  // LDS writes
+  if constexpr ((X & 3) == 2)
+    wr16(smem + ((U + 2) & 3) * kStage + kOp + d.ypos[X >> 2], ys[(U8 + 1) & 1].v[X >> 2]);
+  if constexpr (X == 11) dxh_store_chunk(smem, (U + 2) & 3, (threadIdx.x >> 2) & 1, dqo);
+  // VALU chunks: stage s+2 from code set (U + 2) & 3
+  {
+    const CodesH& pc = cs[(U + 2) & 3];
+    if constexpr (X < 6) {
+      tb_chunk<X>(tb, Scale{pc.q, pc.s2}, T);
+    } else {
+      constexpr int dd = (X - 6) / 5, kc = (X - 6) % 5;
+      // decode dd is chunk dd ^ flip: a select between the two code words as
+      // values (a select between the fields would go through scratch)
+      const bool flip = (threadIdx.x & 4) != 0;
+      const uint32_t cx = pc.c.x, cy = pc.c.y;
+      const uint32_t word = (flip != (dd != 0)) ? cy : cx;
+      dq_chunk<kc>(dq, word, T, dqo);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int U8>
+__device__ __forceinline__ void dxh_substep(char* smem, const Dx& d, int s, f32x16_t (&acc)[2][4], FragsH& F,
+                                            CodesH (&cs)[4], YRegs (&ys)[2], const int (&ao)[2], int bm,
+                                            FragOffs fo) {
+  constexpr int U = U8 & 3;
+  __builtin_amdgcn_sched_barrier(0);
+  QLORA_WAIT(63, 0);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  TbState tb;
+  Nf4Table T;
+  DqState dq;
+  bf16x8_t dqo;
+#define QLORA_DXH_SLOT(x) dxh_slot<U8, x>(smem, d, s, acc, F, cs, ys, ao, bm, fo, tb, T, dq, dqo)
+#define QLORA_DXH_SLOT4(x) QLORA_DXH_SLOT(x); QLORA_DXH_SLOT(x + 1); QLORA_DXH_SLOT(x + 2); QLORA_DXH_SLOT(x + 3)
+  QLORA_DXH_SLOT4(0); QLORA_DXH_SLOT4(4); QLORA_DXH_SLOT4(8); QLORA_DXH_SLOT4(12);
+#undef QLORA_DXH_SLOT4
+#undef QLORA_DXH_SLOT
+  // the second dequantized chunk of stage s+2
+  dxh_store_chunk(smem, (U + 2) & 3, ((threadIdx.x >> 2) & 1) ^ 1, dqo);
+}
+
+__global__ __launch_bounds__(kThreads, 1) void nf4_dx_half_kernel(Nf4View W, const bf16_t* __restrict__ dY,
+                                                                  int64_t M, const bf16_t* __restrict__ G,
+                                                                  const bf16_t* __restrict__ Al, int r, float s,
+                                                                  bf16_t* __restrict__ dX, int tiles_k,
+                                                                  int tile_base) {
+  extern __shared__ __align__(16) char smem[];
+  const int tile = tile_base + (int)(blockIdx.x >> 1);
+  const int tk = tile % tiles_k, tm = tile / tiles_k;
+  const int64_t k0 = (int64_t)tk * kTile + 128 * (int64_t)(blockIdx.x & 1), m0 = (int64_t)tm * kTile;
+  const int t = threadIdx.x, lane = t & 63, wr = (t >> 6) >> 1, wc = (t >> 6) & 1;
+  const int64_t N = W.N, K = W.K;
+
+  Dx d;
+  d.yr = make_rsrc(dY, (uint32_t)(M * N * 2));
+  d.cr = make_rsrc(W.codes, (uint32_t)(N * K / 2));
+  d.ar = make_rsrc(W.absmax_q, (uint32_t)(N * (K >> 6)));
+  d.gr = make_rsrc(W.group_scale, (uint32_t)(((N * (K >> 6) + 255) >> 8) * 4));
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int idx = t + kThreads * q, row = idx >> 2, c = idx & 3;
+    const int64_t ym = min(m0 + row, M - 1);
+    d.yo[q] = (uint32_t)(ym * N * 2 + c * 16);
+    d.ypos[q] = spos(row, c);
+  }
+  {
+    const int64_t kc = min(k0 + 16 * (t & 7), K - 16);   // columns past K: any in-range block
+    const int64_t n = t >> 3;
+    d.kb = (uint32_t)(K >> 6);
+    d.co = (uint32_t)(n * (K / 2) + kc / 2);
+    d.ao = (uint32_t)(n * (K >> 6) + (kc >> 6));
+    d.ablk = d.ao;
+    d.cstride = (uint32_t)(32 * (K / 2));
+    d.astride = (uint32_t)(32 * (K >> 6));
+  }
+  d.nsub = (int)((N + 31) >> 5);
+  // A fragment i: as a source lane of its 16-lane group (g, sl) a lane reads
+  // row 8 (g >> 1) + (sl >> 2) and columns 64 wc + 32 i + 16 (g & 1) + 4 (sl & 3)
+  int ao[2];
+  {
+    const int g = lane >> 4, sl = lane & 15, n0 = 8 * (g >> 1) + (sl >> 2);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) ao[i] = tposh(n0, wc * 4 + 2 * i + (g & 1)) + 8 * (sl & 3);
+  }
+  const FragOffs fo = frag_offs(lane);
+  const int bm = wr * 128 * 64;
+
+  f32x16_t acc[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+  CodesH cs[4];
+  YRegs ys[2];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) dxh_load_codes(cs[p], d, p);
+  dx_load_y(ys[0], d, 0);
+  dx_store_y(smem, d, ys[0], 0);
+  dx_load_y(ys[0], d, 1);
+  dx_store_y(smem, d, ys[0], 1);
+  dx_load_y(ys[1], d, 2);   // stored by substep 0
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const Nf4Table T = make_table(block_scale(cs[p].q, cs[p].s2));
+    const int flip = (t >> 2) & 1;
+    const uint32_t cx = cs[p].c.x, cy = cs[p].c.y;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      uint32_t o[4];
+      dequant8((k ^ flip) ? cy : cx, T, o);
+      dxh_store_chunk(smem, p, k ^ flip, __builtin_bit_cast(bf16x8_t, make_uint4(o[0], o[1], o[2], o[3])));
+    }
+  }
+  QLORA_WAIT(0, 0);
+  __builtin_amdgcn_s_barrier();
+  FragsH F;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) F.a0[i] = tfragh(smem + ao[i]);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) F.b0[j] = rd16(smem + kOp + bm + j * 2048 + fo.o0);
+  int st = 0;
+#define QLORA_DXH_SUB(u) dxh_substep<u>(smem, d, st + u, acc, F, cs, ys, ao, bm, fo)
+  for (; st + 8 <= d.nsub; st += 8) {
+    QLORA_DXH_SUB(0); QLORA_DXH_SUB(1); QLORA_DXH_SUB(2); QLORA_DXH_SUB(3);
+    QLORA_DXH_SUB(4); QLORA_DXH_SUB(5); QLORA_DXH_SUB(6); QLORA_DXH_SUB(7);
+  }
+  const int rem = d.nsub - st;
+  if (rem >= 1) QLORA_DXH_SUB(0);
+  if (rem >= 2) QLORA_DXH_SUB(1);
+  if (rem >= 3) QLORA_DXH_SUB(2);
+  if (rem >= 4) QLORA_DXH_SUB(3);
+  if (rem >= 5) QLORA_DXH_SUB(4);
+  if (rem >= 6) QLORA_DXH_SUB(5);
+  if (rem >= 7) QLORA_DXH_SUB(6);
+#undef QLORA_DXH_SUB
+  QLORA_WAIT(0, 0);
+  __builtin_amdgcn_s_barrier();
+
+  if (r > 0) {
+    // acc += (s G) A over the rank, 32 at a time (as in nf4_dx_kernel)
+    for (int j0 = 0; j0 < r; j0 += 32) {
+      char* wb = smem;
+      char* yb = smem + kOp;
+      {
+        const int n = t >> 3, jj = t & 7, flip = (t >> 2) & 1;
+        const int64_t row = j0 + n;
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          const int p = k ^ flip, ch = 2 * jj + p;
+          const int64_t col = k0 + 8 * ch;
+          uint4 v = make_uint4(0u, 0u, 0u, 0u);
+          if (row < r && col < K) v = *reinterpret_cast<const uint4*>(Al + row * K + col);
+          wr16(wb + tposh(n, ch >> 1) + 16 * (ch & 1), v);
+        }
+      }
+      tail_tokens(yb, G, M, r, m0, j0, s);
+      QLORA_WAIT(0, 0);
+      __builtin_amdgcn_s_barrier();
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const int o = kk ? fo.o1 : fo.o0;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) F.a0[i] = tfragh(wb + ao[i] + kk * 16 * kWRowH);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) F.b0[j] = rd16(yb + bm + j * 2048 + o);
+        mfma_block<2, 4>(acc, F.a0, F.b0);
+      }
+      QLORA_WAIT(0, 0);
+      __builtin_amdgcn_s_barrier();
+    }
+  }
+  store_tile(acc, dX, K, M, K, m0, k0);
+}
+
 }  // namespace
 
 hipError_t launch_fwd(const Nf4View& W, const bf16_t* X, int64_t M, const bf16_t* U, const bf16_t* B, int r,
@@ -1481,11 +1768,24 @@ hipError_t launch_dx(const Nf4View& W, const bf16_t* dY, int64_t M, const bf16_t
                      float s, bf16_t* dX, hipStream_t st) {
   const int tiles_k = (int)((W.K + kTile - 1) / kTile);
   const int tiles_m = (int)((M + kTile - 1) / kTile);
+  const int tiles = tiles_k * tiles_m;
+  // As in the forward: a last round that would leave at least half of the
+  // CUs idle runs as 128-column halves in a second launch.
+  const int cus = device_cu_count();
+  const int rest = tiles % cus;
+  const int main_tiles = (tiles > cus && rest > 0 && 2 * rest <= cus) ? tiles - rest : tiles;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&nf4_dx_kernel),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsDx);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(nf4_dx_kernel, dim3(tiles_k * tiles_m), dim3(kThreads), kLdsDx, st, W, dY, M, G, A, r, s, dX,
+  hipLaunchKernelGGL(nf4_dx_kernel, dim3(main_tiles), dim3(kThreads), kLdsDx, st, W, dY, M, G, A, r, s, dX,
                      tiles_k, tiles_m);
+  e = hipGetLastError();
+  if (e != hipSuccess || main_tiles == tiles) return e;
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&nf4_dx_half_kernel),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsDx);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(nf4_dx_half_kernel, dim3(2 * (tiles - main_tiles)), dim3(kThreads), kLdsDx, st, W, dY, M, G, A,
+                     r, s, dX, tiles_k, main_tiles);
   return hipGetLastError();
 }
 

@@ -79,6 +79,8 @@ def test_small_config():
     (513, 264, 320, 128),      # largest rank
     (64, 8, 64, 8),            # minimum N / K / r
     (4300, 4104, 128, 16),     # 17 x 17 tiles: on 256 CUs the 33-tile last forward round runs as 128-row halves
+    (4300, 360, 4160, 16),     # 17 x 17 dX tiles: the 33-tile last round runs as 128-column halves, the last
+                               # k tile is a quarter full, and the contraction has a ragged 12-stage tail
 ])
 def test_shapes(M, N, K, r):
     _run(_case(M, N, K, r, seed=M + N + K + r), f"M{M} N{N} K{K} r{r}")
