@@ -77,8 +77,11 @@ def traffic_for(kernel):
     return e.get("hbm_bytes_per_launch")
 
 
+# rocprofv3 kernel name -> bench kernel; a launch of the fused GEMMs may add a
+# half-tile tail dispatch, whose bytes count towards that launch
 TRAFFIC_KERNELS = {"nf4_fwd_r_kernel": "fwd_kernel", "nf4_fwd_kernel": "fwd_kernel", "nf4_dx_kernel": "dx_kernel",
                    "quantize_kernel": "quantize_kernel", "nf4_gemv_kernel": "gemv_kernel"}
+TAIL_KERNELS = {"nf4_fwd_n32_kernel": "fwd_kernel", "nf4_dx_half_kernel": "dx_kernel"}
 
 
 def summarize_pmc(fetch_csv, write_csv, copy_mib):
@@ -100,21 +103,26 @@ def summarize_pmc(fetch_csv, write_csv, copy_mib):
                 key = "copy_probe"
             acc.setdefault(key, {}).setdefault(row["Dispatch_Id"], 0.0)
             acc[key][row["Dispatch_Id"]] += float(row["Counter_Value"])
-        return {k: sum(v.values()) / len(v) * 1024.0 for k, v in acc.items()}   # bytes per dispatch
+        # bytes summed over the dispatches, and the dispatch count
+        return {k: (sum(v.values()) * 1024.0, len(v)) for k, v in acc.items()}
 
     fetch = per_kernel(fetch_csv, "FETCH_SIZE")
     write = per_kernel(write_csv, "WRITE_SIZE")
     probe = copy_mib * 1024 * 1024
-    f_scale = probe / fetch["copy_probe"]
-    w_scale = probe / write["copy_probe"]
-    out = {"_note": "HBM bytes per launch = FETCH_SIZE x fetch_scale + WRITE_SIZE x write_scale, averaged over "
-                    "the dispatches of one bench run; scales from an elementwise copy of copy_probe_bytes",
+    f_scale = probe / (fetch["copy_probe"][0] / fetch["copy_probe"][1])
+    w_scale = probe / (write["copy_probe"][0] / write["copy_probe"][1])
+    out = {"_note": "HBM bytes per launch = FETCH_SIZE x fetch_scale + WRITE_SIZE x write_scale, summed over the "
+                    "dispatches of one bench run (a fused GEMM's half-tile tail dispatches included) and divided by "
+                    "the number of launches; scales from an elementwise copy of copy_probe_bytes",
            "copy_probe_bytes": probe, "fetch_scale": f_scale, "write_scale": w_scale}
     for k, name in TRAFFIC_KERNELS.items():
         if k in fetch and k in write:
-            out[name] = {"source_digest": source_digest(), "fetch_bytes_per_launch": fetch[k] * f_scale,
-                         "write_bytes_per_launch": write[k] * w_scale,
-                         "hbm_bytes_per_launch": fetch[k] * f_scale + write[k] * w_scale}
+            tails = [t for t, n in TAIL_KERNELS.items() if n == name]
+            fb = fetch[k][0] + sum(fetch[t][0] for t in tails if t in fetch)
+            wb = write[k][0] + sum(write[t][0] for t in tails if t in write)
+            fpl, wpl = fb / fetch[k][1] * f_scale, wb / write[k][1] * w_scale
+            out[name] = {"source_digest": source_digest(), "fetch_bytes_per_launch": fpl,
+                         "write_bytes_per_launch": wpl, "hbm_bytes_per_launch": fpl + wpl}
     return out
 
 
