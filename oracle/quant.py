@@ -34,6 +34,7 @@ import numpy as np
 
 from .bf16 import bf16_bits_to_f32, f32_to_bf16_bits
 from .nf4 import nf4_levels, q8_levels
+from .codebooks import levels as codebook_levels, zero_code
 
 BLOCKSIZE = 64
 GROUP_BLOCKS = 256
@@ -74,11 +75,15 @@ def storage_sizes(numel):
     return (numel + 1) // 2, nb, 4 * ng
 
 
-def quantize(w_bits):
+def quantize(w_bits, codebook="nf4"):
     """Quantize bf16 weights (uint16 bit patterns, row-major, any shape).
 
     Returns (codes uint8 [ceil(n/2)], absmax_q uint8 [nb], s2 float32 [ng]).
+    ``codebook`` selects the 4-bit levels: "nf4" (the method's), or "fp4"
+    and "int4" (the formats the pages compare it with; readings R15, R16 in
+    codebooks.py), all quantized the same way.
     """
+    lv = codebook_levels(codebook)
     w = bf16_bits_to_f32(np.asarray(w_bits).ravel())
     n = w.size
     nb = -(-n // BLOCKSIZE)
@@ -90,12 +95,13 @@ def quantize(w_bits):
     blocks = padded.reshape(nb, BLOCKSIZE)
     absmax = np.max(np.abs(blocks), axis=1)                      # fp32, exact
 
-    # normalise and encode; blocks with absmax 0 keep code 7 (R6)
-    codes_full = np.full(nb * BLOCKSIZE, 7, dtype=np.uint8)
+    # normalise and encode; blocks with absmax 0 keep the code of the level 0
+    # (7 for NF4: R6)
+    codes_full = np.full(nb * BLOCKSIZE, zero_code(lv), dtype=np.uint8)
     nz = absmax > 0
     if np.any(nz):
         x = (blocks[nz] / absmax[nz, None]).astype(np.float32)    # IEEE fp32 division
-        codes_full.reshape(nb, BLOCKSIZE)[nz] = nf4_encode(x).reshape(-1, BLOCKSIZE)
+        codes_full.reshape(nb, BLOCKSIZE)[nz] = _nearest_index(x, lv).reshape(-1, BLOCKSIZE)
     codes_el = codes_full[:n]
 
     # pack two codes per byte, element 2j in the low nibble (R8)
@@ -116,7 +122,7 @@ def quantize(w_bits):
     return packed, absmax_q, s2
 
 
-def dequant(codes, absmax_q, s2, numel):
+def dequant(codes, absmax_q, s2, numel, codebook="nf4"):
     """Dequantize to bf16 bit patterns (uint16, flat, `numel` elements)."""
     codes = np.asarray(codes, dtype=np.uint8)
     el = np.empty(2 * codes.size, dtype=np.uint8)
@@ -126,7 +132,7 @@ def dequant(codes, absmax_q, s2, numel):
     blk = np.arange(numel) // BLOCKSIZE
     grp = blk // GROUP_BLOCKS
     q8 = q8_levels()
-    lv = nf4_levels()
+    lv = codebook_levels(codebook)
     t = (q8[np.asarray(absmax_q)[blk]] * np.asarray(s2, dtype=np.float32)[grp]).astype(np.float32)
     w = (lv[el] * t).astype(np.float32)
     return f32_to_bf16_bits(w)
