@@ -198,6 +198,37 @@ def cpu_baseline(lin, M, r, alpha, dev_tensors, min_seconds=10.0, max_reps=20):
             "host_cpu_count": os.cpu_count()}
 
 
+def codebook_study(L, dev, q_bytes, reps=5):
+    """Quantize the layer set with each 4-bit codebook (HBM rate, same bytes
+    as NF4) and the relative RMS error of its dequantized q weight: the
+    pages' comparison of NF4 with FP4 and Int4, on the synthetic weights."""
+    import torch
+    from bit_quantized_finetuning_nf4_amd import ops
+    qs = [ops.QuantizedWeight.empty(o["N"], o["K"], dev) for o in L]
+    W0 = L[0]["W"]
+    back = torch.empty_like(W0)
+    ref = W0.double()
+    res = {}
+    for cb in ("nf4", "fp4", "int4"):
+        for o, q in zip(L, qs):
+            ops.quantize(o["W"], out=q, codebook=cb)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            for o, q in zip(L, qs):
+                ops.quantize(o["W"], out=q, codebook=cb)
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / reps
+        ops.dequant(qs[0], out=back, codebook=cb)
+        err = ((back.double() - ref).pow(2).mean().sqrt() / ref.pow(2).mean().sqrt()).item()
+        res[cb] = {"quantize_ms": ms, "quantize_gbps": q_bytes / (ms * 1e-3) / 1e9,
+                   f"rel_rmse_{L[0]['name']}": err}
+    del qs, back, ref
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -207,6 +238,8 @@ def main():
     ap.add_argument("--decode-layers", type=int, default=80)
     ap.add_argument("--decode-passes", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-codebook-study", action="store_true",
+                    help="skip quantizing the layer set with FP4 and Int4 after the timed steps")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after the timed steps, run one elementwise copy (negation) of this many MiB: "
                          "a kernel of known traffic for scaling the FETCH_SIZE / WRITE_SIZE counters")
@@ -366,6 +399,9 @@ def main():
         "layer_gemv_gbps": g_bytes / (ph["decode_gemv"] * 1e-3) / 1e9,
     }
     log(f"[bench] step {ms_step:.3f} ms, {value:.1f} TFLOP/s; phases {ph}")
+    if not args.no_codebook_study:
+        out["codebooks"] = codebook_study(L, dev, q_bytes)
+        log(f"[bench] codebooks {out['codebooks']}")
 
     # ---- 80-layer batch-1 decode pass (about 65e9 weights) ----
     if args.decode_layers > 0:

@@ -163,6 +163,26 @@ void qlora_nf4_levels(float out[16]) {
   std::memcpy(out, bits, sizeof(bits));
 }
 
+qlora_status qlora_codebook_levels(qlora_codebook cb, float out[16]) {
+  // Same bit patterns as the device tables (device.h), where the
+  // constructions are given.
+  static const uint32_t fp4[16] = {
+      0xBF800000u, 0xBF2AAAABu, 0xBF000000u, 0xBEAAAAABu, 0xBE800000u, 0xBE2AAAABu,
+      0xBDAAAAABu, 0x00000000u, 0x00000000u, 0x3DAAAAABu, 0x3E2AAAABu, 0x3E800000u,
+      0x3EAAAAABu, 0x3F000000u, 0x3F2AAAABu, 0x3F800000u};
+  static const uint32_t int4[16] = {
+      0xBF924925u, 0xBF800000u, 0xBF5B6DB7u, 0xBF36DB6Eu, 0xBF124925u, 0xBEDB6DB7u,
+      0xBE924925u, 0xBE124925u, 0x00000000u, 0x3E124925u, 0x3E924925u, 0x3EDB6DB7u,
+      0x3F124925u, 0x3F36DB6Eu, 0x3F5B6DB7u, 0x3F800000u};
+  if (!out) return QLORA_E_NULL;
+  switch (cb) {
+    case QLORA_CODEBOOK_NF4: qlora_nf4_levels(out); return QLORA_OK;
+    case QLORA_CODEBOOK_FP4: std::memcpy(out, fp4, sizeof(fp4)); return QLORA_OK;
+    case QLORA_CODEBOOK_INT4: std::memcpy(out, int4, sizeof(int4)); return QLORA_OK;
+  }
+  return QLORA_E_UNSUPPORTED;
+}
+
 qlora_status qlora_sizes(int64_t rows, int64_t cols, int32_t blocksize, int32_t group_blocks,
                          size_t* codes_bytes, size_t* absmax_q_bytes, size_t* scale_bytes) {
   if (rows <= 0 || cols <= 0) return QLORA_E_SHAPE;
@@ -195,7 +215,11 @@ size_t qlora_workspace_bytes(qlora_op op, int64_t M, int64_t N, int64_t K, int32
   return 0;
 }
 
-qlora_status qlora_quantize(const uint16_t* W, const qlora_nf4_weight* q, void* stream) {
+static bool known_codebook(int cb) { return cb == QLORA_CODEBOOK_NF4 || cb == QLORA_CODEBOOK_FP4 || cb == QLORA_CODEBOOK_INT4; }
+
+qlora_status qlora_quantize_codebook(const uint16_t* W, const qlora_nf4_weight* q, qlora_codebook cb,
+                                     void* stream) {
+  if (!known_codebook(cb)) return QLORA_E_UNSUPPORTED;
   qlora_status st = check_weight(q);
   if (st != QLORA_OK) return st;
   if (!W) return QLORA_E_NULL;
@@ -203,10 +227,16 @@ qlora_status qlora_quantize(const uint16_t* W, const qlora_nf4_weight* q, void* 
   if (q->rows > INT64_MAX / q->cols) return QLORA_E_SHAPE;
   const int64_t n = q->rows * q->cols;
   if ((n + 16383) / 16384 > 0x7FFFFFFF) return QLORA_E_SHAPE;
-  return hip_status(launch_quantize(W, n, q->codes, q->absmax_q, q->group_scale, (hipStream_t)stream));
+  return hip_status(launch_quantize(W, n, q->codes, q->absmax_q, q->group_scale, (int)cb, (hipStream_t)stream));
 }
 
-qlora_status qlora_dequant(const qlora_nf4_weight* q, uint16_t* W_out, void* stream) {
+qlora_status qlora_quantize(const uint16_t* W, const qlora_nf4_weight* q, void* stream) {
+  return qlora_quantize_codebook(W, q, QLORA_CODEBOOK_NF4, stream);
+}
+
+qlora_status qlora_dequant_codebook(const qlora_nf4_weight* q, qlora_codebook cb, uint16_t* W_out,
+                                    void* stream) {
+  if (!known_codebook(cb)) return QLORA_E_UNSUPPORTED;
   qlora_status st = check_weight(q);
   if (st != QLORA_OK) return st;
   if (!W_out) return QLORA_E_NULL;
@@ -214,7 +244,11 @@ qlora_status qlora_dequant(const qlora_nf4_weight* q, uint16_t* W_out, void* str
   if (q->rows > INT64_MAX / q->cols) return QLORA_E_SHAPE;
   const int64_t n = q->rows * q->cols;
   if ((n + 63) / 64 / 256 > 0x7FFFFFFF) return QLORA_E_SHAPE;
-  return hip_status(launch_dequant(q->codes, q->absmax_q, q->group_scale, n, W_out, (hipStream_t)stream));
+  return hip_status(launch_dequant(q->codes, q->absmax_q, q->group_scale, n, (int)cb, W_out, (hipStream_t)stream));
+}
+
+qlora_status qlora_dequant(const qlora_nf4_weight* q, uint16_t* W_out, void* stream) {
+  return qlora_dequant_codebook(q, QLORA_CODEBOOK_NF4, W_out, stream);
 }
 
 qlora_status qlora_linear_fwd(const qlora_nf4_weight* W, const uint16_t* X, int64_t M, const uint16_t* A,

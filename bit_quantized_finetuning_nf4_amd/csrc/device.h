@@ -35,6 +35,46 @@ __constant__ constexpr uint32_t kNf4ThreshBits[15] = {
     0xBE0D38B9u, 0xBD3A7869u, 0x3D22FB01u, 0x3DF6485Fu, 0x3E5067DCu,
     0x3E9582D1u, 0x3EC753F5u, 0x3F006D01u, 0x3F248DACu, 0x3F5C89D8u};
 
+// The two other 4-bit codebooks that the pages compare NF4 with (deepfa.ir
+// blog, "1. 4-bit NormalFloat (NF4)" and its results list), quantized and
+// dequantized the same way.  FP4 is E2M1 (sign, two exponent bits with
+// bias 1, one mantissa bit: +-{0, 0.5, 1, 1.5, 2, 3, 4, 6}) divided by 6;
+// its two zeros are both +0 (codes 7 and 8).  Int4 is k/7 for the
+// two's-complement k = -8..7.  Levels rounded to fp32, ascending.
+__constant__ constexpr uint32_t kFp4LevelBits[16] = {
+    0xBF800000u, 0xBF2AAAABu, 0xBF000000u, 0xBEAAAAABu, 0xBE800000u, 0xBE2AAAABu,
+    0xBDAAAAABu, 0x00000000u, 0x00000000u, 0x3DAAAAABu, 0x3E2AAAABu, 0x3E800000u,
+    0x3EAAAAABu, 0x3F000000u, 0x3F2AAAABu, 0x3F800000u};
+__constant__ constexpr uint32_t kInt4LevelBits[16] = {
+    0xBF924925u, 0xBF800000u, 0xBF5B6DB7u, 0xBF36DB6Eu, 0xBF124925u, 0xBEDB6DB7u,
+    0xBE924925u, 0xBE124925u, 0x00000000u, 0x3E124925u, 0x3E924925u, 0x3EDB6DB7u,
+    0x3F124925u, 0x3F36DB6Eu, 0x3F5B6DB7u, 0x3F800000u};
+// Their thresholds, as for NF4; FP4's zero pair gets the threshold of the
+// next distinct pair twice (T_7 = T_8), so that code 8 is never produced
+// (ties go to the lower index).
+__constant__ constexpr uint32_t kFp4ThreshBits[15] = {
+    0xBF555556u, 0xBF155556u, 0xBED55556u, 0xBE955556u, 0xBE555556u,
+    0xBE000001u, 0xBD2AAAABu, 0x3D2AAAABu, 0x3D2AAAABu, 0x3E000000u,
+    0x3E555555u, 0x3E955555u, 0x3ED55555u, 0x3F155555u, 0x3F555555u};
+__constant__ constexpr uint32_t kInt4ThreshBits[15] = {
+    0xBF892493u, 0xBF6DB6DCu, 0xBF492493u, 0xBF24924Au, 0xBF000001u,
+    0xBEB6DB6Eu, 0xBE5B6DB8u, 0xBD924925u, 0x3D924925u, 0x3E5B6DB7u,
+    0x3EB6DB6Eu, 0x3F000000u, 0x3F249249u, 0x3F492492u, 0x3F6DB6DBu};
+
+// Codebook selectors (the values of qlora_codebook).
+constexpr int kCbNf4 = 0, kCbFp4 = 1, kCbInt4 = 2;
+template <int CB>
+__device__ __forceinline__ uint32_t cb_level_bits(int i) {
+  return CB == kCbNf4 ? kNf4LevelBits[i] : CB == kCbFp4 ? kFp4LevelBits[i] : kInt4LevelBits[i];
+}
+template <int CB>
+__device__ __forceinline__ uint32_t cb_thresh_bits(int i) {
+  return CB == kCbNf4 ? kNf4ThreshBits[i] : CB == kCbFp4 ? kFp4ThreshBits[i] : kInt4ThreshBits[i];
+}
+// The code of an all-zero block: the lowest index of a zero level.
+template <int CB>
+constexpr uint32_t cb_zero_code() { return CB == kCbInt4 ? 8u : 7u; }
+
 __device__ __forceinline__ float u2f(uint32_t u) { return __builtin_bit_cast(float, u); }
 __device__ __forceinline__ uint32_t f2u(float f) { return __builtin_bit_cast(uint32_t, f); }
 
@@ -79,11 +119,12 @@ struct Nf4Table {
   uint32_t hi[4];
 };
 
+template <int CB = kCbNf4>
 __device__ __forceinline__ Nf4Table make_table(float t) {
   uint32_t p[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i)
-    p[i] = pack_bf16x2(u2f(kNf4LevelBits[2 * i]) * t, u2f(kNf4LevelBits[2 * i + 1]) * t);
+    p[i] = pack_bf16x2(u2f(cb_level_bits<CB>(2 * i)) * t, u2f(cb_level_bits<CB>(2 * i + 1)) * t);
   Nf4Table T;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {

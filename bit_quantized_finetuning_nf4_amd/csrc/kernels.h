@@ -19,10 +19,11 @@ struct Nf4View {
 // Compute units of the current device (256 if the query fails).
 int device_cu_count();
 
+// codebook: 0 NF4, 1 FP4, 2 Int4 (the values of qlora_codebook)
 hipError_t launch_quantize(const bf16_t* W, int64_t numel, uint8_t* codes, uint8_t* absmax_q,
-                           float* group_scale, hipStream_t s);
+                           float* group_scale, int codebook, hipStream_t s);
 hipError_t launch_dequant(const uint8_t* codes, const uint8_t* absmax_q, const float* group_scale,
-                          int64_t numel, bf16_t* out, hipStream_t s);
+                          int64_t numel, int codebook, bf16_t* out, hipStream_t s);
 
 // Y = X deq(W)^T + s * U * B^T  (U already holds X A^T in bf16; r may be 0)
 hipError_t launch_fwd(const Nf4View& W, const bf16_t* X, int64_t M, const bf16_t* U, const bf16_t* B,

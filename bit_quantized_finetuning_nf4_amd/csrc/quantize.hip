@@ -11,8 +11,9 @@
 
 namespace qlora {
 
-// NF4 codes of eight fp32 values x = RN32(w / a): c = #{k : x > T_k} over
-// the 15 ascending thresholds, by binary search with the code's bits found
+// 4-bit codes of eight fp32 values x = RN32(w / a): c = #{k : x > T_k} over
+// the 15 ascending thresholds of codebook CB (FP4's has one threshold twice,
+// which the count handles alike), by binary search with the code's bits found
 // most significant first.  The first step compares with T_7 (a constant),
 // the others with T_{8c+3}, T_{4c+1}, T_{2c} from an LDS copy of the table:
 // 4 compares instead of 15.  A compare is the sign of T - x: the difference
@@ -22,11 +23,12 @@ namespace qlora {
 // eight searches advance step by step together, so that each step's eight
 // LDS reads are in flight at once.
 __device__ __forceinline__ uint32_t gt_bit(float t, float x) { return __builtin_bit_cast(uint32_t, t - x); }
+template <int CB>
 __device__ __forceinline__ uint32_t nf4_codes8(const float (&x)[8], const float* thr) {
   uint32_t c[8];
   float t[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) c[i] = gt_bit(u2f(kNf4ThreshBits[7]), x[i]) >> 31;
+  for (int i = 0; i < 8; ++i) c[i] = gt_bit(u2f(cb_thresh_bits<CB>(7)), x[i]) >> 31;
 #pragma unroll
   for (int i = 0; i < 8; ++i) t[i] = thr[8 * c[i] + 3];
 #pragma unroll
@@ -73,6 +75,7 @@ __device__ __forceinline__ uint32_t q8_code(float y) {
 // One workgroup of 256 threads per group of 256 blocks.  Each lane encodes
 // 8 consecutive weights per pass; 8 lanes form one block, 32 blocks per
 // pass, 8 passes per group.  Block absmaxes go to LDS for the second level.
+template <int CB>
 __global__ __launch_bounds__(256) void quantize_kernel(const bf16_t* __restrict__ W, int64_t numel,
                                                        uint8_t* __restrict__ codes,
                                                        uint8_t* __restrict__ absmax_q,
@@ -81,7 +84,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(const bf16_t* __restrict_
   __shared__ float red[8];
   __shared__ float thr[16];
   const int tid = threadIdx.x;
-  if (tid < 15) thr[tid] = u2f(kNf4ThreshBits[tid]);
+  if (tid < 15) thr[tid] = u2f(cb_thresh_bits<CB>(tid));
   __syncthreads();
   const int64_t g = blockIdx.x;
   const int64_t gbase = g * (int64_t)kGroupBlocks * kBlock;
@@ -126,7 +129,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(const bf16_t* __restrict_
     const int blk = pass * 32 + (tid >> 3);
     if ((tid & 7) == 0) amax[blk] = m;
 
-    uint32_t packed = 0x77777777u;
+    uint32_t packed = cb_zero_code<CB>() * 0x11111111u;   // all-zero block: the code of the level 0
     if (m > 0.0f) {
       // x = RN32(w / a) from the fp64 product w * r, r ~ 1/a.  w and a are
       // bf16 (at most 8 significant bits) and an fp32 rounding boundary B is
@@ -144,7 +147,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(const bf16_t* __restrict_
       float x[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) x[i] = (float)((double)f[i] * r);
-      packed = nf4_codes8(x, thr);
+      packed = nf4_codes8<CB>(x, thr);
     }
     if (e0 + 8 <= numel) {
       *reinterpret_cast<uint32_t*>(codes + (e0 >> 1)) = packed;
@@ -181,6 +184,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(const bf16_t* __restrict_
 }
 
 // One lane per block of 64 weights: 32 bytes of codes -> 128 bytes of bf16.
+template <int CB>
 __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict__ codes,
                                                       const uint8_t* __restrict__ absmax_q,
                                                       const float* __restrict__ group_scale,
@@ -189,7 +193,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict_
   const int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (b >= nb) return;
   const float t = block_scale(absmax_q[b], group_scale[b / kGroupBlocks]);
-  const Nf4Table T = make_table(t);
+  const Nf4Table T = make_table<CB>(t);
   const int64_t e0 = b * kBlock;
   if (e0 + kBlock <= numel) {
     const uint4* src = reinterpret_cast<const uint4*>(codes + (e0 >> 1));
@@ -225,19 +229,22 @@ int device_cu_count() {
 }
 
 hipError_t launch_quantize(const bf16_t* W, int64_t numel, uint8_t* codes, uint8_t* absmax_q,
-                           float* group_scale, hipStream_t s) {
+                           float* group_scale, int codebook, hipStream_t s) {
   const int64_t nb = (numel + kBlock - 1) / kBlock;
   const int64_t ng = (nb + kGroupBlocks - 1) / kGroupBlocks;
-  hipLaunchKernelGGL(quantize_kernel, dim3((unsigned)ng), dim3(256), 0, s, W, numel, codes, absmax_q,
-                     group_scale, nb);
+  auto* fn = codebook == kCbFp4 ? &quantize_kernel<kCbFp4> : codebook == kCbInt4 ? &quantize_kernel<kCbInt4>
+                                                                                  : &quantize_kernel<kCbNf4>;
+  hipLaunchKernelGGL(fn, dim3((unsigned)ng), dim3(256), 0, s, W, numel, codes, absmax_q, group_scale, nb);
   return hipGetLastError();
 }
 
 hipError_t launch_dequant(const uint8_t* codes, const uint8_t* absmax_q, const float* group_scale,
-                          int64_t numel, bf16_t* out, hipStream_t s) {
+                          int64_t numel, int codebook, bf16_t* out, hipStream_t s) {
   const int64_t nb = (numel + kBlock - 1) / kBlock;
-  hipLaunchKernelGGL(dequant_kernel, dim3((unsigned)((nb + 255) / 256)), dim3(256), 0, s, codes, absmax_q,
-                     group_scale, numel, nb, out);
+  auto* fn = codebook == kCbFp4 ? &dequant_kernel<kCbFp4> : codebook == kCbInt4 ? &dequant_kernel<kCbInt4>
+                                                                                : &dequant_kernel<kCbNf4>;
+  hipLaunchKernelGGL(fn, dim3((unsigned)((nb + 255) / 256)), dim3(256), 0, s, codes, absmax_q, group_scale, numel,
+                     nb, out);
   return hipGetLastError();
 }
 

@@ -54,6 +54,23 @@ def nf4_levels():
     return torch.tensor(list(buf), dtype=torch.float32)
 
 
+# qlora_codebook values
+CODEBOOKS = {"nf4": 0, "fp4": 1, "int4": 2}
+
+
+def _codebook(name):
+    if name not in CODEBOOKS:
+        raise ValueError(f"unknown codebook {name!r}: one of {sorted(CODEBOOKS)}")
+    return CODEBOOKS[name]
+
+
+def codebook_levels(name="nf4"):
+    """The 16 fp32 levels of a codebook ("nf4", "fp4", "int4") as the library holds them."""
+    buf = (ctypes.c_float * 16)()
+    check(lib().qlora_codebook_levels(_codebook(name), buf), "qlora_codebook_levels")
+    return torch.tensor(list(buf), dtype=torch.float32)
+
+
 def workspace_bytes(op, M=0, N=0, K=0, r=0, njobs=0):
     return int(lib().qlora_workspace_bytes(op, M, N, K, r, njobs))
 
@@ -90,23 +107,32 @@ class QuantizedWeight:
         return self.codes.numel() + self.absmax_q.numel() + 4 * self.group_scale.numel()
 
 
-def quantize(W: torch.Tensor, out: Optional[QuantizedWeight] = None) -> QuantizedWeight:
-    """bf16 W [rows x cols] -> NF4 codes + 8-bit absmax codes + fp32 group scales."""
+def quantize(W: torch.Tensor, out: Optional[QuantizedWeight] = None, codebook: str = "nf4") -> QuantizedWeight:
+    """bf16 W [rows x cols] -> 4-bit codes (NF4 unless another codebook is
+    named) + 8-bit absmax codes + fp32 group scales."""
     _need(W, torch.bfloat16, "W")
     rows, cols = (W.shape[0], W.shape[1]) if W.dim() == 2 else (1, W.numel())
     q = out if out is not None else QuantizedWeight.empty(rows, cols, W.device)
     d = q.desc()
-    check(lib().qlora_quantize(_ptr(W), ctypes.byref(d), _stream()), "qlora_quantize")
+    if codebook == "nf4":
+        check(lib().qlora_quantize(_ptr(W), ctypes.byref(d), _stream()), "qlora_quantize")
+    else:
+        check(lib().qlora_quantize_codebook(_ptr(W), ctypes.byref(d), _codebook(codebook), _stream()),
+              "qlora_quantize_codebook")
     return q
 
 
-def dequant(q: QuantizedWeight, out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """NF4 weight -> bf16 [rows x cols]."""
+def dequant(q: QuantizedWeight, out: Optional[torch.Tensor] = None, codebook: str = "nf4") -> torch.Tensor:
+    """4-bit weight -> bf16 [rows x cols], with the codebook it was quantized with."""
     if out is None:
         out = torch.empty(q.rows, q.cols, dtype=torch.bfloat16, device=q.codes.device)
     _need(out, torch.bfloat16, "out")
     d = q.desc()
-    check(lib().qlora_dequant(ctypes.byref(d), _ptr(out), _stream()), "qlora_dequant")
+    if codebook == "nf4":
+        check(lib().qlora_dequant(ctypes.byref(d), _ptr(out), _stream()), "qlora_dequant")
+    else:
+        check(lib().qlora_dequant_codebook(ctypes.byref(d), _codebook(codebook), _ptr(out), _stream()),
+              "qlora_dequant_codebook")
     return out
 
 

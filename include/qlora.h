@@ -135,6 +135,37 @@ qlora_status qlora_quantize(const uint16_t* W, const qlora_nf4_weight* q, void* 
  * Glossary "Definition": converted back to BFloat16 for the calculation. */
 qlora_status qlora_dequant(const qlora_nf4_weight* q, uint16_t* W_out, void* stream);
 
+/* 4-bit codebooks.  The pages compare NF4 with FP4 and Int4 and report that
+ * NF4 has the lower quantization error (deepfa.ir blog, "1. 4-bit
+ * NormalFloat (NF4)" and its results list).  FP4 is E2M1 (sign, two exponent
+ * bits with bias 1, one mantissa bit) divided by its largest value 6; its
+ * two zeros are both +0 (codes 7 and 8, and code 8 is never produced).
+ * Int4 is k/7 for the two's-complement k = -8..7 (code 0, -8/7, is never
+ * produced from absmax-normalised values).  All three are quantized the
+ * same way: blockwise absmax, nearest level with ties to the lower index,
+ * 8-bit double quantization; an all-zero block stores the code of the
+ * level 0 (7 for NF4 and FP4, 8 for Int4).  The fused GEMMs and the GEMV
+ * read NF4 only. */
+typedef enum {
+  QLORA_CODEBOOK_NF4 = 0,
+  QLORA_CODEBOOK_FP4 = 1,
+  QLORA_CODEBOOK_INT4 = 2
+} qlora_codebook;
+
+/* The 16 fp32 levels of a codebook, ascending, as the device tables hold
+ * them.  QLORA_E_NULL for a NULL out, QLORA_E_UNSUPPORTED for an unknown
+ * codebook. */
+qlora_status qlora_codebook_levels(qlora_codebook cb, float out[16]);
+
+/* qlora_quantize / qlora_dequant with the levels of codebook cb (same
+ * arguments, layout and errors; QLORA_E_UNSUPPORTED for an unknown
+ * codebook).  A weight must be dequantized with the codebook it was
+ * quantized with; the descriptor does not record it. */
+qlora_status qlora_quantize_codebook(const uint16_t* W, const qlora_nf4_weight* q, qlora_codebook cb,
+                                     void* stream);
+qlora_status qlora_dequant_codebook(const qlora_nf4_weight* q, qlora_codebook cb, uint16_t* W_out,
+                                    void* stream);
+
 /* Forward: Y [M x N] = X deq(W)^T + s (X A^T) B^T, s = RN32(alpha / r).
  * X [M x K], A [r x K], B [N x r], Y bf16 (overwritten).  r == 0 (A = B =
  * NULL) gives the frozen layer alone.  U_save (nullable) receives

@@ -141,3 +141,27 @@ def test_validation_happens_before_any_launch(L):
     assert L.qlora_gemv_run(ctypes.byref(plan), None) == 3
     jobs[0].r = 16
     assert L.qlora_gemv(jobs, 1, None, 0, None) == 1
+
+
+@pytest.mark.parametrize("name,cb", [("nf4", 0), ("fp4", 1), ("int4", 2)])
+def test_codebook_tables_bitwise_equal_oracle(L, name, cb):
+    buf = (ctypes.c_float * 16)()
+    assert L.qlora_codebook_levels(cb, buf) == 0
+    got = np.array(list(buf), dtype=np.float32).view(np.uint32)
+    assert np.array_equal(got, oracle.codebook_levels(name).view(np.uint32))
+
+
+def test_codebook_calls_reject_bad_arguments_on_the_host(L):
+    buf = (ctypes.c_float * 16)()
+    assert L.qlora_codebook_levels(3, buf) == 4
+    assert L.qlora_codebook_levels(-1, buf) == 4
+    assert L.qlora_codebook_levels(0, None) == 1
+    fake = ctypes.c_void_p(4096)
+    d = _desc(codes=4096, aq=8192, s2=12288)
+    assert L.qlora_quantize_codebook(fake, ctypes.byref(d), 3, None) == 4
+    assert L.qlora_quantize_codebook(None, ctypes.byref(d), 1, None) == 1
+    assert L.qlora_quantize_codebook(ctypes.c_void_p(4098), ctypes.byref(d), 2, None) == 2
+    assert L.qlora_dequant_codebook(ctypes.byref(d), 7, fake, None) == 4
+    assert L.qlora_dequant_codebook(ctypes.byref(d), 1, None, None) == 1
+    neg = _desc(rows=0, codes=4096, aq=8192, s2=12288)
+    assert L.qlora_dequant_codebook(ctypes.byref(neg), 2, fake, None) == 3

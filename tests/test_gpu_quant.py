@@ -17,20 +17,20 @@ from tests.helpers import bits_to_torch, torch_to_bits
 pytestmark = pytest.mark.gpu
 
 
-def _gpu_quantize(bits, shape):
+def _gpu_quantize(bits, shape, codebook="nf4"):
     W = bits_to_torch(bits.reshape(shape))
-    q = ops.quantize(W)
-    deq = ops.dequant(q)
+    q = ops.quantize(W, codebook=codebook)
+    deq = ops.dequant(q, codebook=codebook)
     torch.cuda.synchronize()
     return (q.codes.cpu().numpy(), q.absmax_q.cpu().numpy(), q.group_scale.cpu().numpy(),
             torch_to_bits(deq).ravel())
 
 
-def _check(bits, shape, label):
-    print(f"[quant parity] {label} shape={shape}", flush=True)
-    codes, aq, s2, deq = _gpu_quantize(bits, shape)
-    rc, raq, rs2 = oracle.quantize(bits)
-    rdeq = oracle.dequant(rc, raq, rs2, bits.size)
+def _check(bits, shape, label, codebook="nf4"):
+    print(f"[quant parity] {codebook} {label} shape={shape}", flush=True)
+    codes, aq, s2, deq = _gpu_quantize(bits, shape, codebook)
+    rc, raq, rs2 = oracle.quantize(bits, codebook)
+    rdeq = oracle.dequant(rc, raq, rs2, bits.size, codebook)
     assert np.array_equal(codes, rc), f"{label}: NF4 codes differ at {np.flatnonzero(codes != rc)[:8]}"
     assert np.array_equal(aq, raq), f"{label}: absmax codes differ at {np.flatnonzero(aq != raq)[:8]}"
     assert np.array_equal(s2.view(np.uint32), rs2.view(np.uint32)), f"{label}: group scales differ"
@@ -104,7 +104,7 @@ def test_quantize_deterministic_and_bounded():
     assert torch.all(buf[:128] == 0x7BCD) and torch.all(buf[128 + n:] == 0x7BCD)
 
 
-def _near_boundary_blocks():
+def _near_boundary_blocks(codebook="nf4"):
     """Blocks whose quotients w / a sit as close as bf16 allows to every
     decision point of the encoding: the midpoint of two adjacent NF4 levels
     (where the nearest level changes) and the fp32 rounding boundary next to
@@ -112,9 +112,11 @@ def _near_boundary_blocks():
     One block per (absmax mantissa, side): its first element is the absmax a
     (1 + j/128 times a power of two), the others are the three bf16 values
     around a * target for each target."""
-    L = oracle.nf4_levels().astype(np.float64)
+    L = oracle.codebook_levels(codebook).astype(np.float64)
     targets = []
     for k in range(15):
+        if L[k] == L[k + 1] or L[k] < -1:     # FP4's zero pair; Int4's -8/7, beyond any x
+            continue
         mid = (L[k] + L[k + 1]) / 2
         lo = np.float32(mid)
         if float(lo) > mid:
@@ -132,6 +134,8 @@ def _near_boundary_blocks():
         ws = np.array(ws, dtype=np.uint32)
         for half in range(2):
             part = ws[half * 45:(half + 1) * 45]
+            if part.size == 0:
+                continue
             blk = np.zeros(64, dtype=np.uint32)
             blk[0] = np.array([a], dtype=np.float32).view(np.uint32)[0] >> 16
             blk[1:1 + part.size] = part
@@ -149,3 +153,58 @@ def _near_boundary_blocks():
 def test_quantize_near_decision_boundaries():
     bits = _near_boundary_blocks()
     _check(bits, (bits.size // 64, 64), "quotients at level midpoints and fp32 rounding boundaries")
+
+
+CODEBOOKS = ["fp4", "int4"]
+
+
+@pytest.mark.parametrize("codebook", CODEBOOKS)
+def test_codebook_levels_bitwise(codebook):
+    assert np.array_equal(ops.codebook_levels(codebook).numpy().view(np.uint32),
+                          oracle.codebook_levels(codebook).view(np.uint32))
+
+
+@pytest.mark.parametrize("codebook", CODEBOOKS)
+def test_codebook_small_config(codebook):
+    d = synth.small_numpy(0)
+    _check(d["W"].ravel(), (1024, 1024), "1024x1024 N(0,0.02)", codebook)
+
+
+@pytest.mark.parametrize("codebook", CODEBOOKS)
+@pytest.mark.parametrize("rows,cols", [(1, 1), (1, 65), (3, 7), (129, 130), (5, 64 * 257 + 35)])
+def test_codebook_ragged(codebook, rows, cols):
+    rng = np.random.default_rng(rows * 1000 + cols + 17)
+    bits = synth.to_bf16_bits(rng.standard_normal(rows * cols) * 0.02)
+    _check(bits, (rows, cols), "ragged", codebook)
+
+
+@pytest.mark.parametrize("codebook", CODEBOOKS)
+def test_codebook_special_values(codebook):
+    rng = np.random.default_rng(9)
+    n = 64 * 256 * 2 + 64 * 3
+    w = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    w[: 64 * 256] = 0.0                                   # an all-zero group
+    w[64 * 256: 64 * 256 + 64] = 0.0                      # an all-zero block in a live group
+    w[64 * 300: 64 * 301] = np.where(rng.random(64) < 0.5, 1.0, -1.0) * 0.03
+    w[64 * 302] = 0.5
+    w[64 * 400: 64 * 401] = rng.standard_normal(64) * 1e-38
+    w[64 * 401: 64 * 402] = -0.0
+    _check(synth.to_bf16_bits(w), (n // 64, 64), "special values", codebook)
+
+
+@pytest.mark.parametrize("codebook", CODEBOOKS)
+def test_codebook_near_decision_boundaries(codebook):
+    bits = _near_boundary_blocks(codebook)
+    _check(bits, (bits.size // 64, 64), "quotients at level midpoints and fp32 rounding boundaries", codebook)
+
+
+def test_nf4_has_the_lowest_error_on_the_gpu():
+    # the pages' comparison, through the library's own quantize and dequant
+    W = synth.normal_bf16((2048, 4096), 0.02, 12, "cuda", outliers=0.001)
+    ref = W.double()
+    err = {}
+    for cb in ("nf4", "fp4", "int4"):
+        back = ops.dequant(ops.quantize(W, codebook=cb), codebook=cb).double()
+        err[cb] = ((back - ref).pow(2).mean().sqrt() / ref.pow(2).mean().sqrt()).item()
+    print(f"[codebook rel rmse] {err}", flush=True)
+    assert err["nf4"] < err["fp4"] and err["nf4"] < err["int4"], err
