@@ -221,7 +221,7 @@ def codebook_study(L, dev, q_bytes, reps=5):
         b.record()
         torch.cuda.synchronize()
         ms = a.elapsed_time(b) / reps
-        ops.dequant(qs[0], out=back, codebook=cb)
+        ops.dequant(qs[0], out=back)
         err = ((back.double() - ref).pow(2).mean().sqrt() / ref.pow(2).mean().sqrt()).item()
         res[cb] = {"quantize_ms": ms, "quantize_gbps": q_bytes / (ms * 1e-3) / 1e9,
                    f"rel_rmse_{L[0]['name']}": err}

@@ -22,7 +22,7 @@ STATUS_NAMES = {
 EXPORTS = [
     "qlora_status_str", "qlora_last_hip_error", "qlora_version", "qlora_nf4_levels",
     "qlora_sizes", "qlora_workspace_bytes", "qlora_quantize", "qlora_dequant",
-    "qlora_codebook_levels", "qlora_quantize_codebook", "qlora_dequant_codebook",
+    "qlora_codebook_levels",
     "qlora_linear_fwd", "qlora_linear_bwd", "qlora_gemv", "qlora_gemv_prepare", "qlora_gemv_run",
     "qlora_lora_down", "qlora_lora_dy_b", "qlora_lora_grads", "qlora_nf4_fwd", "qlora_nf4_dx",
 ]
@@ -37,6 +37,7 @@ class Nf4WeightDesc(ctypes.Structure):
         ("codes", ctypes.c_void_p),
         ("absmax_q", ctypes.c_void_p),
         ("group_scale", ctypes.c_void_p),
+        ("codebook", ctypes.c_int32),
     ]
 
 
@@ -102,10 +103,6 @@ def lib():
     L.qlora_dequant.argtypes = [W, vp, vp]
     L.qlora_codebook_levels.restype = ctypes.c_int
     L.qlora_codebook_levels.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_float)]
-    L.qlora_quantize_codebook.restype = ctypes.c_int
-    L.qlora_quantize_codebook.argtypes = [vp, W, ctypes.c_int, vp]
-    L.qlora_dequant_codebook.restype = ctypes.c_int
-    L.qlora_dequant_codebook.argtypes = [W, ctypes.c_int, vp, vp]
     L.qlora_linear_fwd.restype = ctypes.c_int
     L.qlora_linear_fwd.argtypes = [W, vp, i64, vp, vp, i32, f32, vp, vp, vp, sz, vp]
     L.qlora_linear_bwd.restype = ctypes.c_int

@@ -43,6 +43,8 @@ qlora_status check_weight(const qlora_nf4_weight* q) {
   if (!q) return QLORA_E_NULL;
   if (q->rows <= 0 || q->cols <= 0) return QLORA_E_SHAPE;
   if (q->blocksize != 64 || q->group_blocks != 256) return QLORA_E_UNSUPPORTED;
+  if (q->codebook != QLORA_CODEBOOK_NF4 && q->codebook != QLORA_CODEBOOK_FP4 && q->codebook != QLORA_CODEBOOK_INT4)
+    return QLORA_E_UNSUPPORTED;
   if (!q->codes || !q->absmax_q || !q->group_scale) return QLORA_E_NULL;
   if (!aligned16(q->codes) || (reinterpret_cast<uintptr_t>(q->group_scale) & 3u)) return QLORA_E_ALIGN;
   return QLORA_OK;
@@ -77,7 +79,7 @@ qlora_status check_rank(int32_t r, const void* A, const void* B) {
 }
 
 Nf4View view(const qlora_nf4_weight* q) {
-  return Nf4View{q->codes, q->absmax_q, q->group_scale, q->rows, q->cols};
+  return Nf4View{q->codes, q->absmax_q, q->group_scale, q->rows, q->cols, q->codebook};
 }
 
 struct FwdLayout {
@@ -215,11 +217,7 @@ size_t qlora_workspace_bytes(qlora_op op, int64_t M, int64_t N, int64_t K, int32
   return 0;
 }
 
-static bool known_codebook(int cb) { return cb == QLORA_CODEBOOK_NF4 || cb == QLORA_CODEBOOK_FP4 || cb == QLORA_CODEBOOK_INT4; }
-
-qlora_status qlora_quantize_codebook(const uint16_t* W, const qlora_nf4_weight* q, qlora_codebook cb,
-                                     void* stream) {
-  if (!known_codebook(cb)) return QLORA_E_UNSUPPORTED;
+qlora_status qlora_quantize(const uint16_t* W, const qlora_nf4_weight* q, void* stream) {
   qlora_status st = check_weight(q);
   if (st != QLORA_OK) return st;
   if (!W) return QLORA_E_NULL;
@@ -227,16 +225,11 @@ qlora_status qlora_quantize_codebook(const uint16_t* W, const qlora_nf4_weight* 
   if (q->rows > INT64_MAX / q->cols) return QLORA_E_SHAPE;
   const int64_t n = q->rows * q->cols;
   if ((n + 16383) / 16384 > 0x7FFFFFFF) return QLORA_E_SHAPE;
-  return hip_status(launch_quantize(W, n, q->codes, q->absmax_q, q->group_scale, (int)cb, (hipStream_t)stream));
+  return hip_status(
+      launch_quantize(W, n, q->codes, q->absmax_q, q->group_scale, q->codebook, (hipStream_t)stream));
 }
 
-qlora_status qlora_quantize(const uint16_t* W, const qlora_nf4_weight* q, void* stream) {
-  return qlora_quantize_codebook(W, q, QLORA_CODEBOOK_NF4, stream);
-}
-
-qlora_status qlora_dequant_codebook(const qlora_nf4_weight* q, qlora_codebook cb, uint16_t* W_out,
-                                    void* stream) {
-  if (!known_codebook(cb)) return QLORA_E_UNSUPPORTED;
+qlora_status qlora_dequant(const qlora_nf4_weight* q, uint16_t* W_out, void* stream) {
   qlora_status st = check_weight(q);
   if (st != QLORA_OK) return st;
   if (!W_out) return QLORA_E_NULL;
@@ -244,11 +237,8 @@ qlora_status qlora_dequant_codebook(const qlora_nf4_weight* q, qlora_codebook cb
   if (q->rows > INT64_MAX / q->cols) return QLORA_E_SHAPE;
   const int64_t n = q->rows * q->cols;
   if ((n + 63) / 64 / 256 > 0x7FFFFFFF) return QLORA_E_SHAPE;
-  return hip_status(launch_dequant(q->codes, q->absmax_q, q->group_scale, n, (int)cb, W_out, (hipStream_t)stream));
-}
-
-qlora_status qlora_dequant(const qlora_nf4_weight* q, uint16_t* W_out, void* stream) {
-  return qlora_dequant_codebook(q, QLORA_CODEBOOK_NF4, W_out, stream);
+  return hip_status(
+      launch_dequant(q->codes, q->absmax_q, q->group_scale, n, q->codebook, W_out, (hipStream_t)stream));
 }
 
 qlora_status qlora_linear_fwd(const qlora_nf4_weight* W, const uint16_t* X, int64_t M, const uint16_t* A,
@@ -404,6 +394,8 @@ qlora_status qlora_gemv_prepare(const qlora_gemv_job* jobs, int32_t njobs, void*
     const qlora_gemv_job& J = jobs[i];
     qlora_status st = check_weight(J.W);
     if (st != QLORA_OK) return st;
+    // one codebook per call: the kernel builds its decode table once
+    if (J.W->codebook != jobs[0].W->codebook) return QLORA_E_UNSUPPORTED;
     if (J.W->cols % 64 != 0 || J.W->cols > kMaxGemvCols || J.W->rows > 0x7FFFFFFF) return QLORA_E_UNSUPPORTED;
     // codes addressed with 32-bit byte offsets, including the prefetch of
     // one row's worth of blocks past the last row
@@ -437,7 +429,8 @@ qlora_status qlora_gemv_prepare(const qlora_gemv_job* jobs, int32_t njobs, void*
   const size_t table_bytes = gemv_table_bound(njobs, 1);
   if (ws_bytes < u_bytes || ws_bytes - u_bytes < table_bytes) return QLORA_E_WORKSPACE;
   GemvLaunch L{};
-  qlora_status st = hip_status(gemv_prepare(buf.data(), njobs, ws_at(ws, u_bytes), table_bytes, &L, (hipStream_t)stream));
+  qlora_status st = hip_status(
+      gemv_prepare(buf.data(), njobs, jobs[0].W->codebook, ws_at(ws, u_bytes), table_bytes, &L, (hipStream_t)stream));
   if (st != QLORA_OK) return st;
   static_assert(sizeof(GemvLaunch) + sizeof(uint64_t) <= sizeof(qlora_gemv_plan), "plan storage");
   std::memset(plan, 0, sizeof(*plan));

@@ -211,7 +211,7 @@ struct Frags {
 // code DMA of chunk s/4 + 2 (U8 & 3 == 2), dequantization of stage s+2,
 // scales of block s/2 + 2 (U8 even; the table of block (s+2)/2 is built
 // from the scales loaded two substeps earlier).
-template <int U8>
+template <int CB, int U8>
 __device__ __forceinline__ void fwd_substep(char* smem, const Fwd& f, int s, f32x16_t (&acc)[4][4], Frags& F,
                                             Nf4Table& T, Scale& sA, Scale& sB, int an, int bm, FragOffs fo) {
   constexpr int U = U8 & 3;
@@ -225,8 +225,8 @@ __device__ __forceinline__ void fwd_substep(char* smem, const Fwd& f, int s, f32
   if (U == 2) sB = fwd_scale(f, (s >> 1) + 2);
   __builtin_amdgcn_sched_barrier(0);
   const uint4 cw = rdu16(smem + kCodeBase + ((PS >> 2) & 1) * kCodes + spos(threadIdx.x, PS & 3));
-  if (U == 0) T = make_table(block_scale(sB.q, sB.s2));
-  if (U == 2) T = make_table(block_scale(sA.q, sA.s2));
+  if (U == 0) T = make_table<CB>(block_scale(sB.q, sB.s2));
+  if (U == 2) T = make_table<CB>(block_scale(sA.q, sA.s2));
   // first half: k16 0 of stage s; read k16 1
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -252,6 +252,7 @@ __device__ __forceinline__ void fwd_substep(char* smem, const Fwd& f, int s, f32
   schedule_half<1>();
 }
 
+template <int CB>
 __global__ __launch_bounds__(kThreads, 1) void nf4_fwd_kernel(Nf4View W, const bf16_t* __restrict__ X, int64_t M,
                                                               const bf16_t* __restrict__ U,
                                                               const bf16_t* __restrict__ Bl, int r, float s,
@@ -298,7 +299,7 @@ __global__ __launch_bounds__(kThreads, 1) void nf4_fwd_kernel(Nf4View W, const b
   fwd_dma_x(smem, f, 2, 2);
   QLORA_WAIT(0, 0);
   __builtin_amdgcn_s_barrier();
-  Nf4Table T = make_table(block_scale(sA.q, sA.s2));
+  Nf4Table T = make_table<CB>(block_scale(sA.q, sA.s2));
 #pragma unroll
   for (int st = 0; st < 2; ++st) {
     const uint4 cw = rdu16(smem + kCodeBase + spos(t, st));
@@ -315,7 +316,7 @@ __global__ __launch_bounds__(kThreads, 1) void nf4_fwd_kernel(Nf4View W, const b
   }
   // K % 64 == 0, so the stage count is even
   int st = 0;
-#define QLORA_FWD_SUB(u) fwd_substep<u>(smem, f, st + u, acc, F, T, sA, sB, an, bm, fo)
+#define QLORA_FWD_SUB(u) fwd_substep<CB, u>(smem, f, st + u, acc, F, T, sA, sB, an, bm, fo)
   for (; st + 8 <= f.nsub; st += 8) {
     QLORA_FWD_SUB(0); QLORA_FWD_SUB(1); QLORA_FWD_SUB(2); QLORA_FWD_SUB(3);
     QLORA_FWD_SUB(4); QLORA_FWD_SUB(5); QLORA_FWD_SUB(6); QLORA_FWD_SUB(7);
@@ -530,15 +531,16 @@ struct TbState {
   uint32_t p[8];
   Nf4Table T;   // the table of the lane's own row, before the lane-half swap
 };
-// The products by the levels 0 (code 7) and 1 (code 15) are 0 and t
+// Product of level i of codebook CB with t; the levels 0 and 1 give 0 and t
 // exactly (t is finite and not negative), so they are not multiplied out.
-template <int K>
+template <int CB>
+__device__ __forceinline__ float level_times(int i, float t) {
+  const uint32_t l = cb_level_bits<CB>(i);
+  return l == 0u ? 0.0f : l == 0x3F800000u ? t : u2f(l) * t;
+}
+template <int CB, int K>
 __device__ __forceinline__ void tb_chunk(TbState& b, const Scale& sc, Nf4Table& T) {
-  auto pair = [&](int i) {
-    const float lo = u2f(kNf4LevelBits[2 * i]) * b.t;
-    const float hi = (2 * i + 1 == 7) ? 0.0f : (2 * i + 1 == 15) ? b.t : u2f(kNf4LevelBits[2 * i + 1]) * b.t;
-    b.p[i] = pack_bf16x2(lo, hi);
-  };
+  auto pair = [&](int i) { b.p[i] = pack_bf16x2(level_times<CB>(2 * i, b.t), level_times<CB>(2 * i + 1, b.t)); };
   if constexpr (K == 0) {
     b.t = block_scale(sc.q, sc.s2);
     pair(0);
@@ -577,7 +579,7 @@ __device__ __forceinline__ void tb_chunk(TbState& b, const Scale& sc, Nf4Table& 
 //                 even s: step 1 of stage s+1 in 0..9, step 0 in 16..25
 //                 (step 0 is written over the step 0 registers of stage s,
 //                 last read by slot 15)
-template <int U8, int X>
+template <int CB, int U8, int X>
 __device__ __forceinline__ void fwdr_slot(char* smem, const FwdR& f, int s, f32x16_t (&acc)[2][8], FragsR& F,
                                           Nf4Table (&T)[2], Scale (&sc)[4][2], bf16x8_t (&n1)[2], DqState& dq,
                                           TbState& tb, const RdBase& rb) {
@@ -618,7 +620,7 @@ __device__ __forceinline__ void fwdr_slot(char* smem, const FwdR& f, int s, f32x
     if constexpr (X < 6) {
       const bool hi = (threadIdx.x & 32) != 0;
       const Scale mine{hi ? sc[SL][1].q : sc[SL][0].q, hi ? sc[SL][1].s2 : sc[SL][0].s2};
-      tb_chunk<X>(tb, mine, tb.T);
+      tb_chunk<CB, X>(tb, mine, tb.T);
     } else if constexpr (X == 6) {
       // lanes 0..31 hold row 0's table and lanes 32..63 row 1's: swapping the
       // upper half of one copy with the lower half of another gives each row's
@@ -644,7 +646,7 @@ __device__ __forceinline__ void fwdr_slot(char* smem, const FwdR& f, int s, f32x
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int U8>
+template <int CB, int U8>
 __device__ __forceinline__ void fwdr_substep(char* smem, const FwdR& f, int s, f32x16_t (&acc)[2][8], FragsR& F,
                                              Nf4Table (&T)[2], Scale (&sc)[4][2], const RdBase& rb) {
   __builtin_amdgcn_sched_barrier(0);
@@ -658,7 +660,7 @@ __device__ __forceinline__ void fwdr_substep(char* smem, const FwdR& f, int s, f
   bf16x8_t n1[2];
   DqState dq;
   TbState tb;
-#define QLORA_FWDR_SLOT(x) fwdr_slot<U8, x>(smem, f, s, acc, F, T, sc, n1, dq, tb, rb)
+#define QLORA_FWDR_SLOT(x) fwdr_slot<CB, U8, x>(smem, f, s, acc, F, T, sc, n1, dq, tb, rb)
 #define QLORA_FWDR_SLOT4(x) QLORA_FWDR_SLOT(x); QLORA_FWDR_SLOT(x + 1); QLORA_FWDR_SLOT(x + 2); QLORA_FWDR_SLOT(x + 3)
   QLORA_FWDR_SLOT4(0); QLORA_FWDR_SLOT4(4); QLORA_FWDR_SLOT4(8); QLORA_FWDR_SLOT4(12);
   QLORA_FWDR_SLOT4(16); QLORA_FWDR_SLOT4(20); QLORA_FWDR_SLOT4(24); QLORA_FWDR_SLOT4(28);
@@ -670,6 +672,7 @@ __device__ __forceinline__ void fwdr_substep(char* smem, const FwdR& f, int s, f
   F.c[1] = cn1;
 }
 
+template <int CB>
 __global__ __launch_bounds__(kThreads, 1) void nf4_fwd_r_kernel(Nf4View W, const bf16_t* __restrict__ X, int64_t M,
                                                                 const bf16_t* __restrict__ U,
                                                                 const bf16_t* __restrict__ Bl, int r, float s,
@@ -738,7 +741,7 @@ __global__ __launch_bounds__(kThreads, 1) void nf4_fwd_r_kernel(Nf4View W, const
   FragsR F;
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    T[i] = make_table(block_scale(sc[0][i].q, sc[0][i].s2));
+    T[i] = make_table<CB>(block_scale(sc[0][i].q, sc[0][i].s2));
     const uint2 c = fwdr_codes(smem, f, i, 0);
     F.a0[i] = deq_frag(c.x, T[i]);
     F.a1[i] = deq_frag(c.y, T[i]);
@@ -760,7 +763,7 @@ __global__ __launch_bounds__(kThreads, 1) void nf4_fwd_r_kernel(Nf4View W, const
   // K % 64 == 0, so the stage count is even; the loop's stage counter stays a
   // multiple of 8, so ring positions follow from the substep index alone
   int st = 0;
-#define QLORA_FWDR_SUB(u) fwdr_substep<u>(smem, f, st + u, acc, F, T, sc, rb)
+#define QLORA_FWDR_SUB(u) fwdr_substep<CB, u>(smem, f, st + u, acc, F, T, sc, rb)
   for (; st + 8 <= f.nsub; st += 8) {
     QLORA_FWDR_SUB(0); QLORA_FWDR_SUB(1); QLORA_FWDR_SUB(2); QLORA_FWDR_SUB(3);
     QLORA_FWDR_SUB(4); QLORA_FWDR_SUB(5); QLORA_FWDR_SUB(6); QLORA_FWDR_SUB(7);
@@ -900,7 +903,7 @@ __device__ __forceinline__ uint2 fwd8_codes(const char* smem, const Fwd8& f, int
   return make_uint2(v.x, v.y);
 }
 
-template <int WAVES, int U8, int X>
+template <int CB, int WAVES, int U8, int X>
 __device__ __forceinline__ void fwd8_slot(char* smem, const Fwd8& f, int s, f32x16_t (&acc)[8], bf16x8_t (&b)[8],
                                           bf16x8_t& a0, bf16x8_t& a1, bf16x8_t& n1, uint2& c, uint2& cn,
                                           Nf4Table& T, Scale (&sc)[4], DqState& dq, TbState& tb, int fo0, int fo1) {
@@ -926,7 +929,7 @@ __device__ __forceinline__ void fwd8_slot(char* smem, const Fwd8& f, int s, f32x
   // VALU chunks
   if constexpr (kOdd) {
     constexpr int SL = ((U8 + 1) >> 1) & 3;
-    if constexpr (X < 6) tb_chunk<X>(tb, sc[SL], T);
+    if constexpr (X < 6) tb_chunk<CB, X>(tb, sc[SL], T);
     else if constexpr (X < 11) dq_chunk<X - 6>(dq, c.y, T, n1);
     else dq_chunk<X - 11>(dq, c.x, T, a0);
   } else {
@@ -936,7 +939,7 @@ __device__ __forceinline__ void fwd8_slot(char* smem, const Fwd8& f, int s, f32x
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int WAVES, int U8>
+template <int CB, int WAVES, int U8>
 __device__ __forceinline__ void fwd8_substep(char* smem, const Fwd8& f, int s, f32x16_t (&acc)[8], bf16x8_t (&b)[8],
                                              bf16x8_t& a0, bf16x8_t& a1, uint2& c, Nf4Table& T, Scale (&sc)[4],
                                              int fo0, int fo1) {
@@ -948,7 +951,7 @@ __device__ __forceinline__ void fwd8_substep(char* smem, const Fwd8& f, int s, f
   uint2 cn;
   DqState dq;
   TbState tb;
-#define QLORA_FWD8_SLOT(x) fwd8_slot<WAVES, U8, x>(smem, f, s, acc, b, a0, a1, n1, c, cn, T, sc, dq, tb, fo0, fo1)
+#define QLORA_FWD8_SLOT(x) fwd8_slot<CB, WAVES, U8, x>(smem, f, s, acc, b, a0, a1, n1, c, cn, T, sc, dq, tb, fo0, fo1)
 #define QLORA_FWD8_SLOT4(x) QLORA_FWD8_SLOT(x); QLORA_FWD8_SLOT(x + 1); QLORA_FWD8_SLOT(x + 2); QLORA_FWD8_SLOT(x + 3)
   QLORA_FWD8_SLOT4(0); QLORA_FWD8_SLOT4(4); QLORA_FWD8_SLOT4(8); QLORA_FWD8_SLOT4(12);
 #undef QLORA_FWD8_SLOT4
@@ -977,7 +980,7 @@ __device__ __forceinline__ void tail_tokens8(char* dst, const bf16_t* Ut, int64_
 // tail_base + b / 2 in the row-major order of a tiles_n x tiles_m grid of
 // 256 x 256 tiles: the split last round of a launch whose tile count is not
 // a multiple of the CU count.
-template <int WAVES>
+template <int CB, int WAVES>
 __global__ __launch_bounds__(64 * WAVES, 1) void nf4_fwd_n32_kernel(Nf4View W, const bf16_t* __restrict__ X,
                                                                     int64_t M, const bf16_t* __restrict__ U,
                                                                     const bf16_t* __restrict__ Bl, int r, float s,
@@ -1046,7 +1049,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void nf4_fwd_n32_kernel(Nf4View W, c
     for (int q = 0; q < 16 / WAVES; ++q) fwd8_dma_x<WAVES>(smem, f, q, st, st);
   QLORA_WAIT(0, 0);
   __builtin_amdgcn_s_barrier();
-  Nf4Table T = make_table(block_scale(sc[0].q, sc[0].s2));
+  Nf4Table T = make_table<CB>(block_scale(sc[0].q, sc[0].s2));
   bf16x8_t a0, a1;
   {
     const uint2 c0 = fwd8_codes(smem, f, 0);
@@ -1059,7 +1062,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void nf4_fwd_n32_kernel(Nf4View W, c
   for (int j = 0; j < 8; ++j) b[j] = rd16(smem + j * 2048 + fo0);
   // K % 64 == 0, so the stage count is even
   int st = 0;
-#define QLORA_FWD8_SUB(u) fwd8_substep<WAVES, u>(smem, f, st + u, acc, b, a0, a1, c, T, sc, fo0, fo1)
+#define QLORA_FWD8_SUB(u) fwd8_substep<CB, WAVES, u>(smem, f, st + u, acc, b, a0, a1, c, T, sc, fo0, fo1)
   for (; st + 8 <= f.nsub; st += 8) {
     QLORA_FWD8_SUB(0); QLORA_FWD8_SUB(1); QLORA_FWD8_SUB(2); QLORA_FWD8_SUB(3);
     QLORA_FWD8_SUB(4); QLORA_FWD8_SUB(5); QLORA_FWD8_SUB(6); QLORA_FWD8_SUB(7);
@@ -1211,7 +1214,7 @@ __device__ __forceinline__ uint32_t u4_word(const uint4& v) {
   return I == 0 ? v.x : I == 1 ? v.y : I == 2 ? v.z : v.w;
 }
 
-template <int U8, int X>
+template <int CB, int U8, int X>
 __device__ __forceinline__ void dx_slot(char* smem, const Dx& d, int s, f32x16_t (&acc)[4][4], Frags& F,
                                         Codes (&cs)[4], YRegs (&ys)[2], const int (&ao)[4], int bm, FragOffs fo,
                                         TbState& tb, Nf4Table& T, DqState& dq, bf16x8_t& dqo) {
@@ -1271,7 +1274,7 @@ __device__ __forceinline__ void dx_slot(char* smem, const Dx& d, int s, f32x16_t
   {
     const Codes& pc = cs[(U + 2) & 3];
     if constexpr (X < 6) {
-      tb_chunk<X>(tb, Scale{pc.q, pc.s2}, T);
+      tb_chunk<CB, X>(tb, Scale{pc.q, pc.s2}, T);
     } else if constexpr (X < 26) {
       constexpr int dd = (X - 6) / 5, kc = (X - 6) % 5;
       // chunk dd ^ flip: a select between two fixed words (a runtime index
@@ -1284,7 +1287,7 @@ __device__ __forceinline__ void dx_slot(char* smem, const Dx& d, int s, f32x16_t
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int U8>
+template <int CB, int U8>
 __device__ __forceinline__ void dx_substep(char* smem, const Dx& d, int s, f32x16_t (&acc)[4][4], Frags& F,
                                            Codes (&cs)[4], YRegs (&ys)[2], const int (&ao)[4], int bm,
                                            FragOffs fo) {
@@ -1296,7 +1299,7 @@ __device__ __forceinline__ void dx_substep(char* smem, const Dx& d, int s, f32x1
   Nf4Table T;
   DqState dq;
   bf16x8_t dqo;
-#define QLORA_DX_SLOT(x) dx_slot<U8, x>(smem, d, s, acc, F, cs, ys, ao, bm, fo, tb, T, dq, dqo)
+#define QLORA_DX_SLOT(x) dx_slot<CB, U8, x>(smem, d, s, acc, F, cs, ys, ao, bm, fo, tb, T, dq, dqo)
 #define QLORA_DX_SLOT4(x) QLORA_DX_SLOT(x); QLORA_DX_SLOT(x + 1); QLORA_DX_SLOT(x + 2); QLORA_DX_SLOT(x + 3)
   QLORA_DX_SLOT4(0); QLORA_DX_SLOT4(4); QLORA_DX_SLOT4(8); QLORA_DX_SLOT4(12);
   QLORA_DX_SLOT4(16); QLORA_DX_SLOT4(20); QLORA_DX_SLOT4(24); QLORA_DX_SLOT4(28);
@@ -1304,6 +1307,7 @@ __device__ __forceinline__ void dx_substep(char* smem, const Dx& d, int s, f32x1
 #undef QLORA_DX_SLOT
 }
 
+template <int CB>
 __global__ __launch_bounds__(kThreads, 1) void nf4_dx_kernel(Nf4View W, const bf16_t* __restrict__ dY, int64_t M,
                                                              const bf16_t* __restrict__ G,
                                                              const bf16_t* __restrict__ Al, int r, float s,
@@ -1363,7 +1367,7 @@ __global__ __launch_bounds__(kThreads, 1) void nf4_dx_kernel(Nf4View W, const bf
   dx_load_y(ys[1], d, 2);   // stored by substep 0
 #pragma unroll
   for (int p = 0; p < 2; ++p) {
-    const Nf4Table T = make_table(block_scale(cs[p].q, cs[p].s2));
+    const Nf4Table T = make_table<CB>(block_scale(cs[p].q, cs[p].s2));
     dx_produce(smem, cs[p], T, p, 0);
     dx_produce(smem, cs[p], T, p, 1);
   }
@@ -1376,7 +1380,7 @@ __global__ __launch_bounds__(kThreads, 1) void nf4_dx_kernel(Nf4View W, const bf
     F.b0[i] = rd16(smem + kOp + bm + i * 2048 + fo.o0);
   }
   int st = 0;
-#define QLORA_DX_SUB(u) dx_substep<u>(smem, d, st + u, acc, F, cs, ys, ao, bm, fo)
+#define QLORA_DX_SUB(u) dx_substep<CB, u>(smem, d, st + u, acc, F, cs, ys, ao, bm, fo)
   for (; st + 8 <= d.nsub; st += 8) {
     QLORA_DX_SUB(0); QLORA_DX_SUB(1); QLORA_DX_SUB(2); QLORA_DX_SUB(3);
     QLORA_DX_SUB(4); QLORA_DX_SUB(5); QLORA_DX_SUB(6); QLORA_DX_SUB(7);
@@ -1486,7 +1490,7 @@ __device__ __forceinline__ void dxh_store_chunk(char* smem, int buf, int p, cons
 //                 s+2 (the second follows the last slot)
 //   VALU chunks   slots 0..5: table of the thread's row and block; slots
 //                 6..15: the two decodes, five chunks each
-template <int U8, int X>
+template <int CB, int U8, int X>
 __device__ __forceinline__ void dxh_slot(char* smem, const Dx& d, int s, f32x16_t (&acc)[2][4], FragsH& F,
                                          CodesH (&cs)[4], YRegs (&ys)[2], const int (&ao)[2], int bm, FragOffs fo,
                                          TbState& tb, Nf4Table& T, DqState& dq, bf16x8_t& dqo) {
@@ -1545,7 +1549,7 @@ __device__ __forceinline__ void dxh_slot(char* smem, const Dx& d, int s, f32x16_
   {
     const CodesH& pc = cs[(U + 2) & 3];
     if constexpr (X < 6) {
-      tb_chunk<X>(tb, Scale{pc.q, pc.s2}, T);
+      tb_chunk<CB, X>(tb, Scale{pc.q, pc.s2}, T);
     } else {
       constexpr int dd = (X - 6) / 5, kc = (X - 6) % 5;
       // decode dd is chunk dd ^ flip: a select between the two code words as
@@ -1559,7 +1563,7 @@ __device__ __forceinline__ void dxh_slot(char* smem, const Dx& d, int s, f32x16_
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int U8>
+template <int CB, int U8>
 __device__ __forceinline__ void dxh_substep(char* smem, const Dx& d, int s, f32x16_t (&acc)[2][4], FragsH& F,
                                             CodesH (&cs)[4], YRegs (&ys)[2], const int (&ao)[2], int bm,
                                             FragOffs fo) {
@@ -1572,7 +1576,7 @@ __device__ __forceinline__ void dxh_substep(char* smem, const Dx& d, int s, f32x
   Nf4Table T;
   DqState dq;
   bf16x8_t dqo;
-#define QLORA_DXH_SLOT(x) dxh_slot<U8, x>(smem, d, s, acc, F, cs, ys, ao, bm, fo, tb, T, dq, dqo)
+#define QLORA_DXH_SLOT(x) dxh_slot<CB, U8, x>(smem, d, s, acc, F, cs, ys, ao, bm, fo, tb, T, dq, dqo)
 #define QLORA_DXH_SLOT4(x) QLORA_DXH_SLOT(x); QLORA_DXH_SLOT(x + 1); QLORA_DXH_SLOT(x + 2); QLORA_DXH_SLOT(x + 3)
   QLORA_DXH_SLOT4(0); QLORA_DXH_SLOT4(4); QLORA_DXH_SLOT4(8); QLORA_DXH_SLOT4(12);
 #undef QLORA_DXH_SLOT4
@@ -1581,6 +1585,7 @@ __device__ __forceinline__ void dxh_substep(char* smem, const Dx& d, int s, f32x
   dxh_store_chunk(smem, (U + 2) & 3, ((threadIdx.x >> 2) & 1) ^ 1, dqo);
 }
 
+template <int CB>
 __global__ __launch_bounds__(kThreads, 1) void nf4_dx_half_kernel(Nf4View W, const bf16_t* __restrict__ dY,
                                                                   int64_t M, const bf16_t* __restrict__ G,
                                                                   const bf16_t* __restrict__ Al, int r, float s,
@@ -1646,7 +1651,7 @@ __global__ __launch_bounds__(kThreads, 1) void nf4_dx_half_kernel(Nf4View W, con
   dx_load_y(ys[1], d, 2);   // stored by substep 0
 #pragma unroll
   for (int p = 0; p < 2; ++p) {
-    const Nf4Table T = make_table(block_scale(cs[p].q, cs[p].s2));
+    const Nf4Table T = make_table<CB>(block_scale(cs[p].q, cs[p].s2));
     const int flip = (t >> 2) & 1;
     const uint32_t cx = cs[p].c.x, cy = cs[p].c.y;
 #pragma unroll
@@ -1664,7 +1669,7 @@ __global__ __launch_bounds__(kThreads, 1) void nf4_dx_half_kernel(Nf4View W, con
 #pragma unroll
   for (int j = 0; j < 4; ++j) F.b0[j] = rd16(smem + kOp + bm + j * 2048 + fo.o0);
   int st = 0;
-#define QLORA_DXH_SUB(u) dxh_substep<u>(smem, d, st + u, acc, F, cs, ys, ao, bm, fo)
+#define QLORA_DXH_SUB(u) dxh_substep<CB, u>(smem, d, st + u, acc, F, cs, ys, ao, bm, fo)
   for (; st + 8 <= d.nsub; st += 8) {
     QLORA_DXH_SUB(0); QLORA_DXH_SUB(1); QLORA_DXH_SUB(2); QLORA_DXH_SUB(3);
     QLORA_DXH_SUB(4); QLORA_DXH_SUB(5); QLORA_DXH_SUB(6); QLORA_DXH_SUB(7);
@@ -1719,21 +1724,24 @@ __global__ __launch_bounds__(kThreads, 1) void nf4_dx_half_kernel(Nf4View W, con
 
 }  // namespace
 
-hipError_t launch_fwd(const Nf4View& W, const bf16_t* X, int64_t M, const bf16_t* U, const bf16_t* B, int r,
-                      float s, bf16_t* Y, hipStream_t st) {
+namespace {
+
+template <int CB>
+hipError_t launch_fwd_cb(const Nf4View& W, const bf16_t* X, int64_t M, const bf16_t* U, const bf16_t* B, int r,
+                        float s, bf16_t* Y, hipStream_t st) {
   const int tiles_n = (int)((W.N + kTile - 1) / kTile);
   const int tiles_m = (int)((M + kTile - 1) / kTile);
   const int tiles = tiles_n * tiles_m;
 #if defined(QLORA_FWD_LDS_WEIGHTS) || defined(QLORA_FWD_EIGHT_WAVES)
 #if defined(QLORA_FWD_LDS_WEIGHTS)
-  auto* fn = &nf4_fwd_kernel;
+  auto* fn = &nf4_fwd_kernel<CB>;
   const size_t lds = kLdsFwd;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
                                      (int)lds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(fn, dim3(tiles), dim3(kThreads), lds, st, W, X, M, U, B, r, s, Y, tiles_n, tiles_m);
 #else
-  auto* fn = &nf4_fwd_n32_kernel<8>;
+  auto* fn = &nf4_fwd_n32_kernel<CB, 8>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
                                      (int)kLdsFwdR);
   if (e != hipSuccess) return e;
@@ -1747,14 +1755,14 @@ hipError_t launch_fwd(const Nf4View& W, const bf16_t* X, int64_t M, const bf16_t
   const int cus = device_cu_count();   // the tail split needs the round size
   const int rest = tiles % cus;
   const int main_tiles = (tiles > cus && rest > 0 && 2 * rest <= cus) ? tiles - rest : tiles;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&nf4_fwd_r_kernel),
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&nf4_fwd_r_kernel<CB>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsFwdR);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(nf4_fwd_r_kernel, dim3(main_tiles), dim3(kThreads), kLdsFwdR, st, W, X, M, U, B, r, s, Y,
+  hipLaunchKernelGGL(nf4_fwd_r_kernel<CB>, dim3(main_tiles), dim3(kThreads), kLdsFwdR, st, W, X, M, U, B, r, s, Y,
                      tiles_n, tiles_m);
   e = hipGetLastError();
   if (e != hipSuccess || main_tiles == tiles) return e;
-  auto* tail = &nf4_fwd_n32_kernel<4>;
+  auto* tail = &nf4_fwd_n32_kernel<CB, 4>;
   e = hipFuncSetAttribute(reinterpret_cast<const void*>(tail), hipFuncAttributeMaxDynamicSharedMemorySize,
                           (int)kLdsFwdR);
   if (e != hipSuccess) return e;
@@ -1764,8 +1772,9 @@ hipError_t launch_fwd(const Nf4View& W, const bf16_t* X, int64_t M, const bf16_t
 #endif
 }
 
-hipError_t launch_dx(const Nf4View& W, const bf16_t* dY, int64_t M, const bf16_t* G, const bf16_t* A, int r,
-                     float s, bf16_t* dX, hipStream_t st) {
+template <int CB>
+hipError_t launch_dx_cb(const Nf4View& W, const bf16_t* dY, int64_t M, const bf16_t* G, const bf16_t* A, int r,
+                       float s, bf16_t* dX, hipStream_t st) {
   const int tiles_k = (int)((W.K + kTile - 1) / kTile);
   const int tiles_m = (int)((M + kTile - 1) / kTile);
   const int tiles = tiles_k * tiles_m;
@@ -1774,19 +1783,37 @@ hipError_t launch_dx(const Nf4View& W, const bf16_t* dY, int64_t M, const bf16_t
   const int cus = device_cu_count();
   const int rest = tiles % cus;
   const int main_tiles = (tiles > cus && rest > 0 && 2 * rest <= cus) ? tiles - rest : tiles;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&nf4_dx_kernel),
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&nf4_dx_kernel<CB>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsDx);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(nf4_dx_kernel, dim3(main_tiles), dim3(kThreads), kLdsDx, st, W, dY, M, G, A, r, s, dX,
+  hipLaunchKernelGGL(nf4_dx_kernel<CB>, dim3(main_tiles), dim3(kThreads), kLdsDx, st, W, dY, M, G, A, r, s, dX,
                      tiles_k, tiles_m);
   e = hipGetLastError();
   if (e != hipSuccess || main_tiles == tiles) return e;
-  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&nf4_dx_half_kernel),
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&nf4_dx_half_kernel<CB>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsDx);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(nf4_dx_half_kernel, dim3(2 * (tiles - main_tiles)), dim3(kThreads), kLdsDx, st, W, dY, M, G, A,
+  hipLaunchKernelGGL(nf4_dx_half_kernel<CB>, dim3(2 * (tiles - main_tiles)), dim3(kThreads), kLdsDx, st, W, dY, M, G, A,
                      r, s, dX, tiles_k, main_tiles);
   return hipGetLastError();
+}
+
+}  // namespace
+
+// The codebook is a template parameter of the kernels (its levels are
+// literals in the block-table code).
+hipError_t launch_fwd(const Nf4View& W, const bf16_t* X, int64_t M, const bf16_t* U, const bf16_t* B, int r,
+                      float s, bf16_t* Y, hipStream_t st) {
+  if (W.codebook == kCbFp4) return launch_fwd_cb<kCbFp4>(W, X, M, U, B, r, s, Y, st);
+  if (W.codebook == kCbInt4) return launch_fwd_cb<kCbInt4>(W, X, M, U, B, r, s, Y, st);
+  return launch_fwd_cb<kCbNf4>(W, X, M, U, B, r, s, Y, st);
+}
+
+hipError_t launch_dx(const Nf4View& W, const bf16_t* dY, int64_t M, const bf16_t* G, const bf16_t* A, int r,
+                     float s, bf16_t* dX, hipStream_t st) {
+  if (W.codebook == kCbFp4) return launch_dx_cb<kCbFp4>(W, dY, M, G, A, r, s, dX, st);
+  if (W.codebook == kCbInt4) return launch_dx_cb<kCbInt4>(W, dY, M, G, A, r, s, dX, st);
+  return launch_dx_cb<kCbNf4>(W, dY, M, G, A, r, s, dX, st);
 }
 
 }  // namespace qlora

@@ -95,9 +95,10 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-// bf16 (round to nearest even) of the unscaled NF4 level c.
+// bf16 (round to nearest even) of the unscaled level c of codebook CB.
+template <int CB>
 __device__ __forceinline__ uint32_t level_bf16(int c) {
-  return pack_bf16x2(u2f(kNf4LevelBits[c]), 0.0f) & 0xFFFFu;
+  return pack_bf16x2(u2f(cb_level_bits<CB>(c)), 0.0f) & 0xFFFFu;
 }
 
 __device__ __forceinline__ f32x4_t mfma16x16x32(const bf16x8_t& a, const bf16x8_t& b, const f32x4_t& c) {
@@ -171,7 +172,7 @@ __global__ __launch_bounds__(kDownThreads) void lora_down_kernel(const GemvJob* 
 // reads its two blocks' absmax codes with one 2-byte load, otherwise with two
 // byte loads.  A row of at most 32768 columns touches at most three
 // 256-block groups, so three group scales per row cover a tile.
-template <bool kPair>
+template <bool kPair, int CB>
 __global__ __launch_bounds__(kGvThreads) void nf4_gemv_kernel(const GemvJob* __restrict__ jobs,
                                                               const int4* __restrict__ segs,
                                                               const int* __restrict__ range, int max_steps) {
@@ -183,10 +184,10 @@ __global__ __launch_bounds__(kGvThreads) void nf4_gemv_kernel(const GemvJob* __r
   // tables, once: thread (w, lane) writes code-byte entries e = w + 16 i of
   // column lane; the first 256 threads write Q8; the first 32 the zero run
   {
-    const uint32_t lo = level_bf16(__builtin_amdgcn_readfirstlane(w));   // w is wave-uniform: a scalar load
+    const uint32_t lo = level_bf16<CB>(__builtin_amdgcn_readfirstlane(w));   // w is wave-uniform: a scalar load
 #pragma unroll
     for (int i = 0; i < 16; ++i)
-      lds_st32((uint32_t)(w + 16 * i) * 256u + 4u * lane, lo | (level_bf16(i) << 16));
+      lds_st32((uint32_t)(w + 16 * i) * 256u + 4u * lane, lo | (level_bf16<CB>(i) << 16));
     if (tid < 256) lds_st32(kQ8Off + 4u * tid, __builtin_bit_cast(uint32_t, q8_value((uint32_t)tid)));
     if (tid < kZeroBytes / 16) lds_st128(kZeroOff + 16u * tid, make_uint4(0u, 0u, 0u, 0u));
   }
@@ -460,23 +461,35 @@ LaunchPlan plan_launch(const GemvJob* jobs, int njobs, bool pair, int max_groups
 
 int device_cus() { return std::min(device_cu_count(), kMaxGvGroups); }
 
-template <bool kPair>
+template <bool kPair, int CB>
 hipError_t launch_main(const GemvJob* djobs, const int4* segs, const int* range, int groups, int max_steps,
                        hipStream_t st) {
   if (groups <= 0) return hipSuccess;
   // The kernel addresses its LDS from 0, which holds only while the
   // compiler has given it no static LDS.
   hipFuncAttributes fa{};
-  hipError_t e = hipFuncGetAttributes(&fa, reinterpret_cast<const void*>(&nf4_gemv_kernel<kPair>));
+  hipError_t e = hipFuncGetAttributes(&fa, reinterpret_cast<const void*>(&nf4_gemv_kernel<kPair, CB>));
   if (e != hipSuccess) return e;
   if (fa.sharedSizeBytes != 0) return hipErrorInvalidKernelFile;
   const size_t lds = (size_t)kXOff + (size_t)max_steps * 1024;
-  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&nf4_gemv_kernel<kPair>),
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&nf4_gemv_kernel<kPair, CB>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(nf4_gemv_kernel<kPair>, dim3(groups), dim3(kGvThreads), lds, st, djobs, segs, range,
+  hipLaunchKernelGGL((nf4_gemv_kernel<kPair, CB>), dim3(groups), dim3(kGvThreads), lds, st, djobs, segs, range,
                      max_steps);
   return hipGetLastError();
+}
+
+// The two launches of the GEMV (jobs whose absmax codes pair up, then the
+// rest), for codebook CB.
+template <int CB>
+hipError_t launch_both(const GemvLaunch& L, const GemvJob* djobs, const uint8_t* dev, hipStream_t st) {
+  const hipError_t e = launch_main<true, CB>(djobs, reinterpret_cast<const int4*>(dev + L.seg_off[0]),
+                                             reinterpret_cast<const int*>(dev + L.rng_off[0]), L.groups[0],
+                                             L.max_steps[0], st);
+  if (e != hipSuccess) return e;
+  return launch_main<false, CB>(djobs, reinterpret_cast<const int4*>(dev + L.seg_off[1]),
+                                reinterpret_cast<const int*>(dev + L.rng_off[1]), L.groups[1], L.max_steps[1], st);
 }
 
 }  // namespace
@@ -496,8 +509,8 @@ size_t gemv_lds_bytes(int64_t K) {
   return (size_t)kXOff + (size_t)nsteps * 1024;
 }
 
-hipError_t gemv_prepare(const GemvJob* jobs, int njobs, void* table, size_t table_bytes, GemvLaunch* out,
-                        hipStream_t st) {
+hipError_t gemv_prepare(const GemvJob* jobs, int njobs, int codebook, void* table, size_t table_bytes,
+                        GemvLaunch* out, hipStream_t st) {
   const int groups = device_cus();
   const LaunchPlan lp[2] = {plan_launch(jobs, njobs, true, groups), plan_launch(jobs, njobs, false, groups)};
   std::vector<int2> down;
@@ -516,6 +529,7 @@ hipError_t gemv_prepare(const GemvJob* jobs, int njobs, void* table, size_t tabl
   }
   L.down_off = off;
   L.n_down = (int)down.size();
+  L.codebook = codebook;
   off += up256(down.size() * sizeof(int2));
   if (off > table_bytes) return hipErrorInvalidValue;   // the caller's check makes this unreachable
   std::vector<uint8_t> host(off, 0);
@@ -541,12 +555,9 @@ hipError_t gemv_run(const GemvLaunch& L, hipStream_t st) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const hipError_t e = launch_main<true>(djobs, reinterpret_cast<const int4*>(dev + L.seg_off[0]),
-                                         reinterpret_cast<const int*>(dev + L.rng_off[0]), L.groups[0],
-                                         L.max_steps[0], st);
-  if (e != hipSuccess) return e;
-  return launch_main<false>(djobs, reinterpret_cast<const int4*>(dev + L.seg_off[1]),
-                            reinterpret_cast<const int*>(dev + L.rng_off[1]), L.groups[1], L.max_steps[1], st);
+  if (L.codebook == kCbFp4) return launch_both<kCbFp4>(L, djobs, dev, st);
+  if (L.codebook == kCbInt4) return launch_both<kCbInt4>(L, djobs, dev, st);
+  return launch_both<kCbNf4>(L, djobs, dev, st);
 }
 
 }  // namespace qlora

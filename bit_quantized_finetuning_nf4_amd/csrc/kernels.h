@@ -14,6 +14,7 @@ struct Nf4View {
   const float* group_scale;
   int64_t N;  // rows
   int64_t K;  // cols, K % 64 == 0 on the GEMM/GEMV paths
+  int codebook;  // 0 NF4, 1 FP4, 2 Int4 (the values of qlora_codebook)
 };
 
 // Compute units of the current device (256 if the query fails).
@@ -74,9 +75,10 @@ struct GemvLaunch {
   uint64_t seg_off[2], rng_off[2], down_off;
   int32_t groups[2], max_steps[2];
   int32_t n_down;
+  int32_t codebook;  // shared by every job of the call
 };
-hipError_t gemv_prepare(const GemvJob* jobs, int njobs, void* table, size_t table_bytes, GemvLaunch* out,
-                        hipStream_t st);
+hipError_t gemv_prepare(const GemvJob* jobs, int njobs, int codebook, void* table, size_t table_bytes,
+                        GemvLaunch* out, hipStream_t st);
 hipError_t gemv_run(const GemvLaunch& L, hipStream_t st);
 
 }  // namespace qlora

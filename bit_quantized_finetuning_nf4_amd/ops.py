@@ -84,55 +84,54 @@ def workspace(nbytes, device):
 
 @dataclass
 class QuantizedWeight:
-    """An NF4 + double-quantized weight [rows x cols] held in torch tensors."""
+    """A 4-bit (NF4 unless another codebook is named) + double-quantized
+    weight [rows x cols] held in torch tensors."""
     rows: int
     cols: int
     codes: torch.Tensor        # uint8 [ceil(rows*cols/2)]
     absmax_q: torch.Tensor     # uint8 [nb]
     group_scale: torch.Tensor  # float32 [ng]
+    codebook: str = "nf4"      # "nf4", "fp4" or "int4"
 
     def desc(self) -> Nf4WeightDesc:
         return Nf4WeightDesc(self.rows, self.cols, BLOCKSIZE, GROUP_BLOCKS, self.codes.data_ptr(),
-                             self.absmax_q.data_ptr(), self.group_scale.data_ptr())
+                             self.absmax_q.data_ptr(), self.group_scale.data_ptr(), _codebook(self.codebook))
 
     @staticmethod
-    def empty(rows, cols, device):
+    def empty(rows, cols, device, codebook="nf4"):
         c, a, s = sizes(rows, cols)
         return QuantizedWeight(rows, cols,
                                torch.empty(c, dtype=torch.uint8, device=device),
                                torch.empty(a, dtype=torch.uint8, device=device),
-                               torch.empty(s // 4, dtype=torch.float32, device=device))
+                               torch.empty(s // 4, dtype=torch.float32, device=device), codebook)
 
     def nbytes(self):
         return self.codes.numel() + self.absmax_q.numel() + 4 * self.group_scale.numel()
 
 
-def quantize(W: torch.Tensor, out: Optional[QuantizedWeight] = None, codebook: str = "nf4") -> QuantizedWeight:
-    """bf16 W [rows x cols] -> 4-bit codes (NF4 unless another codebook is
-    named) + 8-bit absmax codes + fp32 group scales."""
+def quantize(W: torch.Tensor, out: Optional[QuantizedWeight] = None,
+             codebook: Optional[str] = None) -> QuantizedWeight:
+    """bf16 W [rows x cols] -> 4-bit codes + 8-bit absmax codes + fp32 group
+    scales.  The codebook is the one named, else out's, else NF4; the
+    result records it."""
     _need(W, torch.bfloat16, "W")
     rows, cols = (W.shape[0], W.shape[1]) if W.dim() == 2 else (1, W.numel())
     q = out if out is not None else QuantizedWeight.empty(rows, cols, W.device)
+    if codebook is not None:
+        _codebook(codebook)
+        q.codebook = codebook
     d = q.desc()
-    if codebook == "nf4":
-        check(lib().qlora_quantize(_ptr(W), ctypes.byref(d), _stream()), "qlora_quantize")
-    else:
-        check(lib().qlora_quantize_codebook(_ptr(W), ctypes.byref(d), _codebook(codebook), _stream()),
-              "qlora_quantize_codebook")
+    check(lib().qlora_quantize(_ptr(W), ctypes.byref(d), _stream()), "qlora_quantize")
     return q
 
 
-def dequant(q: QuantizedWeight, out: Optional[torch.Tensor] = None, codebook: str = "nf4") -> torch.Tensor:
-    """4-bit weight -> bf16 [rows x cols], with the codebook it was quantized with."""
+def dequant(q: QuantizedWeight, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """4-bit weight -> bf16 [rows x cols], with its codebook."""
     if out is None:
         out = torch.empty(q.rows, q.cols, dtype=torch.bfloat16, device=q.codes.device)
     _need(out, torch.bfloat16, "out")
     d = q.desc()
-    if codebook == "nf4":
-        check(lib().qlora_dequant(ctypes.byref(d), _ptr(out), _stream()), "qlora_dequant")
-    else:
-        check(lib().qlora_dequant_codebook(ctypes.byref(d), _codebook(codebook), _ptr(out), _stream()),
-              "qlora_dequant_codebook")
+    check(lib().qlora_dequant(ctypes.byref(d), _ptr(out), _stream()), "qlora_dequant")
     return out
 
 

@@ -62,7 +62,9 @@ typedef enum {
                               on the GEMM/GEMV paths, rows % 8 != 0 or
                               rows*cols/2 >= 2^32 on the GEMM paths, M*rows
                               or M*cols >= 2^31 on the fused GEMMs, r
-                              outside [0,128] or r % 8 != 0, too many jobs */
+                              outside [0,128] or r % 8 != 0, too many jobs,
+                              an unknown codebook, GEMV jobs of different
+                              codebooks in one call */
   QLORA_E_WORKSPACE = 5,   /* ws_bytes smaller than qlora_workspace_bytes()  */
   QLORA_E_HIP = 6          /* a HIP launch/copy error; see qlora_last_hip_error */
 } qlora_status;
@@ -77,6 +79,23 @@ typedef enum {
 /* A quantized weight: host struct holding device pointers.
  * codes: ceil(rows*cols/2) bytes; absmax_q: nb bytes; group_scale: ng fp32,
  * with nb = ceil(rows*cols/64), ng = ceil(nb/256). */
+/* 4-bit codebooks.  The pages compare NF4 with FP4 and Int4 and report that
+ * NF4 has the lower quantization error (deepfa.ir blog, "1. 4-bit
+ * NormalFloat (NF4)" and its results list).  FP4 is E2M1 (sign, two exponent
+ * bits with bias 1, one mantissa bit) divided by its largest value 6; its
+ * two zeros are both +0 (codes 7 and 8, and code 8 is never produced).
+ * Int4 is k/7 for the two's-complement k = -8..7 (code 0, -8/7, is never
+ * produced from absmax-normalised values).  All three are quantized the
+ * same way: blockwise absmax, nearest level with ties to the lower index,
+ * 8-bit double quantization; an all-zero block stores the code of the
+ * level 0 (7 for NF4 and FP4, 8 for Int4).  A weight descriptor names its
+ * codebook, and every call that reads or writes the weight uses it. */
+typedef enum {
+  QLORA_CODEBOOK_NF4 = 0,
+  QLORA_CODEBOOK_FP4 = 1,
+  QLORA_CODEBOOK_INT4 = 2
+} qlora_codebook;
+
 typedef struct {
   int64_t rows;           /* N, output features                       */
   int64_t cols;           /* K, input features                        */
@@ -85,6 +104,7 @@ typedef struct {
   uint8_t* codes;
   uint8_t* absmax_q;
   float* group_scale;
+  int32_t codebook;       /* qlora_codebook of the 4-bit codes (0 = NF4) */
 } qlora_nf4_weight;
 
 /* One batch-1 decode product y = deq(W) x + (alpha/r) B (A x). */
@@ -127,7 +147,8 @@ qlora_status qlora_sizes(int64_t rows, int64_t cols, int32_t blocksize, int32_t 
 size_t qlora_workspace_bytes(qlora_op op, int64_t M, int64_t N, int64_t K, int32_t r, int32_t njobs);
 
 /* Quantize bf16 W [rows x cols] into q (codes, absmax_q, group_scale are
- * overwritten).  Any rows*cols >= 1 (ragged last block and group allowed).
+ * overwritten) with the levels of q->codebook.  Any rows*cols >= 1 (ragged
+ * last block and group allowed).
  * Glossary "Definition" and deepfa.ir "1. NF4" / "2. Double Quantization". */
 qlora_status qlora_quantize(const uint16_t* W, const qlora_nf4_weight* q, void* stream);
 
@@ -135,36 +156,10 @@ qlora_status qlora_quantize(const uint16_t* W, const qlora_nf4_weight* q, void* 
  * Glossary "Definition": converted back to BFloat16 for the calculation. */
 qlora_status qlora_dequant(const qlora_nf4_weight* q, uint16_t* W_out, void* stream);
 
-/* 4-bit codebooks.  The pages compare NF4 with FP4 and Int4 and report that
- * NF4 has the lower quantization error (deepfa.ir blog, "1. 4-bit
- * NormalFloat (NF4)" and its results list).  FP4 is E2M1 (sign, two exponent
- * bits with bias 1, one mantissa bit) divided by its largest value 6; its
- * two zeros are both +0 (codes 7 and 8, and code 8 is never produced).
- * Int4 is k/7 for the two's-complement k = -8..7 (code 0, -8/7, is never
- * produced from absmax-normalised values).  All three are quantized the
- * same way: blockwise absmax, nearest level with ties to the lower index,
- * 8-bit double quantization; an all-zero block stores the code of the
- * level 0 (7 for NF4 and FP4, 8 for Int4).  The fused GEMMs and the GEMV
- * read NF4 only. */
-typedef enum {
-  QLORA_CODEBOOK_NF4 = 0,
-  QLORA_CODEBOOK_FP4 = 1,
-  QLORA_CODEBOOK_INT4 = 2
-} qlora_codebook;
-
 /* The 16 fp32 levels of a codebook, ascending, as the device tables hold
  * them.  QLORA_E_NULL for a NULL out, QLORA_E_UNSUPPORTED for an unknown
  * codebook. */
 qlora_status qlora_codebook_levels(qlora_codebook cb, float out[16]);
-
-/* qlora_quantize / qlora_dequant with the levels of codebook cb (same
- * arguments, layout and errors; QLORA_E_UNSUPPORTED for an unknown
- * codebook).  A weight must be dequantized with the codebook it was
- * quantized with; the descriptor does not record it. */
-qlora_status qlora_quantize_codebook(const uint16_t* W, const qlora_nf4_weight* q, qlora_codebook cb,
-                                     void* stream);
-qlora_status qlora_dequant_codebook(const qlora_nf4_weight* q, qlora_codebook cb, uint16_t* W_out,
-                                    void* stream);
 
 /* Forward: Y [M x N] = X deq(W)^T + s (X A^T) B^T, s = RN32(alpha / r).
  * X [M x K], A [r x K], B [N x r], Y bf16 (overwritten).  r == 0 (A = B =

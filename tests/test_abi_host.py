@@ -158,10 +158,17 @@ def test_codebook_calls_reject_bad_arguments_on_the_host(L):
     assert L.qlora_codebook_levels(0, None) == 1
     fake = ctypes.c_void_p(4096)
     d = _desc(codes=4096, aq=8192, s2=12288)
-    assert L.qlora_quantize_codebook(fake, ctypes.byref(d), 3, None) == 4
-    assert L.qlora_quantize_codebook(None, ctypes.byref(d), 1, None) == 1
-    assert L.qlora_quantize_codebook(ctypes.c_void_p(4098), ctypes.byref(d), 2, None) == 2
-    assert L.qlora_dequant_codebook(ctypes.byref(d), 7, fake, None) == 4
-    assert L.qlora_dequant_codebook(ctypes.byref(d), 1, None, None) == 1
-    neg = _desc(rows=0, codes=4096, aq=8192, s2=12288)
-    assert L.qlora_dequant_codebook(ctypes.byref(neg), 2, fake, None) == 3
+    for cb in (3, -1, 100):
+        d.codebook = cb
+        assert L.qlora_quantize(fake, ctypes.byref(d), None) == 4
+        assert L.qlora_dequant(ctypes.byref(d), fake, None) == 4
+        assert L.qlora_linear_fwd(ctypes.byref(d), fake, 4, None, None, 0, 0.0, fake, None, None, 0, None) == 4
+
+
+def test_gemv_rejects_mixed_codebooks_on_the_host(L):
+    d0 = _desc(codes=4096, aq=8192, s2=12288)
+    d1 = _desc(codes=4096, aq=8192, s2=12288)
+    d1.codebook = 2
+    jobs = (_lib.GemvJobDesc * 2)(_lib.GemvJobDesc(ctypes.pointer(d0), 4096, None, None, 0, 0.0, 4096),
+                                   _lib.GemvJobDesc(ctypes.pointer(d1), 4096, None, None, 0, 0.0, 4096))
+    assert L.qlora_gemv(jobs, 2, ctypes.c_void_p(4096), 1 << 20, None) == 4

@@ -23,25 +23,25 @@ def _job(N, K, r, seed, ab_std=0.01):
                 B=g((N, r), ab_std) if r else None, alpha=16.0)
 
 
-def _oracle_y(d):
-    c, a, s = oracle.quantize(d["W"])
-    Wd = oracle.bf16_bits_to_f64(oracle.dequant(c, a, s, d["W"].size)).reshape(d["W"].shape)
+def _oracle_y(d, codebook="nf4"):
+    c, a, s = oracle.quantize(d["W"], codebook)
+    Wd = oracle.bf16_bits_to_f64(oracle.dequant(c, a, s, d["W"].size, codebook)).reshape(d["W"].shape)
     f = lambda k: None if d[k] is None else oracle.bf16_bits_to_f64(d[k]).reshape(d[k].shape)
     return oracle.gemv(Wd, f("x"), f("A"), f("B"), d["alpha"])
 
 
-def _run(ds, label):
-    print(f"[gemv parity] {label}: {len(ds)} jobs", flush=True)
+def _run(ds, label, codebook="nf4"):
+    print(f"[gemv parity] {codebook} {label}: {len(ds)} jobs", flush=True)
     jobs = []
     for d in ds:
-        q = ops.quantize(bits_to_torch(d["W"]))
+        q = ops.quantize(bits_to_torch(d["W"]), codebook=codebook)
         jobs.append(ops.GemvJob(q, bits_to_torch(d["x"]),
                                 None if d["A"] is None else bits_to_torch(d["A"]),
                                 None if d["B"] is None else bits_to_torch(d["B"]), d["alpha"]))
     ys = ops.gemv(jobs)
     torch.cuda.synchronize()
     for i, (d, y) in enumerate(zip(ds, ys)):
-        assert_close(torch_to_f64(y), _oracle_y(d), f"{label} job {i}")
+        assert_close(torch_to_f64(y), _oracle_y(d, codebook), f"{label} job {i}")
 
 
 def test_small_config_one_token():
@@ -93,3 +93,20 @@ def test_prepared_plan_reruns_with_new_inputs():
         torch.cuda.synchronize()
         for i, (d, y) in enumerate(zip(ds, ys)):
             assert_close(torch_to_f64(y), _oracle_y(d), f"run {run} job {i}")
+
+
+@pytest.mark.parametrize("codebook", ["fp4", "int4"])
+def test_other_codebooks(codebook):
+    # FP4 and Int4 weights (one codebook per call), single and grouped jobs
+    _run([_job(1024, 1024, 64, seed=31)], "N1024 K1024 r64", codebook)
+    _run([_job(37, 22016, 64, seed=32), _job(300, 1536, 8, seed=33), _job(64, 320, 0, seed=34)], "grouped",
+         codebook)
+
+
+def test_mixed_codebooks_in_one_call_are_rejected():
+    d = _job(64, 128, 0, seed=35)
+    W = bits_to_torch(d["W"])
+    jobs = [ops.GemvJob(ops.quantize(W, codebook="nf4"), bits_to_torch(d["x"]), None, None, 0.0),
+            ops.GemvJob(ops.quantize(W, codebook="fp4"), bits_to_torch(d["x"]), None, None, 0.0)]
+    with pytest.raises(RuntimeError, match="UNSUPPORTED"):
+        ops.gemv(jobs)

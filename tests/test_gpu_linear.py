@@ -18,17 +18,17 @@ from tests.helpers import assert_close, bits_to_torch, torch_to_bits, torch_to_f
 pytestmark = pytest.mark.gpu
 
 
-def _oracle_deq(W_bits):
-    c, a, s = oracle.quantize(W_bits)
-    return oracle.bf16_bits_to_f64(oracle.dequant(c, a, s, W_bits.size)).reshape(W_bits.shape)
+def _oracle_deq(W_bits, codebook="nf4"):
+    c, a, s = oracle.quantize(W_bits, codebook)
+    return oracle.bf16_bits_to_f64(oracle.dequant(c, a, s, W_bits.size, codebook)).reshape(W_bits.shape)
 
 
-def _run(d, label, save_u=True, need_dx=True, check_u=True):
-    print(f"[linear parity] {label}", flush=True)
+def _run(d, label, save_u=True, need_dx=True, check_u=True, codebook="nf4"):
+    print(f"[linear parity] {codebook} {label}", flush=True)
     W = bits_to_torch(d["W"])
     X, A, B, dY = (bits_to_torch(d[k]) if d[k] is not None else None for k in ("X", "A", "B", "dY"))
     alpha = d["alpha"]
-    q = ops.quantize(W)
+    q = ops.quantize(W, codebook=codebook)
     if A is not None:
         Y, U = ops.linear_fwd(q, X, A, B, alpha, save_u=True)
     else:
@@ -36,7 +36,7 @@ def _run(d, label, save_u=True, need_dx=True, check_u=True):
     dX, dA, dB = ops.linear_bwd(q, X, dY, A, B, alpha, U=U if save_u else None, need_dx=need_dx)
     torch.cuda.synchronize()
 
-    Wd = _oracle_deq(d["W"])
+    Wd = _oracle_deq(d["W"], codebook)
     f = lambda k: None if d[k] is None else oracle.bf16_bits_to_f64(d[k]).reshape(d[k].shape)
     Xr, Ar, Br, dYr = f("X"), f("A"), f("B"), f("dY")
     Yr = oracle.linear_fwd(Wd, Xr, Ar, Br, alpha)
@@ -154,3 +154,11 @@ def test_workspace_too_small_is_rejected_without_launch():
     ws = torch.empty(16, dtype=torch.uint8, device="cuda")
     with pytest.raises(RuntimeError, match="WORKSPACE"):
         ops.linear_fwd(q, X, A, B, 16.0, ws=ws)
+
+
+@pytest.mark.parametrize("codebook", ["fp4", "int4"])
+@pytest.mark.parametrize("M,N,K,r", [(300, 1032, 1088, 64), (4300, 360, 4160, 16)])
+def test_other_codebooks(codebook, M, N, K, r):
+    # FP4 and Int4 weights through the fused forward and backward, including
+    # the half-tile dX launch of the second shape
+    _run(_case(M, N, K, r, seed=M + N + K + r + 1), f"M{M} N{N} K{K} r{r}", codebook=codebook)

@@ -20,7 +20,7 @@ pytestmark = pytest.mark.gpu
 def _gpu_quantize(bits, shape, codebook="nf4"):
     W = bits_to_torch(bits.reshape(shape))
     q = ops.quantize(W, codebook=codebook)
-    deq = ops.dequant(q, codebook=codebook)
+    deq = ops.dequant(q)
     torch.cuda.synchronize()
     return (q.codes.cpu().numpy(), q.absmax_q.cpu().numpy(), q.group_scale.cpu().numpy(),
             torch_to_bits(deq).ravel())
@@ -204,7 +204,7 @@ def test_nf4_has_the_lowest_error_on_the_gpu():
     ref = W.double()
     err = {}
     for cb in ("nf4", "fp4", "int4"):
-        back = ops.dequant(ops.quantize(W, codebook=cb), codebook=cb).double()
+        back = ops.dequant(ops.quantize(W, codebook=cb)).double()
         err[cb] = ((back - ref).pow(2).mean().sqrt() / ref.pow(2).mean().sqrt()).item()
     print(f"[codebook rel rmse] {err}", flush=True)
     assert err["nf4"] < err["fp4"] and err["nf4"] < err["int4"], err
