@@ -16,7 +16,7 @@ Sources (the QLoRA pages):
     "2. Double Quantization" and "QLoRA's Working Process".
 
 Where those pages leave a step open, the reading taken is stated in the
-docstring of the function that implements it (readings R1-R16).
+docstring of the function that implements it (readings R1-R17).
 
 Every function here is pinned by a test in ``tests/test_oracle_*.py``
 against something other than itself (closed forms, exact rational
@@ -30,6 +30,7 @@ from .quant import (nf4_encode, q8_encode, quantize, dequant, storage_sizes,
 from .linear import linear_fwd, linear_bwd, adapter_grads, gemv, lora_scale
 from .codebooks import fp4_levels, int4_levels, e2m1_value, zero_code, CODEBOOKS
 from .codebooks import levels as codebook_levels
+from .optim import adamw_step
 
 __all__ = [
     "nf4_levels", "nf4_levels_fp64", "q8_levels", "NF4_OFFSET",
@@ -38,4 +39,5 @@ __all__ = [
     "BLOCKSIZE", "GROUP_BLOCKS",
     "linear_fwd", "linear_bwd", "gemv", "lora_scale",
     "fp4_levels", "int4_levels", "e2m1_value", "zero_code", "CODEBOOKS", "codebook_levels",
+    "adamw_step",
 ]
