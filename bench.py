@@ -229,6 +229,37 @@ def codebook_study(L, dev, q_bytes, reps=5):
     return res
 
 
+def optimizer_study(L, r, dev, reps=5):
+    """The AdamW step over every LoRA value of the layer set (one flat fp32
+    buffer each for p, g, m, v and a bf16 copy; 30 bytes per value), with the
+    moments on the device and, as a paged optimizer's CPU-resident states,
+    in pinned host memory."""
+    import torch
+    from bit_quantized_finetuning_nf4_amd import ops
+    n = sum(r * (o["N"] + o["K"]) for o in L)
+    g = torch.randn(n, device=dev) * 1e-3
+    p = torch.randn(n, device=dev) * 1e-2
+    pb = torch.empty(n, dtype=torch.bfloat16, device=dev)
+    res = {"values": n, "bytes_per_value": 30}
+    for where in ("device", "pinned_host"):
+        if where == "device":
+            m, v = torch.zeros(n, device=dev), torch.zeros(n, device=dev)
+        else:
+            m, v = torch.zeros(n, pin_memory=True), torch.zeros(n, pin_memory=True)
+        ops.adamw(p, g, m, v, 1, p_bf16=pb)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for t in range(reps):
+            ops.adamw(p, g, m, v, t + 2, p_bf16=pb)
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / reps
+        res[f"{where}_moments"] = {"ms": ms, "gbps": 30 * n / (ms * 1e-3) / 1e9}
+        del m, v
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -239,7 +270,8 @@ def main():
     ap.add_argument("--decode-passes", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-codebook-study", action="store_true",
-                    help="skip quantizing the layer set with FP4 and Int4 after the timed steps")
+                    help="skip the side studies after the timed steps: the layer set quantized with FP4 and "
+                         "Int4, and the AdamW step over its LoRA values")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after the timed steps, run one elementwise copy (negation) of this many MiB: "
                          "a kernel of known traffic for scaling the FETCH_SIZE / WRITE_SIZE counters")
@@ -402,6 +434,8 @@ def main():
     if not args.no_codebook_study:
         out["codebooks"] = codebook_study(L, dev, q_bytes)
         log(f"[bench] codebooks {out['codebooks']}")
+        out["optimizer"] = optimizer_study(L, r, dev)
+        log(f"[bench] optimizer {out['optimizer']}")
 
     # ---- 80-layer batch-1 decode pass (about 65e9 weights) ----
     if args.decode_layers > 0:

@@ -22,7 +22,7 @@ STATUS_NAMES = {
 EXPORTS = [
     "qlora_status_str", "qlora_last_hip_error", "qlora_version", "qlora_nf4_levels",
     "qlora_sizes", "qlora_workspace_bytes", "qlora_quantize", "qlora_dequant",
-    "qlora_codebook_levels",
+    "qlora_codebook_levels", "qlora_adamw",
     "qlora_linear_fwd", "qlora_linear_bwd", "qlora_gemv", "qlora_gemv_prepare", "qlora_gemv_run",
     "qlora_lora_down", "qlora_lora_dy_b", "qlora_lora_grads", "qlora_nf4_fwd", "qlora_nf4_dx",
 ]
@@ -103,6 +103,8 @@ def lib():
     L.qlora_dequant.argtypes = [W, vp, vp]
     L.qlora_codebook_levels.restype = ctypes.c_int
     L.qlora_codebook_levels.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_float)]
+    L.qlora_adamw.restype = ctypes.c_int
+    L.qlora_adamw.argtypes = [vp, vp, vp, vp, vp, i64, f32, f32, f32, f32, f32, i32, vp]
     L.qlora_linear_fwd.restype = ctypes.c_int
     L.qlora_linear_fwd.argtypes = [W, vp, i64, vp, vp, i32, f32, vp, vp, vp, sz, vp]
     L.qlora_linear_bwd.restype = ctypes.c_int

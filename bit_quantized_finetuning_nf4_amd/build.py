@@ -17,7 +17,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libqlora.so")
-SOURCES = ["quantize.hip", "gemm.hip", "gemm_nf4.hip", "gemv.hip", "capi.hip"]
+SOURCES = ["quantize.hip", "gemm.hip", "gemm_nf4.hip", "gemv.hip", "optim.hip", "capi.hip"]
 ARCH = "gfx950"
 
 

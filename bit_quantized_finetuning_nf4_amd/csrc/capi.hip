@@ -11,6 +11,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstring>
 #include <vector>
 
@@ -215,6 +216,20 @@ size_t qlora_workspace_bytes(qlora_op op, int64_t M, int64_t N, int64_t K, int32
       return lora_part_bytes(M, N, K, r);
   }
   return 0;
+}
+
+qlora_status qlora_adamw(float* p, uint16_t* p_bf16, const float* grad, float* m, float* v, int64_t n,
+                         float lr, float beta1, float beta2, float eps, float weight_decay, int32_t step,
+                         void* stream) {
+  if (!p || !grad || !m || !v) return QLORA_E_NULL;
+  if (!aligned16(p) || !aligned16(grad) || !aligned16(m) || !aligned16(v) || (p_bf16 && !aligned16(p_bf16)))
+    return QLORA_E_ALIGN;
+  if (n <= 0 || step < 1) return QLORA_E_SHAPE;
+  if (!(beta1 >= 0.0f && beta1 < 1.0f) || !(beta2 >= 0.0f && beta2 < 1.0f) || !(eps > 0.0f) ||
+      !std::isfinite(lr) || !std::isfinite(weight_decay))
+    return QLORA_E_SHAPE;
+  return hip_status(launch_adamw(p, p_bf16, grad, m, v, n, lr, beta1, beta2, eps, weight_decay, step,
+                                 (hipStream_t)stream));
 }
 
 qlora_status qlora_quantize(const uint16_t* W, const qlora_nf4_weight* q, void* stream) {

@@ -21,6 +21,10 @@ struct Nf4View {
 int device_cu_count();
 
 // codebook: 0 NF4, 1 FP4, 2 Int4 (the values of qlora_codebook)
+// One AdamW step over n parameters (p_bf16 may be null); see optim.hip.
+hipError_t launch_adamw(float* p, bf16_t* p_bf16, const float* g, float* m, float* v, int64_t n, float lr,
+                        float beta1, float beta2, float eps, float weight_decay, int step, hipStream_t st);
+
 hipError_t launch_quantize(const bf16_t* W, int64_t numel, uint8_t* codes, uint8_t* absmax_q,
                            float* group_scale, int codebook, hipStream_t s);
 hipError_t launch_dequant(const uint8_t* codes, const uint8_t* absmax_q, const float* group_scale,

@@ -324,3 +324,19 @@ def nf4_dx(q: QuantizedWeight, dY, G=None, A=None, alpha: float = 0.0, out=None)
     check(lib().qlora_nf4_dx(ctypes.byref(d), _ptr(dY), M, _ptr(G), _ptr(A), r, float(alpha), _ptr(dX),
                              _stream()), "qlora_nf4_dx")
     return dX
+
+
+def adamw(p: torch.Tensor, grad: torch.Tensor, m: torch.Tensor, v: torch.Tensor, step: int, lr: float = 1e-4,
+          beta1: float = 0.9, beta2: float = 0.999, eps: float = 1e-8, weight_decay: float = 0.0,
+          p_bf16: Optional[torch.Tensor] = None):
+    """One AdamW step in place: fp32 p, grad, m, v of one shape (device or
+    pinned host memory); p_bf16 (optional, bf16) receives the bf16 copy."""
+    n = p.numel()
+    for t, name in ((p, "p"), (grad, "grad"), (m, "m"), (v, "v")):
+        if t.dtype != torch.float32 or not t.is_contiguous() or t.numel() != n:
+            raise ValueError(f"{name} must be a contiguous float32 tensor of {n} elements")
+    if p_bf16 is not None and (p_bf16.dtype != torch.bfloat16 or not p_bf16.is_contiguous() or p_bf16.numel() != n):
+        raise ValueError(f"p_bf16 must be a contiguous bfloat16 tensor of {n} elements")
+    check(lib().qlora_adamw(p.data_ptr(), None if p_bf16 is None else p_bf16.data_ptr(), grad.data_ptr(),
+                            m.data_ptr(), v.data_ptr(), n, lr, beta1, beta2, eps, weight_decay, step, _stream()),
+          "qlora_adamw")

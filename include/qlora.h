@@ -156,6 +156,22 @@ qlora_status qlora_quantize(const uint16_t* W, const qlora_nf4_weight* q, void* 
  * Glossary "Definition": converted back to BFloat16 for the calculation. */
 qlora_status qlora_dequant(const qlora_nf4_weight* q, uint16_t* W_out, void* stream);
 
+/* One AdamW step on n trainable values (the LoRA matrices after a backward
+ * pass; the pages' paged optimizers keep such states movable between GPU
+ * and CPU memory: glossary "Definition", deepfa.ir "3. Paged Optimizers").
+ * p [n] fp32 master values, grad [n] fp32 (dA or dB), m and v [n] fp32
+ * moments, all updated in place; p_bf16 [n] (nullable) receives the bf16
+ * copy the layer reads (round to nearest even).  For step >= 1:
+ *   m = b1 m + (1-b1) g;  v = b2 v + (1-b2) g^2;
+ *   p = p - lr ((m / (1 - b1^step)) / (sqrt(v / (1 - b2^step)) + eps) + wd p).
+ * Any pointer may be device memory or pinned host memory (hipHostMalloc):
+ * the kernel reads and writes host memory in place over the host link.
+ * Pointers 16-byte aligned, n >= 1, 0 <= beta < 1, eps > 0, step >= 1;
+ * QLORA_E_NULL / _ALIGN / _SHAPE otherwise. */
+qlora_status qlora_adamw(float* p, uint16_t* p_bf16, const float* grad, float* m, float* v, int64_t n,
+                         float lr, float beta1, float beta2, float eps, float weight_decay, int32_t step,
+                         void* stream);
+
 /* The 16 fp32 levels of a codebook, ascending, as the device tables hold
  * them.  QLORA_E_NULL for a NULL out, QLORA_E_UNSUPPORTED for an unknown
  * codebook. */

@@ -172,3 +172,14 @@ def test_gemv_rejects_mixed_codebooks_on_the_host(L):
     jobs = (_lib.GemvJobDesc * 2)(_lib.GemvJobDesc(ctypes.pointer(d0), 4096, None, None, 0, 0.0, 4096),
                                    _lib.GemvJobDesc(ctypes.pointer(d1), 4096, None, None, 0, 0.0, 4096))
     assert L.qlora_gemv(jobs, 2, ctypes.c_void_p(4096), 1 << 20, None) == 4
+
+
+def test_adamw_rejects_bad_arguments_on_the_host(L):
+    f = ctypes.c_void_p(4096)
+    a = lambda **k: L.qlora_adamw(k.get("p", f), k.get("pb", None), k.get("g", f), k.get("m", f), k.get("v", f),
+                                  k.get("n", 8), k.get("lr", 1e-3), k.get("b1", 0.9), k.get("b2", 0.999),
+                                  k.get("eps", 1e-8), k.get("wd", 0.0), k.get("t", 1), None)
+    assert a(p=None) == 1 and a(g=None) == 1 and a(m=None) == 1 and a(v=None) == 1
+    assert a(p=ctypes.c_void_p(4100)) == 2 and a(pb=ctypes.c_void_p(4098)) == 2
+    assert a(n=0) == 3 and a(t=0) == 3 and a(b1=1.0) == 3 and a(b2=-0.1) == 3 and a(eps=0.0) == 3
+    assert a(lr=float("nan")) == 3 and a(wd=float("inf")) == 3
