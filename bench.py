@@ -53,14 +53,20 @@ def gemv_bytes(N, K, r):
     return N * K // 2 + N * K // 64 + 4 * (-(-N * K // 16384)) + 2 * r * (N + K) + 2 * (N + K)
 
 
-def source_digest():
-    """Digest of every kernel source: traffic figures taken on other sources are not reported."""
+# the device code of each kernel whose traffic is reported: its source file
+# and the device headers it includes
+KERNEL_SOURCES = {"fwd_kernel": ["gemm_nf4.hip"], "dx_kernel": ["gemm_nf4.hip"],
+                  "quantize_kernel": ["quantize.hip"], "gemv_kernel": ["gemv.hip"]}
+DEVICE_HEADERS = ["device.h", "lds.h"]
+
+
+def source_digest(kernel):
+    """Digest of a kernel's device code: traffic figures taken on other code are not reported."""
     h = hashlib.sha256()
     d = os.path.join(ROOT, "bit_quantized_finetuning_nf4_amd", "csrc")
-    for f in sorted(os.listdir(d)):
-        if f.endswith((".hip", ".h")):
-            h.update(f.encode())
-            h.update(open(os.path.join(d, f), "rb").read())
+    for f in KERNEL_SOURCES[kernel] + DEVICE_HEADERS:
+        h.update(f.encode())
+        h.update(open(os.path.join(d, f), "rb").read())
     return h.hexdigest()[:16]
 
 
@@ -72,7 +78,7 @@ def traffic_for(kernel):
         return None
     d = json.load(open(p))
     e = d.get(kernel)
-    if not e or e.get("source_digest") != source_digest():
+    if not e or e.get("source_digest") != source_digest(kernel):
         return None
     return e.get("hbm_bytes_per_launch")
 
@@ -121,7 +127,7 @@ def summarize_pmc(fetch_csv, write_csv, copy_mib):
             fb = fetch[k][0] + sum(fetch[t][0] for t in tails if t in fetch)
             wb = write[k][0] + sum(write[t][0] for t in tails if t in write)
             fpl, wpl = fb / fetch[k][1] * f_scale, wb / write[k][1] * w_scale
-            out[name] = {"source_digest": source_digest(), "fetch_bytes_per_launch": fpl,
+            out[name] = {"source_digest": source_digest(name), "fetch_bytes_per_launch": fpl,
                          "write_bytes_per_launch": wpl, "hbm_bytes_per_launch": fpl + wpl}
     return out
 
