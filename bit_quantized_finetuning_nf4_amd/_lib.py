@@ -50,6 +50,7 @@ class GemvJobDesc(ctypes.Structure):
         ("r", ctypes.c_int32),
         ("alpha", ctypes.c_float),
         ("y", ctypes.c_void_p),
+        ("m", ctypes.c_int32),
     ]
 
 

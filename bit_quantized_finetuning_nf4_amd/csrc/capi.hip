@@ -28,9 +28,15 @@ constexpr size_t kAlign = 256;
 constexpr int kMaxRank = 128;
 constexpr int kMaxJobs = 4096;
 constexpr int64_t kMaxGemvCols = 32768;
+constexpr int32_t kMaxGemvTokens = 16;
 constexpr uint64_t kPlanMagic = 0x51474D56504C414EULL;   // marks a plan filled by qlora_gemv_prepare  // x is staged whole in LDS beside the 64 KiB table
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// GEMV scratch for u = A x: kMaxRank fp32 per token slot, max(m, 1) slots per job.
+size_t gemv_u_bytes(int64_t njobs, int64_t max_m) {
+  return align_up((size_t)njobs * (size_t)std::max<int64_t>(max_m, 1) * kMaxRank * sizeof(float));
+}
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -209,8 +215,8 @@ size_t qlora_workspace_bytes(qlora_op op, int64_t M, int64_t N, int64_t K, int32
       if (M <= 0 || N <= 0 || K <= 0 || r < 0 || r > kMaxRank) return 0;
       return bwd_layout(M, N, K, r).total;
     case QLORA_OP_GEMV:
-      if (njobs <= 0 || njobs > kMaxJobs || N <= 0) return 0;
-      return align_up((size_t)njobs * kMaxRank * sizeof(float)) + gemv_table_bound(njobs, N);
+      if (njobs <= 0 || njobs > kMaxJobs || N <= 0 || M < 0 || M > kMaxGemvTokens) return 0;
+      return gemv_u_bytes(njobs, M) + gemv_table_bound(njobs, N);
     case QLORA_OP_LORA:
       if (M <= 0 || N <= 0 || K <= 0 || r < 0 || r > kMaxRank) return 0;
       return lora_part_bytes(M, N, K, r);
@@ -405,10 +411,14 @@ qlora_status qlora_gemv_prepare(const qlora_gemv_job* jobs, int32_t njobs, void*
   if (!jobs || !plan) return QLORA_E_NULL;
   if (njobs <= 0) return QLORA_E_SHAPE;
   if (njobs > kMaxJobs) return QLORA_E_UNSUPPORTED;
+  int32_t max_m = 1;
   for (int i = 0; i < njobs; ++i) {
     const qlora_gemv_job& J = jobs[i];
     qlora_status st = check_weight(J.W);
     if (st != QLORA_OK) return st;
+    if (J.m < 0) return QLORA_E_SHAPE;
+    if (J.m > kMaxGemvTokens) return QLORA_E_UNSUPPORTED;
+    max_m = std::max(max_m, J.m);
     // one codebook per call: the kernel builds its decode table once
     if (J.W->codebook != jobs[0].W->codebook) return QLORA_E_UNSUPPORTED;
     if (J.W->cols % 64 != 0 || J.W->cols > kMaxGemvCols || J.W->rows > 0x7FFFFFFF) return QLORA_E_UNSUPPORTED;
@@ -434,13 +444,15 @@ qlora_status qlora_gemv_prepare(const qlora_gemv_job* jobs, int32_t njobs, void*
     D.A = J.r > 0 ? J.A : nullptr;
     D.B = J.r > 0 ? J.B : nullptr;
     D.y = J.y;
-    D.u = J.r > 0 ? reinterpret_cast<float*>(ws_at(ws, (size_t)i * kMaxRank * sizeof(float))) : nullptr;
+    D.u = J.r > 0 ? reinterpret_cast<float*>(ws_at(ws, (size_t)i * (size_t)max_m * kMaxRank * sizeof(float)))
+                  : nullptr;
     D.N = (int32_t)J.W->rows;
     D.K = (int32_t)J.W->cols;
     D.r = J.r;
     D.s = J.r > 0 ? (float)((double)J.alpha / (double)J.r) : 0.0f;
+    D.m = std::max(J.m, 1);
   }
-  const size_t u_bytes = align_up((size_t)njobs * kMaxRank * sizeof(float));
+  const size_t u_bytes = gemv_u_bytes(njobs, max_m);
   const size_t table_bytes = gemv_table_bound(njobs, 1);
   if (ws_bytes < u_bytes || ws_bytes - u_bytes < table_bytes) return QLORA_E_WORKSPACE;
   GemvLaunch L{};

@@ -65,6 +65,20 @@ constexpr int kQ8Off = kLutBytes, kZeroOff = kQ8Off + kQ8Bytes, kXOff = kZeroOff
 constexpr int kMaxGvGroups = 1024;                         // persistent workgroups per launch, at most
 constexpr int kDownThreads = 256;                          // u = A x: one workgroup per adapter row
 constexpr int kDownUnroll = 4;                             // 16-byte loads of A per thread in flight
+constexpr int kBtWaves = 16;                               // small-batch kernel: waves per workgroup
+constexpr int kBtThreads = 64 * kBtWaves;
+constexpr int kBtSets = 2;                                 // 16-row sets per wave
+constexpr int kBtRows = kBtWaves * kBtSets * 16;           // weight rows per tile (512)
+constexpr int kBtTokens = 16;                              // most tokens per job
+constexpr int kBtRank = 128;                               // largest adapter rank the library accepts
+constexpr int kBtChunkSteps = 8;                           // 128-column steps per staged x chunk
+constexpr int kBtXRow = kBtChunkSteps * 256 + 16;          // LDS bytes per token row of a chunk (padded)
+constexpr int kBtXBuf = kBtTokens * kBtXRow;
+constexpr int kBtSuRow = kBtRank * 2 + 16;                 // LDS bytes per token row of s u (padded)
+constexpr int kBtZeroOff = kQ8Off + kQ8Bytes, kBtZeroBytes = 2048;
+constexpr int kBtSuOff = kBtZeroOff + kBtZeroBytes, kBtXOff = kBtSuOff + kBtTokens * kBtSuRow;
+constexpr int kBtLds = kBtXOff + 2 * kBtXBuf;              // 139,008 bytes
+static_assert(kBtLds <= 160 * 1024, "LDS of the small-batch kernel");
 static_assert(kGvThreads == 1024, "the table fill below assumes 16 waves");
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
@@ -127,38 +141,54 @@ __device__ __forceinline__ bf16x8_t decode8(uint32_t c, uint32_t col) {
 
 }  // namespace
 
-// Phase 1: u = A x for every job with r > 0 (fp32, into the job's scratch).
-// One workgroup per adapter row: each thread keeps up to kDownUnroll
-// 16-byte loads of A (and of x, an L2 hit) in flight, then the workgroup
-// sums its partials.
+// Phase 1: u = A x for every job with r > 0 (fp32, into the job's scratch;
+// u[t r + j] for token t).  One workgroup per adapter row: each thread keeps
+// up to kDownUnroll 16-byte loads of A in flight and dots them with every
+// token's x (L2 hits), then the workgroup sums its partials.
 __global__ __launch_bounds__(kDownThreads) void lora_down_kernel(const GemvJob* __restrict__ jobs,
                                                                  const int2* __restrict__ map) {
-  __shared__ float part[kDownThreads / 64];
-  const int2 m = map[blockIdx.x];
-  const GemvJob& J = jobs[m.x];
-  const int K = J.K, row = m.y;
-  const rsrc_t arr = make_rsrc(J.A + (int64_t)row * K, (uint32_t)K * 2u);   // zero past the row
-  const rsrc_t xr = make_rsrc(J.x, (uint32_t)K * 2u);
-  float acc = 0.0f;
+  __shared__ float part[kBtTokens][kDownThreads / 64];
+  const int2 mp = map[blockIdx.x];
+  const GemvJob& J = jobs[mp.x];
+  const int K = J.K, row = mp.y, m = J.m;
+  const uint32_t kb = (uint32_t)K * 2u, xend = (uint32_t)m * kb;
+  const rsrc_t arr = make_rsrc(J.A + (int64_t)row * K, kb);   // zero past the row
+  const rsrc_t xr = make_rsrc(J.x, xend);
+  float acc[kBtTokens];
+#pragma unroll
+  for (int t = 0; t < kBtTokens; ++t) acc[t] = 0.0f;
   for (int c0 = 0; c0 < K / 8; c0 += kDownThreads * kDownUnroll) {
-    uint4 av[kDownUnroll], xv[kDownUnroll];
+    uint4 av[kDownUnroll];
+    uint32_t off[kDownUnroll];
 #pragma unroll
     for (int u = 0; u < kDownUnroll; ++u) {
-      const uint32_t off = 16u * (uint32_t)(c0 + (int)threadIdx.x + u * kDownThreads);
-      av[u] = buf_load16(arr, off);
-      xv[u] = buf_load16(xr, off);
+      off[u] = 16u * (uint32_t)(c0 + (int)threadIdx.x + u * kDownThreads);
+      av[u] = buf_load16(arr, off[u]);
     }
 #pragma unroll
-    for (int u = 0; u < kDownUnroll; ++u) acc += dot8(av[u], xv[u]);
-  }
-  acc = wave_sum(acc);
-  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = acc;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    float t = 0.0f;
+    for (int t = 0; t < kBtTokens; ++t) {
+      if (t < m) {   // uniform
+        uint4 xv[kDownUnroll];
 #pragma unroll
-    for (int i = 0; i < kDownThreads / 64; ++i) t += part[i];
-    J.u[row] = t;
+        for (int u = 0; u < kDownUnroll; ++u) xv[u] = buf_load16(xr, off[u] < kb ? (uint32_t)t * kb + off[u] : xend);
+#pragma unroll
+        for (int u = 0; u < kDownUnroll; ++u) acc[t] += dot8(av[u], xv[u]);
+      }
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < kBtTokens; ++t) {
+    if (t < m) {
+      const float v = wave_sum(acc[t]);
+      if ((threadIdx.x & 63) == 0) part[t][threadIdx.x >> 6] = v;
+    }
+  }
+  __syncthreads();
+  if ((int)threadIdx.x < m) {
+    float v = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kDownThreads / 64; ++i) v += part[threadIdx.x][i];
+    J.u[threadIdx.x * J.r + row] = v;
   }
 }
 
@@ -395,6 +425,297 @@ __global__ __launch_bounds__(kGvThreads) void nf4_gemv_kernel(const GemvJob* __r
   }
 }
 
+// Small-batch decode: jobs of m = 2..16 tokens, Y [m x N] = X deq(W)^T +
+// s (X A^T) B^T.
+//
+// The batch-1 kernel packs (row, position) pairs into the MFMA columns and
+// spends its spare A rows on block masking; with m tokens that layout costs
+// m/2 times the MFMAs and m copies of x in LDS.  Here the product takes the
+// plain layout: B operand = decoded weights (column c = weight row c, k-group
+// g), A operand = x (row = token, zero past m), so lane c + 16g ends with
+// tokens 4g..4g+3 of row c and applies that row's block scales to its fp32
+// partials.
+//
+//   * Loads.  A step is 128 columns (two NF4 blocks) of a 16-row set; lane
+//     (c, g) reads code bytes 16g..16g+15 of row c's 64-byte run, so its
+//     dword j holds columns 32g + 8j .. 32g + 8j + 7 and MFMA j takes dword
+//     j of every lane.
+//   * Blocks kept apart.  The k-groups of one MFMA span both blocks of the
+//     step (g = 0, 1 the first, g = 2, 3 the second), so each MFMA runs twice,
+//     against x restricted to one block: the other half of the lanes reads a
+//     zero run.  D0 collects the first block, D1 the second, each with its
+//     own scale.  The matrix unit has room for the doubled work: at 16 tokens
+//     it needs under half of the time the codes take to stream.
+//   * x in LDS.  The eight waves of a workgroup walk the same columns in
+//     lockstep, one 1024-column chunk of all sixteen token rows (zero past m
+//     and past K) at a time, double buffered: a chunk's steps run between the
+//     global loads of the next chunk and their LDS stores, then one barrier.
+//   * Decode table, persistence, cost-balanced tile ranges and loads running
+//     ahead across tile boundaries as in the batch-1 kernel; a tile is 512
+//     rows (eight waves of four sets).
+//   * LoRA.  s u (bf16, zero past m and r) is staged per job; the
+//     up-projection s U B^T is r/32 MFMAs per set at tile end, with B read
+//     straight from memory.
+template <int CB>
+__global__ __launch_bounds__(kBtThreads) void nf4_gemv_batch_kernel(const GemvJob* __restrict__ jobs,
+                                                                    const int4* __restrict__ segs,
+                                                                    const int* __restrict__ range) {
+  extern __shared__ __align__(16) uint8_t lds_dyn[];  // addressed from 0 (see lds_ld32)
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int c = lane & 15, g = lane >> 4;
+  const uint32_t col = 4u * lane;
+
+  // tables, once: wave w writes code-byte entries e = w + 8 i of column lane
+  {
+    const int wu = __builtin_amdgcn_readfirstlane(w);
+#pragma unroll
+    for (int i = 0; i < 256 / kBtWaves; ++i) {
+      const int e = wu + kBtWaves * i;
+      lds_st32((uint32_t)e * 256u + 4u * lane, level_bf16<CB>(e & 15) | (level_bf16<CB>(e >> 4) << 16));
+    }
+    if (tid < 256) lds_st32(kQ8Off + 4u * tid, __builtin_bit_cast(uint32_t, q8_value((uint32_t)tid)));
+    if (tid < kBtZeroBytes / 16) lds_st128(kBtZeroOff + 16u * tid, make_uint4(0u, 0u, 0u, 0u));
+  }
+
+  // x operand of lane (token c, k-group g) within a chunk buffer; the half of
+  // the lanes outside a block reads the zero run instead
+  const uint32_t xlane = kBtXOff + (uint32_t)c * kBtXRow + 64u * (uint32_t)g;
+  const bool second = g >= 2;
+  int cc = 0;   // x chunks staged so far: buffer cc & 1 holds the current one
+
+  for (int si = range[blockIdx.x]; si < range[blockIdx.x + 1]; ++si) {
+    const int4 sg = segs[si];
+    const GemvJob& J = jobs[sg.x];
+    const int K = J.K, N = J.N, nblk = K >> 6, R = J.r, m = J.m;
+    // 128-column steps per row, rounded up to whole chunks: the steps past
+    // the row meet zero x (staged zero past K), so they add exactly zero
+    const int nch = ((nblk + 1) / 2 + kBtChunkSteps - 1) / kBtChunkSteps, nst = nch * kBtChunkSteps;
+    const uint32_t nb = (uint32_t)N * (uint32_t)nblk;
+    const rsrc_t cr = make_rsrc(J.codes, nb * 32u);
+    const rsrc_t ar = make_rsrc(J.absmax_q, nb);
+    const rsrc_t sr = make_rsrc(J.group_scale, ((nb + 255u) >> 8) * 4u);
+    const uint32_t bend = (uint32_t)N * (uint32_t)R * 2u;
+    const rsrc_t br = make_rsrc(J.B, bend);
+    const uint32_t xend = (uint32_t)m * (uint32_t)K * 2u;
+    const rsrc_t xr = make_rsrc(J.x, xend);
+
+    // x chunk ch: 16-byte piece p = tid + kBtThreads q is columns
+    // 1024 ch + 8 (p & 127) of token p >> 7 (zero past m or K)
+    constexpr int kXq = kBtTokens * 128 / kBtThreads;   // 16-byte x pieces per thread and chunk
+    auto load_x = [&](uint4 (&v)[kXq], int ch) __attribute__((always_inline)) {
+#pragma unroll
+      for (int q = 0; q < kXq; ++q) {
+        const int p = tid + kBtThreads * q, t = p >> 7, k = kBtChunkSteps * 128 * ch + 8 * (p & 127);
+        v[q] = buf_load16(xr, (t < m && k < K) ? ((uint32_t)t * (uint32_t)K + (uint32_t)k) * 2u : xend);
+      }
+    };
+    auto store_x = [&](const uint4 (&v)[kXq], int buf) __attribute__((always_inline)) {
+#pragma unroll
+      for (int q = 0; q < kXq; ++q) {
+        const int p = tid + kBtThreads * q;
+        lds_st128(kBtXOff + (uint32_t)buf * kBtXBuf + (uint32_t)(p >> 7) * kBtXRow + 16u * (uint32_t)(p & 127), v[q]);
+      }
+    };
+    {   // stage the job: x chunk 0 and s u
+      uint4 xv[kXq];
+      load_x(xv, 0);
+      constexpr int kSq = kBtTokens * kBtRank / 2 / kBtThreads;   // s u pairs per thread
+      uint32_t su[kSq];
+#pragma unroll
+      for (int q = 0; q < kSq; ++q) {
+        const int p = tid + kBtThreads * q, t = p >> 6, j = 2 * (p & 63);
+        const bool on = t < m && j < R;   // R is a multiple of 8
+        su[q] = on ? pack_bf16x2(J.s * J.u[t * R + j], J.s * J.u[t * R + j + 1]) : 0u;
+      }
+      __syncthreads();   // every wave is done with the previous job's buffers
+      store_x(xv, cc & 1);
+#pragma unroll
+      for (int q = 0; q < kSq; ++q) {
+        const int p = tid + kBtThreads * q;
+        lds_st32(kBtSuOff + (uint32_t)(p >> 6) * kBtSuRow + 4u * (uint32_t)(p & 63), su[q]);
+      }
+      __syncthreads();
+    }
+
+    // Row of set k in tile t; rows past N read the first byte past the
+    // arrays (zero codes, absmax code 0, so block scale 0).
+    const int t_first = sg.y, t_last = sg.y + sg.z - 1;
+    auto row_of = [&](int t, int k) __attribute__((always_inline)) {
+      return t * kBtRows + 16 * kBtSets * w + 16 * k + c;
+    };
+    auto rbase_of = [&](int t, int k) __attribute__((always_inline)) -> uint32_t {
+      const int row = row_of(t, k);
+      return (uint32_t)(row < N ? row : N) * (uint32_t)nblk;
+    };
+    uint32_t rbc[kBtSets], rbn[kBtSets];
+    float s2c[kBtSets][3], s2n[kBtSets][3];
+    auto load_s2 = [&](float (&dst)[kBtSets][3], const uint32_t (&rb)[kBtSets]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int k = 0; k < kBtSets; ++k)
+#pragma unroll
+        for (int i = 0; i < 3; ++i)
+          dst[k][i] = u2f(__builtin_amdgcn_raw_buffer_load_b32(sr, ((rb[k] >> 8) + i) * 4u, 0, 0));
+    };
+    auto load_step = [&](uint4 (&c_)[kBtSets], const uint32_t (&rb)[kBtSets], int s) __attribute__((always_inline)) {
+#pragma unroll
+      for (int k = 0; k < kBtSets; ++k) c_[k] = buf_load16(cr, rb[k] * 32u + 64u * (uint32_t)s + 16u * (uint32_t)g);
+    };
+    // The absmax codes of a chunk (16 blocks per row): lane (c, g) loads
+    // blocks 4g..4g+3 of row c once per chunk, a chunk ahead, and a step
+    // takes its two from lane c + 16 (s >> 1) (byte loads spread over sixteen
+    // rows each cost as much address work as a code load).
+    auto load_aq = [&](uint32_t (&a_)[kBtSets], int t, int ch) __attribute__((always_inline)) {
+#pragma unroll
+      for (int k = 0; k < kBtSets; ++k) {
+        const uint32_t b = rbase_of(t, k) + 16u * (uint32_t)ch + 4u * (uint32_t)g;
+        a_[k] = __builtin_amdgcn_raw_buffer_load_b8(ar, b, 0, 0) |
+                ((uint32_t)__builtin_amdgcn_raw_buffer_load_b8(ar, b + 1u, 0, 0) << 8) |
+                ((uint32_t)__builtin_amdgcn_raw_buffer_load_b8(ar, b + 2u, 0, 0) << 16) |
+                ((uint32_t)__builtin_amdgcn_raw_buffer_load_b8(ar, b + 3u, 0, 0) << 24);
+      }
+    };
+#pragma unroll
+    for (int k = 0; k < kBtSets; ++k) {
+      rbc[k] = rbase_of(t_first, k);
+      rbn[k] = rbase_of(t_first + 1 <= t_last ? t_first + 1 : t_last, k);
+    }
+    load_s2(s2c, rbc);
+    // code loads run one step ahead, across tile boundaries; past the
+    // segment's last step they stay on it
+    int tl = t_first, sl = 0;
+    auto load_next = [&](uint4 (&c_)[kBtSets]) __attribute__((always_inline)) {
+      uint32_t rb[kBtSets];
+#pragma unroll
+      for (int k = 0; k < kBtSets; ++k) rb[k] = rbase_of(tl, k);
+      load_step(c_, rb, sl);
+      if (tl < t_last || sl + 1 < nst) {
+        if (++sl == nst) {
+          sl = 0;
+          ++tl;
+        }
+      }
+    };
+    uint4 cs[kBtSets];
+    load_next(cs);
+    uint32_t aqc[kBtSets];
+    load_aq(aqc, t_first, 0);
+
+    for (int t = t_first; t <= t_last; ++t) {
+      load_s2(s2n, rbn);
+      uint32_t gb1[kBtSets], gb2[kBtSets];   // first block (within the row) of its second and third group
+#pragma unroll
+      for (int k = 0; k < kBtSets; ++k) {
+        gb1[k] = 256u - (rbc[k] & 255u);
+        gb2[k] = gb1[k] + 256u;
+      }
+      float acc[kBtSets][4];
+#pragma unroll
+      for (int k = 0; k < kBtSets; ++k)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[k][i] = 0.0f;
+
+      // one step: S is the step within the row, s within the chunk; base0 and
+      // base1 address its x
+      auto step = [&](int S, int s, uint32_t base0, uint32_t base1) __attribute__((always_inline)) {
+        uint4 csn[kBtSets];
+        load_next(csn);
+        __builtin_amdgcn_sched_barrier(0);   // keep the loads ahead of this step's work
+        // k-group dword j of both sets against one pair of x operands
+        const uint32_t bi = 2u * (uint32_t)S;
+        f32x4_t D0[kBtSets], D1[kBtSets];
+#pragma unroll
+        for (int k = 0; k < kBtSets; ++k) D0[k] = D1[k] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const bf16x8_t a0 = __builtin_bit_cast(bf16x8_t, lds_ld128(base0 + 16u * (uint32_t)j));
+          const bf16x8_t a1 = __builtin_bit_cast(bf16x8_t, lds_ld128(base1 + 16u * (uint32_t)j));
+#pragma unroll
+          for (int k = 0; k < kBtSets; ++k) {
+            const uint32_t cw = j == 0 ? cs[k].x : j == 1 ? cs[k].y : j == 2 ? cs[k].z : cs[k].w;
+            const bf16x8_t b = decode8(cw, col);
+            D0[k] = mfma16x16x32(a0, b, D0[k]);
+            D1[k] = mfma16x16x32(a1, b, D1[k]);
+          }
+          __builtin_amdgcn_sched_barrier(0);   // one dword's decode in flight at a time
+        }
+#pragma unroll
+        for (int k = 0; k < kBtSets; ++k) {
+          const uint32_t aq = (uint32_t)__shfl((int)aqc[k], c + 16 * (s >> 1)) >> (16 * (s & 1));
+          const float q0 = lds_ldf(kQ8Off + 4u * (aq & 0xFFu));
+          const float q1 = lds_ldf(kQ8Off + 4u * ((aq >> 8) & 0xFFu));
+          // the group scales as register values: a select over the array's
+          // elements would become a select of addresses and keep the array
+          // in memory
+          float v0 = s2c[k][0], v1 = s2c[k][1], v2 = s2c[k][2];
+          asm volatile("" : "+v"(v0), "+v"(v1), "+v"(v2));
+          const float s20 = bi >= gb2[k] ? v2 : bi >= gb1[k] ? v1 : v0;
+          const float s21 = bi + 1u >= gb2[k] ? v2 : bi + 1u >= gb1[k] ? v1 : v0;
+          const float t0 = q0 * s20, t1 = q1 * s21;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[k][i] += t0 * D0[k][i] + t1 * D1[k][i];
+        }
+#pragma unroll
+        for (int k = 0; k < kBtSets; ++k) cs[k] = csn[k];
+      };
+
+      for (int ch = 0; ch < nch; ++ch) {
+        uint4 xv[kXq];
+        load_x(xv, ch + 1 < nch ? ch + 1 : 0);   // the next chunk (of the next tile after the last)
+        uint32_t aqn[kBtSets];
+        load_aq(aqn, ch + 1 < nch ? t : (t + 1 <= t_last ? t + 1 : t_last), ch + 1 < nch ? ch + 1 : 0);
+        // a lane of the other block half reads the zero run at a fixed address
+        const uint32_t xb = xlane + (uint32_t)(cc & 1) * kBtXBuf;
+        uint32_t base0 = second ? (uint32_t)kBtZeroOff : xb, base1 = second ? xb : (uint32_t)kBtZeroOff;
+        const uint32_t inc0 = second ? 0u : 256u, inc1 = second ? 256u : 0u;
+        // a runtime loop over whole chunks (as the batch-1 kernel's): the
+        // waits stay exact and nothing is unrolled into register pressure
+        const int S0 = ch * kBtChunkSteps;
+        for (int s = 0; s < kBtChunkSteps; ++s) {
+          step(S0 + s, s, base0, base1);
+          base0 += inc0;
+          base1 += inc1;
+        }
+        store_x(xv, (cc + 1) & 1);
+#pragma unroll
+        for (int k = 0; k < kBtSets; ++k) aqc[k] = aqn[k];
+        __syncthreads();
+        ++cc;
+      }
+
+      // Tile end: the LoRA term by MFMA (A = s u of token c, B = ranks of
+      // weight row c; ranks past r read zero on both sides), then y.
+#pragma unroll
+      for (int k = 0; k < kBtSets; ++k) {
+        const int row = row_of(t, k);
+        const uint32_t roff = (uint32_t)(row < N ? row : N) * (uint32_t)R * 2u;
+        f32x4_t L = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int kk = 0; kk < kBtRank / 32; ++kk) {
+          if (32 * kk < R) {   // uniform
+            const uint32_t rk = 32u * (uint32_t)kk + 8u * (uint32_t)g;
+            const uint4 bv = buf_load16(br, rk < (uint32_t)R ? roff + 2u * rk : bend);
+            const u32x4_t av = lds_ld128(kBtSuOff + (uint32_t)c * kBtSuRow + 2u * rk);
+            L = mfma16x16x32(__builtin_bit_cast(bf16x8_t, av), __builtin_bit_cast(bf16x8_t, bv), L);
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int tok = 4 * g + i;
+          if (tok < m && row < N)
+            J.y[(int64_t)tok * N + row] = (bf16_t)(pack_bf16x2(acc[k][i] + L[i], 0.0f) & 0xFFFFu);
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < kBtSets; ++k) {
+        rbc[k] = rbn[k];
+        rbn[k] = rbase_of(t + 2 <= t_last ? t + 2 : t_last, k);
+#pragma unroll
+        for (int i = 0; i < 3; ++i) s2c[k][i] = s2n[k][i];
+      }
+    }
+  }
+}
+
 namespace {
 
 // Jobs whose absmax codes can be read two at a time (an even number of
@@ -414,16 +735,21 @@ struct LaunchPlan {
   int groups() const { return range.empty() ? 0 : (int)range.size() - 1; }
 };
 
-LaunchPlan plan_launch(const GemvJob* jobs, int njobs, bool pair, int max_groups) {
+// The three launches of a call: batch-1 jobs whose absmax codes pair up,
+// the other batch-1 jobs, and jobs of two or more tokens.
+int job_kind(const GemvJob& J) { return J.m > 1 ? 2 : pair_job(J) ? 0 : 1; }
+
+LaunchPlan plan_launch(const GemvJob* jobs, int njobs, int kind, int max_groups) {
   LaunchPlan lp;
   struct Tile { int job, t; double cost; };
   std::vector<Tile> tiles;
   double total = 0.0;
+  const int tile_rows = kind == 2 ? kBtRows : kGvRows;
   for (int i = 0; i < njobs; ++i) {
-    if (pair_job(jobs[i]) != pair) continue;
-    const int nt = (jobs[i].N + kGvRows - 1) / kGvRows;
+    if (job_kind(jobs[i]) != kind) continue;
+    const int nt = (jobs[i].N + tile_rows - 1) / tile_rows;
     for (int t = 0; t < nt; ++t) {
-      const int rows = std::min(kGvRows, jobs[i].N - t * kGvRows);
+      const int rows = std::min(tile_rows, jobs[i].N - t * tile_rows);
       const double cost = (double)rows * (double)jobs[i].K;
       tiles.push_back({i, t, cost});
       total += cost;
@@ -480,16 +806,33 @@ hipError_t launch_main(const GemvJob* djobs, const int4* segs, const int* range,
   return hipGetLastError();
 }
 
-// The two launches of the GEMV (jobs whose absmax codes pair up, then the
-// rest), for codebook CB.
 template <int CB>
-hipError_t launch_both(const GemvLaunch& L, const GemvJob* djobs, const uint8_t* dev, hipStream_t st) {
-  const hipError_t e = launch_main<true, CB>(djobs, reinterpret_cast<const int4*>(dev + L.seg_off[0]),
-                                             reinterpret_cast<const int*>(dev + L.rng_off[0]), L.groups[0],
-                                             L.max_steps[0], st);
+hipError_t launch_batch(const GemvJob* djobs, const int4* segs, const int* range, int groups, hipStream_t st) {
+  if (groups <= 0) return hipSuccess;
+  hipFuncAttributes fa{};
+  hipError_t e = hipFuncGetAttributes(&fa, reinterpret_cast<const void*>(&nf4_gemv_batch_kernel<CB>));
   if (e != hipSuccess) return e;
-  return launch_main<false, CB>(djobs, reinterpret_cast<const int4*>(dev + L.seg_off[1]),
-                                reinterpret_cast<const int*>(dev + L.rng_off[1]), L.groups[1], L.max_steps[1], st);
+  if (fa.sharedSizeBytes != 0) return hipErrorInvalidKernelFile;
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&nf4_gemv_batch_kernel<CB>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, kBtLds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((nf4_gemv_batch_kernel<CB>), dim3(groups), dim3(kBtThreads), kBtLds, st, djobs, segs, range);
+  return hipGetLastError();
+}
+
+// The three launches of the GEMV (batch-1 jobs whose absmax codes pair up,
+// the other batch-1 jobs, jobs of several tokens), for codebook CB.
+template <int CB>
+hipError_t launch_all(const GemvLaunch& L, const GemvJob* djobs, const uint8_t* dev, hipStream_t st) {
+  hipError_t e = launch_main<true, CB>(djobs, reinterpret_cast<const int4*>(dev + L.seg_off[0]),
+                                       reinterpret_cast<const int*>(dev + L.rng_off[0]), L.groups[0],
+                                       L.max_steps[0], st);
+  if (e != hipSuccess) return e;
+  e = launch_main<false, CB>(djobs, reinterpret_cast<const int4*>(dev + L.seg_off[1]),
+                             reinterpret_cast<const int*>(dev + L.rng_off[1]), L.groups[1], L.max_steps[1], st);
+  if (e != hipSuccess) return e;
+  return launch_batch<CB>(djobs, reinterpret_cast<const int4*>(dev + L.seg_off[2]),
+                          reinterpret_cast<const int*>(dev + L.rng_off[2]), L.groups[2], st);
 }
 
 }  // namespace
@@ -500,7 +843,7 @@ size_t gemv_table_bound(int njobs, int64_t max_rows) {
   // group boundary) and group offsets | lora_down map
   const size_t segs = (size_t)njobs + kMaxGvGroups;
   const size_t downs = (size_t)njobs * 128;
-  return up256((size_t)njobs * sizeof(GemvJob)) + 2 * (up256(segs * sizeof(int4)) + up256((kMaxGvGroups + 1) * sizeof(int))) +
+  return up256((size_t)njobs * sizeof(GemvJob)) + kGvKinds * (up256(segs * sizeof(int4)) + up256((kMaxGvGroups + 1) * sizeof(int))) +
          up256(downs * sizeof(int2));
 }
 
@@ -512,14 +855,15 @@ size_t gemv_lds_bytes(int64_t K) {
 hipError_t gemv_prepare(const GemvJob* jobs, int njobs, int codebook, void* table, size_t table_bytes,
                         GemvLaunch* out, hipStream_t st) {
   const int groups = device_cus();
-  const LaunchPlan lp[2] = {plan_launch(jobs, njobs, true, groups), plan_launch(jobs, njobs, false, groups)};
+  const LaunchPlan lp[kGvKinds] = {plan_launch(jobs, njobs, 0, groups), plan_launch(jobs, njobs, 1, groups),
+                                   plan_launch(jobs, njobs, 2, groups)};
   std::vector<int2> down;
   for (int i = 0; i < njobs; ++i)
     for (int t = 0; t < jobs[i].r; ++t) down.push_back(make_int2(i, t));
   // layout: jobs | per launch kind: segments, group offsets | u = A x map
   GemvLaunch L{};
   size_t off = up256((size_t)njobs * sizeof(GemvJob));
-  for (int k = 0; k < 2; ++k) {
+  for (int k = 0; k < kGvKinds; ++k) {
     L.seg_off[k] = off;
     off += up256(lp[k].segs.size() * sizeof(int4));
     L.rng_off[k] = off;
@@ -534,7 +878,7 @@ hipError_t gemv_prepare(const GemvJob* jobs, int njobs, int codebook, void* tabl
   if (off > table_bytes) return hipErrorInvalidValue;   // the caller's check makes this unreachable
   std::vector<uint8_t> host(off, 0);
   std::memcpy(host.data(), jobs, (size_t)njobs * sizeof(GemvJob));
-  for (int k = 0; k < 2; ++k) {
+  for (int k = 0; k < kGvKinds; ++k) {
     if (!lp[k].segs.empty()) std::memcpy(host.data() + L.seg_off[k], lp[k].segs.data(), lp[k].segs.size() * sizeof(int4));
     if (!lp[k].range.empty()) std::memcpy(host.data() + L.rng_off[k], lp[k].range.data(), lp[k].range.size() * sizeof(int));
   }
@@ -555,9 +899,9 @@ hipError_t gemv_run(const GemvLaunch& L, hipStream_t st) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (L.codebook == kCbFp4) return launch_both<kCbFp4>(L, djobs, dev, st);
-  if (L.codebook == kCbInt4) return launch_both<kCbInt4>(L, djobs, dev, st);
-  return launch_both<kCbNf4>(L, djobs, dev, st);
+  if (L.codebook == kCbFp4) return launch_all<kCbFp4>(L, djobs, dev, st);
+  if (L.codebook == kCbInt4) return launch_all<kCbInt4>(L, djobs, dev, st);
+  return launch_all<kCbNf4>(L, djobs, dev, st);
 }
 
 }  // namespace qlora

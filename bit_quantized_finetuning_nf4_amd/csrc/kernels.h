@@ -60,11 +60,12 @@ struct GemvJob {
   const bf16_t* A;
   const bf16_t* B;
   bf16_t* y;
-  float* u;  // r fp32 scratch (A x)
+  float* u;  // m x r fp32 scratch (A x per token)
   int32_t N;
   int32_t K;
   int32_t r;
   float s;
+  int32_t m;  // tokens: x is [m x K], y [m x N]
 };
 // gemv_prepare writes the job table (jobs, per-workgroup tile segments and
 // the u = A x map) into `table` (device memory of at least
@@ -74,10 +75,11 @@ struct GemvJob {
 size_t gemv_table_bound(int njobs, int64_t max_rows);
 size_t gemv_lds_bytes(int64_t K);
 // What gemv_run needs besides the table in device memory.
+constexpr int kGvKinds = 3;   // launches per call: batch-1 (two absmax layouts), several tokens
 struct GemvLaunch {
   void* table;
-  uint64_t seg_off[2], rng_off[2], down_off;
-  int32_t groups[2], max_steps[2];
+  uint64_t seg_off[kGvKinds], rng_off[kGvKinds], down_off;
+  int32_t groups[kGvKinds], max_steps[kGvKinds];
   int32_t n_down;
   int32_t codebook;  // shared by every job of the call
 };

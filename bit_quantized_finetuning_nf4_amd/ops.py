@@ -189,6 +189,8 @@ def linear_bwd(q: QuantizedWeight, X: torch.Tensor, dY: torch.Tensor, A=None, B=
 
 @dataclass
 class GemvJob:
+    """One decode product: x is [cols] (one token) or [m x cols] (m <= 16
+    tokens); y, when given, has the matching shape [rows] or [m x rows]."""
     q: QuantizedWeight
     x: torch.Tensor
     A: Optional[torch.Tensor] = None
@@ -209,19 +211,11 @@ class GemvPlan:
         self.outputs = []
         self._keep = list(jobs)
         for i, j in enumerate(jobs):
-            _need(j.x, torch.bfloat16, "x", (j.q.cols,))
-            r = 0 if j.A is None else j.A.shape[0]
-            if r:
-                _need(j.A, torch.bfloat16, "A", (r, j.q.cols))
-                _need(j.B, torch.bfloat16, "B", (j.q.rows, r))
-            y = j.y if j.y is not None else torch.empty(j.q.rows, dtype=torch.bfloat16, device=j.x.device)
-            self.outputs.append(y)
             self._descs[i] = j.q.desc()
-            self._arr[i] = GemvJobDesc(ctypes.pointer(self._descs[i]), j.x.data_ptr(),
-                                       None if r == 0 else j.A.data_ptr(), None if r == 0 else j.B.data_ptr(),
-                                       r, float(j.alpha), y.data_ptr())
+            self._arr[i], y = _gemv_desc(j, self._descs[i])
+            self.outputs.append(y)
         self.n = n
-        nbytes = workspace_bytes(_lib.QLORA_OP_GEMV, N=max(j.q.rows for j in jobs),
+        nbytes = workspace_bytes(_lib.QLORA_OP_GEMV, M=max(_tokens(j) for j in jobs), N=max(j.q.rows for j in jobs),
                                  K=max(j.q.cols for j in jobs), njobs=n)
         self.ws = ws if ws is not None else workspace(nbytes, jobs[0].x.device)
         self._plan = GemvPlanDesc()
@@ -233,22 +227,39 @@ class GemvPlan:
         return self.outputs
 
 
+def _tokens(j):
+    return 1 if j.x.dim() == 1 else int(j.x.shape[0])
+
+
+def _gemv_desc(j, desc):
+    """(job descriptor, y) for one GemvJob; desc must outlive the call."""
+    m = _tokens(j)
+    one = j.x.dim() == 1
+    _need(j.x, torch.bfloat16, "x", (j.q.cols,) if one else (m, j.q.cols))
+    r = 0 if j.A is None else j.A.shape[0]
+    if r:
+        _need(j.A, torch.bfloat16, "A", (r, j.q.cols))
+        _need(j.B, torch.bfloat16, "B", (j.q.rows, r))
+    shape = (j.q.rows,) if one else (m, j.q.rows)
+    y = j.y if j.y is not None else torch.empty(shape, dtype=torch.bfloat16, device=j.x.device)
+    _need(y, torch.bfloat16, "y", shape)
+    return GemvJobDesc(ctypes.pointer(desc), j.x.data_ptr(), None if r == 0 else j.A.data_ptr(),
+                       None if r == 0 else j.B.data_ptr(), r, float(j.alpha), y.data_ptr(), m), y
+
+
 def gemv(jobs: Sequence[GemvJob], ws=None):
-    """Batch-1 decode for independent linears; returns the list of y tensors."""
+    """Decode (one token or a batch of up to 16 per job) for independent
+    linears; returns the list of y tensors."""
     n = len(jobs)
     descs = (Nf4WeightDesc * n)()
     arr = (GemvJobDesc * n)()
     outs = []
     for i, j in enumerate(jobs):
-        _need(j.x, torch.bfloat16, "x", (j.q.cols,))
-        r = 0 if j.A is None else j.A.shape[0]
-        y = j.y if j.y is not None else torch.empty(j.q.rows, dtype=torch.bfloat16, device=j.x.device)
-        outs.append(y)
         descs[i] = j.q.desc()
-        arr[i] = GemvJobDesc(ctypes.pointer(descs[i]), j.x.data_ptr(), None if r == 0 else j.A.data_ptr(),
-                             None if r == 0 else j.B.data_ptr(), r, float(j.alpha), y.data_ptr())
-    nbytes = workspace_bytes(_lib.QLORA_OP_GEMV, N=max(j.q.rows for j in jobs), K=max(j.q.cols for j in jobs),
-                             njobs=n)
+        arr[i], y = _gemv_desc(j, descs[i])
+        outs.append(y)
+    nbytes = workspace_bytes(_lib.QLORA_OP_GEMV, M=max(_tokens(j) for j in jobs), N=max(j.q.rows for j in jobs),
+                             K=max(j.q.cols for j in jobs), njobs=n)
     if ws is None:
         ws = workspace(nbytes, jobs[0].x.device)
     check(lib().qlora_gemv(arr, n, _ptr(ws), 0 if ws is None else ws.numel(), _stream()), "qlora_gemv")

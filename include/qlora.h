@@ -110,12 +110,13 @@ typedef struct {
 /* One batch-1 decode product y = deq(W) x + (alpha/r) B (A x). */
 typedef struct {
   const qlora_nf4_weight* W;  /* host pointer to the descriptor            */
-  const uint16_t* x;          /* [cols] bf16                               */
+  const uint16_t* x;          /* [m x cols] bf16 ([cols] for one token)    */
   const uint16_t* A;          /* [r x cols] bf16, NULL when r == 0         */
   const uint16_t* B;          /* [rows x r] bf16, NULL when r == 0         */
   int32_t r;
   float alpha;
-  uint16_t* y;                /* [rows] bf16, overwritten                  */
+  uint16_t* y;                /* [m x rows] bf16, overwritten              */
+  int32_t m;                  /* tokens: 0 or 1 for one, at most 16        */
 } qlora_gemv_job;
 
 /* Name of a status code (static string). */
@@ -238,15 +239,20 @@ qlora_status qlora_nf4_fwd(const qlora_nf4_weight* W, const uint16_t* X, int64_t
 qlora_status qlora_nf4_dx(const qlora_nf4_weight* W, const uint16_t* dY, int64_t M, const uint16_t* G,
                           const uint16_t* A, int32_t r, float alpha, uint16_t* dX, void* stream);
 
-/* Batch-1 decode for njobs independent products (host job array, read
- * before return): y = deq(W) x + s B (A x), s = RN32(alpha / r), y bf16
- * (overwritten).  Each job needs cols % 64 == 0 and cols <= 32768 (x is
- * staged whole in on-chip memory), and rows * r * 2 < 2^32.  njobs <= 4096.
- * ws is sized by qlora_workspace_bytes(QLORA_OP_GEMV, 0, max rows, max
- * cols, 0, njobs); it holds u = A x and the job table, which the call writes
- * with an asynchronous host-to-device copy on `stream`.  Equivalent to
- * qlora_gemv_prepare followed by qlora_gemv_run.
- * whatthefuture.ai article: 4-bit inference speed. */
+/* Decode for njobs independent products (host job array, read before
+ * return): for each of the job's m tokens (rows of x and y),
+ * y = deq(W) x + s B (A x), s = RN32(alpha / r), y bf16 (overwritten); the
+ * forward product at a batch of m <= 16 tokens.  Each job needs
+ * cols % 64 == 0 and cols <= 32768, and rows * r * 2 < 2^32.
+ * njobs <= 4096.  A job's m may be 0 or 1 (one token, x [cols], y [rows])
+ * up to 16 (x [m x cols], y [m x rows]); m < 0 is QLORA_E_SHAPE, m > 16
+ * QLORA_E_UNSUPPORTED.  ws is sized by qlora_workspace_bytes(QLORA_OP_GEMV,
+ * largest m (0 or 1 for one token), max rows, max cols, 0, njobs); it holds
+ * u = A x and the job table, which the call writes with an asynchronous
+ * host-to-device copy on `stream`.  Equivalent to qlora_gemv_prepare
+ * followed by qlora_gemv_run.
+ * whatthefuture.ai article: 4-bit inference is slow (the 8-16x speed-up
+ * its authors expected). */
 qlora_status qlora_gemv(const qlora_gemv_job* jobs, int32_t njobs, void* ws, size_t ws_bytes,
                         void* stream);
 

@@ -174,6 +174,29 @@ def test_gemv_rejects_mixed_codebooks_on_the_host(L):
     assert L.qlora_gemv(jobs, 2, ctypes.c_void_p(4096), 1 << 20, None) == 4
 
 
+
+def test_gemv_token_counts_on_the_host(L):
+    # m < 0 is a shape error, m > 16 unsupported; the workspace grows with the
+    # largest m, and a workspace sized for one token is too small for sixteen
+    d = _desc(codes=4096, aq=8192, s2=12288)
+    fake = ctypes.c_void_p(4096)
+    job = _lib.GemvJobDesc(ctypes.pointer(d), 4096, None, None, 0, 0.0, 4096, 1)
+    jobs = (_lib.GemvJobDesc * 1)(job)
+    op = _lib.QLORA_OP_GEMV
+    one = L.qlora_workspace_bytes(op, 1, 64, 64, 0, 1)
+    assert L.qlora_workspace_bytes(op, 0, 64, 64, 0, 1) == one
+    assert L.qlora_workspace_bytes(op, 16, 64, 64, 0, 1) > one
+    assert L.qlora_workspace_bytes(op, 17, 64, 64, 0, 1) == 0
+    assert L.qlora_workspace_bytes(op, -1, 64, 64, 0, 1) == 0
+    jobs[0].m = -1
+    assert L.qlora_gemv(jobs, 1, fake, 1 << 20, None) == 3
+    jobs[0].m = 17
+    assert L.qlora_gemv(jobs, 1, fake, 1 << 20, None) == 4
+    jobs[0].m = 16
+    assert L.qlora_gemv(jobs, 1, fake, one, None) == 5
+    plan = _lib.GemvPlanDesc()
+    assert L.qlora_gemv_prepare(jobs, 1, fake, one, ctypes.byref(plan), None) == 5
+
 def test_adamw_rejects_bad_arguments_on_the_host(L):
     f = ctypes.c_void_p(4096)
     a = lambda **k: L.qlora_adamw(k.get("p", f), k.get("pb", None), k.get("g", f), k.get("m", f), k.get("v", f),
