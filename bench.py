@@ -49,8 +49,75 @@ def linear_flops(M, N, K, r):
     return 4 * M * N * K + 6 * M * r * (N + K)
 
 
-def gemv_bytes(N, K, r):
-    return N * K // 2 + N * K // 64 + 4 * (-(-N * K // 16384)) + 2 * r * (N + K) + 2 * (N + K)
+def gemv_bytes(N, K, r, m=1):
+    # codes, absmax codes, group scales, A and B, and m rows of x and y
+    return N * K // 2 + N * K // 64 + 4 * (-(-N * K // 16384)) + 2 * r * (N + K) + 2 * m * (N + K)
+
+
+def decode_batch_study(jobs, layers, r, alpha, passes, dev):
+    """Decode of m = 2..16 tokens over the same quantized layers as the
+    batch-1 pass (one grouped call of 7 jobs per layer), and dense bf16
+    decode (F.linear on bf16 weights) timed on 8 layers and scaled to the
+    layer count, for the 4-bit versus 16-bit decode comparison."""
+    import torch
+    from bit_quantized_finetuning_nf4_amd import ops, synth
+    E = lambda: torch.cuda.Event(enable_timing=True)
+
+    def timed(fn):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        evs = [(E(), E()) for _ in range(passes)]
+        for a, b in evs:
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        return sum(a.elapsed_time(b) for a, b in evs) / len(evs)
+
+    shapes = [(j.q.rows, j.q.cols) for j in jobs]
+    out = {"workload": f"{layers} layers x 7 LLaMA-65B-shaped linears, m tokens per linear, LoRA r={r} fused; "
+                       f"{len(jobs)} jobs in one grouped call", "tokens": {}}
+    one_ms = None
+    for m in (1, 2, 4, 8, 16):
+        xs = {}
+        mj = []
+        for li, j in enumerate(jobs):
+            key = (li // 7, j.q.cols)
+            if key not in xs:
+                shape = (j.q.cols,) if m == 1 else (m, j.q.cols)
+                xs[key] = synth.normal_bf16(shape, 1.0, 20_000_000 + 1000 * m + 2 * key[0] + (j.q.cols > 8192), dev)
+            mj.append(ops.GemvJob(j.q, xs[key], j.A, j.B, alpha))
+        plan = ops.GemvPlan(mj)
+        ms = timed(plan)
+        nbytes = sum(gemv_bytes(N, K, r, m) for N, K in shapes)
+        one_ms = ms if m == 1 else one_ms
+        out["tokens"][str(m)] = {"ms_per_pass": ms, "gbps": nbytes / (ms * 1e-3) / 1e9,
+                                 "frac_of_hbm_peak": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+                                 "tokens_per_s": m / (ms * 1e-3), "vs_batch1_tokens_per_s": m * one_ms / ms}
+        log(f"[bench] decode m={m}: {ms:.3f} ms per pass, {out['tokens'][str(m)]['gbps']:.0f} GB/s")
+        del plan, mj, xs
+    # dense bf16 weights: 8 layers (about 13 GB), scaled to `layers`
+    dl = min(8, layers)
+    Ws = [synth.normal_bf16((N, K), 0.02, 30_000_000 + i, dev) for i, (N, K) in enumerate(shapes[:7 * dl])]
+    dense = {"layers_timed": dl, "how": "torch.nn.functional.linear on bf16 weights, one call per linear"}
+    for m in (1, 16):
+        xa = synth.normal_bf16((m, 8192), 1.0, 31_000_000 + m, dev)
+        xd = synth.normal_bf16((m, 22016), 1.0, 32_000_000 + m, dev)
+
+        def run():
+            for W in Ws:
+                torch.nn.functional.linear(xd if W.shape[1] == 22016 else xa, W)
+
+        ms = timed(run) * layers / dl
+        nf4 = out["tokens"][str(m)]["ms_per_pass"]
+        dense[f"m{m}"] = {"ms_per_pass": ms, "gbps": sum(2 * N * K for N, K in shapes) / (ms * 1e-3) / 1e9,
+                          "tokens_per_s": m / (ms * 1e-3), "nf4_speedup": ms / nf4}
+        log(f"[bench] dense bf16 decode m={m}: {ms:.3f} ms per {layers}-layer pass (NF4 {ms / nf4:.2f}x faster)")
+    out["bf16_dense"] = dense
+    del Ws
+    torch.cuda.empty_cache()
+    return out
 
 
 # the device code of each kernel whose traffic is reported: its source file
@@ -277,7 +344,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-codebook-study", action="store_true",
                     help="skip the side studies after the timed steps: the layer set quantized with FP4 and "
-                         "Int4, and the AdamW step over its LoRA values")
+                         "Int4, the AdamW step over its LoRA values, and decode of 2-16 tokens (and of dense bf16 "
+                         "weights) over the decode layers")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after the timed steps, run one elementwise copy (negation) of this many MiB: "
                          "a kernel of known traffic for scaling the FETCH_SIZE / WRITE_SIZE counters")
@@ -480,7 +548,10 @@ def main():
                          "bytes_per_pass": nbytes, "ms_per_pass": pass_ms, "gbps": gbps,
                          "frac_of_hbm_peak": gbps / PEAK_HBM_GBPS}
         log(f"[bench] decode pass {pass_ms:.3f} ms, {gbps:.0f} GB/s")
-        del jobs, dplan
+        del dplan
+        if not args.no_codebook_study:
+            out["decode_batch"] = decode_batch_study(jobs, args.decode_layers, r, alpha, args.decode_passes, dev)
+        del jobs
         torch.cuda.empty_cache()
 
     if not args.no_cpu_baseline:
