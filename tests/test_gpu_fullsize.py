@@ -4,8 +4,8 @@ times (same seeds, sizes and calls).
 The oracle quantizes each whole weight (about 30 s for 1.8e8 weights) and
 computes, in fp64: the quantized storage of every group (bit-exact), Y and dX
 on sampled token rows (every column; rows are independent), and dA, dB in
-full.  The decode GEMV of one 65B-shaped layer set is checked on sampled
-output rows.
+full.  The decode GEMV of one 65B-shaped layer set, at one token and at 16
+tokens, is checked on sampled output rows.
 """
 
 import numpy as np
@@ -88,3 +88,28 @@ def test_decode_gemv_65b_layer_set():
         Wd = np.stack([deq[n] for n in rows])
         yr = oracle.gemv(Wd, torch_to_f64(x), torch_to_f64(A), torch_to_f64(B)[rows], alpha)
         assert_close(torch_to_f64(y)[rows], yr, f"decode {name} {N}x{K} (64 rows)")
+
+
+def test_decode_batch_65b_layer_set():
+    # 16 tokens per linear (the largest batch the decode study times), with
+    # its x recipe; the forward oracle on sampled output rows of every token
+    cfg = synth.LAYER_SETS["llama65b"]
+    r, alpha, m = cfg["r"], cfg["alpha"], 16
+    xs = {K: synth.normal_bf16((m, K), 1.0, 20_000_000 + 1000 * m + (K > 8192), "cuda") for K in (8192, 22016)}
+    jobs, data = [], []
+    for i, (name, N, K) in enumerate(cfg["linears"]):
+        seed = synth.layer_set_seed(4, i, layer=1)
+        W = synth.normal_bf16((N, K), 0.02, seed * 16, "cuda", outliers=cfg["outliers"])
+        A = synth.normal_bf16((r, K), 0.01, seed * 16 + 1, "cuda")
+        B = synth.normal_bf16((N, r), 0.01, seed * 16 + 2, "cuda")
+        jobs.append(ops.GemvJob(ops.quantize(W), xs[K], A, B, alpha))
+        data.append((name, N, K, torch_to_bits(W).ravel(), xs[K], A, B))
+    print("[fullsize] decode batch: 7 jobs of 16 tokens", flush=True)
+    ys = ops.gemv(jobs)
+    torch.cuda.synchronize()
+    for (name, N, K, w_bits, x, A, B), y in zip(data, ys):
+        rows = _rows(N, 48, N + K + 11)
+        deq = oracle_quantize_rows(w_bits, K, rows)
+        Wd = np.stack([deq[n] for n in rows])
+        Yr = oracle.linear_fwd(Wd, torch_to_f64(x), torch_to_f64(A), torch_to_f64(B)[rows], alpha)
+        assert_close(torch_to_f64(y)[:, rows], Yr, f"decode batch {name} {N}x{K} (16 tokens, 48 rows)")
