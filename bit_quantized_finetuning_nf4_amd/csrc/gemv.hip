@@ -456,7 +456,7 @@ __global__ __launch_bounds__(kGvThreads) void nf4_gemv_kernel(const GemvJob* __r
 //   * LoRA.  s u (bf16, zero past m and r) is staged per job; the
 //     up-projection s U B^T is r/32 MFMAs per set at tile end, with B read
 //     straight from memory.
-template <int CB>
+template <bool kQuad, int CB>
 __global__ __launch_bounds__(kBtThreads) void nf4_gemv_batch_kernel(const GemvJob* __restrict__ jobs,
                                                                     const int4* __restrict__ segs,
                                                                     const int* __restrict__ range) {
@@ -568,6 +568,10 @@ __global__ __launch_bounds__(kBtThreads) void nf4_gemv_batch_kernel(const GemvJo
 #pragma unroll
       for (int k = 0; k < kBtSets; ++k) {
         const uint32_t b = rbase_of(t, k) + 16u * (uint32_t)ch + 4u * (uint32_t)g;
+        if constexpr (kQuad) {   // 4-byte aligned: one load
+          a_[k] = __builtin_amdgcn_raw_buffer_load_b32(ar, b, 0, 0);
+          continue;
+        }
         a_[k] = __builtin_amdgcn_raw_buffer_load_b8(ar, b, 0, 0) |
                 ((uint32_t)__builtin_amdgcn_raw_buffer_load_b8(ar, b + 1u, 0, 0) << 8) |
                 ((uint32_t)__builtin_amdgcn_raw_buffer_load_b8(ar, b + 2u, 0, 0) << 16) |
@@ -735,16 +739,23 @@ struct LaunchPlan {
   int groups() const { return range.empty() ? 0 : (int)range.size() - 1; }
 };
 
-// The three launches of a call: batch-1 jobs whose absmax codes pair up,
-// the other batch-1 jobs, and jobs of two or more tokens.
-int job_kind(const GemvJob& J) { return J.m > 1 ? 2 : pair_job(J) ? 0 : 1; }
+// Jobs of several tokens whose absmax rows can be read four bytes at a
+// time (a multiple of 4 blocks per row and a 4-byte aligned array).
+bool quad_job(const GemvJob& J) {
+  return (J.K % 256) == 0 && (reinterpret_cast<uintptr_t>(J.absmax_q) & 3u) == 0;
+}
+
+// The four launches of a call: batch-1 jobs whose absmax codes pair up,
+// the other batch-1 jobs, jobs of two or more tokens with 4-byte aligned
+// absmax rows, and the other jobs of several tokens.
+int job_kind(const GemvJob& J) { return J.m > 1 ? (quad_job(J) ? 2 : 3) : pair_job(J) ? 0 : 1; }
 
 LaunchPlan plan_launch(const GemvJob* jobs, int njobs, int kind, int max_groups) {
   LaunchPlan lp;
   struct Tile { int job, t; double cost; };
   std::vector<Tile> tiles;
   double total = 0.0;
-  const int tile_rows = kind == 2 ? kBtRows : kGvRows;
+  const int tile_rows = kind >= 2 ? kBtRows : kGvRows;
   for (int i = 0; i < njobs; ++i) {
     if (job_kind(jobs[i]) != kind) continue;
     const int nt = (jobs[i].N + tile_rows - 1) / tile_rows;
@@ -806,22 +817,22 @@ hipError_t launch_main(const GemvJob* djobs, const int4* segs, const int* range,
   return hipGetLastError();
 }
 
-template <int CB>
+template <bool kQuad, int CB>
 hipError_t launch_batch(const GemvJob* djobs, const int4* segs, const int* range, int groups, hipStream_t st) {
   if (groups <= 0) return hipSuccess;
   hipFuncAttributes fa{};
-  hipError_t e = hipFuncGetAttributes(&fa, reinterpret_cast<const void*>(&nf4_gemv_batch_kernel<CB>));
+  hipError_t e = hipFuncGetAttributes(&fa, reinterpret_cast<const void*>(&nf4_gemv_batch_kernel<kQuad, CB>));
   if (e != hipSuccess) return e;
   if (fa.sharedSizeBytes != 0) return hipErrorInvalidKernelFile;
-  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&nf4_gemv_batch_kernel<CB>),
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&nf4_gemv_batch_kernel<kQuad, CB>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, kBtLds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((nf4_gemv_batch_kernel<CB>), dim3(groups), dim3(kBtThreads), kBtLds, st, djobs, segs, range);
+  hipLaunchKernelGGL((nf4_gemv_batch_kernel<kQuad, CB>), dim3(groups), dim3(kBtThreads), kBtLds, st, djobs, segs,
+                     range);
   return hipGetLastError();
 }
 
-// The three launches of the GEMV (batch-1 jobs whose absmax codes pair up,
-// the other batch-1 jobs, jobs of several tokens), for codebook CB.
+// The four launches of the GEMV (see job_kind), for codebook CB.
 template <int CB>
 hipError_t launch_all(const GemvLaunch& L, const GemvJob* djobs, const uint8_t* dev, hipStream_t st) {
   hipError_t e = launch_main<true, CB>(djobs, reinterpret_cast<const int4*>(dev + L.seg_off[0]),
@@ -831,8 +842,11 @@ hipError_t launch_all(const GemvLaunch& L, const GemvJob* djobs, const uint8_t* 
   e = launch_main<false, CB>(djobs, reinterpret_cast<const int4*>(dev + L.seg_off[1]),
                              reinterpret_cast<const int*>(dev + L.rng_off[1]), L.groups[1], L.max_steps[1], st);
   if (e != hipSuccess) return e;
-  return launch_batch<CB>(djobs, reinterpret_cast<const int4*>(dev + L.seg_off[2]),
-                          reinterpret_cast<const int*>(dev + L.rng_off[2]), L.groups[2], st);
+  e = launch_batch<true, CB>(djobs, reinterpret_cast<const int4*>(dev + L.seg_off[2]),
+                             reinterpret_cast<const int*>(dev + L.rng_off[2]), L.groups[2], st);
+  if (e != hipSuccess) return e;
+  return launch_batch<false, CB>(djobs, reinterpret_cast<const int4*>(dev + L.seg_off[3]),
+                                 reinterpret_cast<const int*>(dev + L.rng_off[3]), L.groups[3], st);
 }
 
 }  // namespace
@@ -855,8 +869,8 @@ size_t gemv_lds_bytes(int64_t K) {
 hipError_t gemv_prepare(const GemvJob* jobs, int njobs, int codebook, void* table, size_t table_bytes,
                         GemvLaunch* out, hipStream_t st) {
   const int groups = device_cus();
-  const LaunchPlan lp[kGvKinds] = {plan_launch(jobs, njobs, 0, groups), plan_launch(jobs, njobs, 1, groups),
-                                   plan_launch(jobs, njobs, 2, groups)};
+  LaunchPlan lp[kGvKinds];
+  for (int k = 0; k < kGvKinds; ++k) lp[k] = plan_launch(jobs, njobs, k, groups);
   std::vector<int2> down;
   for (int i = 0; i < njobs; ++i)
     for (int t = 0; t < jobs[i].r; ++t) down.push_back(make_int2(i, t));

@@ -75,7 +75,7 @@ struct GemvJob {
 size_t gemv_table_bound(int njobs, int64_t max_rows);
 size_t gemv_lds_bytes(int64_t K);
 // What gemv_run needs besides the table in device memory.
-constexpr int kGvKinds = 3;   // launches per call: batch-1 (two absmax layouts), several tokens
+constexpr int kGvKinds = 4;   // launches per call: batch-1 and several tokens, two absmax layouts each
 struct GemvLaunch {
   void* table;
   uint64_t seg_off[kGvKinds], rng_off[kGvKinds], down_off;
