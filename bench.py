@@ -152,7 +152,7 @@ def traffic_for(kernel):
 
 # rocprofv3 kernel name -> bench kernel; a launch of the fused GEMMs may add a
 # half-tile tail dispatch, whose bytes count towards that launch
-TRAFFIC_KERNELS = {"nf4_fwd_r_kernel": "fwd_kernel", "nf4_fwd_kernel": "fwd_kernel", "nf4_dx_kernel": "dx_kernel",
+TRAFFIC_KERNELS = {"nf4_fwd_r_kernel": "fwd_kernel", "nf4_dx_kernel": "dx_kernel",
                    "quantize_kernel": "quantize_kernel", "nf4_gemv_kernel": "gemv_kernel"}
 TAIL_KERNELS = {"nf4_fwd_n32_kernel": "fwd_kernel", "nf4_dx_half_kernel": "dx_kernel"}
 

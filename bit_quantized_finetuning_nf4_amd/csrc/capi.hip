@@ -29,7 +29,7 @@ constexpr int kMaxRank = 128;
 constexpr int kMaxJobs = 4096;
 constexpr int64_t kMaxGemvCols = 32768;
 constexpr int32_t kMaxGemvTokens = 16;
-constexpr uint64_t kPlanMagic = 0x51474D56504C414EULL;   // marks a plan filled by qlora_gemv_prepare  // x is staged whole in LDS beside the 64 KiB table
+constexpr uint64_t kPlanMagic = 0x51474D56504C414EULL;   // marks a plan filled by qlora_gemv_prepare
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -75,6 +75,12 @@ qlora_status check_tokens(int64_t M, const qlora_nf4_weight* q) {
   if (M > (int64_t)0x7FFFFFFF / q->cols || M > (int64_t)0x7FFFFFFF / q->rows) return QLORA_E_UNSUPPORTED;
   return QLORA_OK;
 }
+
+// The LoRA side products address a 128-row tile of the large operand
+// (128 C bf16) and the rank-side operand (r C bf16, r <= 128) with 32-bit
+// byte ranges: C (K or N) below 2^24.
+constexpr int64_t kMaxSkinnyCols = (int64_t)1 << 24;
+bool skinny_cols_ok(int64_t C) { return C < kMaxSkinnyCols; }
 
 qlora_status check_rank(int32_t r, const void* A, const void* B) {
   if (r < 0 || r > kMaxRank || r % 8 != 0) return QLORA_E_UNSUPPORTED;
@@ -271,6 +277,7 @@ qlora_status qlora_linear_fwd(const qlora_nf4_weight* W, const uint16_t* X, int6
   if (!X || !Y) return QLORA_E_NULL;
   if (!aligned16(X) || !aligned16(Y) || (U_save && !aligned16(U_save))) return QLORA_E_ALIGN;
   if ((st = check_rank(r, A, B)) != QLORA_OK) return st;
+  if (r > 0 && !skinny_cols_ok(W->cols)) return QLORA_E_UNSUPPORTED;
   const FwdLayout L = fwd_layout(M, W->rows, W->cols, r);
   if (ws_bytes < L.total) return QLORA_E_WORKSPACE;
   if (L.total > 0 && !ws) return QLORA_E_NULL;
@@ -303,6 +310,7 @@ qlora_status qlora_linear_bwd(const qlora_nf4_weight* W, const uint16_t* X, cons
   if (r > 0) {
     if (!dA || !dB || !X) return QLORA_E_NULL;
     if (!aligned16(dA) || !aligned16(dB) || !aligned16(X)) return QLORA_E_ALIGN;
+    if (!skinny_cols_ok(W->cols) || !skinny_cols_ok(W->rows)) return QLORA_E_UNSUPPORTED;
   } else {
     if (dA || dB) return QLORA_E_SHAPE;  // no adapter, no adapter gradients
   }
@@ -343,6 +351,7 @@ qlora_status qlora_lora_down(const uint16_t* X, const uint16_t* A, int64_t M, in
   qlora_status st = check_adapter_rank(r);
   if (st != QLORA_OK) return st;
   if (M <= 0 || M > 0x7FFFFFFF || K <= 0 || K % 8 != 0) return QLORA_E_SHAPE;
+  if (!skinny_cols_ok(K)) return QLORA_E_UNSUPPORTED;
   if (!X || !A || !U) return QLORA_E_NULL;
   if (!aligned16(X) || !aligned16(A) || !aligned16(U)) return QLORA_E_ALIGN;
   if ((st = check_ws(ws, ws_bytes, align_up(skinny_partial_bytes(M, r, K, kXAt)))) != QLORA_OK) return st;
@@ -354,6 +363,7 @@ qlora_status qlora_lora_dy_b(const uint16_t* dY, const uint16_t* B, int64_t M, i
   qlora_status st = check_adapter_rank(r);
   if (st != QLORA_OK) return st;
   if (M <= 0 || M > 0x7FFFFFFF || N <= 0 || N % 8 != 0) return QLORA_E_SHAPE;
+  if (!skinny_cols_ok(N)) return QLORA_E_UNSUPPORTED;
   if (!dY || !B || !G) return QLORA_E_NULL;
   if (!aligned16(dY) || !aligned16(B) || !aligned16(G)) return QLORA_E_ALIGN;
   if ((st = check_ws(ws, ws_bytes, align_up(skinny_partial_bytes(M, r, N, kDyB)))) != QLORA_OK) return st;

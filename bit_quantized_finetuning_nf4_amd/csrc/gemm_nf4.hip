@@ -67,20 +67,6 @@ __device__ __forceinline__ void mfma_block(f32x16_t (&acc)[FI][FJ], const bf16x8
     for (int j = 0; j < FJ; ++j) acc[i][j] = mfma32x32x16(a[i], b[j], acc[i][j]);
 }
 
-// One MFMA half-stage: 16 MFMAs, the fragment reads of the next half early
-// (READS DS reads per slot), six VALU producer instructions after each MFMA
-// and the producer's LDS writes late.
-template <int READS>
-__device__ __forceinline__ void schedule_half() {
-#pragma unroll
-  for (int x = 0; x < 16; ++x) {
-    QLORA_SCHED(kSchedMfma, 1);
-    if (x < 8) QLORA_SCHED(kSchedDsRead, READS);
-    QLORA_SCHED(kSchedValu, 6);
-    if (x == 11 || x == 15) QLORA_SCHED(kSchedDsWrite, 1);
-  }
-}
-
 // Tile order: consecutive workgroups share the token tile (the column-side
 // tiles vary fastest); the eight XCDs receive contiguous ranges.
 __device__ __forceinline__ void map_tile(int tiles_c, int tiles_r, int& tc, int& tr) {
@@ -138,230 +124,21 @@ __device__ __forceinline__ void tail_tokens(char* dst, const bf16_t* T, int64_t 
   }
 }
 
-// ===========================================================================
-// Forward: Y = X deq(W)^T + s U B^T.  Weight half = W rows n0.. (dequantized
-// by thread t = row t), token half = X rows m0.. (DMA).  The NF4 codes of
-// four stages (64 bytes per row) are also brought in by DMA, into a double
-// buffer after the ring: one coalesced 64-byte piece per row instead of a
-// 16-byte scattered load per row and stage.
-// ===========================================================================
-constexpr int kCodes = kTile * 64;               // codes of 4 stages
-constexpr int kCodeBase = kStages * kStage;      // 128 KiB
-constexpr size_t kLdsFwd = (size_t)kCodeBase + 2 * kCodes;   // 160 KiB
-
 // DMA pattern for a 256-row x 64-byte tile: wave w, instruction q covers
 // rows 64 q + 16 w .. +15 (1 KiB, lane-linear); lane j -> row + (j >> 2),
 // position j & 3, which holds chunk (j & 3) ^ ((j >> 4) & 3).
 __device__ __forceinline__ int dma_row(int q, int w, int j) { return 64 * q + 16 * w + (j >> 2); }
 __device__ __forceinline__ int dma_chunk(int j) { return (j & 3) ^ ((j >> 4) & 3); }
 
-struct Fwd {
-  rsrc_t xr, cr;          // X, NF4 codes
-  uint32_t xo[4], co[4];  // per-lane byte offsets of the four DMA instructions
-  const uint8_t* aq;      // absmax codes of the owned row
-  const float* gs;        // group scales
-  uint32_t ablk0;         // block index of (owned row, block 0)
-  int nsub, nblk, w;
-};
-
+// Second-level constants of a block: its 8-bit absmax code and group scale.
 struct Scale {
   uint32_t q;
   float s2;
 };
 
-__device__ __forceinline__ void fwd_dma_x(char* smem, const Fwd& f, int stage, int buf) {
-  const uint32_t soff = (uint32_t)min(stage, f.nsub - 1) * 64u;
-  char* dst = smem + buf * kStage + kOp;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) dma16(f.xr, dst + (64 * q + 16 * f.w) * 64, f.xo[q], soff);
-}
-template <int BUF>   // BUF == chunk & 1
-__device__ __forceinline__ void fwd_dma_codes(char* smem, const Fwd& f, int chunk) {
-  const int nch = (f.nsub + 3) >> 2;
-  const uint32_t soff = (uint32_t)min(chunk, nch - 1) * 64u;
-  char* dst = smem + kCodeBase + BUF * kCodes;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) dma16(f.cr, dst + (64 * q + 16 * f.w) * 64, f.co[q], soff);
-}
-__device__ __forceinline__ Scale fwd_scale(const Fwd& f, int blk) {
-  const int b = min(blk, f.nblk - 1);
-  return Scale{f.aq[b], f.gs[(f.ablk0 + (uint32_t)b) >> 8]};
-}
-
-// Dequantize chunks c0, c0+1 (8 elements each) of the owned row's codes of a
-// stage into ring buffer `buf`.
-__device__ __forceinline__ void fwd_produce(char* smem, const uint4& cw, const Nf4Table& T, int buf, int c0) {
-  char* row = smem + buf * kStage;
-#pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int c = c0 + k;
-    const uint32_t word = c == 0 ? cw.x : c == 1 ? cw.y : c == 2 ? cw.z : cw.w;
-    uint32_t o[4];
-    dequant8(word, T, o);
-    wr16(row + spos(threadIdx.x, c), make_uint4(o[0], o[1], o[2], o[3]));
-  }
-}
-
 struct Frags {
   bf16x8_t a0[4], b0[4], a1[4], b1[4];
 };
-
-// Substep s, U8 = s mod 8 (ring slot U8 & 3, code buffer of the produced
-// stage ((U8 + 2) >> 2) & 1): MFMAs on stage s, token DMA of stage s+3,
-// code DMA of chunk s/4 + 2 (U8 & 3 == 2), dequantization of stage s+2,
-// scales of block s/2 + 2 (U8 even; the table of block (s+2)/2 is built
-// from the scales loaded two substeps earlier).
-template <int CB, int U8>
-__device__ __forceinline__ void fwd_substep(char* smem, const Fwd& f, int s, f32x16_t (&acc)[4][4], Frags& F,
-                                            Nf4Table& T, Scale& sA, Scale& sB, int an, int bm, FragOffs fo) {
-  constexpr int U = U8 & 3;
-  constexpr int PS = U8 + 2;
-  const char* cur = smem + U * kStage;
-  const char* nxt = smem + ((U + 1) & 3) * kStage;
-  __builtin_amdgcn_sched_barrier(0);
-  fwd_dma_x(smem, f, s + 3, (U + 3) & 3);
-  if (U == 2) fwd_dma_codes<(U8 >> 2)>(smem, f, (s >> 2) + 2);
-  if (U == 0) sA = fwd_scale(f, (s >> 1) + 2);
-  if (U == 2) sB = fwd_scale(f, (s >> 1) + 2);
-  __builtin_amdgcn_sched_barrier(0);
-  const uint4 cw = rdu16(smem + kCodeBase + ((PS >> 2) & 1) * kCodes + spos(threadIdx.x, PS & 3));
-  if (U == 0) T = make_table<CB>(block_scale(sB.q, sB.s2));
-  if (U == 2) T = make_table<CB>(block_scale(sA.q, sA.s2));
-  // first half: k16 0 of stage s; read k16 1
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    F.a1[i] = rd16(cur + an + i * 2048 + fo.o1);
-    F.b1[i] = rd16(cur + kOp + bm + i * 2048 + fo.o1);
-  }
-  mfma_block<4, 4>(acc, F.a0, F.b0);
-  fwd_produce(smem, cw, T, (U + 2) & 3, 0);
-  schedule_half<1>();
-  // The token tile of stage s+1 (issued two substeps ago) has landed once
-  // at most the loads of the last two substeps are in flight: 4 token DMAs
-  // per substep, 4 code DMAs at U == 2, 2 scale loads at even U.
-  QLORA_WAIT(U == 0 ? 10 : U == 1 ? 10 : 14, 0);
-  __builtin_amdgcn_s_barrier();
-  // second half: k16 1 of stage s; read k16 0 of stage s+1
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    F.a0[i] = rd16(nxt + an + i * 2048 + fo.o0);
-    F.b0[i] = rd16(nxt + kOp + bm + i * 2048 + fo.o0);
-  }
-  mfma_block<4, 4>(acc, F.a1, F.b1);
-  fwd_produce(smem, cw, T, (U + 2) & 3, 2);
-  schedule_half<1>();
-}
-
-template <int CB>
-__global__ __launch_bounds__(kThreads, 1) void nf4_fwd_kernel(Nf4View W, const bf16_t* __restrict__ X, int64_t M,
-                                                              const bf16_t* __restrict__ U,
-                                                              const bf16_t* __restrict__ Bl, int r, float s,
-                                                              bf16_t* __restrict__ Y, int tiles_n, int tiles_m) {
-  extern __shared__ __align__(16) char smem[];
-  int tn, tm;
-  map_tile(tiles_n, tiles_m, tn, tm);
-  const int64_t n0 = (int64_t)tn * kTile, m0 = (int64_t)tm * kTile;
-  const int t = threadIdx.x, lane = t & 63, wr = (t >> 6) >> 1, wc = (t >> 6) & 1;
-  const int64_t N = W.N, K = W.K;
-
-  Fwd f;
-  f.w = __builtin_amdgcn_readfirstlane(t >> 6);
-  __builtin_assume(f.w >= 0 && f.w < 4);
-  f.xr = make_rsrc(X, (uint32_t)(M * K * 2));
-  f.cr = make_rsrc(W.codes, (uint32_t)(N * K / 2));
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    // rows past the end re-read the last row: finite data, never stored
-    const int row = dma_row(q, t >> 6, lane);
-    const int64_t xm = min(m0 + row, M - 1), wn = min(n0 + row, N - 1);
-    f.xo[q] = (uint32_t)(xm * K * 2 + dma_chunk(lane) * 16);
-    f.co[q] = (uint32_t)(wn * (K / 2) + dma_chunk(lane) * 16);
-  }
-  const int64_t own = min(n0 + t, N - 1);
-  f.ablk0 = (uint32_t)(own * (K >> 6));
-  f.aq = W.absmax_q + f.ablk0;
-  f.gs = W.group_scale;
-  f.nsub = (int)(K >> 5);
-  f.nblk = (int)(K >> 6);
-  const FragOffs fo = frag_offs(lane);
-  const int an = wc * 128 * 64, bm = wr * 128 * 64;
-
-  f32x16_t acc[4][4];
-  zero_acc(acc);
-
-  // prologue: code chunks 0 and 1, scales of blocks 0 and 1, token stages
-  // 0..2; then stages 0 and 1 are dequantized
-  fwd_dma_codes<0>(smem, f, 0);
-  fwd_dma_codes<1>(smem, f, 1);
-  Scale sA = fwd_scale(f, 0), sB = fwd_scale(f, 1);
-  fwd_dma_x(smem, f, 0, 0);
-  fwd_dma_x(smem, f, 1, 1);
-  fwd_dma_x(smem, f, 2, 2);
-  QLORA_WAIT(0, 0);
-  __builtin_amdgcn_s_barrier();
-  Nf4Table T = make_table<CB>(block_scale(sA.q, sA.s2));
-#pragma unroll
-  for (int st = 0; st < 2; ++st) {
-    const uint4 cw = rdu16(smem + kCodeBase + spos(t, st));
-    fwd_produce(smem, cw, T, st, 0);
-    fwd_produce(smem, cw, T, st, 2);
-  }
-  QLORA_WAIT(0, 0);
-  __builtin_amdgcn_s_barrier();
-  Frags F;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    F.a0[i] = rd16(smem + an + i * 2048 + fo.o0);
-    F.b0[i] = rd16(smem + kOp + bm + i * 2048 + fo.o0);
-  }
-  // K % 64 == 0, so the stage count is even
-  int st = 0;
-#define QLORA_FWD_SUB(u) fwd_substep<CB, u>(smem, f, st + u, acc, F, T, sA, sB, an, bm, fo)
-  for (; st + 8 <= f.nsub; st += 8) {
-    QLORA_FWD_SUB(0); QLORA_FWD_SUB(1); QLORA_FWD_SUB(2); QLORA_FWD_SUB(3);
-    QLORA_FWD_SUB(4); QLORA_FWD_SUB(5); QLORA_FWD_SUB(6); QLORA_FWD_SUB(7);
-  }
-  const int rem = f.nsub - st;
-  if (rem >= 2) { QLORA_FWD_SUB(0); QLORA_FWD_SUB(1); }
-  if (rem >= 4) { QLORA_FWD_SUB(2); QLORA_FWD_SUB(3); }
-  if (rem >= 6) { QLORA_FWD_SUB(4); QLORA_FWD_SUB(5); }
-#undef QLORA_FWD_SUB
-  // drain the DMAs still in flight (clamped re-loads) before reusing the ring
-  QLORA_WAIT(0, 0);
-  __builtin_amdgcn_s_barrier();
-
-  if (r > 0) {
-    // LoRA up-projection: acc += (s U) B^T over the rank, 32 at a time
-    for (int j0 = 0; j0 < r; j0 += 32) {
-      char* wb = smem;
-      char* xb = smem + kOp;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int idx = t + kThreads * e;
-        const int row = idx >> 2, c = idx & 3, col = j0 + 8 * c;
-        uint4 v = make_uint4(0u, 0u, 0u, 0u);
-        if (col < r && n0 + row < N) v = *reinterpret_cast<const uint4*>(Bl + (n0 + row) * r + col);
-        wr16(wb + spos(row, c), v);
-      }
-      tail_tokens(xb, U, M, r, m0, j0, s);
-      QLORA_WAIT(0, 0);
-      __builtin_amdgcn_s_barrier();
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const int o = kk ? fo.o1 : fo.o0;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          F.a0[i] = rd16(wb + an + i * 2048 + o);
-          F.b0[i] = rd16(xb + bm + i * 2048 + o);
-        }
-        mfma_block<4, 4>(acc, F.a0, F.b0);
-      }
-      QLORA_WAIT(0, 0);
-      __builtin_amdgcn_s_barrier();
-    }
-  }
-  store_tile(acc, Y, N, M, N, m0, n0);
-}
 
 // ===========================================================================
 // Forward with the weight operand in registers.  Wave w owns weight rows
@@ -393,11 +170,8 @@ __global__ __launch_bounds__(kThreads, 1) void nf4_fwd_kernel(Nf4View W, const b
 //                dequantize step 0 of stage s+1 into the registers step 0
 //                of stage s has just freed.
 // ===========================================================================
-#ifndef QLORA_FWDR_AHEAD
-#define QLORA_FWDR_AHEAD 6
-#endif
 constexpr int kRSlots = 8;                                            // token ring depth (stage s in slot s & 7)
-constexpr int kRAhead = QLORA_FWDR_AHEAD;                             // token stages DMA'd ahead of use
+constexpr int kRAhead = 6;                                            // token stages DMA'd ahead of use
 // The refilled slot (stage s + kRAhead - 8) was last read in substep s-1 at
 // the latest; the code chunk DMA'd at substep 2c-7 is read at substep 2c-2.
 static_assert(kRAhead >= 2 && kRAhead <= 6, "ring / code-chunk schedule");
@@ -828,18 +602,14 @@ __global__ __launch_bounds__(kThreads, 1) void nf4_fwd_r_kernel(Nf4View W, const
 }
 
 // ===========================================================================
-// Forward with eight waves (two per SIMD), built with QLORA_FWD_EIGHT_WAVES.
-// It takes 9 % fewer cycles per stage than the four-wave kernel but draws
-// more power (twice the LDS reads), and under sustained load its clock
-// settles about 10 % lower, so it is not the default.  The tile is still 256 weight
-// rows x 256 tokens, but wave w owns only weight rows n0 + 32 w .. +31 (one
-// A fragment) against all 256 tokens: 8 accumulator tiles (128 registers),
-// so two waves share each SIMD.  A wave issues one instruction per cycle
-// slot at best, and one wave alone cannot keep the matrix unit busy while
-// it also issues the decode, the LDS reads and the loads; with two waves the
-// SIMD issues one wave's VALU or LDS work beside the other's MFMA.  The
-// decode per MFMA is unchanged (each weight still feeds 256 tokens); the
-// token fragments are read from LDS twice as often (1 KiB per MFMA).
+// Forward with 32 weight rows per wave: the tile is WAVES x 32 weight rows
+// x 256 tokens, and wave w owns weight rows n0 + 32 w .. +31 (one A
+// fragment) against all 256 tokens: 8 accumulator tiles (128 registers).
+// With WAVES = 4 it runs 128-row tiles: the halves of a launch's ragged last
+// round, and whole launches whose 256-row tiles would leave CUs idle.  The
+// decode per MFMA is the 256-row kernel's (each weight still feeds 256
+// tokens); the token fragments are read from LDS twice as often (1 KiB per
+// MFMA).
 //
 // Substep s (stage s, ring slot s & 7), one barrier each, 16 MFMA slots
 // x = 8 kk + j (fragment j, k16 step kk), fenced from one another:
@@ -853,10 +623,7 @@ __global__ __launch_bounds__(kThreads, 1) void nf4_fwd_r_kernel(Nf4View W, const
 //   step 1 of stage s+1 is decoded next, step 0 after slot 7 (into the
 //   registers of step 0 of stage s).
 // ===========================================================================
-#ifndef QLORA_FWD8_AHEAD
-#define QLORA_FWD8_AHEAD 6
-#endif
-constexpr int kR8Ahead = QLORA_FWD8_AHEAD;
+constexpr int kR8Ahead = 6;                                          // token stages DMA'd ahead of use
 static_assert(kR8Ahead >= 2 && kR8Ahead <= 6, "ring / code-chunk schedule");
 // Loads of substep v, token DMAs first: 16 / WAVES token DMAs per wave, then
 // 1 code DMA (odd v) or 2 scale loads (even v).
@@ -1732,23 +1499,6 @@ hipError_t launch_fwd_cb(const Nf4View& W, const bf16_t* X, int64_t M, const bf1
   const int tiles_n = (int)((W.N + kTile - 1) / kTile);
   const int tiles_m = (int)((M + kTile - 1) / kTile);
   const int tiles = tiles_n * tiles_m;
-#if defined(QLORA_FWD_LDS_WEIGHTS) || defined(QLORA_FWD_EIGHT_WAVES)
-#if defined(QLORA_FWD_LDS_WEIGHTS)
-  auto* fn = &nf4_fwd_kernel<CB>;
-  const size_t lds = kLdsFwd;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     (int)lds);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(fn, dim3(tiles), dim3(kThreads), lds, st, W, X, M, U, B, r, s, Y, tiles_n, tiles_m);
-#else
-  auto* fn = &nf4_fwd_n32_kernel<CB, 8>;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     (int)kLdsFwdR);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(fn, dim3(tiles), dim3(512), kLdsFwdR, st, W, X, M, U, B, r, s, Y, tiles_n, tiles_m, -1);
-#endif
-  return hipGetLastError();
-#else
   // When the last round of 256 x 256 tiles would leave at least half the CUs
   // idle, its tiles run as two 128-row halves each, in a second launch of
   // the 32-rows-per-wave kernel, so that round takes about half as long.
@@ -1769,7 +1519,6 @@ hipError_t launch_fwd_cb(const Nf4View& W, const bf16_t* X, int64_t M, const bf1
   hipLaunchKernelGGL(tail, dim3(2 * (tiles - main_tiles)), dim3(kThreads), kLdsFwdR, st, W, X, M, U, B, r, s, Y,
                      tiles_n, tiles_m, main_tiles);
   return hipGetLastError();
-#endif
 }
 
 template <int CB>

@@ -32,7 +32,7 @@
 //   * Persistent workgroups.  One 16-wave workgroup per CU (the 64 KiB table
 //     and x fill its LDS) walks a contiguous, cost-balanced range of row
 //     tiles.  The tables are built once; x is restaged only when the job's
-//     x changes; the code loads run one step ahead straight across tile
+//     x pointer or length changes; the code loads run one step ahead straight across tile
 //     boundaries, and each tile's LoRA rows and the next tile's group scales
 //     are fetched when the tile starts, so no tile boundary waits on memory.
 //
@@ -53,10 +53,6 @@ constexpr int kGvWaves = 16;                               // waves per workgrou
 constexpr int kGvThreads = 64 * kGvWaves;
 constexpr int kGvSets = 2;                                 // sets of four rows per wave
 constexpr int kGvRows = kGvWaves * 4 * kGvSets;            // weight rows per workgroup
-#ifndef QLORA_GEMV_AHEAD
-#define QLORA_GEMV_AHEAD 1
-#endif
-constexpr int kGvAhead = QLORA_GEMV_AHEAD;                 // steps of code loads in flight per wave (1 or 2)
 constexpr int kStepBlocks = 8;                             // NF4 blocks per row per step (256 code bytes)
 constexpr int kLutBytes = 256 * 64 * 4;                    // 256 entries x 64 lane columns
 constexpr int kZeroBytes = 512;                            // zero run read by the off-diagonal A lanes
@@ -232,7 +228,10 @@ __global__ __launch_bounds__(kGvThreads) void nf4_gemv_kernel(const GemvJob* __r
   const uint32_t pblk = 2u * (uint32_t)p;               // first of the lane's two blocks within a step
   const uint32_t rchunk = (uint32_t)(4 * g + p);        // the lane's 8-rank chunk of the LoRA term
 
+  // x in LDS belongs to (staged, staged_k); two jobs may share an x
+  // pointer with different K, and the zero padding past K differs.
   const void* staged = nullptr;
+  int staged_k = 0;
   for (int si = range[blockIdx.x]; si < range[blockIdx.x + 1]; ++si) {
     const int4 sg = segs[si];
     const GemvJob& J = jobs[sg.x];
@@ -245,7 +244,7 @@ __global__ __launch_bounds__(kGvThreads) void nf4_gemv_kernel(const GemvJob* __r
     const rsrc_t br = make_rsrc(J.B, (uint32_t)N * (uint32_t)R * 2u);
     const rsrc_t ur = make_rsrc(J.u, (uint32_t)R * 4u);
 
-    if (J.x != staged) {   // uniform: restage x (zero-padded to whole steps)
+    if (J.x != staged || K != staged_k) {   // uniform: restage x (zero-padded to whole steps)
       const rsrc_t xr = make_rsrc(J.x, (uint32_t)K * 2u);
       constexpr int kXChunks = 4;   // 16-byte chunks per thread: K <= 32768
       uint4 xv[kXChunks];
@@ -259,6 +258,7 @@ __global__ __launch_bounds__(kGvThreads) void nf4_gemv_kernel(const GemvJob* __r
       }
       __syncthreads();
       staged = J.x;
+      staged_k = K;
     }
 
     // The lane's u chunk (zero past r: range check).
@@ -308,7 +308,7 @@ __global__ __launch_bounds__(kGvThreads) void nf4_gemv_kernel(const GemvJob* __r
       rbn[k] = rbase_of(t_first + 1 <= t_last ? t_first + 1 : t_last, k);
     }
     load_s2(s2c, rbc);
-    // Loads run kGvAhead steps ahead of use, straight across tile
+    // Loads run one step ahead of use, straight across tile
     // boundaries: (tl, sl) is the next step to load; past the segment's
     // last step it stays on that step (a re-read of cached lines).
     int tl = t_first, sl = 0;
@@ -325,9 +325,6 @@ __global__ __launch_bounds__(kGvThreads) void nf4_gemv_kernel(const GemvJob* __r
       }
     };
     load_next(cs, aq);
-    uint4 cs1[kGvSets];
-    uint32_t aq1[kGvSets];
-    if constexpr (kGvAhead == 2) load_next(cs1, aq1);
 
     for (int t = t_first; t <= t_last; ++t) {
       // tile start: this tile's LoRA rows and the next tile's group scales
@@ -350,7 +347,7 @@ __global__ __launch_bounds__(kGvThreads) void nf4_gemv_kernel(const GemvJob* __r
       uint32_t xa = xa0;
 
       for (int s = 0; s < nsteps; ++s) {
-        // the loads kGvAhead steps ahead first
+        // the next step's loads first
         uint4 csn[kGvSets];
         uint32_t aqn[kGvSets];
         load_next(csn, aqn);
@@ -383,15 +380,8 @@ __global__ __launch_bounds__(kGvThreads) void nf4_gemv_kernel(const GemvJob* __r
         xa += xinc;
 #pragma unroll
         for (int k = 0; k < kGvSets; ++k) {
-          if constexpr (kGvAhead == 2) {
-            cs[k] = cs1[k];
-            aq[k] = aq1[k];
-            cs1[k] = csn[k];
-            aq1[k] = aqn[k];
-          } else {
-            cs[k] = csn[k];
-            aq[k] = aqn[k];
-          }
+          cs[k] = csn[k];
+          aq[k] = aqn[k];
         }
       }
 

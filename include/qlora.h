@@ -61,8 +61,10 @@ typedef enum {
   QLORA_E_UNSUPPORTED = 4, /* blocksize != 64, group != 256, cols % 64 != 0
                               on the GEMM/GEMV paths, rows % 8 != 0 or
                               rows*cols/2 >= 2^32 on the GEMM paths, M*rows
-                              or M*cols >= 2^31 on the fused GEMMs, r
-                              outside [0,128] or r % 8 != 0, too many jobs,
+                              or M*cols >= 2^31 on the fused GEMMs, rows
+                              or cols >= 2^24 where a LoRA side product
+                              runs over them, r outside [0,128] or
+                              r % 8 != 0, too many jobs,
                               an unknown codebook, GEMV jobs of different
                               codebooks in one call */
   QLORA_E_WORKSPACE = 5,   /* ws_bytes smaller than qlora_workspace_bytes()  */
@@ -210,12 +212,13 @@ qlora_status qlora_linear_bwd(const qlora_nf4_weight* W, const uint16_t* X, cons
  * qlora_workspace_bytes(QLORA_OP_LORA, M, N, K, r, 0). */
 
 /* U [M x r] = X A^T (bf16).  deepfa.ir "LoRA: Prerequisite": the adapter's
- * down-projection.  r in (0, 128], r % 8 == 0, K % 8 == 0. */
+ * down-projection.  r in (0, 128], r % 8 == 0, K % 8 == 0, K < 2^24
+ * (QLORA_E_UNSUPPORTED otherwise). */
 qlora_status qlora_lora_down(const uint16_t* X, const uint16_t* A, int64_t M, int64_t K, int32_t r,
                              uint16_t* U, void* ws, size_t ws_bytes, void* stream);
 
 /* G [M x r] = dY B (bf16): the gradient reaching the adapter's
- * down-projection output.  N % 8 == 0. */
+ * down-projection output.  N % 8 == 0, N < 2^24. */
 qlora_status qlora_lora_dy_b(const uint16_t* dY, const uint16_t* B, int64_t M, int64_t N, int32_t r,
                              uint16_t* G, void* ws, size_t ws_bytes, void* stream);
 

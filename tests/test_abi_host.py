@@ -143,6 +143,25 @@ def test_validation_happens_before_any_launch(L):
     assert L.qlora_gemv(jobs, 1, None, 0, None) == 1
 
 
+def test_lora_side_products_reject_32_bit_overflow(L):
+    """The LoRA products address a 128-row tile of X or dY and the rank-side
+    operand with 32-bit byte ranges: a K or N of 2^24 or more is refused
+    before any launch (one token, so the token-matrix limits pass)."""
+    fake = ctypes.c_void_p(4096)
+    big = 1 << 24
+    assert L.qlora_lora_down(fake, fake, 1, big, 64, fake, fake, 1 << 30, None) == 4
+    assert L.qlora_lora_down(fake, fake, 1, big - 8, 64, fake, None, 0, None) != 4
+    assert L.qlora_lora_dy_b(fake, fake, 1, big, 64, fake, fake, 1 << 30, None) == 4
+    wide = _desc(rows=8, cols=big, codes=4096, aq=8192, s2=12288)
+    assert L.qlora_linear_fwd(ctypes.byref(wide), fake, 1, fake, fake, 64, 16.0, fake, None, fake, 1 << 40,
+                              None) == 4
+    assert L.qlora_linear_bwd(ctypes.byref(wide), fake, fake, 1, fake, fake, 64, 16.0, None, fake, fake, fake,
+                              fake, 1 << 40, None) == 4
+    tall = _desc(rows=big, cols=64, codes=4096, aq=8192, s2=12288)
+    assert L.qlora_linear_bwd(ctypes.byref(tall), fake, fake, 1, fake, fake, 64, 16.0, None, fake, fake, fake,
+                              fake, 1 << 40, None) == 4
+
+
 @pytest.mark.parametrize("name,cb", [("nf4", 0), ("fp4", 1), ("int4", 2)])
 def test_codebook_tables_bitwise_equal_oracle(L, name, cb):
     buf = (ctypes.c_float * 16)()

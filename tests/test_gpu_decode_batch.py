@@ -20,11 +20,13 @@ from tests.helpers import assert_close, bits_to_torch, torch_to_f64
 pytestmark = pytest.mark.gpu
 
 
-def _job(N, K, r, m, seed):
+def _job(N, K, r, m, seed, ab_std=0.01, w_std=0.02):
+    """w_std = 0 gives W = 0 exactly, so Y is the LoRA term alone."""
     rng = np.random.default_rng(seed)
     g = lambda shape, std: synth.to_bf16_bits(rng.standard_normal(shape) * std)
-    return dict(W=g((N, K), 0.02), x=g((m, K) if m else (K,), 1.0), A=g((r, K), 0.01) if r else None,
-                B=g((N, r), 0.01) if r else None, alpha=16.0)
+    W = g((N, K), w_std) if w_std else np.zeros((N, K), dtype=np.uint16)
+    return dict(W=W, x=g((m, K) if m else (K,), 1.0), A=g((r, K), ab_std) if r else None,
+                B=g((N, r), ab_std) if r else None, alpha=16.0)
 
 
 def _oracle_y(d, codebook="nf4"):
@@ -61,6 +63,35 @@ def _run(ds, label, codebook="nf4"):
                                      (40, 22016, 64, 4)])
 def test_single_job_shapes(N, K, r, m):
     _run([_job(N, K, r, m, seed=N + K + r + m)], f"N{N} K{K} r{r} m{m}")
+
+
+# The LoRA term carries Y in these cases, so a mistake in the m-token
+# u = A x, in the staged s u or in the up-projection MFMAs at tile end
+# cannot hide inside the tolerance of the base product.
+@pytest.mark.parametrize("N,K,r,m", [(1024, 1024, 64, 2), (520, 8192, 128, 16), (40, 22016, 64, 5),
+                                     (1100, 2112, 128, 9), (300, 640, 64, 16)])
+def test_lora_only_weight_zero(N, K, r, m):
+    _run([_job(N, K, r, m, seed=8000 + N + r + m, ab_std=1.0, w_std=0.0)], f"W=0 N{N} K{K} r{r} m{m}")
+
+
+@pytest.mark.parametrize("r,ab_std,m", [(64, 1.0, 4), (128, 1.0, 16), (128, 0.2, 8), (64, 0.2, 2)])
+def test_lora_dominant_stress(r, ab_std, m):
+    d = _job(768, 4096, r, m, seed=8100 + r + m, ab_std=ab_std)
+    f = lambda k: oracle.bf16_bits_to_f64(d[k]).reshape(d[k].shape)
+    lora = d["alpha"] / r * (f("x") @ f("A").T) @ f("B").T
+    assert np.linalg.norm(lora) > 0.9 * np.linalg.norm(_oracle_y(d))
+    _run([d], f"stress r{r} ab{ab_std} m{m}")
+
+
+def test_lora_stress_mixed_call():
+    # batch-1 and m-token jobs, W = 0 and LoRA-dominant and ordinary, in one call
+    ds = [_job(1024, 1024, 64, 16, seed=8200, ab_std=1.0, w_std=0.0),
+          _job(512, 8192, 128, 0, seed=8201, ab_std=1.0),
+          _job(40, 22016, 64, 3, seed=8202),
+          _job(300, 1536, 128, 8, seed=8203, ab_std=0.2, w_std=0.0),
+          _job(1536, 512, 8, 1, seed=8204, ab_std=1.0, w_std=0.0),
+          _job(700, 1088, 32, 12, seed=8205, ab_std=1.0)]
+    _run(ds, "stress mixed")
 
 
 def test_tokens_past_the_first_are_not_the_first_token_repeated():

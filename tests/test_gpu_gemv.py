@@ -16,10 +16,13 @@ from tests.helpers import assert_close, bits_to_torch, torch_to_f64
 pytestmark = pytest.mark.gpu
 
 
-def _job(N, K, r, seed, ab_std=0.01):
+def _job(N, K, r, seed, ab_std=0.01, w_std=0.02):
+    """w_std = 0 gives W = 0 exactly (every block all-zero), so y is the
+    LoRA term alone."""
     rng = np.random.default_rng(seed)
     g = lambda shape, std: synth.to_bf16_bits(rng.standard_normal(shape) * std)
-    return dict(W=g((N, K), 0.02), x=g((K,), 1.0), A=g((r, K), ab_std) if r else None,
+    W = g((N, K), w_std) if w_std else np.zeros((N, K), dtype=np.uint16)
+    return dict(W=W, x=g((K,), 1.0), A=g((r, K), ab_std) if r else None,
                 B=g((N, r), ab_std) if r else None, alpha=16.0)
 
 
@@ -55,6 +58,56 @@ def test_small_config_one_token():
                                    (64, 320, 0), (37, 22016, 64), (300, 1536, 8)])
 def test_single_job_shapes(N, K, r):
     _run([_job(N, K, r, seed=N + K + r)], f"N{N} K{K} r{r}")
+
+
+# The LoRA side path carries y, so a mistake in u = A x, in its scale or in
+# the up-projection at tile start cannot hide inside the tolerance of a base
+# product that dominates y (deepfa.ir blog, "LoRA: Prerequisite": the
+# adapter's low-rank product is added to the frozen layer's).
+@pytest.mark.parametrize("N,K,r", [(1024, 1024, 64), (257, 8192, 128), (37, 22016, 64), (300, 1536, 128)])
+def test_lora_only_weight_zero(N, K, r):
+    d = _job(N, K, r, seed=7000 + N + r, ab_std=1.0, w_std=0.0)
+    _run([d], f"W=0 N{N} K{K} r{r}")
+
+
+@pytest.mark.parametrize("r,ab_std", [(64, 1.0), (128, 1.0), (128, 0.2)])
+def test_lora_dominant_stress(r, ab_std):
+    d = _job(768, 4096, r, seed=7100 + r, ab_std=ab_std)
+    ref = _oracle_y(d)
+    # the case is only a stress case if the LoRA term carries most of y
+    f = lambda k: oracle.bf16_bits_to_f64(d[k]).reshape(d[k].shape)
+    lora = d["alpha"] / r * f("B") @ (f("A") @ f("x"))
+    assert np.linalg.norm(lora) > 0.9 * np.linalg.norm(ref)
+    _run([d], f"stress r{r} ab{ab_std}")
+
+
+def test_lora_stress_mixed_call():
+    # W = 0, LoRA-dominant and ordinary jobs of several shapes in one call
+    ds = [_job(1024, 1024, 64, seed=7200, ab_std=1.0, w_std=0.0), _job(512, 8192, 128, seed=7201, ab_std=1.0),
+          _job(37, 22016, 64, seed=7202), _job(300, 1536, 128, seed=7203, ab_std=0.2, w_std=0.0),
+          _job(64, 320, 0, seed=7204), _job(1536, 512, 8, seed=7205, ab_std=1.0)]
+    _run(ds, "stress mixed")
+
+
+def test_jobs_sharing_x_with_different_lengths():
+    """Two jobs read one x buffer, over different lengths K: each must see
+    its own K columns with zero beyond (the x staged for the first job must
+    not serve the second)."""
+    x_full = synth.to_bf16_bits(np.random.default_rng(7300).standard_normal(4096))
+    x = bits_to_torch(x_full)
+    ds, jobs = [], []
+    for i, (N, K) in enumerate([(512, 4096), (300, 1088), (700, 4096), (64, 2112)]):
+        d = _job(N, K, 64, seed=7310 + i, ab_std=0.2)
+        d["x"] = x_full[:K]
+        ds.append(d)
+        q = ops.quantize(bits_to_torch(d["W"]))
+        jobs.append(ops.GemvJob(q, x[:K], bits_to_torch(d["A"]), bits_to_torch(d["B"]), d["alpha"]))
+    assert all(j.x.data_ptr() == x.data_ptr() for j in jobs)
+    print("[gemv parity] one x buffer, four lengths", flush=True)
+    ys = ops.gemv(jobs)
+    torch.cuda.synchronize()
+    for i, (d, y) in enumerate(zip(ds, ys)):
+        assert_close(torch_to_f64(y), _oracle_y(d), f"shared x job {i}")
 
 
 def test_grouped_batch_mixed_shapes():
