@@ -25,7 +25,11 @@ EXPORTS = [
     "qlora_codebook_levels", "qlora_adamw",
     "qlora_linear_fwd", "qlora_linear_bwd", "qlora_gemv", "qlora_gemv_prepare", "qlora_gemv_run",
     "qlora_lora_down", "qlora_lora_dy_b", "qlora_lora_grads", "qlora_nf4_fwd", "qlora_nf4_dx",
+    "qlora_linear_fwd_noalloc",
 ]
+
+# QLORA_STATIC_SCRATCH_BYTES: scratch array of qlora_linear_fwd_noalloc per device
+STATIC_SCRATCH_BYTES = 32 << 20
 
 
 class Nf4WeightDesc(ctypes.Structure):
@@ -108,6 +112,8 @@ def lib():
     L.qlora_adamw.argtypes = [vp, vp, vp, vp, vp, i64, f32, f32, f32, f32, f32, i32, vp]
     L.qlora_linear_fwd.restype = ctypes.c_int
     L.qlora_linear_fwd.argtypes = [W, vp, i64, vp, vp, i32, f32, vp, vp, vp, sz, vp]
+    L.qlora_linear_fwd_noalloc.restype = ctypes.c_int
+    L.qlora_linear_fwd_noalloc.argtypes = [W, vp, i64, vp, vp, i32, f32, vp, vp, vp]
     L.qlora_linear_bwd.restype = ctypes.c_int
     L.qlora_linear_bwd.argtypes = [W, vp, vp, i64, vp, vp, i32, f32, vp, vp, vp, vp, vp, sz, vp]
     L.qlora_gemv.restype = ctypes.c_int

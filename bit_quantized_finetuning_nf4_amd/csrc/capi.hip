@@ -8,11 +8,14 @@
 //   BWD  (r > 0): G bf16 [M x r] | U bf16 [M x r] | split partials (fp32,
 //                 the largest of X A^T, dY B, G^T X, dY^T U)
 //   GEMV        : per job, 128 fp32 for u = A x | the device job table
+// qlora_linear_fwd_noalloc carves the FWD layout out of `scratch` below
+// instead of a caller workspace.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "../../include/qlora.h"
@@ -148,6 +151,69 @@ qlora_status check_adapter_rank(int32_t r) {
 
 }  // namespace
 
+// Scratch of qlora_linear_fwd_noalloc: one array per device, held until the
+// process ends.  In host code `scratch` only names the symbol; its device
+// address comes from hipGetSymbolAddress, looked up once per device.
+static __device__ __align__(256) unsigned char scratch[QLORA_STATIC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];   // device address of `scratch`, per device
+
+// The device address of `scratch` on the current device.
+qlora_status static_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e);
+  if (dev < 0 || dev >= kMaxDevices) return QLORA_E_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e);
+    if (!p) return QLORA_E_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return QLORA_OK;
+}
+
+// Argument checks of the forward, before any workspace is looked at.
+qlora_status check_fwd(const qlora_nf4_weight* W, const uint16_t* X, int64_t M, const uint16_t* A,
+                       const uint16_t* B, int32_t r, const uint16_t* Y, const uint16_t* U_save) {
+  qlora_status st = check_gemm_weight(W);
+  if (st != QLORA_OK) return st;
+  if ((st = check_tokens(M, W)) != QLORA_OK) return st;
+  if (!X || !Y) return QLORA_E_NULL;
+  if (!aligned16(X) || !aligned16(Y) || (U_save && !aligned16(U_save))) return QLORA_E_ALIGN;
+  if ((st = check_rank(r, A, B)) != QLORA_OK) return st;
+  if (r > 0 && !skinny_cols_ok(W->cols)) return QLORA_E_UNSUPPORTED;
+  return QLORA_OK;
+}
+
+// The forward's launches, on a workspace of the FWD layout.
+qlora_status run_fwd(const qlora_nf4_weight* W, const uint16_t* X, int64_t M, const uint16_t* A,
+                     const uint16_t* B, int32_t r, float alpha, uint16_t* Y, uint16_t* U_save, void* ws,
+                     hipStream_t s) {
+  const FwdLayout L = fwd_layout(M, W->rows, W->cols, r);
+  const Nf4View v = view(W);
+  const bf16_t* U = nullptr;
+  float sc = 0.0f;
+  if (r > 0) {
+    sc = (float)((double)alpha / (double)r);  // s = RN32(alpha / r)
+    bf16_t* Ud = U_save ? U_save : reinterpret_cast<bf16_t*>(ws_at(ws, L.u));
+    float* part = reinterpret_cast<float*>(ws_at(ws, L.part));
+    qlora_status st = hip_status(launch_xat(X, A, M, W->cols, r, part, Ud, nullptr, 1.0f, s));
+    if (st != QLORA_OK) return st;
+    U = Ud;
+  }
+  return hip_status(launch_fwd(v, X, M, U, B, r, sc, Y, s));
+}
+
+}  // namespace
+
 extern "C" {
 
 const char* qlora_status_str(qlora_status s) {
@@ -271,30 +337,25 @@ qlora_status qlora_dequant(const qlora_nf4_weight* q, uint16_t* W_out, void* str
 qlora_status qlora_linear_fwd(const qlora_nf4_weight* W, const uint16_t* X, int64_t M, const uint16_t* A,
                               const uint16_t* B, int32_t r, float alpha, uint16_t* Y, uint16_t* U_save,
                               void* ws, size_t ws_bytes, void* stream) {
-  qlora_status st = check_gemm_weight(W);
+  qlora_status st = check_fwd(W, X, M, A, B, r, Y, U_save);
   if (st != QLORA_OK) return st;
-  if ((st = check_tokens(M, W)) != QLORA_OK) return st;
-  if (!X || !Y) return QLORA_E_NULL;
-  if (!aligned16(X) || !aligned16(Y) || (U_save && !aligned16(U_save))) return QLORA_E_ALIGN;
-  if ((st = check_rank(r, A, B)) != QLORA_OK) return st;
-  if (r > 0 && !skinny_cols_ok(W->cols)) return QLORA_E_UNSUPPORTED;
   const FwdLayout L = fwd_layout(M, W->rows, W->cols, r);
   if (ws_bytes < L.total) return QLORA_E_WORKSPACE;
   if (L.total > 0 && !ws) return QLORA_E_NULL;
   if (L.total > 0 && !aligned16(ws)) return QLORA_E_ALIGN;
-  hipStream_t s = (hipStream_t)stream;
-  const Nf4View v = view(W);
-  const bf16_t* U = nullptr;
-  float sc = 0.0f;
-  if (r > 0) {
-    sc = (float)((double)alpha / (double)r);  // s = RN32(alpha / r)
-    bf16_t* Ud = U_save ? U_save : reinterpret_cast<bf16_t*>(ws_at(ws, L.u));
-    float* part = reinterpret_cast<float*>(ws_at(ws, L.part));
-    st = hip_status(launch_xat(X, A, M, W->cols, r, part, Ud, nullptr, 1.0f, s));
-    if (st != QLORA_OK) return st;
-    U = Ud;
-  }
-  return hip_status(launch_fwd(v, X, M, U, B, r, sc, Y, s));
+  return run_fwd(W, X, M, A, B, r, alpha, Y, U_save, ws, (hipStream_t)stream);
+}
+
+qlora_status qlora_linear_fwd_noalloc(const qlora_nf4_weight* W, const uint16_t* X, int64_t M, const uint16_t* A,
+                                      const uint16_t* B, int32_t r, float alpha, uint16_t* Y, uint16_t* U_save,
+                                      void* stream) {
+  qlora_status st = check_fwd(W, X, M, A, B, r, Y, U_save);
+  if (st != QLORA_OK) return st;
+  const FwdLayout L = fwd_layout(M, W->rows, W->cols, r);
+  if (L.total > QLORA_STATIC_SCRATCH_BYTES) return QLORA_E_WORKSPACE;
+  void* ws = nullptr;
+  if (L.total > 0 && (st = static_scratch(&ws)) != QLORA_OK) return st;
+  return run_fwd(W, X, M, A, B, r, alpha, Y, U_save, ws, (hipStream_t)stream);
 }
 
 qlora_status qlora_linear_bwd(const qlora_nf4_weight* W, const uint16_t* X, const uint16_t* dY, int64_t M,

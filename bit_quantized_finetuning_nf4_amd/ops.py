@@ -158,6 +158,29 @@ def linear_fwd(q: QuantizedWeight, X: torch.Tensor, A=None, B=None, alpha: float
     return (Y, U) if save_u else Y
 
 
+def linear_fwd_noalloc(q: QuantizedWeight, X: torch.Tensor, A=None, B=None, alpha: float = 0.0,
+                       save_u: bool = False, out=None, u_out=None):
+    """linear_fwd through qlora_linear_fwd_noalloc: the library's scratch
+    array replaces the workspace, so only the outputs (when not given) are
+    allocated here.  Returns Y, or (Y, U) with save_u."""
+    _need(X, torch.bfloat16, "X")
+    M = X.shape[0]
+    r = 0 if A is None else A.shape[0]
+    if r:
+        _need(A, torch.bfloat16, "A", (r, q.cols))
+        _need(B, torch.bfloat16, "B", (q.rows, r))
+    Y = out if out is not None else torch.empty(M, q.rows, dtype=torch.bfloat16, device=X.device)
+    _need(Y, torch.bfloat16, "Y", (M, q.rows))
+    U = None
+    if save_u and r:
+        U = u_out if u_out is not None else torch.empty(M, r, dtype=torch.bfloat16, device=X.device)
+        _need(U, torch.bfloat16, "U", (M, r))
+    d = q.desc()
+    check(lib().qlora_linear_fwd_noalloc(ctypes.byref(d), _ptr(X), M, _ptr(A), _ptr(B), r, float(alpha), _ptr(Y),
+                                         _ptr(U), _stream()), "qlora_linear_fwd_noalloc")
+    return (Y, U) if save_u else Y
+
+
 def linear_bwd(q: QuantizedWeight, X: torch.Tensor, dY: torch.Tensor, A=None, B=None, alpha: float = 0.0,
                U: Optional[torch.Tensor] = None, need_dx: bool = True, dX=None, dA=None, dB=None, ws=None):
     """Returns (dX, dA, dB): dX bf16 [M x K] (or None), dA [r x K] and dB [N x r] fp32 (or None)."""

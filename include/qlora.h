@@ -31,15 +31,18 @@
  *     tensors travel as uint16_t bit patterns; all are row-major, contiguous.
  *   - The library never allocates or frees memory and never synchronizes.
  *     Scratch memory is the caller's `ws` buffer, sized by
- *     qlora_workspace_bytes().
+ *     qlora_workspace_bytes(), except for qlora_linear_fwd_noalloc, whose
+ *     scratch is a fixed array the library holds on each device.
  *   - Every call is asynchronous on `stream` (a hipStream_t; NULL = the
  *     default stream).  Device-side faults surface at the caller's next
  *     synchronization.
  *   - All argument checks happen before any launch: a status other than
  *     QLORA_OK means nothing was enqueued.
- *   - The library keeps no mutable global state and is thread-safe; two
- *     calls that share an output or workspace buffer must be ordered by the
- *     caller (same stream, or events).
+ *   - The library is thread-safe.  Its only mutable global state is the
+ *     per-device address of the scratch array of qlora_linear_fwd_noalloc,
+ *     looked up once under a lock.  Two calls that share an output or
+ *     workspace buffer must be ordered by the caller (same stream, or
+ *     events).
  *   - Alignment: codes, X, dY, Y, dX, A, B, U, x, y and ws must be 16-byte
  *     aligned (QLORA_E_ALIGN otherwise).
  */
@@ -202,6 +205,27 @@ qlora_status qlora_linear_bwd(const qlora_nf4_weight* W, const uint16_t* X, cons
                               int64_t M, const uint16_t* A, const uint16_t* B, int32_t r,
                               float alpha, const uint16_t* U_saved, uint16_t* dX,
                               float* dA, float* dB, void* ws, size_t ws_bytes, void* stream);
+
+/* Bytes of the scratch array of qlora_linear_fwd_noalloc on each device. */
+#define QLORA_STATIC_SCRATCH_BYTES ((size_t)32 << 20)
+
+/* qlora_linear_fwd without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  Same arguments, result and errors as
+ * qlora_linear_fwd; the scratch it would take from `ws` (U when U_save is
+ * NULL, and the split partial sums of X A^T) comes from a 32 MiB array the
+ * library holds on each device from its first use until the process ends.
+ * It calls no allocating routine.  A call needing more than
+ * QLORA_STATIC_SCRATCH_BYTES, i.e. qlora_workspace_bytes(QLORA_OP_FWD, M,
+ * N, K, r, 0) > QLORA_STATIC_SCRATCH_BYTES (for example M = 65536 at
+ * r = 128), returns QLORA_E_WORKSPACE before enqueuing anything.  The array
+ * is shared by every call on one device and keeps the last call's
+ * contents: calls that overlap on one device (concurrent streams, several
+ * host threads) race on it and must be ordered by the caller.  The current
+ * device must be the one `stream` belongs to. */
+qlora_status qlora_linear_fwd_noalloc(const qlora_nf4_weight* W, const uint16_t* X, int64_t M,
+                                      const uint16_t* A, const uint16_t* B, int32_t r, float alpha,
+                                      uint16_t* Y, uint16_t* U_save, void* stream);
 
 /* ---- Building blocks of the forward and backward passes ----------------
  * qlora_linear_fwd = qlora_lora_down + qlora_nf4_fwd;

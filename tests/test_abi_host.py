@@ -162,6 +162,22 @@ def test_lora_side_products_reject_32_bit_overflow(L):
                               fake, 1 << 40, None) == 4
 
 
+def test_noalloc_forward_rejects_oversize_and_bad_arguments_on_the_host(L):
+    """qlora_linear_fwd_noalloc: the same checks as qlora_linear_fwd, and a
+    call whose scratch exceeds the static array is refused before anything
+    touches the GPU."""
+    fake = ctypes.c_void_p(4096)
+    d = _desc(rows=1024, cols=8192, codes=4096, aq=8192, s2=12288)
+    need = L.qlora_workspace_bytes(0, 65536, 1024, 8192, 128, 0)
+    assert need > _lib.STATIC_SCRATCH_BYTES
+    assert L.qlora_linear_fwd_noalloc(ctypes.byref(d), fake, 65536, fake, fake, 128, 16.0, fake, None, None) == 5
+    assert L.qlora_linear_fwd_noalloc(ctypes.byref(d), None, 4, None, None, 0, 0.0, fake, None, None) == 1
+    assert L.qlora_linear_fwd_noalloc(ctypes.byref(d), fake, 4, fake, fake, 12, 1.0, fake, None, None) == 4
+    assert L.qlora_linear_fwd_noalloc(ctypes.byref(d), ctypes.c_void_p(4098), 4, None, None, 0, 0.0, fake, None,
+                                      None) == 2
+    assert L.qlora_linear_fwd_noalloc(ctypes.byref(d), fake, 0, None, None, 0, 0.0, fake, None, None) == 3
+
+
 @pytest.mark.parametrize("name,cb", [("nf4", 0), ("fp4", 1), ("int4", 2)])
 def test_codebook_tables_bitwise_equal_oracle(L, name, cb):
     buf = (ctypes.c_float * 16)()
