@@ -8,19 +8,29 @@ quantization over 256-block groups):
 
   1. quantize the seven bf16 weights (block absmax, NF4 codes, 8-bit absmax
      codes against fp32 group scales);
-  2. forward: U = X A^T, then the fused NF4 GEMM Y = X deq(W)^T + s U B^T;
-  3. backward: G = dY B, the fused NF4 GEMM dX = dY deq(W) + s G A, then
-     dA = s G^T X and dB = s dY^T U;
+  2. forward, per linear: U = X A^T; W dequantized once to bf16; the dense
+     bf16 GEMM Y = X deq(W)^T + s U B^T;
+  3. backward, per linear: G = dY B; W dequantized once, transposed; the
+     dense GEMM dX = dY deq(W) + s G A; dA = s G^T X and dB = s dY^T U;
   4. batch-1 decode: y = deq(W) x + s B (A x) for the seven linears in one
      grouped call.
 
+Steps 2 and 3 are the building blocks of qlora_linear_fwd / qlora_linear_bwd
+on their staged path (what those calls run at 1024 tokens and more when the
+workspace holds the bf16 weight).  The fused path (W decoded inside each
+256-token product tile) is timed the same way beside it.
+
 `value` is the fwd+bwd algorithmic work, sum over linears of
 4MNK + 6Mr(N+K) flops, divided by the wall time of whole steps (quantize and
-decode included).  HIP events on the launch stream bracket every fused GEMM
-launch; the slower of the two fused GEMMs is reported against the dense bf16
-MFMA peak.  The CPU oracle (fp64 numpy) is timed on one linear of the same
-workload.  With --decode-layers > 0 the 80-layer decode pass (about 65e9
-weights) is also timed and reported as HBM bandwidth.
+decode included).  HIP events on the launch stream bracket every dense GEMM
+launch; their flops over their summed durations is the roofline figure
+against the dense bf16 MFMA peak.  The 7B and 13B layer sets and the small
+1024x1024 case are timed the same way (fwd + bwd phases), dequantization is
+timed on the 65B gate weight (360 MB of bf16 out), and the shader clock is
+sampled with the box's smi tool while steps run.  The CPU oracle (fp64
+numpy) is timed on one linear of the same workload.  With --decode-layers > 0
+the 80-layer decode pass (about 65e9 weights) is also timed and reported as
+HBM bandwidth.
 
 Inputs are synthetic and seeded (bit_quantized_finetuning_nf4_amd.synth);
 they are resident in HBM before timing starts.
@@ -30,7 +40,9 @@ import argparse
 import hashlib
 import json
 import os
+import subprocess
 import sys
+import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -122,7 +134,8 @@ def decode_batch_study(jobs, layers, r, alpha, passes, dev):
 
 # the device code of each kernel whose traffic is reported: its source file
 # and the device headers it includes
-KERNEL_SOURCES = {"fwd_kernel": ["gemm_nf4.hip"], "dx_kernel": ["gemm_nf4.hip"],
+KERNEL_SOURCES = {"fwd_kernel": ["gemm_nf4.hip", "gemm_common.h"], "dx_kernel": ["gemm_nf4.hip", "gemm_common.h"],
+                  "dense_gemm": ["gemm_bf16.hip", "gemm_common.h"],
                   "quantize_kernel": ["quantize.hip"], "gemv_kernel": ["gemv.hip"]}
 DEVICE_HEADERS = ["device.h", "lds.h"]
 
@@ -152,7 +165,7 @@ def traffic_for(kernel):
 
 # rocprofv3 kernel name -> bench kernel; a launch of the fused GEMMs may add a
 # half-tile tail dispatch, whose bytes count towards that launch
-TRAFFIC_KERNELS = {"nf4_fwd_r_kernel": "fwd_kernel", "nf4_dx_kernel": "dx_kernel",
+TRAFFIC_KERNELS = {"nf4_fwd_r_kernel": "fwd_kernel", "nf4_dx_kernel": "dx_kernel", "bf16_fwd_kernel": "dense_gemm",
                    "quantize_kernel": "quantize_kernel", "nf4_gemv_kernel": "gemv_kernel"}
 TAIL_KERNELS = {"nf4_fwd_n32_kernel": "fwd_kernel", "nf4_dx_half_kernel": "dx_kernel"}
 
@@ -216,7 +229,7 @@ def summarize_mfma(csv_path, simds=1024, xccs=8):
     per = {}
     for row in csv.DictReader(open(csv_path)):
         m = re.search(r"(\w+_kernel)\b", row["Kernel_Name"])
-        if not m or not any(k in row["Kernel_Name"] for k in ("qlora", "nf4", "skinny")):
+        if not m or not any(k in row["Kernel_Name"] for k in ("qlora", "nf4", "skinny", "bf16_fwd")):
             continue
         d = per.setdefault(m.group(1), {}).setdefault(row["Dispatch_Id"], {})
         d[row["Counter_Name"]] = d.get(row["Counter_Name"], 0.0) + float(row["Counter_Value"])
@@ -333,6 +346,232 @@ def optimizer_study(L, r, dev, reps=5):
     return res
 
 
+class ClockSampler:
+    """Samples the shader clock (MHz, mean over the XCDs) with the box's smi
+    tool in a subprocess loop while the GPU works; the median of the samples
+    taken inside [start, stop] is the clock observed during the timed steps."""
+
+    def __init__(self):
+        self.samples, self._stop, self.tool = [], threading.Event(), None
+        for tool in (["amd-smi", "metric", "-c", "--json"], ["rocm-smi", "--showclocks", "--json"]):
+            try:
+                if self._read(tool) is not None:
+                    self.tool = tool
+                    break
+            except Exception:
+                pass
+
+    @staticmethod
+    def _read(tool):
+        out = subprocess.run(tool, capture_output=True, text=True, timeout=5).stdout
+        j = json.loads(out[out.index("{") if out.lstrip().startswith("{") else out.index("["):])
+        vals = []
+
+        def walk(o):
+            if isinstance(o, dict):
+                for k, v in o.items():
+                    if k.startswith("gfx_") and isinstance(v, dict) and isinstance(v.get("clk"), dict):
+                        vals.append(float(v["clk"]["value"]))
+                    elif "sclk clock speed" in k and isinstance(v, str):
+                        vals.append(float(v.strip("()Mhz")))
+                    else:
+                        walk(v)
+            elif isinstance(o, list):
+                for v in o:
+                    walk(v)
+        walk(j)
+        return sum(vals) / len(vals) if vals else None
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                v = self._read(self.tool)
+                if v is not None:
+                    self.samples.append(v)
+            except Exception:
+                pass
+
+    def __enter__(self):
+        if self.tool:
+            self._t = threading.Thread(target=self._run, daemon=True)
+            self._t.start()
+        return self
+
+    def __exit__(self, *a):
+        self._stop.set()
+        if self.tool:
+            self._t.join(timeout=10)
+
+    def result(self):
+        if not self.samples:
+            return None
+        v = sorted(self.samples)
+        return {"tool": " ".join(self.tool), "samples": len(v), "median_mhz": v[len(v) // 2],
+                "min_mhz": v[0], "max_mhz": v[-1]}
+
+
+class LayerSet:
+    """Inputs, outputs and scratch of one layer set, resident on the device,
+    and one step of the path over it (staged or fused products)."""
+
+    def __init__(self, name, dev, with_decode=True):
+        import torch
+        from bit_quantized_finetuning_nf4_amd import ops, synth
+        from bit_quantized_finetuning_nf4_amd import _lib
+        self.ops, self.torch = ops, torch
+        cfg = synth.LAYER_SETS[name]
+        self.name, self.M, self.r, self.alpha = name, cfg["M"], cfg["r"], cfg["alpha"]
+        set_index = {"small": 0, "llama7b": 1, "llama13b": 2, "llama65b": 3}[name]
+        M, r = self.M, self.r
+        self.L = []
+        for i, (lname, N, K) in enumerate(cfg["linears"]):
+            t = synth.linear_inputs(N, K, M, r, synth.layer_set_seed(set_index, i), dev, outliers=cfg["outliers"])
+            o = dict(name=lname, N=N, K=K, q=ops.QuantizedWeight.empty(N, K, dev), **t,
+                     x=t["X"][0].contiguous(),
+                     Y=torch.empty(M, N, dtype=torch.bfloat16, device=dev),
+                     U=torch.empty(M, r, dtype=torch.bfloat16, device=dev),
+                     G=torch.empty(M, r, dtype=torch.bfloat16, device=dev),
+                     dX=torch.empty(M, K, dtype=torch.bfloat16, device=dev),
+                     dA=torch.empty(r, K, dtype=torch.float32, device=dev),
+                     dB=torch.empty(N, r, dtype=torch.float32, device=dev))
+            self.L.append(o)
+        self.ws = ops.workspace(max(ops.workspace_bytes(_lib.QLORA_OP_LORA, M, o["N"], o["K"], r) for o in self.L),
+                                dev)
+        self.wbuf = torch.empty(max(o["N"] * o["K"] for o in self.L), dtype=torch.bfloat16, device=dev)
+        self.plan = (ops.GemvPlan([ops.GemvJob(o["q"], o["x"], o["A"], o["B"], self.alpha) for o in self.L])
+                     if with_decode else None)
+        self.fl_step = sum(linear_flops(M, o["N"], o["K"], r) for o in self.L)
+        self.fl_fwd = [2 * M * o["N"] * o["K"] + 2 * M * o["N"] * r for o in self.L]
+        self.fl_dx = [2 * M * o["N"] * o["K"] + 2 * M * o["K"] * r for o in self.L]
+        self.q_bytes = sum(2 * o["N"] * o["K"] + o["q"].nbytes() for o in self.L)
+        self.g_bytes = sum(gemv_bytes(o["N"], o["K"], r) for o in self.L)
+        for o in self.L:
+            ops.quantize(o["W"], out=o["q"])
+        torch.cuda.synchronize()
+
+    def step(self, path, record=None):
+        """One step; with `record` (a list) HIP events bracket the phases and
+        every product launch."""
+        ops, torch, a, L = self.ops, self.torch, self.alpha, self.L
+        E = lambda: torch.cuda.Event(enable_timing=True)
+        ev = dict(p=[E() for _ in range(5)], f=[(E(), E()) for _ in L], d=[(E(), E()) for _ in L]) \
+            if record is not None else None
+        mark = (lambda e: e.record()) if ev else (lambda e: None)
+        if ev:
+            mark(ev["p"][0])
+        for o in L:
+            ops.quantize(o["W"], out=o["q"])
+        if ev:
+            mark(ev["p"][1])
+        for i, o in enumerate(L):
+            ops.lora_down(o["X"], o["A"], U=o["U"], ws=self.ws)
+            if path == "staged":
+                Wd = ops.dequant(o["q"], out=self.wbuf[:o["N"] * o["K"]].view(o["N"], o["K"]))
+                if ev:
+                    mark(ev["f"][i][0])
+                ops.bf16_fwd(Wd, o["X"], o["U"], o["B"], a, out=o["Y"])
+            else:
+                if ev:
+                    mark(ev["f"][i][0])
+                ops.nf4_fwd(o["q"], o["X"], o["U"], o["B"], a, out=o["Y"])
+            if ev:
+                mark(ev["f"][i][1])
+        if ev:
+            mark(ev["p"][2])
+        for i, o in enumerate(L):
+            ops.lora_dy_b(o["dY"], o["B"], G=o["G"], ws=self.ws)
+            if path == "staged":
+                WdT = ops.dequant_t(o["q"], out=self.wbuf[:o["N"] * o["K"]].view(o["K"], o["N"]))
+                if ev:
+                    mark(ev["d"][i][0])
+                ops.bf16_dx(WdT, o["dY"], o["G"], o["A"], a, out=o["dX"])
+            else:
+                if ev:
+                    mark(ev["d"][i][0])
+                ops.nf4_dx(o["q"], o["dY"], o["G"], o["A"], a, out=o["dX"])
+            if ev:
+                mark(ev["d"][i][1])
+            ops.lora_grads(o["X"], o["dY"], o["U"], o["G"], a, dA=o["dA"], dB=o["dB"], ws=self.ws)
+        if ev:
+            mark(ev["p"][3])
+        if self.plan is not None:
+            self.plan()
+        if ev:
+            mark(ev["p"][4])
+            record.append(ev)
+
+    def run(self, path, steps, warmup):
+        """Timed steps: wall time per step, phases and per-product times."""
+        torch = self.torch
+        for _ in range(warmup):
+            self.step(path)
+        torch.cuda.synchronize()
+        record = []
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            self.step(path, record)
+        torch.cuda.synchronize()
+        ms_step = (time.perf_counter() - t0) * 1e3 / steps
+        ph = {"quantize": 0.0, "forward": 0.0, "backward": 0.0, "decode_gemv": 0.0}
+        fwd_ms = dx_ms = 0.0
+        for ev in record:
+            p = ev["p"]
+            ph["quantize"] += p[0].elapsed_time(p[1])
+            ph["forward"] += p[1].elapsed_time(p[2])
+            ph["backward"] += p[2].elapsed_time(p[3])
+            ph["decode_gemv"] += p[3].elapsed_time(p[4])
+            fwd_ms += sum(x.elapsed_time(y) for x, y in ev["f"])
+            dx_ms += sum(x.elapsed_time(y) for x, y in ev["d"])
+        ph = {k: v / steps for k, v in ph.items()}
+        fwd_ms, dx_ms = fwd_ms / steps, dx_ms / steps
+        n = len(self.L)
+        gemm_tf = (sum(self.fl_fwd) + sum(self.fl_dx)) / ((fwd_ms + dx_ms) * 1e-3) / 1e12
+        return {
+            "path": path, "ms_per_step": ms_step, "phases_ms": ph,
+            "fwd_bwd_tflops": self.fl_step / ((ph["forward"] + ph["backward"]) * 1e-3) / 1e12,
+            "products": {
+                "kernel": "bf16_fwd_kernel (dense bf16 GEMM)" if path == "staged"
+                          else "nf4_fwd_r_kernel / nf4_dx_kernel (fused NF4 GEMMs)",
+                "launches_per_step": 2 * n,
+                "fwd_avg_launch_ms": fwd_ms / n, "dx_avg_launch_ms": dx_ms / n,
+                "fwd_tflops": sum(self.fl_fwd) / (fwd_ms * 1e-3) / 1e12,
+                "dx_tflops": sum(self.fl_dx) / (dx_ms * 1e-3) / 1e12,
+                "tflops": gemm_tf, "frac_of_bf16_peak": gemm_tf / PEAK_BF16_TFLOPS},
+        }
+
+
+def dequant_study(dev, reps=10):
+    """qlora_dequant and qlora_dequant_t on the 65B gate weight (22016 x 8192:
+    0.516 B/weight read, 360 MB of bf16 written, beyond the 256 MB last-level
+    cache), as HBM bandwidth."""
+    import torch
+    from bit_quantized_finetuning_nf4_amd import ops, synth
+    N, K = 22016, 8192
+    W = synth.normal_bf16((N, K), 0.02, 77, dev, outliers=0.001)
+    q = ops.quantize(W)
+    out = torch.empty_like(W)
+    outT = torch.empty(K, N, dtype=torch.bfloat16, device=dev)
+    del W
+    nbytes = N * K * 2 + q.nbytes()
+    res = {"weight": f"{N}x{K}", "bytes_per_call": nbytes}
+    for name, fn in (("dequant", lambda: ops.dequant(q, out=out)), ("dequant_t", lambda: ops.dequant_t(q, out=outT))):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / reps
+        res[name] = {"ms": ms, "gbps": nbytes / (ms * 1e-3) / 1e9,
+                     "frac_of_hbm_peak": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS}
+    del q, out, outT
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -346,6 +585,8 @@ def main():
                     help="skip the side studies after the timed steps: the layer set quantized with FP4 and "
                          "Int4, the AdamW step over its LoRA values, and decode of 2-16 tokens (and of dense bf16 "
                          "weights) over the decode layers")
+    ap.add_argument("--no-other-sets", action="store_true",
+                    help="skip the 7B, 13B and small layer sets and the dequant leg")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after the timed steps, run one elementwise copy (negation) of this many MiB: "
                          "a kernel of known traffic for scaling the FETCH_SIZE / WRITE_SIZE counters")
@@ -368,86 +609,19 @@ def main():
         sys.exit(2)
 
     import torch
-    from bit_quantized_finetuning_nf4_amd import ops, synth
-    from bit_quantized_finetuning_nf4_amd import _lib
+    from bit_quantized_finetuning_nf4_amd import synth
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     cfg = synth.LAYER_SETS[args.workload]
     M, r, alpha = cfg["M"], cfg["r"], cfg["alpha"]
     set_index = {"llama7b": 1, "llama13b": 2, "llama65b": 3}[args.workload]
-    lins = cfg["linears"]
-    log(f"[bench] workload {args.workload}: {len(lins)} linears, M={M}, r={r}")
-
-    # ---- inputs and outputs, resident before timing ----
-    L = []
-    for i, (name, N, K) in enumerate(lins):
-        t = synth.linear_inputs(N, K, M, r, synth.layer_set_seed(set_index, i), dev, outliers=cfg["outliers"])
-        q = ops.QuantizedWeight.empty(N, K, dev)
-        o = dict(name=name, N=N, K=K, q=q, **t,
-                 x=t["X"][0].contiguous(),
-                 Y=torch.empty(M, N, dtype=torch.bfloat16, device=dev),
-                 U=torch.empty(M, r, dtype=torch.bfloat16, device=dev),
-                 G=torch.empty(M, r, dtype=torch.bfloat16, device=dev),
-                 dX=torch.empty(M, K, dtype=torch.bfloat16, device=dev),
-                 dA=torch.empty(r, K, dtype=torch.float32, device=dev),
-                 dB=torch.empty(N, r, dtype=torch.float32, device=dev))
-        L.append(o)
-    ws_bytes = max(ops.workspace_bytes(_lib.QLORA_OP_LORA, M, o["N"], o["K"], r) for o in L)
-    ws = ops.workspace(ws_bytes, dev)
-    plan = ops.GemvPlan([ops.GemvJob(o["q"], o["x"], o["A"], o["B"], alpha) for o in L])
-    torch.cuda.synchronize()
-
-    fl_step = sum(linear_flops(M, o["N"], o["K"], r) for o in L)
-    fl_fwd = [2 * M * o["N"] * o["K"] + 2 * M * o["N"] * r for o in L]   # fused forward GEMM
-    fl_dx = [2 * M * o["N"] * o["K"] + 2 * M * o["K"] * r for o in L]    # fused dX GEMM
-    q_bytes = sum(2 * o["N"] * o["K"] + o["q"].nbytes() for o in L)
-    g_bytes = sum(gemv_bytes(o["N"], o["K"], r) for o in L)
-
-    E = lambda: torch.cuda.Event(enable_timing=True)
-    record = []
-
-    def step(timed):
-        ev = dict(p=[E() for _ in range(5)], f=[(E(), E()) for _ in L], d=[(E(), E()) for _ in L]) if timed else None
-        if timed:
-            ev["p"][0].record()
-        for o in L:
-            ops.quantize(o["W"], out=o["q"])
-        if timed:
-            ev["p"][1].record()
-        for i, o in enumerate(L):
-            ops.lora_down(o["X"], o["A"], U=o["U"], ws=ws)
-            if timed:
-                ev["f"][i][0].record()
-            ops.nf4_fwd(o["q"], o["X"], o["U"], o["B"], alpha, out=o["Y"])
-            if timed:
-                ev["f"][i][1].record()
-        if timed:
-            ev["p"][2].record()
-        for i, o in enumerate(L):
-            ops.lora_dy_b(o["dY"], o["B"], G=o["G"], ws=ws)
-            if timed:
-                ev["d"][i][0].record()
-            ops.nf4_dx(o["q"], o["dY"], o["G"], o["A"], alpha, out=o["dX"])
-            if timed:
-                ev["d"][i][1].record()
-            ops.lora_grads(o["X"], o["dY"], o["U"], o["G"], alpha, dA=o["dA"], dB=o["dB"], ws=ws)
-        if timed:
-            ev["p"][3].record()
-        plan()
-        if timed:
-            ev["p"][4].record()
-            record.append(ev)
-
-    for _ in range(args.warmup):
-        step(False)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step(True)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_step = (t1 - t0) * 1e3 / args.steps
+    log(f"[bench] workload {args.workload}: {len(cfg['linears'])} linears, M={M}, r={r}")
+    S = LayerSet(args.workload, dev)
+    L = S.L
+    head = S.run("staged", args.steps, args.warmup)
+    ms_step = head["ms_per_step"]
+    log(f"[bench] staged step {ms_step:.3f} ms; phases {head['phases_ms']}; products {head['products']}")
 
     if args.copy_probe_mib > 0:
         n = args.copy_probe_mib * 1024 * 1024 // 4
@@ -458,63 +632,90 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    ph = {"quantize": 0.0, "forward": 0.0, "backward": 0.0, "decode_gemv": 0.0}
-    fwd_ms, dx_ms = 0.0, 0.0
-    for ev in record:
-        p = ev["p"]
-        ph["quantize"] += p[0].elapsed_time(p[1])
-        ph["forward"] += p[1].elapsed_time(p[2])
-        ph["backward"] += p[2].elapsed_time(p[3])
-        ph["decode_gemv"] += p[3].elapsed_time(p[4])
-        fwd_ms += sum(a.elapsed_time(b) for a, b in ev["f"])
-        dx_ms += sum(a.elapsed_time(b) for a, b in ev["d"])
-    K_ = args.steps
-    ph = {k: v / K_ for k, v in ph.items()}
-    fwd_ms /= K_
-    dx_ms /= K_
-    fwd_tf = sum(fl_fwd) / (fwd_ms * 1e-3) / 1e12
-    dx_tf = sum(fl_dx) / (dx_ms * 1e-3) / 1e12
-    kernels = {
-        "fwd_kernel": {"launches_per_step": len(L), "avg_launch_ms": fwd_ms / len(L), "tflops": fwd_tf,
-                       "flops_per_step": sum(fl_fwd)},
-        "dx_kernel": {"launches_per_step": len(L), "avg_launch_ms": dx_ms / len(L), "tflops": dx_tf,
-                      "flops_per_step": sum(fl_dx)},
-    }
-    dom = "dx_kernel" if dx_ms >= fwd_ms else "fwd_kernel"
-    k = kernels[dom]
-    traffic = traffic_for(dom)
-    roof = {"kernel": dom, "bound": "mfma", "achieved": k["tflops"], "peak": PEAK_BF16_TFLOPS,
-            "unit": "TFLOP/s", "frac": k["tflops"] / PEAK_BF16_TFLOPS,
-            "traffic": traffic,
-            "per_launch": "flops of the fused GEMM = 2MNK + 2Mr(N or K) for each of the 7 linears; "
-                          "achieved = their sum / the sum of the launches' HIP-event durations"}
-    value = fl_step / (ms_step * 1e-3) / 1e12
+    # the shader clock while the same steps run (a separate window, so the
+    # sampling subprocess stays out of the timed region above)
+    sampler = ClockSampler()
+    with sampler:
+        t_end = time.perf_counter() + 2.0
+        while time.perf_counter() < t_end:
+            for _ in range(10):
+                S.step("staged")
+            torch.cuda.synchronize()
+    clock = sampler.result()
+    log(f"[bench] clock {clock}")
+
+    fused = S.run("fused", args.steps, args.warmup)
+    log(f"[bench] fused step {fused['ms_per_step']:.3f} ms; fwd+bwd {fused['fwd_bwd_tflops']:.0f} TFLOP/s")
+
+    prod = head["products"]
+    traffic = traffic_for("dense_gemm")
+    roof = {"kernel": "dense_gemm (bf16_fwd_kernel, forward and dX launches)", "bound": "mfma",
+            "achieved": prod["tflops"], "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": prod["tflops"] / PEAK_BF16_TFLOPS, "traffic": traffic,
+            "per_launch": "flops of the dense GEMM = 2MNK + 2Mr(N) (forward) or 2MNK + 2Mr(K) (dX) for each of the "
+                          "7 linears; achieved = their sum / the sum of the 14 launches' HIP-event durations"}
+    if clock:
+        roof["clock_mhz_median"] = clock["median_mhz"]
+        roof["frac_at_measured_clock"] = prod["tflops"] / (PEAK_BF16_TFLOPS * clock["median_mhz"] / 2400.0)
+    value = S.fl_step / (ms_step * 1e-3) / 1e12
+    fb = head["fwd_bwd_tflops"]
     out = {
         "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": f"{args.workload} layer set: " + ", ".join(f"{o['name']} {o['N']}x{o['K']}" for o in L)
                    + f"; M={M} tokens; LoRA r={r} alpha={alpha}; NF4 blocksize 64, 8-bit double quant per 256 blocks"
-                   + "; step = quantize + fwd + bwd + batch-1 decode GEMV",
+                   + "; step = quantize + fwd + bwd (staged: W dequantized once per product, dense bf16 GEMM) "
+                     "+ batch-1 decode GEMV",
                    "global_batch": M, "seq_len": M, "parallelism": "none (1 GPU)"},
         "roofline": roof,
-        "phases_ms": ph,
-        "kernels": kernels,
-        "fwd_bwd_tflops": fl_step / ((ph["forward"] + ph["backward"]) * 1e-3) / 1e12,
-        "quantize_gbps": q_bytes / (ph["quantize"] * 1e-3) / 1e9,
-        "layer_gemv_gbps": g_bytes / (ph["decode_gemv"] * 1e-3) / 1e9,
+        "phases_ms": head["phases_ms"],
+        "products": prod,
+        "fwd_bwd_tflops": fb,
+        "targets": {"fwd_bwd_frac_of_bf16_peak": fb / PEAK_BF16_TFLOPS, "fwd_bwd_target_frac": 0.50,
+                    "fwd_bwd_shortfall_ms": max(0.0, (head["phases_ms"]["forward"] + head["phases_ms"]["backward"])
+                                                - S.fl_step / (0.5 * PEAK_BF16_TFLOPS * 1e12) * 1e3)},
+        "fused_path": {k: fused[k] for k in ("ms_per_step", "phases_ms", "fwd_bwd_tflops", "products")},
+        "clock": clock,
+        "quantize_gbps": S.q_bytes / (head["phases_ms"]["quantize"] * 1e-3) / 1e9,
+        "layer_gemv_gbps": S.g_bytes / (head["phases_ms"]["decode_gemv"] * 1e-3) / 1e9,
     }
-    log(f"[bench] step {ms_step:.3f} ms, {value:.1f} TFLOP/s; phases {ph}")
     if not args.no_codebook_study:
-        out["codebooks"] = codebook_study(L, dev, q_bytes)
+        out["codebooks"] = codebook_study(L, dev, S.q_bytes)
         log(f"[bench] codebooks {out['codebooks']}")
         out["optimizer"] = optimizer_study(L, r, dev)
         log(f"[bench] optimizer {out['optimizer']}")
+    del S, L
+    torch.cuda.empty_cache()
+
+    if not args.no_other_sets:
+        out["dequant"] = dequant_study(dev)
+        log(f"[bench] dequant {out['dequant']}")
+        sets = {}
+        for name in ("llama7b", "llama13b", "small"):
+            if name == args.workload:
+                continue
+            T = LayerSet(name, dev, with_decode=False)
+            paths = ("staged", "fused") if T.M >= 1024 else ("fused",)
+            res = {"M": T.M, "r": T.r, "linears": [f"{o['name']} {o['N']}x{o['K']}" for o in T.L],
+                   "flops_per_step": T.fl_step}
+            for pth in paths:
+                rr = T.run(pth, args.steps, args.warmup)
+                res[pth] = {"fwd_bwd_tflops": rr["fwd_bwd_tflops"],
+                            "fwd_bwd_frac_of_bf16_peak": rr["fwd_bwd_tflops"] / PEAK_BF16_TFLOPS,
+                            "phases_ms": rr["phases_ms"], "products_tflops": rr["products"]["tflops"],
+                            "products_frac": rr["products"]["frac_of_bf16_peak"]}
+            res["path_taken_by_qlora_linear"] = "staged" if T.M >= 1024 else "fused"
+            sets[name] = res
+            log(f"[bench] {name}: " + ", ".join(f"{pth} {res[pth]['fwd_bwd_tflops']:.0f} TF/s" for pth in paths))
+            del T
+            torch.cuda.empty_cache()
+        out["layer_sets"] = sets
 
     # ---- 80-layer batch-1 decode pass (about 65e9 weights) ----
     if args.decode_layers > 0:
-        del L, plan
-        torch.cuda.empty_cache()
+        from bit_quantized_finetuning_nf4_amd import ops
+        E = lambda: torch.cuda.Event(enable_timing=True)
         c65 = synth.LAYER_SETS["llama65b"]
         jobs, nbytes = [], 0
         for layer in range(args.decode_layers):
@@ -546,7 +747,8 @@ def main():
         out["decode"] = {"workload": f"{args.decode_layers} layers x 7 LLaMA-65B-shaped linears, batch 1, "
                                      f"LoRA r={r} fused; {len(jobs)} jobs in one grouped call",
                          "bytes_per_pass": nbytes, "ms_per_pass": pass_ms, "gbps": gbps,
-                         "frac_of_hbm_peak": gbps / PEAK_HBM_GBPS}
+                         "frac_of_hbm_peak": gbps / PEAK_HBM_GBPS, "target_frac": 0.70,
+                         "target_shortfall_ms": max(0.0, pass_ms - nbytes / (0.7 * PEAK_HBM_GBPS * 1e9) * 1e3)}
         log(f"[bench] decode pass {pass_ms:.3f} ms, {gbps:.0f} GB/s")
         del dplan
         if not args.no_codebook_study:

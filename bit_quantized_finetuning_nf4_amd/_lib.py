@@ -12,6 +12,7 @@ LIB_PATH = os.path.join(_HERE, "libqlora.so")
 
 QLORA_OK = 0
 QLORA_OP_FWD, QLORA_OP_BWD, QLORA_OP_GEMV, QLORA_OP_LORA = 0, 1, 2, 3
+QLORA_OP_FWD_FUSED, QLORA_OP_BWD_FUSED = 4, 5
 
 STATUS_NAMES = {
     0: "QLORA_OK", 1: "QLORA_E_NULL", 2: "QLORA_E_ALIGN", 3: "QLORA_E_SHAPE",
@@ -25,7 +26,7 @@ EXPORTS = [
     "qlora_codebook_levels", "qlora_adamw",
     "qlora_linear_fwd", "qlora_linear_bwd", "qlora_gemv", "qlora_gemv_prepare", "qlora_gemv_run",
     "qlora_lora_down", "qlora_lora_dy_b", "qlora_lora_grads", "qlora_nf4_fwd", "qlora_nf4_dx",
-    "qlora_linear_fwd_noalloc",
+    "qlora_linear_fwd_noalloc", "qlora_bf16_fwd", "qlora_dequant_t", "qlora_bf16_dx",
 ]
 
 # QLORA_STATIC_SCRATCH_BYTES: scratch array of qlora_linear_fwd_noalloc per device
@@ -106,6 +107,8 @@ def lib():
     L.qlora_quantize.argtypes = [vp, W, vp]
     L.qlora_dequant.restype = ctypes.c_int
     L.qlora_dequant.argtypes = [W, vp, vp]
+    L.qlora_dequant_t.restype = ctypes.c_int
+    L.qlora_dequant_t.argtypes = [W, vp, vp]
     L.qlora_codebook_levels.restype = ctypes.c_int
     L.qlora_codebook_levels.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_float)]
     L.qlora_adamw.restype = ctypes.c_int
@@ -130,6 +133,10 @@ def lib():
     L.qlora_lora_grads.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, f32, vp, vp, vp, sz, vp]
     L.qlora_nf4_fwd.restype = ctypes.c_int
     L.qlora_nf4_fwd.argtypes = [W, vp, i64, vp, vp, i32, f32, vp, vp]
+    L.qlora_bf16_fwd.restype = ctypes.c_int
+    L.qlora_bf16_fwd.argtypes = [vp, i64, i64, vp, i64, vp, vp, i32, f32, vp, vp]
+    L.qlora_bf16_dx.restype = ctypes.c_int
+    L.qlora_bf16_dx.argtypes = [vp, i64, i64, vp, i64, vp, vp, i32, f32, vp, vp]
     L.qlora_nf4_dx.restype = ctypes.c_int
     L.qlora_nf4_dx.argtypes = [W, vp, i64, vp, vp, i32, f32, vp, vp]
     _lib = L

@@ -5,8 +5,15 @@
 // from the caller's workspace, carved as follows (each piece 256-byte
 // aligned):
 //   FWD  (r > 0): U bf16 [M x r] | split partials of X A^T (fp32)
+//        staged : ... | deq(W) bf16 [N x K]
 //   BWD  (r > 0): G bf16 [M x r] | U bf16 [M x r] | split partials (fp32,
 //                 the largest of X A^T, dY B, G^T X, dY^T U)
+//        staged : ... | deq(W)^T bf16 [K x N]
+// A staged call dequantizes W once into the workspace and multiplies with
+// the dense bf16 kernel; otherwise the fused kernels decode W inside each
+// 256-token tile.  Staging pays off once a weight would be decoded several
+// times, so it is taken from kStagedMinTokens tokens on, when the workspace
+// holds the bf16 weight.
 //   GEMV        : per job, 128 fp32 for u = A x | the device job table
 // qlora_linear_fwd_noalloc carves the FWD layout out of `scratch` below
 // instead of a caller workspace.
@@ -98,32 +105,52 @@ Nf4View view(const qlora_nf4_weight* q) {
   return Nf4View{q->codes, q->absmax_q, q->group_scale, q->rows, q->cols, q->codebook};
 }
 
+constexpr int64_t kStagedMinTokens = 1024;
+
+// The staged path's bf16 weight is addressed with 32-bit byte offsets, and
+// the transposing dequant grid has ceil(N / 64) rows.  The dense kernel runs
+// its contraction in whole pairs of 32-wide stages: K % 64 == 0 holds on
+// every GEMM path; dX contracts over N, so its staged form needs N % 64 == 0.
+bool staged_ok(int64_t M, int64_t N, int64_t K) {
+  return M >= kStagedMinTokens && N <= (int64_t)0x7FFFFFFF / K && (N + 63) / 64 <= 65535;
+}
+bool staged_bwd_ok(int64_t M, int64_t N, int64_t K) { return staged_ok(M, N, K) && N % 64 == 0; }
+
 struct FwdLayout {
-  size_t u, part, total;
+  size_t u, part, wd, total;
 };
-FwdLayout fwd_layout(int64_t M, int64_t N, int64_t K, int32_t r) {
-  FwdLayout L{0, 0, 0};
-  if (r == 0) return L;
-  L.u = 0;
-  L.part = align_up((size_t)M * r * 2);
-  L.total = L.part + align_up(skinny_partial_bytes(M, r, K, kXAt));
-  (void)N;
+FwdLayout fwd_layout(int64_t M, int64_t N, int64_t K, int32_t r, bool staged) {
+  FwdLayout L{0, 0, 0, 0};
+  if (r > 0) {
+    L.u = 0;
+    L.part = align_up((size_t)M * r * 2);
+    L.total = L.part + align_up(skinny_partial_bytes(M, r, K, kXAt));
+  }
+  if (staged) {
+    L.wd = L.total;
+    L.total += align_up((size_t)N * (size_t)K * 2);
+  }
   return L;
 }
 
 size_t lora_part_bytes(int64_t M, int64_t N, int64_t K, int32_t r);
 
 struct BwdLayout {
-  size_t g, u, part, total;
+  size_t g, u, part, wdt, total;
 };
-BwdLayout bwd_layout(int64_t M, int64_t N, int64_t K, int32_t r) {
-  BwdLayout L{0, 0, 0, 0};
-  if (r == 0) return L;
-  const size_t mr = align_up((size_t)M * r * 2);
-  L.g = 0;
-  L.u = mr;
-  L.part = 2 * mr;
-  L.total = L.part + lora_part_bytes(M, N, K, r);
+BwdLayout bwd_layout(int64_t M, int64_t N, int64_t K, int32_t r, bool staged) {
+  BwdLayout L{0, 0, 0, 0, 0};
+  if (r > 0) {
+    const size_t mr = align_up((size_t)M * r * 2);
+    L.g = 0;
+    L.u = mr;
+    L.part = 2 * mr;
+    L.total = L.part + lora_part_bytes(M, N, K, r);
+  }
+  if (staged) {
+    L.wdt = L.total;
+    L.total += align_up((size_t)N * (size_t)K * 2);
+  }
   return L;
 }
 
@@ -196,8 +223,8 @@ qlora_status check_fwd(const qlora_nf4_weight* W, const uint16_t* X, int64_t M, 
 // The forward's launches, on a workspace of the FWD layout.
 qlora_status run_fwd(const qlora_nf4_weight* W, const uint16_t* X, int64_t M, const uint16_t* A,
                      const uint16_t* B, int32_t r, float alpha, uint16_t* Y, uint16_t* U_save, void* ws,
-                     hipStream_t s) {
-  const FwdLayout L = fwd_layout(M, W->rows, W->cols, r);
+                     bool staged, hipStream_t s) {
+  const FwdLayout L = fwd_layout(M, W->rows, W->cols, r, staged);
   const Nf4View v = view(W);
   const bf16_t* U = nullptr;
   float sc = 0.0f;
@@ -208,6 +235,13 @@ qlora_status run_fwd(const qlora_nf4_weight* W, const uint16_t* X, int64_t M, co
     qlora_status st = hip_status(launch_xat(X, A, M, W->cols, r, part, Ud, nullptr, 1.0f, s));
     if (st != QLORA_OK) return st;
     U = Ud;
+  }
+  if (staged) {
+    bf16_t* Wd = reinterpret_cast<bf16_t*>(ws_at(ws, L.wd));
+    qlora_status st = hip_status(launch_dequant(W->codes, W->absmax_q, W->group_scale, W->rows * W->cols,
+                                                W->codebook, Wd, s));
+    if (st != QLORA_OK) return st;
+    return hip_status(launch_bf16_fwd(Wd, W->rows, W->cols, X, M, U, B, false, r, sc, Y, s));
   }
   return hip_status(launch_fwd(v, X, M, U, B, r, sc, Y, s));
 }
@@ -281,11 +315,13 @@ qlora_status qlora_sizes(int64_t rows, int64_t cols, int32_t blocksize, int32_t 
 size_t qlora_workspace_bytes(qlora_op op, int64_t M, int64_t N, int64_t K, int32_t r, int32_t njobs) {
   switch (op) {
     case QLORA_OP_FWD:
+    case QLORA_OP_FWD_FUSED:
       if (M <= 0 || N <= 0 || K <= 0 || r < 0 || r > kMaxRank) return 0;
-      return fwd_layout(M, N, K, r).total;
+      return fwd_layout(M, N, K, r, op == QLORA_OP_FWD && staged_ok(M, N, K)).total;
     case QLORA_OP_BWD:
+    case QLORA_OP_BWD_FUSED:
       if (M <= 0 || N <= 0 || K <= 0 || r < 0 || r > kMaxRank) return 0;
-      return bwd_layout(M, N, K, r).total;
+      return bwd_layout(M, N, K, r, op == QLORA_OP_BWD && staged_bwd_ok(M, N, K)).total;
     case QLORA_OP_GEMV:
       if (njobs <= 0 || njobs > kMaxJobs || N <= 0 || M < 0 || M > kMaxGemvTokens) return 0;
       return gemv_u_bytes(njobs, M) + gemv_table_bound(njobs, N);
@@ -329,9 +365,20 @@ qlora_status qlora_dequant(const qlora_nf4_weight* q, uint16_t* W_out, void* str
   if (!aligned16(W_out)) return QLORA_E_ALIGN;
   if (q->rows > INT64_MAX / q->cols) return QLORA_E_SHAPE;
   const int64_t n = q->rows * q->cols;
-  if ((n + 63) / 64 / 256 > 0x7FFFFFFF) return QLORA_E_SHAPE;
+  if ((n + 63) / 64 / 64 > 0x7FFFFFFF) return QLORA_E_SHAPE;   // the launch's workgroup count
   return hip_status(
       launch_dequant(q->codes, q->absmax_q, q->group_scale, n, q->codebook, W_out, (hipStream_t)stream));
+}
+
+qlora_status qlora_dequant_t(const qlora_nf4_weight* q, uint16_t* Wt_out, void* stream) {
+  qlora_status st = check_weight(q);
+  if (st != QLORA_OK) return st;
+  if (!Wt_out) return QLORA_E_NULL;
+  if (!aligned16(Wt_out)) return QLORA_E_ALIGN;
+  if (q->cols % 64 != 0 || q->rows % 8 != 0) return QLORA_E_UNSUPPORTED;
+  if (q->cols / 64 > 0x7FFFFFFF || (q->rows + 63) / 64 > 65535) return QLORA_E_UNSUPPORTED;
+  return hip_status(launch_dequant_t(q->codes, q->absmax_q, q->group_scale, q->rows, q->cols, q->codebook, Wt_out,
+                                     (hipStream_t)stream));
 }
 
 qlora_status qlora_linear_fwd(const qlora_nf4_weight* W, const uint16_t* X, int64_t M, const uint16_t* A,
@@ -339,11 +386,13 @@ qlora_status qlora_linear_fwd(const qlora_nf4_weight* W, const uint16_t* X, int6
                               void* ws, size_t ws_bytes, void* stream) {
   qlora_status st = check_fwd(W, X, M, A, B, r, Y, U_save);
   if (st != QLORA_OK) return st;
-  const FwdLayout L = fwd_layout(M, W->rows, W->cols, r);
+  const bool staged = staged_ok(M, W->rows, W->cols) &&
+                      ws_bytes >= fwd_layout(M, W->rows, W->cols, r, true).total;
+  const FwdLayout L = fwd_layout(M, W->rows, W->cols, r, staged);
   if (ws_bytes < L.total) return QLORA_E_WORKSPACE;
   if (L.total > 0 && !ws) return QLORA_E_NULL;
   if (L.total > 0 && !aligned16(ws)) return QLORA_E_ALIGN;
-  return run_fwd(W, X, M, A, B, r, alpha, Y, U_save, ws, (hipStream_t)stream);
+  return run_fwd(W, X, M, A, B, r, alpha, Y, U_save, ws, staged, (hipStream_t)stream);
 }
 
 qlora_status qlora_linear_fwd_noalloc(const qlora_nf4_weight* W, const uint16_t* X, int64_t M, const uint16_t* A,
@@ -351,11 +400,11 @@ qlora_status qlora_linear_fwd_noalloc(const qlora_nf4_weight* W, const uint16_t*
                                       void* stream) {
   qlora_status st = check_fwd(W, X, M, A, B, r, Y, U_save);
   if (st != QLORA_OK) return st;
-  const FwdLayout L = fwd_layout(M, W->rows, W->cols, r);
+  const FwdLayout L = fwd_layout(M, W->rows, W->cols, r, false);   // the fused path: no bf16 weight
   if (L.total > QLORA_STATIC_SCRATCH_BYTES) return QLORA_E_WORKSPACE;
   void* ws = nullptr;
   if (L.total > 0 && (st = static_scratch(&ws)) != QLORA_OK) return st;
-  return run_fwd(W, X, M, A, B, r, alpha, Y, U_save, ws, (hipStream_t)stream);
+  return run_fwd(W, X, M, A, B, r, alpha, Y, U_save, ws, false, (hipStream_t)stream);
 }
 
 qlora_status qlora_linear_bwd(const qlora_nf4_weight* W, const uint16_t* X, const uint16_t* dY, int64_t M,
@@ -375,16 +424,26 @@ qlora_status qlora_linear_bwd(const qlora_nf4_weight* W, const uint16_t* X, cons
   } else {
     if (dA || dB) return QLORA_E_SHAPE;  // no adapter, no adapter gradients
   }
-  const BwdLayout L = bwd_layout(M, W->rows, W->cols, r);
+  const bool staged = dX && staged_bwd_ok(M, W->rows, W->cols) &&
+                      ws_bytes >= bwd_layout(M, W->rows, W->cols, r, true).total;
+  const BwdLayout L = bwd_layout(M, W->rows, W->cols, r, staged);
   if (ws_bytes < L.total) return QLORA_E_WORKSPACE;
   if (L.total > 0 && !ws) return QLORA_E_NULL;
   if (L.total > 0 && !aligned16(ws)) return QLORA_E_ALIGN;
   hipStream_t s = (hipStream_t)stream;
   const Nf4View v = view(W);
   const int64_t N = W->rows, K = W->cols;
+  // dX = dY deq(W) + s G A: the dense kernel on deq(W)^T, or the fused one
+  auto run_dx = [&](const bf16_t* G, float sc) -> qlora_status {
+    if (!staged) return hip_status(launch_dx(v, dY, M, G, r > 0 ? A : nullptr, r, sc, dX, s));
+    bf16_t* WdT = reinterpret_cast<bf16_t*>(ws_at(ws, L.wdt));
+    qlora_status st2 = hip_status(launch_dequant_t(W->codes, W->absmax_q, W->group_scale, N, K, W->codebook, WdT, s));
+    if (st2 != QLORA_OK) return st2;
+    return hip_status(launch_bf16_fwd(WdT, K, N, dY, M, G, r > 0 ? A : nullptr, true, r, sc, dX, s));
+  };
   if (r == 0) {
     if (!dX) return QLORA_OK;
-    return hip_status(launch_dx(v, dY, M, nullptr, nullptr, 0, 0.0f, dX, s));
+    return run_dx(nullptr, 0.0f);
   }
   const float sc = (float)((double)alpha / (double)r);
   bf16_t* G = reinterpret_cast<bf16_t*>(ws_at(ws, L.g));
@@ -399,7 +458,7 @@ qlora_status qlora_linear_bwd(const qlora_nf4_weight* W, const uint16_t* X, cons
   st = hip_status(launch_dyb(dY, B, M, N, r, part, G, 1.0f, s));
   if (st != QLORA_OK) return st;
   if (dX) {
-    st = hip_status(launch_dx(v, dY, M, G, A, r, sc, dX, s));
+    st = run_dx(G, sc);
     if (st != QLORA_OK) return st;
   }
   st = hip_status(launch_gtx(G, X, M, K, r, part, dA, sc, s));
@@ -462,6 +521,40 @@ qlora_status qlora_nf4_fwd(const qlora_nf4_weight* W, const uint16_t* X, int64_t
   const float sc = r > 0 ? (float)((double)alpha / (double)r) : 0.0f;
   return hip_status(launch_fwd(view(W), X, M, r > 0 ? U : nullptr, r > 0 ? B : nullptr, r, sc, Y,
                                (hipStream_t)stream));
+}
+
+qlora_status qlora_bf16_fwd(const uint16_t* Wd, int64_t N, int64_t K, const uint16_t* X, int64_t M,
+                            const uint16_t* U, const uint16_t* B, int32_t r, float alpha, uint16_t* Y,
+                            void* stream) {
+  if (N <= 0 || K <= 0 || M <= 0) return QLORA_E_SHAPE;
+  if (K % 64 != 0 || N % 8 != 0) return QLORA_E_UNSUPPORTED;
+  // Wd, X and Y are addressed with 32-bit byte offsets
+  if (N > (int64_t)0x7FFFFFFF / K || M > (int64_t)0x7FFFFFFF / K || M > (int64_t)0x7FFFFFFF / N)
+    return QLORA_E_UNSUPPORTED;
+  if (!Wd || !X || !Y) return QLORA_E_NULL;
+  if (!aligned16(Wd) || !aligned16(X) || !aligned16(Y)) return QLORA_E_ALIGN;
+  qlora_status st = check_rank(r, U, B);
+  if (st != QLORA_OK) return st;
+  const float sc = r > 0 ? (float)((double)alpha / (double)r) : 0.0f;
+  return hip_status(launch_bf16_fwd(Wd, N, K, X, M, r > 0 ? U : nullptr, r > 0 ? B : nullptr, false, r, sc, Y,
+                                    (hipStream_t)stream));
+}
+
+qlora_status qlora_bf16_dx(const uint16_t* WdT, int64_t N, int64_t K, const uint16_t* dY, int64_t M,
+                           const uint16_t* G, const uint16_t* A, int32_t r, float alpha, uint16_t* dX,
+                           void* stream) {
+  if (N <= 0 || K <= 0 || M <= 0) return QLORA_E_SHAPE;
+  if (K % 64 != 0 || N % 64 != 0) return QLORA_E_UNSUPPORTED;
+  if (N > (int64_t)0x7FFFFFFF / K || M > (int64_t)0x7FFFFFFF / K || M > (int64_t)0x7FFFFFFF / N)
+    return QLORA_E_UNSUPPORTED;
+  if (!WdT || !dY || !dX) return QLORA_E_NULL;
+  if (!aligned16(WdT) || !aligned16(dY) || !aligned16(dX)) return QLORA_E_ALIGN;
+  qlora_status st = check_rank(r, G, A);
+  if (st != QLORA_OK) return st;
+  const float sc = r > 0 ? (float)((double)alpha / (double)r) : 0.0f;
+  // dX [M x K] = dY [M x N] (WdT [K x N])^T + s G (A^T)^T
+  return hip_status(launch_bf16_fwd(WdT, K, N, dY, M, r > 0 ? G : nullptr, r > 0 ? A : nullptr, true, r, sc, dX,
+                                    (hipStream_t)stream));
 }
 
 qlora_status qlora_nf4_dx(const qlora_nf4_weight* W, const uint16_t* dY, int64_t M, const uint16_t* G,

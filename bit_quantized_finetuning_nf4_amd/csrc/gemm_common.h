@@ -1,0 +1,118 @@
+// gemm_common.h -- tile geometry, tile order, output store and LoRA-tail
+// staging shared by the fused NF4 GEMMs and the dense bf16 GEMMs (gfx950).
+//
+// 256 threads (4 waves), 256 x 256 output tiles, stages of 32 along the
+// contraction; operand tiles in LDS are rows of 32 bf16 (64 bytes) with
+// 16-byte chunk c of row r at c ^ ((r >> 2) & 3) (spos, lds.h).
+#pragma once
+#include "device.h"
+#include "kernels.h"
+#include "lds.h"
+
+namespace qlora {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kTile = 256;
+constexpr int kStages = 4;                       // ring depth
+constexpr int kOp = kTile * 64;                  // 16 KiB: 256 rows x 32 bf16
+constexpr int kStage = 2 * kOp;                  // weight half at 0, token half at kOp
+
+// Fragment read offsets in a 64-byte-row tile for the two k16 halves of a
+// stage: lane (lr, h) reads chunk 2 kk + h of row lr.
+struct FragOffs {
+  int o0, o1;
+};
+__device__ __forceinline__ FragOffs frag_offs(int lane) {
+  const int lr = lane & 31, h = lane >> 5;
+  return FragOffs{spos(lr, h), spos(lr, 2 + h)};
+}
+
+__device__ __forceinline__ void zero_acc(f32x16_t (&acc)[4][4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+}
+
+template <int FI, int FJ>
+__device__ __forceinline__ void mfma_block(f32x16_t (&acc)[FI][FJ], const bf16x8_t (&a)[FI], const bf16x8_t (&b)[FJ]) {
+#pragma unroll
+  for (int i = 0; i < FI; ++i)
+#pragma unroll
+    for (int j = 0; j < FJ; ++j) acc[i][j] = mfma32x32x16(a[i], b[j], acc[i][j]);
+}
+
+// Tile order: consecutive workgroups share the token tile (the column-side
+// tiles vary fastest); the eight XCDs receive contiguous ranges.
+__device__ __forceinline__ void map_tile(int tiles_c, int tiles_r, int& tc, int& tr) {
+  (void)tiles_r;
+  const int nwg = (int)gridDim.x;   // the launch may cover only the first tiles of the grid
+  int id = blockIdx.x;
+  if ((nwg & 7) == 0) id = (id & 7) * (nwg >> 3) + (id >> 3);
+  tc = id % tiles_c;
+  tr = id / tiles_c;
+}
+
+// Output: lane (lr, h) of wave (wr, wc) holds token row0 + 128 wr + 32 j + lr
+// and columns col0 + 32 FI wc + 32 i + 8 q + 4 h + 0..3.
+template <int FI>
+__device__ __forceinline__ void store_tile(const f32x16_t (&acc)[FI][4], bf16_t* out, int64_t ld, int64_t rows,
+                                           int64_t cols, int64_t row0, int64_t col0) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wr = w >> 1, wc = w & 1, lr = lane & 31, h = lane >> 5;
+#pragma unroll
+  for (int i = 0; i < FI; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t row = row0 + wr * 128 + 32 * j + lr;
+      if (row >= rows) continue;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t col = col0 + wc * 32 * FI + 32 * i + 8 * q + 4 * h;
+        if (col < cols)  // cols % 8 == 0: the four columns are all in range
+          *reinterpret_cast<uint2*>(out + row * ld + col) =
+              make_uint2(pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
+                         pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]));
+      }
+    }
+}
+
+// 16 bytes of a bf16 row scaled by s (fp32 product rounded to bf16).
+__device__ __forceinline__ uint4 scale16(uint4 v, float s) {
+  v.x = pack_bf16x2(bf2f(v.x & 0xFFFFu) * s, bf2f(v.x >> 16) * s);
+  v.y = pack_bf16x2(bf2f(v.y & 0xFFFFu) * s, bf2f(v.y >> 16) * s);
+  v.z = pack_bf16x2(bf2f(v.z & 0xFFFFu) * s, bf2f(v.z >> 16) * s);
+  v.w = pack_bf16x2(bf2f(v.w & 0xFFFFu) * s, bf2f(v.w >> 16) * s);
+  return v;
+}
+
+// Token half of the LoRA tail: (s T)[row0 + row, j0 + 8 c ..] into a
+// 64-byte-row tile (T is rows x rank, zero past the rank and the last row).
+__device__ __forceinline__ void tail_tokens(char* dst, const bf16_t* T, int64_t rows, int r, int64_t row0, int j0,
+                                            float s) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int idx = threadIdx.x + kThreads * e;
+    const int row = idx >> 2, c = idx & 3, col = j0 + 8 * c;
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (col < r && row0 + row < rows) v = scale16(*reinterpret_cast<const uint4*>(T + (row0 + row) * r + col), s);
+    wr16(dst + spos(row, c), v);
+  }
+}
+
+// DMA pattern for a 256-row x 64-byte tile: wave w, instruction q covers
+// rows 64 q + 16 w .. +15 (1 KiB, lane-linear); lane j -> row + (j >> 2),
+// position j & 3, which holds chunk (j & 3) ^ ((j >> 4) & 3).
+__device__ __forceinline__ int dma_row(int q, int w, int j) { return 64 * q + 16 * w + (j >> 2); }
+__device__ __forceinline__ int dma_chunk(int j) { return (j & 3) ^ ((j >> 4) & 3); }
+
+// Operand fragments of a 128 x 128 wave sub-tile: A (column side) and B
+// (token side), k16 steps 0 and 1.
+struct Frags {
+  bf16x8_t a0[4], b0[4], a1[4], b1[4];
+};
+
+}  // namespace
+}  // namespace qlora

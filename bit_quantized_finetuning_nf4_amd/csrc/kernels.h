@@ -30,6 +30,10 @@ hipError_t launch_quantize(const bf16_t* W, int64_t numel, uint8_t* codes, uint8
 hipError_t launch_dequant(const uint8_t* codes, const uint8_t* absmax_q, const float* group_scale,
                           int64_t numel, int codebook, bf16_t* out, hipStream_t s);
 
+// WdT [K x N] = deq(W)^T (bf16) for W [N x K], K % 64 == 0, N < 65536 * 64.
+hipError_t launch_dequant_t(const uint8_t* codes, const uint8_t* absmax_q, const float* group_scale, int64_t N,
+                            int64_t K, int codebook, bf16_t* out, hipStream_t s);
+
 // Y = X deq(W)^T + s * U * B^T  (U already holds X A^T in bf16; r may be 0)
 hipError_t launch_fwd(const Nf4View& W, const bf16_t* X, int64_t M, const bf16_t* U, const bf16_t* B,
                       int r, float s, bf16_t* Y, hipStream_t st);
@@ -37,6 +41,13 @@ hipError_t launch_fwd(const Nf4View& W, const bf16_t* X, int64_t M, const bf16_t
 // dX = dY deq(W) + s * G * A  (G = dY B in bf16; r may be 0)
 hipError_t launch_dx(const Nf4View& W, const bf16_t* dY, int64_t M, const bf16_t* G, const bf16_t* A,
                      int r, float s, bf16_t* dX, hipStream_t st);
+
+// Dense bf16 product on a weight already in bf16, Wd [N x K]:
+// Y [M x N] = X Wd^T + s * U * B'^T (r may be 0), where B' [N x r] is B, or,
+// with b_trans, the transpose of B [r x N].  The backward runs it on the
+// transposed weight: dX = dY (W^T)^T + s G (A^T)^T.
+hipError_t launch_bf16_fwd(const bf16_t* Wd, int64_t N, int64_t K, const bf16_t* X, int64_t M, const bf16_t* U,
+                           const bf16_t* B, bool b_trans, int r, float s, bf16_t* Y, hipStream_t st);
 
 // Skinny products with a deterministic split-contraction reduction.
 // out_bf16 / out_f32 (either may be null) receive scale * result.

@@ -183,31 +183,32 @@ __global__ __launch_bounds__(256) void quantize_kernel(const bf16_t* __restrict_
   if (tid == 0) group_scale[g] = s2;
 }
 
-// One lane per block of 64 weights: 32 bytes of codes -> 128 bytes of bf16.
+// Four lanes per block of 64 weights: lane p of the four takes weights
+// 16 p .. 16 p + 15 (8 code bytes -> 32 bytes of bf16), so a wave reads 512
+// contiguous code bytes and writes 2 KiB of contiguous bf16.  Each lane builds
+// its block's table (the block scale and the 16 products with the levels).
 template <int CB>
 __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict__ codes,
                                                       const uint8_t* __restrict__ absmax_q,
                                                       const float* __restrict__ group_scale,
                                                       int64_t numel, int64_t nb,
                                                       bf16_t* __restrict__ out) {
-  const int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t b = g >> 2;
   if (b >= nb) return;
   const float t = block_scale(absmax_q[b], group_scale[b / kGroupBlocks]);
   const Nf4Table T = make_table<CB>(t);
-  const int64_t e0 = b * kBlock;
-  if (e0 + kBlock <= numel) {
-    const uint4* src = reinterpret_cast<const uint4*>(codes + (e0 >> 1));
-    const uint4 c0 = src[0], c1 = src[1];
-    const uint32_t cw[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+  const int64_t e0 = (g << 4);   // first of the lane's 16 weights
+  if (e0 + 16 <= numel) {
+    const uint2 c = *reinterpret_cast<const uint2*>(codes + (e0 >> 1));
+    uint32_t o[8];
+    dequant8(c.x, T, o);
+    dequant8(c.y, T, o + 4);
     uint4* dst = reinterpret_cast<uint4*>(out + e0);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      uint32_t o[4];
-      dequant8(cw[i], T, o);
-      dst[i] = make_uint4(o[0], o[1], o[2], o[3]);
-    }
-  } else {
-    // ragged last block
+    dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
+    dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
+  } else if (e0 < numel) {
+    // ragged end of the last block
     const int64_t n = numel - e0;
     for (int64_t i = 0; i < n; i += 8) {
       uint32_t cw = 0;
@@ -218,6 +219,57 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict_
       for (int j = 0; j < 8 && i + j < n; ++j)
         out[e0 + i + j] = (bf16_t)(o[j >> 1] >> (16 * (j & 1)));
     }
+  }
+}
+
+// Transposed dequantization, WdT [K x N] = deq(W)^T for W [N x K] with
+// K % 64 == 0 (the dense backward multiplies by it).  A workgroup takes a
+// 64-row x 64-column tile of W, which is one block per row: thread t decodes
+// rows 2 (t >> 3) and 2 (t >> 3) + 1, columns 8 (t & 7) .. +7, packs each
+// column's two rows into one dword and stores it to LDS at [column][row
+// pair] (rows of 33 dwords, so that the eight column groups of a wave fall in
+// distinct banks); then thread t writes 32 contiguous bytes (16 rows of W) of
+// WdT row k0 + (t >> 2).  Rows past N decode as zero and are not written.
+constexpr int kTrStride = 33;
+template <int CB>
+__global__ __launch_bounds__(256) void dequant_t_kernel(const uint8_t* __restrict__ codes,
+                                                        const uint8_t* __restrict__ absmax_q,
+                                                        const float* __restrict__ group_scale, int64_t N,
+                                                        int64_t K, bf16_t* __restrict__ out) {
+  __shared__ uint32_t tile[64 * kTrStride];
+  const int t = threadIdx.x, rp = t >> 3, cg = t & 7;
+  const int64_t n0 = (int64_t)blockIdx.y * 64, k0 = (int64_t)blockIdx.x * 64;
+  uint32_t c[2];
+  Nf4Table T[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int64_t row = n0 + 2 * rp + i;
+    if (row < N) {
+      const int64_t b = (row * K + k0) >> 6;
+      T[i] = make_table<CB>(block_scale(absmax_q[b], group_scale[b / kGroupBlocks]));
+      c[i] = *reinterpret_cast<const uint32_t*>(codes + ((row * K + k0 + 8 * cg) >> 1));
+    } else {
+      T[i] = make_table<CB>(0.0f);
+      c[i] = 0u;
+    }
+  }
+  uint32_t o[8];
+  dequant8x2_pairs(c[0], c[1], T[0], T[1], o);
+#pragma unroll
+  for (int k = 0; k < 8; ++k) tile[(8 * cg + k) * kTrStride + rp] = o[k];
+  __syncthreads();
+  const int kk = t >> 2, q = t & 3;
+  uint32_t v[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = tile[kk * kTrStride + 8 * q + e];
+  const int64_t ncol = n0 + 16 * q;
+  bf16_t* dst = out + (k0 + kk) * N + ncol;
+  if (ncol + 16 <= N) {
+    uint4* d4 = reinterpret_cast<uint4*>(dst);
+    d4[0] = make_uint4(v[0], v[1], v[2], v[3]);
+    d4[1] = make_uint4(v[4], v[5], v[6], v[7]);
+  } else {
+    for (int e = 0; e < 16 && ncol + e < N; ++e) dst[e] = (bf16_t)(v[e >> 1] >> (16 * (e & 1)));
   }
 }
 
@@ -243,8 +295,17 @@ hipError_t launch_dequant(const uint8_t* codes, const uint8_t* absmax_q, const f
   const int64_t nb = (numel + kBlock - 1) / kBlock;
   auto* fn = codebook == kCbFp4 ? &dequant_kernel<kCbFp4> : codebook == kCbInt4 ? &dequant_kernel<kCbInt4>
                                                                                 : &dequant_kernel<kCbNf4>;
-  hipLaunchKernelGGL(fn, dim3((unsigned)((nb + 255) / 256)), dim3(256), 0, s, codes, absmax_q, group_scale, numel,
+  hipLaunchKernelGGL(fn, dim3((unsigned)((4 * nb + 255) / 256)), dim3(256), 0, s, codes, absmax_q, group_scale, numel,
                      nb, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_dequant_t(const uint8_t* codes, const uint8_t* absmax_q, const float* group_scale, int64_t N,
+                            int64_t K, int codebook, bf16_t* out, hipStream_t s) {
+  auto* fn = codebook == kCbFp4 ? &dequant_t_kernel<kCbFp4> : codebook == kCbInt4 ? &dequant_t_kernel<kCbInt4>
+                                                                                  : &dequant_t_kernel<kCbNf4>;
+  hipLaunchKernelGGL(fn, dim3((unsigned)(K / 64), (unsigned)((N + 63) / 64)), dim3(256), 0, s, codes, absmax_q,
+                     group_scale, N, K, out);
   return hipGetLastError();
 }
 

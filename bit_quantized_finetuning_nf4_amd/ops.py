@@ -135,9 +135,32 @@ def dequant(q: QuantizedWeight, out: Optional[torch.Tensor] = None) -> torch.Ten
     return out
 
 
+def dequant_t(q: QuantizedWeight, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """4-bit weight -> its transpose in bf16, [cols x rows]."""
+    if out is None:
+        out = torch.empty(q.cols, q.rows, dtype=torch.bfloat16, device=q.codes.device)
+    _need(out, torch.bfloat16, "out", (q.cols, q.rows))
+    d = q.desc()
+    check(lib().qlora_dequant_t(ctypes.byref(d), _ptr(out), _stream()), "qlora_dequant_t")
+    return out
+
+
+PATHS = ("auto", "fused")
+
+
+def _op(path, staged_op, fused_op):
+    if path not in PATHS:
+        raise ValueError(f"path must be one of {PATHS}, got {path!r}")
+    return staged_op if path == "auto" else fused_op
+
+
 def linear_fwd(q: QuantizedWeight, X: torch.Tensor, A=None, B=None, alpha: float = 0.0,
-               save_u: bool = False, out=None, u_out=None, ws=None):
-    """Y = X deq(W)^T + (alpha/r) (X A^T) B^T.  Returns Y, or (Y, U) with save_u."""
+               save_u: bool = False, out=None, u_out=None, ws=None, path: str = "auto"):
+    """Y = X deq(W)^T + (alpha/r) (X A^T) B^T.  Returns Y, or (Y, U) with save_u.
+
+    path "auto" sizes the workspace for the staged path (the library takes it
+    from 1024 tokens on: W dequantized once, then the dense bf16 product);
+    "fused" sizes it for the fused path only (W decoded inside the product)."""
     _need(X, torch.bfloat16, "X")
     M = X.shape[0]
     r = 0 if A is None else A.shape[0]
@@ -148,9 +171,11 @@ def linear_fwd(q: QuantizedWeight, X: torch.Tensor, A=None, B=None, alpha: float
     U = None
     if save_u and r:
         U = u_out if u_out is not None else torch.empty(M, r, dtype=torch.bfloat16, device=X.device)
-    nbytes = workspace_bytes(_lib.QLORA_OP_FWD, M, q.rows, q.cols, r)
+    nbytes = workspace_bytes(_op(path, _lib.QLORA_OP_FWD, _lib.QLORA_OP_FWD_FUSED), M, q.rows, q.cols, r)
     if ws is None:
         ws = workspace(nbytes, X.device)
+    elif ws.numel() > nbytes:
+        ws = ws[:nbytes]
     d = q.desc()
     check(lib().qlora_linear_fwd(ctypes.byref(d), _ptr(X), M, _ptr(A), _ptr(B), r, float(alpha), _ptr(Y),
                                  _ptr(U), _ptr(ws), 0 if ws is None else ws.numel(), _stream()),
@@ -182,8 +207,10 @@ def linear_fwd_noalloc(q: QuantizedWeight, X: torch.Tensor, A=None, B=None, alph
 
 
 def linear_bwd(q: QuantizedWeight, X: torch.Tensor, dY: torch.Tensor, A=None, B=None, alpha: float = 0.0,
-               U: Optional[torch.Tensor] = None, need_dx: bool = True, dX=None, dA=None, dB=None, ws=None):
-    """Returns (dX, dA, dB): dX bf16 [M x K] (or None), dA [r x K] and dB [N x r] fp32 (or None)."""
+               U: Optional[torch.Tensor] = None, need_dx: bool = True, dX=None, dA=None, dB=None, ws=None,
+               path: str = "auto"):
+    """Returns (dX, dA, dB): dX bf16 [M x K] (or None), dA [r x K] and dB [N x r] fp32 (or None).
+    path as in linear_fwd."""
     _need(dY, torch.bfloat16, "dY")
     M = dY.shape[0]
     r = 0 if A is None else A.shape[0]
@@ -199,9 +226,11 @@ def linear_bwd(q: QuantizedWeight, X: torch.Tensor, dY: torch.Tensor, A=None, B=
         dX = dX if dX is not None else torch.empty(M, q.cols, dtype=torch.bfloat16, device=dY.device)
     else:
         dX = None
-    nbytes = workspace_bytes(_lib.QLORA_OP_BWD, M, q.rows, q.cols, r)
+    nbytes = workspace_bytes(_op(path, _lib.QLORA_OP_BWD, _lib.QLORA_OP_BWD_FUSED), M, q.rows, q.cols, r)
     if ws is None:
         ws = workspace(nbytes, dY.device)
+    elif ws.numel() > nbytes:
+        ws = ws[:nbytes]
     d = q.desc()
     check(lib().qlora_linear_bwd(ctypes.byref(d), _ptr(X), _ptr(dY), M, _ptr(A), _ptr(B), r, float(alpha),
                                  _ptr(U), _ptr(dX), _ptr(dA), _ptr(dB), _ptr(ws),
@@ -346,6 +375,42 @@ def nf4_fwd(q: QuantizedWeight, X, U=None, B=None, alpha: float = 0.0, out=None)
     check(lib().qlora_nf4_fwd(ctypes.byref(d), _ptr(X), M, _ptr(U), _ptr(B), r, float(alpha), _ptr(Y),
                               _stream()), "qlora_nf4_fwd")
     return Y
+
+
+def bf16_fwd(Wd: torch.Tensor, X, U=None, B=None, alpha: float = 0.0, out=None):
+    """The dense forward GEMM on a dequantized weight Wd [N x K] (bf16):
+    Y = X Wd^T + s U B^T."""
+    _need(Wd, torch.bfloat16, "Wd")
+    _need(X, torch.bfloat16, "X")
+    N, K = Wd.shape
+    M = X.shape[0]
+    r = 0 if U is None else U.shape[1]
+    if r:
+        _need(U, torch.bfloat16, "U", (M, r))
+        _need(B, torch.bfloat16, "B", (N, r))
+    Y = out if out is not None else torch.empty(M, N, dtype=torch.bfloat16, device=X.device)
+    _need(Y, torch.bfloat16, "Y", (M, N))
+    check(lib().qlora_bf16_fwd(_ptr(Wd), N, K, _ptr(X), M, _ptr(U), _ptr(B), r, float(alpha), _ptr(Y), _stream()),
+          "qlora_bf16_fwd")
+    return Y
+
+
+def bf16_dx(WdT: torch.Tensor, dY, G=None, A=None, alpha: float = 0.0, out=None):
+    """The dense backward GEMM on the transposed bf16 weight WdT [K x N]:
+    dX = dY WdT^T + s G A."""
+    _need(WdT, torch.bfloat16, "WdT")
+    _need(dY, torch.bfloat16, "dY")
+    K, N = WdT.shape
+    M = dY.shape[0]
+    r = 0 if G is None else G.shape[1]
+    if r:
+        _need(G, torch.bfloat16, "G", (M, r))
+        _need(A, torch.bfloat16, "A", (r, K))
+    dX = out if out is not None else torch.empty(M, K, dtype=torch.bfloat16, device=dY.device)
+    _need(dX, torch.bfloat16, "dX", (M, K))
+    check(lib().qlora_bf16_dx(_ptr(WdT), N, K, _ptr(dY), M, _ptr(G), _ptr(A), r, float(alpha), _ptr(dX), _stream()),
+          "qlora_bf16_dx")
+    return dX
 
 
 def nf4_dx(q: QuantizedWeight, dY, G=None, A=None, alpha: float = 0.0, out=None):

@@ -75,10 +75,12 @@ typedef enum {
 } qlora_status;
 
 typedef enum {
-  QLORA_OP_FWD = 0,   /* qlora_linear_fwd                                   */
-  QLORA_OP_BWD = 1,   /* qlora_linear_bwd                                   */
+  QLORA_OP_FWD = 0,   /* qlora_linear_fwd (room for the staged path)        */
+  QLORA_OP_BWD = 1,   /* qlora_linear_bwd (room for the staged path)        */
   QLORA_OP_GEMV = 2,  /* qlora_gemv                                         */
-  QLORA_OP_LORA = 3   /* qlora_lora_down, qlora_lora_dy_b, qlora_lora_grads */
+  QLORA_OP_LORA = 3,  /* qlora_lora_down, qlora_lora_dy_b, qlora_lora_grads */
+  QLORA_OP_FWD_FUSED = 4,  /* qlora_linear_fwd, fused path only             */
+  QLORA_OP_BWD_FUSED = 5   /* qlora_linear_bwd, fused path only             */
 } qlora_op;
 
 /* A quantized weight: host struct holding device pointers.
@@ -162,6 +164,12 @@ qlora_status qlora_quantize(const uint16_t* W, const qlora_nf4_weight* q, void* 
  * Glossary "Definition": converted back to BFloat16 for the calculation. */
 qlora_status qlora_dequant(const qlora_nf4_weight* q, uint16_t* W_out, void* stream);
 
+/* Dequantize q into the transposed bf16 weight Wt_out [cols x rows]
+ * (overwritten): Wt_out[k][n] = deq(W)[n][k], bit-identical to
+ * qlora_dequant's values.  cols % 64 == 0, rows % 8 == 0, rows < 4194240
+ * (QLORA_E_UNSUPPORTED otherwise).  The staged backward multiplies dY by it. */
+qlora_status qlora_dequant_t(const qlora_nf4_weight* q, uint16_t* Wt_out, void* stream);
+
 /* One AdamW step on n trainable values (the LoRA matrices after a backward
  * pass; the pages' paged optimizers keep such states movable between GPU
  * and CPU memory: glossary "Definition", deepfa.ir "3. Paged Optimizers").
@@ -183,7 +191,19 @@ qlora_status qlora_adamw(float* p, uint16_t* p_bf16, const float* grad, float* m
  * codebook. */
 qlora_status qlora_codebook_levels(qlora_codebook cb, float out[16]);
 
-/* Forward: Y [M x N] = X deq(W)^T + s (X A^T) B^T, s = RN32(alpha / r).
+/* Two paths compute qlora_linear_fwd and qlora_linear_bwd; both give the
+ * defined result within the stated tolerances (they differ only in the
+ * order of fp32 accumulation):
+ *   - fused: the product kernels decode W to bf16 inside each 256-token
+ *     tile (deepfa.ir "QLoRA's Working Process": converted to BF16 on the
+ *     fly); workspace qlora_workspace_bytes(QLORA_OP_FWD_FUSED / _BWD_FUSED);
+ *   - staged: W is dequantized once into the workspace (deq(W) for the
+ *     forward, deq(W)^T for dX), then multiplied by the dense bf16 kernel,
+ *     so each weight is decoded once per call instead of once per 256
+ *     tokens.  Taken when M >= 1024, rows * cols < 2^31 (and, for dX,
+ *     rows % 64 == 0) and ws_bytes >= qlora_workspace_bytes(QLORA_OP_FWD /
+ *     _BWD), which then includes rows * cols * 2 bytes for the bf16 weight.
+ * Forward: Y [M x N] = X deq(W)^T + s (X A^T) B^T, s = RN32(alpha / r).
  * X [M x K], A [r x K], B [N x r], Y bf16 (overwritten).  r == 0 (A = B =
  * NULL) gives the frozen layer alone.  U_save (nullable) receives
  * U = X A^T [M x r] in bf16 for the backward pass.  Requires K % 64 == 0.
@@ -259,6 +279,27 @@ qlora_status qlora_lora_grads(const uint16_t* X, const uint16_t* dY, const uint1
  * Process": dequantization to BF16 on the fly inside the product. */
 qlora_status qlora_nf4_fwd(const qlora_nf4_weight* W, const uint16_t* X, int64_t M, const uint16_t* U,
                            const uint16_t* B, int32_t r, float alpha, uint16_t* Y, void* stream);
+
+/* The dense forward GEMM on a weight already dequantized to bf16 (for
+ * example by qlora_dequant): Y [M x N] = X Wd^T + s U B^T, with Wd [N x K]
+ * bf16 and U = X A^T given (r == 0: U = B = NULL).  K % 64 == 0, N % 8 == 0,
+ * N*K, M*K and M*N below 2^31 (QLORA_E_UNSUPPORTED otherwise).  No
+ * workspace.  deepfa.ir "QLoRA's Working Process": the weights are converted
+ * to BF16 for the computation; here the conversion is a separate pass, so a
+ * weight is decoded once per product instead of once per token tile. */
+qlora_status qlora_bf16_fwd(const uint16_t* Wd, int64_t N, int64_t K, const uint16_t* X, int64_t M,
+                            const uint16_t* U, const uint16_t* B, int32_t r, float alpha, uint16_t* Y,
+                            void* stream);
+
+/* The dense backward GEMM on the transposed bf16 weight (for example from
+ * qlora_dequant_t): dX [M x K] = dY WdT^T + s G A, with WdT [K x N] bf16,
+ * dY [M x N], G = dY B [M x r] given and A [r x K] (r == 0: G = A = NULL).
+ * N % 64 == 0, K % 64 == 0, N*K, M*K and M*N below 2^31
+ * (QLORA_E_UNSUPPORTED otherwise).  No workspace.  insights4ai page:
+ * gradients flow through the frozen weights into the adapters. */
+qlora_status qlora_bf16_dx(const uint16_t* WdT, int64_t N, int64_t K, const uint16_t* dY, int64_t M,
+                           const uint16_t* G, const uint16_t* A, int32_t r, float alpha, uint16_t* dX,
+                           void* stream);
 
 /* The fused backward GEMM: dX = dY deq(W) + s G A, with G = dY B given
  * (r == 0: G = A = NULL).  No workspace.  insights4ai page: gradients flow

@@ -1,0 +1,84 @@
+"""GPU parity of the dense bf16 GEMM on a dequantized weight (qlora_dequant
+followed by qlora_bf16_fwd) against the fp64 oracle.
+
+Y = X deq(W)^T + s (X A^T) B^T within the forward tolerances, on shapes that
+span several 256 x 256 tiles with ragged edges, r = 0, a LoRA-dominant case,
+and the largest rank.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from bit_quantized_finetuning_nf4_amd import ops, synth
+from tests.helpers import assert_close, bits_to_torch, torch_to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(N, K, M, r, seed, ab_std=0.01, w_std=0.02):
+    rng = np.random.default_rng(seed)
+    g = lambda shape, std: synth.to_bf16_bits(rng.standard_normal(shape) * std)
+    W = g((N, K), w_std) if w_std else np.zeros((N, K), dtype=np.uint16)
+    return dict(W=W, X=g((M, K), 1.0), A=g((r, K), ab_std) if r else None, B=g((N, r), ab_std) if r else None,
+                alpha=16.0)
+
+
+def _oracle(d):
+    c, a, s = oracle.quantize(d["W"])
+    Wd = oracle.bf16_bits_to_f64(oracle.dequant(c, a, s, d["W"].size)).reshape(d["W"].shape)
+    f = lambda k: None if d[k] is None else oracle.bf16_bits_to_f64(d[k]).reshape(d[k].shape)
+    return Wd, oracle.linear_fwd(Wd, f("X"), f("A"), f("B"), d["alpha"])
+
+
+@pytest.mark.parametrize("N,K,M,r", [(1024, 1024, 256, 8), (1000, 576, 300, 16), (264, 8192, 520, 64),
+                                     (512, 1088, 777, 0), (768, 2048, 1024, 128), (8, 64, 1, 8)])
+def test_dense_forward_matches_oracle(N, K, M, r):
+    d = _case(N, K, M, r, seed=N + K + M + r)
+    print(f"[dense parity] N{N} K{K} M{M} r{r}", flush=True)
+    q = ops.quantize(bits_to_torch(d["W"]))
+    Wd = ops.dequant(q)
+    X = bits_to_torch(d["X"])
+    U = ops.lora_down(X, bits_to_torch(d["A"])) if r else None
+    Y = ops.bf16_fwd(Wd, X, U, bits_to_torch(d["B"]) if r else None, d["alpha"])
+    torch.cuda.synchronize()
+    Wref, Yref = _oracle(d)
+    assert np.array_equal(torch_to_f64(Wd), Wref)   # the dequantized weight is bit-exact
+    assert_close(torch_to_f64(Y), Yref, f"Y N{N} K{K} M{M} r{r}")
+
+
+@pytest.mark.parametrize("w_std,ab_std", [(0.0, 1.0), (0.02, 1.0)])
+def test_dense_forward_lora_stress(w_std, ab_std):
+    # W = 0 (pure LoRA) and a LoRA-dominant case: the tail cannot hide
+    d = _case(520, 1024, 600, 64, seed=77, ab_std=ab_std, w_std=w_std)
+    q = ops.quantize(bits_to_torch(d["W"]))
+    X = bits_to_torch(d["X"])
+    U = ops.lora_down(X, bits_to_torch(d["A"]))
+    Y = ops.bf16_fwd(ops.dequant(q), X, U, bits_to_torch(d["B"]), d["alpha"])
+    torch.cuda.synchronize()
+    assert_close(torch_to_f64(Y), _oracle(d)[1], f"stress w{w_std} ab{ab_std}")
+
+
+@pytest.mark.parametrize("N,K,M,r", [(1024, 1024, 256, 8), (1088, 576, 300, 16), (320, 8192, 520, 128),
+                                     (512, 1088, 777, 0), (64, 64, 1, 8)])
+def test_dense_dx_matches_oracle(N, K, M, r):
+    """qlora_dequant_t then qlora_bf16_dx: dX = dY deq(W) + s (dY B) A."""
+    rng = np.random.default_rng(N + K + M + r + 1)
+    g = lambda shape, std: synth.to_bf16_bits(rng.standard_normal(shape) * std)
+    d = dict(W=g((N, K), 0.02), dY=g((M, N), 1.0), A=g((r, K), 0.2) if r else None,
+             B=g((N, r), 0.2) if r else None, alpha=16.0)
+    print(f"[dense dX parity] N{N} K{K} M{M} r{r}", flush=True)
+    q = ops.quantize(bits_to_torch(d["W"]))
+    dY = bits_to_torch(d["dY"])
+    A = bits_to_torch(d["A"]) if r else None
+    G = ops.lora_dy_b(dY, bits_to_torch(d["B"])) if r else None
+    dX = ops.bf16_dx(ops.dequant_t(q), dY, G, A, d["alpha"])
+    torch.cuda.synchronize()
+    c, a, s = oracle.quantize(d["W"])
+    Wd = oracle.bf16_bits_to_f64(oracle.dequant(c, a, s, d["W"].size)).reshape(N, K)
+    f = lambda k: None if d[k] is None else oracle.bf16_bits_to_f64(d[k]).reshape(d[k].shape)
+    dXr = f("dY") @ Wd
+    if r:
+        dXr = dXr + d["alpha"] / r * (f("dY") @ f("B")) @ f("A")
+    assert_close(torch_to_f64(dX), dXr, f"dX N{N} K{K} M{M} r{r}")

@@ -40,8 +40,13 @@ def test_linear_full_shape(set_name, li):
     t = synth.linear_inputs(N, K, M, r, synth.layer_set_seed(SET_INDEX[set_name], li), "cuda",
                             outliers=cfg["outliers"])
     q = ops.quantize(t["W"])
-    Y, U = ops.linear_fwd(q, t["X"], t["A"], t["B"], alpha, save_u=True)
-    dX, dA, dB = ops.linear_bwd(q, t["X"], t["dY"], t["A"], t["B"], alpha, U=U)
+    # both paths: staged (dequantize once, dense product; what bench.py times)
+    # and fused (decode inside the product)
+    outs = {}
+    for path in ("auto", "fused"):
+        Y, U = ops.linear_fwd(q, t["X"], t["A"], t["B"], alpha, save_u=True, path=path)
+        dX, dA, dB = ops.linear_bwd(q, t["X"], t["dY"], t["A"], t["B"], alpha, U=U, path=path)
+        outs[path] = (Y, dX, dA, dB)
     torch.cuda.synchronize()
 
     # quantized storage: every byte against the oracle's quantization
@@ -59,10 +64,11 @@ def test_linear_full_shape(set_name, li):
     Yr = oracle.linear_fwd(Wd, X[rows], A, B, alpha)
     dXr, _, _ = oracle.linear_bwd(Wd, X[rows], dY[rows], A, B, alpha)
     dAr, dBr = oracle.adapter_grads(X, dY, A, B, alpha)
-    assert_close(torch_to_f64(Y)[rows], Yr, f"{label} Y (48 rows)")
-    assert_close(torch_to_f64(dX)[rows], dXr, f"{label} dX (48 rows)")
-    assert_close(torch_to_f64(dA), dAr, f"{label} dA")
-    assert_close(torch_to_f64(dB), dBr, f"{label} dB")
+    for path, (Y, dX, dA, dB) in outs.items():
+        assert_close(torch_to_f64(Y)[rows], Yr, f"{label} {path} Y (48 rows)")
+        assert_close(torch_to_f64(dX)[rows], dXr, f"{label} {path} dX (48 rows)")
+        assert_close(torch_to_f64(dA), dAr, f"{label} {path} dA")
+        assert_close(torch_to_f64(dB), dBr, f"{label} {path} dB")
 
 
 def test_decode_gemv_65b_layer_set():

@@ -23,17 +23,17 @@ def _oracle_deq(W_bits, codebook="nf4"):
     return oracle.bf16_bits_to_f64(oracle.dequant(c, a, s, W_bits.size, codebook)).reshape(W_bits.shape)
 
 
-def _run(d, label, save_u=True, need_dx=True, check_u=True, codebook="nf4"):
-    print(f"[linear parity] {codebook} {label}", flush=True)
+def _run(d, label, save_u=True, need_dx=True, check_u=True, codebook="nf4", path="auto"):
+    print(f"[linear parity] {codebook} {label} path={path}", flush=True)
     W = bits_to_torch(d["W"])
     X, A, B, dY = (bits_to_torch(d[k]) if d[k] is not None else None for k in ("X", "A", "B", "dY"))
     alpha = d["alpha"]
     q = ops.quantize(W, codebook=codebook)
     if A is not None:
-        Y, U = ops.linear_fwd(q, X, A, B, alpha, save_u=True)
+        Y, U = ops.linear_fwd(q, X, A, B, alpha, save_u=True, path=path)
     else:
-        Y, U = ops.linear_fwd(q, X), None
-    dX, dA, dB = ops.linear_bwd(q, X, dY, A, B, alpha, U=U if save_u else None, need_dx=need_dx)
+        Y, U = ops.linear_fwd(q, X, path=path), None
+    dX, dA, dB = ops.linear_bwd(q, X, dY, A, B, alpha, U=U if save_u else None, need_dx=need_dx, path=path)
     torch.cuda.synchronize()
 
     Wd = _oracle_deq(d["W"], codebook)
@@ -83,7 +83,45 @@ def test_small_config():
                                # k tile is a quarter full, and the contraction has a ragged 12-stage tail
 ])
 def test_shapes(M, N, K, r):
-    _run(_case(M, N, K, r, seed=M + N + K + r), f"M{M} N{N} K{K} r{r}")
+    # from 1024 tokens the library stages W (dequantized once, dense product);
+    # the fused path is then run on its own as well
+    d = _case(M, N, K, r, seed=M + N + K + r)
+    _run(d, f"M{M} N{N} K{K} r{r}")
+    if M >= 1024:
+        _run(d, f"M{M} N{N} K{K} r{r}", path="fused")
+
+
+# The staged path (M >= 1024): dequantize once into the workspace, then the
+# dense bf16 product; dX multiplies dY by deq(W)^T with the LoRA term s G A
+# read from A column-wise.  Ragged tiles in every dimension, r = 0, the
+# largest rank, and the LoRA stress cases.
+@pytest.mark.parametrize("M,N,K,r", [
+    (1024, 1024, 1024, 8),
+    (1100, 1088, 576, 16),     # ragged M; N and K not multiples of 256
+    (2048, 320, 8192, 128),
+    (1300, 832, 2112, 0),
+    (1024, 64, 64, 64),
+    (1100, 1000, 576, 16),     # N % 64 != 0: staged forward, fused dX
+])
+def test_staged_shapes(M, N, K, r):
+    _run(_case(M, N, K, r, seed=3 * M + N + K + r), f"staged M{M} N{N} K{K} r{r}")
+
+
+def test_staged_lora_stress():
+    _run(_case(1024, 520, 1024, 64, seed=61, ab_std=1.0, zero_w=True), "staged W=0 A,B~N(0,1)")
+    _run(_case(1100, 776, 576, 128, seed=62, ab_std=1.0), "staged A,B~N(0,1) r128")
+
+
+@pytest.mark.parametrize("N,K", [(256, 1024), (1000, 576), (8, 64), (1032, 4160)])
+def test_dequant_transposed_is_bit_exact(N, K):
+    rng = np.random.default_rng(N + K)
+    W = synth.to_bf16_bits(rng.standard_normal((N, K)) * 0.02)
+    q = ops.quantize(bits_to_torch(W))
+    Wt = ops.dequant_t(q)
+    Wd = ops.dequant(q)
+    torch.cuda.synchronize()
+    assert torch.equal(Wt.view(torch.int16), Wd.t().contiguous().view(torch.int16))
+    assert np.array_equal(torch_to_f64(Wt), _oracle_deq(W).T)
 
 
 def test_rank_zero_is_frozen_layer_only():

@@ -1,11 +1,12 @@
 """GPU parity of qlora_linear_fwd_noalloc (the forward without a workspace
 argument, for callers that cannot allocate) against qlora_linear_fwd.
 
-Two calls in a row, the second on a smaller input, each compared with the
-workspace entry point bit for bit (they run the same kernels) and with the
-fp64 oracle within the forward tolerances; U comes back as well.  Then a
-rank-0 call (no scratch needed) and a call that returns U through the
-scratch-free path only.
+The no-allocation call always takes the fused path (its 32 MiB array cannot
+hold a bf16 weight), so the reference is qlora_linear_fwd with a workspace
+sized for the fused path: the same kernels, compared bit for bit, and both
+within the forward tolerances of the fp64 oracle.  Two calls in a row, the
+second on a smaller input; U comes back as well.  Then a rank-0 call (no
+scratch needed) and a call that keeps U in the array only.
 """
 
 import numpy as np
@@ -41,7 +42,7 @@ def _check(d, label):
     B = None if d["B"] is None else bits_to_torch(d["B"])
     r = 0 if A is None else A.shape[0]
     Yn, Un = ops.linear_fwd_noalloc(q, X, A, B, d["alpha"], save_u=True)
-    Yw, Uw = ops.linear_fwd(q, X, A, B, d["alpha"], save_u=True)
+    Yw, Uw = ops.linear_fwd(q, X, A, B, d["alpha"], save_u=True, path="fused")
     torch.cuda.synchronize()
     assert torch.equal(Yn.view(torch.int16), Yw.view(torch.int16)), f"{label}: Y differs from qlora_linear_fwd"
     if r:
@@ -66,7 +67,7 @@ def test_u_is_recomputed_into_scratch_when_not_saved():
     d = _case(768, 2048, 512, 64, seed=904)
     q, X, A, B = _check(d, "N768 K2048 M512 r64 (saved U)")
     Y1 = ops.linear_fwd_noalloc(q, X, A, B, d["alpha"])
-    Y2 = ops.linear_fwd(q, X, A, B, d["alpha"])
+    Y2 = ops.linear_fwd(q, X, A, B, d["alpha"], path="fused")
     torch.cuda.synchronize()
     assert torch.equal(Y1.view(torch.int16), Y2.view(torch.int16))
 
