@@ -10,18 +10,27 @@
 // 256 threads (4 waves), 256 x 256 output tile, wave (wr, wc) a 128 x 128
 // sub-tile (tokens 128 wr.., weight rows 128 wc..) in 256 accumulator
 // registers, bf16 MFMA 32x32x16 with fp32 accumulation.  The contraction runs
-// in stages of 32 through a ring of five LDS stage buffers (weight half +
-// token half, 64-byte rows), filled by buffer->LDS DMA three and four stages
-// ahead, in pairs of stages that cover whole 128-byte lines; one barrier per
-// stage.
+// in pairs of 32-wide stages: a pair (64 columns: one 128-byte line of every
+// row) comes into one of two LDS pair slots by buffer->LDS DMA, each
+// instruction moving 8 whole rows, one pair ahead; one barrier per pair.
+#include <algorithm>
+
 #include "gemm_common.h"
 
 namespace qlora {
 namespace {
 
-constexpr int kDRing = 5;                               // stage s in ring slot s mod 5
-constexpr size_t kLdsDense = (size_t)kDRing * kStage;   // 160 KiB
+constexpr int kPairOp = kTile * 128;                    // 32 KiB: 256 rows x 64 bf16 (two stages)
+constexpr int kPairSlot = 2 * kPairOp;                  // weight rows at 0, token rows at kPairOp
+constexpr size_t kLdsDense = 2 * (size_t)kPairSlot;     // 128 KiB: two pair slots
 constexpr int kDGroup = 4;                              // token tiles per tile group (tile order)
+
+// Pair slots hold two consecutive 32-wide stages (one 64-wide stage): rows of
+// 128 bytes, 16-byte chunk c of row r at position c ^ ((r >> 1) & 7), so the
+// 16 lanes of one read quarter (16 consecutive rows, one chunk) and a DMA
+// instruction's 64 lanes (8 whole rows) cover all 64 LDS banks.  Chunks
+// 0..3 are the even stage, 4..7 the odd one.
+__device__ __forceinline__ int pos128(int r, int c) { return r * 128 + 16 * (c ^ ((r >> 1) & 7)); }
 
 // Tile order of the dense GEMMs.  The eight XCDs receive contiguous ranges of
 // tile ids (the hardware hands workgroups to XCDs round robin); ids run over
@@ -42,99 +51,100 @@ __device__ __forceinline__ void map_tile_grouped(int tiles_c, int tiles_r, int& 
 
 struct DenseOps {
   rsrc_t wr_, xr;           // weight rows, token rows
-  uint32_t wo[4], xo[4];    // lane offsets of the four DMA instructions per operand (stage 0)
-  int nsub, w;
+  uint32_t wo[8], xo[8];    // lane offsets of the eight DMA instructions per operand (pair 0)
+  int npair, w;
 };
 
-// Stage `stage` of both operands into ring slot `slot`: DMA instruction q of
-// wave w fills tile rows 64 q + 16 w .. +15 (lane j: row + (j >> 2), holding
-// chunk dma_chunk(j) at position j & 3).  Past the last stage the last one
-// is re-loaded (never read).
-__device__ __forceinline__ void dense_dma(char* smem, const DenseOps& f, int stage, int slot) {
-  const uint32_t soff = (uint32_t)min(stage, f.nsub - 1) * 64u;
-  char* dst = smem + slot * kStage + 16 * f.w * 64;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) dma16(f.wr_, dst + 64 * q * 64, f.wo[q], soff);
-#pragma unroll
-  for (int q = 0; q < 4; ++q) dma16(f.xr, dst + kOp + 64 * q * 64, f.xo[q], soff);
+// DMA of pair `pair` (64 columns of every row) of both operands into pair
+// slot `dst`: weight instruction q < 2 FI and token instruction q < 8 of
+// wave w fill rows 8 (4 q + w) .. +7 of their tile, 128 bytes each (lane j:
+// row + (j >> 3), position j & 7).  DMA d of a pair is weight instruction d
+// for d < 2 FI, token instruction d - 2 FI after.  Past the last pair the last
+// one is re-loaded (never read).
+template <int FI>
+__device__ __forceinline__ void pair_dma(char* dst, const DenseOps& f, int pair, int d) {
+  const uint32_t soff = (uint32_t)min(pair, f.npair - 1) * 128u;
+  const bool wrow = d < 2 * FI;
+  const int q = wrow ? d : d - 2 * FI;
+  char* dd = dst + (wrow ? 0 : kPairOp) + 8 * (4 * q + f.w) * 128;
+  if (wrow)
+    dma16(f.wr_, dd, f.wo[q], soff);
+  else
+    dma16(f.xr, dd, f.xo[q], soff);
 }
 
-// MFMA slot X (0..31) of substep s (stage s at cur, s+1 at nxt; stage
-// s+3 and s+4 go to fill0 and fill1): X = 16 kk + 4 i + j is fragment pair (i, j) of
-// k16 step kk.  The LDS reads and the DMAs are spread one per two slots, so
-// that the four waves (which leave each barrier together) do not queue their
-// reads on the LDS at once:
-//   LDS reads   read q (fragments A0, B0, B1, B2, B3, A1, A2, A3 in that
-//               order) in slot 2 q: step 1 of stage s; in slot 16 + 2 q: step
-//               0 of stage s+1, into the registers step 0 of stage s has
-//               finished with.  The MFMA of slot 16 + 4 i + j uses read
-//               max(i + 4 [i > 0], 1 + j), issued at least ten slots before.
-//   DMA         odd substeps only, odd slots: stages s+3 and s+4, the two
-//               halves of the same 128-byte lines (a stage is 64 bytes of a
-//               row), one after the other, so that the second request of a
-//               line meets the first one's pending miss in the L1 instead of
-//               going to L2 again: slot 4 q + 1 and 4 q + 3 are instruction
-//               q (four weight-row, then four token-row) of stage s+3 and of
-//               stage s+4.
-template <int X, bool ODD>
-__device__ __forceinline__ void fwd_dense_slot(const char* cur, const char* nxt, char* fill0, char* fill1,
-                                               const DenseOps& f, int s, f32x16_t (&acc)[4][4], Frags& F, int am,
-                                               int bm, FragOffs fo) {
-  constexpr int kk = X >> 4, i = (X >> 2) & 3, j = X & 3, y = X & 15;
+// Read offsets of the lane within a pair slot: stage half hf, k16 step kk ->
+// chunk 4 hf + 2 kk + h of row lr.
+struct PairOffs {
+  int o[2][2];
+};
+
+// MFMA slot X (0 .. 8 FI - 1) of substep s: X = 4 FI kk + 4 i + j is
+// fragment pair (i, j) of k16 step kk (FI weight fragments of 32 rows, four
+// token fragments).  Stage s is half HF of the pair slot at cur; stage s+1 is
+// the other half of cur (HF = 0) or half 0 of the next slot (HF = 1).
+//   LDS reads   read q (fragments A0, B0, B1, B2, B3, A1, .., A(FI-1) in
+//               that order) in slot rd_slot(q): step 1 of stage s; in slot
+//               4 FI + rd_slot(q): step 0 of stage s+1, into the registers
+//               step 0 of stage s has finished with.
+//   barrier     odd substeps, before slot 4 FI: this wave's DMAs of the next
+//               pair have landed and its reads of this pair have completed;
+//               after it the next pair is visible to every wave and no wave
+//               reads this pair's slot any more.
+//   DMA         odd substeps, slots 4 FI ..: the pair after next into this
+//               pair's slot (2 FI weight-row, then 8 token-row instructions of
+//               8 whole 128-byte rows each), spread over the second half.
+template <int FI>
+constexpr int rd_slot(int q) { return q * 4 * FI / (FI + 4); }
+template <int FI>
+constexpr int dma_slot(int d) { return 4 * FI + d * 4 * FI / (2 * FI + 8); }
+
+template <int FI, int X, int HF>
+__device__ __forceinline__ void dense_slot(const char* cur, const char* nxt, char* fill, const DenseOps& f,
+                                           int pair, f32x16_t (&acc)[FI][4], Frags& F, int am, int bm,
+                                           const PairOffs& po) {
+  constexpr int H = 4 * FI;   // slots per k16 step
+  constexpr int kk = X / H, y = X % H, i = y >> 2, j = y & 3;
+  if constexpr (HF == 1 && X == H) {
+    QLORA_WAIT(0, 0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+  }
   if constexpr (kk == 0)
     acc[i][j] = mfma32x32x16(F.a0[i], F.b0[j], acc[i][j]);
   else
     acc[i][j] = mfma32x32x16(F.a1[i], F.b1[j], acc[i][j]);
-  if constexpr ((y & 1) == 0) {
-    constexpr int q = y >> 1;                               // read 0..7
-    constexpr bool isA = q == 0 || q >= 5;
-    constexpr int fr = q == 0 ? 0 : q >= 5 ? q - 4 : q - 1;   // fragment index
-    const char* base = (kk == 0 ? cur : nxt) + (isA ? am : kOp + bm) + fr * 2048;
-    const int o = kk == 0 ? fo.o1 : fo.o0;
-    if constexpr (isA) {
-      if constexpr (kk == 0) F.a1[fr] = rd16(base + o); else F.a0[fr] = rd16(base + o);
+#pragma unroll
+  for (int q = 0; q < FI + 4; ++q) {
+    if (rd_slot<FI>(q) != y) continue;
+    const bool isA = q == 0 || q >= 5;
+    const int fr = q == 0 ? 0 : q >= 5 ? q - 4 : q - 1;   // fragment index
+    // step 1 of stage s (half HF of cur), or step 0 of stage s+1
+    const char* slot = kk == 0 ? cur : (HF == 0 ? cur : nxt);
+    const int o = kk == 0 ? po.o[HF][1] : po.o[HF ^ 1][0];
+    const char* base = slot + (isA ? am : kPairOp + bm) + fr * 32 * 128 + o;
+    if (isA) {
+      if (kk == 0) F.a1[fr] = rd16(base); else F.a0[fr] = rd16(base);
     } else {
-      if constexpr (kk == 0) F.b1[fr] = rd16(base + o); else F.b0[fr] = rd16(base + o);
+      if (kk == 0) F.b1[fr] = rd16(base); else F.b0[fr] = rd16(base);
     }
   }
-  if constexpr (ODD && (X & 1)) {
-    constexpr int q = X >> 2, second = (X >> 1) & 1;   // instruction 0..7, stage s+3 or s+4
-    const uint32_t soff = (uint32_t)min(s + 3 + second, f.nsub - 1) * 64u;
-    char* dst = (second ? fill1 : fill0) + (q >= 4 ? kOp : 0) + (64 * (q & 3) + 16 * f.w) * 64;
-    if constexpr (q < 4)
-      dma16(f.wr_, dst, f.wo[q], soff);
-    else
-      dma16(f.xr, dst, f.xo[q - 4], soff);
+  if constexpr (HF == 1 && kk == 1) {
+#pragma unroll
+    for (int d = 0; d < 2 * FI + 8; ++d)
+      if (dma_slot<FI>(d) == X) pair_dma<FI>(fill, f, pair + 2, d);
   }
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// One barrier per substep.  Before it, this wave's DMAs of stage s+1 must
-// have landed: at an even substep (stage s+1 was DMA'd three substeps ago)
-// only the sixteen DMAs of the last odd substep may still be in flight; at an
-// odd one (stage s+1 DMA'd two substeps ago, interleaved with stage s+2) only
-// the last DMA, of stage s+2.  The barrier then makes stage s+1 visible to
-// every wave and certifies that every wave has finished reading stage s-1,
-// whose slot (with stage s-2's) an odd substep refills.  Stage t sits in ring
-// slot t mod 5; sl is stage s's.
-template <bool ODD>
-__device__ __forceinline__ void fwd_dense_substep(char* smem, const DenseOps& f, int s, int sl,
-                                                  f32x16_t (&acc)[4][4], Frags& F, int am, int bm, FragOffs fo) {
-  auto slot = [](int v) { return v >= kDRing ? v - kDRing : v; };
-  const char* cur = smem + sl * kStage;
-  const char* nxt = smem + slot(sl + 1) * kStage;
-  char* fill0 = smem + slot(sl + 3) * kStage;
-  char* fill1 = smem + slot(sl + 4) * kStage;
-  __builtin_amdgcn_sched_barrier(0);
-  QLORA_WAIT(ODD ? 1 : 16, 0);
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_sched_barrier(0);
-#define QLORA_FD_SLOT(x) fwd_dense_slot<x, ODD>(cur, nxt, fill0, fill1, f, s, acc, F, am, bm, fo)
-#define QLORA_FD_SLOT4(x) QLORA_FD_SLOT(x); QLORA_FD_SLOT(x + 1); QLORA_FD_SLOT(x + 2); QLORA_FD_SLOT(x + 3)
-  QLORA_FD_SLOT4(0); QLORA_FD_SLOT4(4); QLORA_FD_SLOT4(8); QLORA_FD_SLOT4(12);
-  QLORA_FD_SLOT4(16); QLORA_FD_SLOT4(20); QLORA_FD_SLOT4(24); QLORA_FD_SLOT4(28);
-#undef QLORA_FD_SLOT4
-#undef QLORA_FD_SLOT
+template <int FI, int HF, int X>
+__device__ __forceinline__ void dense_slots(const char* cur, const char* nxt, char* fill, const DenseOps& f,
+                                            int pair, f32x16_t (&acc)[FI][4], Frags& F, int am, int bm,
+                                            const PairOffs& po) {
+  if constexpr (X < 8 * FI) {
+    dense_slot<FI, X, HF>(cur, nxt, fill, f, pair, acc, F, am, bm, po);
+    dense_slots<FI, HF, X + 1>(cur, nxt, fill, f, pair, acc, F, am, bm, po);
+  }
 }
 
 // Weight half of the LoRA tail: B'[row0 + row, j0 + 8 c ..] into a 64-byte-row
@@ -162,62 +172,88 @@ __device__ __forceinline__ void tail_rows(char* dst, const bf16_t* Bm, bool b_tr
   }
 }
 
+// FI: weight fragments per wave, so the tile is 64 FI weight rows x 256
+// tokens (FI = 4, 3 or 2); its tiles start at weight row n_begin.
+template <int FI>
 __global__ __launch_bounds__(kThreads, 1) void bf16_fwd_kernel(const bf16_t* __restrict__ Wd, int64_t N, int64_t K,
                                                                const bf16_t* __restrict__ X, int64_t M,
                                                                const bf16_t* __restrict__ U,
                                                                const bf16_t* __restrict__ Bl, int b_trans, int r,
-                                                               float s, bf16_t* __restrict__ Y, int tiles_n,
-                                                               int tiles_m) {
+                                                               float s, bf16_t* __restrict__ Y, int64_t n_begin,
+                                                               int tiles_n, int tiles_m) {
   extern __shared__ __align__(16) char smem[];
   int tn, tm;
   map_tile_grouped(tiles_n, tiles_m, tn, tm);
-  const int64_t n0 = (int64_t)tn * kTile, m0 = (int64_t)tm * kTile;
+  const int64_t n0 = n_begin + (int64_t)tn * 64 * FI, m0 = (int64_t)tm * kTile;
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6, wr = wv >> 1, wc = wv & 1;
 
   DenseOps f;
   f.w = __builtin_amdgcn_readfirstlane(wv);
   __builtin_assume(f.w >= 0 && f.w < 4);
-  f.nsub = (int)(K >> 5);
+  f.npair = (int)(K >> 6);
   f.wr_ = make_rsrc(Wd, (uint32_t)(N * K * 2));
   f.xr = make_rsrc(X, (uint32_t)(M * K * 2));
+  {
+    // lane j of DMA instruction q: row 8 (4 q + w) + (j >> 3), position j & 7
+    // holding chunk (j & 7) ^ ((row >> 1) & 7) = (j & 7) ^ ((4 w + (j >> 4)) & 7)
+    const int c = (lane & 7) ^ ((4 * f.w + (lane >> 4)) & 7);
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    // rows past the end re-read the last row: finite data, never stored
-    const int row = dma_row(q, f.w, lane);
-    f.wo[q] = (uint32_t)(min(n0 + row, N - 1) * K * 2 + dma_chunk(lane) * 16);
-    f.xo[q] = (uint32_t)(min(m0 + row, M - 1) * K * 2 + dma_chunk(lane) * 16);
+    for (int q = 0; q < 8; ++q) {
+      // rows past the end re-read the last row: finite data, never stored
+      const int row = 8 * (4 * q + f.w) + (lane >> 3);
+      if (q < 2 * FI) f.wo[q] = (uint32_t)(min(n0 + row, N - 1) * K * 2 + c * 16);
+      f.xo[q] = (uint32_t)(min(m0 + row, M - 1) * K * 2 + c * 16);
+    }
   }
-  const FragOffs fo = frag_offs(lane);
-  const int am = wc * 128 * 64, bm = wr * 128 * 64;
-
-  f32x16_t acc[4][4];
-  zero_acc(acc);
-
-  // stages 0..3 in slots 0..3; substep 1 starts the pairs (4, 5)
+  PairOffs po;
+  {
+    const int lr = lane & 31, h = lane >> 5;
 #pragma unroll
-  for (int st = 0; st < 4; ++st) dense_dma(smem, f, st, st);
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) po.o[hf][kk] = pos128(lr, 4 * hf + 2 * kk + h);
+  }
+  const int am = wc * 32 * FI * 128, bm = wr * 128 * 128;
+
+  f32x16_t acc[FI][4];
+#pragma unroll
+  for (int i = 0; i < FI; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+  // pairs 0 and 1 into slots 0 and 1
+#pragma unroll
+  for (int d = 0; d < 2 * FI + 8; ++d) {
+    pair_dma<FI>(smem, f, 0, d);
+    pair_dma<FI>(smem + kPairSlot, f, 1, d);
+  }
   QLORA_WAIT(0, 0);
   __builtin_amdgcn_s_barrier();
   Frags F;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    F.a0[i] = rd16(smem + am + i * 2048 + fo.o0);
-    F.b0[i] = rd16(smem + kOp + bm + i * 2048 + fo.o0);
+    if (i < FI) F.a0[i] = rd16(smem + am + i * 32 * 128 + po.o[0][0]);
+    F.b0[i] = rd16(smem + kPairOp + bm + i * 32 * 128 + po.o[0][0]);
   }
-  // K % 64 == 0: the stage count is even
-  int sl = 0;
-  for (int st = 0; st < f.nsub; st += 2) {
-    fwd_dense_substep<false>(smem, f, st, sl, acc, F, am, bm, fo);
-    sl = sl + 1 == kDRing ? 0 : sl + 1;
-    fwd_dense_substep<true>(smem, f, st + 1, sl, acc, F, am, bm, fo);
-    sl = sl + 1 == kDRing ? 0 : sl + 1;
+  // K % 64 == 0: whole pairs of 32-wide stages
+  for (int pr = 0; pr < f.npair; ++pr) {
+    char* cur = smem + (pr & 1) * kPairSlot;
+    char* nxt = smem + ((pr & 1) ^ 1) * kPairSlot;
+    __builtin_amdgcn_sched_barrier(0);
+    dense_slots<FI, 0, 0>(cur, nxt, cur, f, pr, acc, F, am, bm, po);
+    __builtin_amdgcn_sched_barrier(0);
+    dense_slots<FI, 1, 0>(cur, nxt, cur, f, pr, acc, F, am, bm, po);
   }
-  // drain the DMAs still in flight (clamped re-loads) before reusing the ring
+  // drain the DMAs still in flight (clamped re-loads) before reusing LDS
   QLORA_WAIT(0, 0);
   __builtin_amdgcn_s_barrier();
 
   if (r > 0) {
-    // acc += B (s U)^T over the rank, 32 at a time
+    // acc += B (s U)^T over the rank, 32 at a time, through 64-byte-row tiles
+    const FragOffs fo = frag_offs(lane);
+    const int am64 = wc * 32 * FI * 64, bm64 = wr * 128 * 64;
     for (int j0 = 0; j0 < r; j0 += 32) {
       tail_rows(smem, Bl, b_trans != 0, N, r, n0, j0);
       tail_tokens(smem + kOp, U, M, r, m0, j0, s);
@@ -228,30 +264,92 @@ __global__ __launch_bounds__(kThreads, 1) void bf16_fwd_kernel(const bf16_t* __r
         const int o = kk ? fo.o1 : fo.o0;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          F.a0[i] = rd16(smem + am + i * 2048 + o);
-          F.b0[i] = rd16(smem + kOp + bm + i * 2048 + o);
+          if (i < FI) F.a0[i] = rd16(smem + am64 + i * 2048 + o);
+          F.b0[i] = rd16(smem + kOp + bm64 + i * 2048 + o);
         }
-        mfma_block<4, 4>(acc, F.a0, F.b0);
+#pragma unroll
+        for (int i = 0; i < FI; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[i][j] = mfma32x32x16(F.a0[i], F.b0[j], acc[i][j]);
       }
       QLORA_WAIT(0, 0);
       __builtin_amdgcn_s_barrier();
     }
   }
-  store_tile<4>(acc, Y, N, M, N, m0, n0);
+  store_tile<FI>(acc, Y, N, M, N, m0, n0);
 }
 
 }  // namespace
 
+namespace {
+
+// Tiles of 64 FI weight rows over rows [n_begin, n_begin + n_rows) of the
+// N-row weight (N is every array's extent and leading dimension).
+template <int FI>
+hipError_t launch_fi(const bf16_t* Wd, int64_t N, int64_t K, const bf16_t* X, int64_t M, const bf16_t* U,
+                     const bf16_t* B, bool b_trans, int r, float s, bf16_t* Y, int64_t n_begin, int64_t n_rows,
+                     hipStream_t st) {
+  const int tiles_n = (int)((n_rows + 64 * FI - 1) / (64 * FI));
+  const int tiles_m = (int)((M + kTile - 1) / kTile);
+  auto* fn = &bf16_fwd_kernel<FI>;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     (int)kLdsDense);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(fn, dim3(tiles_n * tiles_m), dim3(kThreads), kLdsDense, st, Wd, N, K, X, M, U, B, (int)b_trans, r,
+                     s, Y, n_begin, tiles_n, tiles_m);
+  return hipGetLastError();
+}
+
+// Time of weight rows [n_begin, N) in 64 FI-row tiles, in units of one round
+// of 256-row tiles: rounds x FI / 4, with a small charge for the narrower
+// tiles' extra LDS reads per MFMA.
+double tile_cost(int64_t rows, int64_t tiles_m, int fi, int cus) {
+  const int64_t tiles = (rows + 64 * fi - 1) / (64 * fi) * tiles_m;
+  const double eff = fi == 4 ? 1.0 : fi == 3 ? 1.06 : 1.12;
+  return (double)((tiles + cus - 1) / cus) * fi / 4.0 * eff;
+}
+int best_fi(int64_t rows, int64_t tiles_m, int cus) {
+  int best = 4;
+  for (int fi = 3; fi >= 2; --fi)
+    if (tile_cost(rows, tiles_m, fi, cus) < tile_cost(rows, tiles_m, best, cus)) best = fi;
+  return best;
+}
+
+hipError_t launch_rows(int fi, const bf16_t* Wd, int64_t N, int64_t K, const bf16_t* X, int64_t M,
+                       const bf16_t* U, const bf16_t* B, bool b_trans, int r, float s, bf16_t* Y, int64_t n_begin,
+                       hipStream_t st) {
+  const int64_t n_rows = N - n_begin;
+  if (fi == 3) return launch_fi<3>(Wd, N, K, X, M, U, B, b_trans, r, s, Y, n_begin, n_rows, st);
+  if (fi == 2) return launch_fi<2>(Wd, N, K, X, M, U, B, b_trans, r, s, Y, n_begin, n_rows, st);
+  return launch_fi<4>(Wd, N, K, X, M, U, B, b_trans, r, s, Y, n_begin, n_rows, st);
+}
+
+}  // namespace
+
+// The grid is sized for the CU count.  Weight rows are cut into a part that
+// fills whole rounds of 256-row tiles and a remainder, whose tile width (256,
+// 192 or 128 rows) minimizes its time; a shape with fewer 256-row tiles than
+// CUs is all remainder.
 hipError_t launch_bf16_fwd(const bf16_t* Wd, int64_t N, int64_t K, const bf16_t* X, int64_t M, const bf16_t* U,
                            const bf16_t* B, bool b_trans, int r, float s, bf16_t* Y, hipStream_t st) {
-  const int tiles_n = (int)((N + kTile - 1) / kTile);
-  const int tiles_m = (int)((M + kTile - 1) / kTile);
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bf16_fwd_kernel),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsDense);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(bf16_fwd_kernel, dim3(tiles_n * tiles_m), dim3(kThreads), kLdsDense, st, Wd, N, K, X, M, U, B,
-                     (int)b_trans, r, s, Y, tiles_n, tiles_m);
-  return hipGetLastError();
+  const int cus = device_cu_count();
+  const int64_t tiles_m = (M + kTile - 1) / kTile;
+  const int64_t tiles_n = (N + kTile - 1) / kTile;
+  int64_t n_split = 0;   // rows of the whole-round part
+  if (tiles_n * tiles_m > cus && cus % tiles_m == 0) {
+    const int64_t per_round = cus / tiles_m;   // 256-row column tiles per round
+    n_split = std::min(N, (tiles_n * tiles_m / cus) * per_round * kTile);
+    if (n_split >= N || tile_cost(N - n_split, tiles_m, best_fi(N - n_split, tiles_m, cus), cus) >=
+                            tile_cost(N - n_split, tiles_m, 4, cus))
+      n_split = 0;   // nothing left over, or the remainder gains nothing from narrower tiles: one launch
+  }
+  if (n_split > 0) {
+    hipError_t e = launch_fi<4>(Wd, N, K, X, M, U, B, b_trans, r, s, Y, 0, n_split, st);
+    if (e != hipSuccess) return e;
+    // the remainder's tiles address rows from n_split on, in the same arrays
+    return launch_rows(best_fi(N - n_split, tiles_m, cus), Wd, N, K, X, M, U, B, b_trans, r, s, Y, n_split, st);
+  }
+  return launch_rows(best_fi(N, tiles_m, cus), Wd, N, K, X, M, U, B, b_trans, r, s, Y, 0, st);
 }
 
 }  // namespace qlora

@@ -223,53 +223,67 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict_
 }
 
 // Transposed dequantization, WdT [K x N] = deq(W)^T for W [N x K] with
-// K % 64 == 0 (the dense backward multiplies by it).  A workgroup takes a
-// 64-row x 64-column tile of W, which is one block per row: thread t decodes
-// rows 2 (t >> 3) and 2 (t >> 3) + 1, columns 8 (t & 7) .. +7, packs each
-// column's two rows into one dword and stores it to LDS at [column][row
-// pair] (rows of 33 dwords, so that the eight column groups of a wave fall in
-// distinct banks); then thread t writes 32 contiguous bytes (16 rows of W) of
-// WdT row k0 + (t >> 2).  Rows past N decode as zero and are not written.
+// K % 64 == 0 (the dense backward multiplies by it).  A workgroup takes 64
+// rows x 256 columns of W, so each row's codes are one whole 128-byte line:
+// thread t decodes rows 2 (t & 31) and 2 (t & 31) + 1, columns 32 (t >> 5)
+// .. +31 (half a block of each row), packs each column's two rows into one
+// dword and stores it to LDS at [column][row pair] (rows of 33 dwords: the
+// 32 row pairs of a wave's half fall in 32 consecutive banks, the other half
+// 32 banks on); then the waves write WdT rows k0 .. k0 + 255, 128 bytes (64
+// rows of W) each, eight whole rows per store instruction.  Rows past N
+// decode as zero and are not written; columns past K are neither read nor
+// written.
 constexpr int kTrStride = 33;
 template <int CB>
 __global__ __launch_bounds__(256) void dequant_t_kernel(const uint8_t* __restrict__ codes,
                                                         const uint8_t* __restrict__ absmax_q,
                                                         const float* __restrict__ group_scale, int64_t N,
                                                         int64_t K, bf16_t* __restrict__ out) {
-  __shared__ uint32_t tile[64 * kTrStride];
-  const int t = threadIdx.x, rp = t >> 3, cg = t & 7;
-  const int64_t n0 = (int64_t)blockIdx.y * 64, k0 = (int64_t)blockIdx.x * 64;
-  uint32_t c[2];
-  Nf4Table T[2];
+  __shared__ uint32_t tile[256 * kTrStride];
+  const int t = threadIdx.x, rp = t & 31, cg = t >> 5;
+  const int64_t n0 = (int64_t)blockIdx.y * 64, k0 = (int64_t)blockIdx.x * 256;
+  const int64_t kc = k0 + 32 * cg;
+  if (kc < K) {
+    uint4 c[2];
+    Nf4Table T[2];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int64_t row = n0 + 2 * rp + i;
-    if (row < N) {
-      const int64_t b = (row * K + k0) >> 6;
-      T[i] = make_table<CB>(block_scale(absmax_q[b], group_scale[b / kGroupBlocks]));
-      c[i] = *reinterpret_cast<const uint32_t*>(codes + ((row * K + k0 + 8 * cg) >> 1));
-    } else {
-      T[i] = make_table<CB>(0.0f);
-      c[i] = 0u;
+    for (int i = 0; i < 2; ++i) {
+      const int64_t row = n0 + 2 * rp + i;
+      if (row < N) {
+        const int64_t b = (row * K + kc) >> 6;
+        T[i] = make_table<CB>(block_scale(absmax_q[b], group_scale[b / kGroupBlocks]));
+        c[i] = *reinterpret_cast<const uint4*>(codes + ((row * K + kc) >> 1));
+      } else {
+        T[i] = make_table<CB>(0.0f);
+        c[i] = make_uint4(0u, 0u, 0u, 0u);
+      }
+    }
+    const uint32_t w0[4] = {c[0].x, c[0].y, c[0].z, c[0].w}, w1[4] = {c[1].x, c[1].y, c[1].z, c[1].w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint32_t o[8];
+      dequant8x2_pairs(w0[j], w1[j], T[0], T[1], o);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) tile[(32 * cg + 8 * j + k) * kTrStride + rp] = o[k];
     }
   }
-  uint32_t o[8];
-  dequant8x2_pairs(c[0], c[1], T[0], T[1], o);
-#pragma unroll
-  for (int k = 0; k < 8; ++k) tile[(8 * cg + k) * kTrStride + rp] = o[k];
   __syncthreads();
-  const int kk = t >> 2, q = t & 3;
-  uint32_t v[8];
+  // write-out: each store instruction of a wave covers 8 whole 128-byte rows
+  // of WdT (lane l: row 8 q + (l >> 3) of the wave's 64, 16-byte chunk l & 7)
+  const int lane = t & 63, w = t >> 6, c = lane & 7;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) v[e] = tile[kk * kTrStride + 8 * q + e];
-  const int64_t ncol = n0 + 16 * q;
-  bf16_t* dst = out + (k0 + kk) * N + ncol;
-  if (ncol + 16 <= N) {
-    uint4* d4 = reinterpret_cast<uint4*>(dst);
-    d4[0] = make_uint4(v[0], v[1], v[2], v[3]);
-    d4[1] = make_uint4(v[4], v[5], v[6], v[7]);
-  } else {
-    for (int e = 0; e < 16 && ncol + e < N; ++e) dst[e] = (bf16_t)(v[e >> 1] >> (16 * (e & 1)));
+  for (int q = 0; q < 8; ++q) {
+    const int kk = 64 * w + 8 * q + (lane >> 3);
+    if (k0 + kk >= K) continue;
+    const uint32_t* src = tile + kk * kTrStride + 4 * c;
+    const uint4 v = make_uint4(src[0], src[1], src[2], src[3]);
+    bf16_t* dst = out + (k0 + kk) * N + n0 + 8 * c;
+    if (n0 + 8 * c + 8 <= N) {
+      *reinterpret_cast<uint4*>(dst) = v;
+    } else {
+      const uint32_t vw[4] = {v.x, v.y, v.z, v.w};
+      for (int e = 0; e < 8 && n0 + 8 * c + e < N; ++e) dst[e] = (bf16_t)(vw[e >> 1] >> (16 * (e & 1)));
+    }
   }
 }
 
@@ -304,8 +318,8 @@ hipError_t launch_dequant_t(const uint8_t* codes, const uint8_t* absmax_q, const
                             int64_t K, int codebook, bf16_t* out, hipStream_t s) {
   auto* fn = codebook == kCbFp4 ? &dequant_t_kernel<kCbFp4> : codebook == kCbInt4 ? &dequant_t_kernel<kCbInt4>
                                                                                   : &dequant_t_kernel<kCbNf4>;
-  hipLaunchKernelGGL(fn, dim3((unsigned)(K / 64), (unsigned)((N + 63) / 64)), dim3(256), 0, s, codes, absmax_q,
-                     group_scale, N, K, out);
+  hipLaunchKernelGGL(fn, dim3((unsigned)((K + 255) / 256), (unsigned)((N + 63) / 64)), dim3(256), 0, s, codes,
+                     absmax_q, group_scale, N, K, out);
   return hipGetLastError();
 }
 

@@ -82,3 +82,25 @@ def test_dense_dx_matches_oracle(N, K, M, r):
     if r:
         dXr = dXr + d["alpha"] / r * (f("dY") @ f("B")) @ f("A")
     assert_close(torch_to_f64(dX), dXr, f"dX N{N} K{K} M{M} r{r}")
+
+
+# Tile widths: on 256 CUs, (5120 rows, 2048 tokens) runs 192-row tiles in one
+# round; (4352 rows, 4096 tokens) fills one round of 256-row tiles and runs
+# the last 256 rows as 128-row tiles in a second launch; small shapes run
+# 128-row tiles.  Forward (weight rows = N) and dX (output columns = K).
+@pytest.mark.parametrize("N,K,M", [(5120, 128, 2048), (4352, 128, 4096), (320, 512, 300)])
+def test_dense_forward_tile_widths(N, K, M):
+    r = 16
+    d = _case(N, K, M, r, seed=N + 2 * K + M, ab_std=0.2)
+    print(f"[dense widths] fwd N{N} K{K} M{M}", flush=True)
+    q = ops.quantize(bits_to_torch(d["W"]))
+    X = bits_to_torch(d["X"])
+    U = ops.lora_down(X, bits_to_torch(d["A"]))
+    Y = ops.bf16_fwd(ops.dequant(q), X, U, bits_to_torch(d["B"]), d["alpha"])
+    torch.cuda.synchronize()
+    assert_close(torch_to_f64(Y), _oracle(d)[1], f"Y N{N} K{K} M{M}")
+
+
+@pytest.mark.parametrize("N,K,M", [(128, 5120, 2048), (128, 4352, 4096)])
+def test_dense_dx_tile_widths(N, K, M):
+    test_dense_dx_matches_oracle(N, K, M, 16)
