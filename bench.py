@@ -319,7 +319,9 @@ def optimizer_study(L, r, dev, reps=5):
     """The AdamW step over every LoRA value of the layer set (one flat fp32
     buffer each for p, g, m, v and a bf16 copy; 30 bytes per value), with the
     moments on the device and, as a paged optimizer's CPU-resident states,
-    in pinned host memory."""
+    in pinned host memory; then the paged optimizer (qlora_paged_adamw) on
+    the 14 adapter tensors with its moments in a pinned host backing store,
+    at a device budget that holds them all and at a quarter of that."""
     import torch
     from bit_quantized_finetuning_nf4_amd import ops
     n = sum(r * (o["N"] + o["K"]) for o in L)
@@ -343,6 +345,27 @@ def optimizer_study(L, r, dev, reps=5):
         ms = a.elapsed_time(b) / reps
         res[f"{where}_moments"] = {"ms": ms, "gbps": 30 * n / (ms * 1e-3) / 1e9}
         del m, v
+    # paged: the adapters of the set as separate tensors (A and B per linear)
+    sizes = [r * o["K"] for o in L] + [o["N"] * r for o in L]
+    ps = [torch.randn(k, device=dev) * 1e-2 for k in sizes]
+    gs = [torch.randn(k, device=dev) * 1e-3 for k in sizes]
+    bs = [torch.empty(k, dtype=torch.bfloat16, device=dev) for k in sizes]
+    state = sum(2 * (-(-4 * k // 256) * 256) for k in sizes)
+    copy_stream = torch.cuda.Stream()
+    paged = {"tensors": len(sizes), "moment_bytes": state}
+    for name, budget in (("all_resident", state), ("quarter_budget", state // 4)):
+        opt = ops.PagedAdamW(ps, gs, budget, p_bf16=bs, copy_stream=copy_stream)
+        opt.step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            opt.step()
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / reps
+        paged[name] = {"budget_bytes": budget, "layout": opt.layout, "ms_per_step": ms}
+        del opt
+    res["paged"] = paged
+    del ps, gs, bs
     return res
 
 

@@ -27,7 +27,9 @@ EXPORTS = [
     "qlora_linear_fwd", "qlora_linear_bwd", "qlora_gemv", "qlora_gemv_prepare", "qlora_gemv_run",
     "qlora_lora_down", "qlora_lora_dy_b", "qlora_lora_grads", "qlora_nf4_fwd", "qlora_nf4_dx",
     "qlora_linear_fwd_noalloc", "qlora_bf16_fwd", "qlora_dequant_t", "qlora_bf16_dx",
+    "qlora_paged_layout_of", "qlora_paged_adamw",
 ]
+QLORA_PAGED_LOAD, QLORA_PAGED_STORE = 1, 2
 
 # QLORA_STATIC_SCRATCH_BYTES: scratch array of qlora_linear_fwd_noalloc per device
 STATIC_SCRATCH_BYTES = 32 << 20
@@ -62,6 +64,26 @@ class GemvJobDesc(ctypes.Structure):
 class GemvPlanDesc(ctypes.Structure):
     """qlora_gemv_plan: filled by qlora_gemv_prepare, read by qlora_gemv_run."""
     _fields_ = [("priv", ctypes.c_uint64 * 16)]
+
+
+class PagedTensorDesc(ctypes.Structure):
+    _fields_ = [
+        ("p", ctypes.c_void_p),
+        ("p_bf16", ctypes.c_void_p),
+        ("grad", ctypes.c_void_p),
+        ("m", ctypes.c_void_p),
+        ("v", ctypes.c_void_p),
+        ("n", ctypes.c_int64),
+    ]
+
+
+class PagedLayoutDesc(ctypes.Structure):
+    _fields_ = [
+        ("resident", ctypes.c_int32),
+        ("resident_bytes", ctypes.c_size_t),
+        ("chunk", ctypes.c_size_t),
+        ("staging_bytes", ctypes.c_size_t),
+    ]
 
 
 class QloraError(RuntimeError):
@@ -109,6 +131,11 @@ def lib():
     L.qlora_dequant.argtypes = [W, vp, vp]
     L.qlora_dequant_t.restype = ctypes.c_int
     L.qlora_dequant_t.argtypes = [W, vp, vp]
+    L.qlora_paged_layout_of.restype = ctypes.c_int
+    L.qlora_paged_layout_of.argtypes = [ctypes.POINTER(PagedTensorDesc), i32, sz, ctypes.POINTER(PagedLayoutDesc)]
+    L.qlora_paged_adamw.restype = ctypes.c_int
+    L.qlora_paged_adamw.argtypes = [ctypes.POINTER(PagedTensorDesc), i32, vp, sz, f32, f32, f32, f32, f32, i32, i32,
+                                    vp, vp]
     L.qlora_codebook_levels.restype = ctypes.c_int
     L.qlora_codebook_levels.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_float)]
     L.qlora_adamw.restype = ctypes.c_int

@@ -346,6 +346,40 @@ qlora_status qlora_adamw(float* p, uint16_t* p_bf16, const float* grad, float* m
                                  (hipStream_t)stream));
 }
 
+qlora_status qlora_paged_layout_of(const qlora_paged_tensor* t, int32_t ntensors, size_t dev_bytes,
+                                   qlora_paged_layout* out) {
+  if (!t || !out) return QLORA_E_NULL;
+  if (ntensors <= 0) return QLORA_E_SHAPE;
+  for (int i = 0; i < ntensors; ++i)
+    if (t[i].n <= 0 || t[i].n > ((int64_t)1 << 40)) return QLORA_E_SHAPE;
+  return paged_plan(t, ntensors, dev_bytes, out) ? QLORA_OK : QLORA_E_WORKSPACE;
+}
+
+qlora_status qlora_paged_adamw(const qlora_paged_tensor* t, int32_t ntensors, void* dev_ws, size_t dev_bytes,
+                               float lr, float beta1, float beta2, float eps, float weight_decay, int32_t step,
+                               int32_t flags, void* stream, void* copy_stream) {
+  if (!t) return QLORA_E_NULL;
+  if (ntensors <= 0 || step < 1) return QLORA_E_SHAPE;
+  if (flags & ~(QLORA_PAGED_LOAD | QLORA_PAGED_STORE)) return QLORA_E_UNSUPPORTED;
+  if (!(beta1 >= 0.0f && beta1 < 1.0f) || !(beta2 >= 0.0f && beta2 < 1.0f) || !(eps > 0.0f) ||
+      !std::isfinite(lr) || !std::isfinite(weight_decay))
+    return QLORA_E_SHAPE;
+  for (int i = 0; i < ntensors; ++i) {
+    const qlora_paged_tensor& x = t[i];
+    if (!x.p || !x.grad || !x.m || !x.v) return QLORA_E_NULL;
+    if (!aligned16(x.p) || !aligned16(x.grad) || !aligned16(x.m) || !aligned16(x.v) ||
+        (x.p_bf16 && !aligned16(x.p_bf16)))
+      return QLORA_E_ALIGN;
+    if (x.n <= 0 || x.n > ((int64_t)1 << 40)) return QLORA_E_SHAPE;
+  }
+  qlora_paged_layout L;
+  if (!paged_plan(t, ntensors, dev_bytes, &L)) return QLORA_E_WORKSPACE;
+  if (!dev_ws) return QLORA_E_NULL;
+  if (reinterpret_cast<uintptr_t>(dev_ws) & 255u) return QLORA_E_ALIGN;
+  return hip_status(paged_adamw(t, ntensors, static_cast<char*>(dev_ws), L, lr, beta1, beta2, eps, weight_decay,
+                                step, flags, (hipStream_t)stream, (hipStream_t)copy_stream));
+}
+
 qlora_status qlora_quantize(const uint16_t* W, const qlora_nf4_weight* q, void* stream) {
   qlora_status st = check_weight(q);
   if (st != QLORA_OK) return st;

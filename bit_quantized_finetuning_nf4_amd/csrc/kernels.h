@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "../../include/qlora.h"
+
 namespace qlora {
 
 typedef uint16_t bf16_t;
@@ -61,6 +63,12 @@ hipError_t launch_gtx(const bf16_t* G, const bf16_t* X, int64_t M, int64_t K, in
                       float* dA, float scale, hipStream_t st);
 hipError_t launch_dytu(const bf16_t* dY, const bf16_t* U, int64_t M, int64_t N, int r, float* part,
                        float* dB, float scale, hipStream_t st);
+
+// The paged optimizer's layout and step (paged.hip).
+bool paged_plan(const qlora_paged_tensor* t, int nt, size_t dev_bytes, qlora_paged_layout* L);
+hipError_t paged_adamw(const qlora_paged_tensor* t, int nt, char* ws, const qlora_paged_layout& L, float lr,
+                       float b1, float b2, float eps, float wd, int step, int flags, hipStream_t st,
+                       hipStream_t copy_stream);
 
 // Batch-1 decode.
 struct GemvJob {

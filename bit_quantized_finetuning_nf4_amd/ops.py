@@ -12,7 +12,7 @@ from typing import Optional, Sequence
 import torch
 
 from . import _lib
-from ._lib import GemvJobDesc, GemvPlanDesc, Nf4WeightDesc, check, lib
+from ._lib import GemvJobDesc, GemvPlanDesc, Nf4WeightDesc, PagedLayoutDesc, PagedTensorDesc, check, lib
 
 BLOCKSIZE = 64
 GROUP_BLOCKS = 256
@@ -439,3 +439,53 @@ def adamw(p: torch.Tensor, grad: torch.Tensor, m: torch.Tensor, v: torch.Tensor,
     check(lib().qlora_adamw(p.data_ptr(), None if p_bf16 is None else p_bf16.data_ptr(), grad.data_ptr(),
                             m.data_ptr(), v.data_ptr(), n, lr, beta1, beta2, eps, weight_decay, step, _stream()),
           "qlora_adamw")
+
+
+class PagedAdamW:
+    """AdamW with the moments in a pinned host backing store, paged through a
+    device buffer of `budget_bytes` (qlora_paged_adamw).  params / grads:
+    lists of fp32 device tensors (grads refilled by the caller before each
+    step); p_bf16: optional matching bf16 device tensors.  The host moments
+    are allocated pinned here, zero; step() runs one update on the current
+    stream, with the host <-> device copies on copy_stream (a torch Stream)."""
+
+    def __init__(self, params, grads, budget_bytes, p_bf16=None, lr=1e-4, beta1=0.9, beta2=0.999, eps=1e-8,
+                 weight_decay=0.0, copy_stream=None):
+        n = len(params)
+        self.params, self.grads = list(params), list(grads)
+        self.p_bf16 = list(p_bf16) if p_bf16 is not None else [None] * n
+        for i in range(n):
+            p, g = self.params[i], self.grads[i]
+            if p.dtype != torch.float32 or g.dtype != torch.float32 or not p.is_cuda or not g.is_cuda:
+                raise ValueError("params and grads must be float32 GPU tensors")
+            if not p.is_contiguous() or not g.is_contiguous() or p.numel() != g.numel():
+                raise ValueError("params and grads must be contiguous and of equal size")
+            if self.p_bf16[i] is not None:
+                _need(self.p_bf16[i], torch.bfloat16, "p_bf16")
+        self.m = [torch.zeros(p.numel(), dtype=torch.float32, pin_memory=True) for p in self.params]
+        self.v = [torch.zeros(p.numel(), dtype=torch.float32, pin_memory=True) for p in self.params]
+        self.descs = (PagedTensorDesc * n)()
+        for i in range(n):
+            pb = self.p_bf16[i]
+            self.descs[i] = PagedTensorDesc(self.params[i].data_ptr(), None if pb is None else pb.data_ptr(),
+                                            self.grads[i].data_ptr(), self.m[i].data_ptr(), self.v[i].data_ptr(),
+                                            self.params[i].numel())
+        self.n = n
+        lay = PagedLayoutDesc()
+        check(lib().qlora_paged_layout_of(self.descs, n, int(budget_bytes), ctypes.byref(lay)), "qlora_paged_layout_of")
+        self.layout = dict(resident=lay.resident, resident_bytes=lay.resident_bytes, chunk=lay.chunk,
+                           staging_bytes=lay.staging_bytes)
+        self.budget = int(budget_bytes)
+        self.ws = torch.empty(max(self.budget, 256), dtype=torch.uint8, device=self.params[0].device)
+        self.hp = (lr, beta1, beta2, eps, weight_decay)
+        self.copy_stream = copy_stream
+        self.t = 0
+
+    def step(self, store=False):
+        """One update; store=True also writes the resident moments back to the host."""
+        self.t += 1
+        flags = (_lib.QLORA_PAGED_LOAD if self.t == 1 else 0) | (_lib.QLORA_PAGED_STORE if store else 0)
+        cs = None if self.copy_stream is None else ctypes.c_void_p(self.copy_stream.cuda_stream)
+        check(lib().qlora_paged_adamw(self.descs, self.n, ctypes.c_void_p(self.ws.data_ptr()), self.budget,
+                                      *[float(x) for x in self.hp], self.t, flags, _stream(), cs),
+              "qlora_paged_adamw")

@@ -186,6 +186,61 @@ qlora_status qlora_adamw(float* p, uint16_t* p_bf16, const float* grad, float* m
                          float lr, float beta1, float beta2, float eps, float weight_decay, int32_t step,
                          void* stream);
 
+/* ---- The paged optimizer ------------------------------------------------
+ * The pages' paged optimizers (glossary "Definition": they manage memory
+ * spikes; deepfa.ir "3. Paged Optimizers": states move between GPU and CPU
+ * memory).  The moments of every tensor live in a pinned host backing store
+ * (hipHostMalloc or torch pin_memory; pageable memory works but serializes
+ * the copies); the step pages them through a device buffer of the caller's
+ * size:
+ *   - when every tensor's moments fit, all are resident in the buffer;
+ *   - otherwise two staging slots of `chunk` values are carved first and the
+ *     leading tensors whose moments fit the rest are resident; the others
+ *     are copied host -> device chunk by chunk on copy_stream, updated on
+ *     stream, and copied back, each chunk's copy overlapping the update of
+ *     the one before (events order the streams; a NULL copy_stream, or the
+ *     compute stream itself, runs everything in order on `stream`).
+ * Resident moments stay in the buffer between calls: pass QLORA_PAGED_LOAD
+ * on the first step (and after changing the buffer) to fill them from the
+ * backing store, QLORA_PAGED_STORE to write them back after the step.  The
+ * layout depends only on the tensor sizes and dev_bytes. */
+typedef struct {
+  float* p;              /* device [n] fp32 master values, updated in place */
+  uint16_t* p_bf16;      /* device [n] bf16 copy of p (nullable)             */
+  const float* grad;     /* device [n] fp32 gradient                         */
+  float* m;              /* host [n] backing store of the first moment       */
+  float* v;              /* host [n] backing store of the second moment      */
+  int64_t n;
+} qlora_paged_tensor;
+
+typedef struct {
+  int32_t resident;      /* leading tensors whose moments stay on the device */
+  size_t resident_bytes; /* their share of the buffer                        */
+  size_t chunk;          /* values per staging slot (0: nothing is paged)    */
+  size_t staging_bytes;  /* the two slots' share of the buffer               */
+} qlora_paged_layout;
+
+#define QLORA_PAGED_LOAD 1
+#define QLORA_PAGED_STORE 2
+
+/* Host only: the layout qlora_paged_adamw uses for these tensors and a
+ * dev_bytes buffer.  A staging slot holds chunk = min(4M, dev_bytes / 32)
+ * values rounded down to a multiple of 64, so the slots take at most half
+ * the buffer; QLORA_E_WORKSPACE when not every state fits and dev_bytes is
+ * below 2 KiB. */
+qlora_status qlora_paged_layout_of(const qlora_paged_tensor* t, int32_t ntensors, size_t dev_bytes,
+                                   qlora_paged_layout* out);
+
+/* One AdamW step (the update of qlora_adamw) on every tensor, with its
+ * moments paged as above.  dev_ws: device buffer of dev_bytes, 256-byte
+ * aligned.  step >= 1; flags: QLORA_PAGED_LOAD | QLORA_PAGED_STORE.  Every
+ * p, grad, p_bf16 16-byte aligned, n >= 1.  Errors as qlora_adamw, and
+ * QLORA_E_WORKSPACE as qlora_paged_layout_of.  The call creates and releases
+ * a few HIP events; it allocates no memory. */
+qlora_status qlora_paged_adamw(const qlora_paged_tensor* t, int32_t ntensors, void* dev_ws, size_t dev_bytes,
+                               float lr, float beta1, float beta2, float eps, float weight_decay, int32_t step,
+                               int32_t flags, void* stream, void* copy_stream);
+
 /* The 16 fp32 levels of a codebook, ascending, as the device tables hold
  * them.  QLORA_E_NULL for a NULL out, QLORA_E_UNSUPPORTED for an unknown
  * codebook. */

@@ -241,3 +241,43 @@ def test_adamw_rejects_bad_arguments_on_the_host(L):
     assert a(p=ctypes.c_void_p(4100)) == 2 and a(pb=ctypes.c_void_p(4098)) == 2
     assert a(n=0) == 3 and a(t=0) == 3 and a(b1=1.0) == 3 and a(b2=-0.1) == 3 and a(eps=0.0) == 3
     assert a(lr=float("nan")) == 3 and a(wd=float("inf")) == 3
+
+
+def _paged(L, sizes, budget):
+    from bit_quantized_finetuning_nf4_amd._lib import PagedLayoutDesc, PagedTensorDesc
+    descs = (PagedTensorDesc * len(sizes))()
+    for i, n in enumerate(sizes):
+        descs[i] = PagedTensorDesc(4096, None, 4096, 4096, 4096, n)   # never dereferenced
+    lay = PagedLayoutDesc()
+    st = L.qlora_paged_layout_of(descs, len(sizes), budget, ctypes.byref(lay))
+    return st, lay
+
+
+def test_paged_optimizer_layout_policy(L):
+    """The paging policy is host arithmetic: everything resident when the
+    moments fit; otherwise two staging slots and the longest prefix of
+    tensors whose moments fit the rest, never more than the budget."""
+    sizes = [4096, 5, 64, 700, 300000, 1000003]
+    state = lambda n: 2 * (-(-4 * n // 256) * 256)            # m and v, 256-byte aligned each
+    total = sum(state(n) for n in sizes)
+    st, lay = _paged(L, sizes, total)
+    assert st == 0 and lay.resident == len(sizes) and lay.chunk == 0 and lay.staging_bytes == 0
+    for budget in (total - 1, total // 2, 1 << 20, 65536, 2048):
+        st, lay = _paged(L, sizes, budget)
+        assert st == 0, budget
+        assert 64 <= lay.chunk <= (4 << 20) and lay.chunk % 64 == 0
+        assert lay.staging_bytes == 2 * state(lay.chunk)
+        assert lay.staging_bytes + lay.resident_bytes <= budget
+        assert lay.resident_bytes == sum(state(n) for n in sizes[:lay.resident])
+        if lay.resident < len(sizes):   # the prefix is as long as the budget allows
+            assert lay.staging_bytes + lay.resident_bytes + state(sizes[lay.resident]) > budget
+    assert _paged(L, sizes, 2047)[0] == 5                      # not even two minimal slots
+    assert _paged(L, [0], 1 << 20)[0] == 3
+    fake = ctypes.c_void_p(4096)
+    from bit_quantized_finetuning_nf4_amd._lib import PagedTensorDesc
+    d = (PagedTensorDesc * 1)(PagedTensorDesc(4096, None, 4096, 4096, 4096, 1000))
+    assert L.qlora_paged_adamw(d, 1, fake, 1 << 20, 1e-3, 0.9, 0.999, 1e-8, 0.0, 0, 0, None, None) == 3   # step 0
+    assert L.qlora_paged_adamw(d, 1, fake, 1 << 20, 1e-3, 1.0, 0.999, 1e-8, 0.0, 1, 0, None, None) == 3   # beta1 1
+    assert L.qlora_paged_adamw(d, 1, ctypes.c_void_p(4096 + 16), 1 << 20, 1e-3, 0.9, 0.999, 1e-8, 0.0, 1, 0, None,
+                               None) == 2                                                            # ws alignment
+    assert L.qlora_paged_adamw(d, 1, fake, 512, 1e-3, 0.9, 0.999, 1e-8, 0.0, 1, 0, None, None) in (0, 5)

@@ -75,3 +75,63 @@ def test_adamw_states_in_pinned_host_memory():
     torch.cuda.synchronize()
     for a, b in zip(dev, host):
         assert torch.equal(a.cpu().view(torch.int32), b.view(torch.int32))
+
+
+# The paged optimizer: moments in pinned host memory, paged through a device
+# buffer.  Tensors of several sizes (the leading small ones become resident
+# under a partial budget, the large one is paged in chunks); three steps with
+# new gradients each; budgets that hold everything, about half, and 64 KiB
+# (one resident tensor, every other chunk paged); copies on a second stream
+# or in order on the compute stream.  The update must be bit-identical to
+# qlora_adamw on device-resident moments (the same arithmetic per value), and
+# within the fp64 oracle's tolerance.
+PAGED_SIZES = [4096, 5, 64, 700, 300_000, 1_000_003]
+
+
+@pytest.mark.parametrize("budget", ["all", "half", "64k"])
+@pytest.mark.parametrize("two_streams", [True, False])
+def test_paged_adamw_matches_resident_adamw(budget, two_streams):
+    print(f"[paged adamw] budget={budget} two_streams={two_streams}", flush=True)
+    rng = np.random.default_rng(11)
+    total = sum(2 * (-(-4 * n // 256) * 256) for n in PAGED_SIZES)
+    nbytes = {"all": total, "half": total // 2, "64k": 65536}[budget]
+    p0 = [rng.standard_normal(n).astype(np.float32) for n in PAGED_SIZES]
+    grads = [[(rng.standard_normal(n) * 10.0 ** rng.integers(-4, 0)).astype(np.float32) for n in PAGED_SIZES]
+             for _ in range(3)]
+    # reference: qlora_adamw with the moments on the device
+    rp = [torch.from_numpy(a).cuda() for a in p0]
+    rm = [torch.zeros(n, device="cuda") for n in PAGED_SIZES]
+    rv = [torch.zeros(n, device="cuda") for n in PAGED_SIZES]
+    rb = [torch.empty(n, dtype=torch.bfloat16, device="cuda") for n in PAGED_SIZES]
+    # paged
+    pp = [torch.from_numpy(a).cuda() for a in p0]
+    pg = [torch.empty(n, device="cuda") for n in PAGED_SIZES]
+    pb = [torch.empty(n, dtype=torch.bfloat16, device="cuda") for n in PAGED_SIZES]
+    opt = ops.PagedAdamW(pp, pg, nbytes, p_bf16=pb, copy_stream=torch.cuda.Stream() if two_streams else None, **HP)
+    lay = opt.layout
+    if budget == "all":
+        assert lay["resident"] == len(PAGED_SIZES) and lay["chunk"] == 0
+    elif budget == "half":
+        assert 0 < lay["resident"] < len(PAGED_SIZES) and lay["chunk"] > 0
+    else:
+        assert lay["resident"] == 1 and 0 < lay["chunk"] < 300_000
+    ref = [a.astype(np.float64) for a in p0]
+    om = [np.zeros(n) for n in PAGED_SIZES]
+    ov = [np.zeros(n) for n in PAGED_SIZES]
+    for t in range(3):
+        for i, g in enumerate(grads[t]):
+            gd = torch.from_numpy(g).cuda()
+            pg[i].copy_(gd)
+            ops.adamw(rp[i], gd, rm[i], rv[i], t + 1, p_bf16=rb[i], **HP)
+            ref[i], om[i], ov[i] = oracle.adamw_step(ref[i], g.astype(np.float64), om[i], ov[i], HP32["lr"],
+                                                     HP32["beta1"], HP32["beta2"], HP32["eps"],
+                                                     HP32["weight_decay"], t + 1)
+        opt.step(store=(t == 2))
+    torch.cuda.synchronize()
+    for i, n in enumerate(PAGED_SIZES):
+        assert torch.equal(pp[i].view(torch.int32), rp[i].view(torch.int32)), f"p of tensor {i} (n={n})"
+        assert torch.equal(pb[i].view(torch.int16), rb[i].view(torch.int16)), f"bf16 copy of tensor {i}"
+        assert torch.equal(opt.m[i].view(torch.int32), rm[i].cpu().view(torch.int32)), f"m of tensor {i}"
+        assert torch.equal(opt.v[i].view(torch.int32), rv[i].cpu().view(torch.int32)), f"v of tensor {i}"
+        _close(pp[i].cpu().numpy(), ref[i], f"p tensor {i} vs oracle", np.max(np.abs(ref[i])))
+        _close(opt.m[i].numpy(), om[i], f"m tensor {i} vs oracle", np.max(np.abs(om[i])))
