@@ -35,6 +35,7 @@ import numpy as np
 from .bf16 import bf16_bits_to_f32, f32_to_bf16_bits
 from .nf4 import nf4_levels, q8_levels
 from .codebooks import levels as codebook_levels, zero_code
+from .secondlevel import levels as absmax_levels
 
 BLOCKSIZE = 64
 GROUP_BLOCKS = 256
@@ -75,13 +76,14 @@ def storage_sizes(numel):
     return (numel + 1) // 2, nb, 4 * ng
 
 
-def quantize(w_bits, codebook="nf4"):
+def quantize(w_bits, codebook="nf4", absmax_format="linear"):
     """Quantize bf16 weights (uint16 bit patterns, row-major, any shape).
 
     Returns (codes uint8 [ceil(n/2)], absmax_q uint8 [nb], s2 float32 [ng]).
     ``codebook`` selects the 4-bit levels: "nf4" (the method's), or "fp4"
     and "int4" (the formats the pages compare it with; readings R15, R16 in
-    codebooks.py), all quantized the same way.
+    codebooks.py), all quantized the same way.  ``absmax_format`` selects the
+    second-level code: "linear" (R9) or "fp8" (R19, secondlevel.py).
     """
     lv = codebook_levels(codebook)
     w = bf16_bits_to_f32(np.asarray(w_bits).ravel())
@@ -118,11 +120,11 @@ def quantize(w_bits, codebook="nf4"):
     gz = s2_per_block > 0
     if np.any(gz):
         y = (absmax[gz] / s2_per_block[gz]).astype(np.float32)
-        absmax_q[gz] = q8_encode(y)
+        absmax_q[gz] = _nearest_index(y, absmax_levels(absmax_format))
     return packed, absmax_q, s2
 
 
-def dequant(codes, absmax_q, s2, numel, codebook="nf4"):
+def dequant(codes, absmax_q, s2, numel, codebook="nf4", absmax_format="linear"):
     """Dequantize to bf16 bit patterns (uint16, flat, `numel` elements)."""
     codes = np.asarray(codes, dtype=np.uint8)
     el = np.empty(2 * codes.size, dtype=np.uint8)
@@ -131,7 +133,7 @@ def dequant(codes, absmax_q, s2, numel, codebook="nf4"):
     el = el[:numel]
     blk = np.arange(numel) // BLOCKSIZE
     grp = blk // GROUP_BLOCKS
-    q8 = q8_levels()
+    q8 = absmax_levels(absmax_format)
     lv = codebook_levels(codebook)
     t = (q8[np.asarray(absmax_q)[blk]] * np.asarray(s2, dtype=np.float32)[grp]).astype(np.float32)
     w = (lv[el] * t).astype(np.float32)
