@@ -285,9 +285,11 @@ def cpu_baseline(lin, M, r, alpha, dev_tensors, min_seconds=10.0, max_reps=20):
 
 
 def codebook_study(L, dev, q_bytes, reps=5):
-    """Quantize the layer set with each 4-bit codebook (HBM rate, same bytes
-    as NF4) and the relative RMS error of its dequantized q weight: the
-    pages' comparison of NF4 with FP4 and Int4, on the synthetic weights."""
+    """Quantize the layer set with each 4-bit codebook and each second-level
+    format of the block constants (HBM rate, same bytes as NF4 with the
+    linear code) and the relative RMS error of its dequantized q weight: the
+    pages' comparison of NF4 with FP4 and Int4, and the linear against the
+    FP8 second level, on the synthetic weights."""
     import torch
     from bit_quantized_finetuning_nf4_amd import ops
     qs = [ops.QuantizedWeight.empty(o["N"], o["K"], dev) for o in L]
@@ -295,22 +297,22 @@ def codebook_study(L, dev, q_bytes, reps=5):
     back = torch.empty_like(W0)
     ref = W0.double()
     res = {}
-    for cb in ("nf4", "fp4", "int4"):
+    for cb, fmt in (("nf4", "linear"), ("fp4", "linear"), ("int4", "linear"), ("nf4", "fp8")):
         for o, q in zip(L, qs):
-            ops.quantize(o["W"], out=q, codebook=cb)
+            ops.quantize(o["W"], out=q, codebook=cb, absmax_format=fmt)
         torch.cuda.synchronize()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
         for _ in range(reps):
             for o, q in zip(L, qs):
-                ops.quantize(o["W"], out=q, codebook=cb)
+                ops.quantize(o["W"], out=q, codebook=cb, absmax_format=fmt)
         b.record()
         torch.cuda.synchronize()
         ms = a.elapsed_time(b) / reps
         ops.dequant(qs[0], out=back)
         err = ((back.double() - ref).pow(2).mean().sqrt() / ref.pow(2).mean().sqrt()).item()
-        res[cb] = {"quantize_ms": ms, "quantize_gbps": q_bytes / (ms * 1e-3) / 1e9,
-                   f"rel_rmse_{L[0]['name']}": err}
+        res[cb if fmt == "linear" else f"{cb}_fp8_absmax"] = {
+            "quantize_ms": ms, "quantize_gbps": q_bytes / (ms * 1e-3) / 1e9, f"rel_rmse_{L[0]['name']}": err}
     del qs, back, ref
     return res
 

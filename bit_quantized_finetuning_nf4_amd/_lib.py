@@ -45,6 +45,7 @@ class Nf4WeightDesc(ctypes.Structure):
         ("absmax_q", ctypes.c_void_p),
         ("group_scale", ctypes.c_void_p),
         ("codebook", ctypes.c_int32),
+        ("absmax_format", ctypes.c_int32),
     ]
 
 

@@ -62,6 +62,7 @@ qlora_status check_weight(const qlora_nf4_weight* q) {
   if (q->blocksize != 64 || q->group_blocks != 256) return QLORA_E_UNSUPPORTED;
   if (q->codebook != QLORA_CODEBOOK_NF4 && q->codebook != QLORA_CODEBOOK_FP4 && q->codebook != QLORA_CODEBOOK_INT4)
     return QLORA_E_UNSUPPORTED;
+  if (q->absmax_format != QLORA_ABSMAX_LINEAR8 && q->absmax_format != QLORA_ABSMAX_FP8) return QLORA_E_UNSUPPORTED;
   if (!q->codes || !q->absmax_q || !q->group_scale) return QLORA_E_NULL;
   if (!aligned16(q->codes) || (reinterpret_cast<uintptr_t>(q->group_scale) & 3u)) return QLORA_E_ALIGN;
   return QLORA_OK;
@@ -102,7 +103,7 @@ qlora_status check_rank(int32_t r, const void* A, const void* B) {
 }
 
 Nf4View view(const qlora_nf4_weight* q) {
-  return Nf4View{q->codes, q->absmax_q, q->group_scale, q->rows, q->cols, q->codebook};
+  return Nf4View{q->codes, q->absmax_q, q->group_scale, q->rows, q->cols, q->codebook, q->absmax_format};
 }
 
 constexpr int64_t kStagedMinTokens = 1024;
@@ -239,7 +240,7 @@ qlora_status run_fwd(const qlora_nf4_weight* W, const uint16_t* X, int64_t M, co
   if (staged) {
     bf16_t* Wd = reinterpret_cast<bf16_t*>(ws_at(ws, L.wd));
     qlora_status st = hip_status(launch_dequant(W->codes, W->absmax_q, W->group_scale, W->rows * W->cols,
-                                                W->codebook, Wd, s));
+                                                W->codebook, W->absmax_format, Wd, s));
     if (st != QLORA_OK) return st;
     return hip_status(launch_bf16_fwd(Wd, W->rows, W->cols, X, M, U, B, false, r, sc, Y, s));
   }
@@ -389,7 +390,8 @@ qlora_status qlora_quantize(const uint16_t* W, const qlora_nf4_weight* q, void* 
   const int64_t n = q->rows * q->cols;
   if ((n + 16383) / 16384 > 0x7FFFFFFF) return QLORA_E_SHAPE;
   return hip_status(
-      launch_quantize(W, n, q->codes, q->absmax_q, q->group_scale, q->codebook, (hipStream_t)stream));
+      launch_quantize(W, n, q->codes, q->absmax_q, q->group_scale, q->codebook, q->absmax_format,
+                      (hipStream_t)stream));
 }
 
 qlora_status qlora_dequant(const qlora_nf4_weight* q, uint16_t* W_out, void* stream) {
@@ -401,7 +403,8 @@ qlora_status qlora_dequant(const qlora_nf4_weight* q, uint16_t* W_out, void* str
   const int64_t n = q->rows * q->cols;
   if ((n + 63) / 64 / 64 > 0x7FFFFFFF) return QLORA_E_SHAPE;   // the launch's workgroup count
   return hip_status(
-      launch_dequant(q->codes, q->absmax_q, q->group_scale, n, q->codebook, W_out, (hipStream_t)stream));
+      launch_dequant(q->codes, q->absmax_q, q->group_scale, n, q->codebook, q->absmax_format, W_out,
+                     (hipStream_t)stream));
 }
 
 qlora_status qlora_dequant_t(const qlora_nf4_weight* q, uint16_t* Wt_out, void* stream) {
@@ -411,7 +414,8 @@ qlora_status qlora_dequant_t(const qlora_nf4_weight* q, uint16_t* Wt_out, void* 
   if (!aligned16(Wt_out)) return QLORA_E_ALIGN;
   if (q->cols % 64 != 0 || q->rows % 8 != 0) return QLORA_E_UNSUPPORTED;
   if (q->cols / 64 > 0x7FFFFFFF || (q->rows + 63) / 64 > 65535) return QLORA_E_UNSUPPORTED;
-  return hip_status(launch_dequant_t(q->codes, q->absmax_q, q->group_scale, q->rows, q->cols, q->codebook, Wt_out,
+  return hip_status(launch_dequant_t(q->codes, q->absmax_q, q->group_scale, q->rows, q->cols, q->codebook,
+                                     q->absmax_format, Wt_out,
                                      (hipStream_t)stream));
 }
 
@@ -471,7 +475,8 @@ qlora_status qlora_linear_bwd(const qlora_nf4_weight* W, const uint16_t* X, cons
   auto run_dx = [&](const bf16_t* G, float sc) -> qlora_status {
     if (!staged) return hip_status(launch_dx(v, dY, M, G, r > 0 ? A : nullptr, r, sc, dX, s));
     bf16_t* WdT = reinterpret_cast<bf16_t*>(ws_at(ws, L.wdt));
-    qlora_status st2 = hip_status(launch_dequant_t(W->codes, W->absmax_q, W->group_scale, N, K, W->codebook, WdT, s));
+    qlora_status st2 = hip_status(
+        launch_dequant_t(W->codes, W->absmax_q, W->group_scale, N, K, W->codebook, W->absmax_format, WdT, s));
     if (st2 != QLORA_OK) return st2;
     return hip_status(launch_bf16_fwd(WdT, K, N, dY, M, G, r > 0 ? A : nullptr, true, r, sc, dX, s));
   };
@@ -617,8 +622,10 @@ qlora_status qlora_gemv_prepare(const qlora_gemv_job* jobs, int32_t njobs, void*
     if (J.m < 0) return QLORA_E_SHAPE;
     if (J.m > kMaxGemvTokens) return QLORA_E_UNSUPPORTED;
     max_m = std::max(max_m, J.m);
-    // one codebook per call: the kernel builds its decode table once
-    if (J.W->codebook != jobs[0].W->codebook) return QLORA_E_UNSUPPORTED;
+    // one codebook and second-level format per call: the kernel builds its
+    // decode tables once
+    if (J.W->codebook != jobs[0].W->codebook || J.W->absmax_format != jobs[0].W->absmax_format)
+      return QLORA_E_UNSUPPORTED;
     if (J.W->cols % 64 != 0 || J.W->cols > kMaxGemvCols || J.W->rows > 0x7FFFFFFF) return QLORA_E_UNSUPPORTED;
     // codes addressed with 32-bit byte offsets, including the prefetch of
     // one row's worth of blocks past the last row
@@ -655,7 +662,8 @@ qlora_status qlora_gemv_prepare(const qlora_gemv_job* jobs, int32_t njobs, void*
   if (ws_bytes < u_bytes || ws_bytes - u_bytes < table_bytes) return QLORA_E_WORKSPACE;
   GemvLaunch L{};
   qlora_status st = hip_status(
-      gemv_prepare(buf.data(), njobs, jobs[0].W->codebook, ws_at(ws, u_bytes), table_bytes, &L, (hipStream_t)stream));
+      gemv_prepare(buf.data(), njobs, jobs[0].W->codebook | (jobs[0].W->absmax_format << 8), ws_at(ws, u_bytes),
+                   table_bytes, &L, (hipStream_t)stream));
   if (st != QLORA_OK) return st;
   static_assert(sizeof(GemvLaunch) + sizeof(uint64_t) <= sizeof(qlora_gemv_plan), "plan storage");
   std::memset(plan, 0, sizeof(*plan));

@@ -187,8 +187,27 @@ __device__ __forceinline__ void dequant8x2_pairs(uint32_t c0, uint32_t c1, const
   }
 }
 
-// Block scale t = RN32(Q8[q] * s2).
-__device__ __forceinline__ float block_scale(uint32_t q, float s2) { return q8_value(q) * s2; }
+// Second-level formats of the block constants (the values of
+// qlora_absmax_format): the linear code Q8 above, or FP8 E4M3 (sign 0, four
+// exponent bits with bias 7, three mantissa bits, largest finite value 448)
+// divided by 448: Q[q] = RN32(e4m3(q) / 448), q = 0..126.  e4m3(q) is
+// (8 + m) 2^(e - 10) (exponent field e > 0) or m 2^-9 (e = 0), exact in fp64;
+// the product with RN64(1/448) is within 2^-52 relative of the quotient,
+// which is either exact in fp32 (8 + m = 14) or has the period-3 binary
+// expansion of a seventh and so lies at least about 2^-27 relative from
+// every fp32 rounding boundary: rounding the product gives RN32(e4m3 / 448).
+constexpr int kAbsLinear = 0, kAbsFp8 = 1;
+__device__ __forceinline__ float fp8_value(uint32_t q) {
+  const uint32_t e = (q >> 3) & 15u, m = q & 7u;
+  const double v = e ? (double)(8u + m) * (double)(1u << e) * (1.0 / 1024.0) : (double)m * (1.0 / 512.0);
+  return (float)(v * (1.0 / 448.0));
+}
+__device__ __forceinline__ float absmax_value(uint32_t q, int fmt) {
+  return fmt == kAbsFp8 ? fp8_value(q) : q8_value(q);
+}
+
+// Block scale t = RN32(Q[q] * s2) for the second-level format fmt.
+__device__ __forceinline__ float block_scale(uint32_t q, float s2, int fmt) { return absmax_value(q, fmt) * s2; }
 
 // ---------------------------------------------------------------------------
 // LDS tiles: rows of 64 bf16 (128 B = 8 chunks of 16 B); chunk c of row r is

@@ -99,6 +99,7 @@ struct FwdR {
   uint32_t ablk0[2];      // block index of (row, block 0)
   int nsub, nblk, w;
   int crow[2];            // code-chunk byte offset of the lane's 8-byte piece in row i
+  int absfmt;             // second-level format of the block constants
 };
 
 __device__ __forceinline__ void fwdr_dma_x(char* smem, const FwdR& f, int stage, int slot) {
@@ -211,10 +212,10 @@ __device__ __forceinline__ float level_times(int i, float t) {
   return l == 0u ? 0.0f : l == 0x3F800000u ? t : u2f(l) * t;
 }
 template <int CB, int K>
-__device__ __forceinline__ void tb_chunk(TbState& b, const Scale& sc, Nf4Table& T) {
+__device__ __forceinline__ void tb_chunk(TbState& b, const Scale& sc, Nf4Table& T, int fmt) {
   auto pair = [&](int i) { b.p[i] = pack_bf16x2(level_times<CB>(2 * i, b.t), level_times<CB>(2 * i + 1, b.t)); };
   if constexpr (K == 0) {
-    b.t = block_scale(sc.q, sc.s2);
+    b.t = block_scale(sc.q, sc.s2, fmt);
     pair(0);
   } else if constexpr (K < 4) {
     pair(2 * K - 1);
@@ -292,7 +293,7 @@ __device__ __forceinline__ void fwdr_slot(char* smem, const FwdR& f, int s, f32x
     if constexpr (X < 6) {
       const bool hi = (threadIdx.x & 32) != 0;
       const Scale mine{hi ? sc[SL][1].q : sc[SL][0].q, hi ? sc[SL][1].s2 : sc[SL][0].s2};
-      tb_chunk<CB, X>(tb, mine, tb.T);
+      tb_chunk<CB, X>(tb, mine, tb.T, f.absfmt);
     } else if constexpr (X == 6) {
       // lanes 0..31 hold row 0's table and lanes 32..63 row 1's: swapping the
       // upper half of one copy with the lower half of another gives each row's
@@ -382,6 +383,7 @@ __global__ __launch_bounds__(kThreads, 1) void nf4_fwd_r_kernel(Nf4View W, const
   }
   f.gs = W.group_scale;
   f.nsub = (int)(K >> 5);
+  f.absfmt = W.absfmt;
   f.nblk = (int)(K >> 6);
   // token fragment offsets: lane (lr, h) reads chunk 2h + kk of token row lr (+ 32 j)
   const int fo0 = spos(lr, 2 * h), fo1 = spos(lr, 2 * h + 1);
@@ -413,7 +415,7 @@ __global__ __launch_bounds__(kThreads, 1) void nf4_fwd_r_kernel(Nf4View W, const
   FragsR F;
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    T[i] = make_table<CB>(block_scale(sc[0][i].q, sc[0][i].s2));
+    T[i] = make_table<CB>(block_scale(sc[0][i].q, sc[0][i].s2, f.absfmt));
     const uint2 c = fwdr_codes(smem, f, i, 0);
     F.a0[i] = deq_frag(c.x, T[i]);
     F.a1[i] = deq_frag(c.y, T[i]);
@@ -549,6 +551,7 @@ struct Fwd8 {
   uint32_t ablk0;
   int nsub, nblk, w;
   int crow;               // byte offset of the lane's 8 code bytes in a chunk buffer (stage half 0)
+  int absfmt;             // second-level format of the block constants
 };
 
 // Token DMA instruction q of wave w fills tile rows 16 ((16 / WAVES) w + q) .. +15.
@@ -594,7 +597,7 @@ __device__ __forceinline__ void fwd8_slot(char* smem, const Fwd8& f, int s, f32x
   // VALU chunks
   if constexpr (kOdd) {
     constexpr int SL = ((U8 + 1) >> 1) & 3;
-    if constexpr (X < 6) tb_chunk<CB, X>(tb, sc[SL], T);
+    if constexpr (X < 6) tb_chunk<CB, X>(tb, sc[SL], T, f.absfmt);
     else if constexpr (X < 11) dq_chunk<X - 6>(dq, c.y, T, n1);
     else dq_chunk<X - 11>(dq, c.x, T, a0);
   } else {
@@ -670,6 +673,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void nf4_fwd_n32_kernel(Nf4View W, c
   f.w = __builtin_amdgcn_readfirstlane(t >> 6);
   __builtin_assume(f.w >= 0 && f.w < WAVES);
   f.nsub = (int)(K >> 5);
+  f.absfmt = W.absfmt;
   f.nblk = (int)(K >> 6);
   f.xr = make_rsrc(X, (uint32_t)(M * K * 2));
   f.cr = make_rsrc(W.codes, (uint32_t)(N * K / 2));
@@ -714,7 +718,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void nf4_fwd_n32_kernel(Nf4View W, c
     for (int q = 0; q < 16 / WAVES; ++q) fwd8_dma_x<WAVES>(smem, f, q, st, st);
   QLORA_WAIT(0, 0);
   __builtin_amdgcn_s_barrier();
-  Nf4Table T = make_table<CB>(block_scale(sc[0].q, sc[0].s2));
+  Nf4Table T = make_table<CB>(block_scale(sc[0].q, sc[0].s2, f.absfmt));
   bf16x8_t a0, a1;
   {
     const uint2 c0 = fwd8_codes(smem, f, 0);
@@ -812,6 +816,7 @@ struct Dx {
   uint32_t cstride, astride;  // per-stage strides (32 rows)
   uint32_t ablk, kb;          // block index at stage 0, K / 64
   int nsub;
+  int absfmt;             // second-level format of the block constants
 };
 struct Codes {
   uint4 c;
@@ -939,7 +944,7 @@ __device__ __forceinline__ void dx_slot(char* smem, const Dx& d, int s, f32x16_t
   {
     const Codes& pc = cs[(U + 2) & 3];
     if constexpr (X < 6) {
-      tb_chunk<CB, X>(tb, Scale{pc.q, pc.s2}, T);
+      tb_chunk<CB, X>(tb, Scale{pc.q, pc.s2}, T, d.absfmt);
     } else if constexpr (X < 26) {
       constexpr int dd = (X - 6) / 5, kc = (X - 6) % 5;
       // chunk dd ^ flip: a select between two fixed words (a runtime index
@@ -1007,6 +1012,7 @@ __global__ __launch_bounds__(kThreads, 1) void nf4_dx_kernel(Nf4View W, const bf
     d.astride = (uint32_t)(32 * (K >> 6));
   }
   d.nsub = (int)((N + 31) >> 5);
+  d.absfmt = W.absfmt;
   // A fragment i: as a source lane of its 16-lane group (g, sl) a lane reads
   // row 8 (g >> 1) + (sl >> 2) and columns 128 wc + 32 i + 16 (g & 1) + 4 (sl & 3)
   int ao[4];
@@ -1032,7 +1038,7 @@ __global__ __launch_bounds__(kThreads, 1) void nf4_dx_kernel(Nf4View W, const bf
   dx_load_y(ys[1], d, 2);   // stored by substep 0
 #pragma unroll
   for (int p = 0; p < 2; ++p) {
-    const Nf4Table T = make_table<CB>(block_scale(cs[p].q, cs[p].s2));
+    const Nf4Table T = make_table<CB>(block_scale(cs[p].q, cs[p].s2, d.absfmt));
     dx_produce(smem, cs[p], T, p, 0);
     dx_produce(smem, cs[p], T, p, 1);
   }
@@ -1214,7 +1220,7 @@ __device__ __forceinline__ void dxh_slot(char* smem, const Dx& d, int s, f32x16_
   {
     const CodesH& pc = cs[(U + 2) & 3];
     if constexpr (X < 6) {
-      tb_chunk<CB, X>(tb, Scale{pc.q, pc.s2}, T);
+      tb_chunk<CB, X>(tb, Scale{pc.q, pc.s2}, T, d.absfmt);
     } else {
       constexpr int dd = (X - 6) / 5, kc = (X - 6) % 5;
       // decode dd is chunk dd ^ flip: a select between the two code words as
@@ -1286,6 +1292,7 @@ __global__ __launch_bounds__(kThreads, 1) void nf4_dx_half_kernel(Nf4View W, con
     d.astride = (uint32_t)(32 * (K >> 6));
   }
   d.nsub = (int)((N + 31) >> 5);
+  d.absfmt = W.absfmt;
   // A fragment i: as a source lane of its 16-lane group (g, sl) a lane reads
   // row 8 (g >> 1) + (sl >> 2) and columns 64 wc + 32 i + 16 (g & 1) + 4 (sl & 3)
   int ao[2];
@@ -1316,7 +1323,7 @@ __global__ __launch_bounds__(kThreads, 1) void nf4_dx_half_kernel(Nf4View W, con
   dx_load_y(ys[1], d, 2);   // stored by substep 0
 #pragma unroll
   for (int p = 0; p < 2; ++p) {
-    const Nf4Table T = make_table<CB>(block_scale(cs[p].q, cs[p].s2));
+    const Nf4Table T = make_table<CB>(block_scale(cs[p].q, cs[p].s2, d.absfmt));
     const int flip = (t >> 2) & 1;
     const uint32_t cx = cs[p].c.x, cy = cs[p].c.y;
 #pragma unroll

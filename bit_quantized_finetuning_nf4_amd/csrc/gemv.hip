@@ -201,7 +201,8 @@ __global__ __launch_bounds__(kDownThreads) void lora_down_kernel(const GemvJob* 
 template <bool kPair, int CB>
 __global__ __launch_bounds__(kGvThreads) void nf4_gemv_kernel(const GemvJob* __restrict__ jobs,
                                                               const int4* __restrict__ segs,
-                                                              const int* __restrict__ range, int max_steps) {
+                                                              const int* __restrict__ range, int max_steps,
+                                                              int absfmt) {
   extern __shared__ __align__(16) uint8_t lds_dyn[];  // addressed from 0 (see lds_ld32)
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int c = lane & 15, g = lane >> 4, r = c >> 2, p = c & 3;
@@ -214,7 +215,7 @@ __global__ __launch_bounds__(kGvThreads) void nf4_gemv_kernel(const GemvJob* __r
 #pragma unroll
     for (int i = 0; i < 16; ++i)
       lds_st32((uint32_t)(w + 16 * i) * 256u + 4u * lane, lo | (level_bf16<CB>(i) << 16));
-    if (tid < 256) lds_st32(kQ8Off + 4u * tid, __builtin_bit_cast(uint32_t, q8_value((uint32_t)tid)));
+    if (tid < 256) lds_st32(kQ8Off + 4u * tid, __builtin_bit_cast(uint32_t, absmax_value((uint32_t)tid, absfmt)));
     if (tid < kZeroBytes / 16) lds_st128(kZeroOff + 16u * tid, make_uint4(0u, 0u, 0u, 0u));
   }
 
@@ -449,7 +450,7 @@ __global__ __launch_bounds__(kGvThreads) void nf4_gemv_kernel(const GemvJob* __r
 template <bool kQuad, int CB>
 __global__ __launch_bounds__(kBtThreads) void nf4_gemv_batch_kernel(const GemvJob* __restrict__ jobs,
                                                                     const int4* __restrict__ segs,
-                                                                    const int* __restrict__ range) {
+                                                                    const int* __restrict__ range, int absfmt) {
   extern __shared__ __align__(16) uint8_t lds_dyn[];  // addressed from 0 (see lds_ld32)
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int c = lane & 15, g = lane >> 4;
@@ -463,7 +464,7 @@ __global__ __launch_bounds__(kBtThreads) void nf4_gemv_batch_kernel(const GemvJo
       const int e = wu + kBtWaves * i;
       lds_st32((uint32_t)e * 256u + 4u * lane, level_bf16<CB>(e & 15) | (level_bf16<CB>(e >> 4) << 16));
     }
-    if (tid < 256) lds_st32(kQ8Off + 4u * tid, __builtin_bit_cast(uint32_t, q8_value((uint32_t)tid)));
+    if (tid < 256) lds_st32(kQ8Off + 4u * tid, __builtin_bit_cast(uint32_t, absmax_value((uint32_t)tid, absfmt)));
     if (tid < kBtZeroBytes / 16) lds_st128(kBtZeroOff + 16u * tid, make_uint4(0u, 0u, 0u, 0u));
   }
 
@@ -790,7 +791,7 @@ int device_cus() { return std::min(device_cu_count(), kMaxGvGroups); }
 
 template <bool kPair, int CB>
 hipError_t launch_main(const GemvJob* djobs, const int4* segs, const int* range, int groups, int max_steps,
-                       hipStream_t st) {
+                       int absfmt, hipStream_t st) {
   if (groups <= 0) return hipSuccess;
   // The kernel addresses its LDS from 0, which holds only while the
   // compiler has given it no static LDS.
@@ -803,12 +804,13 @@ hipError_t launch_main(const GemvJob* djobs, const int4* segs, const int* range,
                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((nf4_gemv_kernel<kPair, CB>), dim3(groups), dim3(kGvThreads), lds, st, djobs, segs, range,
-                     max_steps);
+                     max_steps, absfmt);
   return hipGetLastError();
 }
 
 template <bool kQuad, int CB>
-hipError_t launch_batch(const GemvJob* djobs, const int4* segs, const int* range, int groups, hipStream_t st) {
+hipError_t launch_batch(const GemvJob* djobs, const int4* segs, const int* range, int groups, int absfmt,
+                        hipStream_t st) {
   if (groups <= 0) return hipSuccess;
   hipFuncAttributes fa{};
   hipError_t e = hipFuncGetAttributes(&fa, reinterpret_cast<const void*>(&nf4_gemv_batch_kernel<kQuad, CB>));
@@ -818,25 +820,26 @@ hipError_t launch_batch(const GemvJob* djobs, const int4* segs, const int* range
                           hipFuncAttributeMaxDynamicSharedMemorySize, kBtLds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((nf4_gemv_batch_kernel<kQuad, CB>), dim3(groups), dim3(kBtThreads), kBtLds, st, djobs, segs,
-                     range);
+                     range, absfmt);
   return hipGetLastError();
 }
 
 // The four launches of the GEMV (see job_kind), for codebook CB.
 template <int CB>
-hipError_t launch_all(const GemvLaunch& L, const GemvJob* djobs, const uint8_t* dev, hipStream_t st) {
+hipError_t launch_all(const GemvLaunch& L, const GemvJob* djobs, const uint8_t* dev, int absfmt, hipStream_t st) {
   hipError_t e = launch_main<true, CB>(djobs, reinterpret_cast<const int4*>(dev + L.seg_off[0]),
                                        reinterpret_cast<const int*>(dev + L.rng_off[0]), L.groups[0],
-                                       L.max_steps[0], st);
+                                       L.max_steps[0], absfmt, st);
   if (e != hipSuccess) return e;
   e = launch_main<false, CB>(djobs, reinterpret_cast<const int4*>(dev + L.seg_off[1]),
-                             reinterpret_cast<const int*>(dev + L.rng_off[1]), L.groups[1], L.max_steps[1], st);
+                             reinterpret_cast<const int*>(dev + L.rng_off[1]), L.groups[1], L.max_steps[1], absfmt,
+                             st);
   if (e != hipSuccess) return e;
   e = launch_batch<true, CB>(djobs, reinterpret_cast<const int4*>(dev + L.seg_off[2]),
-                             reinterpret_cast<const int*>(dev + L.rng_off[2]), L.groups[2], st);
+                             reinterpret_cast<const int*>(dev + L.rng_off[2]), L.groups[2], absfmt, st);
   if (e != hipSuccess) return e;
   return launch_batch<false, CB>(djobs, reinterpret_cast<const int4*>(dev + L.seg_off[3]),
-                                 reinterpret_cast<const int*>(dev + L.rng_off[3]), L.groups[3], st);
+                                 reinterpret_cast<const int*>(dev + L.rng_off[3]), L.groups[3], absfmt, st);
 }
 
 }  // namespace
@@ -903,9 +906,10 @@ hipError_t gemv_run(const GemvLaunch& L, hipStream_t st) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (L.codebook == kCbFp4) return launch_all<kCbFp4>(L, djobs, dev, st);
-  if (L.codebook == kCbInt4) return launch_all<kCbInt4>(L, djobs, dev, st);
-  return launch_all<kCbNf4>(L, djobs, dev, st);
+  const int cb = L.codebook & 0xFF, absfmt = L.codebook >> 8;
+  if (cb == kCbFp4) return launch_all<kCbFp4>(L, djobs, dev, absfmt, st);
+  if (cb == kCbInt4) return launch_all<kCbInt4>(L, djobs, dev, absfmt, st);
+  return launch_all<kCbNf4>(L, djobs, dev, absfmt, st);
 }
 
 }  // namespace qlora

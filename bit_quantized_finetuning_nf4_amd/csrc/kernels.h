@@ -17,6 +17,7 @@ struct Nf4View {
   int64_t N;  // rows
   int64_t K;  // cols, K % 64 == 0 on the GEMM/GEMV paths
   int codebook;  // 0 NF4, 1 FP4, 2 Int4 (the values of qlora_codebook)
+  int absfmt;    // second-level format (the values of qlora_absmax_format)
 };
 
 // Compute units of the current device (256 if the query fails).
@@ -28,13 +29,13 @@ hipError_t launch_adamw(float* p, bf16_t* p_bf16, const float* g, float* m, floa
                         float beta1, float beta2, float eps, float weight_decay, int step, hipStream_t st);
 
 hipError_t launch_quantize(const bf16_t* W, int64_t numel, uint8_t* codes, uint8_t* absmax_q,
-                           float* group_scale, int codebook, hipStream_t s);
+                           float* group_scale, int codebook, int absfmt, hipStream_t s);
 hipError_t launch_dequant(const uint8_t* codes, const uint8_t* absmax_q, const float* group_scale,
-                          int64_t numel, int codebook, bf16_t* out, hipStream_t s);
+                          int64_t numel, int codebook, int absfmt, bf16_t* out, hipStream_t s);
 
 // WdT [K x N] = deq(W)^T (bf16) for W [N x K], K % 64 == 0, N < 65536 * 64.
 hipError_t launch_dequant_t(const uint8_t* codes, const uint8_t* absmax_q, const float* group_scale, int64_t N,
-                            int64_t K, int codebook, bf16_t* out, hipStream_t s);
+                            int64_t K, int codebook, int absfmt, bf16_t* out, hipStream_t s);
 
 // Y = X deq(W)^T + s * U * B^T  (U already holds X A^T in bf16; r may be 0)
 hipError_t launch_fwd(const Nf4View& W, const bf16_t* X, int64_t M, const bf16_t* U, const bf16_t* B,
@@ -100,7 +101,7 @@ struct GemvLaunch {
   uint64_t seg_off[kGvKinds], rng_off[kGvKinds], down_off;
   int32_t groups[kGvKinds], max_steps[kGvKinds];
   int32_t n_down;
-  int32_t codebook;  // shared by every job of the call
+  int32_t codebook;  // shared by every job of the call: 4-bit codebook | second-level format << 8
 };
 hipError_t gemv_prepare(const GemvJob* jobs, int njobs, int codebook, void* table, size_t table_bytes,
                         GemvLaunch* out, hipStream_t st);

@@ -72,6 +72,20 @@ __device__ __forceinline__ uint32_t q8_code(float y) {
   return (uint32_t)best;
 }
 
+// Nearest FP8 second-level value to y in [0, 1], ties to the lower index:
+// the largest code whose value is <= y (a binary search over the increasing
+// 127 values), then the nearer of it and the next one by exact fp64
+// distances.
+__device__ __forceinline__ uint32_t fp8_code(float y) {
+  int lo = 0, hi = 126;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (fp8_value((uint32_t)mid) <= y) lo = mid; else hi = mid - 1;
+  }
+  if (lo < 126 && (double)fp8_value((uint32_t)lo + 1u) - (double)y < (double)y - (double)fp8_value((uint32_t)lo)) ++lo;
+  return (uint32_t)lo;
+}
+
 // One workgroup of 256 threads per group of 256 blocks.  Each lane encodes
 // 8 consecutive weights per pass; 8 lanes form one block, 32 blocks per
 // pass, 8 passes per group.  Block absmaxes go to LDS for the second level.
@@ -79,7 +93,8 @@ template <int CB>
 __global__ __launch_bounds__(256) void quantize_kernel(const bf16_t* __restrict__ W, int64_t numel,
                                                        uint8_t* __restrict__ codes,
                                                        uint8_t* __restrict__ absmax_q,
-                                                       float* __restrict__ group_scale, int64_t nb) {
+                                                       float* __restrict__ group_scale, int64_t nb,
+                                                       int absfmt) {
   __shared__ float amax[kGroupBlocks];
   __shared__ float red[8];
   __shared__ float thr[16];
@@ -176,7 +191,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(const bf16_t* __restrict_
     uint32_t q = 0;
     if (s2 > 0.0f) {
       const float y = (float)((double)amax[tid] / (double)s2);  // RN32(a / s2)
-      q = q8_code(y);
+      q = absfmt == kAbsFp8 ? fp8_code(y) : q8_code(y);
     }
     absmax_q[b] = (uint8_t)q;
   }
@@ -191,12 +206,12 @@ template <int CB>
 __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict__ codes,
                                                       const uint8_t* __restrict__ absmax_q,
                                                       const float* __restrict__ group_scale,
-                                                      int64_t numel, int64_t nb,
+                                                      int64_t numel, int64_t nb, int absfmt,
                                                       bf16_t* __restrict__ out) {
   const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t b = g >> 2;
   if (b >= nb) return;
-  const float t = block_scale(absmax_q[b], group_scale[b / kGroupBlocks]);
+  const float t = block_scale(absmax_q[b], group_scale[b / kGroupBlocks], absfmt);
   const Nf4Table T = make_table<CB>(t);
   const int64_t e0 = (g << 4);   // first of the lane's 16 weights
   if (e0 + 16 <= numel) {
@@ -238,7 +253,7 @@ template <int CB>
 __global__ __launch_bounds__(256) void dequant_t_kernel(const uint8_t* __restrict__ codes,
                                                         const uint8_t* __restrict__ absmax_q,
                                                         const float* __restrict__ group_scale, int64_t N,
-                                                        int64_t K, bf16_t* __restrict__ out) {
+                                                        int64_t K, int absfmt, bf16_t* __restrict__ out) {
   __shared__ uint32_t tile[256 * kTrStride];
   const int t = threadIdx.x, rp = t & 31, cg = t >> 5;
   const int64_t n0 = (int64_t)blockIdx.y * 64, k0 = (int64_t)blockIdx.x * 256;
@@ -251,7 +266,7 @@ __global__ __launch_bounds__(256) void dequant_t_kernel(const uint8_t* __restric
       const int64_t row = n0 + 2 * rp + i;
       if (row < N) {
         const int64_t b = (row * K + kc) >> 6;
-        T[i] = make_table<CB>(block_scale(absmax_q[b], group_scale[b / kGroupBlocks]));
+        T[i] = make_table<CB>(block_scale(absmax_q[b], group_scale[b / kGroupBlocks], absfmt));
         c[i] = *reinterpret_cast<const uint4*>(codes + ((row * K + kc) >> 1));
       } else {
         T[i] = make_table<CB>(0.0f);
@@ -295,31 +310,31 @@ int device_cu_count() {
 }
 
 hipError_t launch_quantize(const bf16_t* W, int64_t numel, uint8_t* codes, uint8_t* absmax_q,
-                           float* group_scale, int codebook, hipStream_t s) {
+                           float* group_scale, int codebook, int absfmt, hipStream_t s) {
   const int64_t nb = (numel + kBlock - 1) / kBlock;
   const int64_t ng = (nb + kGroupBlocks - 1) / kGroupBlocks;
   auto* fn = codebook == kCbFp4 ? &quantize_kernel<kCbFp4> : codebook == kCbInt4 ? &quantize_kernel<kCbInt4>
                                                                                   : &quantize_kernel<kCbNf4>;
-  hipLaunchKernelGGL(fn, dim3((unsigned)ng), dim3(256), 0, s, W, numel, codes, absmax_q, group_scale, nb);
+  hipLaunchKernelGGL(fn, dim3((unsigned)ng), dim3(256), 0, s, W, numel, codes, absmax_q, group_scale, nb, absfmt);
   return hipGetLastError();
 }
 
 hipError_t launch_dequant(const uint8_t* codes, const uint8_t* absmax_q, const float* group_scale,
-                          int64_t numel, int codebook, bf16_t* out, hipStream_t s) {
+                          int64_t numel, int codebook, int absfmt, bf16_t* out, hipStream_t s) {
   const int64_t nb = (numel + kBlock - 1) / kBlock;
   auto* fn = codebook == kCbFp4 ? &dequant_kernel<kCbFp4> : codebook == kCbInt4 ? &dequant_kernel<kCbInt4>
                                                                                 : &dequant_kernel<kCbNf4>;
   hipLaunchKernelGGL(fn, dim3((unsigned)((4 * nb + 255) / 256)), dim3(256), 0, s, codes, absmax_q, group_scale, numel,
-                     nb, out);
+                     nb, absfmt, out);
   return hipGetLastError();
 }
 
 hipError_t launch_dequant_t(const uint8_t* codes, const uint8_t* absmax_q, const float* group_scale, int64_t N,
-                            int64_t K, int codebook, bf16_t* out, hipStream_t s) {
+                            int64_t K, int codebook, int absfmt, bf16_t* out, hipStream_t s) {
   auto* fn = codebook == kCbFp4 ? &dequant_t_kernel<kCbFp4> : codebook == kCbInt4 ? &dequant_t_kernel<kCbInt4>
                                                                                   : &dequant_t_kernel<kCbNf4>;
   hipLaunchKernelGGL(fn, dim3((unsigned)((K + 255) / 256), (unsigned)((N + 63) / 64)), dim3(256), 0, s, codes,
-                     absmax_q, group_scale, N, K, out);
+                     absmax_q, group_scale, N, K, absfmt, out);
   return hipGetLastError();
 }
 

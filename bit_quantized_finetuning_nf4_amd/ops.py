@@ -56,6 +56,14 @@ def nf4_levels():
 
 # qlora_codebook values
 CODEBOOKS = {"nf4": 0, "fp4": 1, "int4": 2}
+# qlora_absmax_format values (second-level code of the block constants)
+ABSMAX_FORMATS = {"linear": 0, "fp8": 1}
+
+
+def _absfmt(name):
+    if name not in ABSMAX_FORMATS:
+        raise ValueError(f"unknown absmax format {name!r}: one of {sorted(ABSMAX_FORMATS)}")
+    return ABSMAX_FORMATS[name]
 
 
 def _codebook(name):
@@ -92,34 +100,39 @@ class QuantizedWeight:
     absmax_q: torch.Tensor     # uint8 [nb]
     group_scale: torch.Tensor  # float32 [ng]
     codebook: str = "nf4"      # "nf4", "fp4" or "int4"
+    absmax_format: str = "linear"   # "linear" or "fp8"
 
     def desc(self) -> Nf4WeightDesc:
         return Nf4WeightDesc(self.rows, self.cols, BLOCKSIZE, GROUP_BLOCKS, self.codes.data_ptr(),
-                             self.absmax_q.data_ptr(), self.group_scale.data_ptr(), _codebook(self.codebook))
+                             self.absmax_q.data_ptr(), self.group_scale.data_ptr(), _codebook(self.codebook),
+                             _absfmt(self.absmax_format))
 
     @staticmethod
-    def empty(rows, cols, device, codebook="nf4"):
+    def empty(rows, cols, device, codebook="nf4", absmax_format="linear"):
         c, a, s = sizes(rows, cols)
         return QuantizedWeight(rows, cols,
                                torch.empty(c, dtype=torch.uint8, device=device),
                                torch.empty(a, dtype=torch.uint8, device=device),
-                               torch.empty(s // 4, dtype=torch.float32, device=device), codebook)
+                               torch.empty(s // 4, dtype=torch.float32, device=device), codebook, absmax_format)
 
     def nbytes(self):
         return self.codes.numel() + self.absmax_q.numel() + 4 * self.group_scale.numel()
 
 
 def quantize(W: torch.Tensor, out: Optional[QuantizedWeight] = None,
-             codebook: Optional[str] = None) -> QuantizedWeight:
+             codebook: Optional[str] = None, absmax_format: Optional[str] = None) -> QuantizedWeight:
     """bf16 W [rows x cols] -> 4-bit codes + 8-bit absmax codes + fp32 group
-    scales.  The codebook is the one named, else out's, else NF4; the
-    result records it."""
+    scales.  The codebook and the second-level format are the ones named,
+    else out's, else NF4 and linear; the result records them."""
     _need(W, torch.bfloat16, "W")
     rows, cols = (W.shape[0], W.shape[1]) if W.dim() == 2 else (1, W.numel())
     q = out if out is not None else QuantizedWeight.empty(rows, cols, W.device)
     if codebook is not None:
         _codebook(codebook)
         q.codebook = codebook
+    if absmax_format is not None:
+        _absfmt(absmax_format)
+        q.absmax_format = absmax_format
     d = q.desc()
     check(lib().qlora_quantize(_ptr(W), ctypes.byref(d), _stream()), "qlora_quantize")
     return q

@@ -22,7 +22,8 @@
  *     j, element 2j+1 the high nibble.  A code indexes the ascending NF4
  *     table (0 = -1, 7 = 0, 15 = +1).
  *   - absmax_q: one byte per block, the index of the nearest level of
- *     Q8[k] = RN32(k/255) to RN32(absmax_b / s2_g) (ties to the lower index).
+ *     Q8[k] = RN32(k/255) (or of the FP8 levels, see qlora_absmax_format) to
+ *     RN32(absmax_b / s2_g) (ties to the lower index).
  *   - group_scale: one fp32 per group, s2_g = largest block absmax.
  *   - Dequantized value: RNE_bf16(RN32(L[c] * RN32(Q8[q] * s2))).
  *
@@ -68,8 +69,9 @@ typedef enum {
                               or cols >= 2^24 where a LoRA side product
                               runs over them, r outside [0,128] or
                               r % 8 != 0, too many jobs,
-                              an unknown codebook, GEMV jobs of different
-                              codebooks in one call */
+                              an unknown codebook or second-level format,
+                              GEMV jobs of different codebooks or formats
+                              in one call */
   QLORA_E_WORKSPACE = 5,   /* ws_bytes smaller than qlora_workspace_bytes()  */
   QLORA_E_HIP = 6          /* a HIP launch/copy error; see qlora_last_hip_error */
 } qlora_status;
@@ -103,6 +105,22 @@ typedef enum {
   QLORA_CODEBOOK_INT4 = 2
 } qlora_codebook;
 
+/* Second-level format of the 8-bit block-constant codes (double
+ * quantization: glossary "Definition", deepfa.ir "2. Double Quantization";
+ * the pages name no format).  Both encode y = RN32(absmax_b / s2_g) as the
+ * nearest level, ties to the lower index, and decode t = RN32(Q[q] * s2):
+ *   LINEAR8: Q[k] = RN32(k / 255), k = 0..255;
+ *   FP8:     Q[k] = RN32(e4m3(k) / 448), k = 0..126, where e4m3(k) is the
+ *            value of the FP8 E4M3 bit pattern k (sign 0, 4 exponent bits
+ *            with bias 7 and subnormals, 3 mantissa bits; 448 = code 126 is
+ *            the largest finite value).  Relative rather than absolute steps:
+ *            constants far below their group's largest keep about 3 bits of
+ *            precision instead of rounding to zero. */
+typedef enum {
+  QLORA_ABSMAX_LINEAR8 = 0,
+  QLORA_ABSMAX_FP8 = 1
+} qlora_absmax_format;
+
 typedef struct {
   int64_t rows;           /* N, output features                       */
   int64_t cols;           /* K, input features                        */
@@ -112,6 +130,7 @@ typedef struct {
   uint8_t* absmax_q;
   float* group_scale;
   int32_t codebook;       /* qlora_codebook of the 4-bit codes (0 = NF4) */
+  int32_t absmax_format;  /* qlora_absmax_format of absmax_q (0 = linear) */
 } qlora_nf4_weight;
 
 /* One batch-1 decode product y = deq(W) x + (alpha/r) B (A x). */
