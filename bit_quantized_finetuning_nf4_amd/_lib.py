@@ -13,6 +13,7 @@ LIB_PATH = os.path.join(_HERE, "libqlora.so")
 QLORA_OK = 0
 QLORA_OP_FWD, QLORA_OP_BWD, QLORA_OP_GEMV, QLORA_OP_LORA = 0, 1, 2, 3
 QLORA_OP_FWD_FUSED, QLORA_OP_BWD_FUSED = 4, 5
+QLORA_OP_GROUP_FWD, QLORA_OP_GROUP_BWD = 6, 7
 
 STATUS_NAMES = {
     0: "QLORA_OK", 1: "QLORA_E_NULL", 2: "QLORA_E_ALIGN", 3: "QLORA_E_SHAPE",
@@ -27,7 +28,7 @@ EXPORTS = [
     "qlora_linear_fwd", "qlora_linear_bwd", "qlora_gemv", "qlora_gemv_prepare", "qlora_gemv_run",
     "qlora_lora_down", "qlora_lora_dy_b", "qlora_lora_grads", "qlora_nf4_fwd", "qlora_nf4_dx",
     "qlora_linear_fwd_noalloc", "qlora_bf16_fwd", "qlora_dequant_t", "qlora_bf16_dx",
-    "qlora_paged_layout_of", "qlora_paged_adamw",
+    "qlora_paged_layout_of", "qlora_paged_adamw", "qlora_group_fwd", "qlora_group_bwd",
 ]
 QLORA_PAGED_LOAD, QLORA_PAGED_STORE = 1, 2
 
@@ -167,6 +168,11 @@ def lib():
     L.qlora_bf16_dx.argtypes = [vp, i64, i64, vp, i64, vp, vp, i32, f32, vp, vp]
     L.qlora_nf4_dx.restype = ctypes.c_int
     L.qlora_nf4_dx.argtypes = [W, vp, i64, vp, vp, i32, f32, vp, vp]
+    Wg = ctypes.POINTER(Nf4WeightDesc)
+    L.qlora_group_fwd.restype = ctypes.c_int
+    L.qlora_group_fwd.argtypes = [Wg, i32, vp, i64, vp, vp, i32, f32, vp, vp, vp, sz, vp]
+    L.qlora_group_bwd.restype = ctypes.c_int
+    L.qlora_group_bwd.argtypes = [Wg, i32, vp, vp, i64, vp, vp, i32, f32, vp, vp, vp, vp, vp, sz, vp]
     _lib = L
     return L
 

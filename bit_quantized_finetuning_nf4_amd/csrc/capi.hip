@@ -166,6 +166,52 @@ size_t lora_part_bytes(int64_t M, int64_t N, int64_t K, int32_t r) {
   return align_up(p);
 }
 
+// Layer-set groups: G weights of one shape N x K read the same input, with
+// the adapters stacked (A [G r x K], B [G N x r]) and the outputs side by
+// side (Y, dY [M x G N]).  Always staged.
+//   GROUP_FWD: U bf16 [M x G r] | partials of X A^T | deq(W_g) stacked [G N x K]
+//   GROUP_BWD: G bf16 [M x G r] | U bf16 [M x G r] | partials (largest of the
+//              four products) | deq(W_g)^T side by side [K x G N] (with dX)
+constexpr int kMaxGroupRank = 256;   // G r: the largest rank tile of the side products
+
+bool group_sizes_ok(int64_t M, int64_t N, int64_t K, int32_t r, int32_t G) {
+  if (M <= 0 || N <= 0 || K <= 0 || G < 1 || r < 0 || r > kMaxRank || (int64_t)G * r > kMaxGroupRank) return false;
+  const int64_t NG = (int64_t)G * N;
+  return NG <= (int64_t)0x7FFFFFFF / K;
+}
+
+FwdLayout group_fwd_layout(int64_t M, int64_t N, int64_t K, int32_t r, int32_t G) {
+  FwdLayout L{0, 0, 0, 0};
+  const int32_t rg = G * r;
+  if (r > 0) {
+    L.part = align_up((size_t)M * rg * 2);
+    L.total = L.part + align_up(skinny_partial_bytes(M, rg, K, kXAt));
+  }
+  L.wd = L.total;
+  L.total += align_up((size_t)G * (size_t)N * (size_t)K * 2);
+  return L;
+}
+
+BwdLayout group_bwd_layout(int64_t M, int64_t N, int64_t K, int32_t r, int32_t G, bool with_dx) {
+  BwdLayout L{0, 0, 0, 0, 0};
+  const int32_t rg = G * r;
+  if (r > 0) {
+    const size_t mr = align_up((size_t)M * rg * 2);
+    L.u = mr;
+    L.part = 2 * mr;
+    size_t p = skinny_partial_bytes(M, rg, K, kXAt);
+    p = std::max(p, skinny_partial_bytes(M, rg, N, kDyB));
+    p = std::max(p, skinny_partial_bytes(rg, K, M, kGtX));
+    p = std::max(p, (size_t)G * skinny_partial_bytes(N, r, M, kDytU));
+    L.total = L.part + align_up(p);
+  }
+  if (with_dx) {
+    L.wdt = L.total;
+    L.total += align_up((size_t)G * (size_t)N * (size_t)K * 2);
+  }
+  return L;
+}
+
 qlora_status check_ws(void* ws, size_t ws_bytes, size_t need) {
   if (ws_bytes < need) return QLORA_E_WORKSPACE;
   if (need > 0 && !ws) return QLORA_E_NULL;
@@ -329,6 +375,12 @@ size_t qlora_workspace_bytes(qlora_op op, int64_t M, int64_t N, int64_t K, int32
     case QLORA_OP_LORA:
       if (M <= 0 || N <= 0 || K <= 0 || r < 0 || r > kMaxRank) return 0;
       return lora_part_bytes(M, N, K, r);
+    case QLORA_OP_GROUP_FWD:
+      if (!group_sizes_ok(M, N, K, r, njobs)) return 0;
+      return group_fwd_layout(M, N, K, r, njobs).total;
+    case QLORA_OP_GROUP_BWD:
+      if (!group_sizes_ok(M, N, K, r, njobs)) return 0;
+      return group_bwd_layout(M, N, K, r, njobs, true).total;
   }
   return 0;
 }
@@ -415,8 +467,7 @@ qlora_status qlora_dequant_t(const qlora_nf4_weight* q, uint16_t* Wt_out, void* 
   if (q->cols % 64 != 0 || q->rows % 8 != 0) return QLORA_E_UNSUPPORTED;
   if (q->cols / 64 > 0x7FFFFFFF || (q->rows + 63) / 64 > 65535) return QLORA_E_UNSUPPORTED;
   return hip_status(launch_dequant_t(q->codes, q->absmax_q, q->group_scale, q->rows, q->cols, q->codebook,
-                                     q->absmax_format, Wt_out,
-                                     (hipStream_t)stream));
+                                     q->absmax_format, Wt_out, q->rows, (hipStream_t)stream));
 }
 
 qlora_status qlora_linear_fwd(const qlora_nf4_weight* W, const uint16_t* X, int64_t M, const uint16_t* A,
@@ -476,7 +527,7 @@ qlora_status qlora_linear_bwd(const qlora_nf4_weight* W, const uint16_t* X, cons
     if (!staged) return hip_status(launch_dx(v, dY, M, G, r > 0 ? A : nullptr, r, sc, dX, s));
     bf16_t* WdT = reinterpret_cast<bf16_t*>(ws_at(ws, L.wdt));
     qlora_status st2 = hip_status(
-        launch_dequant_t(W->codes, W->absmax_q, W->group_scale, N, K, W->codebook, W->absmax_format, WdT, s));
+        launch_dequant_t(W->codes, W->absmax_q, W->group_scale, N, K, W->codebook, W->absmax_format, WdT, N, s));
     if (st2 != QLORA_OK) return st2;
     return hip_status(launch_bf16_fwd(WdT, K, N, dY, M, G, r > 0 ? A : nullptr, true, r, sc, dX, s));
   };
@@ -503,6 +554,117 @@ qlora_status qlora_linear_bwd(const qlora_nf4_weight* W, const uint16_t* X, cons
   st = hip_status(launch_gtx(G, X, M, K, r, part, dA, sc, s));
   if (st != QLORA_OK) return st;
   return hip_status(launch_dytu(dY, U, M, N, r, part, dB, sc, s));
+}
+
+namespace {
+
+// Arguments common to both group calls: G weights of one GEMM-path shape
+// N x K with N % 64 == 0, the stacked adapters, and the token count.
+qlora_status check_group(const qlora_nf4_weight* W, int32_t G, int64_t M, int32_t r, const uint16_t* A,
+                         const uint16_t* B) {
+  if (!W) return QLORA_E_NULL;
+  if (G < 1) return QLORA_E_SHAPE;
+  for (int32_t g = 0; g < G; ++g) {
+    qlora_status st = check_gemm_weight(&W[g]);
+    if (st != QLORA_OK) return st;
+    if (W[g].rows != W[0].rows || W[g].cols != W[0].cols) return QLORA_E_SHAPE;
+  }
+  qlora_status st = check_rank(r, A, B);
+  if (st != QLORA_OK) return st;
+  const int64_t N = W[0].rows, K = W[0].cols;
+  if (N % 64 != 0 || !group_sizes_ok(1, N, K, r, G)) return QLORA_E_UNSUPPORTED;
+  const int64_t NG = (int64_t)G * N;
+  if (M <= 0 || M > 0x7FFFFFFF) return QLORA_E_SHAPE;
+  if (M > (int64_t)0x7FFFFFFF / K || M > (int64_t)0x7FFFFFFF / NG) return QLORA_E_UNSUPPORTED;
+  if (r > 0 && (!skinny_cols_ok(K) || !skinny_cols_ok(NG))) return QLORA_E_UNSUPPORTED;
+  return QLORA_OK;
+}
+
+// deq(W_g) into rows g N .. of the stack, or deq(W_g)^T into columns g N ..
+qlora_status group_dequant(const qlora_nf4_weight* W, int32_t G, bool transposed, bf16_t* out, hipStream_t s) {
+  const int64_t N = W[0].rows, K = W[0].cols;
+  for (int32_t g = 0; g < G; ++g) {
+    const qlora_nf4_weight& q = W[g];
+    hipError_t e = transposed ? launch_dequant_t(q.codes, q.absmax_q, q.group_scale, N, K, q.codebook,
+                                                 q.absmax_format, out + g * N, (int64_t)G * N, s)
+                              : launch_dequant(q.codes, q.absmax_q, q.group_scale, N * K, q.codebook,
+                                               q.absmax_format, out + g * N * K, s);
+    if (e != hipSuccess) return hip_status(e);
+  }
+  return QLORA_OK;
+}
+
+}  // namespace
+
+qlora_status qlora_group_fwd(const qlora_nf4_weight* W, int32_t G, const uint16_t* X, int64_t M,
+                             const uint16_t* A, const uint16_t* B, int32_t r, float alpha, uint16_t* Y,
+                             uint16_t* U_save, void* ws, size_t ws_bytes, void* stream) {
+  qlora_status st = check_group(W, G, M, r, A, B);
+  if (st != QLORA_OK) return st;
+  if (!X || !Y) return QLORA_E_NULL;
+  if (!aligned16(X) || !aligned16(Y) || (U_save && !aligned16(U_save))) return QLORA_E_ALIGN;
+  const int64_t N = W[0].rows, K = W[0].cols;
+  const FwdLayout L = group_fwd_layout(M, N, K, r, G);
+  if ((st = check_ws(ws, ws_bytes, L.total)) != QLORA_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  const bf16_t* U = nullptr;
+  float sc = 0.0f;
+  if (r > 0) {
+    sc = (float)((double)alpha / (double)r);  // s = RN32(alpha / r)
+    bf16_t* Ud = U_save ? U_save : reinterpret_cast<bf16_t*>(ws_at(ws, L.u));
+    // every adapter's U in one pass over X: U [M x G r] = X [A_0; A_1; ..]^T
+    st = hip_status(launch_xat(X, A, M, K, G * r, reinterpret_cast<float*>(ws_at(ws, L.part)), Ud, nullptr, 1.0f, s));
+    if (st != QLORA_OK) return st;
+    U = Ud;
+  }
+  bf16_t* Wd = reinterpret_cast<bf16_t*>(ws_at(ws, L.wd));
+  if ((st = group_dequant(W, G, false, Wd, s)) != QLORA_OK) return st;
+  return hip_status(launch_bf16_group(Wd, (int64_t)G * N, K, X, M, U, G * r, B, false, r, N, sc, Y, s));
+}
+
+qlora_status qlora_group_bwd(const qlora_nf4_weight* W, int32_t G, const uint16_t* X, const uint16_t* dY,
+                             int64_t M, const uint16_t* A, const uint16_t* B, int32_t r, float alpha,
+                             const uint16_t* U_saved, uint16_t* dX, float* dA, float* dB, void* ws,
+                             size_t ws_bytes, void* stream) {
+  qlora_status st = check_group(W, G, M, r, A, B);
+  if (st != QLORA_OK) return st;
+  if (!dY) return QLORA_E_NULL;
+  if (!aligned16(dY) || (dX && !aligned16(dX)) || (U_saved && !aligned16(U_saved))) return QLORA_E_ALIGN;
+  if (r > 0) {
+    if (!dA || !dB || !X) return QLORA_E_NULL;
+    if (!aligned16(dA) || !aligned16(dB) || !aligned16(X)) return QLORA_E_ALIGN;
+  } else if (dA || dB) {
+    return QLORA_E_SHAPE;   // no adapter, no adapter gradients
+  }
+  const int64_t N = W[0].rows, K = W[0].cols, NG = (int64_t)G * N;
+  const int32_t rg = G * r;
+  const BwdLayout L = group_bwd_layout(M, N, K, r, G, dX != nullptr);
+  if ((st = check_ws(ws, ws_bytes, L.total)) != QLORA_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  // dX = sum_g dY_g deq(W_g) + s sum_g G_g A_g: one dense product contracting
+  // over the G N columns of dY, with the stacked adapters as a rank-G r tail
+  auto run_dx = [&](const bf16_t* Gm, float sc) -> qlora_status {
+    bf16_t* WdT = reinterpret_cast<bf16_t*>(ws_at(ws, L.wdt));
+    qlora_status st2 = group_dequant(W, G, true, WdT, s);
+    if (st2 != QLORA_OK) return st2;
+    return hip_status(launch_bf16_group(WdT, K, NG, dY, M, Gm, rg, r > 0 ? A : nullptr, true, rg, K, sc, dX, s));
+  };
+  if (r == 0) return dX ? run_dx(nullptr, 0.0f) : QLORA_OK;
+  const float sc = (float)((double)alpha / (double)r);
+  bf16_t* Gm = reinterpret_cast<bf16_t*>(ws_at(ws, L.g));
+  float* part = reinterpret_cast<float*>(ws_at(ws, L.part));
+  const bf16_t* U = U_saved;
+  if (!U) {
+    bf16_t* Ud = reinterpret_cast<bf16_t*>(ws_at(ws, L.u));
+    if ((st = hip_status(launch_xat(X, A, M, K, rg, part, Ud, nullptr, 1.0f, s))) != QLORA_OK) return st;
+    U = Ud;
+  }
+  // G [M x G r]: group g is dY_g B_g
+  if ((st = hip_status(launch_dyb_group(dY, NG, B, M, N, r, G, part, Gm, 1.0f, s))) != QLORA_OK) return st;
+  if (dX && (st = run_dx(Gm, sc)) != QLORA_OK) return st;
+  // dA [G r x K] = s G^T X in one pass over X; dB_g = s dY_g^T U_g
+  if ((st = hip_status(launch_gtx(Gm, X, M, K, rg, part, dA, sc, s))) != QLORA_OK) return st;
+  return hip_status(launch_dytu_group(dY, NG, U, rg, M, N, r, G, part, dB, sc, s));
 }
 
 qlora_status qlora_lora_down(const uint16_t* X, const uint16_t* A, int64_t M, int64_t K, int32_t r, uint16_t* U,

@@ -78,25 +78,28 @@ struct RowShape {
 
 template <int RP, bool QT>
 __global__ __launch_bounds__(kThreads, 1) void rskinny_kernel(const bf16_t* __restrict__ P, int64_t M, int64_t C,
-                                                              const bf16_t* __restrict__ Q, int r,
-                                                              int stages_per_split, int tiles_m,
+                                                              int64_t ldp, int64_t p_gs,
+                                                              const bf16_t* __restrict__ Q, int r, int64_t q_gs,
+                                                              int stages_per_split, int tiles_m, int ldo,
                                                               float* __restrict__ part) {
   using S = RowShape<RP, QT>;
   extern __shared__ __align__(16) char smem[];
-  const int tm = blockIdx.x % tiles_m, sp = blockIdx.x / tiles_m;
+  const int tm = blockIdx.x % tiles_m, sp = blockIdx.x / tiles_m, g = blockIdx.y;
   const int t = threadIdx.x, w = t >> 6, lane = t & 63, lr = lane & 31, h = lane >> 5;
   const int64_t m0 = (int64_t)tm * 128;
   const int nst = (int)((C + 31) / 32);
   const int s0 = sp * stages_per_split, s1 = min(nst, s0 + stages_per_split);
+  P += g * p_gs;
+  Q += g * q_gs;
   // P rows of this tile only (rows past M read as zero); Q whole
-  const rsrc_t pr = make_rsrc(P + m0 * C, (uint32_t)(min((int64_t)128, M - m0) * C * 2));
+  const rsrc_t pr = make_rsrc(P + m0 * ldp, (uint32_t)(((min((int64_t)128, M - m0) - 1) * ldp + C) * 2));
   const rsrc_t qr = make_rsrc(Q, (uint32_t)((int64_t)r * C * 2));
   uint32_t po[2], qo[S::kQDma > 0 ? S::kQDma : 1];
   int pl[2], ql[S::kQDma > 0 ? S::kQDma : 1];
 #pragma unroll
   for (int q = 0; q < 2; ++q) {   // P: instruction q of wave w fills rows 16 (2w + q) .. +15
     const int row = 16 * (2 * w + q) + (lane >> 2), ch = (lane & 3) ^ ((lane >> 4) & 3);
-    po[q] = (uint32_t)(row * C * 2 + ch * 16);
+    po[q] = (uint32_t)(row * ldp * 2 + ch * 16);
     pl[q] = 16 * (2 * w + q) * 64;
   }
 #pragma unroll
@@ -162,8 +165,9 @@ __global__ __launch_bounds__(kThreads, 1) void rskinny_kernel(const bf16_t* __re
     }
     QLORA_WAIT(0, 0);
   }
-  // D[j][m]: lane (lr, h) holds m = m0 + 32 w + lr, j = 32 f + 8 q + 4 h + 0..3
-  float* out = part + (int64_t)sp * M * r;
+  // D[j][m]: lane (lr, h) holds m = m0 + 32 w + lr, j = 32 f + 8 q + 4 h + 0..3,
+  // stored at column g r + j of the split's [M x ldo] partial
+  float* out = part + (int64_t)sp * M * ldo + (int64_t)g * r;
   const int64_t m = m0 + 32 * w + lr;
   if (m < M) {
 #pragma unroll
@@ -172,7 +176,7 @@ __global__ __launch_bounds__(kThreads, 1) void rskinny_kernel(const bf16_t* __re
       for (int q = 0; q < 4; ++q) {
         const int j = 32 * f + 8 * q + 4 * h;
         if (j < r)
-          *reinterpret_cast<float4*>(out + m * r + j) =
+          *reinterpret_cast<float4*>(out + m * ldo + j) =
               make_float4(acc[f][4 * q], acc[f][4 * q + 1], acc[f][4 * q + 2], acc[f][4 * q + 3]);
       }
   }
@@ -196,41 +200,45 @@ struct ColShape {
 
 template <int RP, bool DB>
 __global__ __launch_bounds__(kThreads, 1) void cskinny_kernel(const bf16_t* __restrict__ Big, int64_t M, int64_t C,
-                                                              const bf16_t* __restrict__ Sm, int r,
-                                                              int stages_per_split, int tiles_c,
+                                                              int64_t ldb, int64_t big_gs,
+                                                              const bf16_t* __restrict__ Sm, int r, int lds,
+                                                              int64_t sm_gs, int stages_per_split, int tiles_c,
                                                               float* __restrict__ part) {
   using S = ColShape<RP>;
   extern __shared__ __align__(16) char smem[];
-  const int tc = blockIdx.x % tiles_c, sp = blockIdx.x / tiles_c;
+  const int tc = blockIdx.x % tiles_c, sp = blockIdx.x / tiles_c, g = blockIdx.y;
   const int t = threadIdx.x, w = t >> 6, lane = t & 63, lr = lane & 31, h = lane >> 5;
   const int64_t c0 = (int64_t)tc * 128;
   const int nst = (int)((M + 31) / 32);
   const int s0 = sp * stages_per_split, s1 = min(nst, s0 + stages_per_split);
-  const rsrc_t br = make_rsrc(Big, (uint32_t)(M * C * 2));   // rows past M read as zero
-  const rsrc_t sr = make_rsrc(Sm, (uint32_t)(M * r * 2));
+  Big += g * big_gs;
+  Sm += g * sm_gs;
+  // rows past M read as zero
+  const rsrc_t br = make_rsrc(Big, (uint32_t)(((M - 1) * ldb + C) * 2));
+  const rsrc_t sr = make_rsrc(Sm, (uint32_t)(((M - 1) * lds + r) * 2));
   uint32_t bo[2], so[S::kSmDma];
   int bl[2], sl[S::kSmDma];
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
     int row, col;
     tr_dma_coords<256>(2 * w + q, lane, row, col);
-    bo[q] = (uint32_t)(row * C * 2 + (c0 + col) * 2);   // columns past C: never stored
+    bo[q] = (uint32_t)(row * ldb * 2 + (c0 + col) * 2);   // columns past C: never stored
     bl[q] = (2 * w + q) * 1024;
   }
 #pragma unroll
   for (int q = 0; q < S::kSmDma; ++q) {
     int row, col;
     tr_dma_coords<2 * RP>(S::kSmDma * w + q, lane, row, col);
-    so[q] = (uint32_t)(row * r * 2 + col * 2);
+    so[q] = (uint32_t)(row * lds * 2 + col * 2);   // ranks past r: never stored
     sl[q] = S::kBig + (S::kSmDma * w + q) * 1024;
   }
   auto dma = [&](int st, int slot) {
     const uint32_t ss = (uint32_t)min(st, s1 - 1);
     char* base = smem + slot * S::kStage;
 #pragma unroll
-    for (int q = 0; q < 2; ++q) dma16(br, base + bl[q], bo[q], ss * 32u * (uint32_t)C * 2u);
+    for (int q = 0; q < 2; ++q) dma16(br, base + bl[q], bo[q], ss * 32u * (uint32_t)ldb * 2u);
 #pragma unroll
-    for (int q = 0; q < S::kSmDma; ++q) dma16(sr, base + sl[q], so[q], ss * 32u * (uint32_t)r * 2u);
+    for (int q = 0; q < S::kSmDma; ++q) dma16(sr, base + sl[q], so[q], ss * 32u * (uint32_t)lds * 2u);
   };
 
   constexpr int FJ = RP / 32;
@@ -263,7 +271,8 @@ __global__ __launch_bounds__(kThreads, 1) void cskinny_kernel(const bf16_t* __re
     }
     QLORA_WAIT(0, 0);
   }
-  float* out = part + (int64_t)sp * C * r;
+  // the split's partial holds all groups' outputs, group g at g C r
+  float* out = part + ((int64_t)sp * gridDim.y + g) * C * r;
 #pragma unroll
   for (int f = 0; f < FJ; ++f)
 #pragma unroll
@@ -342,33 +351,56 @@ hipError_t reduce(const float* part, int splits, int64_t n, float scale, float* 
   return hipGetLastError();
 }
 
+// Row contraction over G groups (grid y): group g reads P + g p_gs (rows of
+// stride ldp, C columns) and Q + g q_gs, and writes columns g r .. of the
+// [M x ldo] result.
+struct RowArgs {
+  const bf16_t* P;
+  int64_t M, C, ldp, p_gs;
+  const bf16_t* Q;
+  int r;
+  int64_t q_gs;
+  int G, ldo;
+};
+
 template <int RP, bool QT>
-hipError_t run_rows(const bf16_t* P, int64_t M, int64_t C, const bf16_t* Q, int r, float* part, float scale,
-                    bf16_t* out, bf16_t* out2, hipStream_t st) {
-  const Split sp = split_for((M + 127) / 128, C, QT ? 512 : 256);
+hipError_t run_rows(const RowArgs& a, float* part, float scale, bf16_t* out, bf16_t* out2, hipStream_t st) {
+  const Split sp = split_for((a.M + 127) / 128, a.C, QT ? 512 : 256);
   auto* fn = &rskinny_kernel<RP, QT>;
   const size_t lds = (size_t)kRing * RowShape<RP, QT>::kStage;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
                                      (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(fn, dim3(sp.tiles * sp.splits), dim3(kThreads), lds, st, P, M, C, Q, r, sp.sps, sp.tiles, part);
+  hipLaunchKernelGGL(fn, dim3(sp.tiles * sp.splits, a.G), dim3(kThreads), lds, st, a.P, a.M, a.C, a.ldp, a.p_gs, a.Q,
+                     a.r, a.q_gs, sp.sps, sp.tiles, a.ldo, part);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  return reduce(part, sp.splits, M * r, scale, nullptr, out, out2, st);
+  return reduce(part, sp.splits, a.M * a.ldo, scale, nullptr, out, out2, st);
 }
 
+// Token contraction over G groups (grid y): group g reads Big + g big_gs
+// (rows of stride ldb, C columns) and Sm + g sm_gs (rows of stride lds, r
+// ranks), and writes the g-th C x r block of the result.
+struct ColArgs {
+  const bf16_t* Big;
+  int64_t M, C, ldb, big_gs;
+  const bf16_t* Sm;
+  int r, lds;
+  int64_t sm_gs;
+  int G;
+};
+
 template <int RP, bool DB>
-hipError_t run_cols(const bf16_t* Big, int64_t M, int64_t C, const bf16_t* Sm, int r, float* part, float scale,
-                    float* out, hipStream_t st) {
-  const Split sp = split_for((C + 127) / 128, M, 256);
+hipError_t run_cols(const ColArgs& a, float* part, float scale, float* out, hipStream_t st) {
+  const Split sp = split_for((a.C + 127) / 128, a.M, 256);
   auto* fn = &cskinny_kernel<RP, DB>;
   const size_t lds = (size_t)kRing * ColShape<RP>::kStage;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
                                      (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(fn, dim3(sp.tiles * sp.splits), dim3(kThreads), lds, st, Big, M, C, Sm, r, sp.sps, sp.tiles,
-                     part);
+  hipLaunchKernelGGL(fn, dim3(sp.tiles * sp.splits, a.G), dim3(kThreads), lds, st, a.Big, a.M, a.C, a.ldb,
+                     a.big_gs, a.Sm, a.r, a.lds, a.sm_gs, sp.sps, sp.tiles, part);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  return reduce(part, sp.splits, C * r, scale, out, nullptr, nullptr, st);
+  return reduce(part, sp.splits, (int64_t)a.G * a.C * a.r, scale, out, nullptr, nullptr, st);
 }
 
 }  // namespace
@@ -380,26 +412,43 @@ size_t skinny_partial_bytes(int64_t rows, int64_t cols, int64_t contraction, int
 
 hipError_t launch_xat(const bf16_t* X, const bf16_t* A, int64_t M, int64_t K, int r, float* part, bf16_t* out,
                       bf16_t* out2, float scale, hipStream_t st) {
-  if (r <= 64) return run_rows<64, false>(X, M, K, A, r, part, scale, out, out2, st);
-  return run_rows<128, false>(X, M, K, A, r, part, scale, out, out2, st);
+  const RowArgs a{X, M, K, K, 0, A, r, 0, 1, r};
+  if (r <= 64) return run_rows<64, false>(a, part, scale, out, out2, st);
+  if (r <= 128) return run_rows<128, false>(a, part, scale, out, out2, st);
+  if (r <= 192) return run_rows<192, false>(a, part, scale, out, out2, st);
+  return run_rows<256, false>(a, part, scale, out, out2, st);
+}
+
+hipError_t launch_dyb_group(const bf16_t* dY, int64_t ldy, const bf16_t* B, int64_t M, int64_t N, int r, int G,
+                            float* part, bf16_t* out, float scale, hipStream_t st) {
+  const RowArgs a{dY, M, N, ldy, N, B, r, N * r, G, G * r};
+  if (r <= 64) return run_rows<64, true>(a, part, scale, out, nullptr, st);
+  return run_rows<128, true>(a, part, scale, out, nullptr, st);
 }
 
 hipError_t launch_dyb(const bf16_t* dY, const bf16_t* B, int64_t M, int64_t N, int r, float* part, bf16_t* out,
                       float scale, hipStream_t st) {
-  if (r <= 64) return run_rows<64, true>(dY, M, N, B, r, part, scale, out, nullptr, st);
-  return run_rows<128, true>(dY, M, N, B, r, part, scale, out, nullptr, st);
+  return launch_dyb_group(dY, N, B, M, N, r, 1, part, out, scale, st);
 }
 
 hipError_t launch_gtx(const bf16_t* G, const bf16_t* X, int64_t M, int64_t K, int r, float* part, float* dA,
                       float scale, hipStream_t st) {
-  if (r <= 64) return run_cols<64, false>(X, M, K, G, r, part, scale, dA, st);
-  return run_cols<128, false>(X, M, K, G, r, part, scale, dA, st);
+  const ColArgs a{X, M, K, K, 0, G, r, r, 0, 1};
+  if (r <= 64) return run_cols<64, false>(a, part, scale, dA, st);
+  if (r <= 128) return run_cols<128, false>(a, part, scale, dA, st);
+  return run_cols<256, false>(a, part, scale, dA, st);
+}
+
+hipError_t launch_dytu_group(const bf16_t* dY, int64_t ldy, const bf16_t* U, int ldu, int64_t M, int64_t N, int r,
+                             int G, float* part, float* dB, float scale, hipStream_t st) {
+  const ColArgs a{dY, M, N, ldy, N, U, r, ldu, r, G};
+  if (r <= 64) return run_cols<64, true>(a, part, scale, dB, st);
+  return run_cols<128, true>(a, part, scale, dB, st);
 }
 
 hipError_t launch_dytu(const bf16_t* dY, const bf16_t* U, int64_t M, int64_t N, int r, float* part, float* dB,
                        float scale, hipStream_t st) {
-  if (r <= 64) return run_cols<64, true>(dY, M, N, U, r, part, scale, dB, st);
-  return run_cols<128, true>(dY, M, N, U, r, part, scale, dB, st);
+  return launch_dytu_group(dY, N, U, r, M, N, r, 1, part, dB, scale, st);
 }
 
 }  // namespace qlora

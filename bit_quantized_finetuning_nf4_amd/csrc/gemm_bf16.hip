@@ -148,16 +148,17 @@ __device__ __forceinline__ void dense_slots(const char* cur, const char* nxt, ch
 }
 
 // Weight half of the LoRA tail: B'[row0 + row, j0 + 8 c ..] into a 64-byte-row
-// tile (zero past the rank and past the last row), where B' is B [rows x r]
-// or, with b_trans, the transpose of B [r x rows] (read column-wise).
+// tile (zero past the rank, and for rows outside [lo, hi)), where B' is B
+// [rows x r] or, with b_trans, the transpose of B [r x rows] (read
+// column-wise).
 __device__ __forceinline__ void tail_rows(char* dst, const bf16_t* Bm, bool b_trans, int64_t rows, int r,
-                                          int64_t row0, int j0) {
+                                          int64_t row0, int j0, int64_t lo, int64_t hi) {
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int idx = threadIdx.x + kThreads * e;
     const int row = idx >> 2, c = idx & 3, col = j0 + 8 * c;
     uint4 v = make_uint4(0u, 0u, 0u, 0u);
-    if (col < r && row0 + row < rows) {
+    if (col < r && row0 + row >= lo && row0 + row < hi) {
       if (!b_trans) {
         v = *reinterpret_cast<const uint4*>(Bm + (row0 + row) * r + col);
       } else {
@@ -179,8 +180,8 @@ __global__ __launch_bounds__(kThreads, 1) void bf16_fwd_kernel(const bf16_t* __r
                                                                const bf16_t* __restrict__ X, int64_t M,
                                                                const bf16_t* __restrict__ U,
                                                                const bf16_t* __restrict__ Bl, int b_trans, int r,
-                                                               float s, bf16_t* __restrict__ Y, int64_t n_begin,
-                                                               int tiles_n, int tiles_m) {
+                                                               int ldu, int64_t gn, float s, bf16_t* __restrict__ Y,
+                                                               int64_t n_begin, int tiles_n, int tiles_m) {
   extern __shared__ __align__(16) char smem[];
   int tn, tm;
   map_tile_grouped(tiles_n, tiles_m, tn, tm);
@@ -251,12 +252,18 @@ __global__ __launch_bounds__(kThreads, 1) void bf16_fwd_kernel(const bf16_t* __r
   __builtin_amdgcn_s_barrier();
 
   if (r > 0) {
-    // acc += B (s U)^T over the rank, 32 at a time, through 64-byte-row tiles
+    // acc += B (s U)^T over the rank, 32 at a time, through 64-byte-row tiles.
+    // Weight rows come in groups of gn, each with its own adapter: rows of
+    // group g take columns g r .. of U (row stride ldu) and their rows of B;
+    // a tile that straddles groups runs the tail once per group, with the
+    // other groups' rows zero.
     const FragOffs fo = frag_offs(lane);
     const int am64 = wc * 32 * FI * 64, bm64 = wr * 128 * 64;
+    const int64_t g_last = (min(n0 + 64 * FI, N) - 1) / gn;
+    for (int64_t g = n0 / gn; g <= g_last; ++g)
     for (int j0 = 0; j0 < r; j0 += 32) {
-      tail_rows(smem, Bl, b_trans != 0, N, r, n0, j0);
-      tail_tokens(smem + kOp, U, M, r, m0, j0, s);
+      tail_rows(smem, Bl, b_trans != 0, N, r, n0, j0, g * gn, min((g + 1) * gn, N));
+      tail_tokens(smem + kOp, U + g * r, ldu, M, r, m0, j0, s);
       QLORA_WAIT(0, 0);
       __builtin_amdgcn_s_barrier();
 #pragma unroll
@@ -287,8 +294,8 @@ namespace {
 // N-row weight (N is every array's extent and leading dimension).
 template <int FI>
 hipError_t launch_fi(const bf16_t* Wd, int64_t N, int64_t K, const bf16_t* X, int64_t M, const bf16_t* U,
-                     const bf16_t* B, bool b_trans, int r, float s, bf16_t* Y, int64_t n_begin, int64_t n_rows,
-                     hipStream_t st) {
+                     const bf16_t* B, bool b_trans, int r, int ldu, int64_t gn, float s, bf16_t* Y, int64_t n_begin,
+                     int64_t n_rows, hipStream_t st) {
   const int tiles_n = (int)((n_rows + 64 * FI - 1) / (64 * FI));
   const int tiles_m = (int)((M + kTile - 1) / kTile);
   auto* fn = &bf16_fwd_kernel<FI>;
@@ -296,7 +303,7 @@ hipError_t launch_fi(const bf16_t* Wd, int64_t N, int64_t K, const bf16_t* X, in
                                      (int)kLdsDense);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(fn, dim3(tiles_n * tiles_m), dim3(kThreads), kLdsDense, st, Wd, N, K, X, M, U, B, (int)b_trans, r,
-                     s, Y, n_begin, tiles_n, tiles_m);
+                     ldu, gn, s, Y, n_begin, tiles_n, tiles_m);
   return hipGetLastError();
 }
 
@@ -316,12 +323,12 @@ int best_fi(int64_t rows, int64_t tiles_m, int cus) {
 }
 
 hipError_t launch_rows(int fi, const bf16_t* Wd, int64_t N, int64_t K, const bf16_t* X, int64_t M,
-                       const bf16_t* U, const bf16_t* B, bool b_trans, int r, float s, bf16_t* Y, int64_t n_begin,
-                       hipStream_t st) {
+                       const bf16_t* U, const bf16_t* B, bool b_trans, int r, int ldu, int64_t gn, float s,
+                       bf16_t* Y, int64_t n_begin, hipStream_t st) {
   const int64_t n_rows = N - n_begin;
-  if (fi == 3) return launch_fi<3>(Wd, N, K, X, M, U, B, b_trans, r, s, Y, n_begin, n_rows, st);
-  if (fi == 2) return launch_fi<2>(Wd, N, K, X, M, U, B, b_trans, r, s, Y, n_begin, n_rows, st);
-  return launch_fi<4>(Wd, N, K, X, M, U, B, b_trans, r, s, Y, n_begin, n_rows, st);
+  if (fi == 3) return launch_fi<3>(Wd, N, K, X, M, U, B, b_trans, r, ldu, gn, s, Y, n_begin, n_rows, st);
+  if (fi == 2) return launch_fi<2>(Wd, N, K, X, M, U, B, b_trans, r, ldu, gn, s, Y, n_begin, n_rows, st);
+  return launch_fi<4>(Wd, N, K, X, M, U, B, b_trans, r, ldu, gn, s, Y, n_begin, n_rows, st);
 }
 
 }  // namespace
@@ -330,8 +337,9 @@ hipError_t launch_rows(int fi, const bf16_t* Wd, int64_t N, int64_t K, const bf1
 // fills whole rounds of 256-row tiles and a remainder, whose tile width (256,
 // 192 or 128 rows) minimizes its time; a shape with fewer 256-row tiles than
 // CUs is all remainder.
-hipError_t launch_bf16_fwd(const bf16_t* Wd, int64_t N, int64_t K, const bf16_t* X, int64_t M, const bf16_t* U,
-                           const bf16_t* B, bool b_trans, int r, float s, bf16_t* Y, hipStream_t st) {
+hipError_t launch_bf16_group(const bf16_t* Wd, int64_t N, int64_t K, const bf16_t* X, int64_t M, const bf16_t* U,
+                             int ldu, const bf16_t* B, bool b_trans, int r, int64_t gn, float s, bf16_t* Y,
+                             hipStream_t st) {
   const int cus = device_cu_count();
   const int64_t tiles_m = (M + kTile - 1) / kTile;
   const int64_t tiles_n = (N + kTile - 1) / kTile;
@@ -344,12 +352,18 @@ hipError_t launch_bf16_fwd(const bf16_t* Wd, int64_t N, int64_t K, const bf16_t*
       n_split = 0;   // nothing left over, or the remainder gains nothing from narrower tiles: one launch
   }
   if (n_split > 0) {
-    hipError_t e = launch_fi<4>(Wd, N, K, X, M, U, B, b_trans, r, s, Y, 0, n_split, st);
+    hipError_t e = launch_fi<4>(Wd, N, K, X, M, U, B, b_trans, r, ldu, gn, s, Y, 0, n_split, st);
     if (e != hipSuccess) return e;
     // the remainder's tiles address rows from n_split on, in the same arrays
-    return launch_rows(best_fi(N - n_split, tiles_m, cus), Wd, N, K, X, M, U, B, b_trans, r, s, Y, n_split, st);
+    return launch_rows(best_fi(N - n_split, tiles_m, cus), Wd, N, K, X, M, U, B, b_trans, r, ldu, gn, s, Y, n_split,
+                       st);
   }
-  return launch_rows(best_fi(N, tiles_m, cus), Wd, N, K, X, M, U, B, b_trans, r, s, Y, 0, st);
+  return launch_rows(best_fi(N, tiles_m, cus), Wd, N, K, X, M, U, B, b_trans, r, ldu, gn, s, Y, 0, st);
+}
+
+hipError_t launch_bf16_fwd(const bf16_t* Wd, int64_t N, int64_t K, const bf16_t* X, int64_t M, const bf16_t* U,
+                           const bf16_t* B, bool b_trans, int r, float s, bf16_t* Y, hipStream_t st) {
+  return launch_bf16_group(Wd, N, K, X, M, U, r, B, b_trans, r, N, s, Y, st);
 }
 
 }  // namespace qlora

@@ -89,17 +89,22 @@ __device__ __forceinline__ uint4 scale16(uint4 v, float s) {
 }
 
 // Token half of the LoRA tail: (s T)[row0 + row, j0 + 8 c ..] into a
-// 64-byte-row tile (T is rows x rank, zero past the rank and the last row).
-__device__ __forceinline__ void tail_tokens(char* dst, const bf16_t* T, int64_t rows, int r, int64_t row0, int j0,
-                                            float s) {
+// 64-byte-row tile (T is rows x rank with row stride ld, zero past the rank
+// and the last row).
+__device__ __forceinline__ void tail_tokens(char* dst, const bf16_t* T, int64_t ld, int64_t rows, int r,
+                                            int64_t row0, int j0, float s) {
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int idx = threadIdx.x + kThreads * e;
     const int row = idx >> 2, c = idx & 3, col = j0 + 8 * c;
     uint4 v = make_uint4(0u, 0u, 0u, 0u);
-    if (col < r && row0 + row < rows) v = scale16(*reinterpret_cast<const uint4*>(T + (row0 + row) * r + col), s);
+    if (col < r && row0 + row < rows) v = scale16(*reinterpret_cast<const uint4*>(T + (row0 + row) * ld + col), s);
     wr16(dst + spos(row, c), v);
   }
+}
+__device__ __forceinline__ void tail_tokens(char* dst, const bf16_t* T, int64_t rows, int r, int64_t row0, int j0,
+                                            float s) {
+  tail_tokens(dst, T, r, rows, r, row0, j0, s);
 }
 
 // DMA pattern for a 256-row x 64-byte tile: wave w, instruction q covers

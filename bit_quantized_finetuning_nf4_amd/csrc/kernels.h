@@ -33,9 +33,10 @@ hipError_t launch_quantize(const bf16_t* W, int64_t numel, uint8_t* codes, uint8
 hipError_t launch_dequant(const uint8_t* codes, const uint8_t* absmax_q, const float* group_scale,
                           int64_t numel, int codebook, int absfmt, bf16_t* out, hipStream_t s);
 
-// WdT [K x N] = deq(W)^T (bf16) for W [N x K], K % 64 == 0, N < 65536 * 64.
+// WdT [K x N] = deq(W)^T (bf16) for W [N x K], K % 64 == 0, N < 65536 * 64;
+// rows of WdT are ldo >= N elements apart (a column block of a wider matrix).
 hipError_t launch_dequant_t(const uint8_t* codes, const uint8_t* absmax_q, const float* group_scale, int64_t N,
-                            int64_t K, int codebook, int absfmt, bf16_t* out, hipStream_t s);
+                            int64_t K, int codebook, int absfmt, bf16_t* out, int64_t ldo, hipStream_t s);
 
 // Y = X deq(W)^T + s * U * B^T  (U already holds X A^T in bf16; r may be 0)
 hipError_t launch_fwd(const Nf4View& W, const bf16_t* X, int64_t M, const bf16_t* U, const bf16_t* B,
@@ -51,6 +52,13 @@ hipError_t launch_dx(const Nf4View& W, const bf16_t* dY, int64_t M, const bf16_t
 // transposed weight: dX = dY (W^T)^T + s G (A^T)^T.
 hipError_t launch_bf16_fwd(const bf16_t* Wd, int64_t N, int64_t K, const bf16_t* X, int64_t M, const bf16_t* U,
                            const bf16_t* B, bool b_trans, int r, float s, bf16_t* Y, hipStream_t st);
+// The same over a stack of weights with one adapter each: weight rows come in
+// groups of gn (the last may be shorter), and the rows of group g take
+// columns g r .. g r + r - 1 of U (row stride ldu) in the tail.  gn = N and
+// ldu = r is launch_bf16_fwd.
+hipError_t launch_bf16_group(const bf16_t* Wd, int64_t N, int64_t K, const bf16_t* X, int64_t M, const bf16_t* U,
+                             int ldu, const bf16_t* B, bool b_trans, int r, int64_t gn, float s, bf16_t* Y,
+                             hipStream_t st);
 
 // Skinny products with a deterministic split-contraction reduction.
 // out_bf16 / out_f32 (either may be null) receive scale * result.
@@ -60,10 +68,20 @@ hipError_t launch_xat(const bf16_t* X, const bf16_t* A, int64_t M, int64_t K, in
                       bf16_t* out, bf16_t* out2, float scale, hipStream_t st);
 hipError_t launch_dyb(const bf16_t* dY, const bf16_t* B, int64_t M, int64_t N, int r, float* part,
                       bf16_t* out, float scale, hipStream_t st);
+// G groups: group g reads columns g N .. of dY [M x ldy] and B + g N r, and
+// writes columns g r .. of out [M x G r]; partials: skinny_partial_bytes(M,
+// G r, N, kDyB).
+hipError_t launch_dyb_group(const bf16_t* dY, int64_t ldy, const bf16_t* B, int64_t M, int64_t N, int r, int G,
+                            float* part, bf16_t* out, float scale, hipStream_t st);
 hipError_t launch_gtx(const bf16_t* G, const bf16_t* X, int64_t M, int64_t K, int r, float* part,
                       float* dA, float scale, hipStream_t st);
 hipError_t launch_dytu(const bf16_t* dY, const bf16_t* U, int64_t M, int64_t N, int r, float* part,
                        float* dB, float scale, hipStream_t st);
+// G groups: group g reads columns g N .. of dY [M x ldy] and columns g r ..
+// of U [M x ldu], and writes dB + g N r; partials: G skinny_partial_bytes(N,
+// r, M, kDytU).
+hipError_t launch_dytu_group(const bf16_t* dY, int64_t ldy, const bf16_t* U, int ldu, int64_t M, int64_t N, int r,
+                             int G, float* part, float* dB, float scale, hipStream_t st);
 
 // The paged optimizer's layout and step (paged.hip).
 bool paged_plan(const qlora_paged_tensor* t, int nt, size_t dev_bytes, qlora_paged_layout* L);

@@ -253,7 +253,8 @@ template <int CB>
 __global__ __launch_bounds__(256) void dequant_t_kernel(const uint8_t* __restrict__ codes,
                                                         const uint8_t* __restrict__ absmax_q,
                                                         const float* __restrict__ group_scale, int64_t N,
-                                                        int64_t K, int absfmt, bf16_t* __restrict__ out) {
+                                                        int64_t K, int absfmt, bf16_t* __restrict__ out,
+                                                        int64_t ldo) {
   __shared__ uint32_t tile[256 * kTrStride];
   const int t = threadIdx.x, rp = t & 31, cg = t >> 5;
   const int64_t n0 = (int64_t)blockIdx.y * 64, k0 = (int64_t)blockIdx.x * 256;
@@ -292,7 +293,7 @@ __global__ __launch_bounds__(256) void dequant_t_kernel(const uint8_t* __restric
     if (k0 + kk >= K) continue;
     const uint32_t* src = tile + kk * kTrStride + 4 * c;
     const uint4 v = make_uint4(src[0], src[1], src[2], src[3]);
-    bf16_t* dst = out + (k0 + kk) * N + n0 + 8 * c;
+    bf16_t* dst = out + (k0 + kk) * ldo + n0 + 8 * c;
     if (n0 + 8 * c + 8 <= N) {
       *reinterpret_cast<uint4*>(dst) = v;
     } else {
@@ -330,11 +331,11 @@ hipError_t launch_dequant(const uint8_t* codes, const uint8_t* absmax_q, const f
 }
 
 hipError_t launch_dequant_t(const uint8_t* codes, const uint8_t* absmax_q, const float* group_scale, int64_t N,
-                            int64_t K, int codebook, int absfmt, bf16_t* out, hipStream_t s) {
+                            int64_t K, int codebook, int absfmt, bf16_t* out, int64_t ldo, hipStream_t s) {
   auto* fn = codebook == kCbFp4 ? &dequant_t_kernel<kCbFp4> : codebook == kCbInt4 ? &dequant_t_kernel<kCbInt4>
                                                                                   : &dequant_t_kernel<kCbNf4>;
   hipLaunchKernelGGL(fn, dim3((unsigned)((K + 255) / 256), (unsigned)((N + 63) / 64)), dim3(256), 0, s, codes,
-                     absmax_q, group_scale, N, K, absfmt, out);
+                     absmax_q, group_scale, N, K, absfmt, out, ldo);
   return hipGetLastError();
 }
 

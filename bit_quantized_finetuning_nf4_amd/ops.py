@@ -252,6 +252,77 @@ def linear_bwd(q: QuantizedWeight, X: torch.Tensor, dY: torch.Tensor, A=None, B=
     return dX, dA, dB
 
 
+def _group_descs(qs: Sequence[QuantizedWeight]):
+    if not qs:
+        raise ValueError("a group needs at least one weight")
+    arr = (Nf4WeightDesc * len(qs))()
+    for i, q in enumerate(qs):
+        arr[i] = q.desc()
+    return arr
+
+
+def group_fwd(qs: Sequence[QuantizedWeight], X: torch.Tensor, A=None, B=None, alpha: float = 0.0,
+              save_u: bool = False, out=None, u_out=None, ws=None):
+    """G linears that read the same X (q/k/v, gate/up) in one call.
+
+    A [G r x K] and B [G N x r] are the G adapters stacked; returns Y
+    [M x G N] (Y_g in columns g N ..), or (Y, U) with U [M x G r]."""
+    _need(X, torch.bfloat16, "X")
+    G, N, K, M = len(qs), qs[0].rows, qs[0].cols, X.shape[0]
+    r = 0 if A is None else A.shape[0] // G
+    if A is not None:
+        _need(A, torch.bfloat16, "A", (G * r, K))
+        _need(B, torch.bfloat16, "B", (G * N, r))
+    Y = out if out is not None else torch.empty(M, G * N, dtype=torch.bfloat16, device=X.device)
+    U = None
+    if save_u and r:
+        U = u_out if u_out is not None else torch.empty(M, G * r, dtype=torch.bfloat16, device=X.device)
+    nbytes = workspace_bytes(_lib.QLORA_OP_GROUP_FWD, M, N, K, r, G)
+    if ws is None:
+        ws = workspace(nbytes, X.device)
+    elif ws.numel() > nbytes:
+        ws = ws[:nbytes]
+    descs = _group_descs(qs)
+    check(lib().qlora_group_fwd(descs, G, _ptr(X), M, _ptr(A), _ptr(B), r, float(alpha), _ptr(Y), _ptr(U),
+                                _ptr(ws), 0 if ws is None else ws.numel(), _stream()),
+          "qlora_group_fwd")
+    return (Y, U) if save_u else Y
+
+
+def group_bwd(qs: Sequence[QuantizedWeight], X: torch.Tensor, dY: torch.Tensor, A=None, B=None,
+              alpha: float = 0.0, U: Optional[torch.Tensor] = None, need_dx: bool = True, dX=None, dA=None,
+              dB=None, ws=None):
+    """Backward of group_fwd: dY [M x G N]; returns (dX [M x K] bf16 or None,
+    dA [G r x K] fp32, dB [G N x r] fp32) (the last two None without adapters)."""
+    _need(dY, torch.bfloat16, "dY")
+    G, N, K, M = len(qs), qs[0].rows, qs[0].cols, dY.shape[0]
+    _need(dY, torch.bfloat16, "dY", (M, G * N))
+    r = 0 if A is None else A.shape[0] // G
+    if r:
+        _need(X, torch.bfloat16, "X", (M, K))
+        _need(A, torch.bfloat16, "A", (G * r, K))
+        _need(B, torch.bfloat16, "B", (G * N, r))
+        dA = dA if dA is not None else torch.empty(G * r, K, dtype=torch.float32, device=dY.device)
+        dB = dB if dB is not None else torch.empty(G * N, r, dtype=torch.float32, device=dY.device)
+    else:
+        dA = dB = None
+    if need_dx:
+        dX = dX if dX is not None else torch.empty(M, K, dtype=torch.bfloat16, device=dY.device)
+    else:
+        dX = None
+    nbytes = workspace_bytes(_lib.QLORA_OP_GROUP_BWD, M, N, K, r, G)
+    if ws is None:
+        ws = workspace(nbytes, dY.device)
+    elif ws.numel() > nbytes:
+        ws = ws[:nbytes]
+    descs = _group_descs(qs)
+    check(lib().qlora_group_bwd(descs, G, _ptr(X), _ptr(dY), M, _ptr(A), _ptr(B), r, float(alpha), _ptr(U),
+                                _ptr(dX), _ptr(dA), _ptr(dB), _ptr(ws), 0 if ws is None else ws.numel(),
+                                _stream()),
+          "qlora_group_bwd")
+    return dX, dA, dB
+
+
 @dataclass
 class GemvJob:
     """One decode product: x is [cols] (one token) or [m x cols] (m <= 16

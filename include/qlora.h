@@ -82,7 +82,9 @@ typedef enum {
   QLORA_OP_GEMV = 2,  /* qlora_gemv                                         */
   QLORA_OP_LORA = 3,  /* qlora_lora_down, qlora_lora_dy_b, qlora_lora_grads */
   QLORA_OP_FWD_FUSED = 4,  /* qlora_linear_fwd, fused path only             */
-  QLORA_OP_BWD_FUSED = 5   /* qlora_linear_bwd, fused path only             */
+  QLORA_OP_BWD_FUSED = 5,  /* qlora_linear_bwd, fused path only             */
+  QLORA_OP_GROUP_FWD = 6,  /* qlora_group_fwd (njobs = G, the group size)   */
+  QLORA_OP_GROUP_BWD = 7   /* qlora_group_bwd (njobs = G, the group size)   */
 } qlora_op;
 
 /* A quantized weight: host struct holding device pointers.
@@ -320,6 +322,47 @@ qlora_status qlora_linear_bwd(const qlora_nf4_weight* W, const uint16_t* X, cons
 qlora_status qlora_linear_fwd_noalloc(const qlora_nf4_weight* W, const uint16_t* X, int64_t M,
                                       const uint16_t* A, const uint16_t* B, int32_t r, float alpha,
                                       uint16_t* Y, uint16_t* U_save, void* stream);
+
+/* ---- Layer-set groups ----------------------------------------------------
+ * LoRA adapts several linears of each transformer layer (deepfa.ir blog,
+ * "Optimization Tips", target modules: query and value, extendable to key
+ * and output; the layer sets here adapt all seven linears of a LLaMA layer),
+ * and some of them read the same input: q, k and v read the normalised
+ * hidden state, gate and up the second normalised state.  A group call
+ * computes G such linears as one: each has its own NF4 weight W_g [N x K]
+ * (all G of one shape, N % 64 == 0) and its own adapter (A_g, B_g) of rank
+ * r, with alpha shared.  The adapters are stacked, A [G r x K] = A_0 over
+ * A_1 .., and B [G N x r] = B_0 over B_1 ..; outputs sit side by side,
+ * Y [M x G N] with Y_g in columns g N .. g N + N - 1.  Per linear the
+ * result is the one of qlora_linear_fwd / _bwd; only the data movement is
+ * shared:
+ *   - the G weights are dequantized into one stack and multiplied by one
+ *     dense bf16 product over G N rows (each row group with its own LoRA
+ *     tail), so the token tiles of X are read once per G N rows;
+ *   - U = X A^T for all G adapters is one pass over X (U [M x G r]);
+ *   - dX = sum_g (dY_g deq(W_g) + s G_g A_g) is one product contracting
+ *     over G N, with the G adapters as one rank-G r tail; dA is one pass over
+ *     X.
+ * G r <= 256, G N K < 2^31, M G N < 2^31.  Y_g, U_g, dA_g and dB_g equal
+ * those of qlora_linear_fwd / _bwd on the staged path bit for bit; dX differs
+ * from the bf16 sum of G per-linear dX only in rounding (it is rounded to
+ * bf16 once).  Workspace: qlora_workspace_bytes(QLORA_OP_GROUP_FWD / _BWD,
+ * M, N, K, r, G).  Errors as for qlora_linear_fwd, plus QLORA_E_SHAPE when
+ * the G weights differ in shape and QLORA_E_UNSUPPORTED when N % 64 != 0
+ * or G r > 256. */
+
+/* Y [M x G N] (bf16, overwritten); U_save (nullable) receives U [M x G r]. */
+qlora_status qlora_group_fwd(const qlora_nf4_weight* W, int32_t G, const uint16_t* X, int64_t M,
+                             const uint16_t* A, const uint16_t* B, int32_t r, float alpha, uint16_t* Y,
+                             uint16_t* U_save, void* ws, size_t ws_bytes, void* stream);
+
+/* dY [M x G N]; dX [M x K] (bf16, overwritten; NULL skips it); dA [G r x K]
+ * and dB [G N x r] (fp32, overwritten).  U_saved (nullable) is U [M x G r]
+ * from qlora_group_fwd; when NULL it is recomputed. */
+qlora_status qlora_group_bwd(const qlora_nf4_weight* W, int32_t G, const uint16_t* X, const uint16_t* dY,
+                             int64_t M, const uint16_t* A, const uint16_t* B, int32_t r, float alpha,
+                             const uint16_t* U_saved, uint16_t* dX, float* dA, float* dB, void* ws,
+                             size_t ws_bytes, void* stream);
 
 /* ---- Building blocks of the forward and backward passes ----------------
  * qlora_linear_fwd = qlora_lora_down + qlora_nf4_fwd;

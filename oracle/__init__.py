@@ -16,7 +16,7 @@ Sources (the QLoRA pages):
     "2. Double Quantization" and "QLoRA's Working Process".
 
 Where those pages leave a step open, the reading taken is stated in the
-docstring of the function that implements it (readings R1-R19).
+docstring of the function that implements it (readings R1-R20).
 
 Every function here is pinned by a test in ``tests/test_oracle_*.py``
 against something other than itself (closed forms, exact rational
@@ -31,6 +31,7 @@ from .linear import linear_fwd, linear_bwd, adapter_grads, gemv, lora_scale
 from .codebooks import fp4_levels, int4_levels, e2m1_value, zero_code, CODEBOOKS
 from .codebooks import levels as codebook_levels
 from .optim import adamw_step
+from .group import group_fwd, group_bwd
 from .secondlevel import e4m3_value, fp8_levels, FORMATS as ABSMAX_FORMATS
 from .secondlevel import levels as absmax_levels
 
@@ -41,5 +42,5 @@ __all__ = [
     "BLOCKSIZE", "GROUP_BLOCKS",
     "linear_fwd", "linear_bwd", "gemv", "lora_scale",
     "fp4_levels", "int4_levels", "e2m1_value", "zero_code", "CODEBOOKS", "codebook_levels",
-    "adamw_step", "e4m3_value", "fp8_levels", "ABSMAX_FORMATS", "absmax_levels",
+    "adamw_step", "group_fwd", "group_bwd", "e4m3_value", "fp8_levels", "ABSMAX_FORMATS", "absmax_levels",
 ]

@@ -281,3 +281,43 @@ def test_paged_optimizer_layout_policy(L):
     assert L.qlora_paged_adamw(d, 1, ctypes.c_void_p(4096 + 16), 1 << 20, 1e-3, 0.9, 0.999, 1e-8, 0.0, 1, 0, None,
                                None) == 2                                                            # ws alignment
     assert L.qlora_paged_adamw(d, 1, fake, 512, 1e-3, 0.9, 0.999, 1e-8, 0.0, 1, 0, None, None) in (0, 5)
+
+
+def test_group_calls_validate_on_the_host(L):
+    """Layer-set groups: workspace sizes and every rejection happen on the
+    host, before anything is enqueued (fake, never-dereferenced addresses)."""
+    fwd1 = L.qlora_workspace_bytes(0, 4096, 8192, 8192, 64, 0)   # one linear, staged
+    gf = L.qlora_workspace_bytes(6, 4096, 8192, 8192, 64, 3)
+    gb = L.qlora_workspace_bytes(7, 4096, 8192, 8192, 64, 3)
+    assert gf >= 3 * 8192 * 8192 * 2 + 4096 * 192 * 2 and gf > fwd1
+    assert gb >= 3 * 8192 * 8192 * 2 + 2 * 4096 * 192 * 2
+    assert L.qlora_workspace_bytes(6, 4096, 8192, 8192, 0, 2) == 2 * 8192 * 8192 * 2   # no adapter: the stack only
+    assert L.qlora_workspace_bytes(6, 4096, 8192, 8192, 64, 0) == 0      # G >= 1
+    assert L.qlora_workspace_bytes(6, 4096, 8192, 8192, 64, 5) == 0      # G r > 256
+    assert L.qlora_workspace_bytes(7, 4096, 1 << 16, 1 << 16, 8, 1) == 0  # G N K >= 2^31
+
+    fake = ctypes.c_void_p(4096)
+    big = 1 << 40
+    W = lambda *ds: (Nf4WeightDesc * len(ds))(*ds)
+    three = W(_desc(128, 64), _desc(128, 64), _desc(128, 64))
+    gf = lambda w, g, x, m, a, b, r, y, ws=fake, n=big: L.qlora_group_fwd(w, g, x, m, a, b, r, 16.0, y, None, ws, n,
+                                                                          None)
+    assert gf(None, 3, fake, 4, fake, fake, 16, fake) == 1
+    assert gf(three, 0, fake, 4, fake, fake, 16, fake) == 3                          # G >= 1
+    assert gf(W(_desc(128, 64), _desc(192, 64)), 2, fake, 4, fake, fake, 16, fake) == 3   # shapes differ
+    assert gf(W(_desc(72, 64), _desc(72, 64)), 2, fake, 4, fake, fake, 16, fake) == 4     # N % 64
+    assert gf(three, 3, fake, 4, fake, fake, 96, fake) == 4                          # G r = 288 > 256
+    assert gf(three, 3, fake, 4, fake, fake, 12, fake) == 4                          # r % 8
+    assert gf(three, 3, fake, 4, None, fake, 16, fake) == 1                          # A missing
+    assert gf(three, 3, None, 4, fake, fake, 16, fake) == 1
+    assert gf(three, 3, fake, 0, fake, fake, 16, fake) == 3                          # M >= 1
+    assert gf(three, 3, ctypes.c_void_p(4098), 4, fake, fake, 16, fake) == 2         # X alignment
+    assert gf(three, 3, fake, 4, fake, fake, 16, fake, n=16) == 5                    # workspace too small
+    assert gf(three, 3, fake, 4, fake, fake, 16, fake, ws=None) == 1                 # workspace missing
+    gb = lambda w, g, m, r, dx, da, db, n=big: L.qlora_group_bwd(w, g, fake, fake, m, fake if r else None,
+                                                                 fake if r else None, r, 16.0, None, dx, da, db,
+                                                                 fake, n, None)
+    assert gb(three, 3, 4, 16, fake, None, fake) == 1                                # dA missing
+    assert gb(three, 3, 4, 0, fake, fake, None) == 3                                 # no adapter, no dA
+    assert gb(three, 3, 4, 16, fake, fake, fake, n=16) == 5
+    assert gb(W(_desc(128, 64), _desc(128, 128)), 2, 4, 16, fake, fake, fake) == 3
