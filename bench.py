@@ -8,22 +8,26 @@ quantization over 256-block groups):
 
   1. quantize the seven bf16 weights (block absmax, NF4 codes, 8-bit absmax
      codes against fp32 group scales);
-  2. forward, per linear: U = X A^T; W dequantized once to bf16; the dense
-     bf16 GEMM Y = X deq(W)^T + s U B^T;
-  3. backward, per linear: G = dY B; W dequantized once, transposed; the
-     dense GEMM dX = dY deq(W) + s G A; dA = s G^T X and dB = s dY^T U;
+  2. forward, per group of linears that read the same input (q/k/v, o,
+     gate/up, down): U = X A^T for the group's stacked adapters; the group's
+     weights dequantized once into one bf16 stack; one dense bf16 GEMM
+     Y = X deq(W)^T + s U B^T over the stack, each row group with its own
+     adapter;
+  3. backward, per group: G = dY B; the weights dequantized once, transposed,
+     side by side; one dense GEMM dX = dY deq(W) + s G A contracting over the
+     group's outputs; dA = s G^T X and dB = s dY^T U;
   4. batch-1 decode: y = deq(W) x + s B (A x) for the seven linears in one
      grouped call.
 
-Steps 2 and 3 are the building blocks of qlora_linear_fwd / qlora_linear_bwd
-on their staged path (what those calls run at 1024 tokens and more when the
-workspace holds the bf16 weight).  The fused path (W decoded inside each
-256-token product tile) is timed the same way beside it.
+Steps 2 and 3 are the building blocks of qlora_group_fwd / qlora_group_bwd.
+The same step with one product per linear (the staged path of
+qlora_linear_fwd / _bwd, taken from 1024 tokens on), and with the fused path
+(W decoded inside each 256-token product tile), is timed beside it.
 
 `value` is the fwd+bwd algorithmic work, sum over linears of
 4MNK + 6Mr(N+K) flops, divided by the wall time of whole steps (quantize and
 decode included).  HIP events on the launch stream bracket every dense GEMM
-launch; their flops over their summed durations is the roofline figure
+call; their flops over their summed durations is the roofline figure
 against the dense bf16 MFMA peak.  The 7B and 13B layer sets and the small
 1024x1024 case are timed the same way (fwd + bwd phases), dequantization is
 timed on the 65B gate weight (360 MB of bf16 out), and the shader clock is
@@ -435,9 +439,15 @@ class ClockSampler:
                 "min_mhz": v[0], "max_mhz": v[-1]}
 
 
+# linears of a LLaMA layer that read the same input: the attention
+# projections q/k/v read the normalised hidden state, gate/up the second one
+GROUPS = (("q", "k", "v"), ("o",), ("gate", "up"), ("down",))
+
+
 class LayerSet:
     """Inputs, outputs and scratch of one layer set, resident on the device,
-    and one step of the path over it (staged or fused products)."""
+    and one step of the path over it: grouped, per-linear staged, or fused
+    products."""
 
     def __init__(self, name, dev, with_decode=True):
         import torch
@@ -460,9 +470,28 @@ class LayerSet:
                      dA=torch.empty(r, K, dtype=torch.float32, device=dev),
                      dB=torch.empty(N, r, dtype=torch.float32, device=dev))
             self.L.append(o)
-        self.ws = ops.workspace(max(ops.workspace_bytes(_lib.QLORA_OP_LORA, M, o["N"], o["K"], r) for o in self.L),
-                                dev)
-        self.wbuf = torch.empty(max(o["N"] * o["K"] for o in self.L), dtype=torch.bfloat16, device=dev)
+        # linears that read the same input run as one group on the grouped path
+        names = [o["name"] for o in self.L]
+        parts = GROUPS if all(n in names for grp in GROUPS for n in grp) else tuple((n,) for n in names)
+        self.groups = []
+        for grp in parts:
+            mem = [self.L[names.index(n)] for n in grp]
+            G, N, K = len(mem), mem[0]["N"], mem[0]["K"]
+            cat = lambda key, dim=0: torch.cat([o[key] for o in mem], dim=dim).contiguous() if G > 1 else mem[0][key]
+            self.groups.append(dict(
+                name="/".join(grp), G=G, N=N, K=K, qs=[o["q"] for o in mem], X=mem[0]["X"],
+                A=cat("A"), B=cat("B"), dY=cat("dY", 1),
+                Y=torch.empty(M, G * N, dtype=torch.bfloat16, device=dev),
+                U=torch.empty(M, G * r, dtype=torch.bfloat16, device=dev),
+                Gm=torch.empty(M, G * r, dtype=torch.bfloat16, device=dev),
+                dX=torch.empty(M, K, dtype=torch.bfloat16, device=dev),
+                dA=torch.empty(G * r, K, dtype=torch.float32, device=dev),
+                dB=torch.empty(G * N, r, dtype=torch.float32, device=dev)))
+        self.ws = ops.workspace(max([ops.workspace_bytes(_lib.QLORA_OP_LORA, M, o["N"], o["K"], r) for o in self.L]
+                                    + [ops.workspace_bytes(_lib.QLORA_OP_GROUP_LORA, M, g["N"], g["K"], r, g["G"])
+                                       for g in self.groups]), dev)
+        self.wbuf = torch.empty(max(g["G"] * g["N"] * g["K"] for g in self.groups), dtype=torch.bfloat16,
+                                device=dev)
         self.plan = (ops.GemvPlan([ops.GemvJob(o["q"], o["x"], o["A"], o["B"], self.alpha) for o in self.L])
                      if with_decode else None)
         self.fl_step = sum(linear_flops(M, o["N"], o["K"], r) for o in self.L)
@@ -474,12 +503,18 @@ class LayerSet:
             ops.quantize(o["W"], out=o["q"])
         torch.cuda.synchronize()
 
+    def units(self, path):
+        """The products of one step: one per group on the grouped path, else
+        one per linear."""
+        return self.groups if path == "grouped" else self.L
+
     def step(self, path, record=None):
         """One step; with `record` (a list) HIP events bracket the phases and
-        every product launch."""
+        every dense (or fused) product call."""
         ops, torch, a, L = self.ops, self.torch, self.alpha, self.L
         E = lambda: torch.cuda.Event(enable_timing=True)
-        ev = dict(p=[E() for _ in range(5)], f=[(E(), E()) for _ in L], d=[(E(), E()) for _ in L]) \
+        nu = len(self.units(path))
+        ev = dict(p=[E() for _ in range(5)], f=[(E(), E()) for _ in range(nu)], d=[(E(), E()) for _ in range(nu)]) \
             if record is not None else None
         mark = (lambda e: e.record()) if ev else (lambda e: None)
         if ev:
@@ -488,6 +523,47 @@ class LayerSet:
             ops.quantize(o["W"], out=o["q"])
         if ev:
             mark(ev["p"][1])
+        if path == "grouped":
+            self._grouped(ev, mark)
+        else:
+            self._per_linear(path, ev, mark)
+        if ev:
+            mark(ev["p"][3])
+        if self.plan is not None:
+            self.plan()
+        if ev:
+            mark(ev["p"][4])
+            record.append(ev)
+
+    def _grouped(self, ev, mark):
+        """Forward and backward with q/k/v and gate/up as one group each (the
+        building blocks of qlora_group_fwd / _bwd, so the dense products can
+        be timed on their own)."""
+        ops, a = self.ops, self.alpha
+        for i, g in enumerate(self.groups):
+            G, N, K = g["G"], g["N"], g["K"]
+            ops.lora_down(g["X"], g["A"], U=g["U"], ws=self.ws)
+            Wd = ops.group_dequant(g["qs"], out=self.wbuf[:G * N * K].view(G * N, K))
+            if ev:
+                mark(ev["f"][i][0])
+            ops.bf16_group_fwd(Wd, G, g["X"], g["U"], g["B"], a, out=g["Y"])
+            if ev:
+                mark(ev["f"][i][1])
+        if ev:
+            mark(ev["p"][2])
+        for i, g in enumerate(self.groups):
+            G, N, K = g["G"], g["N"], g["K"]
+            ops.group_lora_dy_b(g["dY"], g["B"], G, Gm=g["Gm"], ws=self.ws)
+            WdT = ops.group_dequant(g["qs"], out=self.wbuf[:G * N * K].view(K, G * N), transposed=True)
+            if ev:
+                mark(ev["d"][i][0])
+            ops.bf16_group_dx(WdT, G, g["dY"], g["Gm"], g["A"], a, out=g["dX"])
+            if ev:
+                mark(ev["d"][i][1])
+            ops.group_lora_grads(g["X"], g["dY"], g["U"], g["Gm"], G, a, dA=g["dA"], dB=g["dB"], ws=self.ws)
+
+    def _per_linear(self, path, ev, mark):
+        ops, a, L = self.ops, self.alpha, self.L
         for i, o in enumerate(L):
             ops.lora_down(o["X"], o["A"], U=o["U"], ws=self.ws)
             if path == "staged":
@@ -517,13 +593,6 @@ class LayerSet:
             if ev:
                 mark(ev["d"][i][1])
             ops.lora_grads(o["X"], o["dY"], o["U"], o["G"], a, dA=o["dA"], dB=o["dB"], ws=self.ws)
-        if ev:
-            mark(ev["p"][3])
-        if self.plan is not None:
-            self.plan()
-        if ev:
-            mark(ev["p"][4])
-            record.append(ev)
 
     def run(self, path, steps, warmup):
         """Timed steps: wall time per step, phases and per-product times."""
@@ -549,16 +618,17 @@ class LayerSet:
             dx_ms += sum(x.elapsed_time(y) for x, y in ev["d"])
         ph = {k: v / steps for k, v in ph.items()}
         fwd_ms, dx_ms = fwd_ms / steps, dx_ms / steps
-        n = len(self.L)
+        n = len(self.units(path))
         gemm_tf = (sum(self.fl_fwd) + sum(self.fl_dx)) / ((fwd_ms + dx_ms) * 1e-3) / 1e12
         return {
             "path": path, "ms_per_step": ms_step, "phases_ms": ph,
             "fwd_bwd_tflops": self.fl_step / ((ph["forward"] + ph["backward"]) * 1e-3) / 1e12,
             "products": {
-                "kernel": "bf16_fwd_kernel (dense bf16 GEMM)" if path == "staged"
-                          else "nf4_fwd_r_kernel / nf4_dx_kernel (fused NF4 GEMMs)",
-                "launches_per_step": 2 * n,
-                "fwd_avg_launch_ms": fwd_ms / n, "dx_avg_launch_ms": dx_ms / n,
+                "kernel": "nf4_fwd_r_kernel / nf4_dx_kernel (fused NF4 GEMMs)" if path == "fused"
+                          else "bf16_fwd_kernel (dense bf16 GEMM)",
+                "calls_per_step": 2 * n,
+                "products": [u["name"] for u in self.units(path)],
+                "fwd_avg_call_ms": fwd_ms / n, "dx_avg_call_ms": dx_ms / n,
                 "fwd_tflops": sum(self.fl_fwd) / (fwd_ms * 1e-3) / 1e12,
                 "dx_tflops": sum(self.fl_dx) / (dx_ms * 1e-3) / 1e12,
                 "tflops": gemm_tf, "frac_of_bf16_peak": gemm_tf / PEAK_BF16_TFLOPS},
@@ -644,9 +714,9 @@ def main():
     log(f"[bench] workload {args.workload}: {len(cfg['linears'])} linears, M={M}, r={r}")
     S = LayerSet(args.workload, dev)
     L = S.L
-    head = S.run("staged", args.steps, args.warmup)
+    head = S.run("grouped", args.steps, args.warmup)
     ms_step = head["ms_per_step"]
-    log(f"[bench] staged step {ms_step:.3f} ms; phases {head['phases_ms']}; products {head['products']}")
+    log(f"[bench] grouped step {ms_step:.3f} ms; phases {head['phases_ms']}; products {head['products']}")
 
     if args.copy_probe_mib > 0:
         n = args.copy_probe_mib * 1024 * 1024 // 4
@@ -664,21 +734,26 @@ def main():
         t_end = time.perf_counter() + 2.0
         while time.perf_counter() < t_end:
             for _ in range(10):
-                S.step("staged")
+                S.step("grouped")
             torch.cuda.synchronize()
     clock = sampler.result()
     log(f"[bench] clock {clock}")
 
+    per_linear = S.run("staged", args.steps, args.warmup)
+    log(f"[bench] per-linear staged step {per_linear['ms_per_step']:.3f} ms; "
+        f"fwd+bwd {per_linear['fwd_bwd_tflops']:.0f} TFLOP/s")
     fused = S.run("fused", args.steps, args.warmup)
     log(f"[bench] fused step {fused['ms_per_step']:.3f} ms; fwd+bwd {fused['fwd_bwd_tflops']:.0f} TFLOP/s")
 
     prod = head["products"]
     traffic = traffic_for("dense_gemm")
-    roof = {"kernel": "dense_gemm (bf16_fwd_kernel, forward and dX launches)", "bound": "mfma",
+    roof = {"kernel": "dense_gemm (bf16_fwd_kernel, forward and dX products)", "bound": "mfma",
             "achieved": prod["tflops"], "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": prod["tflops"] / PEAK_BF16_TFLOPS, "traffic": traffic,
-            "per_launch": "flops of the dense GEMM = 2MNK + 2Mr(N) (forward) or 2MNK + 2Mr(K) (dX) for each of the "
-                          "7 linears; achieved = their sum / the sum of the 14 launches' HIP-event durations"}
+            "per_launch": "flops of the dense GEMM = 2MNK + 2Mr(N) (forward) or 2MNK + 2Mr(K) (dX) summed over the "
+                          "linears of each product (q/k/v, o, gate/up, down); achieved = the sum over the 7 "
+                          "linears / the sum of the 8 product calls' HIP-event durations (a call is one launch, or "
+                          "two when its last round of tiles takes a narrower tile width)"}
     if clock:
         roof["clock_mhz_median"] = clock["median_mhz"]
         roof["frac_at_measured_clock"] = prod["tflops"] / (PEAK_BF16_TFLOPS * clock["median_mhz"] / 2400.0)
@@ -690,8 +765,8 @@ def main():
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": f"{args.workload} layer set: " + ", ".join(f"{o['name']} {o['N']}x{o['K']}" for o in L)
                    + f"; M={M} tokens; LoRA r={r} alpha={alpha}; NF4 blocksize 64, 8-bit double quant per 256 blocks"
-                   + "; step = quantize + fwd + bwd (staged: W dequantized once per product, dense bf16 GEMM) "
-                     "+ batch-1 decode GEMV",
+                   + "; step = quantize + fwd + bwd (q/k/v and gate/up as one group each; staged: W "
+                     "dequantized once per product, dense bf16 GEMM) + batch-1 decode GEMV",
                    "global_batch": M, "seq_len": M, "parallelism": "none (1 GPU)"},
         "roofline": roof,
         "phases_ms": head["phases_ms"],
@@ -700,6 +775,7 @@ def main():
         "targets": {"fwd_bwd_frac_of_bf16_peak": fb / PEAK_BF16_TFLOPS, "fwd_bwd_target_frac": 0.50,
                     "fwd_bwd_shortfall_ms": max(0.0, (head["phases_ms"]["forward"] + head["phases_ms"]["backward"])
                                                 - S.fl_step / (0.5 * PEAK_BF16_TFLOPS * 1e12) * 1e3)},
+        "per_linear_path": {k: per_linear[k] for k in ("ms_per_step", "phases_ms", "fwd_bwd_tflops", "products")},
         "fused_path": {k: fused[k] for k in ("ms_per_step", "phases_ms", "fwd_bwd_tflops", "products")},
         "clock": clock,
         "quantize_gbps": S.q_bytes / (head["phases_ms"]["quantize"] * 1e-3) / 1e9,
@@ -721,7 +797,7 @@ def main():
             if name == args.workload:
                 continue
             T = LayerSet(name, dev, with_decode=False)
-            paths = ("staged", "fused") if T.M >= 1024 else ("fused",)
+            paths = ("grouped", "staged", "fused") if T.M >= 1024 else ("grouped", "fused")
             res = {"M": T.M, "r": T.r, "linears": [f"{o['name']} {o['N']}x{o['K']}" for o in T.L],
                    "flops_per_step": T.fl_step}
             for pth in paths:

@@ -13,7 +13,7 @@ LIB_PATH = os.path.join(_HERE, "libqlora.so")
 QLORA_OK = 0
 QLORA_OP_FWD, QLORA_OP_BWD, QLORA_OP_GEMV, QLORA_OP_LORA = 0, 1, 2, 3
 QLORA_OP_FWD_FUSED, QLORA_OP_BWD_FUSED = 4, 5
-QLORA_OP_GROUP_FWD, QLORA_OP_GROUP_BWD = 6, 7
+QLORA_OP_GROUP_FWD, QLORA_OP_GROUP_BWD, QLORA_OP_GROUP_LORA = 6, 7, 8
 
 STATUS_NAMES = {
     0: "QLORA_OK", 1: "QLORA_E_NULL", 2: "QLORA_E_ALIGN", 3: "QLORA_E_SHAPE",
@@ -29,6 +29,8 @@ EXPORTS = [
     "qlora_lora_down", "qlora_lora_dy_b", "qlora_lora_grads", "qlora_nf4_fwd", "qlora_nf4_dx",
     "qlora_linear_fwd_noalloc", "qlora_bf16_fwd", "qlora_dequant_t", "qlora_bf16_dx",
     "qlora_paged_layout_of", "qlora_paged_adamw", "qlora_group_fwd", "qlora_group_bwd",
+    "qlora_group_dequant", "qlora_group_dequant_t", "qlora_bf16_group_fwd", "qlora_bf16_group_dx",
+    "qlora_group_lora_dy_b", "qlora_group_lora_grads",
 ]
 QLORA_PAGED_LOAD, QLORA_PAGED_STORE = 1, 2
 
@@ -173,6 +175,17 @@ def lib():
     L.qlora_group_fwd.argtypes = [Wg, i32, vp, i64, vp, vp, i32, f32, vp, vp, vp, sz, vp]
     L.qlora_group_bwd.restype = ctypes.c_int
     L.qlora_group_bwd.argtypes = [Wg, i32, vp, vp, i64, vp, vp, i32, f32, vp, vp, vp, vp, vp, sz, vp]
+    for name in ("qlora_group_dequant", "qlora_group_dequant_t"):
+        getattr(L, name).restype = ctypes.c_int
+        getattr(L, name).argtypes = [Wg, i32, vp, vp]
+    L.qlora_bf16_group_fwd.restype = ctypes.c_int
+    L.qlora_bf16_group_fwd.argtypes = [vp, i32, i64, i64, vp, i64, vp, vp, i32, f32, vp, vp]
+    L.qlora_bf16_group_dx.restype = ctypes.c_int
+    L.qlora_bf16_group_dx.argtypes = [vp, i32, i64, i64, vp, i64, vp, vp, i32, f32, vp, vp]
+    L.qlora_group_lora_dy_b.restype = ctypes.c_int
+    L.qlora_group_lora_dy_b.argtypes = [vp, vp, i64, i64, i32, i32, vp, vp, sz, vp]
+    L.qlora_group_lora_grads.restype = ctypes.c_int
+    L.qlora_group_lora_grads.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, i32, f32, vp, vp, vp, sz, vp]
     _lib = L
     return L
 

@@ -180,6 +180,18 @@ bool group_sizes_ok(int64_t M, int64_t N, int64_t K, int32_t r, int32_t G) {
   return NG <= (int64_t)0x7FFFFFFF / K;
 }
 
+// Split partial sums of the group's side products: U = X A^T at rank G r,
+// dY B and G^T X over all groups, and dY^T U per group.
+size_t group_part_bytes(int64_t M, int64_t N, int64_t K, int32_t r, int32_t G) {
+  if (r == 0) return 0;
+  const int32_t rg = G * r;
+  size_t p = skinny_partial_bytes(M, rg, K, kXAt);
+  p = std::max(p, skinny_partial_bytes(M, rg, N, kDyB));
+  p = std::max(p, skinny_partial_bytes(rg, K, M, kGtX));
+  p = std::max(p, (size_t)G * skinny_partial_bytes(N, r, M, kDytU));
+  return align_up(p);
+}
+
 FwdLayout group_fwd_layout(int64_t M, int64_t N, int64_t K, int32_t r, int32_t G) {
   FwdLayout L{0, 0, 0, 0};
   const int32_t rg = G * r;
@@ -199,11 +211,7 @@ BwdLayout group_bwd_layout(int64_t M, int64_t N, int64_t K, int32_t r, int32_t G
     const size_t mr = align_up((size_t)M * rg * 2);
     L.u = mr;
     L.part = 2 * mr;
-    size_t p = skinny_partial_bytes(M, rg, K, kXAt);
-    p = std::max(p, skinny_partial_bytes(M, rg, N, kDyB));
-    p = std::max(p, skinny_partial_bytes(rg, K, M, kGtX));
-    p = std::max(p, (size_t)G * skinny_partial_bytes(N, r, M, kDytU));
-    L.total = L.part + align_up(p);
+    L.total = L.part + group_part_bytes(M, N, K, r, G);
   }
   if (with_dx) {
     L.wdt = L.total;
@@ -372,8 +380,8 @@ size_t qlora_workspace_bytes(qlora_op op, int64_t M, int64_t N, int64_t K, int32
     case QLORA_OP_GEMV:
       if (njobs <= 0 || njobs > kMaxJobs || N <= 0 || M < 0 || M > kMaxGemvTokens) return 0;
       return gemv_u_bytes(njobs, M) + gemv_table_bound(njobs, N);
-    case QLORA_OP_LORA:
-      if (M <= 0 || N <= 0 || K <= 0 || r < 0 || r > kMaxRank) return 0;
+    case QLORA_OP_LORA:   // ranks above 128: qlora_lora_down on a group's stacked adapters
+      if (M <= 0 || N <= 0 || K <= 0 || r < 0 || r > kMaxGroupRank) return 0;
       return lora_part_bytes(M, N, K, r);
     case QLORA_OP_GROUP_FWD:
       if (!group_sizes_ok(M, N, K, r, njobs)) return 0;
@@ -381,6 +389,9 @@ size_t qlora_workspace_bytes(qlora_op op, int64_t M, int64_t N, int64_t K, int32
     case QLORA_OP_GROUP_BWD:
       if (!group_sizes_ok(M, N, K, r, njobs)) return 0;
       return group_bwd_layout(M, N, K, r, njobs, true).total;
+    case QLORA_OP_GROUP_LORA:
+      if (!group_sizes_ok(M, N, K, r, njobs)) return 0;
+      return group_part_bytes(M, N, K, r, njobs);
   }
   return 0;
 }
@@ -558,10 +569,8 @@ qlora_status qlora_linear_bwd(const qlora_nf4_weight* W, const uint16_t* X, cons
 
 namespace {
 
-// Arguments common to both group calls: G weights of one GEMM-path shape
-// N x K with N % 64 == 0, the stacked adapters, and the token count.
-qlora_status check_group(const qlora_nf4_weight* W, int32_t G, int64_t M, int32_t r, const uint16_t* A,
-                         const uint16_t* B) {
+// A group's weights: G >= 1 descriptors of one GEMM-path shape.
+qlora_status check_group_weights(const qlora_nf4_weight* W, int32_t G) {
   if (!W) return QLORA_E_NULL;
   if (G < 1) return QLORA_E_SHAPE;
   for (int32_t g = 0; g < G; ++g) {
@@ -569,13 +578,19 @@ qlora_status check_group(const qlora_nf4_weight* W, int32_t G, int64_t M, int32_
     if (st != QLORA_OK) return st;
     if (W[g].rows != W[0].rows || W[g].cols != W[0].cols) return QLORA_E_SHAPE;
   }
-  qlora_status st = check_rank(r, A, B);
-  if (st != QLORA_OK) return st;
-  const int64_t N = W[0].rows, K = W[0].cols;
-  if (N % 64 != 0 || !group_sizes_ok(1, N, K, r, G)) return QLORA_E_UNSUPPORTED;
+  return QLORA_OK;
+}
+
+// Sizes of a group's products: N % 64 == 0 and K % 64 == 0, G r <= 256, and
+// the stack, X and dY addressed with 32-bit byte offsets (G N K, M K and
+// M G N below 2^31).
+qlora_status check_group_shape(int64_t M, int64_t N, int64_t K, int32_t r, int32_t G) {
+  if (G < 1 || M <= 0 || M > 0x7FFFFFFF || N <= 0 || K <= 0) return QLORA_E_SHAPE;
+  if (r < 0 || r % 8 != 0 || r > kMaxRank || (int64_t)G * r > kMaxGroupRank) return QLORA_E_UNSUPPORTED;
+  if (N % 64 != 0 || K % 64 != 0) return QLORA_E_UNSUPPORTED;
   const int64_t NG = (int64_t)G * N;
-  if (M <= 0 || M > 0x7FFFFFFF) return QLORA_E_SHAPE;
-  if (M > (int64_t)0x7FFFFFFF / K || M > (int64_t)0x7FFFFFFF / NG) return QLORA_E_UNSUPPORTED;
+  if (NG > (int64_t)0x7FFFFFFF / K || M > (int64_t)0x7FFFFFFF / K || M > (int64_t)0x7FFFFFFF / NG)
+    return QLORA_E_UNSUPPORTED;
   if (r > 0 && (!skinny_cols_ok(K) || !skinny_cols_ok(NG))) return QLORA_E_UNSUPPORTED;
   return QLORA_OK;
 }
@@ -594,40 +609,68 @@ qlora_status group_dequant(const qlora_nf4_weight* W, int32_t G, bool transposed
   return QLORA_OK;
 }
 
+float lora_s(float alpha, int32_t r) { return r > 0 ? (float)((double)alpha / (double)r) : 0.0f; }
+
+// The group's products on validated arguments (the building blocks below
+// and the two group calls share them).
+qlora_status group_fwd_product(const bf16_t* Wd, int32_t G, int64_t N, int64_t K, const bf16_t* X, int64_t M,
+                               const bf16_t* U, const bf16_t* B, int32_t r, float alpha, bf16_t* Y, hipStream_t s) {
+  return hip_status(launch_bf16_group(Wd, (int64_t)G * N, K, X, M, r > 0 ? U : nullptr, G * r, r > 0 ? B : nullptr,
+                                      false, r, N, lora_s(alpha, r), Y, s));
+}
+// dX = sum_g dY_g deq(W_g) + s sum_g G_g A_g: one dense product contracting
+// over the G N columns of dY, with the stacked adapters as a rank-G r tail
+qlora_status group_dx_product(const bf16_t* WdT, int32_t G, int64_t N, int64_t K, const bf16_t* dY, int64_t M,
+                              const bf16_t* Gm, const bf16_t* A, int32_t r, float alpha, bf16_t* dX, hipStream_t s) {
+  return hip_status(launch_bf16_group(WdT, K, (int64_t)G * N, dY, M, r > 0 ? Gm : nullptr, G * r,
+                                      r > 0 ? A : nullptr, true, G * r, K, lora_s(alpha, r), dX, s));
+}
+qlora_status group_grads(const bf16_t* X, const bf16_t* dY, const bf16_t* U, const bf16_t* Gm, int64_t M, int64_t N,
+                         int64_t K, int32_t r, int32_t G, float alpha, float* dA, float* dB, float* part,
+                         hipStream_t s) {
+  const float sc = lora_s(alpha, r);
+  // dA [G r x K] = s G^T X in one pass over X; dB_g = s dY_g^T U_g
+  qlora_status st = hip_status(launch_gtx(Gm, X, M, K, G * r, part, dA, sc, s));
+  if (st != QLORA_OK) return st;
+  return hip_status(launch_dytu_group(dY, (int64_t)G * N, U, G * r, M, N, r, G, part, dB, sc, s));
+}
+
 }  // namespace
 
 qlora_status qlora_group_fwd(const qlora_nf4_weight* W, int32_t G, const uint16_t* X, int64_t M,
                              const uint16_t* A, const uint16_t* B, int32_t r, float alpha, uint16_t* Y,
                              uint16_t* U_save, void* ws, size_t ws_bytes, void* stream) {
-  qlora_status st = check_group(W, G, M, r, A, B);
+  qlora_status st = check_group_weights(W, G);
   if (st != QLORA_OK) return st;
+  if ((st = check_rank(r, A, B)) != QLORA_OK) return st;
+  const int64_t N = W[0].rows, K = W[0].cols;
+  if ((st = check_group_shape(M, N, K, r, G)) != QLORA_OK) return st;
   if (!X || !Y) return QLORA_E_NULL;
   if (!aligned16(X) || !aligned16(Y) || (U_save && !aligned16(U_save))) return QLORA_E_ALIGN;
-  const int64_t N = W[0].rows, K = W[0].cols;
   const FwdLayout L = group_fwd_layout(M, N, K, r, G);
   if ((st = check_ws(ws, ws_bytes, L.total)) != QLORA_OK) return st;
   hipStream_t s = (hipStream_t)stream;
-  const bf16_t* U = nullptr;
-  float sc = 0.0f;
+  bf16_t* U = nullptr;
   if (r > 0) {
-    sc = (float)((double)alpha / (double)r);  // s = RN32(alpha / r)
-    bf16_t* Ud = U_save ? U_save : reinterpret_cast<bf16_t*>(ws_at(ws, L.u));
+    U = U_save ? U_save : reinterpret_cast<bf16_t*>(ws_at(ws, L.u));
     // every adapter's U in one pass over X: U [M x G r] = X [A_0; A_1; ..]^T
-    st = hip_status(launch_xat(X, A, M, K, G * r, reinterpret_cast<float*>(ws_at(ws, L.part)), Ud, nullptr, 1.0f, s));
+    st = hip_status(launch_xat(X, A, M, K, G * r, reinterpret_cast<float*>(ws_at(ws, L.part)), U, nullptr, 1.0f, s));
     if (st != QLORA_OK) return st;
-    U = Ud;
   }
   bf16_t* Wd = reinterpret_cast<bf16_t*>(ws_at(ws, L.wd));
   if ((st = group_dequant(W, G, false, Wd, s)) != QLORA_OK) return st;
-  return hip_status(launch_bf16_group(Wd, (int64_t)G * N, K, X, M, U, G * r, B, false, r, N, sc, Y, s));
+  return group_fwd_product(Wd, G, N, K, X, M, U, B, r, alpha, Y, s);
 }
 
 qlora_status qlora_group_bwd(const qlora_nf4_weight* W, int32_t G, const uint16_t* X, const uint16_t* dY,
                              int64_t M, const uint16_t* A, const uint16_t* B, int32_t r, float alpha,
                              const uint16_t* U_saved, uint16_t* dX, float* dA, float* dB, void* ws,
                              size_t ws_bytes, void* stream) {
-  qlora_status st = check_group(W, G, M, r, A, B);
+  qlora_status st = check_group_weights(W, G);
   if (st != QLORA_OK) return st;
+  if ((st = check_rank(r, A, B)) != QLORA_OK) return st;
+  const int64_t N = W[0].rows, K = W[0].cols, NG = (int64_t)G * N;
+  if ((st = check_group_shape(M, N, K, r, G)) != QLORA_OK) return st;
   if (!dY) return QLORA_E_NULL;
   if (!aligned16(dY) || (dX && !aligned16(dX)) || (U_saved && !aligned16(U_saved))) return QLORA_E_ALIGN;
   if (r > 0) {
@@ -636,41 +679,109 @@ qlora_status qlora_group_bwd(const qlora_nf4_weight* W, int32_t G, const uint16_
   } else if (dA || dB) {
     return QLORA_E_SHAPE;   // no adapter, no adapter gradients
   }
-  const int64_t N = W[0].rows, K = W[0].cols, NG = (int64_t)G * N;
-  const int32_t rg = G * r;
   const BwdLayout L = group_bwd_layout(M, N, K, r, G, dX != nullptr);
   if ((st = check_ws(ws, ws_bytes, L.total)) != QLORA_OK) return st;
   hipStream_t s = (hipStream_t)stream;
-  // dX = sum_g dY_g deq(W_g) + s sum_g G_g A_g: one dense product contracting
-  // over the G N columns of dY, with the stacked adapters as a rank-G r tail
-  auto run_dx = [&](const bf16_t* Gm, float sc) -> qlora_status {
-    bf16_t* WdT = reinterpret_cast<bf16_t*>(ws_at(ws, L.wdt));
-    qlora_status st2 = group_dequant(W, G, true, WdT, s);
-    if (st2 != QLORA_OK) return st2;
-    return hip_status(launch_bf16_group(WdT, K, NG, dY, M, Gm, rg, r > 0 ? A : nullptr, true, rg, K, sc, dX, s));
-  };
-  if (r == 0) return dX ? run_dx(nullptr, 0.0f) : QLORA_OK;
-  const float sc = (float)((double)alpha / (double)r);
+  bf16_t* WdT = dX ? reinterpret_cast<bf16_t*>(ws_at(ws, L.wdt)) : nullptr;
+  if (r == 0) {
+    if (!dX) return QLORA_OK;
+    if ((st = group_dequant(W, G, true, WdT, s)) != QLORA_OK) return st;
+    return group_dx_product(WdT, G, N, K, dY, M, nullptr, nullptr, 0, alpha, dX, s);
+  }
   bf16_t* Gm = reinterpret_cast<bf16_t*>(ws_at(ws, L.g));
   float* part = reinterpret_cast<float*>(ws_at(ws, L.part));
   const bf16_t* U = U_saved;
   if (!U) {
     bf16_t* Ud = reinterpret_cast<bf16_t*>(ws_at(ws, L.u));
-    if ((st = hip_status(launch_xat(X, A, M, K, rg, part, Ud, nullptr, 1.0f, s))) != QLORA_OK) return st;
+    if ((st = hip_status(launch_xat(X, A, M, K, G * r, part, Ud, nullptr, 1.0f, s))) != QLORA_OK) return st;
     U = Ud;
   }
   // G [M x G r]: group g is dY_g B_g
   if ((st = hip_status(launch_dyb_group(dY, NG, B, M, N, r, G, part, Gm, 1.0f, s))) != QLORA_OK) return st;
-  if (dX && (st = run_dx(Gm, sc)) != QLORA_OK) return st;
-  // dA [G r x K] = s G^T X in one pass over X; dB_g = s dY_g^T U_g
-  if ((st = hip_status(launch_gtx(Gm, X, M, K, rg, part, dA, sc, s))) != QLORA_OK) return st;
-  return hip_status(launch_dytu_group(dY, NG, U, rg, M, N, r, G, part, dB, sc, s));
+  if (dX) {
+    if ((st = group_dequant(W, G, true, WdT, s)) != QLORA_OK) return st;
+    if ((st = group_dx_product(WdT, G, N, K, dY, M, Gm, A, r, alpha, dX, s)) != QLORA_OK) return st;
+  }
+  return group_grads(X, dY, U, Gm, M, N, K, r, G, alpha, dA, dB, part, s);
+}
+
+qlora_status qlora_group_dequant(const qlora_nf4_weight* W, int32_t G, uint16_t* Wd_out, void* stream) {
+  qlora_status st = check_group_weights(W, G);
+  if (st != QLORA_OK) return st;
+  if (!Wd_out) return QLORA_E_NULL;
+  if (!aligned16(Wd_out)) return QLORA_E_ALIGN;
+  return group_dequant(W, G, false, Wd_out, (hipStream_t)stream);
+}
+
+qlora_status qlora_group_dequant_t(const qlora_nf4_weight* W, int32_t G, uint16_t* WdT_out, void* stream) {
+  qlora_status st = check_group_weights(W, G);
+  if (st != QLORA_OK) return st;
+  if (!WdT_out) return QLORA_E_NULL;
+  if (!aligned16(WdT_out)) return QLORA_E_ALIGN;
+  // the transposing grid has ceil(N / 64) rows; rows of the result are G N apart
+  if ((W[0].rows + 63) / 64 > 65535 || W[0].cols / 64 > 0x7FFFFFFF) return QLORA_E_UNSUPPORTED;
+  return group_dequant(W, G, true, WdT_out, (hipStream_t)stream);
+}
+
+qlora_status qlora_bf16_group_fwd(const uint16_t* Wd, int32_t G, int64_t N, int64_t K, const uint16_t* X, int64_t M,
+                                  const uint16_t* U, const uint16_t* B, int32_t r, float alpha, uint16_t* Y,
+                                  void* stream) {
+  qlora_status st = check_group_shape(M, N, K, r, G);
+  if (st != QLORA_OK) return st;
+  if (!Wd || !X || !Y) return QLORA_E_NULL;
+  if (!aligned16(Wd) || !aligned16(X) || !aligned16(Y)) return QLORA_E_ALIGN;
+  if ((st = check_rank(r, U, B)) != QLORA_OK) return st;
+  return group_fwd_product(Wd, G, N, K, X, M, U, B, r, alpha, Y, (hipStream_t)stream);
+}
+
+qlora_status qlora_bf16_group_dx(const uint16_t* WdT, int32_t G, int64_t N, int64_t K, const uint16_t* dY,
+                                 int64_t M, const uint16_t* Gm, const uint16_t* A, int32_t r, float alpha,
+                                 uint16_t* dX, void* stream) {
+  qlora_status st = check_group_shape(M, N, K, r, G);
+  if (st != QLORA_OK) return st;
+  if (!WdT || !dY || !dX) return QLORA_E_NULL;
+  if (!aligned16(WdT) || !aligned16(dY) || !aligned16(dX)) return QLORA_E_ALIGN;
+  if ((st = check_rank(r, Gm, A)) != QLORA_OK) return st;
+  return group_dx_product(WdT, G, N, K, dY, M, Gm, A, r, alpha, dX, (hipStream_t)stream);
+}
+
+qlora_status qlora_group_lora_dy_b(const uint16_t* dY, const uint16_t* B, int64_t M, int64_t N, int32_t r,
+                                   int32_t G, uint16_t* Gm, void* ws, size_t ws_bytes, void* stream) {
+  qlora_status st = check_adapter_rank(r);
+  if (st != QLORA_OK) return st;
+  if (G < 1 || M <= 0 || M > 0x7FFFFFFF || N <= 0 || N % 8 != 0) return QLORA_E_SHAPE;
+  if ((int64_t)G * r > kMaxGroupRank || !skinny_cols_ok((int64_t)G * N)) return QLORA_E_UNSUPPORTED;
+  if (!dY || !B || !Gm) return QLORA_E_NULL;
+  if (!aligned16(dY) || !aligned16(B) || !aligned16(Gm)) return QLORA_E_ALIGN;
+  if ((st = check_ws(ws, ws_bytes, align_up(skinny_partial_bytes(M, G * r, N, kDyB)))) != QLORA_OK) return st;
+  return hip_status(launch_dyb_group(dY, (int64_t)G * N, B, M, N, r, G, static_cast<float*>(ws), Gm, 1.0f,
+                                     (hipStream_t)stream));
+}
+
+qlora_status qlora_group_lora_grads(const uint16_t* X, const uint16_t* dY, const uint16_t* U, const uint16_t* Gm,
+                                    int64_t M, int64_t N, int64_t K, int32_t r, int32_t G, float alpha, float* dA,
+                                    float* dB, void* ws, size_t ws_bytes, void* stream) {
+  qlora_status st = check_adapter_rank(r);
+  if (st != QLORA_OK) return st;
+  if (G < 1 || M <= 0 || M > 0x7FFFFFFF || N <= 0 || N % 8 != 0 || K <= 0 || K % 8 != 0) return QLORA_E_SHAPE;
+  const int64_t NG = (int64_t)G * N;
+  if ((int64_t)G * r > kMaxGroupRank) return QLORA_E_UNSUPPORTED;
+  // X and dY are addressed with 32-bit byte offsets
+  if (M > (int64_t)0x7FFFFFFF / K || M > (int64_t)0x7FFFFFFF / NG) return QLORA_E_UNSUPPORTED;
+  if (!X || !dY || !U || !Gm || !dA || !dB) return QLORA_E_NULL;
+  if (!aligned16(X) || !aligned16(dY) || !aligned16(U) || !aligned16(Gm) || !aligned16(dA) || !aligned16(dB))
+    return QLORA_E_ALIGN;
+  const size_t need = align_up(std::max(skinny_partial_bytes(G * r, K, M, kGtX),
+                                        (size_t)G * skinny_partial_bytes(N, r, M, kDytU)));
+  if ((st = check_ws(ws, ws_bytes, need)) != QLORA_OK) return st;
+  return group_grads(X, dY, U, Gm, M, N, K, r, G, alpha, dA, dB, static_cast<float*>(ws), (hipStream_t)stream);
 }
 
 qlora_status qlora_lora_down(const uint16_t* X, const uint16_t* A, int64_t M, int64_t K, int32_t r, uint16_t* U,
                              void* ws, size_t ws_bytes, void* stream) {
-  qlora_status st = check_adapter_rank(r);
-  if (st != QLORA_OK) return st;
+  // up to kMaxGroupRank: a group's stacked adapters
+  if (r <= 0 || r > kMaxGroupRank || r % 8 != 0) return QLORA_E_UNSUPPORTED;
+  qlora_status st = QLORA_OK;
   if (M <= 0 || M > 0x7FFFFFFF || K <= 0 || K % 8 != 0) return QLORA_E_SHAPE;
   if (!skinny_cols_ok(K)) return QLORA_E_UNSUPPORTED;
   if (!X || !A || !U) return QLORA_E_NULL;

@@ -497,6 +497,82 @@ def bf16_dx(WdT: torch.Tensor, dY, G=None, A=None, alpha: float = 0.0, out=None)
     return dX
 
 
+def group_dequant(qs: Sequence[QuantizedWeight], out=None, transposed=False):
+    """The G weights dequantized into one stack [G N x K], or side by side
+    transposed [K x G N]."""
+    G, N, K = len(qs), qs[0].rows, qs[0].cols
+    shape = (K, G * N) if transposed else (G * N, K)
+    out = out if out is not None else torch.empty(*shape, dtype=torch.bfloat16, device=qs[0].codes.device)
+    _need(out, torch.bfloat16, "out", shape)
+    fn = lib().qlora_group_dequant_t if transposed else lib().qlora_group_dequant
+    check(fn(_group_descs(qs), G, _ptr(out), _stream()),
+          "qlora_group_dequant_t" if transposed else "qlora_group_dequant")
+    return out
+
+
+def bf16_group_fwd(Wd: torch.Tensor, G: int, X, U=None, B=None, alpha: float = 0.0, out=None):
+    """The group's dense forward product on the stack Wd [G N x K]:
+    Y [M x G N] = X Wd^T + s (U_g B_g^T side by side)."""
+    _need(Wd, torch.bfloat16, "Wd")
+    _need(X, torch.bfloat16, "X")
+    N, K, M = Wd.shape[0] // G, Wd.shape[1], X.shape[0]
+    r = 0 if U is None else U.shape[1] // G
+    if r:
+        _need(U, torch.bfloat16, "U", (M, G * r))
+        _need(B, torch.bfloat16, "B", (G * N, r))
+    Y = out if out is not None else torch.empty(M, G * N, dtype=torch.bfloat16, device=X.device)
+    _need(Y, torch.bfloat16, "Y", (M, G * N))
+    check(lib().qlora_bf16_group_fwd(_ptr(Wd), G, N, K, _ptr(X), M, _ptr(U), _ptr(B), r, float(alpha), _ptr(Y),
+                                     _stream()), "qlora_bf16_group_fwd")
+    return Y
+
+
+def bf16_group_dx(WdT: torch.Tensor, G: int, dY, Gm=None, A=None, alpha: float = 0.0, out=None):
+    """The group's dense dX product on WdT [K x G N]: dX = dY WdT^T + s Gm A."""
+    _need(WdT, torch.bfloat16, "WdT")
+    _need(dY, torch.bfloat16, "dY")
+    K, N, M = WdT.shape[0], WdT.shape[1] // G, dY.shape[0]
+    r = 0 if Gm is None else Gm.shape[1] // G
+    if r:
+        _need(Gm, torch.bfloat16, "Gm", (M, G * r))
+        _need(A, torch.bfloat16, "A", (G * r, K))
+    dX = out if out is not None else torch.empty(M, K, dtype=torch.bfloat16, device=dY.device)
+    _need(dX, torch.bfloat16, "dX", (M, K))
+    check(lib().qlora_bf16_group_dx(_ptr(WdT), G, N, K, _ptr(dY), M, _ptr(Gm), _ptr(A), r, float(alpha), _ptr(dX),
+                                    _stream()), "qlora_bf16_group_dx")
+    return dX
+
+
+def group_lora_dy_b(dY, B, G: int, Gm=None, ws=None):
+    """Gm [M x G r]: columns g r .. are dY_g B_g (bf16)."""
+    _need(dY, torch.bfloat16, "dY")
+    M, N = dY.shape[0], dY.shape[1] // G
+    r = B.shape[1]
+    _need(B, torch.bfloat16, "B", (G * N, r))
+    Gm = Gm if Gm is not None else torch.empty(M, G * r, dtype=torch.bfloat16, device=dY.device)
+    if ws is None:
+        ws = workspace(workspace_bytes(_lib.QLORA_OP_GROUP_LORA, M, N, 64, r, G), dY.device)
+    check(lib().qlora_group_lora_dy_b(_ptr(dY), _ptr(B), M, N, r, G, _ptr(Gm), _ptr(ws),
+                                      0 if ws is None else ws.numel(), _stream()), "qlora_group_lora_dy_b")
+    return Gm
+
+
+def group_lora_grads(X, dY, U, Gm, G: int, alpha, dA=None, dB=None, ws=None):
+    """dA [G r x K] = s Gm^T X and dB [G N x r], dB_g = s dY_g^T U_g (fp32)."""
+    M, K = X.shape
+    N, r = dY.shape[1] // G, U.shape[1] // G
+    for t, n, shp in ((X, "X", (M, K)), (dY, "dY", (M, G * N)), (U, "U", (M, G * r)), (Gm, "Gm", (M, G * r))):
+        _need(t, torch.bfloat16, n, shp)
+    dA = dA if dA is not None else torch.empty(G * r, K, dtype=torch.float32, device=X.device)
+    dB = dB if dB is not None else torch.empty(G * N, r, dtype=torch.float32, device=X.device)
+    if ws is None:
+        ws = workspace(workspace_bytes(_lib.QLORA_OP_GROUP_LORA, M, N, K, r, G), X.device)
+    check(lib().qlora_group_lora_grads(_ptr(X), _ptr(dY), _ptr(U), _ptr(Gm), M, N, K, r, G, float(alpha), _ptr(dA),
+                                       _ptr(dB), _ptr(ws), 0 if ws is None else ws.numel(), _stream()),
+          "qlora_group_lora_grads")
+    return dA, dB
+
+
 def nf4_dx(q: QuantizedWeight, dY, G=None, A=None, alpha: float = 0.0, out=None):
     """The fused backward GEMM: dX = dY deq(W) + s G A."""
     _need(dY, torch.bfloat16, "dY")

@@ -84,7 +84,11 @@ typedef enum {
   QLORA_OP_FWD_FUSED = 4,  /* qlora_linear_fwd, fused path only             */
   QLORA_OP_BWD_FUSED = 5,  /* qlora_linear_bwd, fused path only             */
   QLORA_OP_GROUP_FWD = 6,  /* qlora_group_fwd (njobs = G, the group size)   */
-  QLORA_OP_GROUP_BWD = 7   /* qlora_group_bwd (njobs = G, the group size)   */
+  QLORA_OP_GROUP_BWD = 7,  /* qlora_group_bwd (njobs = G, the group size)   */
+  QLORA_OP_GROUP_LORA = 8  /* the group building blocks' side products:
+                              qlora_lora_down at rank G r,
+                              qlora_group_lora_dy_b, qlora_group_lora_grads
+                              (njobs = G)                                    */
 } qlora_op;
 
 /* A quantized weight: host struct holding device pointers.
@@ -171,8 +175,9 @@ qlora_status qlora_sizes(int64_t rows, int64_t cols, int32_t blocksize, int32_t 
 /* Bytes of scratch the given call needs (0 when none).  FWD/BWD: M tokens,
  * N = rows, K = cols, LoRA rank r; GEMV: njobs jobs, with N and K the
  * largest rows/cols among them; LORA: the split-contraction partial sums of
- * the LoRA side products of one M x N x K, rank-r layer.  Returns 0 for
- * invalid sizes. */
+ * the LoRA side products of one M x N x K, rank-r layer (r up to 256 for
+ * qlora_lora_down on a group's stacked adapters).  Returns 0 for invalid
+ * sizes. */
 size_t qlora_workspace_bytes(qlora_op op, int64_t M, int64_t N, int64_t K, int32_t r, int32_t njobs);
 
 /* Quantize bf16 W [rows x cols] into q (codes, absmax_q, group_scale are
@@ -364,6 +369,47 @@ qlora_status qlora_group_bwd(const qlora_nf4_weight* W, int32_t G, const uint16_
                              const uint16_t* U_saved, uint16_t* dX, float* dA, float* dB, void* ws,
                              size_t ws_bytes, void* stream);
 
+/* Building blocks of the group calls, for callers that keep U and G, or time
+ * the dense products on their own:
+ *   qlora_group_fwd = qlora_lora_down (rank G r, the stacked A)
+ *                     + qlora_group_dequant + qlora_bf16_group_fwd;
+ *   qlora_group_bwd = [qlora_lora_down] + qlora_group_lora_dy_b
+ *                     + qlora_group_dequant_t + qlora_bf16_group_dx
+ *                     + qlora_group_lora_grads.
+ * Same layouts and conditions as the group calls; ws is sized by
+ * qlora_workspace_bytes(QLORA_OP_GROUP_LORA, M, N, K, r, G). */
+
+/* Wd_out [G N x K] bf16: deq(W_g) in rows g N .. g N + N - 1. */
+qlora_status qlora_group_dequant(const qlora_nf4_weight* W, int32_t G, uint16_t* Wd_out, void* stream);
+
+/* WdT_out [K x G N] bf16: deq(W_g)^T in columns g N .. g N + N - 1.
+ * Requires rows < 65536 * 64. */
+qlora_status qlora_group_dequant_t(const qlora_nf4_weight* W, int32_t G, uint16_t* WdT_out, void* stream);
+
+/* Y [M x G N] = X Wd^T + s (U_g B_g^T side by side), Wd [G N x K] the stack,
+ * U [M x G r] and B [G N x r] (r == 0: U = B = NULL).  No workspace. */
+qlora_status qlora_bf16_group_fwd(const uint16_t* Wd, int32_t G, int64_t N, int64_t K, const uint16_t* X,
+                                  int64_t M, const uint16_t* U, const uint16_t* B, int32_t r, float alpha,
+                                  uint16_t* Y, void* stream);
+
+/* dX [M x K] = dY WdT^T + s Gm A, WdT [K x G N], dY [M x G N], Gm [M x G r]
+ * (Gm_g = dY_g B_g) and the stacked A [G r x K] (r == 0: Gm = A = NULL).
+ * No workspace. */
+qlora_status qlora_bf16_group_dx(const uint16_t* WdT, int32_t G, int64_t N, int64_t K, const uint16_t* dY,
+                                 int64_t M, const uint16_t* Gm, const uint16_t* A, int32_t r, float alpha,
+                                 uint16_t* dX, void* stream);
+
+/* Gm [M x G r] (bf16): columns g r .. are dY_g B_g, dY [M x G N], B [G N x r].
+ * r in (0, 128], G r <= 256, N % 8 == 0, G N < 2^24. */
+qlora_status qlora_group_lora_dy_b(const uint16_t* dY, const uint16_t* B, int64_t M, int64_t N, int32_t r,
+                                   int32_t G, uint16_t* Gm, void* ws, size_t ws_bytes, void* stream);
+
+/* dA [G r x K] = s Gm^T X and dB [G N x r] with dB_g = s dY_g^T U_g (fp32,
+ * overwritten); U, Gm [M x G r].  M K and M G N below 2^31. */
+qlora_status qlora_group_lora_grads(const uint16_t* X, const uint16_t* dY, const uint16_t* U, const uint16_t* Gm,
+                                    int64_t M, int64_t N, int64_t K, int32_t r, int32_t G, float alpha,
+                                    float* dA, float* dB, void* ws, size_t ws_bytes, void* stream);
+
 /* ---- Building blocks of the forward and backward passes ----------------
  * qlora_linear_fwd = qlora_lora_down + qlora_nf4_fwd;
  * qlora_linear_bwd = [qlora_lora_down] + qlora_lora_dy_b + qlora_nf4_dx
@@ -373,8 +419,9 @@ qlora_status qlora_group_bwd(const qlora_nf4_weight* W, int32_t G, const uint16_
  * qlora_workspace_bytes(QLORA_OP_LORA, M, N, K, r, 0). */
 
 /* U [M x r] = X A^T (bf16).  deepfa.ir "LoRA: Prerequisite": the adapter's
- * down-projection.  r in (0, 128], r % 8 == 0, K % 8 == 0, K < 2^24
- * (QLORA_E_UNSUPPORTED otherwise). */
+ * down-projection.  r in (0, 256] (above 128: the stacked adapters of a
+ * group, with ws sized by QLORA_OP_GROUP_LORA), r % 8 == 0, K % 8 == 0,
+ * K < 2^24 (QLORA_E_UNSUPPORTED otherwise). */
 qlora_status qlora_lora_down(const uint16_t* X, const uint16_t* A, int64_t M, int64_t K, int32_t r,
                              uint16_t* U, void* ws, size_t ws_bytes, void* stream);
 

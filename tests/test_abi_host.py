@@ -321,3 +321,39 @@ def test_group_calls_validate_on_the_host(L):
     assert gb(three, 3, 4, 0, fake, fake, None) == 3                                 # no adapter, no dA
     assert gb(three, 3, 4, 16, fake, fake, fake, n=16) == 5
     assert gb(W(_desc(128, 64), _desc(128, 128)), 2, 4, 16, fake, fake, fake) == 3
+
+
+def test_group_building_blocks_validate_on_the_host(L):
+    fake, big = ctypes.c_void_p(4096), 1 << 40
+    W = lambda *ds: (Nf4WeightDesc * len(ds))(*ds)
+    two = W(_desc(128, 64), _desc(128, 64))
+    assert L.qlora_group_dequant(None, 2, fake, None) == 1
+    assert L.qlora_group_dequant(two, 0, fake, None) == 3
+    assert L.qlora_group_dequant(two, 2, None, None) == 1
+    assert L.qlora_group_dequant_t(two, 2, ctypes.c_void_p(4100), None) == 2
+    assert L.qlora_group_dequant_t(W(_desc(128, 64), _desc(64, 64)), 2, fake, None) == 3
+    # dense products: G N K, N % 64, ranks
+    assert L.qlora_bf16_group_fwd(fake, 0, 128, 64, fake, 4, None, None, 0, 0.0, fake, None) == 3
+    assert L.qlora_bf16_group_fwd(fake, 2, 72, 64, fake, 4, None, None, 0, 0.0, fake, None) == 4
+    assert L.qlora_bf16_group_fwd(fake, 3, 128, 64, fake, 4, fake, fake, 96, 16.0, fake, None) == 4
+    assert L.qlora_bf16_group_fwd(fake, 2, 128, 64, fake, 4, None, fake, 16, 16.0, fake, None) == 1
+    assert L.qlora_bf16_group_fwd(fake, 2, 1 << 16, 1 << 15, fake, 4, None, None, 0, 0.0, fake, None) == 4
+    assert L.qlora_bf16_group_dx(fake, 2, 128, 64, fake, 4, fake, None, 16, 16.0, fake, None) == 1
+    assert L.qlora_bf16_group_dx(None, 2, 128, 64, fake, 4, None, None, 0, 0.0, fake, None) == 1
+    # side products
+    assert L.qlora_group_lora_dy_b(fake, fake, 4, 128, 16, 2, fake, fake, 16, None) == 5
+    assert L.qlora_group_lora_dy_b(fake, fake, 4, 128, 136, 2, fake, fake, big, None) == 4     # r > 128
+    assert L.qlora_group_lora_dy_b(fake, fake, 4, 128, 128, 3, fake, fake, big, None) == 4     # G r > 256
+    assert L.qlora_group_lora_dy_b(fake, fake, 4, 128, 16, 0, fake, fake, big, None) == 3
+    assert L.qlora_group_lora_grads(fake, fake, fake, fake, 4, 128, 64, 16, 2, 16.0, fake, fake, fake, 16,
+                                    None) == 5
+    assert L.qlora_group_lora_grads(fake, fake, None, fake, 4, 128, 64, 16, 2, 16.0, fake, fake, fake, big,
+                                    None) == 1
+    assert L.qlora_group_lora_grads(fake, fake, fake, fake, 1 << 20, 1 << 12, 64, 16, 2, 16.0, fake, fake, fake,
+                                    big, None) == 4                                            # M G N >= 2^31
+    # lora_down takes a group's stacked adapters (rank up to 256)
+    assert L.qlora_workspace_bytes(3, 4096, 64, 8192, 192, 0) > 0
+    assert L.qlora_workspace_bytes(3, 4096, 64, 8192, 264, 0) == 0
+    assert L.qlora_lora_down(fake, fake, 4, 64, 264, fake, fake, big, None) == 4
+    assert L.qlora_lora_down(fake, fake, 4, 64, 192, fake, fake, 16, None) == 5
+    assert L.qlora_workspace_bytes(8, 4096, 8192, 8192, 64, 3) >= L.qlora_workspace_bytes(3, 4096, 64, 8192, 192, 0)

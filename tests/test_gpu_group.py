@@ -167,3 +167,31 @@ def test_group_full_shape(set_name, idx):
                                         Br[g * N:(g + 1) * N], alpha)
         assert_close(torch_to_f64(dA[g * r:(g + 1) * r]), dAr, f"{label} dA_{g}")
         assert_close(torch_to_f64(dB[g * N:(g + 1) * N]), dBr, f"{label} dB_{g}")
+
+
+@pytest.mark.parametrize("G,M,N,K,r", [(3, 300, 320, 192, 16), (2, 1100, 256, 256, 64)])
+def test_building_blocks_compose_to_the_group_calls(G, M, N, K, r):
+    """lora_down (stacked A) + group_dequant + bf16_group_fwd is group_fwd, and
+    group_lora_dy_b + group_dequant_t + bf16_group_dx + group_lora_grads is
+    group_bwd, bit for bit (the same kernels in the same order)."""
+    print(f"[group building blocks] G={G} M={M} N={N} K={K} r={r}", flush=True)
+    d = _draw(G, M, N, K, r, seed=99 + G)
+    qs = [ops.quantize(bits_to_torch(W)) for W in d["Ws"]]
+    X, dY, A, B = (bits_to_torch(d[k]) for k in ("X", "dY", "A", "B"))
+    alpha = 16.0
+    Y, U = ops.group_fwd(qs, X, A, B, alpha, save_u=True)
+    dX, dA, dB = ops.group_bwd(qs, X, dY, A, B, alpha, U=U)
+
+    U2 = ops.lora_down(X, A)
+    Y2 = ops.bf16_group_fwd(ops.group_dequant(qs), G, X, U2, B, alpha)
+    Gm = ops.group_lora_dy_b(dY, B, G)
+    dX2 = ops.bf16_group_dx(ops.group_dequant(qs, transposed=True), G, dY, Gm, A, alpha)
+    dA2, dB2 = ops.group_lora_grads(X, dY, U2, Gm, G, alpha)
+    torch.cuda.synchronize()
+    for name, a, b in (("U", U, U2), ("Y", Y, Y2), ("dX", dX, dX2), ("dA", dA, dA2), ("dB", dB, dB2)):
+        assert torch.equal(a, b), name
+    # the stacks are the per-weight dequantizations, in place
+    Wd, WdT = ops.group_dequant(qs), ops.group_dequant(qs, transposed=True)
+    for g, q in enumerate(qs):
+        assert torch.equal(Wd[g * N:(g + 1) * N], ops.dequant(q))
+        assert torch.equal(WdT[:, g * N:(g + 1) * N], ops.dequant_t(q))
