@@ -13,6 +13,11 @@
 // in pairs of 32-wide stages: a pair (64 columns: one 128-byte line of every
 // row) comes into one of two LDS pair slots by buffer->LDS DMA, each
 // instruction moving 8 whole rows, one pair ahead; one barrier per pair.
+//
+//   dX        the same kernel on deq(W)^T: dX = dY (W^T)^T + s G (A^T)^T,
+//             with A read column-wise in the LoRA tail;
+//   groups    weight rows in groups of gn, each with its own adapter (the
+//             stacked q/k/v or gate/up weights of one layer).
 #include <algorithm>
 
 #include "gemm_common.h"
@@ -91,13 +96,23 @@ struct PairOffs {
 //               pair have landed and its reads of this pair have completed;
 //               after it the next pair is visible to every wave and no wave
 //               reads this pair's slot any more.
-//   DMA         odd substeps, slots 4 FI ..: the pair after next into this
-//               pair's slot (2 FI weight-row, then 8 token-row instructions of
-//               8 whole 128-byte rows each), spread over the second half.
+//   DMA         the pair after next into this pair's slot (2 FI weight-row,
+//               then 8 token-row instructions of 8 whole 128-byte rows each):
+//               the first FI + 4 in the odd substep's slots 4 FI .., every
+//               other slot; the other FI + 4 in the next pair's even substep,
+//               one every fourth slot.  Issued all in the odd substep's
+//               second half, 16 instructions per wave in 16 MFMA slots
+//               overran the texture address queue (its FIFO full about 10 %
+//               of the cycles) and stalled issue; split, the product ran
+//               about 7 % faster.
 template <int FI>
 constexpr int rd_slot(int q) { return q * 4 * FI / (FI + 4); }
 template <int FI>
-constexpr int dma_slot(int d) { return 4 * FI + d * 4 * FI / (2 * FI + 8); }
+constexpr int dma_half = FI + 4;   // DMAs of a pair issued in its odd substep
+template <int FI>
+constexpr int dma_slot_a(int d) { return 4 * FI + d * 4 * FI / dma_half<FI>; }
+template <int FI>
+constexpr int dma_slot_b(int d) { return (d - dma_half<FI>) * 8 * FI / dma_half<FI>; }
 
 template <int FI, int X, int HF>
 __device__ __forceinline__ void dense_slot(const char* cur, const char* nxt, char* fill, const DenseOps& f,
@@ -131,8 +146,16 @@ __device__ __forceinline__ void dense_slot(const char* cur, const char* nxt, cha
   }
   if constexpr (HF == 1 && kk == 1) {
 #pragma unroll
-    for (int d = 0; d < 2 * FI + 8; ++d)
-      if (dma_slot<FI>(d) == X) pair_dma<FI>(fill, f, pair + 2, d);
+    for (int d = 0; d < dma_half<FI>; ++d)
+      if (dma_slot_a<FI>(d) == X) pair_dma<FI>(fill, f, pair + 2, d);
+  }
+  if constexpr (HF == 0) {
+    // the rest of pair + 1's DMAs into nxt, which no wave reads before the
+    // barrier of this pair (in the first pair they re-load what the
+    // prologue loaded: the same bytes to the same place)
+#pragma unroll
+    for (int d = dma_half<FI>; d < 2 * FI + 8; ++d)
+      if (dma_slot_b<FI>(d) == X) pair_dma<FI>(const_cast<char*>(nxt), f, pair + 1, d);
   }
   __builtin_amdgcn_sched_barrier(0);
 }
@@ -147,29 +170,56 @@ __device__ __forceinline__ void dense_slots(const char* cur, const char* nxt, ch
   }
 }
 
-// Weight half of the LoRA tail: B'[row0 + row, j0 + 8 c ..] into a 64-byte-row
-// tile (zero past the rank, and for rows outside [lo, hi)), where B' is B
-// [rows x r] or, with b_trans, the transpose of B [r x rows] (read
-// column-wise).
-__device__ __forceinline__ void tail_rows(char* dst, const bf16_t* Bm, bool b_trans, int64_t rows, int r,
-                                          int64_t row0, int j0, int64_t lo, int64_t hi) {
+// One 32-wide chunk of the LoRA tail, in registers: the weight half
+// B'[row0 + row, j0 ..] (zero past the rank, and for rows outside [lo, hi))
+// and the token half T[trow0 + row, j0 + 8 c ..] (T is trows x rank with
+// row stride ld; zero past the rank and the last row).  Token half: thread t
+// holds row (t + 256 e) >> 2, 16-byte chunk (t + 256 e) & 3.  Weight half:
+// B' is B [rows x r], held like the tokens; or, with b_trans, the transpose
+// of B [r x rows], read along its rows (coalesced): thread t holds B[j0 +
+// (i >> 5)][row0 + 8 (i & 31) ..] for i = t + 256 e.
+struct TailRegs {
+  uint4 w[4], t[4];
+};
+__device__ __forceinline__ void tail_load(TailRegs& R, const bf16_t* Bm, bool b_trans, int64_t rows, int r,
+                                          int64_t row0, int j0, int64_t lo, int64_t hi, const bf16_t* T,
+                                          int64_t ld, int64_t trows, int64_t trow0) {
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int idx = threadIdx.x + kThreads * e;
     const int row = idx >> 2, c = idx & 3, col = j0 + 8 * c;
     uint4 v = make_uint4(0u, 0u, 0u, 0u);
-    if (col < r && row0 + row >= lo && row0 + row < hi) {
-      if (!b_trans) {
+    if (!b_trans) {
+      if (col < r && row0 + row >= lo && row0 + row < hi)
         v = *reinterpret_cast<const uint4*>(Bm + (row0 + row) * r + col);
-      } else {
-        const bf16_t* p = Bm + (int64_t)col * rows + row0 + row;
-        uint32_t w[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) w[q] = (uint32_t)p[2 * q * rows] | ((uint32_t)p[(2 * q + 1) * rows] << 16);
-        v = make_uint4(w[0], w[1], w[2], w[3]);
-      }
+    } else {
+      // rows % 8 == 0 and lo, hi multiples of 8: the 8 rows are all in or all out
+      const int j = j0 + (idx >> 5);
+      const int64_t rr = row0 + 8 * (idx & 31);
+      if (j < r && rr >= lo && rr < hi) v = *reinterpret_cast<const uint4*>(Bm + (int64_t)j * rows + rr);
     }
-    wr16(dst + spos(row, c), v);
+    R.w[e] = v;
+    uint4 u = make_uint4(0u, 0u, 0u, 0u);
+    if (col < r && trow0 + row < trows) u = *reinterpret_cast<const uint4*>(T + (trow0 + row) * ld + col);
+    R.t[e] = u;
+  }
+}
+// The chunk into LDS: s T as a 64-byte-row tile at dst + kOp; the weights
+// at dst, as a 64-byte-row tile or, with b_trans, as a tile of 32 rank rows
+// x 256 weight rows (512-byte rows, 32-byte block b of rank row n at
+// b ^ (n & 3)) for transposed fragment reads.
+__device__ __forceinline__ void tail_store(char* dst, const TailRegs& R, bool b_trans, float s) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int idx = threadIdx.x + kThreads * e;
+    const int row = idx >> 2, c = idx & 3;
+    if (!b_trans) {
+      wr16(dst + spos(row, c), R.w[e]);
+    } else {
+      const int n = idx >> 5, sg = idx & 31;
+      wr16(dst + n * 512 + 32 * ((sg >> 1) ^ (n & 3)) + 16 * (sg & 1), R.w[e]);
+    }
+    wr16(dst + kOp + spos(row, c), scale16(R.t[e], s));
   }
 }
 
@@ -256,31 +306,43 @@ __global__ __launch_bounds__(kThreads, 1) void bf16_fwd_kernel(const bf16_t* __r
     // Weight rows come in groups of gn, each with its own adapter: rows of
     // group g take columns g r .. of U (row stride ldu) and their rows of B;
     // a tile that straddles groups runs the tail once per group, with the
-    // other groups' rows zero.
+    // other groups' rows zero.  Chunks alternate between two tile pairs:
+    // chunk c + 1 is loaded into registers while chunk c is multiplied, and
+    // one barrier per chunk both publishes a chunk and retires the buffer
+    // the next store overwrites (its readers finished before they stored
+    // their part of the chunk in between).
     const FragOffs fo = frag_offs(lane);
     const int am64 = wc * 32 * FI * 64, bm64 = wr * 128 * 64;
-    const int64_t g_last = (min(n0 + 64 * FI, N) - 1) / gn;
-    for (int64_t g = n0 / gn; g <= g_last; ++g)
-    for (int j0 = 0; j0 < r; j0 += 32) {
-      tail_rows(smem, Bl, b_trans != 0, N, r, n0, j0, g * gn, min((g + 1) * gn, N));
-      tail_tokens(smem + kOp, U + g * r, ldu, M, r, m0, j0, s);
-      QLORA_WAIT(0, 0);
-      __builtin_amdgcn_s_barrier();
+    const int64_t g0 = n0 / gn, g_last = (min(n0 + 64 * FI, N) - 1) / gn;
+    const int nj = (r + 31) / 32;
+    const int nt = (int)(g_last - g0 + 1) * nj;
+    TailRegs R;
+    auto load = [&](int t) {
+      const int64_t g = g0 + t / nj;
+      tail_load(R, Bl, b_trans != 0, N, r, n0, 32 * (t % nj), g * gn, min((g + 1) * gn, N), U + g * r, ldu, M,
+                m0);
+    };
+    load(0);
+    for (int t = 0; t < nt; ++t) {
+      char* buf = smem + (t & 1) * 2 * kOp;
+      tail_store(buf, R, b_trans != 0, s);
+      if (t + 1 < nt) load(t + 1);
+      __syncthreads();
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
         const int o = kk ? fo.o1 : fo.o0;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          if (i < FI) F.a0[i] = rd16(smem + am64 + i * 2048 + o);
-          F.b0[i] = rd16(smem + kOp + bm64 + i * 2048 + o);
+          if (i < FI)
+            F.a0[i] = b_trans ? tr_frag<512>(buf + kk * 16 * 512 + tr_off<512>(wc * FI + i))
+                              : rd16(buf + am64 + i * 2048 + o);
+          F.b0[i] = rd16(buf + kOp + bm64 + i * 2048 + o);
         }
 #pragma unroll
         for (int i = 0; i < FI; ++i)
 #pragma unroll
           for (int j = 0; j < 4; ++j) acc[i][j] = mfma32x32x16(F.a0[i], F.b0[j], acc[i][j]);
       }
-      QLORA_WAIT(0, 0);
-      __builtin_amdgcn_s_barrier();
     }
   }
   store_tile<FI>(acc, Y, N, M, N, m0, n0);

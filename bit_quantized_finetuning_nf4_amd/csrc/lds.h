@@ -45,6 +45,22 @@ __device__ __forceinline__ uint2 rd_tr(const char* p) {
   return __builtin_bit_cast(uint2, v);
 }
 
+// Transposed-read fragment of a tile whose rows (32 per stage, 2 k16 steps)
+// are the contraction and whose columns are an MFMA operand's rows: row
+// pitch PB bytes, 32-byte column block b of row n stored at b ^ (n & 3).
+// Lane (g = lane >> 4, sl = lane & 15) reads row 8 (g >> 1) + (sl >> 2),
+// columns 32 f + 16 (g & 1) + 4 (sl & 3) .. +3; a second read 4 rows down
+// completes the lane's 8 contraction elements.
+template <int PB>
+__device__ __forceinline__ int tr_off(int f) {
+  const int lane = threadIdx.x & 63, g = lane >> 4, sl = lane & 15, n0 = 8 * (g >> 1) + (sl >> 2);
+  return n0 * PB + 32 * ((2 * f + (g & 1)) ^ (n0 & 3)) + 8 * (sl & 3);
+}
+template <int PB>
+__device__ __forceinline__ bf16x8_t tr_frag(const char* p) {
+  const uint2 lo = rd_tr(p), hi = rd_tr(p + 4 * PB);
+  return __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
+}
 // Position of 16-byte chunk c of row r in a 64-byte-row tile.
 __device__ __forceinline__ int spos(int r, int c) { return r * 64 + 16 * (c ^ ((r >> 2) & 3)); }
 

@@ -93,7 +93,10 @@ def test_decode_gemv_65b_layer_set():
         deq = oracle_quantize_rows(w_bits, K, rows)
         Wd = np.stack([deq[n] for n in rows])
         yr = oracle.gemv(Wd, torch_to_f64(x), torch_to_f64(A), torch_to_f64(B)[rows], alpha)
-        assert_close(torch_to_f64(y)[rows], yr, f"decode {name} {N}x{K} (64 rows)")
+        rel, mx = assert_close(torch_to_f64(y)[rows], yr, f"decode {name} {N}x{K} (64 rows)")
+        # the margin of the decode arithmetic (unscaled bf16 levels, fp32 block scale)
+        print(f"[decode error] {name} {N}x{K}: rel Frobenius {rel:.2e}, max {mx / np.max(np.abs(yr)):.2e} "
+              f"of max|ref|", flush=True)
 
 
 def test_decode_batch_65b_layer_set():
@@ -118,4 +121,6 @@ def test_decode_batch_65b_layer_set():
         deq = oracle_quantize_rows(w_bits, K, rows)
         Wd = np.stack([deq[n] for n in rows])
         Yr = oracle.linear_fwd(Wd, torch_to_f64(x), torch_to_f64(A), torch_to_f64(B)[rows], alpha)
-        assert_close(torch_to_f64(y)[:, rows], Yr, f"decode batch {name} {N}x{K} (16 tokens, 48 rows)")
+        rel, mx = assert_close(torch_to_f64(y)[:, rows], Yr, f"decode batch {name} {N}x{K} (16 tokens, 48 rows)")
+        print(f"[decode batch error] {name} {N}x{K}: rel Frobenius {rel:.2e}, max {mx / np.max(np.abs(Yr)):.2e} "
+              f"of max|ref|", flush=True)
