@@ -205,14 +205,20 @@ def summarize_pmc(fetch_csv, write_csv, copy_mib):
                     "dispatches of one bench run (a fused GEMM's half-tile tail dispatches included) and divided by "
                     "the number of launches; scales from an elementwise copy of copy_probe_bytes",
            "copy_probe_bytes": probe, "fetch_scale": f_scale, "write_scale": w_scale}
+    # steps in the run: the step's decode GEMV is one dispatch per step
+    steps = fetch.get("nf4_gemv_kernel", (0, 0))[1]
     for k, name in TRAFFIC_KERNELS.items():
         if k in fetch and k in write:
             tails = [t for t, n in TAIL_KERNELS.items() if n == name]
             fb = fetch[k][0] + sum(fetch[t][0] for t in tails if t in fetch)
             wb = write[k][0] + sum(write[t][0] for t in tails if t in write)
-            fpl, wpl = fb / fetch[k][1] * f_scale, wb / write[k][1] * w_scale
+            # the dense GEMM is timed per product call (8 per grouped step, one
+            # or two dispatches each): its bytes are per call, like `achieved`
+            calls = steps * 2 * len(GROUPS) if name == "dense_gemm" and steps else fetch[k][1]
+            fpl, wpl = fb / calls * f_scale, wb / calls * w_scale
             out[name] = {"source_digest": source_digest(name), "fetch_bytes_per_launch": fpl,
-                         "write_bytes_per_launch": wpl, "hbm_bytes_per_launch": fpl + wpl}
+                         "write_bytes_per_launch": wpl, "hbm_bytes_per_launch": fpl + wpl,
+                         "dispatches": fetch[k][1], "launches": calls}
     return out
 
 
@@ -682,6 +688,9 @@ def main():
                          "weights) over the decode layers")
     ap.add_argument("--no-other-sets", action="store_true",
                     help="skip the 7B, 13B and small layer sets and the dequant leg")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="time the grouped steps only (no clock window, no per-linear or fused steps): for "
+                         "counter runs, where every dispatch should belong to the headline step")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after the timed steps, run one elementwise copy (negation) of this many MiB: "
                          "a kernel of known traffic for scaling the FETCH_SIZE / WRITE_SIZE counters")
@@ -727,23 +736,24 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    # the shader clock while the same steps run (a separate window, so the
-    # sampling subprocess stays out of the timed region above)
-    sampler = ClockSampler()
-    with sampler:
-        t_end = time.perf_counter() + 2.0
-        while time.perf_counter() < t_end:
-            for _ in range(10):
-                S.step("grouped")
-            torch.cuda.synchronize()
-    clock = sampler.result()
-    log(f"[bench] clock {clock}")
-
-    per_linear = S.run("staged", args.steps, args.warmup)
-    log(f"[bench] per-linear staged step {per_linear['ms_per_step']:.3f} ms; "
-        f"fwd+bwd {per_linear['fwd_bwd_tflops']:.0f} TFLOP/s")
-    fused = S.run("fused", args.steps, args.warmup)
-    log(f"[bench] fused step {fused['ms_per_step']:.3f} ms; fwd+bwd {fused['fwd_bwd_tflops']:.0f} TFLOP/s")
+    clock = per_linear = fused = None
+    if not args.headline_only:
+        # the shader clock while the same steps run (a separate window, so the
+        # sampling subprocess stays out of the timed region above)
+        sampler = ClockSampler()
+        with sampler:
+            t_end = time.perf_counter() + 2.0
+            while time.perf_counter() < t_end:
+                for _ in range(10):
+                    S.step("grouped")
+                torch.cuda.synchronize()
+        clock = sampler.result()
+        log(f"[bench] clock {clock}")
+        per_linear = S.run("staged", args.steps, args.warmup)
+        log(f"[bench] per-linear staged step {per_linear['ms_per_step']:.3f} ms; "
+            f"fwd+bwd {per_linear['fwd_bwd_tflops']:.0f} TFLOP/s")
+        fused = S.run("fused", args.steps, args.warmup)
+        log(f"[bench] fused step {fused['ms_per_step']:.3f} ms; fwd+bwd {fused['fwd_bwd_tflops']:.0f} TFLOP/s")
 
     prod = head["products"]
     traffic = traffic_for("dense_gemm")
@@ -775,13 +785,14 @@ def main():
         "targets": {"fwd_bwd_frac_of_bf16_peak": fb / PEAK_BF16_TFLOPS, "fwd_bwd_target_frac": 0.50,
                     "fwd_bwd_shortfall_ms": max(0.0, (head["phases_ms"]["forward"] + head["phases_ms"]["backward"])
                                                 - S.fl_step / (0.5 * PEAK_BF16_TFLOPS * 1e12) * 1e3)},
-        "per_linear_path": {k: per_linear[k] for k in ("ms_per_step", "phases_ms", "fwd_bwd_tflops", "products")},
-        "fused_path": {k: fused[k] for k in ("ms_per_step", "phases_ms", "fwd_bwd_tflops", "products")},
+        "per_linear_path": per_linear and {k: per_linear[k] for k in ("ms_per_step", "phases_ms", "fwd_bwd_tflops",
+                                                                     "products")},
+        "fused_path": fused and {k: fused[k] for k in ("ms_per_step", "phases_ms", "fwd_bwd_tflops", "products")},
         "clock": clock,
         "quantize_gbps": S.q_bytes / (head["phases_ms"]["quantize"] * 1e-3) / 1e9,
         "layer_gemv_gbps": S.g_bytes / (head["phases_ms"]["decode_gemv"] * 1e-3) / 1e9,
     }
-    if not args.no_codebook_study:
+    if not args.no_codebook_study and not args.headline_only:
         out["codebooks"] = codebook_study(L, dev, S.q_bytes)
         log(f"[bench] codebooks {out['codebooks']}")
         out["optimizer"] = optimizer_study(L, r, dev)
@@ -789,7 +800,7 @@ def main():
     del S, L
     torch.cuda.empty_cache()
 
-    if not args.no_other_sets:
+    if not args.no_other_sets and not args.headline_only:
         out["dequant"] = dequant_study(dev)
         log(f"[bench] dequant {out['dequant']}")
         sets = {}
