@@ -27,7 +27,8 @@ namespace {
 
 constexpr int kPairOp = kTile * 128;                    // 32 KiB: 256 rows x 64 bf16 (two stages)
 constexpr int kPairSlot = 2 * kPairOp;                  // weight rows at 0, token rows at kPairOp
-constexpr size_t kLdsDense = 2 * (size_t)kPairSlot;     // 128 KiB: two pair slots
+constexpr size_t kLdsPairs = 2 * (size_t)kPairSlot;     // 128 KiB: two pair slots
+constexpr size_t kLdsDense = kLdsPairs + 2 * kOp;       // + 32 KiB: the first LoRA tail chunk
 constexpr int kDGroup = 4;                              // token tiles per tile group (tile order)
 
 // Pair slots hold two consecutive 32-wide stages (one 64-wide stage): rows of
@@ -223,9 +224,46 @@ __device__ __forceinline__ void tail_store(char* dst, const TailRegs& R, bool b_
   }
 }
 
+// The LoRA tail by DMA, for tiles inside one adapter group with the rank in
+// whole 32-wide chunks.  A chunk takes 32 KiB of LDS in the layouts of
+// tail_store, but the token half holds T itself (unscaled): s is applied to
+// each fragment as it is read, which rounds exactly as tail_store does.
+struct TailSrc {
+  rsrc_t wr, tr;         // weight half (B, or A with b_trans), token half (T)
+  int64_t n0, m0, rows;  // first weight row, first token row, weight rows (N)
+  int r, ld, col0;       // rank, T's row stride, T's first column (the group's)
+  bool bt;
+};
+// DMA of chunk c (ranks 32 c ..) into dst: per wave 4 token and 4 weight
+// instructions of 1 KiB.  Token rows / weight rows (no b_trans): the
+// 256-row x 64-byte pattern of dma_row / dma_chunk.  With b_trans: rank rows
+// n = 2 (4 w + q) + (lane >> 5) of 512 bytes, lane position pc = lane & 31
+// holding 32-byte block (pc >> 1) ^ (n & 3), half pc & 1.  Rows past the
+// arrays read zero (buffer range) or another row's finite values, which only
+// reach outputs past M or N.
+__device__ __forceinline__ void tail_dma(char* dst, const TailSrc& S, int c, int w, int lane) {
+  const int j0 = 32 * c;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int row = dma_row(q, w, lane), ch = dma_chunk(lane);
+    dma16(S.tr, dst + kOp + (64 * q + 16 * w) * 64,
+          (uint32_t)(((S.m0 + row) * S.ld + S.col0 + j0 + 8 * ch) * 2), 0u);
+    if (!S.bt) {
+      dma16(S.wr, dst + (64 * q + 16 * w) * 64, (uint32_t)(((S.n0 + row) * S.r + j0 + 8 * ch) * 2), 0u);
+    } else {
+      const int n = 2 * (4 * w + q) + (lane >> 5), pc = lane & 31;
+      const int e = 8 * (2 * ((pc >> 1) ^ (n & 3)) + (pc & 1));
+      dma16(S.wr, dst + 1024 * (4 * w + q), (uint32_t)(((int64_t)(j0 + n) * S.rows + S.n0 + e) * 2), 0u);
+    }
+  }
+}
+__device__ __forceinline__ bf16x8_t scale_frag(bf16x8_t v, float s) {
+  return __builtin_bit_cast(bf16x8_t, scale16(__builtin_bit_cast(uint4, v), s));
+}
+
 // FI: weight fragments per wave, so the tile is 64 FI weight rows x 256
 // tokens (FI = 4, 3 or 2); its tiles start at weight row n_begin.
-template <int FI>
+template <int FI, bool TD>
 __global__ __launch_bounds__(kThreads, 1) void bf16_fwd_kernel(const bf16_t* __restrict__ Wd, int64_t N, int64_t K,
                                                                const bf16_t* __restrict__ X, int64_t M,
                                                                const bf16_t* __restrict__ U,
@@ -274,6 +312,26 @@ __global__ __launch_bounds__(kThreads, 1) void bf16_fwd_kernel(const bf16_t* __r
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
+  // TD: the LoRA tail by DMA (the launch checked that the rank comes in whole
+  // chunks, that no tile straddles two adapter groups and that the side
+  // arrays fit 32-bit byte offsets); otherwise through registers
+  const int64_t g0 = n0 / gn;
+  const bool tdma = TD && r > 0;
+  // (built where used, so nothing of it stays live through the main loop)
+  auto tail_src = [&]() __attribute__((always_inline)) {
+    TailSrc ts;
+    ts.wr = make_rsrc(Bl, (uint32_t)(N * r * 2));
+    ts.tr = make_rsrc(U, (uint32_t)(M * ldu * 2));
+    ts.n0 = n0;
+    ts.m0 = m0;
+    ts.rows = N;
+    ts.r = r;
+    ts.ld = ldu;
+    ts.col0 = (int)(g0 * r);
+    ts.bt = b_trans != 0;
+    return ts;
+  };
+  if (tdma) tail_dma(smem + kLdsPairs, tail_src(), 0, f.w, lane);   // chunk 0 past the pair slots
   // pairs 0 and 1 into slots 0 and 1
 #pragma unroll
   for (int d = 0; d < 2 * FI + 8; ++d) {
@@ -301,7 +359,51 @@ __global__ __launch_bounds__(kThreads, 1) void bf16_fwd_kernel(const bf16_t* __r
   QLORA_WAIT(0, 0);
   __builtin_amdgcn_s_barrier();
 
-  if (r > 0) {
+  const FragOffs fo = frag_offs(lane);
+  const int am64 = wc * 32 * FI * 64, bm64 = wr * 128 * 64;
+  // acc += the chunk at buf (weights at buf, tokens at buf + kOp); the tokens
+  // are scaled by s as they are read when `raw`
+  auto tail_chunk = [&](const char* buf, bool raw) __attribute__((always_inline)) {
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int o = kk ? fo.o1 : fo.o0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (i < FI)
+          F.a0[i] = b_trans ? tr_frag<512>(buf + kk * 16 * 512 + tr_off<512>(wc * FI + i))
+                            : rd16(buf + am64 + i * 2048 + o);
+        const bf16x8_t b = rd16(buf + kOp + bm64 + i * 2048 + o);
+        F.b0[i] = raw ? scale_frag(b, s) : b;
+      }
+#pragma unroll
+      for (int i = 0; i < FI; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = mfma32x32x16(F.a0[i], F.b0[j], acc[i][j]);
+    }
+  };
+  if constexpr (TD) {
+    if (tdma) {
+      // chunk 0 landed before the drain above; chunks 1 .. go four at a time
+      // into the pair slots, the first four while chunk 0 is multiplied
+      const TailSrc ts = tail_src();
+      const int nt = r / 32;
+      int b0 = 1, bn = min(4, nt - 1);
+      for (int c = 0; c < bn; ++c) tail_dma(smem + c * 2 * kOp, ts, b0 + c, f.w, lane);
+      tail_chunk(smem + kLdsPairs, true);
+      while (bn > 0) {
+        QLORA_WAIT(0, 0);
+        __builtin_amdgcn_s_barrier();
+        for (int c = 0; c < bn; ++c) tail_chunk(smem + c * 2 * kOp, true);
+        b0 += bn;
+        bn = min(4, nt - b0);
+        if (bn > 0) {
+          QLORA_WAIT(0, 0);
+          __builtin_amdgcn_s_barrier();   // every wave is done with the batch's slots
+          for (int c = 0; c < bn; ++c) tail_dma(smem + c * 2 * kOp, ts, b0 + c, f.w, lane);
+        }
+      }
+    }
+  } else if (r > 0) {
     // acc += B (s U)^T over the rank, 32 at a time, through 64-byte-row tiles.
     // Weight rows come in groups of gn, each with its own adapter: rows of
     // group g take columns g r .. of U (row stride ldu) and their rows of B;
@@ -311,9 +413,7 @@ __global__ __launch_bounds__(kThreads, 1) void bf16_fwd_kernel(const bf16_t* __r
     // one barrier per chunk both publishes a chunk and retires the buffer
     // the next store overwrites (its readers finished before they stored
     // their part of the chunk in between).
-    const FragOffs fo = frag_offs(lane);
-    const int am64 = wc * 32 * FI * 64, bm64 = wr * 128 * 64;
-    const int64_t g0 = n0 / gn, g_last = (min(n0 + 64 * FI, N) - 1) / gn;
+    const int64_t g_last = (min(n0 + 64 * FI, N) - 1) / gn;
     const int nj = (r + 31) / 32;
     const int nt = (int)(g_last - g0 + 1) * nj;
     TailRegs R;
@@ -328,21 +428,7 @@ __global__ __launch_bounds__(kThreads, 1) void bf16_fwd_kernel(const bf16_t* __r
       tail_store(buf, R, b_trans != 0, s);
       if (t + 1 < nt) load(t + 1);
       __syncthreads();
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const int o = kk ? fo.o1 : fo.o0;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          if (i < FI)
-            F.a0[i] = b_trans ? tr_frag<512>(buf + kk * 16 * 512 + tr_off<512>(wc * FI + i))
-                              : rd16(buf + am64 + i * 2048 + o);
-          F.b0[i] = rd16(buf + kOp + bm64 + i * 2048 + o);
-        }
-#pragma unroll
-        for (int i = 0; i < FI; ++i)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) acc[i][j] = mfma32x32x16(F.a0[i], F.b0[j], acc[i][j]);
-      }
+      tail_chunk(buf, false);
     }
   }
   store_tile<FI>(acc, Y, N, M, N, m0, n0);
@@ -354,17 +440,31 @@ namespace {
 
 // Tiles of 64 FI weight rows over rows [n_begin, n_begin + n_rows) of the
 // N-row weight (N is every array's extent and leading dimension).
+// Whether the launch's tiles can take the LoRA tail by DMA: the rank in whole
+// 32-wide chunks, no tile across two adapter groups, and U (M x ldu) and B
+// or A (N x r) within 32-bit byte offsets.
+bool tail_by_dma(int64_t N, int64_t M, int r, int ldu, int64_t gn, int64_t n_begin, int tiles_n, int rows) {
+  if (r <= 0 || r % 32 != 0 || M * ldu >= ((int64_t)1 << 30) || N * r >= ((int64_t)1 << 30)) return false;
+  for (int t = 0; t < tiles_n; ++t) {
+    const int64_t lo = n_begin + (int64_t)t * rows, hi = std::min(lo + rows, N) - 1;
+    if (lo / gn != hi / gn) return false;
+  }
+  return true;
+}
+
 template <int FI>
 hipError_t launch_fi(const bf16_t* Wd, int64_t N, int64_t K, const bf16_t* X, int64_t M, const bf16_t* U,
                      const bf16_t* B, bool b_trans, int r, int ldu, int64_t gn, float s, bf16_t* Y, int64_t n_begin,
                      int64_t n_rows, hipStream_t st) {
   const int tiles_n = (int)((n_rows + 64 * FI - 1) / (64 * FI));
   const int tiles_m = (int)((M + kTile - 1) / kTile);
-  auto* fn = &bf16_fwd_kernel<FI>;
+  const bool td = tail_by_dma(N, M, r, ldu, gn, n_begin, tiles_n, 64 * FI);
+  auto* fn = td ? &bf16_fwd_kernel<FI, true> : &bf16_fwd_kernel<FI, false>;
+  const size_t lds = td ? kLdsDense : kLdsPairs;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     (int)kLdsDense);
+                                     (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(fn, dim3(tiles_n * tiles_m), dim3(kThreads), kLdsDense, st, Wd, N, K, X, M, U, B, (int)b_trans, r,
+  hipLaunchKernelGGL(fn, dim3(tiles_n * tiles_m), dim3(kThreads), lds, st, Wd, N, K, X, M, U, B, (int)b_trans, r,
                      ldu, gn, s, Y, n_begin, tiles_n, tiles_m);
   return hipGetLastError();
 }
