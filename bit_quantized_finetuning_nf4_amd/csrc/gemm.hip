@@ -352,8 +352,7 @@ hipError_t run_rows(const RowArgs& a, float* part, float scale, bf16_t* out, bf1
   const Split sp = split_for((a.M + 127) / 128, a.C, QT ? 512 : 256);
   auto* fn = &rskinny_kernel<RP, QT>;
   const size_t lds = (size_t)kRing * RowShape<RP, QT>::kStage;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     (int)lds);
+  hipError_t e = allow_lds(reinterpret_cast<const void*>(fn), (int)lds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(fn, dim3(sp.tiles * sp.splits, a.G), dim3(kThreads), lds, st, a.P, a.M, a.C, a.ldp, a.p_gs, a.Q,
                      a.r, a.q_gs, sp.sps, sp.tiles, a.ldo, part);
@@ -378,8 +377,7 @@ hipError_t run_cols(const ColArgs& a, float* part, float scale, float* out, hipS
   const Split sp = split_for((a.C + 127) / 128, a.M, 256);
   auto* fn = &cskinny_kernel<RP, DB>;
   const size_t lds = (size_t)kRing * ColShape<RP>::kStage;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     (int)lds);
+  hipError_t e = allow_lds(reinterpret_cast<const void*>(fn), (int)lds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(fn, dim3(sp.tiles * sp.splits, a.G), dim3(kThreads), lds, st, a.Big, a.M, a.C, a.ldb,
                      a.big_gs, a.Sm, a.r, a.lds, a.sm_gs, sp.sps, sp.tiles, part);

@@ -461,8 +461,7 @@ hipError_t launch_fi(const bf16_t* Wd, int64_t N, int64_t K, const bf16_t* X, in
   const bool td = tail_by_dma(N, M, r, ldu, gn, n_begin, tiles_n, 64 * FI);
   auto* fn = td ? &bf16_fwd_kernel<FI, true> : &bf16_fwd_kernel<FI, false>;
   const size_t lds = td ? kLdsDense : kLdsPairs;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     (int)lds);
+  hipError_t e = allow_lds(reinterpret_cast<const void*>(fn), (int)lds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(fn, dim3(tiles_n * tiles_m), dim3(kThreads), lds, st, Wd, N, K, X, M, U, B, (int)b_trans, r,
                      ldu, gn, s, Y, n_begin, tiles_n, tiles_m);

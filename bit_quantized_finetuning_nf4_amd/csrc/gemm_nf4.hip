@@ -1410,16 +1410,14 @@ hipError_t launch_fwd_cb(const Nf4View& W, const bf16_t* X, int64_t M, const bf1
   const int cus = device_cu_count();   // the tail split needs the round size
   const int rest = tiles % cus;
   const int main_tiles = (tiles > cus && rest > 0 && 2 * rest <= cus) ? tiles - rest : tiles;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&nf4_fwd_r_kernel<CB>),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsFwdR);
+  hipError_t e = allow_lds(reinterpret_cast<const void*>(&nf4_fwd_r_kernel<CB>), (int)kLdsFwdR);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(nf4_fwd_r_kernel<CB>, dim3(main_tiles), dim3(kThreads), kLdsFwdR, st, W, X, M, U, B, r, s, Y,
                      tiles_n, tiles_m);
   e = hipGetLastError();
   if (e != hipSuccess || main_tiles == tiles) return e;
   auto* tail = &nf4_fwd_n32_kernel<CB, 4>;
-  e = hipFuncSetAttribute(reinterpret_cast<const void*>(tail), hipFuncAttributeMaxDynamicSharedMemorySize,
-                          (int)kLdsFwdR);
+  e = allow_lds(reinterpret_cast<const void*>(tail), (int)kLdsFwdR);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(tail, dim3(2 * (tiles - main_tiles)), dim3(kThreads), kLdsFwdR, st, W, X, M, U, B, r, s, Y,
                      tiles_n, tiles_m, main_tiles);
@@ -1437,15 +1435,13 @@ hipError_t launch_dx_cb(const Nf4View& W, const bf16_t* dY, int64_t M, const bf1
   const int cus = device_cu_count();
   const int rest = tiles % cus;
   const int main_tiles = (tiles > cus && rest > 0 && 2 * rest <= cus) ? tiles - rest : tiles;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&nf4_dx_kernel<CB>),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsDx);
+  hipError_t e = allow_lds(reinterpret_cast<const void*>(&nf4_dx_kernel<CB>), (int)kLdsDx);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(nf4_dx_kernel<CB>, dim3(main_tiles), dim3(kThreads), kLdsDx, st, W, dY, M, G, A, r, s, dX,
                      tiles_k, tiles_m);
   e = hipGetLastError();
   if (e != hipSuccess || main_tiles == tiles) return e;
-  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&nf4_dx_half_kernel<CB>),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsDx);
+  e = allow_lds(reinterpret_cast<const void*>(&nf4_dx_half_kernel<CB>), (int)kLdsDx);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(nf4_dx_half_kernel<CB>, dim3(2 * (tiles - main_tiles)), dim3(kThreads), kLdsDx, st, W, dY, M, G, A,
                      r, s, dX, tiles_k, main_tiles);

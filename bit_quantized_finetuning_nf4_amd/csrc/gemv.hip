@@ -39,6 +39,7 @@
 // The job table lives in device memory (written by one copy per call), so
 // one launch covers every job.
 #include <algorithm>
+#include <mutex>
 #include <cstring>
 #include <vector>
 
@@ -789,20 +790,34 @@ LaunchPlan plan_launch(const GemvJob* jobs, int njobs, int kind, int max_groups)
 
 int device_cus() { return std::min(device_cu_count(), kMaxGvGroups); }
 
+// Both decode kernels address their LDS from 0, which holds only while the
+// compiler has given them no static LDS.  Checked once per kernel, with the
+// dynamic-LDS limit raised to the most any launch asks for.
+hipError_t gemv_lds_ready(const void* fn) {
+  static std::mutex mu;
+  static std::vector<const void*> checked;
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    if (std::find(checked.begin(), checked.end(), fn) == checked.end()) {
+      hipFuncAttributes fa{};
+      hipError_t e = hipFuncGetAttributes(&fa, fn);
+      if (e != hipSuccess) return e;
+      if (fa.sharedSizeBytes != 0) return hipErrorInvalidKernelFile;
+      checked.push_back(fn);
+    }
+  }
+  return allow_lds(fn, kMaxLds);
+}
+
 template <bool kPair, int CB>
 hipError_t launch_main(const GemvJob* djobs, const int4* segs, const int* range, int groups, int max_steps,
                        int absfmt, hipStream_t st) {
   if (groups <= 0) return hipSuccess;
   // The kernel addresses its LDS from 0, which holds only while the
-  // compiler has given it no static LDS.
-  hipFuncAttributes fa{};
-  hipError_t e = hipFuncGetAttributes(&fa, reinterpret_cast<const void*>(&nf4_gemv_kernel<kPair, CB>));
+  // compiler has given it no static LDS (checked once, with the LDS limit).
+  hipError_t e = gemv_lds_ready(reinterpret_cast<const void*>(&nf4_gemv_kernel<kPair, CB>));
   if (e != hipSuccess) return e;
-  if (fa.sharedSizeBytes != 0) return hipErrorInvalidKernelFile;
   const size_t lds = (size_t)kXOff + (size_t)max_steps * 1024;
-  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&nf4_gemv_kernel<kPair, CB>),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  if (e != hipSuccess) return e;
   hipLaunchKernelGGL((nf4_gemv_kernel<kPair, CB>), dim3(groups), dim3(kGvThreads), lds, st, djobs, segs, range,
                      max_steps, absfmt);
   return hipGetLastError();
@@ -812,12 +827,7 @@ template <bool kQuad, int CB>
 hipError_t launch_batch(const GemvJob* djobs, const int4* segs, const int* range, int groups, int absfmt,
                         hipStream_t st) {
   if (groups <= 0) return hipSuccess;
-  hipFuncAttributes fa{};
-  hipError_t e = hipFuncGetAttributes(&fa, reinterpret_cast<const void*>(&nf4_gemv_batch_kernel<kQuad, CB>));
-  if (e != hipSuccess) return e;
-  if (fa.sharedSizeBytes != 0) return hipErrorInvalidKernelFile;
-  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&nf4_gemv_batch_kernel<kQuad, CB>),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, kBtLds);
+  hipError_t e = gemv_lds_ready(reinterpret_cast<const void*>(&nf4_gemv_batch_kernel<kQuad, CB>));
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((nf4_gemv_batch_kernel<kQuad, CB>), dim3(groups), dim3(kBtThreads), kBtLds, st, djobs, segs,
                      range, absfmt);

@@ -23,6 +23,11 @@ struct Nf4View {
 // Compute units of the current device (256 if the query fails).
 int device_cu_count();
 
+// Raise kernel fn's dynamic-LDS limit to `bytes` (the most any of its
+// launches asks for) on the current device, once per device.
+hipError_t allow_lds(const void* fn, int bytes);
+constexpr int kMaxLds = 160 * 1024;
+
 // codebook: 0 NF4, 1 FP4, 2 Int4 (the values of qlora_codebook)
 // One AdamW step over n parameters (p_bf16 may be null); see optim.hip.
 hipError_t launch_adamw(float* p, bf16_t* p_bf16, const float* g, float* m, float* v, int64_t n, float lr,

@@ -6,6 +6,10 @@
 // scaled by its absmax and every scaled weight is stored as the index of the
 // nearest NF4 level; the block absmaxes are quantized a second time to 8-bit
 // codes against one fp32 scale per group of 256 blocks.
+#include <mutex>
+#include <utility>
+#include <vector>
+
 #include "device.h"
 #include "kernels.h"
 
@@ -301,6 +305,23 @@ __global__ __launch_bounds__(256) void dequant_t_kernel(const uint8_t* __restric
       for (int e = 0; e < 8 && n0 + 8 * c + e < N; ++e) dst[e] = (bf16_t)(vw[e >> 1] >> (16 * (e & 1)));
     }
   }
+}
+
+// Kernels whose dynamic-LDS limit has been raised, per device: the
+// attribute call costs a few microseconds of host time, which per-token
+// decode loops and small products would pay on every launch.
+hipError_t allow_lds(const void* fn, int bytes) {
+  static std::mutex mu;
+  static std::vector<std::pair<const void*, int>> done;   // (kernel, device)
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(mu);
+  for (const auto& d : done)
+    if (d.first == fn && d.second == dev) return hipSuccess;
+  e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess) done.emplace_back(fn, dev);
+  return e;
 }
 
 int device_cu_count() {

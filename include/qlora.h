@@ -480,9 +480,12 @@ qlora_status qlora_nf4_dx(const qlora_nf4_weight* W, const uint16_t* dY, int64_t
  * up to 16 (x [m x cols], y [m x rows]); m < 0 is QLORA_E_SHAPE, m > 16
  * QLORA_E_UNSUPPORTED.  ws is sized by qlora_workspace_bytes(QLORA_OP_GEMV,
  * largest m (0 or 1 for one token), max rows, max cols, 0, njobs); it holds
- * u = A x and the job table, which the call writes with an asynchronous
- * host-to-device copy on `stream`.  Equivalent to qlora_gemv_prepare
- * followed by qlora_gemv_run.
+ * u = A x and the job table, which the call writes with a host-to-device
+ * copy on `stream` from a temporary (pageable) host buffer: HIP stages such
+ * a copy before the call returns, so the call may wait for work already
+ * queued on `stream`.  Equivalent to qlora_gemv_prepare followed by
+ * qlora_gemv_run; a decode loop over fixed layers prepares once and runs
+ * the plan, which enqueues only the launches.
  * whatthefuture.ai article: 4-bit inference is slow (the 8-16x speed-up
  * its authors expected). */
 qlora_status qlora_gemv(const qlora_gemv_job* jobs, int32_t njobs, void* ws, size_t ws_bytes,
