@@ -60,21 +60,21 @@ constexpr int kZeroBytes = 512;                            // zero run read by t
 constexpr int kQ8Bytes = 256 * 4;                          // Q8[q] = RN32(q / 255) as fp32
 constexpr int kQ8Off = kLutBytes, kZeroOff = kQ8Off + kQ8Bytes, kXOff = kZeroOff + kZeroBytes;   // LDS layout
 constexpr int kMaxGvGroups = 1024;                         // persistent workgroups per launch, at most
-constexpr int kDownThreads = 256;                          // u = A x: one workgroup per adapter row
-constexpr int kDownUnroll = 4;                             // 16-byte loads of A per thread in flight
+constexpr int kDownWaves = 4;                              // u = A x: one workgroup per 16 adapter rows
+constexpr int kDownThreads = 64 * kDownWaves;
+constexpr int kDownUnroll = 8;                             // 32-column steps per wave in flight
 constexpr int kBtWaves = 16;                               // small-batch kernel: waves per workgroup
 constexpr int kBtThreads = 64 * kBtWaves;
 constexpr int kBtSets = 2;                                 // 16-row sets per wave
 constexpr int kBtRows = kBtWaves * kBtSets * 16;           // weight rows per tile (512)
 constexpr int kBtTokens = 16;                              // most tokens per job
 constexpr int kBtRank = 128;                               // largest adapter rank the library accepts
-constexpr int kBtChunkSteps = 8;                           // 128-column steps per staged x chunk
-constexpr int kBtXRow = kBtChunkSteps * 256 + 16;          // LDS bytes per token row of a chunk (padded)
+constexpr int kBtChunkCols = 1024;                         // columns per staged x chunk (four 256-column spans)
+constexpr int kBtXRow = kBtChunkCols * 2 + 16;             // LDS bytes per token row of a chunk (padded)
 constexpr int kBtXBuf = kBtTokens * kBtXRow;
 constexpr int kBtSuRow = kBtRank * 2 + 16;                 // LDS bytes per token row of s u (padded)
-constexpr int kBtZeroOff = kQ8Off + kQ8Bytes, kBtZeroBytes = 2048;
-constexpr int kBtSuOff = kBtZeroOff + kBtZeroBytes, kBtXOff = kBtSuOff + kBtTokens * kBtSuRow;
-constexpr int kBtLds = kBtXOff + 2 * kBtXBuf;              // 139,008 bytes
+constexpr int kBtSuOff = kQ8Off + kQ8Bytes, kBtXOff = kBtSuOff + kBtTokens * kBtSuRow;
+constexpr int kBtLds = kBtXOff + 2 * kBtXBuf;              // 136,960 bytes
 static_assert(kBtLds <= 160 * 1024, "LDS of the small-batch kernel");
 static_assert(kGvThreads == 1024, "the table fill below assumes 16 waves");
 
@@ -88,22 +88,6 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint32_t bytes) {
 __device__ __forceinline__ uint4 buf_load16(rsrc_t r, uint32_t voff) {
   const u32x4_t v = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
   return make_uint4(v.x, v.y, v.z, v.w);
-}
-
-__device__ __forceinline__ float dot8(uint4 a, uint4 x) {
-  const uint32_t aw[4] = {a.x, a.y, a.z, a.w}, xw[4] = {x.x, x.y, x.z, x.w};
-  float s = 0.0f;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    s += bf2f(aw[e] & 0xFFFFu) * bf2f(xw[e] & 0xFFFFu);
-    s += bf2f(aw[e] >> 16) * bf2f(xw[e] >> 16);
-  }
-  return s;
-}
-
-__device__ __forceinline__ float wave_sum(float v) {
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-  return v;
 }
 
 // bf16 (round to nearest even) of the unscaled level c of codebook CB.
@@ -128,6 +112,26 @@ __device__ __forceinline__ void lds_st128(uint32_t addr, uint4 v) {
   *(lds_u128*)(size_t)addr = u32x4_t{v.x, v.y, v.z, v.w};
 }
 
+// The job table's y and u pointers as global-memory pointers.  Through a
+// generic pointer the accesses become FLAT instructions, and while one of
+// those may be in flight the compiler turns every later wait for a vector
+// load into a wait for all of them, which drains the loads running ahead.
+template <class T>
+__device__ __forceinline__ __attribute__((address_space(1))) T* global_ptr(T* p) {
+  return (__attribute__((address_space(1))) T*)p;
+}
+
+// The value of lane group G (lanes 16G..16G+15) in every group, lane by lane
+// within the group: a permlane32 swap of v with itself pairs groups 0-2 and
+// 1-3, a permlane16 swap of the result with itself then pairs neighbours.
+__device__ __forceinline__ float from_group(float v, int G) {
+  const uint32_t x = __builtin_bit_cast(uint32_t, v);
+  const auto h = __builtin_amdgcn_permlane32_swap(x, x, false, false);   // [0 1 0 1], [2 3 2 3]
+  const uint32_t y = G < 2 ? h[0] : h[1];
+  const auto q = __builtin_amdgcn_permlane16_swap(y, y, false, false);   // even groups everywhere, odd ones
+  return __builtin_bit_cast(float, (G & 1) ? q[1] : q[0]);
+}
+
 // Eight weights (one code dword, element i in nibble i) -> bf16 x 8.  Table
 // address of code byte i: byte << 8 | lane column << 2, built by one v_perm.
 __device__ __forceinline__ bf16x8_t decode8(uint32_t c, uint32_t col) {
@@ -139,53 +143,49 @@ __device__ __forceinline__ bf16x8_t decode8(uint32_t c, uint32_t col) {
 }  // namespace
 
 // Phase 1: u = A x for every job with r > 0 (fp32, into the job's scratch;
-// u[t r + j] for token t).  One workgroup per adapter row: each thread keeps
-// up to kDownUnroll 16-byte loads of A in flight and dots them with every
-// token's x (L2 hits), then the workgroup sums its partials.
+// u[t r + j] for token t).  One workgroup per 16 adapter rows of a job:
+// U [16 tokens x 16 rows] = X A^T by v_mfma_f32_16x16x32_bf16, A operand =
+// x (lane c + 16g: token c, columns 8g..8g+7 of a 32-column step), B operand
+// = the adapter rows (lane c + 16g: row c, the same columns).  The four waves
+// take every fourth step and add their partials in LDS.  Tokens past m and
+// rows past r read zero (buffer range checks).
 __global__ __launch_bounds__(kDownThreads) void lora_down_kernel(const GemvJob* __restrict__ jobs,
                                                                  const int2* __restrict__ map) {
-  __shared__ float part[kBtTokens][kDownThreads / 64];
+  __shared__ float part[kDownWaves][16][17];
   const int2 mp = map[blockIdx.x];
   const GemvJob& J = jobs[mp.x];
-  const int K = J.K, row = mp.y, m = J.m;
-  const uint32_t kb = (uint32_t)K * 2u, xend = (uint32_t)m * kb;
-  const rsrc_t arr = make_rsrc(J.A + (int64_t)row * K, kb);   // zero past the row
-  const rsrc_t xr = make_rsrc(J.x, xend);
-  float acc[kBtTokens];
-#pragma unroll
-  for (int t = 0; t < kBtTokens; ++t) acc[t] = 0.0f;
-  for (int c0 = 0; c0 < K / 8; c0 += kDownThreads * kDownUnroll) {
-    uint4 av[kDownUnroll];
-    uint32_t off[kDownUnroll];
+  const int K = J.K, row0 = mp.y, m = J.m, R = J.r;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, c = lane & 15, g = lane >> 4;
+  const uint32_t kb = (uint32_t)K * 2u;
+  const rsrc_t xr = make_rsrc(J.x, (uint32_t)m * kb);
+  const rsrc_t arr = make_rsrc(J.A + (int64_t)row0 * K, (uint32_t)min(16, R - row0) * kb);
+  const uint32_t lane_off = (uint32_t)c * kb + 16u * (uint32_t)g;
+  const int nst = K / 32;   // K is a multiple of 64
+  f32x4_t D = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int s0 = w; s0 < nst; s0 += kDownWaves * kDownUnroll) {
+    uint4 xv[kDownUnroll], av[kDownUnroll];
 #pragma unroll
     for (int u = 0; u < kDownUnroll; ++u) {
-      off[u] = 16u * (uint32_t)(c0 + (int)threadIdx.x + u * kDownThreads);
-      av[u] = buf_load16(arr, off[u]);
+      const int s = s0 + kDownWaves * u;
+      // steps past the row read past both ranges: zero
+      const uint32_t off = s < nst ? lane_off + 64u * (uint32_t)s : 0xFFFFFFF0u;
+      xv[u] = buf_load16(xr, off);
+      av[u] = buf_load16(arr, off);
     }
 #pragma unroll
-    for (int t = 0; t < kBtTokens; ++t) {
-      if (t < m) {   // uniform
-        uint4 xv[kDownUnroll];
-#pragma unroll
-        for (int u = 0; u < kDownUnroll; ++u) xv[u] = buf_load16(xr, off[u] < kb ? (uint32_t)t * kb + off[u] : xend);
-#pragma unroll
-        for (int u = 0; u < kDownUnroll; ++u) acc[t] += dot8(av[u], xv[u]);
-      }
-    }
+    for (int u = 0; u < kDownUnroll; ++u)
+      D = mfma16x16x32(__builtin_bit_cast(bf16x8_t, xv[u]), __builtin_bit_cast(bf16x8_t, av[u]), D);
   }
+  // lane (c, g) holds tokens 4g..4g+3 of adapter row row0 + c
 #pragma unroll
-  for (int t = 0; t < kBtTokens; ++t) {
-    if (t < m) {
-      const float v = wave_sum(acc[t]);
-      if ((threadIdx.x & 63) == 0) part[t][threadIdx.x >> 6] = v;
-    }
-  }
+  for (int i = 0; i < 4; ++i) part[w][4 * g + i][c] = D[i];
   __syncthreads();
-  if ((int)threadIdx.x < m) {
+  const int t = threadIdx.x >> 4, n = threadIdx.x & 15;
+  if (t < m && row0 + n < R) {
     float v = 0.0f;
 #pragma unroll
-    for (int i = 0; i < kDownThreads / 64; ++i) v += part[threadIdx.x][i];
-    J.u[threadIdx.x * J.r + row] = v;
+    for (int i = 0; i < kDownWaves; ++i) v += part[i][t][n];
+    global_ptr(J.u)[t * R + row0 + n] = v;
   }
 }
 
@@ -404,7 +404,7 @@ __global__ __launch_bounds__(kGvThreads) void nf4_gemv_kernel(const GemvJob* __r
         part += __shfl_xor(part, 32);
         part += __shfl_xor(part, 1);
         part += __shfl_xor(part, 2);
-        if (lane == 4 * r && row < N) J.y[row] = (bf16_t)(pack_bf16x2(part, 0.0f) & 0xFFFFu);
+        if (lane == 4 * r && row < N) global_ptr(J.y)[row] = (bf16_t)(pack_bf16x2(part, 0.0f) & 0xFFFFu);
       }
 #pragma unroll
       for (int k = 0; k < kGvSets; ++k) {
@@ -428,23 +428,31 @@ __global__ __launch_bounds__(kGvThreads) void nf4_gemv_kernel(const GemvJob* __r
 // tokens 4g..4g+3 of row c and applies that row's block scales to its fp32
 // partials.
 //
-//   * Loads.  A step is 128 columns (two NF4 blocks) of a 16-row set; lane
-//     (c, g) reads code bytes 16g..16g+15 of row c's 64-byte run, so its
-//     dword j holds columns 32g + 8j .. 32g + 8j + 7 and MFMA j takes dword
-//     j of every lane.
-//   * Blocks kept apart.  The k-groups of one MFMA span both blocks of the
-//     step (g = 0, 1 the first, g = 2, 3 the second), so each MFMA runs twice,
-//     against x restricted to one block: the other half of the lanes reads a
-//     zero run.  D0 collects the first block, D1 the second, each with its
-//     own scale.  The matrix unit has room for the doubled work: at 16 tokens
-//     it needs under half of the time the codes take to stream.
+//   * Spans.  A span is 256 columns (four NF4 blocks, 128 code bytes) of a
+//     16-row set.  Its codes arrive in two loads that each cover eight whole
+//     rows (8 rows x 128 bytes, eight full lines: loads spread over sixteen
+//     rows stall in the vector L1's address translation).  Load i gives lane
+//     (c, g) bytes 64 (c >> 3) + 16 g of row 8i + (c & 7).
+//   * Two transposes put them in MFMA layout.  DPP row shifts by 8 lanes
+//     under bank masks exchange the load index with lane bit 3, so lane
+//     (c, g) then holds 16-byte chunk 4j + g of its own row c in register j.
+//     permlane32/16 swaps exchange the dword index with lane bits 4-5, so
+//     register (j, d) of lane (c, g) holds dword g of chunk 4j + d.  MFMA
+//     u = 4j + d thus covers the 32 columns of chunk u, all in block u >> 1;
+//     two MFMAs make a block's partial, which gets the block's scale
+//     t = Q8[q] s2 in fp32.
 //   * x in LDS.  The eight waves of a workgroup walk the same columns in
-//     lockstep, one 1024-column chunk of all sixteen token rows (zero past m
-//     and past K) at a time, double buffered: a chunk's steps run between the
-//     global loads of the next chunk and their LDS stores, then one barrier.
+//     lockstep, one 1024-column chunk (four spans) of all sixteen token rows
+//     (zero past m and past K) at a time, double buffered: a chunk's spans
+//     run between the global loads of the next chunk and their LDS stores,
+//     then one barrier.  Lane (t, g) reads the x of MFMA u at byte
+//     64 u + 16 g of token t's span, once for the two sets of its wave.
+//   * Block scales.  Lane (c, g) computes t = Q8[q] s2 of blocks 4g..4g+3
+//     of the chunk for its row c once per chunk; span sp takes its four from
+//     lane group sp by two permlane swaps each.
 //   * Decode table, persistence, cost-balanced tile ranges and loads running
-//     ahead across tile boundaries as in the batch-1 kernel; a tile is 512
-//     rows (eight waves of four sets).
+//     a span ahead across tile boundaries as in the batch-1 kernel; a tile is
+//     512 rows (sixteen waves of two sets).
 //   * LoRA.  s u (bf16, zero past m and r) is staged per job; the
 //     up-projection s U B^T is r/32 MFMAs per set at tile end, with B read
 //     straight from memory.
@@ -457,7 +465,7 @@ __global__ __launch_bounds__(kBtThreads) void nf4_gemv_batch_kernel(const GemvJo
   const int c = lane & 15, g = lane >> 4;
   const uint32_t col = 4u * lane;
 
-  // tables, once: wave w writes code-byte entries e = w + 8 i of column lane
+  // tables, once: wave w writes code-byte entries e = w + kBtWaves i of column lane
   {
     const int wu = __builtin_amdgcn_readfirstlane(w);
 #pragma unroll
@@ -466,22 +474,20 @@ __global__ __launch_bounds__(kBtThreads) void nf4_gemv_batch_kernel(const GemvJo
       lds_st32((uint32_t)e * 256u + 4u * lane, level_bf16<CB>(e & 15) | (level_bf16<CB>(e >> 4) << 16));
     }
     if (tid < 256) lds_st32(kQ8Off + 4u * tid, __builtin_bit_cast(uint32_t, absmax_value((uint32_t)tid, absfmt)));
-    if (tid < kBtZeroBytes / 16) lds_st128(kBtZeroOff + 16u * tid, make_uint4(0u, 0u, 0u, 0u));
   }
 
-  // x operand of lane (token c, k-group g) within a chunk buffer; the half of
-  // the lanes outside a block reads the zero run instead
-  const uint32_t xlane = kBtXOff + (uint32_t)c * kBtXRow + 64u * (uint32_t)g;
-  const bool second = g >= 2;
+  const uint32_t xlane = kBtXOff + (uint32_t)c * kBtXRow + 16u * (uint32_t)g;   // x of lane (token c, k-group g)
+  const uint32_t lrow = (uint32_t)(c & 7), lbyte = 64u * (uint32_t)(c >> 3) + 16u * (uint32_t)g;   // code loads
+  const bool bit3 = (c & 8) != 0;
   int cc = 0;   // x chunks staged so far: buffer cc & 1 holds the current one
 
   for (int si = range[blockIdx.x]; si < range[blockIdx.x + 1]; ++si) {
     const int4 sg = segs[si];
     const GemvJob& J = jobs[sg.x];
     const int K = J.K, N = J.N, nblk = K >> 6, R = J.r, m = J.m;
-    // 128-column steps per row, rounded up to whole chunks: the steps past
-    // the row meet zero x (staged zero past K), so they add exactly zero
-    const int nch = ((nblk + 1) / 2 + kBtChunkSteps - 1) / kBtChunkSteps, nst = nch * kBtChunkSteps;
+    // chunks of 16 blocks per row; the spans past the row meet zero x (staged
+    // zero past K), so they add exactly zero
+    const int nch = (nblk + 15) / 16, nsp = 4 * nch;
     const uint32_t nb = (uint32_t)N * (uint32_t)nblk;
     const rsrc_t cr = make_rsrc(J.codes, nb * 32u);
     const rsrc_t ar = make_rsrc(J.absmax_q, nb);
@@ -497,7 +503,7 @@ __global__ __launch_bounds__(kBtThreads) void nf4_gemv_batch_kernel(const GemvJo
     auto load_x = [&](uint4 (&v)[kXq], int ch) __attribute__((always_inline)) {
 #pragma unroll
       for (int q = 0; q < kXq; ++q) {
-        const int p = tid + kBtThreads * q, t = p >> 7, k = kBtChunkSteps * 128 * ch + 8 * (p & 127);
+        const int p = tid + kBtThreads * q, t = p >> 7, k = kBtChunkCols * ch + 8 * (p & 127);
         v[q] = buf_load16(xr, (t < m && k < K) ? ((uint32_t)t * (uint32_t)K + (uint32_t)k) * 2u : xend);
       }
     };
@@ -517,7 +523,8 @@ __global__ __launch_bounds__(kBtThreads) void nf4_gemv_batch_kernel(const GemvJo
       for (int q = 0; q < kSq; ++q) {
         const int p = tid + kBtThreads * q, t = p >> 6, j = 2 * (p & 63);
         const bool on = t < m && j < R;   // R is a multiple of 8
-        su[q] = on ? pack_bf16x2(J.s * J.u[t * R + j], J.s * J.u[t * R + j + 1]) : 0u;
+        const __attribute__((address_space(1))) float* u = global_ptr(J.u);
+        su[q] = on ? pack_bf16x2(J.s * u[t * R + j], J.s * u[t * R + j + 1]) : 0u;
       }
       __syncthreads();   // every wave is done with the previous job's buffers
       store_x(xv, cc & 1);
@@ -529,37 +536,32 @@ __global__ __launch_bounds__(kBtThreads) void nf4_gemv_batch_kernel(const GemvJo
       __syncthreads();
     }
 
-    // Row of set k in tile t; rows past N read the first byte past the
+    // Row `rr` of set k in tile t; rows past N read the first byte past the
     // arrays (zero codes, absmax code 0, so block scale 0).
     const int t_first = sg.y, t_last = sg.y + sg.z - 1;
-    auto row_of = [&](int t, int k) __attribute__((always_inline)) {
-      return t * kBtRows + 16 * kBtSets * w + 16 * k + c;
-    };
-    auto rbase_of = [&](int t, int k) __attribute__((always_inline)) -> uint32_t {
-      const int row = row_of(t, k);
+    auto rbase = [&](int t, int k, int rr) __attribute__((always_inline)) -> uint32_t {
+      const int row = t * kBtRows + 16 * kBtSets * w + 16 * k + rr;
       return (uint32_t)(row < N ? row : N) * (uint32_t)nblk;
     };
-    uint32_t rbc[kBtSets], rbn[kBtSets];
-    float s2c[kBtSets][3], s2n[kBtSets][3];
-    auto load_s2 = [&](float (&dst)[kBtSets][3], const uint32_t (&rb)[kBtSets]) __attribute__((always_inline)) {
+    // The group scales of the MFMA-layout row c of each set in tile t: a row
+    // of at most 32768 columns touches at most three 256-block groups.
+    float s2c[kBtSets][3];
+    auto load_s2 = [&](int t) __attribute__((always_inline)) {
 #pragma unroll
-      for (int k = 0; k < kBtSets; ++k)
+      for (int k = 0; k < kBtSets; ++k) {
+        const uint32_t rb = rbase(t, k, c);
 #pragma unroll
         for (int i = 0; i < 3; ++i)
-          dst[k][i] = u2f(__builtin_amdgcn_raw_buffer_load_b32(sr, ((rb[k] >> 8) + i) * 4u, 0, 0));
-    };
-    auto load_step = [&](uint4 (&c_)[kBtSets], const uint32_t (&rb)[kBtSets], int s) __attribute__((always_inline)) {
-#pragma unroll
-      for (int k = 0; k < kBtSets; ++k) c_[k] = buf_load16(cr, rb[k] * 32u + 64u * (uint32_t)s + 16u * (uint32_t)g);
+          s2c[k][i] = u2f(__builtin_amdgcn_raw_buffer_load_b32(sr, ((rb >> 8) + i) * 4u, 0, 0));
+      }
     };
     // The absmax codes of a chunk (16 blocks per row): lane (c, g) loads
-    // blocks 4g..4g+3 of row c once per chunk, a chunk ahead, and a step
-    // takes its two from lane c + 16 (s >> 1) (byte loads spread over sixteen
-    // rows each cost as much address work as a code load).
+    // blocks 4g..4g+3 of row c once per chunk, a chunk ahead; span sp takes
+    // its four from lane c + 16 sp.
     auto load_aq = [&](uint32_t (&a_)[kBtSets], int t, int ch) __attribute__((always_inline)) {
 #pragma unroll
       for (int k = 0; k < kBtSets; ++k) {
-        const uint32_t b = rbase_of(t, k) + 16u * (uint32_t)ch + 4u * (uint32_t)g;
+        const uint32_t b = rbase(t, k, c) + 16u * (uint32_t)ch + 4u * (uint32_t)g;
         if constexpr (kQuad) {   // 4-byte aligned: one load
           a_[k] = __builtin_amdgcn_raw_buffer_load_b32(ar, b, 0, 0);
           continue;
@@ -570,88 +572,114 @@ __global__ __launch_bounds__(kBtThreads) void nf4_gemv_batch_kernel(const GemvJo
                 ((uint32_t)__builtin_amdgcn_raw_buffer_load_b8(ar, b + 3u, 0, 0) << 24);
       }
     };
+    // Code loads run a span ahead, across tile boundaries; past the
+    // segment's last span they stay on it.  lb holds the byte offsets of span
+    // 0 of the load tile's rows, plus the lane's bytes.
+    uint32_t lb[kBtSets][2];
+    auto set_lb = [&](int t) __attribute__((always_inline)) {
 #pragma unroll
-    for (int k = 0; k < kBtSets; ++k) {
-      rbc[k] = rbase_of(t_first, k);
-      rbn[k] = rbase_of(t_first + 1 <= t_last ? t_first + 1 : t_last, k);
-    }
-    load_s2(s2c, rbc);
-    // code loads run one step ahead, across tile boundaries; past the
-    // segment's last step they stay on it
+      for (int k = 0; k < kBtSets; ++k)
+#pragma unroll
+        for (int i = 0; i < 2; ++i) lb[k][i] = rbase(t, k, 8 * i + (int)lrow) * 32u + lbyte;
+    };
     int tl = t_first, sl = 0;
-    auto load_next = [&](uint4 (&c_)[kBtSets]) __attribute__((always_inline)) {
-      uint32_t rb[kBtSets];
+    set_lb(tl);
+    auto load_next = [&](uint4 (&c_)[kBtSets][2]) __attribute__((always_inline)) {
 #pragma unroll
-      for (int k = 0; k < kBtSets; ++k) rb[k] = rbase_of(tl, k);
-      load_step(c_, rb, sl);
-      if (tl < t_last || sl + 1 < nst) {
-        if (++sl == nst) {
+      for (int k = 0; k < kBtSets; ++k)
+#pragma unroll
+        for (int i = 0; i < 2; ++i) c_[k][i] = buf_load16(cr, lb[k][i] + 128u * (uint32_t)sl);
+      if (tl < t_last || sl + 1 < nsp) {   // uniform scalar bookkeeping
+        if (++sl == nsp) {
           sl = 0;
           ++tl;
+          set_lb(tl);
         }
       }
     };
-    uint4 cs[kBtSets];
-    load_next(cs);
+    load_s2(t_first);
+    uint4 ca[kBtSets][2], cb[kBtSets][2];   // codes of the current and the next span
+    load_next(ca);
     uint32_t aqc[kBtSets];
     load_aq(aqc, t_first, 0);
 
     for (int t = t_first; t <= t_last; ++t) {
-      load_s2(s2n, rbn);
-      uint32_t gb1[kBtSets], gb2[kBtSets];   // first block (within the row) of its second and third group
-#pragma unroll
-      for (int k = 0; k < kBtSets; ++k) {
-        gb1[k] = 256u - (rbc[k] & 255u);
-        gb2[k] = gb1[k] + 256u;
-      }
       float acc[kBtSets][4];
 #pragma unroll
       for (int k = 0; k < kBtSets; ++k)
 #pragma unroll
         for (int i = 0; i < 4; ++i) acc[k][i] = 0.0f;
+      float tq[kBtSets][4];   // block scales of the lane's four blocks of the current chunk
 
-      // one step: S is the step within the row, s within the chunk; base0 and
-      // base1 address its x
-      auto step = [&](int S, int s, uint32_t base0, uint32_t base1) __attribute__((always_inline)) {
-        uint4 csn[kBtSets];
-        load_next(csn);
-        __builtin_amdgcn_sched_barrier(0);   // keep the loads ahead of this step's work
-        // k-group dword j of both sets against one pair of x operands
-        const uint32_t bi = 2u * (uint32_t)S;
-        f32x4_t D0[kBtSets], D1[kBtSets];
-#pragma unroll
-        for (int k = 0; k < kBtSets; ++k) D0[k] = D1[k] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const bf16x8_t a0 = __builtin_bit_cast(bf16x8_t, lds_ld128(base0 + 16u * (uint32_t)j));
-          const bf16x8_t a1 = __builtin_bit_cast(bf16x8_t, lds_ld128(base1 + 16u * (uint32_t)j));
-#pragma unroll
-          for (int k = 0; k < kBtSets; ++k) {
-            const uint32_t cw = j == 0 ? cs[k].x : j == 1 ? cs[k].y : j == 2 ? cs[k].z : cs[k].w;
-            const bf16x8_t b = decode8(cw, col);
-            D0[k] = mfma16x16x32(a0, b, D0[k]);
-            D1[k] = mfma16x16x32(a1, b, D1[k]);
-          }
-          __builtin_amdgcn_sched_barrier(0);   // one dword's decode in flight at a time
-        }
+      // One span: `cur` holds its codes, `nxt` receives the next span's; sp is
+      // the span within chunk ch, xb the chunk's x of this lane.
+      auto span = [&](uint4 (&cur)[kBtSets][2], uint4 (&nxt)[kBtSets][2], int ch, int sp, uint32_t xb)
+                      __attribute__((always_inline)) {
+        load_next(nxt);
+        __builtin_amdgcn_sched_barrier(0);   // keep the loads ahead of this span's work
+        // MFMA layout: T[k][4 j + d] = dword g of chunk 4j + d of row c
+        uint32_t T[kBtSets][8];
 #pragma unroll
         for (int k = 0; k < kBtSets; ++k) {
-          const uint32_t aq = (uint32_t)__shfl((int)aqc[k], c + 16 * (s >> 1)) >> (16 * (s & 1));
-          const float q0 = lds_ldf(kQ8Off + 4u * (aq & 0xFFu));
-          const float q1 = lds_ldf(kQ8Off + 4u * ((aq >> 8) & 0xFFu));
-          // the group scales as register values: a select over the array's
-          // elements would become a select of addresses and keep the array
-          // in memory
-          float v0 = s2c[k][0], v1 = s2c[k][1], v2 = s2c[k][2];
-          asm volatile("" : "+v"(v0), "+v"(v1), "+v"(v2));
-          const float s20 = bi >= gb2[k] ? v2 : bi >= gb1[k] ? v1 : v0;
-          const float s21 = bi + 1u >= gb2[k] ? v2 : bi + 1u >= gb1[k] ? v1 : v0;
-          const float t0 = q0 * s20, t1 = q1 * s21;
+          uint32_t V[2][4] = {{cur[k][0].x, cur[k][0].y, cur[k][0].z, cur[k][0].w},
+                              {cur[k][1].x, cur[k][1].y, cur[k][1].z, cur[k][1].w}};
+          // load index <-> lane bit 3: lanes with bit 3 set take the other
+          // load from 8 lanes below, the others from 8 lanes above
 #pragma unroll
-          for (int i = 0; i < 4; ++i) acc[k][i] += t0 * D0[k][i] + t1 * D1[k][i];
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t lo = V[0][e], hi = V[1][e];
+            const uint32_t down = (uint32_t)__builtin_amdgcn_mov_dpp((int)hi, 0x118, 0xF, 0xF, false);   // row_shr:8
+            const uint32_t up = (uint32_t)__builtin_amdgcn_mov_dpp((int)lo, 0x108, 0xF, 0xF, false);     // row_shl:8
+            V[0][e] = bit3 ? down : lo;
+            V[1][e] = bit3 ? hi : up;
+          }
+          // dword index <-> lane bits 4-5
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+              const auto v = __builtin_amdgcn_permlane32_swap(V[j][e], V[j][e + 2], false, false);
+              V[j][e] = v[0];
+              V[j][e + 2] = v[1];
+            }
+#pragma unroll
+            for (int e = 0; e < 4; e += 2) {
+              const auto v = __builtin_amdgcn_permlane16_swap(V[j][e], V[j][e + 1], false, false);
+              V[j][e] = v[0];
+              V[j][e + 1] = v[1];
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) T[k][4 * j + e] = V[j][e];
+          }
         }
+        // the span's block scales: blocks 4 sp..4 sp + 3 of the chunk, from lane group sp
+        float ts[kBtSets][4];
 #pragma unroll
-        for (int k = 0; k < kBtSets; ++k) cs[k] = csn[k];
+        for (int k = 0; k < kBtSets; ++k)
+#pragma unroll
+          for (int b = 0; b < 4; ++b) ts[k][b] = from_group(tq[k][b], sp);
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          f32x4_t D[kBtSets];
+#pragma unroll
+          for (int k = 0; k < kBtSets; ++k) D[k] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int u = 2 * b + h;
+            const bf16x8_t a = __builtin_bit_cast(bf16x8_t, lds_ld128(xb + 512u * (uint32_t)sp + 64u * (uint32_t)u));
+#pragma unroll
+            for (int k = 0; k < kBtSets; ++k) D[k] = mfma16x16x32(a, decode8(T[k][u], col), D[k]);
+          }
+#pragma unroll
+          for (int k = 0; k < kBtSets; ++k) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[k][i] += ts[k][b] * D[k][i];
+            // apply the block's partial now: left to itself the compiler
+            // defers these products to the chunk's end and keeps every
+            // block's MFMA result alive until then
+            asm volatile("" : "+v"(acc[k][0]), "+v"(acc[k][1]), "+v"(acc[k][2]), "+v"(acc[k][3]));
+          }
+        }
       };
 
       for (int ch = 0; ch < nch; ++ch) {
@@ -659,18 +687,27 @@ __global__ __launch_bounds__(kBtThreads) void nf4_gemv_batch_kernel(const GemvJo
         load_x(xv, ch + 1 < nch ? ch + 1 : 0);   // the next chunk (of the next tile after the last)
         uint32_t aqn[kBtSets];
         load_aq(aqn, ch + 1 < nch ? t : (t + 1 <= t_last ? t + 1 : t_last), ch + 1 < nch ? ch + 1 : 0);
-        // a lane of the other block half reads the zero run at a fixed address
-        const uint32_t xb = xlane + (uint32_t)(cc & 1) * kBtXBuf;
-        uint32_t base0 = second ? (uint32_t)kBtZeroOff : xb, base1 = second ? xb : (uint32_t)kBtZeroOff;
-        const uint32_t inc0 = second ? 0u : 256u, inc1 = second ? 256u : 0u;
-        // a runtime loop over whole chunks (as the batch-1 kernel's): the
-        // waits stay exact and nothing is unrolled into register pressure
-        const int S0 = ch * kBtChunkSteps;
-        for (int s = 0; s < kBtChunkSteps; ++s) {
-          step(S0 + s, s, base0, base1);
-          base0 += inc0;
-          base1 += inc1;
+        // this chunk's block scales: blocks 4g..4g+3 of row c
+#pragma unroll
+        for (int k = 0; k < kBtSets; ++k) {
+          const uint32_t gb1 = 256u - (rbase(t, k, c) & 255u), gb2 = gb1 + 256u;   // first block of groups 2, 3
+          // the group scales as register values: a select over the array's
+          // elements would become a select of addresses and keep the array
+          // in memory
+          float v0 = s2c[k][0], v1 = s2c[k][1], v2 = s2c[k][2];
+          asm volatile("" : "+v"(v0), "+v"(v1), "+v"(v2));
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const uint32_t bi = 16u * (uint32_t)ch + 4u * (uint32_t)g + (uint32_t)j;   // block within the row
+            const float s2 = bi >= gb2 ? v2 : bi >= gb1 ? v1 : v0;
+            tq[k][j] = lds_ldf(kQ8Off + 4u * ((aqc[k] >> (8 * j)) & 0xFFu)) * s2;
+          }
         }
+        const uint32_t xb = xlane + (uint32_t)(cc & 1) * kBtXBuf;
+        span(ca, cb, ch, 0, xb);
+        span(cb, ca, ch, 1, xb);
+        span(ca, cb, ch, 2, xb);
+        span(cb, ca, ch, 3, xb);
         store_x(xv, (cc + 1) & 1);
 #pragma unroll
         for (int k = 0; k < kBtSets; ++k) aqc[k] = aqn[k];
@@ -678,11 +715,14 @@ __global__ __launch_bounds__(kBtThreads) void nf4_gemv_batch_kernel(const GemvJo
         ++cc;
       }
 
-      // Tile end: the LoRA term by MFMA (A = s u of token c, B = ranks of
-      // weight row c; ranks past r read zero on both sides), then y.
+      // Tile end: the next tile's group scales (loaded here, where the LoRA
+      // loads below wait for memory anyway), the LoRA term by MFMA (A = s u
+      // of token c, B = ranks of weight row c; ranks past r read zero on both
+      // sides), then y.
+      load_s2(t + 1 <= t_last ? t + 1 : t_last);
 #pragma unroll
       for (int k = 0; k < kBtSets; ++k) {
-        const int row = row_of(t, k);
+        const int row = t * kBtRows + 16 * kBtSets * w + 16 * k + c;
         const uint32_t roff = (uint32_t)(row < N ? row : N) * (uint32_t)R * 2u;
         f32x4_t L = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -698,15 +738,8 @@ __global__ __launch_bounds__(kBtThreads) void nf4_gemv_batch_kernel(const GemvJo
         for (int i = 0; i < 4; ++i) {
           const int tok = 4 * g + i;
           if (tok < m && row < N)
-            J.y[(int64_t)tok * N + row] = (bf16_t)(pack_bf16x2(acc[k][i] + L[i], 0.0f) & 0xFFFFu);
+            global_ptr(J.y)[(int64_t)tok * N + row] = (bf16_t)(pack_bf16x2(acc[k][i] + L[i], 0.0f) & 0xFFFFu);
         }
-      }
-#pragma unroll
-      for (int k = 0; k < kBtSets; ++k) {
-        rbc[k] = rbn[k];
-        rbn[k] = rbase_of(t + 2 <= t_last ? t + 2 : t_last, k);
-#pragma unroll
-        for (int i = 0; i < 3; ++i) s2c[k][i] = s2n[k][i];
       }
     }
   }
@@ -876,7 +909,7 @@ hipError_t gemv_prepare(const GemvJob* jobs, int njobs, int codebook, void* tabl
   for (int k = 0; k < kGvKinds; ++k) lp[k] = plan_launch(jobs, njobs, k, groups);
   std::vector<int2> down;
   for (int i = 0; i < njobs; ++i)
-    for (int t = 0; t < jobs[i].r; ++t) down.push_back(make_int2(i, t));
+    for (int t = 0; t < jobs[i].r; t += 16) down.push_back(make_int2(i, t));
   // layout: jobs | per launch kind: segments, group offsets | u = A x map
   GemvLaunch L{};
   size_t off = up256((size_t)njobs * sizeof(GemvJob));
