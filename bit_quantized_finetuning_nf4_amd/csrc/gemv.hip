@@ -500,21 +500,27 @@ __global__ __launch_bounds__(kBtThreads) void nf4_gemv_batch_kernel(const GemvJo
     // x chunk ch: 16-byte piece p = tid + kBtThreads q is columns
     // 1024 ch + 8 (p & 127) of token p >> 7 (zero past m or K)
     constexpr int kXq = kBtTokens * 128 / kBtThreads;   // 16-byte x pieces per thread and chunk
+    // A wave's pieces all belong to one token (64 of its 128), so pieces of
+    // tokens past m are skipped wave by wave: their rows of both buffers are
+    // zeroed when the job is staged and stay zero.
     auto load_x = [&](uint4 (&v)[kXq], int ch) __attribute__((always_inline)) {
 #pragma unroll
       for (int q = 0; q < kXq; ++q) {
         const int p = tid + kBtThreads * q, t = p >> 7, k = kBtChunkCols * ch + 8 * (p & 127);
-        v[q] = buf_load16(xr, (t < m && k < K) ? ((uint32_t)t * (uint32_t)K + (uint32_t)k) * 2u : xend);
+        if (t < m)   // uniform
+          v[q] = buf_load16(xr, k < K ? ((uint32_t)t * (uint32_t)K + (uint32_t)k) * 2u : xend);
       }
     };
     auto store_x = [&](const uint4 (&v)[kXq], int buf) __attribute__((always_inline)) {
 #pragma unroll
       for (int q = 0; q < kXq; ++q) {
         const int p = tid + kBtThreads * q;
-        lds_st128(kBtXOff + (uint32_t)buf * kBtXBuf + (uint32_t)(p >> 7) * kBtXRow + 16u * (uint32_t)(p & 127), v[q]);
+        if ((p >> 7) < m)   // uniform
+          lds_st128(kBtXOff + (uint32_t)buf * kBtXBuf + (uint32_t)(p >> 7) * kBtXRow + 16u * (uint32_t)(p & 127),
+                    v[q]);
       }
     };
-    {   // stage the job: x chunk 0 and s u
+    {   // stage the job: x chunk 0, zero rows past m in both buffers, and s u
       uint4 xv[kXq];
       load_x(xv, 0);
       constexpr int kSq = kBtTokens * kBtRank / 2 / kBtThreads;   // s u pairs per thread
@@ -528,6 +534,15 @@ __global__ __launch_bounds__(kBtThreads) void nf4_gemv_batch_kernel(const GemvJo
       }
       __syncthreads();   // every wave is done with the previous job's buffers
       store_x(xv, cc & 1);
+#pragma unroll
+      for (int q = 0; q < kXq; ++q) {
+        const int p = tid + kBtThreads * q;
+        if ((p >> 7) >= m)   // uniform
+#pragma unroll
+          for (int bf = 0; bf < 2; ++bf)
+            lds_st128(kBtXOff + (uint32_t)bf * kBtXBuf + (uint32_t)(p >> 7) * kBtXRow + 16u * (uint32_t)(p & 127),
+                      make_uint4(0u, 0u, 0u, 0u));
+      }
 #pragma unroll
       for (int q = 0; q < kSq; ++q) {
         const int p = tid + kBtThreads * q;
