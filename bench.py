@@ -54,6 +54,10 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E
+# Untimed decode passes before the timed ones: after an idle gap the first
+# passes run 10-20 % slower and speed up pass by pass (the clocks ramp back
+# up); ten passes (about 70 ms) reach the steady rate a serving loop sees.
+DECODE_WARMUP = 10
 METRIC = "QLoRA linear fwd+bwd TFLOP/s at 7B/65B shapes; NF4 decode GEMV HBM GB/s"
 
 
@@ -80,7 +84,7 @@ def decode_batch_study(jobs, layers, r, alpha, passes, dev):
     E = lambda: torch.cuda.Event(enable_timing=True)
 
     def timed(fn):
-        for _ in range(2):
+        for _ in range(DECODE_WARMUP):
             fn()
         torch.cuda.synchronize()
         evs = [(E(), E()) for _ in range(passes)]
@@ -845,7 +849,7 @@ def main():
             if layer % 20 == 19:
                 log(f"[bench] decode weights: {layer + 1} layers quantized")
         dplan = ops.GemvPlan(jobs)
-        for _ in range(2):
+        for _ in range(DECODE_WARMUP):
             dplan()
         torch.cuda.synchronize()
         evs = [(E(), E()) for _ in range(args.decode_passes)]

@@ -62,7 +62,7 @@ constexpr int kQ8Off = kLutBytes, kZeroOff = kQ8Off + kQ8Bytes, kXOff = kZeroOff
 constexpr int kMaxGvGroups = 1024;                         // persistent workgroups per launch, at most
 constexpr int kDownWaves = 4;                              // u = A x: one workgroup per 16 adapter rows
 constexpr int kDownThreads = 64 * kDownWaves;
-constexpr int kDownUnroll = 8;                             // 32-column steps per wave in flight
+constexpr int kDownUnroll = 4;                             // 32-column steps per wave and batch
 constexpr int kBtWaves = 16;                               // small-batch kernel: waves per workgroup
 constexpr int kBtThreads = 64 * kBtWaves;
 constexpr int kBtSets = 2;                                 // 16-row sets per wave
@@ -147,7 +147,8 @@ __device__ __forceinline__ bf16x8_t decode8(uint32_t c, uint32_t col) {
 // U [16 tokens x 16 rows] = X A^T by v_mfma_f32_16x16x32_bf16, A operand =
 // x (lane c + 16g: token c, columns 8g..8g+7 of a 32-column step), B operand
 // = the adapter rows (lane c + 16g: row c, the same columns).  The four waves
-// take every fourth step and add their partials in LDS.  Tokens past m and
+// take every fourth step, two batches of four steps in flight each, and add
+// their partials in LDS.  Tokens past m and
 // rows past r read zero (buffer range checks).
 __global__ __launch_bounds__(kDownThreads) void lora_down_kernel(const GemvJob* __restrict__ jobs,
                                                                  const int2* __restrict__ map) {
@@ -162,19 +163,33 @@ __global__ __launch_bounds__(kDownThreads) void lora_down_kernel(const GemvJob* 
   const uint32_t lane_off = (uint32_t)c * kb + 16u * (uint32_t)g;
   const int nst = K / 32;   // K is a multiple of 64
   f32x4_t D = {0.0f, 0.0f, 0.0f, 0.0f};
-  for (int s0 = w; s0 < nst; s0 += kDownWaves * kDownUnroll) {
-    uint4 xv[kDownUnroll], av[kDownUnroll];
+  // Batches of kDownUnroll steps (every fourth step), double buffered: the
+  // next batch is issued before this one's MFMAs, so loads stay in flight.
+  // Steps past the row read past both ranges: zero.
+  constexpr int kBatch = kDownWaves * kDownUnroll;
+  auto load = [&](uint4 (&xv)[kDownUnroll], uint4 (&av)[kDownUnroll], int s0) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < kDownUnroll; ++u) {
       const int s = s0 + kDownWaves * u;
-      // steps past the row read past both ranges: zero
       const uint32_t off = s < nst ? lane_off + 64u * (uint32_t)s : 0xFFFFFFF0u;
       xv[u] = buf_load16(xr, off);
       av[u] = buf_load16(arr, off);
     }
+  };
+  auto mma = [&](const uint4 (&xv)[kDownUnroll], const uint4 (&av)[kDownUnroll]) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < kDownUnroll; ++u)
       D = mfma16x16x32(__builtin_bit_cast(bf16x8_t, xv[u]), __builtin_bit_cast(bf16x8_t, av[u]), D);
+  };
+  uint4 xa[kDownUnroll], aa[kDownUnroll], xb[kDownUnroll], ab[kDownUnroll];
+  load(xa, aa, w);
+  for (int s0 = w; s0 < nst; s0 += 2 * kBatch) {
+    load(xb, ab, s0 + kBatch);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(xa, aa);
+    load(xa, aa, s0 + 2 * kBatch);   // unconditional: past the row it reads zero and keeps the waits exact
+    __builtin_amdgcn_sched_barrier(0);
+    mma(xb, ab);
   }
   // lane (c, g) holds tokens 4g..4g+3 of adapter row row0 + c
 #pragma unroll
