@@ -111,6 +111,24 @@ def test_batch_and_single_token_jobs_in_one_call():
     _run([_job(N, K, r, m, seed=200 + i) for i, (N, K, r, m) in enumerate(shapes)], "mixed")
 
 
+def test_one_workgroup_walks_jobs_of_different_token_counts():
+    # 300 one-tile jobs are more than the device's persistent workgroups, so
+    # some workgroups take several jobs in a row; token counts rise and fall
+    # from job to job (staged x rows past m must not reach any output).  The
+    # last two jobs read one x tensor, the second its first 5 rows only.
+    ms = [2 + (7 * i) % 15 for i in range(300)]
+    ds = [_job(64, 128, 8 if i % 3 else 0, m, seed=9000 + i) for i, m in enumerate(ms)]
+    ds.append(_job(64, 128, 8, 16, seed=9998))
+    ds.append(dict(_job(64, 128, 8, 5, seed=9999), x=ds[-1]["x"][:5]))
+    jobs = _jobs(ds)
+    jobs[-1].x = jobs[-2].x[:5]   # the same memory as the 16-token job's first rows
+    print(f"[decode batch parity] {len(ds)} small jobs", flush=True)
+    ys = ops.gemv(jobs)
+    torch.cuda.synchronize()
+    for i, (d, y) in enumerate(zip(ds, ys)):
+        assert_close(torch_to_f64(y), _oracle_y(d), f"job {i} (m = {d['x'].shape[0]})")
+
+
 def test_prepared_plan_reruns_with_new_inputs():
     shapes = [(512, 1024, 64, 8), (1536, 1024, 64, 16), (300, 2048, 16, 0)]
     ds = [_job(N, K, r, m, seed=600 + i) for i, (N, K, r, m) in enumerate(shapes)]
