@@ -60,7 +60,9 @@ constexpr int kZeroBytes = 512;                            // zero run read by t
 constexpr int kQ8Bytes = 256 * 4;                          // Q8[q] = RN32(q / 255) as fp32
 constexpr int kQ8Off = kLutBytes, kZeroOff = kQ8Off + kQ8Bytes, kXOff = kZeroOff + kZeroBytes;   // LDS layout
 constexpr int kMaxGvGroups = 1024;                         // persistent workgroups per launch, at most
-constexpr int kDownWaves = 4;                              // u = A x: one workgroup per 16 adapter rows
+constexpr int kRowThreads = 256;                           // u = A x of one-token jobs: one workgroup per adapter row
+constexpr int kRowUnroll = 4;                              // 16-byte loads of A (and of x) per thread in flight
+constexpr int kDownWaves = 4;                              // u = A x of several tokens: one workgroup per 16 adapter rows
 constexpr int kDownThreads = 64 * kDownWaves;
 constexpr int kDownUnroll = 4;                             // 32-column steps per wave and batch
 constexpr int kBtWaves = 16;                               // small-batch kernel: waves per workgroup
@@ -88,6 +90,22 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint32_t bytes) {
 __device__ __forceinline__ uint4 buf_load16(rsrc_t r, uint32_t voff) {
   const u32x4_t v = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
   return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ float dot8(uint4 a, uint4 x) {
+  const uint32_t aw[4] = {a.x, a.y, a.z, a.w}, xw[4] = {x.x, x.y, x.z, x.w};
+  float s = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    s += bf2f(aw[e] & 0xFFFFu) * bf2f(xw[e] & 0xFFFFu);
+    s += bf2f(aw[e] >> 16) * bf2f(xw[e] >> 16);
+  }
+  return s;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
 }
 
 // bf16 (round to nearest even) of the unscaled level c of codebook CB.
@@ -143,13 +161,51 @@ __device__ __forceinline__ bf16x8_t decode8(uint32_t c, uint32_t col) {
 }  // namespace
 
 // Phase 1: u = A x for every job with r > 0 (fp32, into the job's scratch;
-// u[t r + j] for token t).  One workgroup per 16 adapter rows of a job:
+// u[t r + j] for token t).
+//
+// One-token jobs: one workgroup per adapter row, so that a call of a few
+// jobs still spreads over every CU.  Each thread keeps kRowUnroll 16-byte
+// loads of A and of x in flight (columns past K read zero), and the
+// workgroup adds its threads' dot products in a fixed order.
+__global__ __launch_bounds__(kRowThreads) void lora_row_kernel(const GemvJob* __restrict__ jobs,
+                                                               const int2* __restrict__ map) {
+  __shared__ float part[kRowThreads / 64];
+  const int2 mp = map[blockIdx.x];
+  const GemvJob& J = jobs[mp.x];
+  const int K = J.K, row = mp.y;
+  const uint32_t kb = (uint32_t)K * 2u;
+  const rsrc_t arr = make_rsrc(J.A + (int64_t)row * K, kb);
+  const rsrc_t xr = make_rsrc(J.x, kb);
+  float acc = 0.0f;
+  for (int c0 = 0; c0 < K / 8; c0 += kRowThreads * kRowUnroll) {
+    uint4 av[kRowUnroll], xv[kRowUnroll];
+#pragma unroll
+    for (int u = 0; u < kRowUnroll; ++u) {
+      const uint32_t off = 16u * (uint32_t)(c0 + (int)threadIdx.x + u * kRowThreads);
+      av[u] = buf_load16(arr, off);
+      xv[u] = buf_load16(xr, off);
+    }
+#pragma unroll
+    for (int u = 0; u < kRowUnroll; ++u) acc += dot8(av[u], xv[u]);
+  }
+  const float v = wave_sum(acc);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = v;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float sum = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kRowThreads / 64; ++i) sum += part[i];
+    global_ptr(J.u)[row] = sum;
+  }
+}
+
+// Jobs of several tokens: one workgroup per 16 adapter rows of a job:
 // U [16 tokens x 16 rows] = X A^T by v_mfma_f32_16x16x32_bf16, A operand =
 // x (lane c + 16g: token c, columns 8g..8g+7 of a 32-column step), B operand
 // = the adapter rows (lane c + 16g: row c, the same columns).  The four waves
 // take every fourth step, two batches of four steps in flight each, and add
-// their partials in LDS.  Tokens past m and
-// rows past r read zero (buffer range checks).
+// their partials in LDS.  Tokens past m and rows past r read zero (buffer
+// range checks).
 __global__ __launch_bounds__(kDownThreads) void lora_down_kernel(const GemvJob* __restrict__ jobs,
                                                                  const int2* __restrict__ map) {
   __shared__ float part[kDownWaves][16][17];
@@ -937,9 +993,16 @@ hipError_t gemv_prepare(const GemvJob* jobs, int njobs, int codebook, void* tabl
   const int groups = device_cus();
   LaunchPlan lp[kGvKinds];
   for (int k = 0; k < kGvKinds; ++k) lp[k] = plan_launch(jobs, njobs, k, groups);
+  // u = A x map: an entry per adapter row of the one-token jobs, then an
+  // entry per 16 adapter rows of the others
   std::vector<int2> down;
   for (int i = 0; i < njobs; ++i)
-    for (int t = 0; t < jobs[i].r; t += 16) down.push_back(make_int2(i, t));
+    if (jobs[i].m <= 1)
+      for (int t = 0; t < jobs[i].r; ++t) down.push_back(make_int2(i, t));
+  const int n_rows = (int)down.size();
+  for (int i = 0; i < njobs; ++i)
+    if (jobs[i].m > 1)
+      for (int t = 0; t < jobs[i].r; t += 16) down.push_back(make_int2(i, t));
   // layout: jobs | per launch kind: segments, group offsets | u = A x map
   GemvLaunch L{};
   size_t off = up256((size_t)njobs * sizeof(GemvJob));
@@ -949,10 +1012,11 @@ hipError_t gemv_prepare(const GemvJob* jobs, int njobs, int codebook, void* tabl
     L.rng_off[k] = off;
     off += up256(lp[k].range.size() * sizeof(int));
     L.groups[k] = lp[k].groups();
-    L.max_steps[k] = lp[k].max_steps;
+    if (k < 2) L.max_steps[k] = lp[k].max_steps;
   }
   L.down_off = off;
   L.n_down = (int)down.size();
+  L.n_rows = n_rows;
   L.codebook = codebook;
   off += up256(down.size() * sizeof(int2));
   if (off > table_bytes) return hipErrorInvalidValue;   // the caller's check makes this unreachable
@@ -973,9 +1037,15 @@ hipError_t gemv_prepare(const GemvJob* jobs, int njobs, int codebook, void* tabl
 hipError_t gemv_run(const GemvLaunch& L, hipStream_t st) {
   const uint8_t* dev = static_cast<const uint8_t*>(L.table);
   const GemvJob* djobs = reinterpret_cast<const GemvJob*>(dev);
-  if (L.n_down > 0) {
-    hipLaunchKernelGGL(lora_down_kernel, dim3((unsigned)L.n_down), dim3(kDownThreads), 0, st, djobs,
-                       reinterpret_cast<const int2*>(dev + L.down_off));
+  const int2* map = reinterpret_cast<const int2*>(dev + L.down_off);
+  if (L.n_rows > 0) {
+    hipLaunchKernelGGL(lora_row_kernel, dim3((unsigned)L.n_rows), dim3(kRowThreads), 0, st, djobs, map);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (L.n_down > L.n_rows) {
+    hipLaunchKernelGGL(lora_down_kernel, dim3((unsigned)(L.n_down - L.n_rows)), dim3(kDownThreads), 0, st, djobs,
+                       map + L.n_rows);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

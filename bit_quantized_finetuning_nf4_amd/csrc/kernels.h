@@ -122,8 +122,8 @@ constexpr int kGvKinds = 4;   // launches per call: batch-1 and several tokens, 
 struct GemvLaunch {
   void* table;
   uint64_t seg_off[kGvKinds], rng_off[kGvKinds], down_off;
-  int32_t groups[kGvKinds], max_steps[kGvKinds];
-  int32_t n_down;
+  int32_t groups[kGvKinds], max_steps[2];   // max_steps: the two one-token launches
+  int32_t n_down, n_rows;                    // u = A x map entries, the first n_rows of them one per adapter row
   int32_t codebook;  // shared by every job of the call: 4-bit codebook | second-level format << 8
 };
 hipError_t gemv_prepare(const GemvJob* jobs, int njobs, int codebook, void* table, size_t table_bytes,
