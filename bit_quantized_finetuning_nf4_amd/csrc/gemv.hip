@@ -1,4 +1,7 @@
-// gemv.hip -- batch-1 decode y = deq(W) x + s B (A x) over many linears.
+// gemv.hip -- decode y = deq(W) x + s B (A x) over many linears: batch 1
+// (this header, nf4_gemv_kernel) and up to 16 tokens per linear
+// (nf4_gemv_batch_kernel, further down); u = A x first (lora_row_kernel,
+// lora_down_kernel).
 //
 // whatthefuture.ai article, closing paragraphs: 4-bit inference is slow and
 // an 8-16x speed-up is expected; glossary "QLoRA", Definition: the frozen
@@ -32,12 +35,17 @@
 //   * Persistent workgroups.  One 16-wave workgroup per CU (the 64 KiB table
 //     and x fill its LDS) walks a contiguous, cost-balanced range of row
 //     tiles.  The tables are built once; x is restaged only when the job's
-//     x pointer or length changes; the code loads run one step ahead straight across tile
-//     boundaries, and each tile's LoRA rows and the next tile's group scales
-//     are fetched when the tile starts, so no tile boundary waits on memory.
+//     x pointer or length changes; the code loads run one step ahead
+//     straight across tile boundaries, and each tile's LoRA rows and the
+//     next tile's group scales are fetched when the tile starts, so no tile
+//     boundary waits on memory.
+//   * y (and u) are stored through global-address-space pointers: through
+//     generic ones they become FLAT stores, and while one may be in flight
+//     the compiler turns each wait for a code load into a wait for all
+//     loads, draining the loads that run ahead.
 //
 // The job table lives in device memory (written by one copy per call), so
-// one launch covers every job.
+// one launch per kind of job covers every job.
 #include <algorithm>
 #include <mutex>
 #include <cstring>

@@ -94,7 +94,7 @@ hipError_t paged_adamw(const qlora_paged_tensor* t, int nt, char* ws, const qlor
                        float b1, float b2, float eps, float wd, int step, int flags, hipStream_t st,
                        hipStream_t copy_stream);
 
-// Batch-1 decode.
+// Decode of one to 16 tokens per linear.
 struct GemvJob {
   const uint8_t* codes;
   const uint8_t* absmax_q;
@@ -113,8 +113,10 @@ struct GemvJob {
 // gemv_prepare writes the job table (jobs, per-workgroup tile segments and
 // the u = A x map) into `table` (device memory of at least
 // gemv_table_bound(njobs, max rows) bytes) by one host-to-device copy on
-// `st`; gemv_run then launches u = A x and the NF4 GEMV (two launches of it
-// when some jobs need the byte-wise absmax path).
+// `st`; gemv_run then launches u = A x (one launch for the one-token jobs,
+// one for the others) and the NF4 GEMV (one launch per kind of job present:
+// one token or several, with absmax rows read two or four bytes at a time or
+// byte by byte).
 size_t gemv_table_bound(int njobs, int64_t max_rows);
 size_t gemv_lds_bytes(int64_t K);
 // What gemv_run needs besides the table in device memory.
