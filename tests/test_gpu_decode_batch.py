@@ -58,9 +58,11 @@ def _run(ds, label, codebook="nf4"):
 
 # (1100, 2112): 33 blocks per row (a last step of one block), three x chunks
 # with a short last one, three tiles with a partial last one.
+# (70, 64) and (130, 192): rows of one and three blocks, so most of a
+# chunk's spans lie past the row end and read other rows' codes (or nothing).
 @pytest.mark.parametrize("N,K,r,m", [(300, 640, 16, 2), (1100, 2112, 8, 3), (520, 1024, 0, 16),
                                      (512, 4096, 64, 16), (64, 128, 32, 5), (96, 3072, 128, 8),
-                                     (40, 22016, 64, 4)])
+                                     (40, 22016, 64, 4), (70, 64, 8, 3), (130, 192, 16, 16)])
 def test_single_job_shapes(N, K, r, m):
     _run([_job(N, K, r, m, seed=N + K + r + m)], f"N{N} K{K} r{r} m{m}")
 
