@@ -110,6 +110,7 @@ __global__ __launch_bounds__(kThreads, 1) void rskinny_kernel(const bf16_t* __re
   };
 
   constexpr int FJ = RP / 32;
+  static_assert(!QT || FJ == 2 || FJ == 4, "transposed rank side: RP 64 or 128");
   f32x16_t acc[FJ];
 #pragma unroll
   for (int f = 0; f < FJ; ++f)
@@ -135,15 +136,19 @@ __global__ __launch_bounds__(kThreads, 1) void rskinny_kernel(const bf16_t* __re
         const int ch = QT ? 2 * kk + h : 2 * h + kk;
         bf16x8_t b = rd16(base + spos(32 * w + lr, ch));
         if (32 * st + 8 * ch >= C) b = bf16x8_t{};   // columns past C (C % 8 == 0)
+        bf16x8_t a[FJ];
+        if constexpr (!QT) {
 #pragma unroll
-        for (int f = 0; f < FJ; ++f) {
-          bf16x8_t a;
-          if constexpr (!QT)
-            a = rd16(base + S::kP + spos(32 * f + lr, 2 * h + kk));
-          else
-            a = tr_frag<2 * RP>(base + S::kP + kk * 16 * 2 * RP + tr_off<2 * RP>(f));
-          acc[f] = mfma32x32x16(a, b, acc[f]);
+          for (int f = 0; f < FJ; ++f) a[f] = rd16(base + S::kP + spos(32 * f + lr, 2 * h + kk));
+        } else {
+          // transposed reads in asm blocks (see tr_read2): FJ is 2 or 4
+          constexpr int O = 4 * 2 * RP;
+          const char* qb = base + S::kP + kk * 16 * 2 * RP;
+#pragma unroll
+          for (int f = 0; f < FJ; f += 2) tr_read2<O, O>(qb + tr_off<2 * RP>(f), qb + tr_off<2 * RP>(f + 1), a[f], a[f + 1]);
         }
+#pragma unroll
+        for (int f = 0; f < FJ; ++f) acc[f] = mfma32x32x16(a[f], b, acc[f]);
       }
       slot = slot == kRing - 1 ? 0 : slot + 1;
     }
@@ -226,6 +231,7 @@ __global__ __launch_bounds__(kThreads, 1) void cskinny_kernel(const bf16_t* __re
   };
 
   constexpr int FJ = RP / 32;
+  static_assert(FJ == 2 || FJ == 4 || FJ == 8, "RP 64, 128 or 256");
   f32x16_t acc[FJ];
 #pragma unroll
   for (int f = 0; f < FJ; ++f)
@@ -244,12 +250,23 @@ __global__ __launch_bounds__(kThreads, 1) void cskinny_kernel(const bf16_t* __re
       const char* base = smem + slot * S::kStage;
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        const bf16x8_t bg = tr_frag<256>(base + kk * 16 * 256 + bo_frag);
+        // transposed reads in asm blocks (see tr_read3): the big tile's
+        // fragment and the first two rank fragments, then three at a time
+        constexpr int O = 4 * 2 * RP;
+        const char* sb = base + S::kBig + kk * 16 * 2 * RP;
+        bf16x8_t bg, sm[FJ];
+        tr_read3<4 * 256, O, O>(base + kk * 16 * 256 + bo_frag, sb + tr_off<2 * RP>(0), sb + tr_off<2 * RP>(1), bg,
+                                sm[0], sm[1]);
+        if constexpr (FJ == 4) tr_read2<O, O>(sb + tr_off<2 * RP>(2), sb + tr_off<2 * RP>(3), sm[2], sm[3]);
+        if constexpr (FJ == 8) {
 #pragma unroll
-        for (int f = 0; f < FJ; ++f) {
-          const bf16x8_t sm = tr_frag<2 * RP>(base + S::kBig + kk * 16 * 2 * RP + tr_off<2 * RP>(f));
-          acc[f] = DB ? mfma32x32x16(sm, bg, acc[f]) : mfma32x32x16(bg, sm, acc[f]);
+          for (int f = 2; f < 8; f += 3)
+            tr_read3<O, O, O>(sb + tr_off<2 * RP>(f), sb + tr_off<2 * RP>(f + 1), sb + tr_off<2 * RP>(f + 2), sm[f],
+                              sm[f + 1], sm[f + 2]);
         }
+#pragma unroll
+        for (int f = 0; f < FJ; ++f)
+          acc[f] = DB ? mfma32x32x16(sm[f], bg, acc[f]) : mfma32x32x16(bg, sm[f], acc[f]);
       }
       slot = slot == kRing - 1 ? 0 : slot + 1;
     }

@@ -61,6 +61,64 @@ __device__ __forceinline__ bf16x8_t tr_frag(const char* p) {
   const uint2 lo = rd_tr(p), hi = rd_tr(p + 4 * PB);
   return __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
 }
+// Batched transposed reads.  The compiler cannot tell a ds_read_b64_tr_b16
+// builtin apart from the buffer->LDS DMA writes in flight, so before the
+// first such read it waits for every DMA: a ring that keeps stages in flight
+// would be drained at every stage.  Here the reads of up to three tr_frag
+// fragments (fragment i at p_i, second half O_i bytes further) are issued
+// from one asm block that also waits for them, so its outputs are complete
+// when the block ends; the caller's own vmcnt wait and barrier order the
+// reads after the DMA of the stage they read.
+__device__ __forceinline__ uint32_t lds_addr(const char* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+__device__ __forceinline__ bf16x8_t cat_frag(u32x2_t lo, u32x2_t hi) {
+  return __builtin_bit_cast(bf16x8_t, u32x4_t{lo.x, lo.y, hi.x, hi.y});
+}
+template <int O0>
+__device__ __forceinline__ void tr_read1(const char* p0, bf16x8_t& f0) {
+  u32x2_t a0, a1;
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %2\n\t"
+      "ds_read_b64_tr_b16 %1, %2 offset:%3\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(a0), "=&v"(a1)
+      : "v"(lds_addr(p0)), "i"(O0));
+  f0 = cat_frag(a0, a1);
+}
+template <int O0, int O1>
+__device__ __forceinline__ void tr_read2(const char* p0, const char* p1, bf16x8_t& f0, bf16x8_t& f1) {
+  u32x2_t a0, a1, b0, b1;
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %4\n\t"
+      "ds_read_b64_tr_b16 %1, %4 offset:%6\n\t"
+      "ds_read_b64_tr_b16 %2, %5\n\t"
+      "ds_read_b64_tr_b16 %3, %5 offset:%7\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(a0), "=&v"(a1), "=&v"(b0), "=&v"(b1)
+      : "v"(lds_addr(p0)), "v"(lds_addr(p1)), "i"(O0), "i"(O1));
+  f0 = cat_frag(a0, a1);
+  f1 = cat_frag(b0, b1);
+}
+template <int O0, int O1, int O2>
+__device__ __forceinline__ void tr_read3(const char* p0, const char* p1, const char* p2, bf16x8_t& f0, bf16x8_t& f1,
+                                         bf16x8_t& f2) {
+  u32x2_t a0, a1, b0, b1, c0, c1;
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %6\n\t"
+      "ds_read_b64_tr_b16 %1, %6 offset:%9\n\t"
+      "ds_read_b64_tr_b16 %2, %7\n\t"
+      "ds_read_b64_tr_b16 %3, %7 offset:%10\n\t"
+      "ds_read_b64_tr_b16 %4, %8\n\t"
+      "ds_read_b64_tr_b16 %5, %8 offset:%11\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(a0), "=&v"(a1), "=&v"(b0), "=&v"(b1), "=&v"(c0), "=&v"(c1)
+      : "v"(lds_addr(p0)), "v"(lds_addr(p1)), "v"(lds_addr(p2)), "i"(O0), "i"(O1), "i"(O2));
+  f0 = cat_frag(a0, a1);
+  f1 = cat_frag(b0, b1);
+  f2 = cat_frag(c0, c1);
+}
+
 // Position of 16-byte chunk c of row r in a 64-byte-row tile.
 __device__ __forceinline__ int spos(int r, int c) { return r * 64 + 16 * (c ^ ((r >> 2) & 3)); }
 
