@@ -321,10 +321,11 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(const float* __restric
 }
 
 // Splits of the contraction (stages of 32) for about `target` workgroups,
-// at least 8 stages each.  The targets (256, one per CU of the part this is
-// tuned for, and 512 for dY B) were measured; they are fixed, not the
-// device's CU count, because the workspace size a caller queries must not
-// depend on which device is current.
+// at least 8 stages each.  The target (256, one per CU of the part this is
+// tuned for) was measured; it is fixed, not the device's CU count, because
+// the workspace size a caller queries must not depend on which device is
+// current.  It does not depend on the number of groups a launch covers
+// either, so that a group call sums in the order of the per-linear calls.
 struct Split {
   int tiles, sps, splits;
 };
@@ -342,7 +343,7 @@ Split split_for(int64_t tiles, int64_t contraction, int target) {
 Split kind_split(int64_t rows, int64_t cols, int64_t contraction, int kind) {
   // rows x cols is the output: kXAt, kDyB [M x r]; kGtX [r x K]; kDytU [N x r]
   const int64_t tiles = (kind == kGtX) ? (cols + 127) / 128 : (rows + 127) / 128;
-  return split_for(tiles, contraction, kind == kDyB ? 512 : 256);
+  return split_for(tiles, contraction, 256);
 }
 
 hipError_t reduce(const float* part, int splits, int64_t n, float scale, float* out_f32, bf16_t* out_bf16,
@@ -366,7 +367,7 @@ struct RowArgs {
 
 template <int RP, bool QT>
 hipError_t run_rows(const RowArgs& a, float* part, float scale, bf16_t* out, bf16_t* out2, hipStream_t st) {
-  const Split sp = split_for((a.M + 127) / 128, a.C, QT ? 512 : 256);
+  const Split sp = split_for((a.M + 127) / 128, a.C, 256);
   auto* fn = &rskinny_kernel<RP, QT>;
   const size_t lds = (size_t)kRing * RowShape<RP, QT>::kStage;
   hipError_t e = allow_lds(reinterpret_cast<const void*>(fn), (int)lds);

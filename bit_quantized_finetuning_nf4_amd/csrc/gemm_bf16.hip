@@ -367,11 +367,25 @@ __global__ __launch_bounds__(kThreads, 1) void bf16_fwd_kernel(const bf16_t* __r
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       const int o = kk ? fo.o1 : fo.o0;
+      if (b_trans) {
+        // transposed reads in asm blocks, so that the DMAs of later chunks
+        // stay in flight (see tr_read2)
+        const char* tb = buf + kk * 16 * 512;
+        const int f0 = wc * FI;
+        if constexpr (FI == 3) {
+          tr_read3<2048, 2048, 2048>(tb + tr_off<512>(f0), tb + tr_off<512>(f0 + 1), tb + tr_off<512>(f0 + 2), F.a0[0],
+                                     F.a0[1], F.a0[2]);
+        } else {
+#pragma unroll
+          for (int i = 0; i < FI; i += 2)
+            tr_read2<2048, 2048>(tb + tr_off<512>(f0 + i), tb + tr_off<512>(f0 + i + 1), F.a0[i], F.a0[i + 1]);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < FI; ++i) F.a0[i] = rd16(buf + am64 + i * 2048 + o);
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        if (i < FI)
-          F.a0[i] = b_trans ? tr_frag<512>(buf + kk * 16 * 512 + tr_off<512>(wc * FI + i))
-                            : rd16(buf + am64 + i * 2048 + o);
         const bf16x8_t b = rd16(buf + kOp + bm64 + i * 2048 + o);
         F.b0[i] = raw ? scale_frag(b, s) : b;
       }
