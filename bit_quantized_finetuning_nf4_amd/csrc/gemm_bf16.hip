@@ -445,7 +445,7 @@ __global__ __launch_bounds__(kThreads, 1) void bf16_fwd_kernel(const bf16_t* __r
       tail_chunk(buf, false);
     }
   }
-  store_tile<FI>(acc, Y, N, M, N, m0, n0);
+  store_tile_lds<FI>(acc, Y, N, M, N, m0, n0, smem);
 }
 
 }  // namespace

@@ -1103,7 +1103,7 @@ __global__ __launch_bounds__(kThreads, 1) void nf4_dx_kernel(Nf4View W, const bf
       __builtin_amdgcn_s_barrier();
     }
   }
-  store_tile(acc, dX, K, M, K, m0, k0);
+  store_tile_lds(acc, dX, K, M, K, m0, k0, smem);
 }
 
 // ===========================================================================
@@ -1391,7 +1391,7 @@ __global__ __launch_bounds__(kThreads, 1) void nf4_dx_half_kernel(Nf4View W, con
       __builtin_amdgcn_s_barrier();
     }
   }
-  store_tile(acc, dX, K, M, K, m0, k0);
+  store_tile_lds(acc, dX, K, M, K, m0, k0, smem);
 }
 
 }  // namespace
