@@ -79,45 +79,60 @@ __device__ __forceinline__ void store_tile(const f32x16_t (&acc)[FI][4], bf16_t*
     }
 }
 
-// The same tile through LDS, for callers whose LDS is free at the end (16
-// FI KiB needed).  The direct stores above write 8 bytes per lane into 32
-// rows per instruction, 32 partial cache lines each; here each lane first
-// writes its 8-byte pieces into LDS rows of 16 FI 8-byte units (unit u of
-// row R at u ^ (R & SM), so that the 32 rows of one write instruction fall
-// on different banks), then the workgroup writes the tile out row by row,
-// 16 bytes per lane, a wave instruction covering 1 KiB of whole rows.
-// Units c, c + 1 (c even) sit at the aligned pair (c ^ s) & ~1, swapped
-// when s is odd.
-template <int FI>
-__device__ __forceinline__ void store_tile_lds(const f32x16_t (&acc)[FI][4], bf16_t* out, int64_t ld, int64_t rows,
-                                               int64_t cols, int64_t row0, int64_t col0, char* smem) {
-  constexpr int U = 16 * FI, SM = FI == 3 ? 15 : 31;   // the swizzle stays inside the row
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6, wr = w >> 1, wc = w & 1, lr = lane & 31, h = lane >> 5;
-  QLORA_WAIT(0, 0);   // no load into LDS still in flight
-  __syncthreads();    // and every wave is done with the LDS
-#pragma unroll
-  for (int i = 0; i < FI; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int R = wr * 128 + 32 * j + lr;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int u = wc * 8 * FI + 8 * i + 2 * q + h;
-        *reinterpret_cast<u32x2_t*>(smem + (R * U + (u ^ (R & SM))) * 8) =
-            u32x2_t{pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
-                    pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3])};
-      }
-    }
-  __syncthreads();
+// Output tiles through LDS, for kernels whose LDS is free at the end (16
+// bytes per output column of the tile, 64 KiB per 128 columns of 256
+// tokens).  Direct stores of the MFMA layout write 8 bytes per lane into 32
+// rows per instruction, 32 partial cache lines each.  Instead each lane
+// puts its 8-byte pieces into LDS rows of U 8-byte units (unit u of row R
+// at u ^ (R & SM): the 32 rows of one write instruction fall on different
+// banks, and with U a multiple of 16 and SM < 16, or U a multiple of 32,
+// the unit stays inside its row), then the workgroup writes the tile out row
+// by row, 16 bytes per lane, a wave instruction covering whole rows.  Units
+// c, c + 1 (c even) sit at the aligned pair (c ^ s) & ~1, swapped when s is
+// odd.
+template <int U, int SM>
+__device__ __forceinline__ void lds_put4(char* smem, int R, int u, float x0, float x1, float x2, float x3) {
+  static_assert(U % 32 == 0 || (U % 16 == 0 && SM < 16), "the swizzle must stay inside the row");
+  *reinterpret_cast<u32x2_t*>(smem + (R * U + (u ^ (R & SM))) * 8) = u32x2_t{pack_bf16x2(x0, x1), pack_bf16x2(x2, x3)};
+}
+// The tile's 256 rows out: row R to out + (row0 + R) ld + col0 .. (4 U
+// columns), rows >= rows and columns >= cols skipped (cols % 8 == 0).
+template <int U, int SM>
+__device__ __forceinline__ void lds_tile_out(const char* smem, bf16_t* out, int64_t ld, int64_t rows, int64_t cols,
+                                             int64_t row0, int64_t col0) {
+  const int t = threadIdx.x;
 #pragma unroll 4
   for (int k = 0; k < U / 2; ++k) {
     const int g = k * kThreads + t, R = g / (U / 2), c = 2 * (g % (U / 2)), sw = R & SM;
     u32x4_t v = *reinterpret_cast<const u32x4_t*>(smem + (R * U + ((c ^ sw) & ~1)) * 8);
     if (sw & 1) v = u32x4_t{v.z, v.w, v.x, v.y};
     const int64_t row = row0 + R, col = col0 + 4 * c;
-    if (row < rows && col < cols)  // cols % 8 == 0: the eight columns are all in range
-      *reinterpret_cast<u32x4_t*>(out + row * ld + col) = v;
+    if (row < rows && col < cols) *reinterpret_cast<u32x4_t*>(out + row * ld + col) = v;
   }
+}
+// No load into LDS still in flight, and every wave done with the LDS.
+__device__ __forceinline__ void lds_free_for_output() {
+  QLORA_WAIT(0, 0);
+  __syncthreads();
+}
+
+// store_tile through LDS (16 FI KiB).
+template <int FI>
+__device__ __forceinline__ void store_tile_lds(const f32x16_t (&acc)[FI][4], bf16_t* out, int64_t ld, int64_t rows,
+                                               int64_t cols, int64_t row0, int64_t col0, char* smem) {
+  constexpr int U = 16 * FI, SM = FI == 3 ? 15 : 31;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wr = w >> 1, wc = w & 1, lr = lane & 31, h = lane >> 5;
+  lds_free_for_output();
+#pragma unroll
+  for (int i = 0; i < FI; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        lds_put4<U, SM>(smem, wr * 128 + 32 * j + lr, wc * 8 * FI + 8 * i + 2 * q + h, acc[i][j][4 * q],
+                        acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+  __syncthreads();
+  lds_tile_out<U, SM>(smem, out, ld, rows, cols, row0, col0);
 }
 
 // 16 bytes of a bf16 row scaled by s (fp32 product rounded to bf16).

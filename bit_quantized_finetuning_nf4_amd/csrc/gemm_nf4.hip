@@ -483,22 +483,18 @@ __global__ __launch_bounds__(kThreads, 1) void nf4_fwd_r_kernel(Nf4View W, const
     }
   }
   // Output: lane (lr, h) of wave w holds token m0 + 32 j + lr and weight
-  // columns n0 + 64 w + 32 i + 8 q + 4 h + 0..3.
+  // columns n0 + 64 w + 32 i + 8 q + 4 h + 0..3; out through LDS (128 KiB)
+  lds_free_for_output();
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int64_t row = m0 + 32 * j + lr;
-      if (row >= M) continue;
+    for (int j = 0; j < 8; ++j)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int64_t col = n0 + 64 * f.w + 32 * i + 8 * q + 4 * h;
-        if (col < N)  // N % 8 == 0: the four columns are all in range
-          *reinterpret_cast<uint2*>(Y + row * N + col) =
-              make_uint2(pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
-                         pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]));
-      }
-    }
+      for (int q = 0; q < 4; ++q)
+        lds_put4<64, 31>(smem, 32 * j + lr, 16 * f.w + 8 * i + 2 * q + h, acc[i][j][4 * q], acc[i][j][4 * q + 1],
+                         acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+  __syncthreads();
+  lds_tile_out<64, 31>(smem, Y, N, M, N, m0, n0);
 }
 
 // ===========================================================================
@@ -770,19 +766,17 @@ __global__ __launch_bounds__(64 * WAVES, 1) void nf4_fwd_n32_kernel(Nf4View W, c
     }
   }
   // Output: lane (lr, h) of wave w holds token m0 + 32 j + lr and weight
-  // columns n0 + 32 w + 8 q + 4 h + 0..3.
+  // columns n0 + 32 w + 8 q + 4 h + 0..3; out through LDS (16 WAVES KiB)
+  static_assert(64 * WAVES == kThreads, "the LDS write-out runs on kThreads threads");
+  lds_free_for_output();
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int64_t row = m0 + 32 * j + lr;
-    if (row >= M) continue;
+  for (int j = 0; j < 8; ++j)
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int64_t col = n0 + 32 * f.w + 8 * q + 4 * h;
-      if (col < N)  // N % 8 == 0: the four columns are all in range
-        *reinterpret_cast<uint2*>(Y + row * N + col) = make_uint2(pack_bf16x2(acc[j][4 * q], acc[j][4 * q + 1]),
-                                                                  pack_bf16x2(acc[j][4 * q + 2], acc[j][4 * q + 3]));
-    }
-  }
+    for (int q = 0; q < 4; ++q)
+      lds_put4<8 * WAVES, 31>(smem, 32 * j + lr, 8 * f.w + 2 * q + h, acc[j][4 * q], acc[j][4 * q + 1],
+                              acc[j][4 * q + 2], acc[j][4 * q + 3]);
+  __syncthreads();
+  lds_tile_out<8 * WAVES, 31>(smem, Y, N, M, N, m0, n0);
 }
 
 // ===========================================================================
