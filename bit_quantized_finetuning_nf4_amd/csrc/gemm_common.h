@@ -56,40 +56,17 @@ __device__ __forceinline__ void map_tile(int tiles_c, int tiles_r, int& tc, int&
   tr = id / tiles_c;
 }
 
-// Output: lane (lr, h) of wave (wr, wc) holds token row0 + 128 wr + 32 j + lr
-// and columns col0 + 32 FI wc + 32 i + 8 q + 4 h + 0..3.
-template <int FI>
-__device__ __forceinline__ void store_tile(const f32x16_t (&acc)[FI][4], bf16_t* out, int64_t ld, int64_t rows,
-                                           int64_t cols, int64_t row0, int64_t col0) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wr = w >> 1, wc = w & 1, lr = lane & 31, h = lane >> 5;
-#pragma unroll
-  for (int i = 0; i < FI; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t row = row0 + wr * 128 + 32 * j + lr;
-      if (row >= rows) continue;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int64_t col = col0 + wc * 32 * FI + 32 * i + 8 * q + 4 * h;
-        if (col < cols)  // cols % 8 == 0: the four columns are all in range
-          *reinterpret_cast<uint2*>(out + row * ld + col) =
-              make_uint2(pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
-                         pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]));
-      }
-    }
-}
-
 // Output tiles through LDS, for kernels whose LDS is free at the end (16
 // bytes per output column of the tile, 64 KiB per 128 columns of 256
-// tokens).  Direct stores of the MFMA layout write 8 bytes per lane into 32
-// rows per instruction, 32 partial cache lines each.  Instead each lane
-// puts its 8-byte pieces into LDS rows of U 8-byte units (unit u of row R
-// at u ^ (R & SM): the 32 rows of one write instruction fall on different
-// banks, and with U a multiple of 16 and SM < 16, or U a multiple of 32,
-// the unit stays inside its row), then the workgroup writes the tile out row
-// by row, 16 bytes per lane, a wave instruction covering whole rows.  Units
-// c, c + 1 (c even) sit at the aligned pair (c ^ s) & ~1, swapped when s is
-// odd.
+// tokens).  In the MFMA output layout a lane holds four consecutive columns
+// of one row, so direct 8-byte stores would cover 32 rows per instruction,
+// 32 partial cache lines each.  Instead each lane puts its 8-byte pieces
+// into LDS rows of U 8-byte units (unit u of row R at u ^ (R & SM): the 32
+// rows of one write instruction fall on different banks, and with U a
+// multiple of 16 and SM < 16, or U a multiple of 32, the unit stays inside
+// its row), then the workgroup writes the tile out row by row, 16 bytes per
+// lane, a wave instruction covering whole rows.  Units c, c + 1 (c even) sit
+// at the aligned pair (c ^ s) & ~1, swapped when s is odd.
 template <int U, int SM>
 __device__ __forceinline__ void lds_put4(char* smem, int R, int u, float x0, float x1, float x2, float x3) {
   static_assert(U % 32 == 0 || (U % 16 == 0 && SM < 16), "the swizzle must stay inside the row");
@@ -116,7 +93,9 @@ __device__ __forceinline__ void lds_free_for_output() {
   __syncthreads();
 }
 
-// store_tile through LDS (16 FI KiB).
+// The 256-token x 64 FI-column tile of the 2 x 2 wave grid: lane (lr, h) of
+// wave (wr, wc) holds token row0 + 128 wr + 32 j + lr and columns col0 + 32
+// FI wc + 32 i + 8 q + 4 h + 0..3 (16 FI KiB of LDS).
 template <int FI>
 __device__ __forceinline__ void store_tile_lds(const f32x16_t (&acc)[FI][4], bf16_t* out, int64_t ld, int64_t rows,
                                                int64_t cols, int64_t row0, int64_t col0, char* smem) {
