@@ -15,37 +15,67 @@
 
 namespace qlora {
 
-// 4-bit codes of eight fp32 values x = RN32(w / a): c = #{k : x > T_k} over
-// the 15 ascending thresholds of codebook CB (FP4's has one threshold twice,
-// which the count handles alike), by binary search with the code's bits found
-// most significant first.  The first step compares with T_7 (a constant),
-// the others with T_{8c+3}, T_{4c+1}, T_{2c} from an LDS copy of the table:
-// 4 compares instead of 15.  A compare is the sign of T - x: the difference
-// of two finite floats is rounded without changing its sign and is +0 when
-// they are equal, so its sign bit is [x > T] (no threshold is zero).  The
-// funnel shift (c : d) >> 31 appends that bit to c in one instruction.  The
-// eight searches advance step by step together, so that each step's eight
-// LDS reads are in flight at once.
-__device__ __forceinline__ uint32_t gt_bit(float t, float x) { return __builtin_bit_cast(uint32_t, t - x); }
+// Codes without a division.  The code of w is c = #{k : RN32(w / a) > T_k}
+// over the 15 ascending fp32 thresholds T_k of codebook CB (FP4's has one
+// twice, which the count handles alike).  With B_k the midpoint of T_k and
+// the next fp32 above it, RN32(w / a) > T_k exactly when w / a > B_k: w / a
+// is never a rounding boundary itself (w and a are bf16, a boundary has 25
+// significant bits, see below), so it rounds above T_k exactly when it lies
+// above B_k.  For a > 0 that is w > a B_k, and a B_k (8 by 25 significant
+// bits) is exact in fp64.  For any w representable in fp32, w > p holds
+// exactly when w > RD32(p), the largest fp32 value not above p.  So the
+// block's thresholds c_k = RD32(a B_k) are computed once per block (two per
+// lane of the block's eight) and each weight is compared with them as it is.
+//
+// Why w / a is never a boundary: an fp32 rounding boundary B is an odd
+// multiple of a power of two with 25 significant bits, and a B then has at
+// least 25 significant bits, while w has at most 8.
+
+// The midpoint of T_k and the next fp32 value above it (toward +inf; no
+// threshold is zero), exact in fp64.
 template <int CB>
-__device__ __forceinline__ uint32_t nf4_codes8(const float (&x)[8], const float* thr) {
+__device__ __forceinline__ double thresh_mid(int k) {
+  const uint32_t t = cb_thresh_bits<CB>(k);
+  const uint32_t up = (t & 0x80000000u) ? t - 1u : t + 1u;
+  return 0.5 * ((double)u2f(t) + (double)u2f(up));
+}
+// RD32(p): the largest fp32 value not above p.
+__device__ __forceinline__ float rd32(double p) {
+  const float f = (float)p;
+  if (!((double)f > p)) return f;
+  const uint32_t u = f2u(f);
+  return u2f((u & 0x7FFFFFFFu) == 0u ? 0x80000001u : (f > 0.0f ? u - 1u : u + 1u));
+}
+
+// 4-bit codes of eight weights against the block's thresholds c_0 .. c_14 at
+// tb (LDS): c = #{k : w > c_k} by binary search, the code's bits found most
+// significant first, comparing with c_7, then c_{8c+3}, c_{4c+1}, c_{2c}: 4
+// compares instead of 15.  A compare is the sign of c_k - w: the difference
+// of two floats is rounded without changing its sign and is +0 when they are
+// equal, so its sign bit is [w > c_k] (an infinite c_k gives the right sign
+// too).  The funnel shift (c : d) >> 31 appends that bit to c in one
+// instruction.  The eight searches advance step by step together, so that
+// each step's eight LDS reads are in flight at once.
+__device__ __forceinline__ uint32_t gt_bit(float t, float x) { return __builtin_bit_cast(uint32_t, t - x); }
+__device__ __forceinline__ uint32_t codes8(const float (&w)[8], const float* tb) {
   uint32_t c[8];
   float t[8];
+  const float t7 = tb[7];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) c[i] = gt_bit(u2f(cb_thresh_bits<CB>(7)), x[i]) >> 31;
+  for (int i = 0; i < 8; ++i) c[i] = gt_bit(t7, w[i]) >> 31;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) t[i] = thr[8 * c[i] + 3];
+  for (int i = 0; i < 8; ++i) t[i] = tb[8 * c[i] + 3];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) c[i] = __builtin_amdgcn_alignbit(c[i], gt_bit(t[i], x[i]), 31);
+  for (int i = 0; i < 8; ++i) c[i] = __builtin_amdgcn_alignbit(c[i], gt_bit(t[i], w[i]), 31);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) t[i] = thr[4 * c[i] + 1];
+  for (int i = 0; i < 8; ++i) t[i] = tb[4 * c[i] + 1];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) c[i] = __builtin_amdgcn_alignbit(c[i], gt_bit(t[i], x[i]), 31);
+  for (int i = 0; i < 8; ++i) c[i] = __builtin_amdgcn_alignbit(c[i], gt_bit(t[i], w[i]), 31);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) t[i] = thr[2 * c[i]];
+  for (int i = 0; i < 8; ++i) t[i] = tb[2 * c[i]];
   uint32_t packed = 0u;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) packed |= __builtin_amdgcn_alignbit(c[i], gt_bit(t[i], x[i]), 31) << (4 * i);
+  for (int i = 0; i < 8; ++i) packed |= __builtin_amdgcn_alignbit(c[i], gt_bit(t[i], w[i]), 31) << (4 * i);
   return packed;
 }
 
@@ -101,10 +131,13 @@ __global__ __launch_bounds__(256) void quantize_kernel(const bf16_t* __restrict_
                                                        int absfmt) {
   __shared__ float amax[kGroupBlocks];
   __shared__ float red[8];
-  __shared__ float thr[16];
+  __shared__ float thr[32 * 16];   // a pass's 32 blocks: thresholds c_0 .. c_14 each
   const int tid = threadIdx.x;
-  if (tid < 15) thr[tid] = u2f(cb_thresh_bits<CB>(tid));
-  __syncthreads();
+  // this lane computes c_{2j} and c_{2j+1} of its block, j = tid & 7 (c_15
+  // does not exist and is never read)
+  const int j2 = 2 * (tid & 7);
+  const double bm0 = thresh_mid<CB>(j2), bm1 = j2 + 1 < 15 ? thresh_mid<CB>(j2 + 1) : 0.0;
+  float* tb = thr + (tid >> 3) * 16;   // only this wave's lanes touch its blocks' rows
   const int64_t g = blockIdx.x;
   const int64_t gbase = g * (int64_t)kGroupBlocks * kBlock;
   const int64_t code_bytes = (numel + 1) >> 1;
@@ -150,23 +183,12 @@ __global__ __launch_bounds__(256) void quantize_kernel(const bf16_t* __restrict_
 
     uint32_t packed = cb_zero_code<CB>() * 0x11111111u;   // all-zero block: the code of the level 0
     if (m > 0.0f) {
-      // x = RN32(w / a) from the fp64 product w * r, r ~ 1/a.  w and a are
-      // bf16 (at most 8 significant bits) and an fp32 rounding boundary B is
-      // an odd multiple of a power of two with 25 significant bits, so
-      // w - aB is a nonzero multiple of a power of two that is at least
-      // about 2^-33 |w|: w / a is at least that far, relatively, from every
-      // boundary.  r from the hardware reciprocal and two Newton steps is
-      // within 2^-50 relative of 1/a, the product adds 2^-53, so the product
-      // lies on the same side of every boundary as w / a and rounding it to
-      // fp32 gives RN32(w / a).
       const double ad = (double)m;
-      double r = __builtin_amdgcn_rcp(ad);
-      r = fma(r, fma(-ad, r, 1.0), r);
-      r = fma(r, fma(-ad, r, 1.0), r);
-      float x[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) x[i] = (float)((double)f[i] * r);
-      packed = nf4_codes8<CB>(x, thr);
+      tb[j2] = rd32(ad * bm0);
+      if (j2 + 1 < 15) tb[j2 + 1] = rd32(ad * bm1);
+      // the block's eight lanes are in this wave: its LDS writes above are
+      // done before the reads below
+      packed = codes8(f, tb);
     }
     if (e0 + 8 <= numel) {
       *reinterpret_cast<uint32_t*>(codes + (e0 >> 1)) = packed;
