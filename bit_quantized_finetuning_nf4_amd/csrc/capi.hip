@@ -7,7 +7,8 @@
 //   FWD  (r > 0): U bf16 [M x r] | split partials of X A^T (fp32)
 //        staged : ... | deq(W) bf16 [N x K]
 //   BWD  (r > 0): G bf16 [M x r] | U bf16 [M x r] | split partials (fp32,
-//                 the largest of X A^T, dY B, G^T X, dY^T U)
+//                 the largest of X A^T, dY B and G^T X with dY^T U side by
+//                 side)
 //        staged : ... | deq(W)^T bf16 [K x N]
 // A staged call dequantizes W once into the workspace and multiplies with
 // the dense bf16 kernel; otherwise the fused kernels decode W inside each
@@ -161,8 +162,7 @@ size_t lora_part_bytes(int64_t M, int64_t N, int64_t K, int32_t r) {
   if (r == 0) return 0;
   size_t p = skinny_partial_bytes(M, r, K, kXAt);
   p = std::max(p, skinny_partial_bytes(M, r, N, kDyB));
-  p = std::max(p, skinny_partial_bytes(r, K, M, kGtX));
-  p = std::max(p, skinny_partial_bytes(N, r, M, kDytU));
+  p = std::max(p, grads_partial_bytes(M, N, K, r, 1));
   return align_up(p);
 }
 
@@ -170,8 +170,9 @@ size_t lora_part_bytes(int64_t M, int64_t N, int64_t K, int32_t r) {
 // the adapters stacked (A [G r x K], B [G N x r]) and the outputs side by
 // side (Y, dY [M x G N]).  Always staged.
 //   GROUP_FWD: U bf16 [M x G r] | partials of X A^T | deq(W_g) stacked [G N x K]
-//   GROUP_BWD: G bf16 [M x G r] | U bf16 [M x G r] | partials (largest of the
-//              four products) | deq(W_g)^T side by side [K x G N] (with dX)
+//   GROUP_BWD: G bf16 [M x G r] | U bf16 [M x G r] | partials (the largest
+//              of X A^T, dY B and the two gradients' side by side) |
+//              deq(W_g)^T side by side [K x G N] (with dX)
 constexpr int kMaxGroupRank = 256;   // G r: the largest rank tile of the side products
 
 bool group_sizes_ok(int64_t M, int64_t N, int64_t K, int32_t r, int32_t G) {
@@ -181,14 +182,14 @@ bool group_sizes_ok(int64_t M, int64_t N, int64_t K, int32_t r, int32_t G) {
 }
 
 // Split partial sums of the group's side products: U = X A^T at rank G r,
-// dY B and G^T X over all groups, and dY^T U per group.
+// dY B over all groups, and the gradients (G^T X at rank G r and dY^T U per
+// group, side by side).
 size_t group_part_bytes(int64_t M, int64_t N, int64_t K, int32_t r, int32_t G) {
   if (r == 0) return 0;
   const int32_t rg = G * r;
   size_t p = skinny_partial_bytes(M, rg, K, kXAt);
   p = std::max(p, skinny_partial_bytes(M, rg, N, kDyB));
-  p = std::max(p, skinny_partial_bytes(rg, K, M, kGtX));
-  p = std::max(p, (size_t)G * skinny_partial_bytes(N, r, M, kDytU));
+  p = std::max(p, grads_partial_bytes(M, N, K, r, G));
   return align_up(p);
 }
 
@@ -562,9 +563,7 @@ qlora_status qlora_linear_bwd(const qlora_nf4_weight* W, const uint16_t* X, cons
     st = run_dx(G, sc);
     if (st != QLORA_OK) return st;
   }
-  st = hip_status(launch_gtx(G, X, M, K, r, part, dA, sc, s));
-  if (st != QLORA_OK) return st;
-  return hip_status(launch_dytu(dY, U, M, N, r, part, dB, sc, s));
+  return hip_status(launch_grads(G, X, dY, N, U, r, M, N, K, r, 1, part, dA, dB, sc, s));
 }
 
 namespace {
@@ -630,9 +629,7 @@ qlora_status group_grads(const bf16_t* X, const bf16_t* dY, const bf16_t* U, con
                          hipStream_t s) {
   const float sc = lora_s(alpha, r);
   // dA [G r x K] = s G^T X in one pass over X; dB_g = s dY_g^T U_g
-  qlora_status st = hip_status(launch_gtx(Gm, X, M, K, G * r, part, dA, sc, s));
-  if (st != QLORA_OK) return st;
-  return hip_status(launch_dytu_group(dY, (int64_t)G * N, U, G * r, M, N, r, G, part, dB, sc, s));
+  return hip_status(launch_grads(Gm, X, dY, (int64_t)G * N, U, G * r, M, N, K, r, G, part, dA, dB, sc, s));
 }
 
 }  // namespace
@@ -771,8 +768,7 @@ qlora_status qlora_group_lora_grads(const uint16_t* X, const uint16_t* dY, const
   if (!X || !dY || !U || !Gm || !dA || !dB) return QLORA_E_NULL;
   if (!aligned16(X) || !aligned16(dY) || !aligned16(U) || !aligned16(Gm) || !aligned16(dA) || !aligned16(dB))
     return QLORA_E_ALIGN;
-  const size_t need = align_up(std::max(skinny_partial_bytes(G * r, K, M, kGtX),
-                                        (size_t)G * skinny_partial_bytes(N, r, M, kDytU)));
+  const size_t need = align_up(grads_partial_bytes(M, N, K, r, G));
   if ((st = check_ws(ws, ws_bytes, need)) != QLORA_OK) return st;
   return group_grads(X, dY, U, Gm, M, N, K, r, G, alpha, dA, dB, static_cast<float*>(ws), (hipStream_t)stream);
 }
@@ -813,13 +809,11 @@ qlora_status qlora_lora_grads(const uint16_t* X, const uint16_t* dY, const uint1
   if (!X || !dY || !U || !G || !dA || !dB) return QLORA_E_NULL;
   if (!aligned16(X) || !aligned16(dY) || !aligned16(U) || !aligned16(G) || !aligned16(dA) || !aligned16(dB))
     return QLORA_E_ALIGN;
-  const size_t need = align_up(std::max(skinny_partial_bytes(r, K, M, kGtX), skinny_partial_bytes(N, r, M, kDytU)));
+  const size_t need = align_up(grads_partial_bytes(M, N, K, r, 1));
   if ((st = check_ws(ws, ws_bytes, need)) != QLORA_OK) return st;
   const float sc = (float)((double)alpha / (double)r);
   hipStream_t s = (hipStream_t)stream;
-  st = hip_status(launch_gtx(G, X, M, K, r, static_cast<float*>(ws), dA, sc, s));
-  if (st != QLORA_OK) return st;
-  return hip_status(launch_dytu(dY, U, M, N, r, static_cast<float*>(ws), dB, sc, s));
+  return hip_status(launch_grads(G, X, dY, N, U, r, M, N, K, r, 1, static_cast<float*>(ws), dA, dB, sc, s));
 }
 
 qlora_status qlora_nf4_fwd(const qlora_nf4_weight* W, const uint16_t* X, int64_t M, const uint16_t* U,

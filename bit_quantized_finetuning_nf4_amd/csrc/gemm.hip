@@ -320,6 +320,38 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(const float* __restric
   }
 }
 
+// The reductions of dA and dB in one launch: elements [0, n0) of the
+// output are out0 (partials at part0, splits0 of them), the next n1 are out1
+// (part1, splits1); each sums its splits in order, as reduce_kernel does.
+__global__ __launch_bounds__(kThreads) void reduce2_kernel(const float* __restrict__ part0, int splits0, int64_t n0,
+                                                           float* __restrict__ out0,
+                                                           const float* __restrict__ part1, int splits1, int64_t n1,
+                                                           float* __restrict__ out1, float scale) {
+  int64_t i = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * 4;
+  const float* part = part0;
+  float* out = out0;
+  int splits = splits0;
+  int64_t n = n0;
+  if (i >= n0) {
+    i -= n0;
+    part = part1, out = out1, splits = splits1, n = n1;
+  }
+  if (i >= n) return;
+  float4 acc = *reinterpret_cast<const float4*>(part + i);
+  for (int sp = 1; sp < splits; ++sp) {
+    const float4 v = *reinterpret_cast<const float4*>(part + (int64_t)sp * n + i);
+    acc.x += v.x;
+    acc.y += v.y;
+    acc.z += v.z;
+    acc.w += v.w;
+  }
+  acc.x *= scale;
+  acc.y *= scale;
+  acc.z *= scale;
+  acc.w *= scale;
+  *reinterpret_cast<float4*>(out + i) = acc;
+}
+
 // Splits of the contraction (stages of 32) for about `target` workgroups,
 // at least 32 stages each: shorter splits spend most of their time filling
 // the ring and add partials (the 7B and 13B steps ran 1.1-1.4 % faster than
@@ -392,8 +424,10 @@ struct ColArgs {
   int G;
 };
 
+// The token-contraction product's partials (no reduction); *splits gets
+// their count.
 template <int RP, bool DB>
-hipError_t run_cols(const ColArgs& a, float* part, float scale, float* out, hipStream_t st) {
+hipError_t run_cols(const ColArgs& a, float* part, int* splits, hipStream_t st) {
   const Split sp = split_for((a.C + 127) / 128, a.M, 256);
   auto* fn = &cskinny_kernel<RP, DB>;
   const size_t lds = (size_t)kRing * ColShape<RP>::kStage;
@@ -401,8 +435,8 @@ hipError_t run_cols(const ColArgs& a, float* part, float scale, float* out, hipS
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(fn, dim3(sp.tiles * sp.splits, a.G), dim3(kThreads), lds, st, a.Big, a.M, a.C, a.ldb,
                      a.big_gs, a.Sm, a.r, a.lds, a.sm_gs, sp.sps, sp.tiles, part);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  return reduce(part, sp.splits, (int64_t)a.G * a.C * a.r, scale, out, nullptr, nullptr, st);
+  *splits = sp.splits;
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -433,24 +467,31 @@ hipError_t launch_dyb(const bf16_t* dY, const bf16_t* B, int64_t M, int64_t N, i
   return launch_dyb_group(dY, N, B, M, N, r, 1, part, out, scale, st);
 }
 
-hipError_t launch_gtx(const bf16_t* G, const bf16_t* X, int64_t M, int64_t K, int r, float* part, float* dA,
-                      float scale, hipStream_t st) {
-  const ColArgs a{X, M, K, K, 0, G, r, r, 0, 1};
-  if (r <= 64) return run_cols<64, false>(a, part, scale, dA, st);
-  if (r <= 128) return run_cols<128, false>(a, part, scale, dA, st);
-  return run_cols<256, false>(a, part, scale, dA, st);
+size_t grads_partial_bytes(int64_t M, int64_t N, int64_t K, int r, int G) {
+  const size_t a = skinny_partial_bytes(G * r, K, M, kGtX);
+  return (a + 255) / 256 * 256 + (size_t)G * skinny_partial_bytes(N, r, M, kDytU);
 }
 
-hipError_t launch_dytu_group(const bf16_t* dY, int64_t ldy, const bf16_t* U, int ldu, int64_t M, int64_t N, int r,
-                             int G, float* part, float* dB, float scale, hipStream_t st) {
-  const ColArgs a{dY, M, N, ldy, N, U, r, ldu, r, G};
-  if (r <= 64) return run_cols<64, true>(a, part, scale, dB, st);
-  return run_cols<128, true>(a, part, scale, dB, st);
-}
-
-hipError_t launch_dytu(const bf16_t* dY, const bf16_t* U, int64_t M, int64_t N, int r, float* part, float* dB,
-                       float scale, hipStream_t st) {
-  return launch_dytu_group(dY, N, U, r, M, N, r, 1, part, dB, scale, st);
+hipError_t launch_grads(const bf16_t* Gm, const bf16_t* X, const bf16_t* dY, int64_t ldy, const bf16_t* U, int ldu,
+                        int64_t M, int64_t N, int64_t K, int r, int G, float* part, float* dA, float* dB, float scale,
+                        hipStream_t st) {
+  // dA [G r x K] = s G^T X in one pass over X (the stacked rank as one)
+  const int ra = G * r;
+  const ColArgs a{X, M, K, K, 0, Gm, ra, ra, 0, 1};
+  int sa = 0, sb = 0;
+  hipError_t e = ra <= 64    ? run_cols<64, false>(a, part, &sa, st)
+                 : ra <= 128 ? run_cols<128, false>(a, part, &sa, st)
+                             : run_cols<256, false>(a, part, &sa, st);
+  if (e != hipSuccess) return e;
+  // dB_g [N x r] = s dY_g^T U_g for every group, partials after dA's
+  float* part_b = part + (skinny_partial_bytes(ra, K, M, kGtX) + 255) / 256 * 256 / sizeof(float);
+  const ColArgs b{dY, M, N, ldy, N, U, r, ldu, r, G};
+  e = r <= 64 ? run_cols<64, true>(b, part_b, &sb, st) : run_cols<128, true>(b, part_b, &sb, st);
+  if (e != hipSuccess) return e;
+  const int64_t na = (int64_t)ra * K, nb = (int64_t)G * N * r;
+  hipLaunchKernelGGL(reduce2_kernel, dim3((unsigned)(((na + nb) / 4 + kThreads - 1) / kThreads)), dim3(kThreads), 0, st,
+                     part, sa, na, dA, part_b, sb, nb, dB, scale);
+  return hipGetLastError();
 }
 
 }  // namespace qlora

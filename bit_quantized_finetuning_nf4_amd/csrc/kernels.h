@@ -78,15 +78,14 @@ hipError_t launch_dyb(const bf16_t* dY, const bf16_t* B, int64_t M, int64_t N, i
 // G r, N, kDyB).
 hipError_t launch_dyb_group(const bf16_t* dY, int64_t ldy, const bf16_t* B, int64_t M, int64_t N, int r, int G,
                             float* part, bf16_t* out, float scale, hipStream_t st);
-hipError_t launch_gtx(const bf16_t* G, const bf16_t* X, int64_t M, int64_t K, int r, float* part,
-                      float* dA, float scale, hipStream_t st);
-hipError_t launch_dytu(const bf16_t* dY, const bf16_t* U, int64_t M, int64_t N, int r, float* part,
-                       float* dB, float scale, hipStream_t st);
-// G groups: group g reads columns g N .. of dY [M x ldy] and columns g r ..
-// of U [M x ldu], and writes dB + g N r; partials: G skinny_partial_bytes(N,
-// r, M, kDytU).
-hipError_t launch_dytu_group(const bf16_t* dY, int64_t ldy, const bf16_t* U, int ldu, int64_t M, int64_t N, int r,
-                             int G, float* part, float* dB, float scale, hipStream_t st);
+// The adapter gradients: dA [G r x K] = scale G^T X (Gm [M x G r], X [M x
+// K]) and, per group g, dB_g = scale dY_g^T U_g (columns g N .. of dY [M x
+// ldy], columns g r .. of U [M x ldu]) into dB + g N r; the two split
+// reductions run as one launch.  Partials: grads_partial_bytes(M, N, K, r, G).
+size_t grads_partial_bytes(int64_t M, int64_t N, int64_t K, int r, int G);
+hipError_t launch_grads(const bf16_t* Gm, const bf16_t* X, const bf16_t* dY, int64_t ldy, const bf16_t* U, int ldu,
+                        int64_t M, int64_t N, int64_t K, int r, int G, float* part, float* dA, float* dB, float scale,
+                        hipStream_t st);
 
 // The paged optimizer's layout and step (paged.hip).
 bool paged_plan(const qlora_paged_tensor* t, int nt, size_t dev_bytes, qlora_paged_layout* L);
