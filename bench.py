@@ -41,6 +41,7 @@ they are resident in HBM before timing starts.
 """
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -65,6 +66,63 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+# hipEventCreateWithFlags flag (hip_runtime_api.h): no system-scope fence.
+# A default event (torch.cuda.Event) writes back and invalidates the caches
+# when it is recorded; between two kernels that left a gap of about 6 us,
+# more than 4 % of a 7B-set step with its 21 events.  Events made for timing
+# do not need the fence: the timed loops end with a full device
+# synchronization before any result is read on the host.
+HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000
+
+
+class TimingEvent:
+    """A HIP timing event recorded on torch's current stream (the stream the
+    library's kernels are launched on), from the HIP runtime torch loaded."""
+    _hip = None
+
+    @classmethod
+    def hip(cls):
+        if cls._hip is None:
+            import torch
+            torch.cuda.init()
+            path = next((ln.split()[-1] for ln in open("/proc/self/maps") if "libamdhip64" in ln), None)
+            if path is None:
+                raise RuntimeError("the HIP runtime is not loaded in this process")
+            h = ctypes.CDLL(path)
+            h.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+            h.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+            h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+            h.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            cls._hip = h
+        return cls._hip
+
+    def __init__(self):
+        import torch
+        self._torch = torch
+        self.h = ctypes.c_void_p()
+        rc = self.hip().hipEventCreateWithFlags(
+            ctypes.byref(self.h), HIP_EVENT_DISABLE_SYSTEM_FENCE)
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
+
+    def record(self):
+        rc = self.hip().hipEventRecord(self.h, ctypes.c_void_p(self._torch.cuda.current_stream().cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
+
+    def elapsed_time(self, end):
+        """Milliseconds from this event to `end` (both recorded and done)."""
+        ms = ctypes.c_float()
+        rc = self.hip().hipEventElapsedTime(ctypes.byref(ms), self.h, end.h)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return ms.value
+
+    def __del__(self):
+        if self._hip is not None and self.h:
+            self._hip.hipEventDestroy(self.h)
+
+
 def linear_flops(M, N, K, r):
     return 4 * M * N * K + 6 * M * r * (N + K)
 
@@ -81,7 +139,7 @@ def decode_batch_study(jobs, layers, r, alpha, passes, dev):
     layer count, for the 4-bit versus 16-bit decode comparison."""
     import torch
     from bit_quantized_finetuning_nf4_amd import ops, synth
-    E = lambda: torch.cuda.Event(enable_timing=True)
+    E = TimingEvent
 
     def timed(fn):
         for _ in range(DECODE_WARMUP):
@@ -315,7 +373,7 @@ def codebook_study(L, dev, q_bytes, reps=5):
         for o, q in zip(L, qs):
             ops.quantize(o["W"], out=q, codebook=cb, absmax_format=fmt)
         torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a, b = TimingEvent(), TimingEvent()
         a.record()
         for _ in range(reps):
             for o, q in zip(L, qs):
@@ -352,7 +410,7 @@ def optimizer_study(L, r, dev, reps=5):
             m, v = torch.zeros(n, pin_memory=True), torch.zeros(n, pin_memory=True)
         ops.adamw(p, g, m, v, 1, p_bf16=pb)
         torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a, b = TimingEvent(), TimingEvent()
         a.record()
         for t in range(reps):
             ops.adamw(p, g, m, v, t + 2, p_bf16=pb)
@@ -522,7 +580,7 @@ class LayerSet:
         """One step; with `record` (a list) HIP events bracket the phases and
         every dense (or fused) product call."""
         ops, torch, a, L = self.ops, self.torch, self.alpha, self.L
-        E = lambda: torch.cuda.Event(enable_timing=True)
+        E = TimingEvent
         nu = len(self.units(path))
         ev = dict(p=[E() for _ in range(5)], f=[(E(), E()) for _ in range(nu)], d=[(E(), E()) for _ in range(nu)]) \
             if record is not None else None
@@ -663,7 +721,7 @@ def dequant_study(dev, reps=10):
         for _ in range(3):
             fn()
         torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a, b = TimingEvent(), TimingEvent()
         a.record()
         for _ in range(reps):
             fn()
@@ -831,7 +889,7 @@ def main():
     # ---- 80-layer batch-1 decode pass (about 65e9 weights) ----
     if args.decode_layers > 0:
         from bit_quantized_finetuning_nf4_amd import ops
-        E = lambda: torch.cuda.Event(enable_timing=True)
+        E = TimingEvent
         c65 = synth.LAYER_SETS["llama65b"]
         jobs, nbytes = [], 0
         for layer in range(args.decode_layers):
