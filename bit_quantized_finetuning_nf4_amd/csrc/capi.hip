@@ -594,16 +594,27 @@ qlora_status check_group_shape(int64_t M, int64_t N, int64_t K, int32_t r, int32
   return QLORA_OK;
 }
 
-// deq(W_g) into rows g N .. of the stack, or deq(W_g)^T into columns g N ..
+// deq(W_g) into rows g N .. of the stack, or deq(W_g)^T into columns g N ..;
+// consecutive weights with the same codebook and absmax format (up to
+// kDeqMax of them) share one launch.
 qlora_status group_dequant(const qlora_nf4_weight* W, int32_t G, bool transposed, bf16_t* out, hipStream_t s) {
   const int64_t N = W[0].rows, K = W[0].cols;
-  for (int32_t g = 0; g < G; ++g) {
-    const qlora_nf4_weight& q = W[g];
-    hipError_t e = transposed ? launch_dequant_t(q.codes, q.absmax_q, q.group_scale, N, K, q.codebook,
-                                                 q.absmax_format, out + g * N, (int64_t)G * N, s)
-                              : launch_dequant(q.codes, q.absmax_q, q.group_scale, N * K, q.codebook,
-                                               q.absmax_format, out + g * N * K, s);
+  for (int32_t g = 0; g < G;) {
+    DeqSrcs src{};
+    int n = 0;
+    while (g + n < G && n < kDeqMax && W[g + n].codebook == W[g].codebook &&
+           W[g + n].absmax_format == W[g].absmax_format) {
+      src.codes[n] = W[g + n].codes;
+      src.absmax_q[n] = W[g + n].absmax_q;
+      src.group_scale[n] = W[g + n].group_scale;
+      ++n;
+    }
+    hipError_t e = transposed ? launch_dequant_group(src, n, N, K, W[g].codebook, W[g].absmax_format, true,
+                                                     out + g * N, (int64_t)G * N, N, s)
+                              : launch_dequant_group(src, n, N, K, W[g].codebook, W[g].absmax_format, false,
+                                                     out + g * N * K, 0, N * K, s);
     if (e != hipSuccess) return hip_status(e);
+    g += n;
   }
   return QLORA_OK;
 }

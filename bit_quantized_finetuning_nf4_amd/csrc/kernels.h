@@ -43,6 +43,18 @@ hipError_t launch_dequant(const uint8_t* codes, const uint8_t* absmax_q, const f
 hipError_t launch_dequant_t(const uint8_t* codes, const uint8_t* absmax_q, const float* group_scale, int64_t N,
                             int64_t K, int codebook, int absfmt, bf16_t* out, int64_t ldo, hipStream_t s);
 
+// Up to kDeqMax weights of one shape (N x K), one codebook and one absmax
+// format, dequantized by one launch: weight i to out + i out_gs, as
+// launch_dequant (N K weights) or, transposed, as launch_dequant_t.
+constexpr int kDeqMax = 8;
+struct DeqSrcs {
+  const uint8_t* codes[kDeqMax];
+  const uint8_t* absmax_q[kDeqMax];
+  const float* group_scale[kDeqMax];
+};
+hipError_t launch_dequant_group(const DeqSrcs& src, int n, int64_t N, int64_t K, int codebook, int absfmt,
+                                bool transposed, bf16_t* out, int64_t ldo, int64_t out_gs, hipStream_t s);
+
 // Y = X deq(W)^T + s * U * B^T  (U already holds X A^T in bf16; r may be 0)
 hipError_t launch_fwd(const Nf4View& W, const bf16_t* X, int64_t M, const bf16_t* U, const bf16_t* B,
                       int r, float s, bf16_t* Y, hipStream_t st);

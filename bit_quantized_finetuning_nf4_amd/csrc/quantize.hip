@@ -228,12 +228,16 @@ __global__ __launch_bounds__(256) void quantize_kernel(const bf16_t* __restrict_
 // 16 p .. 16 p + 15 (8 code bytes -> 32 bytes of bf16), so a wave reads 512
 // contiguous code bytes and writes 2 KiB of contiguous bf16.  Each lane builds
 // its block's table (the block scale and the 16 products with the levels).
+// Grid y selects one of the launch's weights (all of one shape): weight i
+// goes to out + i out_gs.
 template <int CB>
-__global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict__ codes,
-                                                      const uint8_t* __restrict__ absmax_q,
-                                                      const float* __restrict__ group_scale,
-                                                      int64_t numel, int64_t nb, int absfmt,
-                                                      bf16_t* __restrict__ out) {
+__global__ __launch_bounds__(256) void dequant_kernel(DeqSrcs src, int64_t numel, int64_t nb, int absfmt,
+                                                      bf16_t* __restrict__ out, int64_t out_gs) {
+  const int wi = blockIdx.y;
+  const uint8_t* __restrict__ codes = src.codes[wi];
+  const uint8_t* __restrict__ absmax_q = src.absmax_q[wi];
+  const float* __restrict__ group_scale = src.group_scale[wi];
+  out += wi * out_gs;
   const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t b = g >> 2;
   if (b >= nb) return;
@@ -273,14 +277,17 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict_
 // 32 banks on); then the waves write WdT rows k0 .. k0 + 255, 128 bytes (64
 // rows of W) each, eight whole rows per store instruction.  Rows past N
 // decode as zero and are not written; columns past K are neither read nor
-// written.
+// written.  Grid z selects one of the launch's weights (all of one shape):
+// weight i goes to the columns from i out_gs on.
 constexpr int kTrStride = 33;
 template <int CB>
-__global__ __launch_bounds__(256) void dequant_t_kernel(const uint8_t* __restrict__ codes,
-                                                        const uint8_t* __restrict__ absmax_q,
-                                                        const float* __restrict__ group_scale, int64_t N,
-                                                        int64_t K, int absfmt, bf16_t* __restrict__ out,
-                                                        int64_t ldo) {
+__global__ __launch_bounds__(256) void dequant_t_kernel(DeqSrcs src, int64_t N, int64_t K, int absfmt,
+                                                        bf16_t* __restrict__ out, int64_t ldo, int64_t out_gs) {
+  const int wi = blockIdx.z;
+  const uint8_t* __restrict__ codes = src.codes[wi];
+  const uint8_t* __restrict__ absmax_q = src.absmax_q[wi];
+  const float* __restrict__ group_scale = src.group_scale[wi];
+  out += wi * out_gs;
   __shared__ uint32_t tile[256 * kTrStride];
   const int t = threadIdx.x, rp = t & 31, cg = t >> 5;
   const int64_t n0 = (int64_t)blockIdx.y * 64, k0 = (int64_t)blockIdx.x * 256;
@@ -363,23 +370,40 @@ hipError_t launch_quantize(const bf16_t* W, int64_t numel, uint8_t* codes, uint8
   return hipGetLastError();
 }
 
+hipError_t launch_dequant_group(const DeqSrcs& src, int n, int64_t N, int64_t K, int codebook, int absfmt,
+                                bool transposed, bf16_t* out, int64_t ldo, int64_t out_gs, hipStream_t s) {
+  if (n < 1 || n > kDeqMax) return hipErrorInvalidValue;
+  if (!transposed) {
+    const int64_t numel = N * K, nb = (numel + kBlock - 1) / kBlock;
+    auto* fn = codebook == kCbFp4 ? &dequant_kernel<kCbFp4> : codebook == kCbInt4 ? &dequant_kernel<kCbInt4>
+                                                                                  : &dequant_kernel<kCbNf4>;
+    hipLaunchKernelGGL(fn, dim3((unsigned)((4 * nb + 255) / 256), (unsigned)n), dim3(256), 0, s, src, numel, nb,
+                       absfmt, out, out_gs);
+  } else {
+    auto* fn = codebook == kCbFp4 ? &dequant_t_kernel<kCbFp4> : codebook == kCbInt4 ? &dequant_t_kernel<kCbInt4>
+                                                                                    : &dequant_t_kernel<kCbNf4>;
+    hipLaunchKernelGGL(fn, dim3((unsigned)((K + 255) / 256), (unsigned)((N + 63) / 64), (unsigned)n), dim3(256), 0,
+                       s, src, N, K, absfmt, out, ldo, out_gs);
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_dequant(const uint8_t* codes, const uint8_t* absmax_q, const float* group_scale,
                           int64_t numel, int codebook, int absfmt, bf16_t* out, hipStream_t s) {
-  const int64_t nb = (numel + kBlock - 1) / kBlock;
-  auto* fn = codebook == kCbFp4 ? &dequant_kernel<kCbFp4> : codebook == kCbInt4 ? &dequant_kernel<kCbInt4>
-                                                                                : &dequant_kernel<kCbNf4>;
-  hipLaunchKernelGGL(fn, dim3((unsigned)((4 * nb + 255) / 256)), dim3(256), 0, s, codes, absmax_q, group_scale, numel,
-                     nb, absfmt, out);
-  return hipGetLastError();
+  DeqSrcs src{};
+  src.codes[0] = codes;
+  src.absmax_q[0] = absmax_q;
+  src.group_scale[0] = group_scale;
+  return launch_dequant_group(src, 1, 1, numel, codebook, absfmt, false, out, 0, 0, s);
 }
 
 hipError_t launch_dequant_t(const uint8_t* codes, const uint8_t* absmax_q, const float* group_scale, int64_t N,
                             int64_t K, int codebook, int absfmt, bf16_t* out, int64_t ldo, hipStream_t s) {
-  auto* fn = codebook == kCbFp4 ? &dequant_t_kernel<kCbFp4> : codebook == kCbInt4 ? &dequant_t_kernel<kCbInt4>
-                                                                                  : &dequant_t_kernel<kCbNf4>;
-  hipLaunchKernelGGL(fn, dim3((unsigned)((K + 255) / 256), (unsigned)((N + 63) / 64)), dim3(256), 0, s, codes,
-                     absmax_q, group_scale, N, K, absfmt, out, ldo);
-  return hipGetLastError();
+  DeqSrcs src{};
+  src.codes[0] = codes;
+  src.absmax_q[0] = absmax_q;
+  src.group_scale[0] = group_scale;
+  return launch_dequant_group(src, 1, N, K, codebook, absfmt, true, out, ldo, 0, s);
 }
 
 }  // namespace qlora

@@ -195,3 +195,21 @@ def test_building_blocks_compose_to_the_group_calls(G, M, N, K, r):
     for g, q in enumerate(qs):
         assert torch.equal(Wd[g * N:(g + 1) * N], ops.dequant(q))
         assert torch.equal(WdT[:, g * N:(g + 1) * N], ops.dequant_t(q))
+
+
+def test_group_dequant_mixed_formats_and_long_groups():
+    """The group dequantization batches consecutive weights of one codebook
+    and absmax format into one launch (at most eight): a group that mixes
+    formats, and one longer than a launch holds, still gives every weight's
+    own dequantization in its place, bit for bit."""
+    print("[group dequant] mixed codebooks / formats, G = 3 and G = 11", flush=True)
+    N, K = 128, 320
+    fmts = [("nf4", "linear"), ("fp4", "linear"), ("nf4", "fp8")]
+    for G, pick in ((3, lambda g: fmts[g]), (11, lambda g: fmts[0] if g != 9 else fmts[2])):
+        Ws = [synth.normal_bf16((N, K), 0.02, 700 + 17 * G + g, "cuda") for g in range(G)]
+        qs = [ops.quantize(W, codebook=pick(g)[0], absmax_format=pick(g)[1]) for g, W in enumerate(Ws)]
+        Wd, WdT = ops.group_dequant(qs), ops.group_dequant(qs, transposed=True)
+        torch.cuda.synchronize()
+        for g, q in enumerate(qs):
+            assert torch.equal(Wd[g * N:(g + 1) * N], ops.dequant(q)), (G, g)
+            assert torch.equal(WdT[:, g * N:(g + 1) * N], ops.dequant_t(q)), (G, g)
