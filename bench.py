@@ -557,6 +557,10 @@ class LayerSet:
                 dB=torch.empty(G * N, r, dtype=torch.float32, device=dev)))
         self.ws = ops.workspace(max([ops.workspace_bytes(_lib.QLORA_OP_LORA, M, o["N"], o["K"], r) for o in self.L]
                                     + [ops.workspace_bytes(_lib.QLORA_OP_GROUP_LORA, M, g["N"], g["K"], r, g["G"])
+                                       for g in self.groups]
+                                    + [ops.workspace_bytes(_lib.QLORA_OP_BF16_DX, M, o["N"], o["K"], r, 1)
+                                       for o in self.L]
+                                    + [ops.workspace_bytes(_lib.QLORA_OP_BF16_DX, M, g["N"], g["K"], r, g["G"])
                                        for g in self.groups]), dev)
         self.wbuf = torch.empty(max(g["G"] * g["N"] * g["K"] for g in self.groups), dtype=torch.bfloat16,
                                 device=dev)
@@ -625,7 +629,7 @@ class LayerSet:
             WdT = ops.group_dequant(g["qs"], out=self.wbuf[:G * N * K].view(K, G * N), transposed=True)
             if ev:
                 mark(ev["d"][i][0])
-            ops.bf16_group_dx(WdT, G, g["dY"], g["Gm"], g["A"], a, out=g["dX"])
+            ops.bf16_group_dx(WdT, G, g["dY"], g["Gm"], g["A"], a, out=g["dX"], ws=self.ws)
             if ev:
                 mark(ev["d"][i][1])
             ops.group_lora_grads(g["X"], g["dY"], g["U"], g["Gm"], G, a, dA=g["dA"], dB=g["dB"], ws=self.ws)
@@ -653,7 +657,7 @@ class LayerSet:
                 WdT = ops.dequant_t(o["q"], out=self.wbuf[:o["N"] * o["K"]].view(o["K"], o["N"]))
                 if ev:
                     mark(ev["d"][i][0])
-                ops.bf16_dx(WdT, o["dY"], o["G"], o["A"], a, out=o["dX"])
+                ops.bf16_dx(WdT, o["dY"], o["G"], o["A"], a, out=o["dX"], ws=self.ws)
             else:
                 if ev:
                     mark(ev["d"][i][0])

@@ -13,7 +13,7 @@ LIB_PATH = os.path.join(_HERE, "libqlora.so")
 QLORA_OK = 0
 QLORA_OP_FWD, QLORA_OP_BWD, QLORA_OP_GEMV, QLORA_OP_LORA = 0, 1, 2, 3
 QLORA_OP_FWD_FUSED, QLORA_OP_BWD_FUSED = 4, 5
-QLORA_OP_GROUP_FWD, QLORA_OP_GROUP_BWD, QLORA_OP_GROUP_LORA = 6, 7, 8
+QLORA_OP_GROUP_FWD, QLORA_OP_GROUP_BWD, QLORA_OP_GROUP_LORA, QLORA_OP_BF16_DX = 6, 7, 8, 9
 
 STATUS_NAMES = {
     0: "QLORA_OK", 1: "QLORA_E_NULL", 2: "QLORA_E_ALIGN", 3: "QLORA_E_SHAPE",
@@ -167,7 +167,7 @@ def lib():
     L.qlora_bf16_fwd.restype = ctypes.c_int
     L.qlora_bf16_fwd.argtypes = [vp, i64, i64, vp, i64, vp, vp, i32, f32, vp, vp]
     L.qlora_bf16_dx.restype = ctypes.c_int
-    L.qlora_bf16_dx.argtypes = [vp, i64, i64, vp, i64, vp, vp, i32, f32, vp, vp]
+    L.qlora_bf16_dx.argtypes = [vp, i64, i64, vp, i64, vp, vp, i32, f32, vp, vp, sz, vp]
     L.qlora_nf4_dx.restype = ctypes.c_int
     L.qlora_nf4_dx.argtypes = [W, vp, i64, vp, vp, i32, f32, vp, vp]
     Wg = ctypes.POINTER(Nf4WeightDesc)
@@ -181,7 +181,7 @@ def lib():
     L.qlora_bf16_group_fwd.restype = ctypes.c_int
     L.qlora_bf16_group_fwd.argtypes = [vp, i32, i64, i64, vp, i64, vp, vp, i32, f32, vp, vp]
     L.qlora_bf16_group_dx.restype = ctypes.c_int
-    L.qlora_bf16_group_dx.argtypes = [vp, i32, i64, i64, vp, i64, vp, vp, i32, f32, vp, vp]
+    L.qlora_bf16_group_dx.argtypes = [vp, i32, i64, i64, vp, i64, vp, vp, i32, f32, vp, vp, sz, vp]
     L.qlora_group_lora_dy_b.restype = ctypes.c_int
     L.qlora_group_lora_dy_b.argtypes = [vp, vp, i64, i64, i32, i32, vp, vp, sz, vp]
     L.qlora_group_lora_grads.restype = ctypes.c_int

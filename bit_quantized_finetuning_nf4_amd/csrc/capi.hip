@@ -138,10 +138,10 @@ FwdLayout fwd_layout(int64_t M, int64_t N, int64_t K, int32_t r, bool staged) {
 size_t lora_part_bytes(int64_t M, int64_t N, int64_t K, int32_t r);
 
 struct BwdLayout {
-  size_t g, u, part, wdt, total;
+  size_t g, u, part, wdt, split, split_bytes, total;
 };
 BwdLayout bwd_layout(int64_t M, int64_t N, int64_t K, int32_t r, bool staged) {
-  BwdLayout L{0, 0, 0, 0, 0};
+  BwdLayout L{0, 0, 0, 0, 0, 0, 0};
   if (r > 0) {
     const size_t mr = align_up((size_t)M * r * 2);
     L.g = 0;
@@ -152,6 +152,10 @@ BwdLayout bwd_layout(int64_t M, int64_t N, int64_t K, int32_t r, bool staged) {
   if (staged) {
     L.wdt = L.total;
     L.total += align_up((size_t)N * (size_t)K * 2);
+    // dX [M x K] contracts over N
+    L.split = L.total;
+    L.split_bytes = dense_split_bytes(K, N, M);
+    L.total += align_up(L.split_bytes);
   }
   return L;
 }
@@ -172,7 +176,8 @@ size_t lora_part_bytes(int64_t M, int64_t N, int64_t K, int32_t r) {
 //   GROUP_FWD: U bf16 [M x G r] | partials of X A^T | deq(W_g) stacked [G N x K]
 //   GROUP_BWD: G bf16 [M x G r] | U bf16 [M x G r] | partials (the largest
 //              of X A^T, dY B and the two gradients' side by side) |
-//              deq(W_g)^T side by side [K x G N] (with dX)
+//              deq(W_g)^T side by side [K x G N] and the dense product's
+//              split partials, if it splits (with dX)
 constexpr int kMaxGroupRank = 256;   // G r: the largest rank tile of the side products
 
 bool group_sizes_ok(int64_t M, int64_t N, int64_t K, int32_t r, int32_t G) {
@@ -206,7 +211,7 @@ FwdLayout group_fwd_layout(int64_t M, int64_t N, int64_t K, int32_t r, int32_t G
 }
 
 BwdLayout group_bwd_layout(int64_t M, int64_t N, int64_t K, int32_t r, int32_t G, bool with_dx) {
-  BwdLayout L{0, 0, 0, 0, 0};
+  BwdLayout L{0, 0, 0, 0, 0, 0, 0};
   const int32_t rg = G * r;
   if (r > 0) {
     const size_t mr = align_up((size_t)M * rg * 2);
@@ -217,6 +222,9 @@ BwdLayout group_bwd_layout(int64_t M, int64_t N, int64_t K, int32_t r, int32_t G
   if (with_dx) {
     L.wdt = L.total;
     L.total += align_up((size_t)G * (size_t)N * (size_t)K * 2);
+    L.split = L.total;
+    L.split_bytes = dense_split_bytes(K, (int64_t)G * N, M);
+    L.total += align_up(L.split_bytes);
   }
   return L;
 }
@@ -393,6 +401,9 @@ size_t qlora_workspace_bytes(qlora_op op, int64_t M, int64_t N, int64_t K, int32
     case QLORA_OP_GROUP_LORA:
       if (!group_sizes_ok(M, N, K, r, njobs)) return 0;
       return group_part_bytes(M, N, K, r, njobs);
+    case QLORA_OP_BF16_DX:
+      if (!group_sizes_ok(M, N, K, r, njobs)) return 0;
+      return dense_split_bytes(K, (int64_t)njobs * N, M);
   }
   return 0;
 }
@@ -541,7 +552,8 @@ qlora_status qlora_linear_bwd(const qlora_nf4_weight* W, const uint16_t* X, cons
     qlora_status st2 = hip_status(
         launch_dequant_t(W->codes, W->absmax_q, W->group_scale, N, K, W->codebook, W->absmax_format, WdT, N, s));
     if (st2 != QLORA_OK) return st2;
-    return hip_status(launch_bf16_fwd(WdT, K, N, dY, M, G, r > 0 ? A : nullptr, true, r, sc, dX, s));
+    return hip_status(launch_bf16_fwd(WdT, K, N, dY, M, G, r > 0 ? A : nullptr, true, r, sc, dX, s,
+                                      reinterpret_cast<float*>(ws_at(ws, L.split)), L.split_bytes));
   };
   if (r == 0) {
     if (!dX) return QLORA_OK;
@@ -631,9 +643,11 @@ qlora_status group_fwd_product(const bf16_t* Wd, int32_t G, int64_t N, int64_t K
 // dX = sum_g dY_g deq(W_g) + s sum_g G_g A_g: one dense product contracting
 // over the G N columns of dY, with the stacked adapters as a rank-G r tail
 qlora_status group_dx_product(const bf16_t* WdT, int32_t G, int64_t N, int64_t K, const bf16_t* dY, int64_t M,
-                              const bf16_t* Gm, const bf16_t* A, int32_t r, float alpha, bf16_t* dX, hipStream_t s) {
+                              const bf16_t* Gm, const bf16_t* A, int32_t r, float alpha, bf16_t* dX, hipStream_t s,
+                              float* split, size_t split_bytes) {
   return hip_status(launch_bf16_group(WdT, K, (int64_t)G * N, dY, M, r > 0 ? Gm : nullptr, G * r,
-                                      r > 0 ? A : nullptr, true, G * r, K, lora_s(alpha, r), dX, s));
+                                      r > 0 ? A : nullptr, true, G * r, K, lora_s(alpha, r), dX, s, split,
+                                      split_bytes));
 }
 qlora_status group_grads(const bf16_t* X, const bf16_t* dY, const bf16_t* U, const bf16_t* Gm, int64_t M, int64_t N,
                          int64_t K, int32_t r, int32_t G, float alpha, float* dA, float* dB, float* part,
@@ -694,7 +708,8 @@ qlora_status qlora_group_bwd(const qlora_nf4_weight* W, int32_t G, const uint16_
   if (r == 0) {
     if (!dX) return QLORA_OK;
     if ((st = group_dequant(W, G, true, WdT, s)) != QLORA_OK) return st;
-    return group_dx_product(WdT, G, N, K, dY, M, nullptr, nullptr, 0, alpha, dX, s);
+    return group_dx_product(WdT, G, N, K, dY, M, nullptr, nullptr, 0, alpha, dX, s,
+                            reinterpret_cast<float*>(ws_at(ws, L.split)), L.split_bytes);
   }
   bf16_t* Gm = reinterpret_cast<bf16_t*>(ws_at(ws, L.g));
   float* part = reinterpret_cast<float*>(ws_at(ws, L.part));
@@ -708,7 +723,9 @@ qlora_status qlora_group_bwd(const qlora_nf4_weight* W, int32_t G, const uint16_
   if ((st = hip_status(launch_dyb_group(dY, NG, B, M, N, r, G, part, Gm, 1.0f, s))) != QLORA_OK) return st;
   if (dX) {
     if ((st = group_dequant(W, G, true, WdT, s)) != QLORA_OK) return st;
-    if ((st = group_dx_product(WdT, G, N, K, dY, M, Gm, A, r, alpha, dX, s)) != QLORA_OK) return st;
+    if ((st = group_dx_product(WdT, G, N, K, dY, M, Gm, A, r, alpha, dX, s,
+                               reinterpret_cast<float*>(ws_at(ws, L.split)), L.split_bytes)) != QLORA_OK)
+      return st;
   }
   return group_grads(X, dY, U, Gm, M, N, K, r, G, alpha, dA, dB, part, s);
 }
@@ -744,13 +761,14 @@ qlora_status qlora_bf16_group_fwd(const uint16_t* Wd, int32_t G, int64_t N, int6
 
 qlora_status qlora_bf16_group_dx(const uint16_t* WdT, int32_t G, int64_t N, int64_t K, const uint16_t* dY,
                                  int64_t M, const uint16_t* Gm, const uint16_t* A, int32_t r, float alpha,
-                                 uint16_t* dX, void* stream) {
+                                 uint16_t* dX, void* ws, size_t ws_bytes, void* stream) {
   qlora_status st = check_group_shape(M, N, K, r, G);
   if (st != QLORA_OK) return st;
   if (!WdT || !dY || !dX) return QLORA_E_NULL;
-  if (!aligned16(WdT) || !aligned16(dY) || !aligned16(dX)) return QLORA_E_ALIGN;
+  if (!aligned16(WdT) || !aligned16(dY) || !aligned16(dX) || (ws && !aligned16(ws))) return QLORA_E_ALIGN;
   if ((st = check_rank(r, Gm, A)) != QLORA_OK) return st;
-  return group_dx_product(WdT, G, N, K, dY, M, Gm, A, r, alpha, dX, (hipStream_t)stream);
+  return group_dx_product(WdT, G, N, K, dY, M, Gm, A, r, alpha, dX, (hipStream_t)stream, static_cast<float*>(ws),
+                          ws ? ws_bytes : 0);
 }
 
 qlora_status qlora_group_lora_dy_b(const uint16_t* dY, const uint16_t* B, int64_t M, int64_t N, int32_t r,
@@ -859,19 +877,19 @@ qlora_status qlora_bf16_fwd(const uint16_t* Wd, int64_t N, int64_t K, const uint
 
 qlora_status qlora_bf16_dx(const uint16_t* WdT, int64_t N, int64_t K, const uint16_t* dY, int64_t M,
                            const uint16_t* G, const uint16_t* A, int32_t r, float alpha, uint16_t* dX,
-                           void* stream) {
+                           void* ws, size_t ws_bytes, void* stream) {
   if (N <= 0 || K <= 0 || M <= 0) return QLORA_E_SHAPE;
   if (K % 64 != 0 || N % 64 != 0) return QLORA_E_UNSUPPORTED;
   if (N > (int64_t)0x7FFFFFFF / K || M > (int64_t)0x7FFFFFFF / K || M > (int64_t)0x7FFFFFFF / N)
     return QLORA_E_UNSUPPORTED;
   if (!WdT || !dY || !dX) return QLORA_E_NULL;
-  if (!aligned16(WdT) || !aligned16(dY) || !aligned16(dX)) return QLORA_E_ALIGN;
+  if (!aligned16(WdT) || !aligned16(dY) || !aligned16(dX) || (ws && !aligned16(ws))) return QLORA_E_ALIGN;
   qlora_status st = check_rank(r, G, A);
   if (st != QLORA_OK) return st;
   const float sc = r > 0 ? (float)((double)alpha / (double)r) : 0.0f;
   // dX [M x K] = dY [M x N] (WdT [K x N])^T + s G (A^T)^T
   return hip_status(launch_bf16_fwd(WdT, K, N, dY, M, r > 0 ? G : nullptr, r > 0 ? A : nullptr, true, r, sc, dX,
-                                    (hipStream_t)stream));
+                                    (hipStream_t)stream, static_cast<float*>(ws), ws ? ws_bytes : 0));
 }
 
 qlora_status qlora_nf4_dx(const qlora_nf4_weight* W, const uint16_t* dY, int64_t M, const uint16_t* G,

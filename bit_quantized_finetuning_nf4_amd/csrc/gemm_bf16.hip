@@ -43,10 +43,15 @@ __device__ __forceinline__ int pos128(int r, int c) { return r * 128 + 16 * (c ^
 // groups of kDGroup token tiles, each group column-tile-major, so that the
 // tiles one XCD holds at a time share a few token tiles and a few weight
 // tiles and both stream through its L2.
-__device__ __forceinline__ void map_tile_grouped(int tiles_c, int tiles_r, int& tc, int& tr) {
+// With the contraction split, ids run split-major: the tiles of one split
+// (which share its column range of both operands) sit on the same XCDs.
+__device__ __forceinline__ int xcd_tile_id() {
   const int nwg = (int)gridDim.x;
   int id = blockIdx.x;
   if ((nwg & 7) == 0) id = (id & 7) * (nwg >> 3) + (id >> 3);
+  return id;
+}
+__device__ __forceinline__ void map_tile_grouped(int id, int tiles_c, int tiles_r, int& tc, int& tr) {
   const int per_group = kDGroup * tiles_c;
   const int g = id / per_group, first = g * kDGroup;
   const int size = min(kDGroup, tiles_r - first);
@@ -261,25 +266,55 @@ __device__ __forceinline__ bf16x8_t scale_frag(bf16x8_t v, float s) {
   return __builtin_bit_cast(bf16x8_t, scale16(__builtin_bit_cast(uint4, v), s));
 }
 
+// fp32 sums of the tile (the lane layout of store_tile_lds): lane (lr, h) of
+// wave (wr, wc) holds token row0 + 128 wr + 32 j + lr, columns col0 + 32 FI
+// wc + 32 i + 8 q + 4 h + 0..3, stored as one 16-byte piece (cols % 4 == 0).
+template <int FI>
+__device__ __forceinline__ void store_tile_f32(const f32x16_t (&acc)[FI][4], float* out, int64_t ld, int64_t rows,
+                                               int64_t cols, int64_t row0, int64_t col0) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wr = w >> 1, wc = w & 1, lr = lane & 31, h = lane >> 5;
+#pragma unroll
+  for (int i = 0; i < FI; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t row = row0 + 128 * wr + 32 * j + lr;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t col = col0 + 32 * FI * wc + 32 * i + 8 * q + 4 * h;
+        if (row < rows && col < cols)
+          *reinterpret_cast<float4*>(out + row * ld + col) =
+              make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+      }
+    }
+}
+
 // FI: weight fragments per wave, so the tile is 64 FI weight rows x 256
 // tokens (FI = 4, 3 or 2); its tiles start at weight row n_begin.
+// Split contraction (part != null): the grid holds the tiles once per split;
+// split p takes contraction pairs p pps .. (64-column pairs), split 0 alone
+// adds the LoRA tail, and each split stores its fp32 sums at part + p M N
+// ([M x N], row stride N) instead of Y.
 template <int FI, bool TD>
 __global__ __launch_bounds__(kThreads, 1) void bf16_fwd_kernel(const bf16_t* __restrict__ Wd, int64_t N, int64_t K,
                                                                const bf16_t* __restrict__ X, int64_t M,
                                                                const bf16_t* __restrict__ U,
                                                                const bf16_t* __restrict__ Bl, int b_trans, int r,
                                                                int ldu, int64_t gn, float s, bf16_t* __restrict__ Y,
-                                                               int64_t n_begin, int tiles_n, int tiles_m) {
+                                                               int64_t n_begin, int tiles_n, int tiles_m, int pps,
+                                                               float* __restrict__ part) {
   extern __shared__ __align__(16) char smem[];
   int tn, tm;
-  map_tile_grouped(tiles_n, tiles_m, tn, tm);
+  int id = xcd_tile_id();
+  const int split = id / (tiles_n * tiles_m);
+  map_tile_grouped(id - split * tiles_n * tiles_m, tiles_n, tiles_m, tn, tm);
   const int64_t n0 = n_begin + (int64_t)tn * 64 * FI, m0 = (int64_t)tm * kTile;
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6, wr = wv >> 1, wc = wv & 1;
 
   DenseOps f;
   f.w = __builtin_amdgcn_readfirstlane(wv);
   __builtin_assume(f.w >= 0 && f.w < 4);
-  f.npair = (int)(K >> 6);
+  const int p0 = split * pps;
+  f.npair = min((int)(K >> 6) - p0, pps);
   f.wr_ = make_rsrc(Wd, (uint32_t)(N * K * 2));
   f.xr = make_rsrc(X, (uint32_t)(M * K * 2));
   {
@@ -290,8 +325,8 @@ __global__ __launch_bounds__(kThreads, 1) void bf16_fwd_kernel(const bf16_t* __r
     for (int q = 0; q < 8; ++q) {
       // rows past the end re-read the last row: finite data, never stored
       const int row = 8 * (4 * q + f.w) + (lane >> 3);
-      if (q < 2 * FI) f.wo[q] = (uint32_t)(min(n0 + row, N - 1) * K * 2 + c * 16);
-      f.xo[q] = (uint32_t)(min(m0 + row, M - 1) * K * 2 + c * 16);
+      if (q < 2 * FI) f.wo[q] = (uint32_t)(min(n0 + row, N - 1) * K * 2 + p0 * 128 + c * 16);
+      f.xo[q] = (uint32_t)(min(m0 + row, M - 1) * K * 2 + p0 * 128 + c * 16);
     }
   }
   PairOffs po;
@@ -316,7 +351,8 @@ __global__ __launch_bounds__(kThreads, 1) void bf16_fwd_kernel(const bf16_t* __r
   // chunks, that no tile straddles two adapter groups and that the side
   // arrays fit 32-bit byte offsets); otherwise through registers
   const int64_t g0 = n0 / gn;
-  const bool tdma = TD && r > 0;
+  const bool tail = r > 0 && split == 0;
+  const bool tdma = TD && tail;
   // (built where used, so nothing of it stays live through the main loop)
   auto tail_src = [&]() __attribute__((always_inline)) {
     TailSrc ts;
@@ -417,7 +453,7 @@ __global__ __launch_bounds__(kThreads, 1) void bf16_fwd_kernel(const bf16_t* __r
         }
       }
     }
-  } else if (r > 0) {
+  } else if (tail) {
     // acc += B (s U)^T over the rank, 32 at a time, through 64-byte-row tiles.
     // Weight rows come in groups of gn, each with its own adapter: rows of
     // group g take columns g r .. of U (row stride ldu) and their rows of B;
@@ -445,7 +481,10 @@ __global__ __launch_bounds__(kThreads, 1) void bf16_fwd_kernel(const bf16_t* __r
       tail_chunk(buf, false);
     }
   }
-  store_tile_lds<FI>(acc, Y, N, M, N, m0, n0, smem);
+  if (part != nullptr)
+    store_tile_f32<FI>(acc, part + (int64_t)split * M * N, N, M, N, m0, n0);
+  else
+    store_tile_lds<FI>(acc, Y, N, M, N, m0, n0, smem);
 }
 
 }  // namespace
@@ -466,10 +505,12 @@ bool tail_by_dma(int64_t N, int64_t M, int r, int ldu, int64_t gn, int64_t n_beg
   return true;
 }
 
+// splits > 1: the contraction in that many parts of whole 64-column pairs,
+// fp32 sums to part (splits x M x N floats), not Y.
 template <int FI>
 hipError_t launch_fi(const bf16_t* Wd, int64_t N, int64_t K, const bf16_t* X, int64_t M, const bf16_t* U,
                      const bf16_t* B, bool b_trans, int r, int ldu, int64_t gn, float s, bf16_t* Y, int64_t n_begin,
-                     int64_t n_rows, hipStream_t st) {
+                     int64_t n_rows, hipStream_t st, int splits = 1, float* part = nullptr) {
   const int tiles_n = (int)((n_rows + 64 * FI - 1) / (64 * FI));
   const int tiles_m = (int)((M + kTile - 1) / kTile);
   const bool td = tail_by_dma(N, M, r, ldu, gn, n_begin, tiles_n, 64 * FI);
@@ -477,9 +518,28 @@ hipError_t launch_fi(const bf16_t* Wd, int64_t N, int64_t K, const bf16_t* X, in
   const size_t lds = td ? kLdsDense : kLdsPairs;
   hipError_t e = allow_lds(reinterpret_cast<const void*>(fn), (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(fn, dim3(tiles_n * tiles_m), dim3(kThreads), lds, st, Wd, N, K, X, M, U, B, (int)b_trans, r,
-                     ldu, gn, s, Y, n_begin, tiles_n, tiles_m);
+  const int npair = (int)(K >> 6);
+  const int pps = splits > 1 ? (npair + splits - 1) / splits : npair;
+  hipLaunchKernelGGL(fn, dim3(tiles_n * tiles_m * splits), dim3(kThreads), lds, st, Wd, N, K, X, M, U, B,
+                     (int)b_trans, r, ldu, gn, s, Y, n_begin, tiles_n, tiles_m, pps, splits > 1 ? part : nullptr);
   return hipGetLastError();
+}
+
+// Y [M x N] (bf16) = the sum of the splits' fp32 partials, added in split
+// order; four values per thread (N % 4 == 0).
+__global__ __launch_bounds__(kThreads) void split_sum_kernel(const float* __restrict__ part, int splits, int64_t n,
+                                                             bf16_t* __restrict__ Y) {
+  const int64_t i = 4 * ((int64_t)blockIdx.x * kThreads + threadIdx.x);
+  if (i >= n) return;
+  float4 a = *reinterpret_cast<const float4*>(part + i);
+  for (int p = 1; p < splits; ++p) {
+    const float4 v = *reinterpret_cast<const float4*>(part + (int64_t)p * n + i);
+    a.x += v.x;
+    a.y += v.y;
+    a.z += v.z;
+    a.w += v.w;
+  }
+  *reinterpret_cast<uint2*>(Y + i) = make_uint2(pack_bf16x2(a.x, a.y), pack_bf16x2(a.z, a.w));
 }
 
 // Time of weight rows [n_begin, N) in 64 FI-row tiles, in units of one round
@@ -508,16 +568,44 @@ hipError_t launch_rows(int fi, const bf16_t* Wd, int64_t N, int64_t K, const bf1
 
 }  // namespace
 
+// Split contraction.  A shape with at most half as many 256 x 256 tiles as
+// CUs, which would otherwise run narrower tiles, and a long contraction runs
+// its 256 x 256 tiles twice, each over half the contraction, and adds the
+// two fp32 partials: the 7B gate/up dX product (128 tiles, 22016 columns)
+// took 411 us on 128-row tiles.  The CU count the size of the partials
+// assumes is fixed (256), so that the workspace a caller queries does not
+// depend on the device; the launch splits only if it has that room.
+constexpr int kSplitCus = 256;
+constexpr int64_t kSplitMinK = 16384;
+int dense_splits(int64_t N, int64_t K, int64_t M, int cus) {
+  const int64_t tiles = ((N + kTile - 1) / kTile) * ((M + kTile - 1) / kTile);
+  return (K >= kSplitMinK && N % 4 == 0 && 2 * tiles <= cus) ? 2 : 1;
+}
+
+size_t dense_split_bytes(int64_t N, int64_t K, int64_t M) {
+  const int sp = dense_splits(N, K, M, kSplitCus);
+  return sp > 1 ? (size_t)sp * (size_t)M * (size_t)N * sizeof(float) : 0;
+}
+
 // The grid is sized for the CU count.  Weight rows are cut into a part that
 // fills whole rounds of 256-row tiles and a remainder, whose tile width (256,
 // 192 or 128 rows) minimizes its time; a shape with fewer 256-row tiles than
-// CUs is all remainder.
+// CUs is all remainder, or a split contraction (above) when part has room.
 hipError_t launch_bf16_group(const bf16_t* Wd, int64_t N, int64_t K, const bf16_t* X, int64_t M, const bf16_t* U,
                              int ldu, const bf16_t* B, bool b_trans, int r, int64_t gn, float s, bf16_t* Y,
-                             hipStream_t st) {
+                             hipStream_t st, float* part, size_t part_bytes) {
   const int cus = device_cu_count();
   const int64_t tiles_m = (M + kTile - 1) / kTile;
   const int64_t tiles_n = (N + kTile - 1) / kTile;
+  const int sp = dense_splits(N, K, M, cus);
+  if (sp > 1 && part != nullptr && part_bytes >= (size_t)sp * (size_t)M * (size_t)N * sizeof(float)) {
+    hipError_t e = launch_fi<4>(Wd, N, K, X, M, U, B, b_trans, r, ldu, gn, s, Y, 0, N, st, sp, part);
+    if (e != hipSuccess) return e;
+    const int64_t n = M * N;
+    hipLaunchKernelGGL(split_sum_kernel, dim3((unsigned)((n / 4 + kThreads - 1) / kThreads)), dim3(kThreads), 0, st,
+                       part, sp, n, Y);
+    return hipGetLastError();
+  }
   int64_t n_split = 0;   // rows of the whole-round part
   if (tiles_n * tiles_m > cus && cus % tiles_m == 0) {
     const int64_t per_round = cus / tiles_m;   // 256-row column tiles per round
@@ -537,8 +625,9 @@ hipError_t launch_bf16_group(const bf16_t* Wd, int64_t N, int64_t K, const bf16_
 }
 
 hipError_t launch_bf16_fwd(const bf16_t* Wd, int64_t N, int64_t K, const bf16_t* X, int64_t M, const bf16_t* U,
-                           const bf16_t* B, bool b_trans, int r, float s, bf16_t* Y, hipStream_t st) {
-  return launch_bf16_group(Wd, N, K, X, M, U, r, B, b_trans, r, N, s, Y, st);
+                           const bf16_t* B, bool b_trans, int r, float s, bf16_t* Y, hipStream_t st, float* part,
+                           size_t part_bytes) {
+  return launch_bf16_group(Wd, N, K, X, M, U, r, B, b_trans, r, N, s, Y, st, part, part_bytes);
 }
 
 }  // namespace qlora

@@ -66,16 +66,22 @@ hipError_t launch_dx(const Nf4View& W, const bf16_t* dY, int64_t M, const bf16_t
 // Dense bf16 product on a weight already in bf16, Wd [N x K]:
 // Y [M x N] = X Wd^T + s * U * B'^T (r may be 0), where B' [N x r] is B, or,
 // with b_trans, the transpose of B [r x N].  The backward runs it on the
-// transposed weight: dX = dY (W^T)^T + s G (A^T)^T.
+// transposed weight: dX = dY (W^T)^T + s G (A^T)^T.  part (part_bytes of
+// fp32 scratch, may be null) lets shapes with few tiles and a long
+// contraction split it (dense_split_bytes(N, K, M) bytes are enough).
 hipError_t launch_bf16_fwd(const bf16_t* Wd, int64_t N, int64_t K, const bf16_t* X, int64_t M, const bf16_t* U,
-                           const bf16_t* B, bool b_trans, int r, float s, bf16_t* Y, hipStream_t st);
+                           const bf16_t* B, bool b_trans, int r, float s, bf16_t* Y, hipStream_t st,
+                           float* part = nullptr, size_t part_bytes = 0);
 // The same over a stack of weights with one adapter each: weight rows come in
 // groups of gn (the last may be shorter), and the rows of group g take
 // columns g r .. g r + r - 1 of U (row stride ldu) in the tail.  gn = N and
 // ldu = r is launch_bf16_fwd.
 hipError_t launch_bf16_group(const bf16_t* Wd, int64_t N, int64_t K, const bf16_t* X, int64_t M, const bf16_t* U,
                              int ldu, const bf16_t* B, bool b_trans, int r, int64_t gn, float s, bf16_t* Y,
-                             hipStream_t st);
+                             hipStream_t st, float* part = nullptr, size_t part_bytes = 0);
+// Scratch for a split contraction of the dense product Y [M x N] over K
+// (0 when such a shape is not split).
+size_t dense_split_bytes(int64_t N, int64_t K, int64_t M);
 
 // Skinny products with a deterministic split-contraction reduction.
 // out_bf16 / out_f32 (either may be null) receive scale * result.

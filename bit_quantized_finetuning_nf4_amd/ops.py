@@ -479,9 +479,10 @@ def bf16_fwd(Wd: torch.Tensor, X, U=None, B=None, alpha: float = 0.0, out=None):
     return Y
 
 
-def bf16_dx(WdT: torch.Tensor, dY, G=None, A=None, alpha: float = 0.0, out=None):
+def bf16_dx(WdT: torch.Tensor, dY, G=None, A=None, alpha: float = 0.0, out=None, ws=None):
     """The dense backward GEMM on the transposed bf16 weight WdT [K x N]:
-    dX = dY WdT^T + s G A."""
+    dX = dY WdT^T + s G A.  Shapes with few output tiles and a long
+    contraction split it in ws (allocated here when not given)."""
     _need(WdT, torch.bfloat16, "WdT")
     _need(dY, torch.bfloat16, "dY")
     K, N = WdT.shape
@@ -492,8 +493,10 @@ def bf16_dx(WdT: torch.Tensor, dY, G=None, A=None, alpha: float = 0.0, out=None)
         _need(A, torch.bfloat16, "A", (r, K))
     dX = out if out is not None else torch.empty(M, K, dtype=torch.bfloat16, device=dY.device)
     _need(dX, torch.bfloat16, "dX", (M, K))
-    check(lib().qlora_bf16_dx(_ptr(WdT), N, K, _ptr(dY), M, _ptr(G), _ptr(A), r, float(alpha), _ptr(dX), _stream()),
-          "qlora_bf16_dx")
+    if ws is None:
+        ws = workspace(workspace_bytes(_lib.QLORA_OP_BF16_DX, M, N, K, r, 1), dY.device)
+    check(lib().qlora_bf16_dx(_ptr(WdT), N, K, _ptr(dY), M, _ptr(G), _ptr(A), r, float(alpha), _ptr(dX),
+                              _ptr(ws), 0 if ws is None else ws.numel(), _stream()), "qlora_bf16_dx")
     return dX
 
 
@@ -527,8 +530,9 @@ def bf16_group_fwd(Wd: torch.Tensor, G: int, X, U=None, B=None, alpha: float = 0
     return Y
 
 
-def bf16_group_dx(WdT: torch.Tensor, G: int, dY, Gm=None, A=None, alpha: float = 0.0, out=None):
-    """The group's dense dX product on WdT [K x G N]: dX = dY WdT^T + s Gm A."""
+def bf16_group_dx(WdT: torch.Tensor, G: int, dY, Gm=None, A=None, alpha: float = 0.0, out=None, ws=None):
+    """The group's dense dX product on WdT [K x G N]: dX = dY WdT^T + s Gm A
+    (ws as for bf16_dx)."""
     _need(WdT, torch.bfloat16, "WdT")
     _need(dY, torch.bfloat16, "dY")
     K, N, M = WdT.shape[0], WdT.shape[1] // G, dY.shape[0]
@@ -538,8 +542,10 @@ def bf16_group_dx(WdT: torch.Tensor, G: int, dY, Gm=None, A=None, alpha: float =
         _need(A, torch.bfloat16, "A", (G * r, K))
     dX = out if out is not None else torch.empty(M, K, dtype=torch.bfloat16, device=dY.device)
     _need(dX, torch.bfloat16, "dX", (M, K))
+    if ws is None:
+        ws = workspace(workspace_bytes(_lib.QLORA_OP_BF16_DX, M, N, K, r, G), dY.device)
     check(lib().qlora_bf16_group_dx(_ptr(WdT), G, N, K, _ptr(dY), M, _ptr(Gm), _ptr(A), r, float(alpha), _ptr(dX),
-                                    _stream()), "qlora_bf16_group_dx")
+                                    _ptr(ws), 0 if ws is None else ws.numel(), _stream()), "qlora_bf16_group_dx")
     return dX
 
 

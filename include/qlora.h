@@ -85,10 +85,13 @@ typedef enum {
   QLORA_OP_BWD_FUSED = 5,  /* qlora_linear_bwd, fused path only             */
   QLORA_OP_GROUP_FWD = 6,  /* qlora_group_fwd (njobs = G, the group size)   */
   QLORA_OP_GROUP_BWD = 7,  /* qlora_group_bwd (njobs = G, the group size)   */
-  QLORA_OP_GROUP_LORA = 8  /* the group building blocks' side products:
+  QLORA_OP_GROUP_LORA = 8, /* the group building blocks' side products:
                               qlora_lora_down at rank G r,
                               qlora_group_lora_dy_b, qlora_group_lora_grads
                               (njobs = G)                                    */
+  QLORA_OP_BF16_DX = 9     /* the split contraction of qlora_bf16_dx
+                              (njobs = 1) and qlora_bf16_group_dx (njobs = G):
+                              0 for shapes that do not split                 */
 } qlora_op;
 
 /* A quantized weight: host struct holding device pointers.
@@ -394,10 +397,14 @@ qlora_status qlora_bf16_group_fwd(const uint16_t* Wd, int32_t G, int64_t N, int6
 
 /* dX [M x K] = dY WdT^T + s Gm A, WdT [K x G N], dY [M x G N], Gm [M x G r]
  * (Gm_g = dY_g B_g) and the stacked A [G r x K] (r == 0: Gm = A = NULL).
- * No workspace. */
+ * ws (may be NULL): with at least qlora_workspace_bytes(QLORA_OP_BF16_DX, M,
+ * N, K, r, G) bytes, a shape with few output tiles and a long contraction
+ * (G N) splits the contraction in two and adds the two fp32 halves; with
+ * less room it runs unsplit.  The two differ only in rounding.  A call
+ * that splits overwrites ws. */
 qlora_status qlora_bf16_group_dx(const uint16_t* WdT, int32_t G, int64_t N, int64_t K, const uint16_t* dY,
                                  int64_t M, const uint16_t* Gm, const uint16_t* A, int32_t r, float alpha,
-                                 uint16_t* dX, void* stream);
+                                 uint16_t* dX, void* ws, size_t ws_bytes, void* stream);
 
 /* Gm [M x G r] (bf16): columns g r .. are dY_g B_g, dY [M x G N], B [G N x r].
  * r in (0, 128], G r <= 256, N % 8 == 0, G N < 2^24. */
@@ -459,11 +466,13 @@ qlora_status qlora_bf16_fwd(const uint16_t* Wd, int64_t N, int64_t K, const uint
  * qlora_dequant_t): dX [M x K] = dY WdT^T + s G A, with WdT [K x N] bf16,
  * dY [M x N], G = dY B [M x r] given and A [r x K] (r == 0: G = A = NULL).
  * N % 64 == 0, K % 64 == 0, N*K, M*K and M*N below 2^31
- * (QLORA_E_UNSUPPORTED otherwise).  No workspace.  insights4ai page:
- * gradients flow through the frozen weights into the adapters. */
+ * (QLORA_E_UNSUPPORTED otherwise).  ws (may be NULL) as for
+ * qlora_bf16_group_dx, sized by qlora_workspace_bytes(QLORA_OP_BF16_DX, M,
+ * N, K, r, 1).  insights4ai page: gradients flow through the frozen weights
+ * into the adapters. */
 qlora_status qlora_bf16_dx(const uint16_t* WdT, int64_t N, int64_t K, const uint16_t* dY, int64_t M,
                            const uint16_t* G, const uint16_t* A, int32_t r, float alpha, uint16_t* dX,
-                           void* stream);
+                           void* ws, size_t ws_bytes, void* stream);
 
 /* The fused backward GEMM: dX = dY deq(W) + s G A, with G = dY B given
  * (r == 0: G = A = NULL).  No workspace.  insights4ai page: gradients flow

@@ -86,6 +86,23 @@ def test_workspace_query(L):
     assert L.qlora_workspace_bytes(0, 0, 8, 8, 16, 0) == 0       # invalid -> 0
 
 
+def test_dense_split_workspace(L):
+    """The dense dX product splits its contraction only for shapes with at
+    most 128 output tiles of 256 x 256 and a contraction of 16384 columns or
+    more; the workspace holds the two fp32 partials."""
+    op = _lib.QLORA_OP_BF16_DX
+    # the 7B gate/up group: dX [2048 x 4096] over 2 x 11008 columns
+    assert L.qlora_workspace_bytes(op, 2048, 11008, 4096, 64, 2) == 2 * 2048 * 4096 * 4
+    # each linear alone (11008 columns), q/k/v (12288), 65B shapes (512 tiles): no split
+    assert L.qlora_workspace_bytes(op, 2048, 11008, 4096, 64, 1) == 0
+    assert L.qlora_workspace_bytes(op, 2048, 4096, 4096, 64, 3) == 0
+    assert L.qlora_workspace_bytes(op, 4096, 22016, 8192, 64, 2) == 0
+    # the group backward's workspace has the partials beside deq(W)^T
+    with_split = L.qlora_workspace_bytes(_lib.QLORA_OP_GROUP_BWD, 2048, 11008, 4096, 64, 2)
+    dq = 2 * 11008 * 4096 * 2
+    assert with_split >= dq + 2 * 2048 * 4096 * 4
+
+
 def _desc(rows=64, cols=64, bs=64, g=256, codes=16, aq=16, s2=16):
     return Nf4WeightDesc(rows, cols, bs, g, codes, aq, s2)
 
@@ -338,8 +355,11 @@ def test_group_building_blocks_validate_on_the_host(L):
     assert L.qlora_bf16_group_fwd(fake, 3, 128, 64, fake, 4, fake, fake, 96, 16.0, fake, None) == 4
     assert L.qlora_bf16_group_fwd(fake, 2, 128, 64, fake, 4, None, fake, 16, 16.0, fake, None) == 1
     assert L.qlora_bf16_group_fwd(fake, 2, 1 << 16, 1 << 15, fake, 4, None, None, 0, 0.0, fake, None) == 4
-    assert L.qlora_bf16_group_dx(fake, 2, 128, 64, fake, 4, fake, None, 16, 16.0, fake, None) == 1
-    assert L.qlora_bf16_group_dx(None, 2, 128, 64, fake, 4, None, None, 0, 0.0, fake, None) == 1
+    assert L.qlora_bf16_group_dx(fake, 2, 128, 64, fake, 4, fake, None, 16, 16.0, fake, None, 0, None) == 1
+    assert L.qlora_bf16_group_dx(None, 2, 128, 64, fake, 4, None, None, 0, 0.0, fake, None, 0, None) == 1
+    # a workspace must be 16-byte aligned
+    assert L.qlora_bf16_group_dx(fake, 2, 128, 64, fake, 4, None, None, 0, 0.0, fake, ctypes.c_void_p(4100), 64,
+                                 None) == 2
     # side products
     assert L.qlora_group_lora_dy_b(fake, fake, 4, 128, 16, 2, fake, fake, 16, None) == 5
     assert L.qlora_group_lora_dy_b(fake, fake, 4, 128, 136, 2, fake, fake, big, None) == 4     # r > 128

@@ -104,3 +104,40 @@ def test_dense_forward_tile_widths(N, K, M):
 @pytest.mark.parametrize("N,K,M", [(128, 5120, 2048), (128, 4352, 4096)])
 def test_dense_dx_tile_widths(N, K, M):
     test_dense_dx_matches_oracle(N, K, M, 16)
+
+
+# Split contraction: dX products with at most 128 output tiles of 256 x 256
+# and a contraction of 16384 columns or more run the contraction in two
+# halves and add the fp32 partials (the 7B gate/up dX has 128 tiles over
+# 22016 columns).  Ragged tokens (300) and output columns (576 = two and a
+# quarter tiles), the LoRA tail (split 0 only) large enough to show.
+@pytest.mark.parametrize("N,K,M,r", [(16384, 576, 300, 32), (16448, 512, 256, 0), (22016, 256, 64, 64)])
+def test_dense_dx_split_contraction(N, K, M, r):
+    rng = np.random.default_rng(N + K + M + r + 5)
+    g = lambda shape, std: synth.to_bf16_bits(rng.standard_normal(shape) * std)
+    d = dict(W=g((N, K), 0.02), dY=g((M, N), 1.0), A=g((r, K), 0.5) if r else None,
+             B=g((N, r), 0.5) if r else None, alpha=16.0)
+    from bit_quantized_finetuning_nf4_amd import _lib
+    split_bytes = ops.workspace_bytes(_lib.QLORA_OP_BF16_DX, M, N, K, r, 1)
+    print(f"[dense dX split] N{N} K{K} M{M} r{r} split workspace {split_bytes}", flush=True)
+    assert split_bytes == 2 * M * K * 4
+    q = ops.quantize(bits_to_torch(d["W"]))
+    dY = bits_to_torch(d["dY"])
+    A = bits_to_torch(d["A"]) if r else None
+    G = ops.lora_dy_b(dY, bits_to_torch(d["B"])) if r else None
+    WdT = ops.dequant_t(q)
+    dX = ops.bf16_dx(WdT, dY, G, A, d["alpha"])                      # split (workspace allocated)
+    small = torch.empty(256, dtype=torch.uint8, device=dY.device)   # too small: unsplit
+    dX1 = ops.bf16_dx(WdT, dY, G, A, d["alpha"], ws=small)
+    torch.cuda.synchronize()
+    c, a, s = oracle.quantize(d["W"])
+    Wd = oracle.bf16_bits_to_f64(oracle.dequant(c, a, s, d["W"].size)).reshape(N, K)
+    f = lambda k: None if d[k] is None else oracle.bf16_bits_to_f64(d[k]).reshape(d[k].shape)
+    dXr = f("dY") @ Wd
+    if r:
+        dXr = dXr + d["alpha"] / r * (f("dY") @ f("B")) @ f("A")
+    assert_close(torch_to_f64(dX), dXr, f"split dX N{N} K{K} M{M} r{r}")
+    assert_close(torch_to_f64(dX1), dXr, f"unsplit dX N{N} K{K} M{M} r{r}")
+    # the two orders of summation differ by rounding only
+    diff = (dX.float() - dX1.float()).abs().max().item()
+    assert diff <= 2e-2 * dX1.float().abs().max().item()
