@@ -18,7 +18,10 @@ QLORA_OP_GROUP_FWD, QLORA_OP_GROUP_BWD, QLORA_OP_GROUP_LORA, QLORA_OP_BF16_DX = 
 STATUS_NAMES = {
     0: "QLORA_OK", 1: "QLORA_E_NULL", 2: "QLORA_E_ALIGN", 3: "QLORA_E_SHAPE",
     4: "QLORA_E_UNSUPPORTED", 5: "QLORA_E_WORKSPACE", 6: "QLORA_E_HIP",
+    7: "QLORA_E_FORMAT", 8: "QLORA_E_TABLE",
 }
+QLORA_E_FORMAT, QLORA_E_TABLE = 7, 8
+QTENSOR_HEADER_BYTES = 64
 
 # every function include/qlora.h declares
 EXPORTS = [
@@ -31,6 +34,7 @@ EXPORTS = [
     "qlora_paged_layout_of", "qlora_paged_adamw", "qlora_group_fwd", "qlora_group_bwd",
     "qlora_group_dequant", "qlora_group_dequant_t", "qlora_bf16_group_fwd", "qlora_bf16_group_dx",
     "qlora_group_lora_dy_b", "qlora_group_lora_grads",
+    "qlora_level_table_id", "qlora_qtensor_header_write", "qlora_qtensor_header_read",
 ]
 QLORA_PAGED_LOAD, QLORA_PAGED_STORE = 1, 2
 
@@ -186,6 +190,13 @@ def lib():
     L.qlora_group_lora_dy_b.argtypes = [vp, vp, i64, i64, i32, i32, vp, vp, sz, vp]
     L.qlora_group_lora_grads.restype = ctypes.c_int
     L.qlora_group_lora_grads.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, i32, f32, vp, vp, vp, sz, vp]
+    L.qlora_level_table_id.restype = ctypes.c_int
+    L.qlora_level_table_id.argtypes = [i32, i32, ctypes.POINTER(ctypes.c_uint64)]
+    L.qlora_qtensor_header_write.restype = ctypes.c_int
+    L.qlora_qtensor_header_write.argtypes = [ctypes.POINTER(Nf4WeightDesc), ctypes.c_char_p, sz]
+    L.qlora_qtensor_header_read.restype = ctypes.c_int
+    L.qlora_qtensor_header_read.argtypes = [ctypes.c_char_p, sz, ctypes.POINTER(Nf4WeightDesc),
+                                            ctypes.POINTER(ctypes.c_uint64)]
     _lib = L
     return L
 

@@ -323,6 +323,8 @@ const char* qlora_status_str(qlora_status s) {
     case QLORA_E_UNSUPPORTED: return "QLORA_E_UNSUPPORTED: unsupported blocksize, group, shape or rank";
     case QLORA_E_WORKSPACE: return "QLORA_E_WORKSPACE: workspace smaller than qlora_workspace_bytes()";
     case QLORA_E_HIP: return "QLORA_E_HIP: HIP launch error (see qlora_last_hip_error)";
+    case QLORA_E_FORMAT: return "QLORA_E_FORMAT: not a serialized weight header (magic, version or size)";
+    case QLORA_E_TABLE: return "QLORA_E_TABLE: the weight was written with other level tables";
   }
   return "QLORA_E_UNKNOWN";
 }

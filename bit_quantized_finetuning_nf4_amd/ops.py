@@ -12,10 +12,25 @@ from typing import Optional, Sequence
 import torch
 
 from . import _lib
-from ._lib import GemvJobDesc, GemvPlanDesc, Nf4WeightDesc, PagedLayoutDesc, PagedTensorDesc, check, lib
+from . import debug as _debug
+from ._lib import GemvJobDesc, GemvPlanDesc, Nf4WeightDesc, PagedLayoutDesc, PagedTensorDesc, lib
+from ._lib import check as _check_status
 
 BLOCKSIZE = 64
 GROUP_BLOCKS = 256
+
+
+def check(status, what):
+    """Raise QloraError for a failed call; under QLORA_DEBUG=1 also
+    synchronize and check the guard bands of the binding's buffers."""
+    _check_status(status, what)
+    if _debug.ENABLED:
+        _debug.after_call(what)
+
+
+def _empty(*shape, dtype, device):
+    """An output or workspace buffer (guarded under QLORA_DEBUG=1)."""
+    return _debug.empty(shape, dtype, device)
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -87,7 +102,7 @@ def workspace(nbytes, device):
     """A workspace tensor (uint8) of at least nbytes, or None when 0."""
     if nbytes == 0:
         return None
-    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+    return _empty(nbytes, dtype=torch.uint8, device=device)
 
 
 @dataclass
@@ -111,12 +126,53 @@ class QuantizedWeight:
     def empty(rows, cols, device, codebook="nf4", absmax_format="linear"):
         c, a, s = sizes(rows, cols)
         return QuantizedWeight(rows, cols,
-                               torch.empty(c, dtype=torch.uint8, device=device),
-                               torch.empty(a, dtype=torch.uint8, device=device),
-                               torch.empty(s // 4, dtype=torch.float32, device=device), codebook, absmax_format)
+                               _empty(c, dtype=torch.uint8, device=device),
+                               _empty(a, dtype=torch.uint8, device=device),
+                               _empty(s // 4, dtype=torch.float32, device=device), codebook, absmax_format)
 
     def nbytes(self):
         return self.codes.numel() + self.absmax_q.numel() + 4 * self.group_scale.numel()
+
+
+def save_quantized(q: QuantizedWeight, path) -> None:
+    """Write q to a file: the library's header (sizes, codebook, second-level
+    format and the digest of their level tables), then codes, absmax_q and
+    group_scale as stored.  Reading it back gives the same bytes."""
+    d = q.desc()
+    hdr = ctypes.create_string_buffer(_lib.QTENSOR_HEADER_BYTES)
+    check(lib().qlora_qtensor_header_write(ctypes.byref(d), hdr, len(hdr)), "qlora_qtensor_header_write")
+    c, a, s = sizes(q.rows, q.cols)
+    arrays = ((q.codes, torch.uint8, c), (q.absmax_q, torch.uint8, a), (q.group_scale, torch.float32, s // 4))
+    for t, dtype, n in arrays:
+        if t.dtype != dtype or t.numel() != n or not t.is_contiguous():
+            raise ValueError(f"quantized weight arrays do not match its {q.rows} x {q.cols} sizes")
+    with open(path, "wb") as f:
+        f.write(hdr.raw)
+        for t, _, _ in arrays:
+            f.write(t.detach().cpu().contiguous().view(torch.uint8).numpy().tobytes())
+
+
+def load_quantized(path, device) -> QuantizedWeight:
+    """Read a weight written by save_quantized onto `device`.  Raises
+    QloraError (QLORA_E_TABLE) when the file was written with level tables
+    other than this library's, QLORA_E_FORMAT when it is not such a file."""
+    with open(path, "rb") as f:
+        blob = f.read()
+    d = Nf4WeightDesc()
+    payload = ctypes.c_uint64()
+    check(lib().qlora_qtensor_header_read(blob, len(blob), ctypes.byref(d), ctypes.byref(payload)),
+          "qlora_qtensor_header_read")
+    h = _lib.QTENSOR_HEADER_BYTES
+    if len(blob) != h + payload.value:
+        raise _lib.QloraError(_lib.QLORA_E_FORMAT, f"load_quantized: {path} holds {len(blob) - h} payload "
+                                                   f"bytes, its header says {payload.value}")
+    c, a, s = sizes(d.rows, d.cols)
+    raw = torch.frombuffer(bytearray(blob[h:]), dtype=torch.uint8)
+    names = {v: k for k, v in CODEBOOKS.items()}
+    fmts = {v: k for k, v in ABSMAX_FORMATS.items()}
+    return QuantizedWeight(int(d.rows), int(d.cols), raw[:c].clone().to(device), raw[c:c + a].clone().to(device),
+                           raw[c + a:c + a + s].clone().view(torch.float32).to(device),
+                           names[d.codebook], fmts[d.absmax_format])
 
 
 def quantize(W: torch.Tensor, out: Optional[QuantizedWeight] = None,
@@ -141,7 +197,7 @@ def quantize(W: torch.Tensor, out: Optional[QuantizedWeight] = None,
 def dequant(q: QuantizedWeight, out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """4-bit weight -> bf16 [rows x cols], with its codebook."""
     if out is None:
-        out = torch.empty(q.rows, q.cols, dtype=torch.bfloat16, device=q.codes.device)
+        out = _empty(q.rows, q.cols, dtype=torch.bfloat16, device=q.codes.device)
     _need(out, torch.bfloat16, "out")
     d = q.desc()
     check(lib().qlora_dequant(ctypes.byref(d), _ptr(out), _stream()), "qlora_dequant")
@@ -151,7 +207,7 @@ def dequant(q: QuantizedWeight, out: Optional[torch.Tensor] = None) -> torch.Ten
 def dequant_t(q: QuantizedWeight, out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """4-bit weight -> its transpose in bf16, [cols x rows]."""
     if out is None:
-        out = torch.empty(q.cols, q.rows, dtype=torch.bfloat16, device=q.codes.device)
+        out = _empty(q.cols, q.rows, dtype=torch.bfloat16, device=q.codes.device)
     _need(out, torch.bfloat16, "out", (q.cols, q.rows))
     d = q.desc()
     check(lib().qlora_dequant_t(ctypes.byref(d), _ptr(out), _stream()), "qlora_dequant_t")
@@ -180,10 +236,10 @@ def linear_fwd(q: QuantizedWeight, X: torch.Tensor, A=None, B=None, alpha: float
     if r:
         _need(A, torch.bfloat16, "A", (r, q.cols))
         _need(B, torch.bfloat16, "B", (q.rows, r))
-    Y = out if out is not None else torch.empty(M, q.rows, dtype=torch.bfloat16, device=X.device)
+    Y = out if out is not None else _empty(M, q.rows, dtype=torch.bfloat16, device=X.device)
     U = None
     if save_u and r:
-        U = u_out if u_out is not None else torch.empty(M, r, dtype=torch.bfloat16, device=X.device)
+        U = u_out if u_out is not None else _empty(M, r, dtype=torch.bfloat16, device=X.device)
     nbytes = workspace_bytes(_op(path, _lib.QLORA_OP_FWD, _lib.QLORA_OP_FWD_FUSED), M, q.rows, q.cols, r)
     if ws is None:
         ws = workspace(nbytes, X.device)
@@ -207,11 +263,11 @@ def linear_fwd_noalloc(q: QuantizedWeight, X: torch.Tensor, A=None, B=None, alph
     if r:
         _need(A, torch.bfloat16, "A", (r, q.cols))
         _need(B, torch.bfloat16, "B", (q.rows, r))
-    Y = out if out is not None else torch.empty(M, q.rows, dtype=torch.bfloat16, device=X.device)
+    Y = out if out is not None else _empty(M, q.rows, dtype=torch.bfloat16, device=X.device)
     _need(Y, torch.bfloat16, "Y", (M, q.rows))
     U = None
     if save_u and r:
-        U = u_out if u_out is not None else torch.empty(M, r, dtype=torch.bfloat16, device=X.device)
+        U = u_out if u_out is not None else _empty(M, r, dtype=torch.bfloat16, device=X.device)
         _need(U, torch.bfloat16, "U", (M, r))
     d = q.desc()
     check(lib().qlora_linear_fwd_noalloc(ctypes.byref(d), _ptr(X), M, _ptr(A), _ptr(B), r, float(alpha), _ptr(Y),
@@ -231,12 +287,12 @@ def linear_bwd(q: QuantizedWeight, X: torch.Tensor, dY: torch.Tensor, A=None, B=
         _need(X, torch.bfloat16, "X", (M, q.cols))
         _need(A, torch.bfloat16, "A", (r, q.cols))
         _need(B, torch.bfloat16, "B", (q.rows, r))
-        dA = dA if dA is not None else torch.empty(r, q.cols, dtype=torch.float32, device=dY.device)
-        dB = dB if dB is not None else torch.empty(q.rows, r, dtype=torch.float32, device=dY.device)
+        dA = dA if dA is not None else _empty(r, q.cols, dtype=torch.float32, device=dY.device)
+        dB = dB if dB is not None else _empty(q.rows, r, dtype=torch.float32, device=dY.device)
     else:
         dA = dB = None
     if need_dx:
-        dX = dX if dX is not None else torch.empty(M, q.cols, dtype=torch.bfloat16, device=dY.device)
+        dX = dX if dX is not None else _empty(M, q.cols, dtype=torch.bfloat16, device=dY.device)
     else:
         dX = None
     nbytes = workspace_bytes(_op(path, _lib.QLORA_OP_BWD, _lib.QLORA_OP_BWD_FUSED), M, q.rows, q.cols, r)
@@ -273,10 +329,10 @@ def group_fwd(qs: Sequence[QuantizedWeight], X: torch.Tensor, A=None, B=None, al
     if A is not None:
         _need(A, torch.bfloat16, "A", (G * r, K))
         _need(B, torch.bfloat16, "B", (G * N, r))
-    Y = out if out is not None else torch.empty(M, G * N, dtype=torch.bfloat16, device=X.device)
+    Y = out if out is not None else _empty(M, G * N, dtype=torch.bfloat16, device=X.device)
     U = None
     if save_u and r:
-        U = u_out if u_out is not None else torch.empty(M, G * r, dtype=torch.bfloat16, device=X.device)
+        U = u_out if u_out is not None else _empty(M, G * r, dtype=torch.bfloat16, device=X.device)
     nbytes = workspace_bytes(_lib.QLORA_OP_GROUP_FWD, M, N, K, r, G)
     if ws is None:
         ws = workspace(nbytes, X.device)
@@ -302,12 +358,12 @@ def group_bwd(qs: Sequence[QuantizedWeight], X: torch.Tensor, dY: torch.Tensor, 
         _need(X, torch.bfloat16, "X", (M, K))
         _need(A, torch.bfloat16, "A", (G * r, K))
         _need(B, torch.bfloat16, "B", (G * N, r))
-        dA = dA if dA is not None else torch.empty(G * r, K, dtype=torch.float32, device=dY.device)
-        dB = dB if dB is not None else torch.empty(G * N, r, dtype=torch.float32, device=dY.device)
+        dA = dA if dA is not None else _empty(G * r, K, dtype=torch.float32, device=dY.device)
+        dB = dB if dB is not None else _empty(G * N, r, dtype=torch.float32, device=dY.device)
     else:
         dA = dB = None
     if need_dx:
-        dX = dX if dX is not None else torch.empty(M, K, dtype=torch.bfloat16, device=dY.device)
+        dX = dX if dX is not None else _empty(M, K, dtype=torch.bfloat16, device=dY.device)
     else:
         dX = None
     nbytes = workspace_bytes(_lib.QLORA_OP_GROUP_BWD, M, N, K, r, G)
@@ -377,7 +433,7 @@ def _gemv_desc(j, desc):
         _need(j.A, torch.bfloat16, "A", (r, j.q.cols))
         _need(j.B, torch.bfloat16, "B", (j.q.rows, r))
     shape = (j.q.rows,) if one else (m, j.q.rows)
-    y = j.y if j.y is not None else torch.empty(shape, dtype=torch.bfloat16, device=j.x.device)
+    y = j.y if j.y is not None else _empty(shape, dtype=torch.bfloat16, device=j.x.device)
     _need(y, torch.bfloat16, "y", shape)
     return GemvJobDesc(ctypes.pointer(desc), j.x.data_ptr(), None if r == 0 else j.A.data_ptr(),
                        None if r == 0 else j.B.data_ptr(), r, float(j.alpha), y.data_ptr(), m), y
@@ -410,7 +466,7 @@ def lora_down(X, A, U=None, ws=None):
     M, K = X.shape
     r = A.shape[0]
     _need(A, torch.bfloat16, "A", (r, K))
-    U = U if U is not None else torch.empty(M, r, dtype=torch.bfloat16, device=X.device)
+    U = U if U is not None else _empty(M, r, dtype=torch.bfloat16, device=X.device)
     if ws is None:
         ws = workspace(workspace_bytes(_lib.QLORA_OP_LORA, M, 8, K, r), X.device)
     check(lib().qlora_lora_down(_ptr(X), _ptr(A), M, K, r, _ptr(U), _ptr(ws), 0 if ws is None else ws.numel(),
@@ -424,7 +480,7 @@ def lora_dy_b(dY, B, G=None, ws=None):
     M, N = dY.shape
     r = B.shape[1]
     _need(B, torch.bfloat16, "B", (N, r))
-    G = G if G is not None else torch.empty(M, r, dtype=torch.bfloat16, device=dY.device)
+    G = G if G is not None else _empty(M, r, dtype=torch.bfloat16, device=dY.device)
     if ws is None:
         ws = workspace(workspace_bytes(_lib.QLORA_OP_LORA, M, N, 8, r), dY.device)
     check(lib().qlora_lora_dy_b(_ptr(dY), _ptr(B), M, N, r, _ptr(G), _ptr(ws), 0 if ws is None else ws.numel(),
@@ -439,8 +495,8 @@ def lora_grads(X, dY, U, G, alpha, dA=None, dB=None, ws=None):
     r = U.shape[1]
     for t, n, shp in ((X, "X", (M, K)), (dY, "dY", (M, N)), (U, "U", (M, r)), (G, "G", (M, r))):
         _need(t, torch.bfloat16, n, shp)
-    dA = dA if dA is not None else torch.empty(r, K, dtype=torch.float32, device=X.device)
-    dB = dB if dB is not None else torch.empty(N, r, dtype=torch.float32, device=X.device)
+    dA = dA if dA is not None else _empty(r, K, dtype=torch.float32, device=X.device)
+    dB = dB if dB is not None else _empty(N, r, dtype=torch.float32, device=X.device)
     if ws is None:
         ws = workspace(workspace_bytes(_lib.QLORA_OP_LORA, M, N, K, r), X.device)
     check(lib().qlora_lora_grads(_ptr(X), _ptr(dY), _ptr(U), _ptr(G), M, N, K, r, float(alpha), _ptr(dA),
@@ -454,7 +510,7 @@ def nf4_fwd(q: QuantizedWeight, X, U=None, B=None, alpha: float = 0.0, out=None)
     _need(X, torch.bfloat16, "X")
     M = X.shape[0]
     r = 0 if U is None else U.shape[1]
-    Y = out if out is not None else torch.empty(M, q.rows, dtype=torch.bfloat16, device=X.device)
+    Y = out if out is not None else _empty(M, q.rows, dtype=torch.bfloat16, device=X.device)
     d = q.desc()
     check(lib().qlora_nf4_fwd(ctypes.byref(d), _ptr(X), M, _ptr(U), _ptr(B), r, float(alpha), _ptr(Y),
                               _stream()), "qlora_nf4_fwd")
@@ -472,7 +528,7 @@ def bf16_fwd(Wd: torch.Tensor, X, U=None, B=None, alpha: float = 0.0, out=None):
     if r:
         _need(U, torch.bfloat16, "U", (M, r))
         _need(B, torch.bfloat16, "B", (N, r))
-    Y = out if out is not None else torch.empty(M, N, dtype=torch.bfloat16, device=X.device)
+    Y = out if out is not None else _empty(M, N, dtype=torch.bfloat16, device=X.device)
     _need(Y, torch.bfloat16, "Y", (M, N))
     check(lib().qlora_bf16_fwd(_ptr(Wd), N, K, _ptr(X), M, _ptr(U), _ptr(B), r, float(alpha), _ptr(Y), _stream()),
           "qlora_bf16_fwd")
@@ -491,7 +547,7 @@ def bf16_dx(WdT: torch.Tensor, dY, G=None, A=None, alpha: float = 0.0, out=None,
     if r:
         _need(G, torch.bfloat16, "G", (M, r))
         _need(A, torch.bfloat16, "A", (r, K))
-    dX = out if out is not None else torch.empty(M, K, dtype=torch.bfloat16, device=dY.device)
+    dX = out if out is not None else _empty(M, K, dtype=torch.bfloat16, device=dY.device)
     _need(dX, torch.bfloat16, "dX", (M, K))
     if ws is None:
         ws = workspace(workspace_bytes(_lib.QLORA_OP_BF16_DX, M, N, K, r, 1), dY.device)
@@ -505,7 +561,7 @@ def group_dequant(qs: Sequence[QuantizedWeight], out=None, transposed=False):
     transposed [K x G N]."""
     G, N, K = len(qs), qs[0].rows, qs[0].cols
     shape = (K, G * N) if transposed else (G * N, K)
-    out = out if out is not None else torch.empty(*shape, dtype=torch.bfloat16, device=qs[0].codes.device)
+    out = out if out is not None else _empty(*shape, dtype=torch.bfloat16, device=qs[0].codes.device)
     _need(out, torch.bfloat16, "out", shape)
     fn = lib().qlora_group_dequant_t if transposed else lib().qlora_group_dequant
     check(fn(_group_descs(qs), G, _ptr(out), _stream()),
@@ -523,7 +579,7 @@ def bf16_group_fwd(Wd: torch.Tensor, G: int, X, U=None, B=None, alpha: float = 0
     if r:
         _need(U, torch.bfloat16, "U", (M, G * r))
         _need(B, torch.bfloat16, "B", (G * N, r))
-    Y = out if out is not None else torch.empty(M, G * N, dtype=torch.bfloat16, device=X.device)
+    Y = out if out is not None else _empty(M, G * N, dtype=torch.bfloat16, device=X.device)
     _need(Y, torch.bfloat16, "Y", (M, G * N))
     check(lib().qlora_bf16_group_fwd(_ptr(Wd), G, N, K, _ptr(X), M, _ptr(U), _ptr(B), r, float(alpha), _ptr(Y),
                                      _stream()), "qlora_bf16_group_fwd")
@@ -540,7 +596,7 @@ def bf16_group_dx(WdT: torch.Tensor, G: int, dY, Gm=None, A=None, alpha: float =
     if r:
         _need(Gm, torch.bfloat16, "Gm", (M, G * r))
         _need(A, torch.bfloat16, "A", (G * r, K))
-    dX = out if out is not None else torch.empty(M, K, dtype=torch.bfloat16, device=dY.device)
+    dX = out if out is not None else _empty(M, K, dtype=torch.bfloat16, device=dY.device)
     _need(dX, torch.bfloat16, "dX", (M, K))
     if ws is None:
         ws = workspace(workspace_bytes(_lib.QLORA_OP_BF16_DX, M, N, K, r, G), dY.device)
@@ -555,7 +611,7 @@ def group_lora_dy_b(dY, B, G: int, Gm=None, ws=None):
     M, N = dY.shape[0], dY.shape[1] // G
     r = B.shape[1]
     _need(B, torch.bfloat16, "B", (G * N, r))
-    Gm = Gm if Gm is not None else torch.empty(M, G * r, dtype=torch.bfloat16, device=dY.device)
+    Gm = Gm if Gm is not None else _empty(M, G * r, dtype=torch.bfloat16, device=dY.device)
     if ws is None:
         ws = workspace(workspace_bytes(_lib.QLORA_OP_GROUP_LORA, M, N, 64, r, G), dY.device)
     check(lib().qlora_group_lora_dy_b(_ptr(dY), _ptr(B), M, N, r, G, _ptr(Gm), _ptr(ws),
@@ -569,8 +625,8 @@ def group_lora_grads(X, dY, U, Gm, G: int, alpha, dA=None, dB=None, ws=None):
     N, r = dY.shape[1] // G, U.shape[1] // G
     for t, n, shp in ((X, "X", (M, K)), (dY, "dY", (M, G * N)), (U, "U", (M, G * r)), (Gm, "Gm", (M, G * r))):
         _need(t, torch.bfloat16, n, shp)
-    dA = dA if dA is not None else torch.empty(G * r, K, dtype=torch.float32, device=X.device)
-    dB = dB if dB is not None else torch.empty(G * N, r, dtype=torch.float32, device=X.device)
+    dA = dA if dA is not None else _empty(G * r, K, dtype=torch.float32, device=X.device)
+    dB = dB if dB is not None else _empty(G * N, r, dtype=torch.float32, device=X.device)
     if ws is None:
         ws = workspace(workspace_bytes(_lib.QLORA_OP_GROUP_LORA, M, N, K, r, G), X.device)
     check(lib().qlora_group_lora_grads(_ptr(X), _ptr(dY), _ptr(U), _ptr(Gm), M, N, K, r, G, float(alpha), _ptr(dA),
@@ -584,7 +640,7 @@ def nf4_dx(q: QuantizedWeight, dY, G=None, A=None, alpha: float = 0.0, out=None)
     _need(dY, torch.bfloat16, "dY")
     M = dY.shape[0]
     r = 0 if G is None else G.shape[1]
-    dX = out if out is not None else torch.empty(M, q.cols, dtype=torch.bfloat16, device=dY.device)
+    dX = out if out is not None else _empty(M, q.cols, dtype=torch.bfloat16, device=dY.device)
     d = q.desc()
     check(lib().qlora_nf4_dx(ctypes.byref(d), _ptr(dY), M, _ptr(G), _ptr(A), r, float(alpha), _ptr(dX),
                              _stream()), "qlora_nf4_dx")
@@ -642,7 +698,7 @@ class PagedAdamW:
         self.layout = dict(resident=lay.resident, resident_bytes=lay.resident_bytes, chunk=lay.chunk,
                            staging_bytes=lay.staging_bytes)
         self.budget = int(budget_bytes)
-        self.ws = torch.empty(max(self.budget, 256), dtype=torch.uint8, device=self.params[0].device)
+        self.ws = _empty(max(self.budget, 256), dtype=torch.uint8, device=self.params[0].device)
         self.hp = (lr, beta1, beta2, eps, weight_decay)
         self.copy_stream = copy_stream
         self.t = 0

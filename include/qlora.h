@@ -73,7 +73,11 @@ typedef enum {
                               GEMV jobs of different codebooks or formats
                               in one call */
   QLORA_E_WORKSPACE = 5,   /* ws_bytes smaller than qlora_workspace_bytes()  */
-  QLORA_E_HIP = 6          /* a HIP launch/copy error; see qlora_last_hip_error */
+  QLORA_E_HIP = 6,         /* a HIP launch/copy error; see qlora_last_hip_error */
+  QLORA_E_FORMAT = 7,      /* not a serialized weight header: wrong magic,
+                              version, header size, or a buffer too short   */
+  QLORA_E_TABLE = 8        /* a serialized weight was written with level
+                              tables other than this library's             */
 } qlora_status;
 
 typedef enum {
@@ -518,6 +522,53 @@ qlora_status qlora_gemv_prepare(const qlora_gemv_job* jobs, int32_t njobs, void*
  * be ordered after it by the caller.  QLORA_E_SHAPE for a plan that
  * qlora_gemv_prepare did not fill. */
 qlora_status qlora_gemv_run(const qlora_gemv_plan* plan, void* stream);
+
+/* ---- Serialized quantized weights -------------------------------------
+ * An adapter is trained against one exact quantized base weight: the pages
+ * store the adapters apart from the frozen model and note that they only
+ * work with the base model (and quantization) they were trained on
+ * (deepfa.ir blog, "LoRA: Prerequisite").  A weight quantized once can be
+ * written out and read back byte for byte; the header records the level
+ * tables it was encoded with, so a file from a library whose tables differ
+ * is refused instead of being decoded with the wrong levels.
+ *
+ * File = header (QLORA_QTENSOR_HEADER_BYTES) | codes | absmax_q |
+ * group_scale (fp32), the three arrays exactly as qlora_sizes() sizes them.
+ * Header, all fields little-endian:
+ *    0  char[8]  magic "QLORAQT1"
+ *    8  uint32   version (1)
+ *   12  uint32   header bytes (64)
+ *   16  int64    rows
+ *   24  int64    cols
+ *   32  int32    blocksize (64)      36  int32  group_blocks (256)
+ *   40  int32    codebook            44  int32  absmax_format
+ *   48  uint64   level-table id (qlora_level_table_id)
+ *   56  uint64   payload bytes (codes + absmax_q + group_scale)
+ * All calls below are host-only and touch no device memory. */
+#define QLORA_QTENSOR_HEADER_BYTES 64
+
+/* 64-bit FNV-1a digest of the tables a weight of this codebook and
+ * second-level format is decoded with: the 16 fp32 levels of the 4-bit
+ * codebook and the fp32 levels of the block-constant code (256 for LINEAR8,
+ * 127 for FP8), as bit patterns, after a version tag.  QLORA_E_NULL for a
+ * NULL id, QLORA_E_UNSUPPORTED for an unknown codebook or format. */
+qlora_status qlora_level_table_id(int32_t codebook, int32_t absmax_format, uint64_t* id);
+
+/* Write the header of q (its sizes, codebook and format; the device
+ * pointers are not read) into out[0 .. QLORA_QTENSOR_HEADER_BYTES).
+ * QLORA_E_NULL, QLORA_E_FORMAT when out_bytes is too small, and the errors
+ * of qlora_sizes / qlora_level_table_id for an invalid descriptor. */
+qlora_status qlora_qtensor_header_write(const qlora_nf4_weight* q, uint8_t* out, size_t out_bytes);
+
+/* Parse a header: fill q's rows, cols, blocksize, group_blocks, codebook and
+ * absmax_format (its pointers are left as they are) and *payload_bytes
+ * (nullable).  QLORA_E_FORMAT for a short buffer, wrong magic, version or
+ * header size, or a payload size that disagrees with the sizes;
+ * QLORA_E_UNSUPPORTED / QLORA_E_SHAPE for sizes or tables this library
+ * does not handle; QLORA_E_TABLE when the recorded level-table id differs
+ * from this library's for that codebook and format. */
+qlora_status qlora_qtensor_header_read(const uint8_t* in, size_t in_bytes, qlora_nf4_weight* q,
+                                       uint64_t* payload_bytes);
 
 #ifdef __cplusplus
 }
