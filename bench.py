@@ -202,7 +202,8 @@ def decode_batch_study(jobs, layers, r, alpha, passes, dev):
 # and the device headers it includes
 KERNEL_SOURCES = {"fwd_kernel": ["gemm_nf4.hip", "gemm_common.h"], "dx_kernel": ["gemm_nf4.hip", "gemm_common.h"],
                   "dense_gemm": ["gemm_bf16.hip", "gemm_common.h"],
-                  "quantize_kernel": ["quantize.hip"], "gemv_kernel": ["gemv.hip"]}
+                  "quantize_kernel": ["quantize.hip"], "gemv_kernel": ["gemv.hip"],
+                  "dequant_kernel": ["quantize.hip"], "dequant_t_kernel": ["quantize.hip"]}
 DEVICE_HEADERS = ["device.h", "lds.h"]
 
 
@@ -232,7 +233,8 @@ def traffic_for(kernel):
 # rocprofv3 kernel name -> bench kernel; a launch of the fused GEMMs may add a
 # half-tile tail dispatch, whose bytes count towards that launch
 TRAFFIC_KERNELS = {"nf4_fwd_r_kernel": "fwd_kernel", "nf4_dx_kernel": "dx_kernel", "bf16_fwd_kernel": "dense_gemm",
-                   "quantize_kernel": "quantize_kernel", "nf4_gemv_kernel": "gemv_kernel"}
+                   "quantize_kernel": "quantize_kernel", "nf4_gemv_kernel": "gemv_kernel",
+                   "dequant_kernel": "dequant_kernel", "dequant_t_kernel": "dequant_t_kernel"}
 TAIL_KERNELS = {"nf4_fwd_n32_kernel": "fwd_kernel", "nf4_dx_half_kernel": "dx_kernel"}
 
 

@@ -29,8 +29,11 @@ def check(status, what):
 
 
 def _empty(*shape, dtype, device):
-    """An output or workspace buffer (guarded under QLORA_DEBUG=1)."""
-    return _debug.empty(shape, dtype, device)
+    """An output or workspace buffer (guarded under QLORA_DEBUG=1); the
+    shape is given as sizes or as one tuple, as for torch.empty."""
+    if len(shape) == 1 and isinstance(shape[0], (tuple, list, torch.Size)):
+        shape = tuple(shape[0])
+    return _debug.empty(tuple(int(d) for d in shape), dtype, device)
 
 
 def _ptr(t: Optional[torch.Tensor]):

@@ -35,3 +35,14 @@ def test_write_into_a_guard_is_caught(enabled, where):
         debug.after_call("qlora_test_call")
     del t, base
     debug.after_call("after the buffer is gone")   # dead buffers are dropped from the check
+
+
+@pytest.mark.parametrize("on", [False, True])
+def test_binding_allocator_takes_sizes_or_one_tuple(monkeypatch, on):
+    from bit_quantized_finetuning_nf4_amd import ops
+    monkeypatch.setattr(debug, "ENABLED", on)
+    monkeypatch.setattr(debug, "_live", [])
+    for args in ((2, 3), ((2, 3),), ([2, 3],), (torch.Size([2, 3]),)):
+        t = ops._empty(*args, dtype=torch.bfloat16, device="cpu")
+        assert t.shape == (2, 3) and t.dtype == torch.bfloat16
+    assert ops._empty(5, dtype=torch.uint8, device="cpu").shape == (5,)
