@@ -230,6 +230,18 @@ def traffic_for(kernel):
     return e.get("hbm_bytes_per_launch")
 
 
+def mfma_counters_for(kernel, source):
+    """MFMA busy fraction, VALU per MFMA and clock of a kernel from the
+    committed counter summary, if it was taken on the current source."""
+    p = os.path.join(ROOT, "profiles", "mfma.json")
+    if not os.path.exists(p):
+        return None
+    e = json.load(open(p)).get(kernel)
+    if not e or e.get("source_digest") != source_digest(source):
+        return None
+    return e
+
+
 # rocprofv3 kernel name -> bench kernel; a launch of the fused GEMMs may add a
 # half-tile tail dispatch, whose bytes count towards that launch
 TRAFFIC_KERNELS = {"nf4_fwd_r_kernel": "fwd_kernel", "nf4_dx_kernel": "dx_kernel", "bf16_fwd_kernel": "dense_gemm",
@@ -770,7 +782,10 @@ def main():
                          "clock from a rocprofv3 --pmc counter_collection.csv of the MFMA_COUNTERS, on stdout")
     args = ap.parse_args()
     if args.summarize_mfma:
-        print(json.dumps(summarize_mfma(args.summarize_mfma), indent=1))
+        res = summarize_mfma(args.summarize_mfma)
+        if "bf16_fwd_kernel" in res:
+            res["bf16_fwd_kernel"]["source_digest"] = source_digest("dense_gemm")
+        print(json.dumps(res, indent=1))
         return
     if args.summarize_pmc:
         print(json.dumps(summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.copy_probe_mib), indent=1))
@@ -832,6 +847,11 @@ def main():
                           "linears of each product (q/k/v, o, gate/up, down); achieved = the sum over the 7 "
                           "linears / the sum of the 8 product calls' HIP-event durations (a call is one launch, or "
                           "two when its last round of tiles takes a narrower tile width)"}
+    mc = mfma_counters_for("bf16_fwd_kernel", "dense_gemm")
+    if mc:
+        roof["counters"] = {"source": "profiles/mfma.json (rocprofv3 --pmc on the same device code)",
+                            "mfma_busy": mc["mfma_busy"], "valu_per_mfma": mc["valu_per_mfma"],
+                            "clock_ghz": mc["clock_ghz"]}
     if clock:
         roof["clock_mhz_median"] = clock["median_mhz"]
         roof["frac_at_measured_clock"] = prod["tflops"] / (PEAK_BF16_TFLOPS * clock["median_mhz"] / 2400.0)
