@@ -232,13 +232,14 @@ __global__ __launch_bounds__(256) void quantize_kernel(const bf16_t* __restrict_
 // goes to out + i out_gs.
 template <int CB>
 __global__ __launch_bounds__(256) void dequant_kernel(DeqSrcs src, int64_t numel, int64_t nb, int absfmt,
-                                                      bf16_t* __restrict__ out, int64_t out_gs) {
-  const int wi = blockIdx.y;
+                                                      bf16_t* __restrict__ out, int64_t out_gs, int rev) {
+  const int wi = rev ? (int)gridDim.y - 1 - (int)blockIdx.y : (int)blockIdx.y;
   const uint8_t* __restrict__ codes = src.codes[wi];
   const uint8_t* __restrict__ absmax_q = src.absmax_q[wi];
   const float* __restrict__ group_scale = src.group_scale[wi];
   out += wi * out_gs;
-  const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t bx = rev ? (int64_t)gridDim.x - 1 - blockIdx.x : (int64_t)blockIdx.x;
+  const int64_t g = bx * blockDim.x + threadIdx.x;
   const int64_t b = g >> 2;
   if (b >= nb) return;
   const float t = block_scale(absmax_q[b], group_scale[b / kGroupBlocks], absfmt);
@@ -282,15 +283,17 @@ __global__ __launch_bounds__(256) void dequant_kernel(DeqSrcs src, int64_t numel
 constexpr int kTrStride = 33;
 template <int CB>
 __global__ __launch_bounds__(256) void dequant_t_kernel(DeqSrcs src, int64_t N, int64_t K, int absfmt,
-                                                        bf16_t* __restrict__ out, int64_t ldo, int64_t out_gs) {
-  const int wi = blockIdx.z;
+                                                        bf16_t* __restrict__ out, int64_t ldo, int64_t out_gs,
+                                                        int rev) {
+  const int wi = rev ? (int)gridDim.z - 1 - (int)blockIdx.z : (int)blockIdx.z;
   const uint8_t* __restrict__ codes = src.codes[wi];
   const uint8_t* __restrict__ absmax_q = src.absmax_q[wi];
   const float* __restrict__ group_scale = src.group_scale[wi];
   out += wi * out_gs;
   __shared__ uint32_t tile[256 * kTrStride];
   const int t = threadIdx.x, rp = t & 31, cg = t >> 5;
-  const int64_t n0 = (int64_t)blockIdx.y * 64, k0 = (int64_t)blockIdx.x * 256;
+  const int64_t by = rev ? (int64_t)gridDim.y - 1 - blockIdx.y : (int64_t)blockIdx.y;
+  const int64_t n0 = by * 64, k0 = (int64_t)blockIdx.x * 256;
   const int64_t kc = k0 + 32 * cg;
   if (kc < K) {
     uint4 c[2];
@@ -370,20 +373,28 @@ hipError_t launch_quantize(const bf16_t* W, int64_t numel, uint8_t* codes, uint8
   return hipGetLastError();
 }
 
+// Write order of a dequantization.  The dense GEMM that follows starts on the
+// first weight rows (forward) or the first contraction columns (dX), so when
+// the bf16 output is larger than the 256 MB last-level cache the workgroups
+// run in reverse: the part written last, which the cache still holds, is the
+// part read first.  Each workgroup computes the same values in either order.
+constexpr int64_t kLlcBytes = (int64_t)256 << 20;
+
 hipError_t launch_dequant_group(const DeqSrcs& src, int n, int64_t N, int64_t K, int codebook, int absfmt,
                                 bool transposed, bf16_t* out, int64_t ldo, int64_t out_gs, hipStream_t s) {
   if (n < 1 || n > kDeqMax) return hipErrorInvalidValue;
+  const int rev = (int64_t)n * N * K * 2 > kLlcBytes ? 1 : 0;
   if (!transposed) {
     const int64_t numel = N * K, nb = (numel + kBlock - 1) / kBlock;
     auto* fn = codebook == kCbFp4 ? &dequant_kernel<kCbFp4> : codebook == kCbInt4 ? &dequant_kernel<kCbInt4>
                                                                                   : &dequant_kernel<kCbNf4>;
     hipLaunchKernelGGL(fn, dim3((unsigned)((4 * nb + 255) / 256), (unsigned)n), dim3(256), 0, s, src, numel, nb,
-                       absfmt, out, out_gs);
+                       absfmt, out, out_gs, rev);
   } else {
     auto* fn = codebook == kCbFp4 ? &dequant_t_kernel<kCbFp4> : codebook == kCbInt4 ? &dequant_t_kernel<kCbInt4>
                                                                                     : &dequant_t_kernel<kCbNf4>;
     hipLaunchKernelGGL(fn, dim3((unsigned)((K + 255) / 256), (unsigned)((N + 63) / 64), (unsigned)n), dim3(256), 0,
-                       s, src, N, K, absfmt, out, ldo, out_gs);
+                       s, src, N, K, absfmt, out, ldo, out_gs, rev);
   }
   return hipGetLastError();
 }

@@ -213,3 +213,26 @@ def test_group_dequant_mixed_formats_and_long_groups():
         for g, q in enumerate(qs):
             assert torch.equal(Wd[g * N:(g + 1) * N], ops.dequant(q)), (G, g)
             assert torch.equal(WdT[:, g * N:(g + 1) * N], ops.dequant_t(q)), (G, g)
+
+
+def test_group_dequant_past_the_last_level_cache_equals_per_weight():
+    """A launch whose bf16 output exceeds 256 MB (the last-level cache) runs
+    its workgroups in reverse order; each weight alone here is below that
+    size and runs in order.  Both must give the same bits: the three 65B
+    q/k/v weights (403 MB stacked, 134 MB each), ragged row count on a
+    fourth group (3 x 8200 rows, so the reversed grid's first workgroup is a
+    partial one)."""
+    for N, K in ((8192, 8192), (8200, 8192)):
+        print(f"[group dequant] reversed order, 3 x {N} x {K}", flush=True)
+        qs = [ops.quantize(synth.normal_bf16((N, K), 0.02, 900 + g, "cuda", outliers=0.001)) for g in range(3)]
+        assert 3 * N * K * 2 > (256 << 20) and N * K * 2 < (256 << 20)
+        Wd = ops.group_dequant(qs)
+        for g, q in enumerate(qs):
+            assert torch.equal(Wd[g * N:(g + 1) * N], ops.dequant(q)), g
+        del Wd
+        WdT = ops.group_dequant(qs, transposed=True)
+        for g, q in enumerate(qs):
+            assert torch.equal(WdT[:, g * N:(g + 1) * N], ops.dequant_t(q)), g
+        del WdT, qs
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
