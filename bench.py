@@ -526,6 +526,14 @@ class ClockSampler:
 GROUPS = (("q", "k", "v"), ("o",), ("gate", "up"), ("down",))
 
 
+def dy_late(dY):
+    """The staged backward's order, as qlora_linear_bwd / qlora_group_bwd take
+    it: G = dY B after the transposed dequantization (right before the dX
+    product, so dY is still in the last-level cache there) when dY is at most
+    128 MB, else first."""
+    return dY.numel() * 2 <= (128 << 20)
+
+
 class LayerSet:
     """Inputs, outputs and scratch of one layer set, resident on the device,
     and one step of the path over it: grouped, per-linear staged, or fused
@@ -639,8 +647,12 @@ class LayerSet:
             mark(ev["p"][2])
         for i, g in enumerate(self.groups):
             G, N, K = g["G"], g["N"], g["K"]
-            ops.group_lora_dy_b(g["dY"], g["B"], G, Gm=g["Gm"], ws=self.ws)
+            late = dy_late(g["dY"])
+            if not late:
+                ops.group_lora_dy_b(g["dY"], g["B"], G, Gm=g["Gm"], ws=self.ws)
             WdT = ops.group_dequant(g["qs"], out=self.wbuf[:G * N * K].view(K, G * N), transposed=True)
+            if late:
+                ops.group_lora_dy_b(g["dY"], g["B"], G, Gm=g["Gm"], ws=self.ws)
             if ev:
                 mark(ev["d"][i][0])
             ops.bf16_group_dx(WdT, G, g["dY"], g["Gm"], g["A"], a, out=g["dX"], ws=self.ws)
@@ -666,9 +678,13 @@ class LayerSet:
         if ev:
             mark(ev["p"][2])
         for i, o in enumerate(L):
-            ops.lora_dy_b(o["dY"], o["B"], G=o["G"], ws=self.ws)
+            late = path == "staged" and dy_late(o["dY"])
+            if not late:
+                ops.lora_dy_b(o["dY"], o["B"], G=o["G"], ws=self.ws)
             if path == "staged":
                 WdT = ops.dequant_t(o["q"], out=self.wbuf[:o["N"] * o["K"]].view(o["K"], o["N"]))
+                if late:
+                    ops.lora_dy_b(o["dY"], o["B"], G=o["G"], ws=self.ws)
                 if ev:
                     mark(ev["d"][i][0])
                 ops.bf16_dx(WdT, o["dY"], o["G"], o["A"], a, out=o["dX"], ws=self.ws)

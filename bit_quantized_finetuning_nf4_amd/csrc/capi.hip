@@ -109,6 +109,13 @@ Nf4View view(const qlora_nf4_weight* q) {
 
 constexpr int64_t kStagedMinTokens = 1024;
 
+// Order of the staged backward.  G = dY B reads dY, which the dX product
+// reads again; when dY (M x N bf16) is at most half the 256 MB last-level
+// cache, G runs after the transposed dequantization, right before the dX
+// product, so that dY is still in the cache there.  A larger dY would push
+// the dequantized weight out instead, so G runs first.
+bool dy_late(int64_t M, int64_t N) { return M * N * 2 <= ((int64_t)128 << 20); }
+
 // The staged path's bf16 weight is addressed with 32-bit byte offsets, and
 // the transposing dequant grid has ceil(N / 64) rows.  The dense kernel runs
 // its contraction in whole pairs of 32-wide stages: K % 64 == 0 holds on
@@ -547,20 +554,23 @@ qlora_status qlora_linear_bwd(const qlora_nf4_weight* W, const uint16_t* X, cons
   hipStream_t s = (hipStream_t)stream;
   const Nf4View v = view(W);
   const int64_t N = W->rows, K = W->cols;
+  bf16_t* WdT = staged ? reinterpret_cast<bf16_t*>(ws_at(ws, L.wdt)) : nullptr;
+  auto dequant_t = [&]() -> qlora_status {
+    return hip_status(
+        launch_dequant_t(W->codes, W->absmax_q, W->group_scale, N, K, W->codebook, W->absmax_format, WdT, N, s));
+  };
   // dX = dY deq(W) + s G A: the dense kernel on deq(W)^T, or the fused one
   auto run_dx = [&](const bf16_t* G, float sc) -> qlora_status {
     if (!staged) return hip_status(launch_dx(v, dY, M, G, r > 0 ? A : nullptr, r, sc, dX, s));
-    bf16_t* WdT = reinterpret_cast<bf16_t*>(ws_at(ws, L.wdt));
-    qlora_status st2 = hip_status(
-        launch_dequant_t(W->codes, W->absmax_q, W->group_scale, N, K, W->codebook, W->absmax_format, WdT, N, s));
-    if (st2 != QLORA_OK) return st2;
     return hip_status(launch_bf16_fwd(WdT, K, N, dY, M, G, r > 0 ? A : nullptr, true, r, sc, dX, s,
                                       reinterpret_cast<float*>(ws_at(ws, L.split)), L.split_bytes));
   };
   if (r == 0) {
     if (!dX) return QLORA_OK;
+    if (staged && (st = dequant_t()) != QLORA_OK) return st;
     return run_dx(nullptr, 0.0f);
   }
+  const bool g_late = staged && dy_late(M, N);
   const float sc = (float)((double)alpha / (double)r);
   bf16_t* G = reinterpret_cast<bf16_t*>(ws_at(ws, L.g));
   float* part = reinterpret_cast<float*>(ws_at(ws, L.part));
@@ -571,9 +581,11 @@ qlora_status qlora_linear_bwd(const qlora_nf4_weight* W, const uint16_t* X, cons
     if (st != QLORA_OK) return st;
     U = Ud;
   }
+  if (staged && g_late && (st = dequant_t()) != QLORA_OK) return st;
   st = hip_status(launch_dyb(dY, B, M, N, r, part, G, 1.0f, s));
   if (st != QLORA_OK) return st;
   if (dX) {
+    if (staged && !g_late && (st = dequant_t()) != QLORA_OK) return st;
     st = run_dx(G, sc);
     if (st != QLORA_OK) return st;
   }
@@ -722,9 +734,11 @@ qlora_status qlora_group_bwd(const qlora_nf4_weight* W, int32_t G, const uint16_
     U = Ud;
   }
   // G [M x G r]: group g is dY_g B_g
+  const bool g_late = dX && dy_late(M, NG);
+  if (g_late && (st = group_dequant(W, G, true, WdT, s)) != QLORA_OK) return st;
   if ((st = hip_status(launch_dyb_group(dY, NG, B, M, N, r, G, part, Gm, 1.0f, s))) != QLORA_OK) return st;
   if (dX) {
-    if ((st = group_dequant(W, G, true, WdT, s)) != QLORA_OK) return st;
+    if (!g_late && (st = group_dequant(W, G, true, WdT, s)) != QLORA_OK) return st;
     if ((st = group_dx_product(WdT, G, N, K, dY, M, Gm, A, r, alpha, dX, s,
                                reinterpret_cast<float*>(ws_at(ws, L.split)), L.split_bytes)) != QLORA_OK)
       return st;
