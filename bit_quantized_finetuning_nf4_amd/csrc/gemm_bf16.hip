@@ -51,10 +51,15 @@ __device__ __forceinline__ int xcd_tile_id() {
   if ((nwg & 7) == 0) id = (id & 7) * (nwg >> 3) + (id >> 3);
   return id;
 }
+// With 16 token tiles or more a group holds 8 of them, so each weight tile
+// streams through an XCD's L2 half as often (the weight is the larger
+// operand of these products): at 4096 tokens the 65B products ran 1.4 %
+// faster than with 4; at 2048 tokens (8 token tiles) 4 stays slightly ahead.
 __device__ __forceinline__ void map_tile_grouped(int id, int tiles_c, int tiles_r, int& tc, int& tr) {
-  const int per_group = kDGroup * tiles_c;
-  const int g = id / per_group, first = g * kDGroup;
-  const int size = min(kDGroup, tiles_r - first);
+  const int grp = tiles_r >= 16 ? 2 * kDGroup : kDGroup;
+  const int per_group = grp * tiles_c;
+  const int g = id / per_group, first = g * grp;
+  const int size = min(grp, tiles_r - first);
   const int local = id - g * per_group;
   tr = first + local % size;
   tc = local / size;
