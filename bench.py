@@ -807,8 +807,9 @@ def main():
         print(json.dumps(summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.copy_probe_mib), indent=1))
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
-              "(sharding is described in DESIGN.md); use --gpus 1", file=sys.stderr)
+        print("bench.py runs on one GPU only: the library has no multi-GPU path (tokens would shard "
+              "data-parallel, with one all-reduce of the adapter gradients per layer); use --gpus 1",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch
